@@ -1,0 +1,218 @@
+"""CPU oracle for the batch-1 decode step (TEST INFRASTRUCTURE ONLY).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The GPU library never calls it, and it
+shares no code with the GPU library.  The arithmetic lives in ``oracle.c``
+(plain float64 C); this module only marshals numpy arrays.
+
+Parity status of each function (how it is pinned, see tests/test_oracle_*.py):
+  bf16 rounding, rmsnorm, gemv, rope, softmax, attend, silu, argmax,
+  decode_step, prefill: pinned by closed forms, hand-worked examples, library
+  special cases and invariants.  Full-model logits beyond those pins have no
+  printed values on the pages to compare against.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_dp = ctypes.POINTER(ctypes.c_double)
+
+
+class _Model(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int32), ("hidden", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("ffn", ctypes.c_int32),
+                ("vocab", ctypes.c_int32), ("max_seq", ctypes.c_int32), ("rms_eps", ctypes.c_double),
+                ("rope_theta", ctypes.c_double), ("dtype", ctypes.c_int32), ("tied", ctypes.c_int32)]
+
+
+def build(force: bool = True) -> str:
+    """Compile liboracle.so (gcc, -O2, no FP contraction, OpenMP over rows)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
+                               "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=False)
+        lib = ctypes.CDLL(_LIB_PATH)
+        v, i32, dbl = ctypes.c_void_p, ctypes.c_int, ctypes.c_double
+        sig = {
+            "or_f64_from_bf16": ([ctypes.c_uint16], dbl),
+            "or_bf16_from_f64": ([dbl], ctypes.c_uint16),
+            "or_rmsnorm": ([v, i32, v, i32, dbl, v], None),
+            "or_gemv": ([v, i32, i32, i32, v, v], None),
+            "or_rope": ([v, i32, i32, i32, dbl], None),
+            "or_softmax": ([v, i32, v], None),
+            "or_attend": ([v, v, v, i32, i32, i32, v], None),
+            "or_silu": ([dbl], dbl),
+            "or_argmax": ([v, i32], i32),
+            "or_decode_step": ([ctypes.POINTER(_Model), v, v, v, i32, i32, v], i32),
+            "or_prefill": ([ctypes.POINTER(_Model), v, v, v, v, i32, i32], i32),
+        }
+        for name, (args, res) in sig.items():
+            f = getattr(lib, name)
+            f.argtypes, f.restype = args, res
+        _lib = lib
+    return _lib
+
+
+def _p(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _dt(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return 0
+    if a.dtype == np.uint16:
+        return 1
+    raise TypeError(f"weights must be float32 or uint16 (bfloat16 bits), got {a.dtype}")
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+# ---- storage conversions -----------------------------------------------------
+
+def bf16_from_f64(x: float) -> int:
+    return int(_load().or_bf16_from_f64(float(x)))
+
+
+def f64_from_bf16(b: int) -> float:
+    return float(_load().or_f64_from_bf16(int(b)))
+
+
+def bf16_array_from_f64(a) -> np.ndarray:
+    a = np.asarray(a, dtype=np.float64)
+    f = _load().or_bf16_from_f64
+    return np.array([f(float(x)) for x in a.ravel()], dtype=np.uint16).reshape(a.shape)
+
+
+def f64_array_from_bf16(a: np.ndarray) -> np.ndarray:
+    a = np.ascontiguousarray(a, dtype=np.uint16)
+    return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)  # exact widening
+
+
+# ---- operators -----------------------------------------------------------------
+
+def rmsnorm(x, g: np.ndarray, eps: float) -> np.ndarray:
+    x = _f64(x)
+    y = np.empty_like(x)
+    _load().or_rmsnorm(_p(x), x.size, _p(g), _dt(g), float(eps), _p(y))
+    return y
+
+
+def gemv(W: np.ndarray, h) -> np.ndarray:
+    h = _f64(h)
+    rows, cols = W.shape
+    assert h.size == cols
+    y = np.empty(rows, dtype=np.float64)
+    _load().or_gemv(_p(W), _dt(W), rows, cols, _p(h), _p(y))
+    return y
+
+
+def rope(v, n_heads: int, head_dim: int, pos: int, theta: float) -> np.ndarray:
+    v = _f64(v).copy()
+    assert v.size == n_heads * head_dim
+    _load().or_rope(_p(v), n_heads, head_dim, pos, float(theta))
+    return v
+
+
+def softmax(s) -> np.ndarray:
+    s = _f64(s)
+    p = np.empty_like(s)
+    _load().or_softmax(_p(s), s.size, _p(p))
+    return p
+
+
+def attend(q, K: np.ndarray, V: np.ndarray) -> np.ndarray:
+    """q [d]; K, V [n_pos][d] float32 or bf16 bits."""
+    q = _f64(q)
+    K = np.ascontiguousarray(K)
+    V = np.ascontiguousarray(V)
+    n_pos, d = K.shape
+    o = np.empty(d, dtype=np.float64)
+    _load().or_attend(_p(q), _p(K), _p(V), _dt(K), d, n_pos, _p(o))
+    return o
+
+
+def silu(z: float) -> float:
+    return float(_load().or_silu(float(z)))
+
+
+def argmax(v) -> int:
+    v = _f64(v)
+    return int(_load().or_argmax(_p(v), v.size))
+
+
+# ---- whole model -----------------------------------------------------------------
+
+LAYER_KINDS = ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate", "w_up", "w_down")
+
+
+class Model:
+    """Shapes plus host weights (numpy, row-major [out][in]) and the oracle's
+    own KV cache arrays [n_layers][n_kv_heads][max_seq][head_dim]."""
+
+    def __init__(self, shape: dict, weights: dict, max_seq: int):
+        self.shape = dict(shape)
+        self.max_seq = int(max_seq)
+        dt = 1 if shape["dtype"] == "bf16" else 0
+        self._m = _Model(shape["n_layers"], shape["hidden"], shape["n_heads"], shape["n_kv_heads"],
+                         shape["head_dim"], shape["ffn"], shape["vocab"], self.max_seq,
+                         float(shape["rms_eps"]), float(shape["rope_theta"]), dt, int(bool(shape["tied"])))
+        self._keep = []
+        ptrs = []
+
+        def add(a):
+            if a is None:
+                ptrs.append(None)
+                return
+            a = np.ascontiguousarray(a)
+            assert _dt(a) == dt, "weight dtype must match the model dtype"
+            self._keep.append(a)
+            ptrs.append(a.ctypes.data)
+
+        add(weights["embed"])
+        add(weights["final_norm"])
+        add(None if shape["tied"] else weights["lm_head"])
+        assert len(weights["layers"]) == shape["n_layers"]
+        for lw in weights["layers"]:
+            for k in LAYER_KINDS:
+                add(lw[k])
+        self._ptrs = (ctypes.c_void_p * len(ptrs))(*ptrs)
+        npdt = np.uint16 if dt else np.float32
+        cache_shape = (shape["n_layers"], shape["n_kv_heads"], self.max_seq, shape["head_dim"])
+        self.k = np.zeros(cache_shape, dtype=npdt)
+        self.v = np.zeros(cache_shape, dtype=npdt)
+
+    def decode_step(self, token: int, pos: int, want_logits: bool = True):
+        logits = np.empty(self.shape["vocab"], dtype=np.float64) if want_logits else None
+        rc = _load().or_decode_step(ctypes.byref(self._m), self._ptrs, _p(self.k), _p(self.v), int(token),
+                                    int(pos), _p(logits) if want_logits else None)
+        if rc != 0:
+            raise ValueError(f"or_decode_step failed with code {rc}")
+        return logits
+
+    def prefill(self, tokens, start_pos: int = 0) -> None:
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        rc = _load().or_prefill(ctypes.byref(self._m), self._ptrs, _p(self.k), _p(self.v), _p(t), t.size,
+                                int(start_pos))
+        if rc != 0:
+            raise ValueError(f"or_prefill failed with code {rc}")
