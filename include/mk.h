@@ -1,0 +1,158 @@
+/*
+ * mk.h -- C ABI of a persistent decode megakernel for AMD MI355X (gfx950).
+ *
+ * One call of mk_decode_step runs one batch-1 autoregressive decode step of
+ * a Llama-style decoder as ONE kernel launch:
+ *   embedding gather -> per layer [RMSNorm -> fused QKV GEMV -> RoPE ->
+ *   KV-cache append -> GQA attention over the cache -> O projection +
+ *   residual -> RMSNorm -> gate/up GEMV + SwiGLU -> down GEMV + residual]
+ *   -> final RMSNorm -> LM-head GEMV (-> optional greedy argmax).
+ *
+ * The operator chain is the one the pages name (cloud.baidu.com/article/
+ * 9434380 "low-latency single-request LLM inference: from operator fusion
+ * to runtime orchestration", section 三 and section 五 step 2, segments A,
+ * B and C); the single launch with an in-kernel weight-prefetch pipeline is
+ * that page's section 4.2 and section 五 step 3, and the MegaKernel tutorial
+ * at developer.baidu.com/article/detail.html?id=8006242, sections 4.1-4.2.
+ *
+ * Conventions for every entry point:
+ *   - Matrices are row-major [out][in] (the layout of a Linear layer weight).
+ *   - "device" pointers are HIP device allocations on the current device;
+ *     "host" pointers are ordinary host memory.
+ *   - Streams are passed as `void *` holding a hipStream_t (NULL = the null
+ *     stream; the pages advise always passing an explicit stream, page
+ *     www.stapisi.com/news/3904786 section 3.3).
+ *   - Every call returns an mk_status; nothing throws across the ABI.
+ *     Argument checks are done on the host before any device work is
+ *     enqueued ("defensive checks on input bounds", cloud.baidu.com/article/
+ *     9434380 section 九).
+ *   - Device-side failures (a grid-wait timeout) are asynchronous: they set
+ *     a device flag that mk_get_device_error reports, after which the handle
+ *     refuses further steps (MK_ERR_STATE).
+ */
+#ifndef MK_H
+#define MK_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MK_OK = 0,
+    MK_ERR_NULL = 1,    /* a required pointer argument is NULL */
+    MK_ERR_SHAPE = 2,   /* unsupported or inconsistent model shape */
+    MK_ERR_DTYPE = 3,   /* unsupported dtype */
+    MK_ERR_RANGE = 4,   /* token id, position or count out of range */
+    MK_ERR_NOMEM = 5,   /* device allocation failed */
+    MK_ERR_HIP = 6,     /* a HIP runtime call failed */
+    MK_ERR_DEVICE = 7,  /* the device reported a failure (grid-wait timeout) */
+    MK_ERR_STATE = 8,   /* the handle was disabled by an earlier device failure */
+    MK_ERR_TUNING = 9   /* a tuning value is out of its documented range */
+} mk_status;
+
+typedef enum { MK_F32 = 0, MK_BF16 = 1 } mk_dtype;
+
+/* Model shape.  Supported: n_heads % n_kv_heads == 0; head_dim * element
+   size equal to 128 or 256 bytes (bf16: head_dim 64 or 128; f32: 32 or 64);
+   hidden and ffn multiples of 8; max_seq >= 1.  rms_eps is added to the mean
+   square inside the square root; RoPE rotates pairs (i, i + head_dim/2) by
+   pos * rope_theta^(-2i/head_dim). */
+typedef struct {
+    int32_t n_layers, hidden, n_heads, n_kv_heads, head_dim, ffn, vocab, max_seq;
+    double rms_eps, rope_theta;
+    mk_dtype dtype;          /* weights and KV cache */
+    int32_t tied_embeddings; /* 1: the LM head is the embedding matrix */
+} mk_model_desc;
+
+/* Device pointers to one layer's weights in the model dtype:
+   attn_norm [H], wq [n_heads*head_dim][H], wk [n_kv*head_dim][H],
+   wv [n_kv*head_dim][H], wo [H][n_heads*head_dim], ffn_norm [H],
+   w_gate [F][H], w_up [F][H], w_down [H][F]. */
+typedef struct {
+    const void *attn_norm, *wq, *wk, *wv, *wo, *ffn_norm, *w_gate, *w_up, *w_down;
+} mk_layer_ptrs;
+
+/* embed [V][H], final_norm [H], lm_head [V][H] (ignored when tied);
+   layers is a HOST array of n_layers entries holding device pointers. */
+typedef struct {
+    const void *embed, *final_norm, *lm_head;
+    const mk_layer_ptrs *layers;
+} mk_weight_ptrs;
+
+/* Caller-owned contiguous KV cache, device memory in the model dtype, each of
+   K and V laid out [n_layers][n_kv_heads][max_seq][head_dim]. */
+typedef struct {
+    void *k, *v;
+    int32_t max_seq; /* must equal the model's max_seq */
+} mk_kv_cache;
+
+/* Tuning knobs.  Zero selects the default for every field.
+     grid:        workgroups of the persistent grid (default: CU count);
+     ring_slots:  16 KiB LDS ring slots per workgroup, 3..8 (default: as many
+                  as fit beside the activation buffer);
+     attn_splits: sequence splits per KV head (default: grid / n_kv_heads);
+     timeout_ms:  grid-wait timeout before the device error flag is raised
+                  (default 2000);
+     cooperative: 1 = cooperative launch (default), 2 = ordinary launch. */
+typedef struct {
+    int32_t grid, ring_slots, attn_splits, timeout_ms, cooperative;
+} mk_tuning;
+
+typedef struct mk_handle mk_handle;
+
+/* Read-only facts about a created handle (for benchmarks and tests). */
+typedef struct {
+    int32_t grid, ring_slots, attn_splits, block_threads, lds_bytes, cu_count;
+    int64_t packed_bytes;    /* library-owned pre-laid-out weight bytes */
+    int64_t weight_bytes;    /* algorithmic weight bytes read per step */
+} mk_info;
+
+/* Create a handle: validates the shape, copies every weight into a
+   library-owned buffer laid out in the kernel's access order (the weight
+   pre-layout of cloud.baidu.com/article/9434380 section 九), builds the RoPE
+   table, and allocates scratch.  The caller may free its weights after this
+   returns.  Synchronous.  tuning may be NULL.  On success *out receives the
+   handle; on failure *out is set to NULL. */
+mk_status mk_create(const mk_model_desc *desc, const mk_weight_ptrs *weights, const mk_tuning *tuning,
+                    mk_handle **out);
+
+/* One decode step for token_id at 0-based position pos: writes K/V of
+   position pos into the cache, reads cache positions [0, pos] (never
+   positions > pos) and writes vocab fp32 logits to logits_out (device).
+   Enqueued on `stream`; returns immediately.  Requires 0 <= token_id < vocab
+   and 0 <= pos < max_seq. */
+mk_status mk_decode_step(mk_handle *h, int32_t token_id, int32_t pos, const mk_kv_cache *kv,
+                         float *logits_out, void *stream);
+
+/* Same step with the token read from device memory (token_in, one int32) and
+   the greedy next token (argmax of the logits, lowest index on ties) written
+   to device memory (token_out, one int32).  Lets a caller enqueue many steps
+   back to back with no host round trip.  logits_out may be NULL.  A token id
+   outside [0, vocab) in token_in raises the device error flag. */
+mk_status mk_decode_step_device_token(mk_handle *h, const int32_t *token_in, int32_t pos, const mk_kv_cache *kv,
+                                      float *logits_out, int32_t *token_out, void *stream);
+
+/* Fill cache positions [start_pos, start_pos + n) from n host token ids: by
+   definition under causal attention this is n decode steps at those
+   positions with the LM head skipped.  Requires n >= 0 and
+   start_pos + n <= max_seq. */
+mk_status mk_prefill_kv(mk_handle *h, const int32_t *tokens, int32_t n, int32_t start_pos, const mk_kv_cache *kv,
+                        void *stream);
+
+/* Synchronizes the handle's last stream and reports a device failure flag:
+   MK_OK, or MK_ERR_DEVICE (after which the handle is disabled). */
+mk_status mk_get_device_error(mk_handle *h);
+
+mk_status mk_get_info(const mk_handle *h, mk_info *info);
+
+const char *mk_status_str(mk_status s);
+
+/* Frees everything the handle owns.  NULL is allowed. */
+void mk_destroy(mk_handle *h);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,149 @@
+"""GPU parity: the HIP megakernel through the C ABI vs the CPU oracle, on the
+same seeded inputs.  Bars: max|dlogit| <= 1e-4 for float32 weights, <= 2e-2
+for bfloat16 weights, and greedy (teacher-forced) agreement on every step."""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import synth
+
+pytestmark = pytest.mark.gpu
+
+SHAPE_KEYS = ("n_layers", "hidden", "n_heads", "n_kv_heads", "head_dim", "ffn", "vocab", "rms_eps", "rope_theta",
+              "dtype", "tied")
+
+
+def shape_of(cfg):
+    d = dataclasses.asdict(cfg)
+    return {k: d[k] for k in SHAPE_KEYS}
+
+
+def tol_of(cfg):
+    return 1e-4 if cfg.dtype == "f32" else 2e-2
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import oracle
+    import transformer_megakernel_persistent_amd as mkp
+    mkp.load_library()
+    return torch, oracle, mkp
+
+
+def to_host(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def put_kv_prefix(cfg, seed, n_pos, ref, kv):
+    """Same synthetic cache contents for positions [0, n_pos) on both sides."""
+    import torch
+    for l in range(cfg.n_layers):
+        for which, host, dev in (("k", ref.k, kv.k), ("v", ref.v, kv.v)):
+            a = synth.gen_kv_prefix(cfg, seed, n_pos, which, l)
+            host[l, :, :n_pos, :] = a
+            t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if a.dtype == np.uint16 else \
+                torch.from_numpy(a)
+            dev[l, :, :n_pos, :] = t.to(dev.device)
+
+
+def run_pair(env, cfg, seed, n_prompt, n_steps, gains="random", tuning=None, use_prefill=True, poison=True,
+             check_kv=True):
+    """Prefill (or synthetic cache) then teacher-forced greedy steps on both
+    sides; returns per-step max|dlogit| and the argmax agreement count."""
+    torch, oracle, mkp = env
+    print(f"[parity] {cfg.name} dtype={cfg.dtype} prompt={n_prompt} steps={n_steps} seed={seed} tuning={tuning}",
+          flush=True)
+    shape = shape_of(cfg)
+    max_seq = n_prompt + n_steps
+    host = synth.gen_weights(cfg, seed=seed, gains=gains)
+    ref = oracle.Model(shape, host, max_seq)
+    dev_w = mkp.upload_weights(host)
+    mk = mkp.MegaKernel(shape, dev_w, max_seq, tuning=tuning)
+    del dev_w
+    kv = mkp.KVCache(shape, max_seq, fill=float("nan") if poison else 0.0)
+    toks = synth.gen_tokens(seed, n_prompt + 1, cfg.vocab)
+    if use_prefill:
+        ref.prefill(toks[:n_prompt])
+        mk.prefill_kv(toks[:n_prompt], 0, kv)
+        torch.cuda.synchronize()
+        assert mk.device_error() == 0
+        if check_kv and n_prompt:
+            kt = to_host(kv.k)[:, :, :n_prompt].astype(np.float64) if cfg.dtype == "f32" else \
+                oracle.f64_array_from_bf16(to_host(kv.k)[:, :, :n_prompt])
+            kr = ref.k[:, :, :n_prompt].astype(np.float64) if cfg.dtype == "f32" else \
+                oracle.f64_array_from_bf16(ref.k[:, :, :n_prompt])
+            assert np.isfinite(kt).all()
+            kv_err = float(np.abs(kt - kr).max())
+            print(f"[parity] prefilled K max|d| = {kv_err:.3e}", flush=True)
+            assert kv_err <= (1e-4 if cfg.dtype == "f32" else 5e-2)
+    else:
+        put_kv_prefix(cfg, seed + 100, n_prompt, ref, kv)
+    logits = torch.empty(cfg.vocab, device="cuda")
+    errs, agree = [], 0
+    tok = int(toks[n_prompt])
+    for s in range(n_steps):
+        pos = n_prompt + s
+        want = ref.decode_step(tok, pos)
+        logits.fill_(float("nan"))
+        mk.decode_step(tok, pos, kv, logits)
+        torch.cuda.synchronize()
+        assert mk.device_error() == 0
+        got = logits.cpu().numpy().astype(np.float64)
+        assert np.isfinite(got).all()
+        errs.append(float(np.abs(got - want).max()))
+        nxt = oracle.argmax(want)
+        agree += int(int(np.argmax(got)) == nxt)
+        tok = nxt  # teacher forcing with the oracle's greedy token
+    print(f"[parity] max|dlogit| per step: {['%.2e' % e for e in errs]}  agree {agree}/{n_steps}", flush=True)
+    mk.close()
+    return errs, agree
+
+
+def test_tiny_fp32_prefill_and_greedy_decode(env):
+    cfg = synth.CONFIGS["tiny"]
+    errs, agree = run_pair(env, cfg, seed=1, n_prompt=cfg.context, n_steps=cfg.decode_steps)
+    assert max(errs) <= 1e-4
+    assert agree == cfg.decode_steps
+
+
+def test_tiny_bf16_gqa4_tied(env):
+    cfg = synth.CONFIGS["tiny"].with_(dtype="bf16", n_heads=8, n_kv_heads=2, head_dim=64, tied=True,
+                                      rope_theta=500000.0)
+    errs, agree = run_pair(env, cfg, seed=2, n_prompt=40, n_steps=8)
+    assert max(errs) <= 2e-2
+    assert agree == 8
+
+
+def test_first_position_with_poisoned_cache(env):
+    # pos = 0: attention over the single just-written position; the rest of
+    # the cache holds NaN and must never be read.
+    cfg = synth.CONFIGS["tiny"]
+    errs, agree = run_pair(env, cfg, seed=3, n_prompt=0, n_steps=3)
+    assert max(errs) <= 1e-4 and agree == 3
+
+
+@pytest.mark.parametrize("grid,splits,ring", [(64, 8, 3), (37, 5, 4), (256, 1, 8)])
+def test_tiny_other_launch_shapes(env, grid, splits, ring):
+    cfg = synth.CONFIGS["tiny"]
+    errs, agree = run_pair(env, cfg, seed=4, n_prompt=21, n_steps=3,
+                           tuning={"grid": grid, "attn_splits": splits, "ring_slots": ring})
+    assert max(errs) <= 1e-4 and agree == 3
+
+
+def test_llama1b_full_size_synthetic_context(env):
+    cfg = synth.CONFIGS["llama1b"]
+    errs, agree = run_pair(env, cfg, seed=5, n_prompt=cfg.context, n_steps=3, gains="ones", use_prefill=False)
+    assert max(errs) <= 2e-2 and agree == 3
+
+
+def test_llama1b_prefill_short_prompt(env):
+    cfg = synth.CONFIGS["llama1b"]
+    errs, agree = run_pair(env, cfg, seed=6, n_prompt=5, n_steps=2, gains="random")
+    assert max(errs) <= 2e-2 and agree == 2

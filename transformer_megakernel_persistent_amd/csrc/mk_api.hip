@@ -1,0 +1,369 @@
+// Host runtime of the C ABI declared in include/mk.h: argument validation,
+// work decomposition, weight pre-layout, scratch ownership and the one
+// launch per decode step.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <vector>
+
+#include "../../include/mk.h"
+#include "mk_internal.h"
+
+extern "C" int mk_kernel_max_blocks_per_cu(int dtype, int gq, int lpp, int lds);
+
+struct mk_handle {
+    mk_model_desc desc;
+    int eb = 0;
+    int device = 0;
+    int cu_count = 0;
+    int cooperative = 1;
+    MkParams base;  // launch-invariant kernel arguments
+    unsigned char *packed = nullptr;
+    int64_t packed_bytes = 0;
+    int64_t weight_bytes = 0;
+    int64_t *wg_off = nullptr;  // [ST_NUM][grid]
+    float *gains = nullptr;     // attn [L][H], ffn [L][H], final [H]
+    void *embed = nullptr;
+    float *rope = nullptr;
+    float *scratch = nullptr;   // x, q, o, a, partials
+    uint32_t *words = nullptr;  // head counters, progress words, error word, argmax counter
+    float *amax_val = nullptr;
+    int32_t *amax_idx = nullptr;
+    uint32_t epoch = 1;
+    bool disabled = false;
+    hipStream_t last_stream = nullptr;
+    int lds_bytes = 0;
+};
+
+namespace {
+
+mk_status hip_fail(hipError_t e) { return e == hipErrorOutOfMemory ? MK_ERR_NOMEM : MK_ERR_HIP; }
+
+#define HIP_TRY(expr)                              \
+    do {                                           \
+        hipError_t e_ = (expr);                    \
+        if (e_ != hipSuccess) return hip_fail(e_); \
+    } while (0)
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct StageShape {
+    int rows, k;
+};
+
+mk_status validate_desc(const mk_model_desc *d) {
+    if (d->dtype != MK_F32 && d->dtype != MK_BF16) return MK_ERR_DTYPE;
+    const int eb = d->dtype == MK_BF16 ? 2 : 4;
+    if (d->n_layers < 1 || d->hidden < 8 || d->n_heads < 1 || d->n_kv_heads < 1 || d->head_dim < 2 || d->ffn < 8 ||
+        d->vocab < 1 || d->max_seq < 1)
+        return MK_ERR_SHAPE;
+    if (d->hidden % 8 || d->ffn % 8 || d->n_heads % d->n_kv_heads) return MK_ERR_SHAPE;
+    const int gq = d->n_heads / d->n_kv_heads;
+    if (gq != 1 && gq != 2 && gq != 4 && gq != 8) return MK_ERR_SHAPE;
+    if (d->head_dim * eb != 128 && d->head_dim * eb != 256) return MK_ERR_SHAPE;
+    if (!(d->rms_eps >= 0.0) || !(d->rope_theta > 0.0)) return MK_ERR_SHAPE;
+    if ((int64_t)d->n_heads * d->head_dim > (1 << 20) || d->hidden > (1 << 20) || d->ffn > (1 << 22))
+        return MK_ERR_SHAPE;
+    return MK_OK;
+}
+
+}  // namespace
+
+extern "C" const char *mk_status_str(mk_status s) {
+    switch (s) {
+    case MK_OK: return "ok";
+    case MK_ERR_NULL: return "null pointer argument";
+    case MK_ERR_SHAPE: return "unsupported or inconsistent model shape";
+    case MK_ERR_DTYPE: return "unsupported dtype";
+    case MK_ERR_RANGE: return "token, position or count out of range";
+    case MK_ERR_NOMEM: return "device allocation failed";
+    case MK_ERR_HIP: return "HIP runtime error";
+    case MK_ERR_DEVICE: return "device reported a failure";
+    case MK_ERR_STATE: return "handle disabled by an earlier device failure";
+    case MK_ERR_TUNING: return "tuning value out of range";
+    }
+    return "unknown status";
+}
+
+extern "C" void mk_destroy(mk_handle *h) {
+    if (!h) return;
+    hipFree(h->packed);
+    hipFree(h->wg_off);
+    hipFree(h->gains);
+    hipFree(h->embed);
+    hipFree(h->rope);
+    hipFree(h->scratch);
+    hipFree(h->words);
+    hipFree(h->amax_val);
+    hipFree(h->amax_idx);
+    delete h;
+}
+
+static mk_status create_impl(const mk_model_desc *desc, const mk_weight_ptrs *wp, const mk_tuning *tun, mk_handle *h) {
+    const mk_model_desc &D = *desc;
+    const int L = D.n_layers, H = D.hidden, nh = D.n_heads, nkv = D.n_kv_heads, d = D.head_dim, F = D.ffn,
+              V = D.vocab;
+    const int dtype = D.dtype == MK_BF16 ? 1 : 0;
+    const int eb = dtype ? 2 : 4;
+    const int gq = nh / nkv;
+    const int lpp = d * eb / 16;
+    h->desc = D;
+    h->eb = eb;
+
+    HIP_TRY(hipGetDevice(&h->device));
+    hipDeviceProp_t prop;
+    HIP_TRY(hipGetDeviceProperties(&prop, h->device));
+    h->cu_count = prop.multiProcessorCount;
+    int wclk_khz = 0;
+    HIP_TRY(hipDeviceGetAttribute(&wclk_khz, hipDeviceAttributeWallClockRate, h->device));
+    if (wclk_khz <= 0) wclk_khz = 100000;
+
+    // tuning
+    mk_tuning t = {0, 0, 0, 0, 0};
+    if (tun) t = *tun;
+    if (t.grid < 0 || t.ring_slots < 0 || t.attn_splits < 0 || t.timeout_ms < 0 || t.cooperative < 0 ||
+        t.cooperative > 2)
+        return MK_ERR_TUNING;
+    if (t.ring_slots != 0 && (t.ring_slots < 3 || t.ring_slots > MK_MAX_RING)) return MK_ERR_TUNING;
+    const int grid = t.grid ? t.grid : h->cu_count;
+    const int splits = t.attn_splits ? t.attn_splits : (grid / nkv > 0 ? grid / nkv : 1);
+    if ((int64_t)splits * nkv > grid) return MK_ERR_TUNING;
+    h->cooperative = t.cooperative == 2 ? 0 : 1;
+    const int timeout_ms = t.timeout_ms ? t.timeout_ms : 2000;
+
+    // stage geometry
+    const StageShape shapes[ST_NUM] = {{(nh + 2 * nkv) * d, H}, {H, nh * d}, {2 * F, H}, {H, F}, {V, H}};
+    MkParams &P = h->base;
+    memset(&P, 0, sizeof P);
+    std::vector<int64_t> off_host((size_t)ST_NUM * grid);
+    int64_t total = 0;
+    int vec_floats = 0, out_rows = 0;
+    const int epc = MK_CHUNK_BYTES / eb;
+    for (int k = 0; k < ST_NUM; ++k) {
+        MkStage &s = P.st[k];
+        s.rows = shapes[k].rows;
+        s.k = shapes[k].k;
+        s.units = (int)ceil_div(s.rows, 4);
+        s.rbp = (int)ceil_div((int64_t)s.k * eb, MK_CHUNK_BYTES);
+        int64_t block = 0;
+        for (int w = 0; w < grid; ++w) {
+            const int u0 = (int)((int64_t)w * s.units / grid), u1 = (int)((int64_t)(w + 1) * s.units / grid);
+            off_host[(size_t)k * grid + w] = block;
+            block += ceil_div((int64_t)(u1 - u0) * s.rbp, 4) * MK_SLOT_BYTES;
+            if ((u1 - u0) * 4 > out_rows) out_rows = (u1 - u0) * 4;
+            if (k == ST_O && (u1 - u0) * 4 > 64) return MK_ERR_SHAPE;  // residual rows kept in LDS
+        }
+        if (s.rbp * epc > vec_floats) vec_floats = s.rbp * epc;
+        s.base = total;
+        s.layer_stride = k == ST_LM ? 0 : block;
+        total += k == ST_LM ? block : block * L;
+    }
+    const int fixed = mk_kernel_lds_bytes(0, vec_floats, out_rows, dtype, d, gq);
+    int ns = t.ring_slots ? t.ring_slots : (MK_LDS_LIMIT - fixed) / MK_SLOT_BYTES;
+    if (ns > MK_MAX_RING) ns = MK_MAX_RING;
+    if (ns < 3 || fixed + ns * MK_SLOT_BYTES > MK_LDS_LIMIT) return MK_ERR_SHAPE;
+    h->lds_bytes = mk_kernel_lds_bytes(ns, vec_floats, out_rows, dtype, d, gq);
+    const int per_cu = mk_kernel_max_blocks_per_cu(dtype, gq, lpp, h->lds_bytes);
+    if (per_cu < 1) return MK_ERR_SHAPE;
+    if (grid > per_cu * h->cu_count) return MK_ERR_TUNING;  // every workgroup must be resident
+
+    // allocations
+    h->packed_bytes = total;
+    HIP_TRY(hipMalloc(&h->packed, total > MK_SLOT_BYTES ? total : MK_SLOT_BYTES));  // the loaders' idle reads touch the first 8 KiB
+    HIP_TRY(hipMalloc(&h->wg_off, off_host.size() * sizeof(int64_t)));
+    HIP_TRY(hipMemcpy(h->wg_off, off_host.data(), off_host.size() * sizeof(int64_t), hipMemcpyHostToDevice));
+    const size_t ngain = (size_t)2 * L * H + H;
+    HIP_TRY(hipMalloc(&h->gains, ngain * sizeof(float)));
+    HIP_TRY(hipMalloc(&h->embed, (size_t)V * H * eb));
+    HIP_TRY(hipMalloc(&h->rope, (size_t)D.max_seq * d * sizeof(float)));
+    const size_t part_floats = (size_t)nkv * splits * gq * (d + 2);
+    const size_t nscratch = (size_t)H + 2 * (size_t)nh * d + F + part_floats;
+    HIP_TRY(hipMalloc(&h->scratch, nscratch * sizeof(float)));
+    HIP_TRY(hipMemset(h->scratch, 0, nscratch * sizeof(float)));
+    const size_t nwords = (size_t)nkv + grid + 2 + 64;
+    HIP_TRY(hipMalloc(&h->words, nwords * sizeof(uint32_t)));
+    HIP_TRY(hipMemset(h->words, 0, nwords * sizeof(uint32_t)));
+    HIP_TRY(hipMalloc(&h->amax_val, grid * sizeof(float)));
+    HIP_TRY(hipMalloc(&h->amax_idx, grid * sizeof(int32_t)));
+
+    // pre-layout, gains, embedding copy
+    for (int k = 0; k < ST_NUM; ++k) P.st[k].wg_off = h->wg_off + (size_t)k * grid;
+    for (int k = 0; k < ST_NUM; ++k) {
+        const int layers = k == ST_LM ? 1 : L;
+        for (int l = 0; l < layers; ++l) {
+            const mk_layer_ptrs &lw = wp->layers[k == ST_LM ? 0 : l];
+            const void *s0 = nullptr, *s1 = nullptr, *s2 = nullptr;
+            switch (k) {
+            case ST_QKV: s0 = lw.wq; s1 = lw.wk; s2 = lw.wv; break;
+            case ST_O: s0 = lw.wo; break;
+            case ST_GU: s0 = lw.w_gate; s1 = lw.w_up; break;
+            case ST_DOWN: s0 = lw.w_down; break;
+            default: s0 = D.tied_embeddings ? wp->embed : wp->lm_head; break;
+            }
+            int rc = mk_launch_prelayout_stage(h->packed + P.st[k].base + (int64_t)l * P.st[k].layer_stride, &P.st[k],
+                                               grid, k, dtype, s0, s1, s2, nh, nkv, d, nullptr);
+            if (rc) return MK_ERR_HIP;
+        }
+    }
+    for (int l = 0; l < L; ++l) {
+        if (mk_launch_to_f32(h->gains + (size_t)l * H, wp->layers[l].attn_norm, H, dtype, nullptr)) return MK_ERR_HIP;
+        if (mk_launch_to_f32(h->gains + (size_t)(L + l) * H, wp->layers[l].ffn_norm, H, dtype, nullptr))
+            return MK_ERR_HIP;
+    }
+    if (mk_launch_to_f32(h->gains + (size_t)2 * L * H, wp->final_norm, H, dtype, nullptr)) return MK_ERR_HIP;
+    HIP_TRY(hipMemcpy(h->embed, wp->embed, (size_t)V * H * eb, hipMemcpyDeviceToDevice));
+
+    // rotary table: angle pos * theta^(-2i/d), evaluated in double
+    {
+        std::vector<float> tab((size_t)D.max_seq * d);
+        for (int pos = 0; pos < D.max_seq; ++pos)
+            for (int i = 0; i < d / 2; ++i) {
+                const double ang = (double)pos * pow(D.rope_theta, -2.0 * (double)i / (double)d);
+                tab[((size_t)pos * (d / 2) + i) * 2] = (float)cos(ang);
+                tab[((size_t)pos * (d / 2) + i) * 2 + 1] = (float)sin(ang);
+            }
+        HIP_TRY(hipMemcpy(h->rope, tab.data(), tab.size() * sizeof(float), hipMemcpyHostToDevice));
+    }
+    HIP_TRY(hipDeviceSynchronize());
+
+    // launch-invariant kernel arguments
+    P.L = L; P.H = H; P.nh = nh; P.nkv = nkv; P.d = d; P.F = F; P.V = V; P.max_seq = D.max_seq;
+    P.eps = (float)D.rms_eps;
+    P.grid = grid; P.ring_slots = ns; P.splits = splits; P.lds_vec_floats = vec_floats; P.lds_out_rows = out_rows;
+    P.packed = h->packed;
+    P.g_attn = h->gains; P.g_ffn = h->gains + (size_t)L * H; P.g_final = h->gains + (size_t)2 * L * H;
+    P.embed = h->embed;
+    P.rope = h->rope;
+    P.x = h->scratch;
+    P.q = P.x + H;
+    P.o = P.q + (size_t)nh * d;
+    P.a = P.o + (size_t)nh * d;
+    P.part = P.a + F;
+    P.head_cnt = h->words;
+    P.flags = h->words + nkv;
+    P.err = P.flags + grid;
+    P.amax_cnt = P.err + 1;
+    P.amax_val = h->amax_val;
+    P.amax_idx = h->amax_idx;
+    P.timeout_ticks = (int64_t)timeout_ms * wclk_khz;
+
+    const int64_t per_layer = (int64_t)((nh + 2 * nkv) * d) * H + (int64_t)H * nh * d + 3LL * H * F + 2LL * H;
+    h->weight_bytes = ((int64_t)L * per_layer + (int64_t)V * H + 2LL * H) * eb;
+    return MK_OK;
+}
+
+extern "C" mk_status mk_create(const mk_model_desc *desc, const mk_weight_ptrs *weights, const mk_tuning *tuning,
+                               mk_handle **out) {
+    if (!out) return MK_ERR_NULL;
+    *out = nullptr;
+    if (!desc || !weights) return MK_ERR_NULL;
+    mk_status s = validate_desc(desc);
+    if (s != MK_OK) return s;
+    if (!weights->embed || !weights->final_norm || !weights->layers || (!desc->tied_embeddings && !weights->lm_head))
+        return MK_ERR_NULL;
+    for (int l = 0; l < desc->n_layers; ++l) {
+        const mk_layer_ptrs &lw = weights->layers[l];
+        if (!lw.attn_norm || !lw.wq || !lw.wk || !lw.wv || !lw.wo || !lw.ffn_norm || !lw.w_gate || !lw.w_up ||
+            !lw.w_down)
+            return MK_ERR_NULL;
+    }
+    mk_handle *h = new mk_handle();
+    s = create_impl(desc, weights, tuning, h);
+    if (s != MK_OK) {
+        mk_destroy(h);
+        return s;
+    }
+    *out = h;
+    return MK_OK;
+}
+
+static mk_status check_kv(const mk_handle *h, const mk_kv_cache *kv) {
+    if (!kv || !kv->k || !kv->v) return MK_ERR_NULL;
+    if (kv->max_seq != h->desc.max_seq) return MK_ERR_SHAPE;
+    return MK_OK;
+}
+
+static mk_status launch(mk_handle *h, const mk_kv_cache *kv, int32_t token, const int32_t *token_dev, int32_t pos,
+                        int want_logits, float *logits, int32_t *token_out, void *stream) {
+    MkParams p = h->base;
+    p.kc = kv->k;
+    p.vc = kv->v;
+    p.token = token;
+    p.token_dev = token_dev;
+    p.pos = pos;
+    p.want_logits = want_logits;
+    p.logits = logits;
+    p.token_out = token_out;
+    p.epoch_base = h->epoch;
+    h->epoch += (uint32_t)mk_points_per_launch(h->desc.n_layers);
+    h->last_stream = (hipStream_t)stream;
+    int rc = mk_launch_decode(&p, h->desc.dtype == MK_BF16 ? 1 : 0, h->cooperative, stream);
+    return rc ? MK_ERR_HIP : MK_OK;
+}
+
+extern "C" mk_status mk_decode_step(mk_handle *h, int32_t token_id, int32_t pos, const mk_kv_cache *kv,
+                                    float *logits_out, void *stream) {
+    if (!h || !logits_out) return MK_ERR_NULL;
+    if (h->disabled) return MK_ERR_STATE;
+    mk_status s = check_kv(h, kv);
+    if (s != MK_OK) return s;
+    if (token_id < 0 || token_id >= h->desc.vocab || pos < 0 || pos >= h->desc.max_seq) return MK_ERR_RANGE;
+    return launch(h, kv, token_id, nullptr, pos, 1, logits_out, nullptr, stream);
+}
+
+extern "C" mk_status mk_decode_step_device_token(mk_handle *h, const int32_t *token_in, int32_t pos,
+                                                 const mk_kv_cache *kv, float *logits_out, int32_t *token_out,
+                                                 void *stream) {
+    if (!h || !token_in || !token_out) return MK_ERR_NULL;
+    if (h->disabled) return MK_ERR_STATE;
+    mk_status s = check_kv(h, kv);
+    if (s != MK_OK) return s;
+    if (pos < 0 || pos >= h->desc.max_seq) return MK_ERR_RANGE;
+    return launch(h, kv, 0, token_in, pos, 1, logits_out, token_out, stream);
+}
+
+extern "C" mk_status mk_prefill_kv(mk_handle *h, const int32_t *tokens, int32_t n, int32_t start_pos,
+                                   const mk_kv_cache *kv, void *stream) {
+    if (!h) return MK_ERR_NULL;
+    if (h->disabled) return MK_ERR_STATE;
+    mk_status s = check_kv(h, kv);
+    if (s != MK_OK) return s;
+    if (n < 0 || start_pos < 0 || (int64_t)start_pos + n > h->desc.max_seq) return MK_ERR_RANGE;
+    if (n > 0 && !tokens) return MK_ERR_NULL;
+    for (int i = 0; i < n; ++i)
+        if (tokens[i] < 0 || tokens[i] >= h->desc.vocab) return MK_ERR_RANGE;
+    for (int i = 0; i < n; ++i) {
+        s = launch(h, kv, tokens[i], nullptr, start_pos + i, 0, nullptr, nullptr, stream);
+        if (s != MK_OK) return s;
+    }
+    return MK_OK;
+}
+
+extern "C" mk_status mk_get_device_error(mk_handle *h) {
+    if (!h) return MK_ERR_NULL;
+    HIP_TRY(hipStreamSynchronize(h->last_stream));
+    uint32_t err = 0;
+    HIP_TRY(hipMemcpy(&err, h->base.err, sizeof err, hipMemcpyDeviceToHost));
+    if (err) {
+        h->disabled = true;
+        return MK_ERR_DEVICE;
+    }
+    return h->disabled ? MK_ERR_STATE : MK_OK;
+}
+
+extern "C" mk_status mk_get_info(const mk_handle *h, mk_info *info) {
+    if (!h || !info) return MK_ERR_NULL;
+    info->grid = h->base.grid;
+    info->ring_slots = h->base.ring_slots;
+    info->attn_splits = h->base.splits;
+    info->block_threads = MK_BLOCK_THREADS;
+    info->lds_bytes = h->lds_bytes;
+    info->cu_count = h->cu_count;
+    info->packed_bytes = h->packed_bytes;
+    info->weight_bytes = h->weight_bytes;
+    return MK_OK;
+}

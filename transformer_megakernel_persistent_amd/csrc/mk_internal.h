@@ -1,0 +1,95 @@
+// Internal definitions shared by the host runtime and the device code.
+//
+// Work decomposition (one persistent workgroup per CU):
+//   - Every matrix-vector stage splits its output rows into "units" of four
+//     consecutive packed rows; unit u of a stage goes to workgroup
+//     w = the w with floor(w*U/G) <= u < floor((w+1)*U/G).  Inside a
+//     workgroup, local row i belongs to consumer wave i % 4.
+//   - A workgroup's weights for a stage are one contiguous block of 16 KiB
+//     "slots".  Slot n holds, for each consumer c, the next 4 KiB of c's rows
+//     (row-major, each row zero-padded to whole 1 KiB chunks).  Loader waves
+//     copy slots into an LDS ring with direct-to-LDS loads; consumer waves
+//     read their 4 KiB piece of the slot.
+//   - Attention splits each KV head's positions [0, pos) into `splits`
+//     contiguous ranges, one per workgroup; position pos (written in the same
+//     step) is folded in by the last split after the producers publish it.
+#pragma once
+#include <stdint.h>
+
+#define MK_SLOT_BYTES 16384
+#define MK_CHUNK_BYTES 1024
+#define MK_CHUNKS_PER_SLOT 16
+#define MK_NUM_LOADERS 2
+#define MK_NUM_CONSUMERS 4
+#define MK_BLOCK_THREADS (64 * (MK_NUM_LOADERS + MK_NUM_CONSUMERS))
+#define MK_MAX_RING 8
+#define MK_LDS_LIMIT 163840
+
+// Stage kinds with weights; the attention stage streams the KV cache.
+enum { ST_QKV = 0, ST_O = 1, ST_GU = 2, ST_DOWN = 3, ST_LM = 4, ST_NUM = 5 };
+
+struct MkStage {
+    int32_t units;        // total units (4 packed rows each)
+    int32_t rbp;          // packed row length in 1 KiB chunks
+    int32_t k;            // input length in elements
+    int32_t rows;         // logical packed rows (units*4 >= rows; the rest are zero)
+    int64_t base;         // byte offset of layer 0's block in the packed buffer
+    int64_t layer_stride; // bytes between consecutive layers' blocks
+    const int64_t *wg_off;   // [grid] byte offset of each workgroup's sub-block in a layer block
+};
+
+struct MkParams {
+    // model
+    int32_t L, H, nh, nkv, d, F, V, max_seq;
+    float eps;
+    // launch shape
+    int32_t grid, ring_slots, splits, lds_vec_floats, lds_out_rows;
+    // weights
+    const unsigned char *packed;
+    MkStage st[ST_NUM];
+    const float *g_attn;   // [L][H]
+    const float *g_ffn;    // [L][H]
+    const float *g_final;  // [H]
+    const void *embed;     // [V][H] in the model dtype
+    const float *rope;     // [max_seq][d/2][2] (cos, sin)
+    // KV cache (caller-owned)
+    void *kc, *vc;
+    // scratch
+    float *x, *q, *o, *a, *part;
+    uint32_t *head_cnt;    // [nkv]
+    uint32_t *flags;       // [grid] progress epochs
+    uint32_t *err;         // device error word
+    float *amax_val;       // [grid]
+    int32_t *amax_idx;     // [grid]
+    uint32_t *amax_cnt;    // one counter
+    // this call
+    int32_t token;
+    const int32_t *token_dev;
+    int32_t pos;
+    int32_t want_logits;
+    float *logits;
+    int32_t *token_out;
+    uint32_t epoch_base;
+    int64_t timeout_ticks; // wall-clock ticks (100 MHz) before a grid wait gives up
+};
+
+// Error codes written to the device error word.
+#define MK_DEVERR_TIMEOUT 1u
+#define MK_DEVERR_TOKEN 2u
+
+// Publish points per launch: 5 per layer + 1.
+static inline int mk_points_per_launch(int L) { return 5 * L + 1; }
+
+// Host-side launchers implemented in the .hip files.
+#ifdef __cplusplus
+extern "C" {
+#endif
+int mk_launch_decode(const MkParams *p, int dtype, int cooperative, void *stream);
+int mk_launch_prelayout_stage(unsigned char *dst, const MkStage *st, int grid, int kind, int dtype,
+                              const void *src0, const void *src1, const void *src2, int nh, int nkv, int d,
+                              void *stream);
+int mk_kernel_lds_bytes(int ring_slots, int vec_floats, int out_rows, int dtype, int d, int gq);
+int mk_launch_to_f32(float *dst, const void *src, int64_t n, int dtype, void *stream);
+#ifdef __cplusplus
+}
+#endif

@@ -1,0 +1,112 @@
+// Weight pre-layout: copies row-major [out][in] weights into the order the
+// decode kernel streams them, once, when a handle is created
+// (cloud.baidu.com/article/9434380 section 九: arrange weights in an
+// access-friendly order ahead of time instead of reordering at run time).
+//
+// Packed row order per stage (four consecutive packed rows form a "unit"):
+//   QKV : query heads, then key heads, then value heads.  Within a query or
+//         key head the rows are paired for rotary encoding: packed rows 2m and
+//         2m+1 are head dims m and m + head_dim/2, so a unit holds head dims
+//         {2e, 2e+1, 2e + d/2, 2e+1 + d/2}: two complete rotation pairs and
+//         two adjacent storage words of the cache row.  Value rows keep their
+//         natural order.
+//   GU  : gate row f and up row f interleaved (packed rows 2f, 2f+1), so a
+//         workgroup owns both halves of every SwiGLU product it emits.
+//   O, DOWN, LM: natural row order.
+// Within a workgroup's block, slot n holds for consumer c the 4 KiB of its row
+// stream at [4n, 4n+4) chunks; consumer c's rows are local rows c, c+4, ...
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mk_internal.h"
+
+namespace {
+
+// One 64-lane wave copies one 1 KiB chunk (16 bytes per lane).
+__global__ __launch_bounds__(256) void prelayout_kernel(unsigned char *dst_block, MkStage st, int grid, int kind,
+                                                        int eb, const unsigned char *src0, const unsigned char *src1,
+                                                        const unsigned char *src2, int nh, int nkv, int d) {
+    const int w = blockIdx.y;
+    const int U = st.units;
+    const int unit0 = (int)(((int64_t)w * U) / grid);
+    const int units = (int)(((int64_t)(w + 1) * U) / grid) - unit0;
+    const int nsl = (units * st.rbp + 3) / 4;
+    const int chunk = blockIdx.x * 4 + (threadIdx.x >> 6);  // chunk index within this workgroup's block
+    const int lane = threadIdx.x & 63;
+    if (chunk >= nsl * MK_CHUNKS_PER_SLOT) return;
+    const int slot = chunk / MK_CHUNKS_PER_SLOT, cc = chunk % MK_CHUNKS_PER_SLOT;
+    const int c = cc / 4, qi = cc % 4;
+    const int qq = slot * 4 + qi;          // position in consumer c's chunk stream
+    const int row_c = qq / st.rbp, kc = qq % st.rbp;
+    uint4 val = make_uint4(0, 0, 0, 0);
+    if (row_c < units) {
+        const int gr = (unit0 + row_c) * 4 + c;  // packed row
+        if (gr < st.rows) {
+            const unsigned char *src = nullptr;
+            int64_t srow = 0;
+            if (kind == ST_QKV) {
+                const int nq = nh * d, nk = nkv * d;
+                if (gr < nq + nk) {
+                    const int r = gr < nq ? gr : gr - nq;
+                    const int head = r / d, wi = r % d;
+                    srow = (int64_t)head * d + wi / 2 + (wi % 2) * (d / 2);
+                    src = gr < nq ? src0 : src1;
+                } else {
+                    srow = gr - nq - nk;
+                    src = src2;
+                }
+            } else if (kind == ST_GU) {
+                srow = gr / 2;
+                src = (gr % 2 == 0) ? src0 : src1;
+            } else {
+                srow = gr;
+                src = src0;
+            }
+            const int64_t row_bytes = (int64_t)st.k * eb;
+            const int64_t off = (int64_t)kc * MK_CHUNK_BYTES + lane * 16;
+            if (off + 16 <= row_bytes) {
+                val = *(const uint4 *)(src + srow * row_bytes + off);
+            } else if (off < row_bytes) {  // partial 16-byte piece at the row end
+                unsigned char tmp[16] = {0};
+                for (int b = 0; b < (int)(row_bytes - off); ++b) tmp[b] = src[srow * row_bytes + off + b];
+                val = *(const uint4 *)tmp;
+            }
+        }
+    }
+    *(uint4 *)(dst_block + st.wg_off[w] + (int64_t)chunk * MK_CHUNK_BYTES + lane * 16) = val;
+}
+
+__global__ void to_f32_kernel(float *dst, const void *src, int64_t n, int dtype) {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        if (dtype == 1) dst[i] = __uint_as_float((uint32_t)((const uint16_t *)src)[i] << 16);
+        else dst[i] = ((const float *)src)[i];
+    }
+}
+
+}  // namespace
+
+extern "C" int mk_launch_prelayout_stage(unsigned char *dst, const MkStage *st, int grid, int kind, int dtype,
+                                         const void *src0, const void *src1, const void *src2, int nh, int nkv,
+                                         int d, void *stream) {
+    // the largest per-workgroup slot count bounds the x-extent of the launch
+    int max_nsl = 0;
+    for (int w = 0; w < grid; ++w) {
+        const int U = st->units;
+        const int u0 = (int)(((int64_t)w * U) / grid), u1 = (int)(((int64_t)(w + 1) * U) / grid);
+        const int nsl = ((u1 - u0) * st->rbp + 3) / 4;
+        if (nsl > max_nsl) max_nsl = nsl;
+    }
+    if (max_nsl == 0) return 0;
+    dim3 g((max_nsl * MK_CHUNKS_PER_SLOT + 3) / 4, grid);
+    hipLaunchKernelGGL(prelayout_kernel, g, dim3(256), 0, (hipStream_t)stream, dst, *st, grid, kind, dtype ? 2 : 4,
+                       (const unsigned char *)src0, (const unsigned char *)src1, (const unsigned char *)src2, nh, nkv, d);
+    return (int)hipGetLastError();
+}
+
+extern "C" int mk_launch_to_f32(float *dst, const void *src, int64_t n, int dtype, void *stream) {
+    if (n <= 0) return 0;
+    int blocks = (int)((n + 255) / 256);
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(to_f32_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, dst, src, n, dtype);
+    return (int)hipGetLastError();
+}
