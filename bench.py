@@ -1,0 +1,220 @@
+"""Decode benchmark: batch-1 greedy decoding through the persistent megakernel.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config llama1b]
+
+A step is one decode step of the whole path (embedding -> all layers ->
+LM head -> greedy argmax), launched as ONE kernel through the C ABI
+(mk_decode_step_device_token): each launch reads the token the previous
+launch wrote, so the timed loop runs with no host round trip.  The default
+workload is the Llama-3.2-1B-shaped decoder with a 2048-token context and
+128 greedy steps; weights are seeded N(0, 0.02) bf16 (synthetic, random
+init) and the context is filled by mk_prefill_kv from seeded token ids.
+
+Prints ONE JSON line.  `value` is tokens/s over the timed steps (wall clock,
+inputs resident in HBM); `roofline` divides the algorithmic bytes of a step
+(every weight once + the K/V rows read at that position) by the average
+kernel duration measured with events on the launch stream; `cpu_baseline`
+times the CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import dataclasses
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
+SHAPE_KEYS = ("n_layers", "hidden", "n_heads", "n_kv_heads", "head_dim", "ffn", "vocab", "rms_eps", "rope_theta",
+              "dtype", "tied")
+KERNEL_SOURCES = ("transformer_megakernel_persistent_amd/csrc/mk_kernel.hip",
+                  "transformer_megakernel_persistent_amd/csrc/mk_prelayout.hip",
+                  "transformer_megakernel_persistent_amd/csrc/mk_internal.h")
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"counters_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_hash") != kernel_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def percentile(xs, q):
+    xs = sorted(xs)
+    if not xs:
+        return float("nan")
+    k = (len(xs) - 1) * q
+    lo, hi = int(k), min(int(k) + 1, len(xs) - 1)
+    return xs[lo] + (xs[hi] - xs[lo]) * (k - lo)
+
+
+def cpu_baseline(cfg, host_w, shape, budget_s: float):
+    """The oracle (plain float64 C) on this host: decode steps of the same
+    model at the same context length, from a synthetic cache, until the
+    time budget is used (at least one step)."""
+    import numpy as np
+
+    import oracle
+    import synth
+    ctx = cfg.context
+    ref = oracle.Model(shape, host_w, ctx + 64)
+    for l in range(cfg.n_layers):
+        ref.k[l, :, :ctx] = synth.gen_kv_prefix(cfg, 7, ctx, "k", l)
+        ref.v[l, :, :ctx] = synth.gen_kv_prefix(cfg, 7, ctx, "v", l)
+    tok, n, t0 = 1, 0, time.perf_counter()
+    while True:
+        lg = ref.decode_step(tok, ctx + n)
+        tok = int(np.argmax(lg))
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= 64:
+            break
+    return {"value": n / el, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{n} greedy decode steps of the same model from a synthetic {ctx}-token cache "
+                      f"(positions {ctx}..{ctx + n - 1}), {el:.1f} s, float64"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="llama1b")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--grid", type=int, default=0)
+    ap.add_argument("--ring", type=int, default=0)
+    ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--seed", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the multi-GPU tensor-parallel design is described but not built).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import transformer_megakernel_persistent_amd as mkp
+
+    cfg = synth.CONFIGS[args.config]
+    steps = args.steps if args.steps is not None else cfg.decode_steps
+    warm = args.warmup
+    shape = {k: v for k, v in dataclasses.asdict(cfg).items() if k in SHAPE_KEYS}
+    ctx = cfg.context
+    max_seq = ctx + warm + steps
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    t = time.perf_counter()
+    host_w = synth.gen_weights(cfg, seed=args.seed)
+    print(f"[bench] {cfg.name}: weights generated in {time.perf_counter() - t:.1f}s", file=sys.stderr, flush=True)
+    dev_w = mkp.upload_weights(host_w, dev)
+    tuning = {"grid": args.grid, "ring_slots": args.ring, "attn_splits": args.splits}
+    mk = mkp.MegaKernel(shape, dev_w, max_seq, tuning=tuning)
+    del dev_w
+    torch.cuda.empty_cache()
+    info = mk.info()
+    kv = mkp.KVCache(shape, max_seq, dev)
+    prompt = synth.gen_tokens(args.seed, ctx + 1, cfg.vocab)
+    t = time.perf_counter()
+    mk.prefill_kv(prompt[:ctx], 0, kv)
+    torch.cuda.synchronize()
+    print(f"[bench] prefill of {ctx} positions: {time.perf_counter() - t:.2f}s", file=sys.stderr, flush=True)
+    if mk.device_error() != 0:
+        raise RuntimeError("device error during prefill")
+
+    stream = torch.cuda.current_stream()
+    tok = torch.tensor([int(prompt[ctx])], dtype=torch.int32, device=dev)
+    toks_out = torch.empty(warm + steps, dtype=torch.int32, device=dev)
+    logits = torch.empty(cfg.vocab, dtype=torch.float32, device=dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+
+    pos = ctx
+    for i in range(warm):
+        mk.decode_step_device_token(tok if i == 0 else toks_out[i - 1:i], pos, kv, logits, toks_out[i:i + 1], stream)
+        pos += 1
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(steps):
+        src = toks_out[warm + i - 1:warm + i] if warm + i > 0 else tok
+        mk.decode_step_device_token(src, pos + i, kv, logits, toks_out[warm + i:warm + i + 1], stream)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if mk.device_error() != 0:
+        raise RuntimeError("device error during the timed steps")
+
+    step_us = [ev[i].elapsed_time(ev[i + 1]) * 1000.0 for i in range(steps)]
+    p50, p99 = percentile(step_us, 0.5), percentile(step_us, 0.99)
+    mean_us = sum(step_us) / len(step_us)
+    bytes_per_step = [cfg.step_bytes(pos + i) for i in range(steps)]
+    mean_bytes = sum(bytes_per_step) / len(bytes_per_step)
+    achieved = mean_bytes / (mean_us * 1e-6) / 1e9
+    gbs_p50 = cfg.step_bytes(pos + steps // 2) / (p50 * 1e-6) / 1e9
+    traffic = traffic_from_profile(cfg.name)
+    tokens = toks_out[warm:].cpu().numpy()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, host_w, shape, args.cpu_budget)
+
+    out = {
+        "metric": "batch-1 decode tokens/s (us/token p50/P99) + achieved HBM GB/s vs peak",
+        "value": steps / wall,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warm,
+        "ms_per_step": wall * 1000.0 / steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic: seeded N(0,0.02) random-init weights, uniform random prompt tokens, greedy decode",
+        "config": {
+            "workload": f"{cfg.name}: {cfg.n_layers}L hidden {cfg.hidden}, {cfg.n_heads}q/{cfg.n_kv_heads}kv heads x "
+                        f"{cfg.head_dim}, SwiGLU {cfg.ffn}, vocab {cfg.vocab}{' tied' if cfg.tied else ''}, "
+                        f"{cfg.dtype} weights+KV, fp32 accumulate; {ctx}-token context, {steps} greedy steps, batch 1",
+            "context": ctx, "global_batch": 1, "decode_positions": [pos, pos + steps - 1],
+            "launches_per_token": 1, "grid": info["grid"], "ring_slots": info["ring_slots"],
+            "attn_splits": info["attn_splits"], "block_threads": info["block_threads"],
+            "lds_bytes": info["lds_bytes"], "parallelism": "single GPU"},
+        "us_per_token_p50": p50,
+        "us_per_token_p99": p99,
+        "us_per_token_mean": mean_us,
+        "gbs_p50": gbs_p50,
+        "bytes_per_step": mean_bytes,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic},
+        "cpu_baseline": cpu,
+        "kernel_hash": kernel_hash(),
+        "first_tokens": [int(x) for x in tokens[:8]],
+    }
+    print(json.dumps(out), flush=True)
+    mk.close()
+
+
+if __name__ == "__main__":
+    main()

@@ -95,9 +95,11 @@ typedef struct {
      attn_splits: sequence splits per KV head (default: grid / n_kv_heads);
      timeout_ms:  grid-wait timeout before the device error flag is raised
                   (default 2000);
-     cooperative: 1 = cooperative launch (default), 2 = ordinary launch. */
+     cooperative: 1 = cooperative launch (default), 2 = ordinary launch;
+     trace:       1 = record a per-workgroup stage timeline on every step
+                  (read it with mk_read_trace; default 0 = off). */
 typedef struct {
-    int32_t grid, ring_slots, attn_splits, timeout_ms, cooperative;
+    int32_t grid, ring_slots, attn_splits, timeout_ms, cooperative, trace;
 } mk_tuning;
 
 typedef struct mk_handle mk_handle;
@@ -146,6 +148,17 @@ mk_status mk_prefill_kv(mk_handle *h, const int32_t *tokens, int32_t n, int32_t 
 mk_status mk_get_device_error(mk_handle *h);
 
 mk_status mk_get_info(const mk_handle *h, mk_info *info);
+
+/* Stage timeline of the most recent step (handles created with trace = 1):
+   synchronizes the last stream, then copies grid * (5*n_layers + 2) * 4
+   uint64 wall-clock ticks (100 MHz on MI355X) into host_out, laid out
+   [workgroup][boundary][event].  Boundary 5l+k is the start of stage k of
+   layer l (k: 0 QKV, 1 attention, 2 O, 3 gate/up, 4 down), 5L the LM head,
+   5L+1 the end of the step.  Events: 0 boundary reached (all of the previous
+   stage consumed), 1 previous stage finished and published, 2 inputs of the
+   next stage available (dependency wait over), 3 inputs loaded.  Unrecorded
+   entries are 0.  capacity is the number of uint64 host_out can hold. */
+mk_status mk_read_trace(mk_handle *h, uint64_t *host_out, int64_t capacity);
 
 const char *mk_status_str(mk_status s);
 

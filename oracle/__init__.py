@@ -63,6 +63,7 @@ def _load():
             "or_argmax": ([v, i32], i32),
             "or_decode_step": ([ctypes.POINTER(_Model), v, v, v, i32, i32, v], i32),
             "or_prefill": ([ctypes.POINTER(_Model), v, v, v, v, i32, i32], i32),
+            "or_num_threads": ([], i32),
         }
         for name, (args, res) in sig.items():
             f = getattr(lib, name)
@@ -154,6 +155,11 @@ def attend(q, K: np.ndarray, V: np.ndarray) -> np.ndarray:
 
 def silu(z: float) -> float:
     return float(_load().or_silu(float(z)))
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's row loops use."""
+    return int(_load().or_num_threads())
 
 
 def argmax(v) -> int:

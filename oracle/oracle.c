@@ -276,3 +276,11 @@ int or_prefill(const or_model *m, const void *const *w, void *kc, void *vc, cons
     }
     return 0;
 }
+
+/* Threads the OpenMP row loops use (reported by the CPU-baseline timing). */
+#ifdef _OPENMP
+#include <omp.h>
+int or_num_threads(void) { return omp_get_max_threads(); }
+#else
+int or_num_threads(void) { return 1; }
+#endif

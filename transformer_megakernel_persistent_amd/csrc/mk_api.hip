@@ -33,6 +33,8 @@ struct mk_handle {
     uint32_t *words = nullptr;  // head counters, progress words, error word, argmax counter
     float *amax_val = nullptr;
     int32_t *amax_idx = nullptr;
+    uint64_t *trace = nullptr;
+    int64_t trace_len = 0;
     uint32_t epoch = 1;
     bool disabled = false;
     hipStream_t last_stream = nullptr;
@@ -100,6 +102,7 @@ extern "C" void mk_destroy(mk_handle *h) {
     hipFree(h->words);
     hipFree(h->amax_val);
     hipFree(h->amax_idx);
+    hipFree(h->trace);
     delete h;
 }
 
@@ -123,10 +126,10 @@ static mk_status create_impl(const mk_model_desc *desc, const mk_weight_ptrs *wp
     if (wclk_khz <= 0) wclk_khz = 100000;
 
     // tuning
-    mk_tuning t = {0, 0, 0, 0, 0};
+    mk_tuning t = {0, 0, 0, 0, 0, 0};
     if (tun) t = *tun;
     if (t.grid < 0 || t.ring_slots < 0 || t.attn_splits < 0 || t.timeout_ms < 0 || t.cooperative < 0 ||
-        t.cooperative > 2)
+        t.cooperative > 2 || t.trace < 0 || t.trace > 1)
         return MK_ERR_TUNING;
     if (t.ring_slots != 0 && (t.ring_slots < 3 || t.ring_slots > MK_MAX_RING)) return MK_ERR_TUNING;
     const int grid = t.grid ? t.grid : h->cu_count;
@@ -162,6 +165,7 @@ static mk_status create_impl(const mk_model_desc *desc, const mk_weight_ptrs *wp
         s.layer_stride = k == ST_LM ? 0 : block;
         total += k == ST_LM ? block : block * L;
     }
+    if (out_rows < splits) out_rows = splits;  // the attention combine keeps split weights there
     const int fixed = mk_kernel_lds_bytes(0, vec_floats, out_rows, dtype, d, gq);
     int ns = t.ring_slots ? t.ring_slots : (MK_LDS_LIMIT - fixed) / MK_SLOT_BYTES;
     if (ns > MK_MAX_RING) ns = MK_MAX_RING;
@@ -180,7 +184,7 @@ static mk_status create_impl(const mk_model_desc *desc, const mk_weight_ptrs *wp
     HIP_TRY(hipMalloc(&h->gains, ngain * sizeof(float)));
     HIP_TRY(hipMalloc(&h->embed, (size_t)V * H * eb));
     HIP_TRY(hipMalloc(&h->rope, (size_t)D.max_seq * d * sizeof(float)));
-    const size_t part_floats = (size_t)nkv * splits * gq * (d + 2);
+    const size_t part_floats = (size_t)nkv * splits * gq * (d + 4);
     const size_t nscratch = (size_t)H + 2 * (size_t)nh * d + F + part_floats;
     HIP_TRY(hipMalloc(&h->scratch, nscratch * sizeof(float)));
     HIP_TRY(hipMemset(h->scratch, 0, nscratch * sizeof(float)));
@@ -189,6 +193,11 @@ static mk_status create_impl(const mk_model_desc *desc, const mk_weight_ptrs *wp
     HIP_TRY(hipMemset(h->words, 0, nwords * sizeof(uint32_t)));
     HIP_TRY(hipMalloc(&h->amax_val, grid * sizeof(float)));
     HIP_TRY(hipMalloc(&h->amax_idx, grid * sizeof(int32_t)));
+    if (t.trace) {
+        h->trace_len = (int64_t)grid * (5 * L + 2) * 4 + (int64_t)grid * 64 * 2;
+        HIP_TRY(hipMalloc(&h->trace, h->trace_len * sizeof(uint64_t)));
+        HIP_TRY(hipMemset(h->trace, 0, h->trace_len * sizeof(uint64_t)));
+    }
 
     // pre-layout, gains, embedding copy
     for (int k = 0; k < ST_NUM; ++k) P.st[k].wg_off = h->wg_off + (size_t)k * grid;
@@ -250,6 +259,7 @@ static mk_status create_impl(const mk_model_desc *desc, const mk_weight_ptrs *wp
     P.amax_val = h->amax_val;
     P.amax_idx = h->amax_idx;
     P.timeout_ticks = (int64_t)timeout_ms * wclk_khz;
+    P.trace = h->trace;
 
     const int64_t per_layer = (int64_t)((nh + 2 * nkv) * d) * H + (int64_t)H * nh * d + 3LL * H * F + 2LL * H;
     h->weight_bytes = ((int64_t)L * per_layer + (int64_t)V * H + 2LL * H) * eb;
@@ -353,6 +363,14 @@ extern "C" mk_status mk_get_device_error(mk_handle *h) {
         return MK_ERR_DEVICE;
     }
     return h->disabled ? MK_ERR_STATE : MK_OK;
+}
+
+extern "C" mk_status mk_read_trace(mk_handle *h, uint64_t *host_out, int64_t capacity) {
+    if (!h || !host_out) return MK_ERR_NULL;
+    if (!h->trace || capacity < h->trace_len) return MK_ERR_RANGE;
+    HIP_TRY(hipStreamSynchronize(h->last_stream));
+    HIP_TRY(hipMemcpy(host_out, h->trace, h->trace_len * sizeof(uint64_t), hipMemcpyDeviceToHost));
+    return MK_OK;
 }
 
 extern "C" mk_status mk_get_info(const mk_handle *h, mk_info *info) {

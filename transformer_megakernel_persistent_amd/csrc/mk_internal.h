@@ -71,6 +71,7 @@ struct MkParams {
     int32_t *token_out;
     uint32_t epoch_base;
     int64_t timeout_ticks; // wall-clock ticks (100 MHz) before a grid wait gives up
+    uint64_t *trace;       // optional [grid][5L+2][4] stage timeline, or null
 };
 
 // Error codes written to the device error word.

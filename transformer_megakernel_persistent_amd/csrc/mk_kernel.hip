@@ -37,6 +37,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "mk_internal.h"
 
 namespace {
@@ -66,6 +68,20 @@ __device__ __forceinline__ void stcu(uint32_t *p, uint32_t v) {
 }
 __device__ __forceinline__ void stci(int32_t *p, int32_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Buffer resources: out-of-range offsets read as zero.  aux bit 4 = sc1
+// (device scope) on gfx950, so these loads observe other workgroups' sc1
+// stores without an L2 invalidate.
+#define MK_SC1 16
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ u4v ld16c(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, MK_SC1);
+}
+__device__ __forceinline__ f4v as_f4(u4v v) {
+    return f4v{__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w)};
 }
 
 // s_waitcnt encoding (gfx9): vmcnt in [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].
@@ -109,23 +125,47 @@ __device__ __forceinline__ float group_sum(float v) {
     if (LPP == 16) v += dpp<0x140>(v);
     return v;
 }
-// Sum / max across the groups: lanes with equal (lane % LPP).
-template <int LPP>
+// Sum / max across the groups of size GS (8, 16 or 32): lanes with equal
+// (lane % GS).  VALU only: DPP row_ror:8 pairs lanes i and i^8 inside a row,
+// and the gfx950 permlane16/32 swaps hand each lane its i^16 / i^32 partner;
+// the sum of the two swapped registers is the pair sum in both lanes.
+__device__ __forceinline__ float pair16_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair32_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair16_max(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair32_max(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+template <int GS>
 __device__ __forceinline__ float xgroup_sum(float v) {
-#pragma unroll
-    for (int m = LPP; m < 64; m <<= 1) v += __shfl_xor(v, m);
-    return v;
+    if (GS <= 8) v += dpp<0x128>(v);  // row_ror:8
+    if (GS <= 16) v = pair16_sum(v);
+    return pair32_sum(v);
 }
-template <int LPP>
+template <int GS>
 __device__ __forceinline__ float xgroup_max(float v) {
-#pragma unroll
-    for (int m = LPP; m < 64; m <<= 1) v = fmaxf(v, __shfl_xor(v, m));
-    return v;
+    if (GS <= 8) v = fmaxf(v, dpp<0x128>(v));
+    if (GS <= 16) v = pair16_max(v);
+    return pair32_max(v);
 }
+// Max over all 64 lanes, result in every lane.
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) v = fmaxf(v, __shfl_xor(v, m));
-    return v;
+    v = fmaxf(v, dpp<0xB1>(v));
+    v = fmaxf(v, dpp<0x4E>(v));
+    v = fmaxf(v, dpp<0x141>(v));
+    v = fmaxf(v, dpp<0x140>(v));
+    v = fmaxf(v, dpp<0x128>(v));  // every lane of a row now holds the row max
+    v = pair16_max(v);
+    return pair32_max(v);
 }
 
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -164,6 +204,26 @@ __device__ __forceinline__ float piece_dot(const LDS unsigned char *wp, const LD
         a = fmaf(w.z, h.z, a);
         a = fmaf(w.w, h.w, a);
         return a;
+    }
+}
+
+// Same with the input elements already in registers.
+template <int DT>
+__device__ __forceinline__ float piece_dot_reg(const LDS unsigned char *wp, const float (&h)[16 / (DT ? 2 : 4)]) {
+    if constexpr (DT == 1) {
+        const u4v w = *(const LDS u4v *)wp;
+        float a = bf_lo(w.x) * h[0];
+        float b = bf_hi(w.x) * h[1];
+        a = fmaf(bf_lo(w.y), h[2], a);
+        b = fmaf(bf_hi(w.y), h[3], b);
+        a = fmaf(bf_lo(w.z), h[4], a);
+        b = fmaf(bf_hi(w.z), h[5], b);
+        a = fmaf(bf_lo(w.w), h[6], a);
+        b = fmaf(bf_hi(w.w), h[7], b);
+        return a + b;
+    } else {
+        const f4v w = *(const LDS f4v *)wp;
+        return fmaf(w.x, h[0], w.y * h[1]) + fmaf(w.z, h[2], w.w * h[3]);
     }
 }
 
@@ -217,7 +277,9 @@ __device__ __forceinline__ int st_of_kind(int kind) {
 
 }  // namespace
 
-template <int DT, int GQ, int LPP>
+// LOGITS = false is the cache-append variant used by prefill: the same step
+// without the final norm, LM head and argmax.
+template <int DT, int GQ, int LPP, bool LOGITS>
 __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const MkParams p) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_[];
     LDS unsigned char *smem = (LDS unsigned char *)smem_;
@@ -226,10 +288,11 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
     constexpr int EPC = MK_CHUNK_BYTES / EB;  // elements per 1 KiB chunk
     constexpr int PPC = 64 / LPP;           // cache positions per 1 KiB chunk
     constexpr int BP = 8 * PPC;             // positions per KV slot (8 K chunks + 8 V chunks)
+    constexpr int DH = LPP * 16 / EB;       // head dim
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int w = blockIdx.x, G = p.grid, NS = p.ring_slots, L = p.L;
-    const int d = p.d;
+    constexpr int d = DH;
 
     // LDS layout: ring | vec | out | cstate | xown | ss | control
     LDS unsigned char *ring = smem;
@@ -238,7 +301,8 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
     LDS float *cst = outv + p.lds_out_rows;
     LDS float *xown = cst + MK_NUM_CONSUMERS * GQ * (d + 2);
     LDS float *ssp = xown + 64;
-    volatile LDS int *ctl = (volatile LDS int *)(ssp + MK_NUM_CONSUMERS);  // [0] go step, [1] abort
+    volatile LDS int *ctl = (volatile LDS int *)(ssp + MK_NUM_CONSUMERS);  // [0] go step, [1] abort step,
+    // [2] combine-job step, [3] this workgroup combines, [4..7] per-consumer combine done
 
     Geo g;
     make_geo(p, w, g);
@@ -269,7 +333,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
         }
     };
 
-    if (tid == 0) { ctl[0] = -1; ctl[1] = 0; }
+    if (tid == 0) { ctl[0] = -1; ctl[1] = 0; ctl[2] = -1; ctl[3] = 0; ctl[4] = ctl[5] = ctl[6] = ctl[7] = -1; }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
@@ -294,7 +358,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
                 if (it_k == 5) { done = true; break; }
                 if (++it_k == 5) {
                     if (++it_l == L) {
-                        if (p.want_logits) it_k = 5; else done = true;
+                        if (LOGITS) it_k = 5; else done = true;
                     } else {
                         it_k = 0;
                     }
@@ -378,7 +442,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
                 ok = vstep();
                 for (int n = 0; n < nslots(kind) && ok; ++n) ok = dstep();
             }
-        if (ok && p.want_logits) {
+        if (ok && LOGITS) {
             ok = vstep();
             for (int n = 0; n < nsl_lm && ok; ++n) ok = dstep();
         }
@@ -388,25 +452,26 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
     }
 
     // ============================== consumers ==============================
+    // Each stage is a block: its per-lane register state (the input slice of
+    // a GEMV, the attention accumulators) is declared inside the block, so
+    // its registers are free again for the next stage.
     const int c = wave - MK_NUM_LOADERS;        // consumer index 0..3
     const int ct = tid - MK_NUM_LOADERS * 64;   // consumer thread 0..255
     int j = 0;      // next ring slot
-    int step = 0;   // step counter (for the consumer-local go flag)
+    int step = 0;   // barriers passed (also the consumer-local go-flag value)
     bool ok = true;
 
-    auto barrier = [&]() -> bool {
+    auto barrier = [&]() {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
         ++step;
-        return true;
     };
 
     // Progress publication (consumer 0, after its stores completed).
     auto publish = [&](int k) {
-        MK_WAIT_VM0();
+        MK_WAIT_VM0();  // every store of the stage is visible before the progress word
         if (lane == 0) stcu(p.flags + w, p.epoch_base + (uint32_t)k);
-        MK_WAIT_VM0();
     };
     // Wait until every workgroup published point k.  Consumer 0 polls; the
     // other consumers wait for its go signal in LDS.  Returns false on abort.
@@ -415,9 +480,20 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
             const uint32_t target = p.epoch_base + (uint32_t)k;
             const int64_t t_start = wall_clock64();
             bool good = true;
+            const __amdgpu_buffer_rsrc_t rf = rsrc(p.flags, (uint32_t)G * 4u);
             while (true) {
                 bool mine = true;
-                for (int i = lane; i < G; i += 64) mine &= (int32_t)(ldcu(p.flags + i) - target) >= 0;
+                u4v fv[4];
+#pragma unroll
+                for (int k4 = 0; k4 < 4; ++k4) fv[k4] = ld16c(rf, (uint32_t)(lane + 64 * k4) * 16u);
+#pragma unroll
+                for (int k4 = 0; k4 < 4; ++k4) {
+                    const int i0 = (lane + 64 * k4) * 4;
+                    mine &= i0 + 0 >= G || (int32_t)(fv[k4].x - target) >= 0;
+                    mine &= i0 + 1 >= G || (int32_t)(fv[k4].y - target) >= 0;
+                    mine &= i0 + 2 >= G || (int32_t)(fv[k4].z - target) >= 0;
+                    mine &= i0 + 3 >= G || (int32_t)(fv[k4].w - target) >= 0;
+                }
                 if (__all(mine)) break;
                 if (ldcu(p.err) != 0u || wall_clock64() - t_start > p.timeout_ticks) {
                     if (lane == 0) stcu(p.err, ldcu(p.err) | MK_DEVERR_TIMEOUT);
@@ -438,145 +514,300 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
         return ctl[1] == 0;
     };
 
-    // ---- input-vector loaders (all consumers) ----
-    // vec[0..n) = gain (.) x (sc1 loads of x, or the embedding row), zero pad to
-    // `pad`, and per-consumer sums of squares of x into ssp[c].
+    // ---- optional stage timeline (consumer 0, lane 0) ----
+    const int nbound = 5 * L + 2;
+    auto stamp = [&](int b, int e) {
+        if (p.trace && c == 0 && lane == 0) p.trace[((size_t)w * nbound + b) * 4 + e] = wall_clock64();
+    };
+    // Data steps of layer 1 (steady state): barrier passed / compute done.
+    int dstep_l1 = 0;
+    auto stamp_step = [&](int l, int e) {
+        if (p.trace && l == 1 && c == 0 && lane == 0 && dstep_l1 < 64)
+            p.trace[(size_t)G * nbound * 4 + ((size_t)w * 64 + dstep_l1) * 2 + e] = wall_clock64();
+        if (e == 1 && l == 1) ++dstep_l1;
+    };
+
+    // ---- input vectors ----
+    // LDS path: vec[0..n) = gain (.) x, zero padded to `pad`, with per-consumer
+    // sums of squares of x in ssp[c].  x is read with 16-byte device-scope
+    // loads (or, for layer 0, from the embedding row), eight per lane before
+    // any is used, so a call costs ceil(n/8192) memory round trips.
     auto load_normed = [&](const float *xsrc, const void *erow, const float *gain, int n, int pad) {
+        const int nqd = n / 4;
+        const __amdgpu_buffer_rsrc_t rx = rsrc(xsrc ? (const void *)xsrc : erow, (uint32_t)n * (xsrc ? 4u : (uint32_t)EB));
         float ss = 0.f;
-        for (int i = ct; i < n / 2; i += 256) {
-            float x0, x1;
-            if (erow) {
-                if constexpr (DT == 1) {
-                    uint32_t wv = ((const uint32_t *)erow)[i];
-                    x0 = bf_lo(wv); x1 = bf_hi(wv);
+        for (int base = ct; base < nqd; base += 256 * 8) {
+            f4v xv[8], gv[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int qi = base + u * 256;
+                if (xsrc) {
+                    xv[u] = as_f4(ld16c(rx, (uint32_t)qi * 16u));
+                } else if constexpr (DT == 1) {
+                    const uint64_t e = qi < nqd ? ((const uint64_t *)erow)[qi] : 0ull;
+                    xv[u] = f4v{bf_lo((uint32_t)e), bf_hi((uint32_t)e), bf_lo((uint32_t)(e >> 32)), bf_hi((uint32_t)(e >> 32))};
                 } else {
-                    x0 = ((const float *)erow)[2 * i]; x1 = ((const float *)erow)[2 * i + 1];
+                    xv[u] = qi < nqd ? ((const f4v *)erow)[qi] : f4v{0.f, 0.f, 0.f, 0.f};
                 }
-            } else {
-                uint64_t v = ldc64(xsrc + 2 * i);
-                x0 = __uint_as_float((uint32_t)v); x1 = __uint_as_float((uint32_t)(v >> 32));
+                gv[u] = qi < nqd ? ((const f4v *)gain)[qi] : f4v{0.f, 0.f, 0.f, 0.f};
             }
-            ss = fmaf(x0, x0, ss);
-            ss = fmaf(x1, x1, ss);
-            vec[2 * i] = gain[2 * i] * x0;
-            vec[2 * i + 1] = gain[2 * i + 1] * x1;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int qi = base + u * 256;
+                if (qi < nqd) {
+                    const f4v x = xv[u];
+                    ss = fmaf(x.x, x.x, ss);
+                    ss = fmaf(x.y, x.y, ss);
+                    ss = fmaf(x.z, x.z, ss);
+                    ss = fmaf(x.w, x.w, ss);
+                    *(LDS f4v *)(vec + 4 * qi) = gv[u] * x;
+                }
+            }
         }
         for (int i = n + ct; i < pad; i += 256) vec[i] = 0.f;
         ss = wave_sum(ss);
         if (lane == 0) ssp[c] = ss;
     };
     auto load_plain = [&](const float *src, int n, int pad) {
-        for (int i = ct; i < n / 2; i += 256) {
-            uint64_t v = ldc64(src + 2 * i);
-            vec[2 * i] = __uint_as_float((uint32_t)v);
-            vec[2 * i + 1] = __uint_as_float((uint32_t)(v >> 32));
+        const int nqd = n / 4;
+        const __amdgpu_buffer_rsrc_t rs = rsrc(src, (uint32_t)n * 4u);
+        for (int base = ct; base < nqd; base += 256 * 8) {
+            u4v v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = ld16c(rs, (uint32_t)(base + u * 256) * 16u);
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (base + u * 256 < nqd) *(LDS f4v *)(vec + 4 * (base + u * 256)) = as_f4(v[u]);
         }
         for (int i = n + ct; i < pad; i += 256) vec[i] = 0.f;
     };
-    auto inv_rms = [&](int n) {
+    auto inv_lds = [&](int n) {
         const float ss = ssp[0] + ssp[1] + ssp[2] + ssp[3];
         return 1.0f / sqrtf(ss / (float)n + p.eps);
     };
-
-    // ---- GEMV state ----
-    int row_c = 0, kc = 0;
-    float acc = 0.f;
-    auto gemv_begin = [&]() { row_c = 0; kc = 0; acc = 0.f; };
-    auto gemv_slot = [&](int st, int buf) {
-        const LDS unsigned char *bp = ring + buf * MK_SLOT_BYTES + c * 4 * MK_CHUNK_BYTES + lane * 16;
-        const int units = g.units[st], rbp = p.st[st].rbp;
+    // Register path (rows of exactly four chunks): every consumer loads the
+    // lane's slice of the input vector -- element q*EPC + lane*EPL + e feeds
+    // chunk q -- straight into registers with the gain applied, and returns
+    // the full sum of squares of x (it sees all 4*EPC elements).
+    auto load_direct = [&](const float *xsrc, const void *erow, const float *gain, float (&hr)[4][EPL]) -> float {
+        f4v xv[4][EPL / 4], gv[4][EPL / 4];
+        const __amdgpu_buffer_rsrc_t rx = rsrc(xsrc ? (const void *)xsrc : erow, 4u * EPC * (xsrc ? 4u : (uint32_t)EB));
 #pragma unroll
-        for (int qi = 0; qi < 4; ++qi) {
-            if (row_c < units) {
-                acc += piece_dot<DT>(bp + qi * MK_CHUNK_BYTES, vec + kc * EPC + lane * EPL);
-                if (++kc == rbp) {
-                    const float t = wave_sum(acc);
-                    if (lane == 0) outv[row_c * 4 + c] = t;
-                    acc = 0.f;
-                    kc = 0;
-                    ++row_c;
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int k4 = 0; k4 < EPL / 4; ++k4) {
+                const int el = q * EPC + lane * EPL + 4 * k4;  // first of 4 elements
+                if (xsrc) {
+                    xv[q][k4] = as_f4(ld16c(rx, (uint32_t)el * 4u));
+                } else if constexpr (DT == 1) {
+                    // one 16-byte load per chunk holds all 8 bf16 elements of the lane
+                    if (k4 == 0) {
+                        const u4v e = __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)el * 2u, 0, 0);
+                        xv[q][0] = f4v{bf_lo(e.x), bf_hi(e.x), bf_lo(e.y), bf_hi(e.y)};
+                        xv[q][1] = f4v{bf_lo(e.z), bf_hi(e.z), bf_lo(e.w), bf_hi(e.w)};
+                    }
+                } else {
+                    xv[q][k4] = as_f4(__builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)el * 4u, 0, 0));
+                }
+                gv[q][k4] = gain ? *(const f4v *)(gain + el) : f4v{1.f, 1.f, 1.f, 1.f};
+            }
+        float ss = 0.f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int k4 = 0; k4 < EPL / 4; ++k4) {
+                const f4v x = xv[q][k4];
+                ss = fmaf(x.x, x.x, ss);
+                ss = fmaf(x.y, x.y, ss);
+                ss = fmaf(x.z, x.z, ss);
+                ss = fmaf(x.w, x.w, ss);
+                const f4v hv = gv[q][k4] * x;
+                hr[q][4 * k4 + 0] = hv.x;
+                hr[q][4 * k4 + 1] = hv.y;
+                hr[q][4 * k4 + 2] = hv.z;
+                hr[q][4 * k4 + 3] = hv.w;
+            }
+        return wave_sum(ss);
+    };
+    auto inv_of = [&](float ss, int n) { return 1.0f / sqrtf(ss / (float)n + p.eps); };
+
+    // ---- GEMV data steps ----
+    // Register path: slot n holds row n of this consumer (4 chunks); the four
+    // 16-byte ring reads are issued before any arithmetic.
+    auto gemv_reg_steps = [&](int st, int l, const float (&hr)[4][EPL]) {
+        const int units = g.units[st];
+        for (int n = 0; n < g.nsl[st]; ++n) {
+            barrier();
+            stamp_step(l, 0);
+            if (n < units) {
+                const LDS unsigned char *bp = ring + (j % NS) * MK_SLOT_BYTES + c * 4 * MK_CHUNK_BYTES + lane * 16;
+                float d[4];
+                if constexpr (DT == 1) {
+                    u4v wv[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) wv[q] = *(const LDS u4v *)(bp + q * MK_CHUNK_BYTES);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        float a = bf_lo(wv[q].x) * hr[q][0];
+                        float b = bf_hi(wv[q].x) * hr[q][1];
+                        a = fmaf(bf_lo(wv[q].y), hr[q][2], a);
+                        b = fmaf(bf_hi(wv[q].y), hr[q][3], b);
+                        a = fmaf(bf_lo(wv[q].z), hr[q][4], a);
+                        b = fmaf(bf_hi(wv[q].z), hr[q][5], b);
+                        a = fmaf(bf_lo(wv[q].w), hr[q][6], a);
+                        b = fmaf(bf_hi(wv[q].w), hr[q][7], b);
+                        d[q] = a + b;
+                    }
+                } else {
+                    f4v wv[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) wv[q] = *(const LDS f4v *)(bp + q * MK_CHUNK_BYTES);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        d[q] = fmaf(wv[q].x, hr[q][0], wv[q].y * hr[q][1]) + fmaf(wv[q].z, hr[q][2], wv[q].w * hr[q][3]);
+                }
+                const float t = wave_sum((d[0] + d[1]) + (d[2] + d[3]));
+                if (lane == 0) outv[n * 4 + c] = t;
+            }
+            ++j;
+            stamp_step(l, 1);
+        }
+    };
+    // LDS path: any row length; the input vector is in vec.
+    auto gemv_lds_steps = [&](int st, int l) {
+        const int units = g.units[st], rbp = p.st[st].rbp;
+        int row_c = 0, kc = 0;
+        float acc = 0.f;
+        for (int n = 0; n < g.nsl[st]; ++n) {
+            barrier();
+            stamp_step(l, 0);
+            const LDS unsigned char *bp = ring + (j % NS) * MK_SLOT_BYTES + c * 4 * MK_CHUNK_BYTES + lane * 16;
+            if ((rbp & 3) == 0) {  // the piece lies inside one row
+                if (row_c < units) {
+                    const LDS float *hp = vec + kc * EPC + lane * EPL;
+                    const float d0 = piece_dot<DT>(bp, hp);
+                    const float d1 = piece_dot<DT>(bp + MK_CHUNK_BYTES, hp + EPC);
+                    const float d2 = piece_dot<DT>(bp + 2 * MK_CHUNK_BYTES, hp + 2 * EPC);
+                    const float d3 = piece_dot<DT>(bp + 3 * MK_CHUNK_BYTES, hp + 3 * EPC);
+                    acc += (d0 + d1) + (d2 + d3);
+                    kc += 4;
+                    if (kc == rbp) {
+                        const float t = wave_sum(acc);
+                        if (lane == 0) outv[row_c * 4 + c] = t;
+                        acc = 0.f;
+                        kc = 0;
+                        ++row_c;
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int qi = 0; qi < 4; ++qi) {
+                    if (row_c < units) {
+                        acc += piece_dot<DT>(bp + qi * MK_CHUNK_BYTES, vec + kc * EPC + lane * EPL);
+                        if (++kc == rbp) {
+                            const float t = wave_sum(acc);
+                            if (lane == 0) outv[row_c * 4 + c] = t;
+                            acc = 0.f;
+                            kc = 0;
+                            ++row_c;
+                        }
+                    }
                 }
             }
+            ++j;
+            stamp_step(l, 1);
         }
     };
 
-    // ---- attention state (per lane) ----
-    float qr[GQ][EPL];
-    float am[GQ], al[GQ], ao[GQ][EPL];
-    float kp[EPL], vp[EPL];
+    // ---- attention (split-K flash decode over this workgroup's positions) ----
     const float scale = 1.0f / sqrtf((float)d);
     const int e0 = (lane % LPP) * EPL;
-    auto attn_begin = [&]() {
+    struct AttnState {
+        float qr[GQ][EPL];           // the lane's dims of the group's query heads
+        float am[GQ], al[GQ];        // running max (wave-uniform), running sum
+        float ao[GQ][EPL];           // running unnormalised output (lane's dims)
+        float kp[EPL], vp[EPL];      // K/V of the position written this step
+    };
+    // Fold NQ groups of positions (each lane holds one position of each group,
+    // PPC positions per group) into the running state: all scores first, then
+    // one running-max update, rescale and V accumulation per head.  Invalid
+    // positions get probability 0 and their V values are never used.
+    auto attn_fold = [&](AttnState &A, auto nq_tag, const float (*kv)[EPL], const float (*vv)[EPL],
+                         const bool *valid) {
+        constexpr int NQ = decltype(nq_tag)::value;
+        float sc[NQ][GQ];
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+#pragma unroll
+            for (int h = 0; h < GQ; ++h) {
+                float t = 0.f;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) t = fmaf(A.qr[h][e], kv[q][e], t);
+                sc[q][h] = t;
+            }
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+#pragma unroll
+            for (int h = 0; h < GQ; ++h) {
+                const float gsum = group_sum<LPP>(sc[q][h]) * scale;  // all lanes take part
+                sc[q][h] = valid[q] ? gsum : -INFINITY;
+            }
 #pragma unroll
         for (int h = 0; h < GQ; ++h) {
-            am[h] = -INFINITY;
-            al[h] = 0.f;
+            float mx = sc[0][h];
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) ao[h][e] = 0.f;
+            for (int q = 1; q < NQ; ++q) mx = fmaxf(mx, sc[q][h]);
+            const float mn = fmaxf(A.am[h], xgroup_max<LPP>(mx));
+            const bool any = mn != -INFINITY;
+            const float alpha = any ? __expf(A.am[h] - mn) : 1.f;
+            float pe[NQ];
+            float lsum = A.al[h] * alpha;
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+                pe[q] = valid[q] ? __expf(sc[q][h] - mn) : 0.f;
+                lsum += pe[q];
+            }
+            A.al[h] = lsum;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                float o = A.ao[h][e] * alpha;
+#pragma unroll
+                for (int q = 0; q < NQ; ++q) o = fmaf(pe[q], valid[q] ? vv[q][e] : 0.f, o);
+                A.ao[h][e] = o;
+            }
+            A.am[h] = any ? mn : A.am[h];
         }
     };
-    // Fold one group of positions (one per lane group) into the running state.
-    auto attn_fold = [&](const float (&kv)[EPL], const float (&vv)[EPL], bool valid) {
-#pragma unroll
-        for (int h = 0; h < GQ; ++h) {
-            float s = 0.f;
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) s = fmaf(qr[h][e], kv[e], s);
-            s = group_sum<LPP>(s) * scale;
-            s = valid ? s : -INFINITY;
-            const float mx = xgroup_max<LPP>(s);
-            const float mn = fmaxf(am[h], mx);
-            if (mn == -INFINITY) continue;  // nothing valid yet (wave-uniform)
-            const float alpha = __expf(am[h] - mn);
-            // Masked positions contribute nothing; their V values are never
-            // touched (they may be unwritten cache contents, e.g. NaN).
-            const float pe = valid ? __expf(s - mn) : 0.f;
-            al[h] = al[h] * alpha + pe;
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) ao[h][e] = valid ? fmaf(pe, vv[e], ao[h][e] * alpha) : ao[h][e] * alpha;
-            am[h] = mn;
+    // This consumer's final state -> LDS record (o over all its positions, m, l).
+    auto attn_finish = [&](AttnState &A) {
+        if (c == 0 && is_last) {  // the position written this step
+            const bool v1[1] = {lane < LPP};
+            attn_fold(A, std::integral_constant<int, 1>{}, &A.kp, &A.vp, v1);
         }
-    };
-    auto attn_finish = [&]() {
-        if (c == 0 && is_last) attn_fold(kp, vp, lane < LPP);  // the position written this step
 #pragma unroll
         for (int h = 0; h < GQ; ++h) {
-            const float lsum = xgroup_sum<LPP>(al[h]);
+            const float lsum = xgroup_sum<LPP>(A.al[h]);
             LDS float *dst = cst + (c * GQ + h) * (d + 2);
 #pragma unroll
             for (int e = 0; e < EPL; ++e) {
-                const float ov = xgroup_sum<LPP>(ao[h][e]);
+                const float ov = xgroup_sum<LPP>(A.ao[h][e]);
                 if (lane < LPP) dst[e0 + e] = ov;
             }
-            if (lane == 0) { dst[d] = am[h]; dst[d + 1] = lsum; }
-        }
-    };
-    auto kv_slot = [&](int n, int buf) {
-        const LDS unsigned char *kb = ring + buf * MK_SLOT_BYTES;
-        const LDS unsigned char *vb = kb + 8 * MK_CHUNK_BYTES;
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int chunk = c * 2 + q;
-            const int tpos = t0 + n * BP + chunk * PPC + lane / LPP;
-            float kv[EPL], vv[EPL];
-            piece_load<DT>(kb + chunk * MK_CHUNK_BYTES + lane * 16, kv);
-            piece_load<DT>(vb + chunk * MK_CHUNK_BYTES + lane * 16, vv);
-            attn_fold(kv, vv, tpos < t1);
+            if (lane == 0) { dst[d] = A.am[h]; dst[d + 1] = lsum; }
         }
     };
 
     // ---- epilogues (consumer 0) ----
-    auto epi_qkv = [&](int l) {
-        const float inv = inv_rms(p.H);
-        const int nq = p.nh * d, nk = p.nkv * d;
+    auto epi_qkv = [&](int l, float inv) {
+        const int nqd = p.nh * d, nk = p.nkv * d;
         const float *rope = p.rope + (size_t)P * d;  // [d/2][2]
         for (int u = lane; u < g.units[ST_QKV]; u += 64) {
             const int gr0 = (g.unit0[ST_QKV] + u) * 4;
             const float y0 = outv[u * 4] * inv, y1 = outv[u * 4 + 1] * inv;
             const float y2 = outv[u * 4 + 2] * inv, y3 = outv[u * 4 + 3] * inv;
-            if (gr0 < nq + nk) {
-                const bool isq = gr0 < nq;
-                const int r = isq ? gr0 : gr0 - nq;
+            if (gr0 < nqd + nk) {
+                const bool isq = gr0 < nqd;
+                const int r = isq ? gr0 : gr0 - nqd;
                 const int head = r / d, m0 = (r % d) / 2;
                 const float c0 = rope[2 * m0], s0 = rope[2 * m0 + 1];
                 const float c1 = rope[2 * m0 + 2], s1 = rope[2 * m0 + 3];
@@ -600,8 +831,8 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
                         stc((float *)row + m0 + 1 + d / 2, b1);
                     }
                 }
-            } else if (gr0 < nq + 2 * nk) {
-                const int r = gr0 - nq - nk;
+            } else if (gr0 < nqd + 2 * nk) {
+                const int r = gr0 - nqd - nk;
                 const int head = r / d, e = r % d;
                 unsigned char *row = (unsigned char *)p.vc + ((size_t)l * p.nkv + head) * head_bytes + (size_t)P * d * EB;
                 if constexpr (DT == 1) {
@@ -626,8 +857,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
             }
         }
     };
-    auto epi_gu = [&]() {
-        const float inv = inv_rms(p.H);
+    auto epi_gu = [&](float inv) {
         for (int m = lane; m < g.units[ST_GU] * 2; m += 64) {
             const int f = g.unit0[ST_GU] * 2 + m;
             if (f < p.F) {
@@ -636,59 +866,91 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
             }
         }
     };
-    auto epi_attn = [&]() {
-        if (!has_split) return;
-        const int stride = d + 2;
-        float *part = p.part + ((size_t)kvj * S + kvs) * GQ * stride;
-        // merge the four consumers' states
+    // Attention epilogue, part 1 (consumer 0): merge the four consumers'
+    // states into this split's partial (o unnormalised, m, l), publish it with
+    // device-scope stores and count the split in.  Returns true in the last
+    // split to arrive for this KV head.
+    constexpr int PSTRIDE = DH + 4;  // partial record: o[DH], m, l, pad (16-byte aligned)
+    auto attn_partial = [&]() -> bool {
+        float *part = p.part + ((size_t)kvj * S + kvs) * GQ * PSTRIDE;
+        constexpr int cs = DH + 2;  // consumer-state record in LDS: o[DH], m, l
         for (int h = 0; h < GQ; ++h) {
             float M = -INFINITY;
-            for (int cc = 0; cc < MK_NUM_CONSUMERS; ++cc) M = fmaxf(M, cst[(cc * GQ + h) * stride + d]);
+            for (int cc = 0; cc < MK_NUM_CONSUMERS; ++cc) M = fmaxf(M, cst[(cc * GQ + h) * cs + d]);
             float Lsum = 0.f;
             float wgt[MK_NUM_CONSUMERS];
             for (int cc = 0; cc < MK_NUM_CONSUMERS; ++cc) {
-                const float mc = cst[(cc * GQ + h) * stride + d];
+                const float mc = cst[(cc * GQ + h) * cs + d];
                 wgt[cc] = (mc == -INFINITY) ? 0.f : __expf(mc - M);
-                Lsum += wgt[cc] * cst[(cc * GQ + h) * stride + d + 1];
+                Lsum += wgt[cc] * cst[(cc * GQ + h) * cs + d + 1];
             }
             for (int e = lane; e < d; e += 64) {
                 float o = 0.f;
-                for (int cc = 0; cc < MK_NUM_CONSUMERS; ++cc) o = fmaf(wgt[cc], cst[(cc * GQ + h) * stride + e], o);
-                stc(part + h * stride + e, o);
+                for (int cc = 0; cc < MK_NUM_CONSUMERS; ++cc) o = fmaf(wgt[cc], cst[(cc * GQ + h) * cs + e], o);
+                stc(part + h * PSTRIDE + e, o);
             }
-            if (lane == 0) { stc(part + h * stride + d, M); stc(part + h * stride + d + 1, Lsum); }
+            if (lane == 0) { stc(part + h * PSTRIDE + d, M); stc(part + h * PSTRIDE + d + 1, Lsum); }
         }
         MK_WAIT_VM0();
         uint32_t old = 0;
         if (lane == 0) old = __hip_atomic_fetch_add(p.head_cnt + kvj, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         old = __builtin_amdgcn_readfirstlane(old);
-        if (old != (uint32_t)(S - 1)) return;
-        // last arriver for this KV head: log-sum-exp merge of all splits
-        MK_COMPILER_BARRIER();
-        const float *pb = p.part + (size_t)kvj * S * GQ * stride;
-        for (int h = 0; h < GQ; ++h) {
-            float M = -INFINITY;
-            for (int s = lane; s < S; s += 64) M = fmaxf(M, ldc(pb + ((size_t)s * GQ + h) * stride + d));
-            M = wave_max(M);
-            float Lsum = 0.f;
-            float o0 = 0.f, o1 = 0.f;
-            for (int s = 0; s < S; ++s) {
-                const float *ps = pb + ((size_t)s * GQ + h) * stride;
-                const float ms = ldc(ps + d);
-                const float wgt = (ms == -INFINITY) ? 0.f : __expf(ms - M);
-                Lsum = fmaf(wgt, ldc(ps + d + 1), Lsum);
-                if (lane < d) o0 = fmaf(wgt, ldc(ps + lane), o0);
-                if (lane + 64 < d) o1 = fmaf(wgt, ldc(ps + lane + 64), o1);
-            }
-            float *od = p.o + ((size_t)kvj * GQ + h) * d;
-            const float invl = 1.0f / Lsum;
-            if (lane < d) stc(od + lane, o0 * invl);
-            if (lane + 64 < d) stc(od + lane + 64, o1 * invl);
-        }
-        if (lane == 0) stcu(p.head_cnt + kvj, 0u);
+        return old == (uint32_t)(S - 1);
     };
-    auto epi_lm = [&]() {
-        const float inv = inv_rms(p.H);
+    // Part 2 (last arriver, one head per call): log-sum-exp merge of the S
+    // split partials of head kvj*GQ + h into o.  Lane (sub, e4) covers head
+    // dims 4*e4..4*e4+3 of the splits s = b + sub + nsub*u; each batch of
+    // eight splits per lane is one memory round trip, merged online.
+    auto attn_combine_head = [&](int h) {
+        constexpr int Q4 = DH / 4, NSUB = 64 / Q4;
+        const int sub = lane / Q4, e4 = lane % Q4;
+        const float *pb = p.part + (size_t)kvj * S * GQ * PSTRIDE;
+        const __amdgpu_buffer_rsrc_t rp = rsrc(pb, (uint32_t)((size_t)S * GQ * PSTRIDE * 4));
+        float M = -INFINITY, Lacc = 0.f;
+        f4v acc = {0.f, 0.f, 0.f, 0.f};
+        for (int b = 0; b < S; b += NSUB * 8) {
+            u4v ov[8], ml[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const uint32_t rec = (uint32_t)(((b + sub + NSUB * u) * GQ + h) * PSTRIDE);
+                ov[u] = ld16c(rp, (rec + 4 * e4) * 4u);
+                ml[u] = ld16c(rp, (rec + d) * 4u);
+            }
+            float mb = -INFINITY;
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (b + sub + NSUB * u < S) mb = fmaxf(mb, __uint_as_float(ml[u].x));
+            const float mn = fmaxf(M, wave_max(mb));
+            if (mn == -INFINITY) continue;  // wave-uniform: no non-empty split yet
+            const float alpha = M == -INFINITY ? 0.f : __expf(M - mn);
+            acc *= alpha;
+            Lacc *= alpha;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const float ms = __uint_as_float(ml[u].x);
+                if (b + sub + NSUB * u < S && ms != -INFINITY) {
+                    const float wgt = __expf(ms - mn);
+                    acc += wgt * as_f4(ov[u]);
+                    Lacc = fmaf(wgt, __uint_as_float(ml[u].y), Lacc);
+                }
+            }
+            M = mn;
+        }
+        acc.x = xgroup_sum<Q4>(acc.x);
+        acc.y = xgroup_sum<Q4>(acc.y);
+        acc.z = xgroup_sum<Q4>(acc.z);
+        acc.w = xgroup_sum<Q4>(acc.w);
+        Lacc = xgroup_sum<Q4>(Lacc);
+        if (sub == 0) {
+            float *od = p.o + ((size_t)kvj * GQ + h) * d + 4 * e4;
+            const float invl = 1.0f / Lacc;
+            stc(od + 0, acc.x * invl);
+            stc(od + 1, acc.y * invl);
+            stc(od + 2, acc.z * invl);
+            stc(od + 3, acc.w * invl);
+        }
+    };
+    auto epi_lm = [&](float inv) {
         float best = -INFINITY;
         int besti = 0x7FFFFFFF;
         for (int i = lane; i < g.units[ST_LM] * 4; i += 64) {
@@ -715,10 +977,27 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
         MK_COMPILER_BARRIER();
         best = -INFINITY;
         besti = 0x7FFFFFFF;
-        for (int i = lane; i < G; i += 64) {
-            const float v = ldc(p.amax_val + i);
-            const int ix = (int)ldcu((const uint32_t *)p.amax_idx + i);
-            if (v > best || (v == best && ix < besti)) { best = v; besti = ix; }
+        {
+            const __amdgpu_buffer_rsrc_t rv = rsrc(p.amax_val, (uint32_t)G * 4u);
+            const __amdgpu_buffer_rsrc_t ri = rsrc(p.amax_idx, (uint32_t)G * 4u);
+            u4v vv[4], iv[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                vv[k] = ld16c(rv, (uint32_t)(lane + 64 * k) * 16u);
+                iv[k] = ld16c(ri, (uint32_t)(lane + 64 * k) * 16u);
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t vs[4] = {vv[k].x, vv[k].y, vv[k].z, vv[k].w};
+                const uint32_t is[4] = {iv[k].x, iv[k].y, iv[k].z, iv[k].w};
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    if ((lane + 64 * k) * 4 + t >= G) continue;
+                    const float v = __uint_as_float(vs[t]);
+                    const int ix = (int)is[t];
+                    if (v > best || (v == best && ix < besti)) { best = v; besti = ix; }
+                }
+            }
         }
         for (int m = 1; m < 64; m <<= 1) {
             const float ob = __shfl_xor(best, m);
@@ -731,158 +1010,238 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
         }
     };
 
+
     // ---- the program ----
     const int nq = p.nh * d;
     for (int l = 0; l < L && ok; ++l) {
-        // stage boundary: [epilogue DOWN(l-1)] + prologue QKV(l)
-        ok = barrier();
-        if (!ok) break;
-        if (l == 0) {
-            int tok = p.token_dev ? p.token_dev[0] : p.token;
-            if (tok < 0 || tok >= p.V) {
-                if (ct == 0) stcu(p.err, ldcu(p.err) | MK_DEVERR_TOKEN);
-                tok = 0;
-            }
-            const unsigned char *erow = (const unsigned char *)p.embed + (size_t)tok * p.H * EB;
-            load_normed(nullptr, erow, p.g_attn, p.H, p.st[ST_QKV].rbp * EPC);
-            for (int i = ct; i < g.units[ST_O] * 4; i += 256) {
-                const int r = g.unit0[ST_O] * 4 + i;
-                float xv = 0.f;
-                if (r < p.H) {
-                    if constexpr (DT == 1) xv = __uint_as_float((uint32_t)((const uint16_t *)erow)[r] << 16);
-                    else xv = ((const float *)erow)[r];
+        // ===== stage QKV(l); boundary: [epilogue DOWN(l-1)] + input x =====
+        float inv_q = 0.f;
+        {
+            barrier();
+            stamp(5 * l, 0);
+            const void *erow = nullptr;
+            if (l == 0) {
+                int tok = p.token_dev ? p.token_dev[0] : p.token;
+                if (tok < 0 || tok >= p.V) {
+                    if (ct == 0) stcu(p.err, ldcu(p.err) | MK_DEVERR_TOKEN);
+                    tok = 0;
                 }
-                xown[i] = xv;
+                erow = (const unsigned char *)p.embed + (size_t)tok * p.H * EB;
+                for (int i = ct; i < g.units[ST_O] * 4; i += 256) {
+                    const int r = g.unit0[ST_O] * 4 + i;
+                    float xv = 0.f;
+                    if (r < p.H) {
+                        if constexpr (DT == 1) xv = __uint_as_float((uint32_t)((const uint16_t *)erow)[r] << 16);
+                        else xv = ((const float *)erow)[r];
+                    }
+                    xown[i] = xv;
+                }
+            } else {
+                if (c == 0) {
+                    epi_residual(ST_DOWN);
+                    publish(5 * (l - 1) + 5);
+                }
+                stamp(5 * l, 1);
+                ok = wait_all(5 * (l - 1) + 5);
+                stamp(5 * l, 2);
             }
-        } else {
-            if (c == 0) {
-                epi_residual(ST_DOWN);
-                publish(5 * (l - 1) + 5);
+            if (!ok) break;
+            const float *gain = p.g_attn + (size_t)l * p.H;
+            if (p.st[ST_QKV].rbp == 4) {
+                float hr[4][EPL];
+                inv_q = inv_of(load_direct(l == 0 ? nullptr : p.x, erow, gain, hr), p.H);
+                stamp(5 * l, 3);
+                gemv_reg_steps(ST_QKV, l, hr);
+            } else {
+                load_normed(l == 0 ? nullptr : p.x, erow, gain, p.H, p.st[ST_QKV].rbp * EPC);
+                stamp(5 * l, 3);
+                gemv_lds_steps(ST_QKV, l);
+                inv_q = -1.f;  // from ssp at the epilogue
             }
-            if (!wait_all(5 * (l - 1) + 5)) ok = false;
-            if (ok) load_normed(p.x, nullptr, p.g_attn + (size_t)l * p.H, p.H, p.st[ST_QKV].rbp * EPC);
         }
-        gemv_begin();
-        for (int n = 0; n < g.nsl[ST_QKV] && ok; ++n) {
-            ok = barrier();
-            if (ok) gemv_slot(ST_QKV, j % NS);
-            ++j;
-        }
-        if (!ok) break;
 
-        // stage boundary: epilogue QKV(l) + prologue attention(l)
-        ok = barrier();
-        if (!ok) break;
-        if (c == 0) {
-            epi_qkv(l);
-            publish(5 * l + 1);
-        }
-        if (has_split) {
-            if (!wait_all(5 * l + 1)) ok = false;
-            if (ok) {
+        // ===== attention(l); boundary: epilogue QKV(l) + q, new K/V row =====
+        {
+            barrier();
+            stamp(5 * l + 1, 0);
+            if (c == 0) {
+                epi_qkv(l, inv_q >= 0.f ? inv_q : inv_lds(p.H));
+                publish(5 * l + 1);
+            }
+            stamp(5 * l + 1, 1);
+            if (has_split) {
+                ok = wait_all(5 * l + 1);
+                stamp(5 * l + 1, 2);
+                if (!ok) break;
+                AttnState A;
                 const float *qb = p.q + (size_t)kvj * GQ * d;
 #pragma unroll
                 for (int h = 0; h < GQ; ++h)
 #pragma unroll
-                    for (int e = 0; e < EPL; ++e) qr[h][e] = ldc(qb + h * d + e0 + e);
+                    for (int e = 0; e < EPL; ++e) A.qr[h][e] = ldc(qb + h * d + e0 + e);
                 if (c == 0 && is_last) {
                     const unsigned char *krow = (const unsigned char *)p.kc + ((size_t)l * p.nkv + kvj) * head_bytes + (size_t)P * d * EB;
                     const unsigned char *vrow = (const unsigned char *)p.vc + ((size_t)l * p.nkv + kvj) * head_bytes + (size_t)P * d * EB;
                     const int off = (lane < LPP ? lane : 0) * 16;
-                    piece_load_dev<DT>(krow + off, kp);
-                    piece_load_dev<DT>(vrow + off, vp);
+                    piece_load_dev<DT>(krow + off, A.kp);
+                    piece_load_dev<DT>(vrow + off, A.vp);
                 }
-                attn_begin();
-                if (nsl_kv == 0) attn_finish();
+#pragma unroll
+                for (int h = 0; h < GQ; ++h) {
+                    A.am[h] = -INFINITY;
+                    A.al[h] = 0.f;
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) A.ao[h][e] = 0.f;
+                }
+                stamp(5 * l + 1, 3);
+                if (nsl_kv == 0) attn_finish(A);
+                for (int n = 0; n < nsl_kv; ++n) {
+                    barrier();
+                    stamp_step(l, 0);
+                    const LDS unsigned char *kb = ring + (j % NS) * MK_SLOT_BYTES;
+                    const LDS unsigned char *vb = kb + 8 * MK_CHUNK_BYTES;
+                    float kv[2][EPL], vv[2][EPL];
+                    bool valid[2];
+#pragma unroll
+                    for (int q = 0; q < 2; ++q) {
+                        const int chunk = c * 2 + q;
+                        valid[q] = t0 + n * BP + chunk * PPC + lane / LPP < t1;
+                        piece_load<DT>(kb + chunk * MK_CHUNK_BYTES + lane * 16, kv[q]);
+                        piece_load<DT>(vb + chunk * MK_CHUNK_BYTES + lane * 16, vv[q]);
+                    }
+                    attn_fold(A, std::integral_constant<int, 2>{}, kv, vv, valid);
+                    if (n == nsl_kv - 1) attn_finish(A);
+                    ++j;
+                    stamp_step(l, 1);
+                }
+            } else {
+                stamp(5 * l + 1, 3);
             }
         }
-        for (int n = 0; n < nsl_kv && ok; ++n) {
-            ok = barrier();
-            if (ok) {
-                kv_slot(n, j % NS);
-                if (n == nsl_kv - 1) attn_finish();
+
+        // ===== stage O(l); boundary: epilogue attention(l) + input o =====
+        {
+            barrier();
+            stamp(5 * l + 2, 0);
+            if (has_split) {
+                if (c == 0) {
+                    const bool last = attn_partial();
+                    ctl[3] = last ? 1 : 0;
+                    ctl[2] = step;
+                } else {
+                    while (ctl[2] != step) __builtin_amdgcn_s_sleep(1);
+                }
+                MK_COMPILER_BARRIER();
+                if (ctl[3]) {
+                    for (int h = c; h < GQ; h += MK_NUM_CONSUMERS) attn_combine_head(h);
+                    MK_WAIT_VM0();
+                    if (lane == 0) ctl[4 + c] = step;
+                    if (c == 0) {
+                        for (int cc = 1; cc < MK_NUM_CONSUMERS; ++cc)
+                            while (ctl[4 + cc] != step) __builtin_amdgcn_s_sleep(1);
+                        MK_COMPILER_BARRIER();
+                        if (lane == 0) stcu(p.head_cnt + kvj, 0u);
+                    }
+                }
             }
-            ++j;
+            if (c == 0) publish(5 * l + 2);
+            stamp(5 * l + 2, 1);
+            ok = wait_all(5 * l + 2);
+            stamp(5 * l + 2, 2);
+            if (!ok) break;
+            if (p.st[ST_O].rbp == 4) {
+                float hr[4][EPL];
+                load_direct(p.o, nullptr, nullptr, hr);
+                stamp(5 * l + 2, 3);
+                gemv_reg_steps(ST_O, l, hr);
+            } else {
+                load_plain(p.o, nq, p.st[ST_O].rbp * EPC);
+                stamp(5 * l + 2, 3);
+                gemv_lds_steps(ST_O, l);
+            }
         }
-        if (!ok) break;
 
-        // stage boundary: epilogue attention(l) + prologue O(l)
-        ok = barrier();
-        if (!ok) break;
-        if (c == 0) {
-            epi_attn();
-            publish(5 * l + 2);
-        }
-        if (!wait_all(5 * l + 2)) { ok = false; break; }
-        load_plain(p.o, nq, p.st[ST_O].rbp * EPC);
-        gemv_begin();
-        for (int n = 0; n < g.nsl[ST_O] && ok; ++n) {
-            ok = barrier();
-            if (ok) gemv_slot(ST_O, j % NS);
-            ++j;
-        }
-        if (!ok) break;
-
-        // stage boundary: epilogue O(l) + prologue gate/up(l)
-        ok = barrier();
-        if (!ok) break;
-        if (c == 0) {
-            epi_residual(ST_O);
-            publish(5 * l + 3);
-        }
-        if (!wait_all(5 * l + 3)) { ok = false; break; }
-        load_normed(p.x, nullptr, p.g_ffn + (size_t)l * p.H, p.H, p.st[ST_GU].rbp * EPC);
-        gemv_begin();
-        for (int n = 0; n < g.nsl[ST_GU] && ok; ++n) {
-            ok = barrier();
-            if (ok) gemv_slot(ST_GU, j % NS);
-            ++j;
-        }
-        if (!ok) break;
-
-        // stage boundary: epilogue gate/up(l) + prologue down(l)
-        ok = barrier();
-        if (!ok) break;
-        if (c == 0) {
-            epi_gu();
-            publish(5 * l + 4);
-        }
-        if (!wait_all(5 * l + 4)) { ok = false; break; }
-        load_plain(p.a, p.F, p.st[ST_DOWN].rbp * EPC);
-        gemv_begin();
-        for (int n = 0; n < g.nsl[ST_DOWN] && ok; ++n) {
-            ok = barrier();
-            if (ok) gemv_slot(ST_DOWN, j % NS);
-            ++j;
-        }
-        if (!ok) break;
-    }
-    if (ok && p.want_logits) {
-        ok = barrier();
-        if (ok) {
+        // ===== stage gate/up(l); boundary: epilogue O(l) + input x =====
+        float inv_g = 0.f;
+        {
+            barrier();
+            stamp(5 * l + 3, 0);
             if (c == 0) {
-                epi_residual(ST_DOWN);
-                publish(5 * (L - 1) + 5);
+                epi_residual(ST_O);
+                publish(5 * l + 3);
             }
-            if (!wait_all(5 * (L - 1) + 5)) ok = false;
+            stamp(5 * l + 3, 1);
+            ok = wait_all(5 * l + 3);
+            stamp(5 * l + 3, 2);
+            if (!ok) break;
+            const float *gain = p.g_ffn + (size_t)l * p.H;
+            if (p.st[ST_GU].rbp == 4) {
+                float hr[4][EPL];
+                inv_g = inv_of(load_direct(p.x, nullptr, gain, hr), p.H);
+                stamp(5 * l + 3, 3);
+                gemv_reg_steps(ST_GU, l, hr);
+            } else {
+                load_normed(p.x, nullptr, gain, p.H, p.st[ST_GU].rbp * EPC);
+                stamp(5 * l + 3, 3);
+                gemv_lds_steps(ST_GU, l);
+                inv_g = -1.f;
+            }
         }
-        if (ok) load_normed(p.x, nullptr, p.g_final, p.H, p.st[ST_LM].rbp * EPC);
-        gemv_begin();
-        for (int n = 0; n < g.nsl[ST_LM] && ok; ++n) {
-            ok = barrier();
-            if (ok) gemv_slot(ST_LM, j % NS);
-            ++j;
+
+        // ===== stage down(l); boundary: epilogue gate/up(l) + input a =====
+        {
+            barrier();
+            stamp(5 * l + 4, 0);
+            if (c == 0) {
+                epi_gu(inv_g >= 0.f ? inv_g : inv_lds(p.H));
+                publish(5 * l + 4);
+            }
+            stamp(5 * l + 4, 1);
+            ok = wait_all(5 * l + 4);
+            stamp(5 * l + 4, 2);
+            if (!ok) break;
+            load_plain(p.a, p.F, p.st[ST_DOWN].rbp * EPC);
+            stamp(5 * l + 4, 3);
+            gemv_lds_steps(ST_DOWN, l);
         }
-        if (ok) {
-            ok = barrier();
-            if (ok && c == 0) epi_lm();
-        }
-    } else if (ok) {
-        ok = barrier();
-        if (ok && c == 0) {
+    }
+    if (ok && LOGITS) {
+        // ===== LM head; boundary: epilogue DOWN(L-1) + input x =====
+        float inv_lm = 0.f;
+        barrier();
+        stamp(5 * L, 0);
+        if (c == 0) {
             epi_residual(ST_DOWN);
             publish(5 * (L - 1) + 5);
         }
+        stamp(5 * L, 1);
+        ok = wait_all(5 * (L - 1) + 5);
+        stamp(5 * L, 2);
+        if (ok) {
+            if (p.st[ST_LM].rbp == 4) {
+                float hr[4][EPL];
+                inv_lm = inv_of(load_direct(p.x, nullptr, p.g_final, hr), p.H);
+                stamp(5 * L, 3);
+                gemv_reg_steps(ST_LM, L, hr);
+            } else {
+                load_normed(p.x, nullptr, p.g_final, p.H, p.st[ST_LM].rbp * EPC);
+                stamp(5 * L, 3);
+                gemv_lds_steps(ST_LM, L);
+                inv_lm = -1.f;
+            }
+            barrier();
+            stamp(5 * L + 1, 0);
+            if (c == 0) epi_lm(inv_lm >= 0.f ? inv_lm : inv_lds(p.H));
+            stamp(5 * L + 1, 1);
+        }
+    } else if (ok) {
+        barrier();
+        stamp(5 * L + 1, 0);
+        if (c == 0) {
+            epi_residual(ST_DOWN);
+            publish(5 * (L - 1) + 5);
+        }
+        stamp(5 * L + 1, 1);
     }
     if (!ok) {
         // Aborted inside step `step` (ctl[1] == step): pass one more barrier,
@@ -898,10 +1257,10 @@ namespace {
 typedef void (*KernelFn)(const MkParams);
 
 template <int DT, int GQ, int LPP>
-KernelFn kfn() { return mk_decode_kernel<DT, GQ, LPP>; }
+KernelFn kfn(bool logits) { return logits ? mk_decode_kernel<DT, GQ, LPP, true> : mk_decode_kernel<DT, GQ, LPP, false>; }
 
-KernelFn pick(int dtype, int gq, int lpp) {
-#define MK_PICK(DT_, GQ_, LPP_) if (dtype == DT_ && gq == GQ_ && lpp == LPP_) return kfn<DT_, GQ_, LPP_>();
+KernelFn pick(int dtype, int gq, int lpp, bool logits) {
+#define MK_PICK(DT_, GQ_, LPP_) if (dtype == DT_ && gq == GQ_ && lpp == LPP_) return kfn<DT_, GQ_, LPP_>(logits);
     MK_PICK(1, 1, 8) MK_PICK(1, 2, 8) MK_PICK(1, 4, 8) MK_PICK(1, 8, 8)
     MK_PICK(1, 1, 16) MK_PICK(1, 2, 16) MK_PICK(1, 4, 16) MK_PICK(1, 8, 16)
     MK_PICK(0, 1, 8) MK_PICK(0, 2, 8) MK_PICK(0, 4, 8) MK_PICK(0, 8, 8)
@@ -913,7 +1272,7 @@ KernelFn pick(int dtype, int gq, int lpp) {
 
 extern "C" int mk_kernel_lds_bytes(int ring_slots, int vec_floats, int out_rows, int dtype, int d, int gq) {
     (void)dtype;
-    const int floats = vec_floats + out_rows + MK_NUM_CONSUMERS * gq * (d + 2) + 64 + MK_NUM_CONSUMERS + 4;
+    const int floats = vec_floats + out_rows + MK_NUM_CONSUMERS * gq * (d + 2) + 64 + MK_NUM_CONSUMERS + 16;
     return ring_slots * MK_SLOT_BYTES + floats * 4;
 }
 
@@ -921,7 +1280,7 @@ extern "C" int mk_launch_decode(const MkParams *p, int dtype, int cooperative, v
     const int eb = dtype ? 2 : 4;
     const int lpp = p->d * eb / 16;
     const int gq = p->nh / p->nkv;
-    KernelFn fn = pick(dtype, gq, lpp);
+    KernelFn fn = pick(dtype, gq, lpp, p->want_logits != 0);
     if (!fn) return (int)hipErrorInvalidValue;
     const int lds = mk_kernel_lds_bytes(p->ring_slots, p->lds_vec_floats, p->lds_out_rows, dtype, p->d, gq);
     hipError_t e = hipFuncSetAttribute((const void *)fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
@@ -937,11 +1296,16 @@ extern "C" int mk_launch_decode(const MkParams *p, int dtype, int cooperative, v
 }
 
 extern "C" int mk_kernel_max_blocks_per_cu(int dtype, int gq, int lpp, int lds) {
-    KernelFn fn = pick(dtype, gq, lpp);
-    if (!fn) return 0;
-    if (hipFuncSetAttribute((const void *)fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess) return 0;
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, (const void *)fn, MK_BLOCK_THREADS, lds) != hipSuccess)
-        return 0;
-    return n;
+    int best = 1 << 30;
+    for (int logits = 0; logits < 2; ++logits) {
+        KernelFn fn = pick(dtype, gq, lpp, logits != 0);
+        if (!fn) return 0;
+        if (hipFuncSetAttribute((const void *)fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
+            return 0;
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, (const void *)fn, MK_BLOCK_THREADS, lds) != hipSuccess)
+            return 0;
+        if (n < best) best = n;
+    }
+    return best;
 }

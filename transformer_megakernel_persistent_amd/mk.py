@@ -20,7 +20,7 @@ MK_ERR_NOMEM, MK_ERR_HIP, MK_ERR_DEVICE, MK_ERR_STATE, MK_ERR_TUNING = 5, 6, 7, 
 MK_F32, MK_BF16 = 0, 1
 
 EXPORTED = ("mk_create", "mk_decode_step", "mk_decode_step_device_token", "mk_prefill_kv", "mk_get_device_error",
-            "mk_get_info", "mk_status_str", "mk_destroy")
+            "mk_get_info", "mk_read_trace", "mk_status_str", "mk_destroy")
 
 
 class ModelDesc(ctypes.Structure):
@@ -46,7 +46,7 @@ class KVDesc(ctypes.Structure):
 
 class Tuning(ctypes.Structure):
     _fields_ = [("grid", ctypes.c_int32), ("ring_slots", ctypes.c_int32), ("attn_splits", ctypes.c_int32),
-                ("timeout_ms", ctypes.c_int32), ("cooperative", ctypes.c_int32)]
+                ("timeout_ms", ctypes.c_int32), ("cooperative", ctypes.c_int32), ("trace", ctypes.c_int32)]
 
 
 class Info(ctypes.Structure):
@@ -74,6 +74,7 @@ def load_library(path: str = LIB_PATH):
         "mk_prefill_kv": ([vp, vp, i32, i32, p(KVDesc), vp], ctypes.c_int),
         "mk_get_device_error": ([vp], ctypes.c_int),
         "mk_get_info": ([vp, p(Info)], ctypes.c_int),
+        "mk_read_trace": ([vp, vp, ctypes.c_int64], ctypes.c_int),
         "mk_status_str": ([ctypes.c_int], ctypes.c_char_p),
         "mk_destroy": ([vp], None),
     }
@@ -176,6 +177,17 @@ class MegaKernel:
         inf = Info()
         _check(load_library().mk_get_info(self._h, ctypes.byref(inf)), "mk_get_info")
         return {f: getattr(inf, f) for f, _ in Info._fields_}
+
+    def read_trace(self):
+        """Stage timeline of the last step as a numpy array [grid][5L+2][4]
+        of wall-clock ticks (handle created with tuning trace=1)."""
+        import numpy as np
+        n_b = 5 * self.shape["n_layers"] + 2
+        grid = self.info()["grid"]
+        raw = np.zeros(grid * n_b * 4 + grid * 64 * 2, dtype=np.uint64)
+        _check(load_library().mk_read_trace(self._h, raw.ctypes.data_as(ctypes.c_void_p), raw.size), "mk_read_trace")
+        self.last_steps = raw[grid * n_b * 4:].reshape(grid, 64, 2)
+        return raw[:grid * n_b * 4].reshape(grid, n_b, 4)
 
     def close(self):
         if getattr(self, "_h", None):
