@@ -105,6 +105,11 @@ def main():
     ap.add_argument("--ring", type=int, default=0)
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--launch", choices=["cooperative", "ordinary"], default="cooperative",
+                    help="cooperative launch (co-residency checked by the runtime) or an ordinary launch")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="after the run, copy BYTES device-to-device three times (a plain copy kernel of known "
+                         "size, to scale rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -130,7 +135,8 @@ def main():
     host_w = synth.gen_weights(cfg, seed=args.seed)
     print(f"[bench] {cfg.name}: weights generated in {time.perf_counter() - t:.1f}s", file=sys.stderr, flush=True)
     dev_w = mkp.upload_weights(host_w, dev)
-    tuning = {"grid": args.grid, "ring_slots": args.ring, "attn_splits": args.splits}
+    tuning = {"grid": args.grid, "ring_slots": args.ring, "attn_splits": args.splits,
+              "cooperative": 1 if args.launch == "cooperative" else 2}
     mk = mkp.MegaKernel(shape, dev_w, max_seq, tuning=tuning)
     del dev_w
     torch.cuda.empty_cache()
@@ -200,7 +206,7 @@ def main():
             "context": ctx, "global_batch": 1, "decode_positions": [pos, pos + steps - 1],
             "launches_per_token": 1, "grid": info["grid"], "ring_slots": info["ring_slots"],
             "attn_splits": info["attn_splits"], "block_threads": info["block_threads"],
-            "lds_bytes": info["lds_bytes"], "parallelism": "single GPU"},
+            "lds_bytes": info["lds_bytes"], "launch": args.launch, "parallelism": "single GPU"},
         "us_per_token_p50": p50,
         "us_per_token_p99": p99,
         "us_per_token_mean": mean_us,
@@ -214,6 +220,14 @@ def main():
     }
     print(json.dumps(out), flush=True)
     mk.close()
+    if args.copy_calibration:
+        n = args.copy_calibration // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n * 4, "copies": 3}), file=sys.stderr, flush=True)
 
 
 if __name__ == "__main__":

@@ -10,7 +10,7 @@
 
 #include <vector>
 
-#include "../../include/mk.h"
+#include "mk.h"
 #include "mk_internal.h"
 
 extern "C" int mk_kernel_max_blocks_per_cu(int dtype, int gq, int lpp, int lds);
@@ -133,6 +133,7 @@ static mk_status create_impl(const mk_model_desc *desc, const mk_weight_ptrs *wp
         return MK_ERR_TUNING;
     if (t.ring_slots != 0 && (t.ring_slots < 3 || t.ring_slots > MK_MAX_RING)) return MK_ERR_TUNING;
     const int grid = t.grid ? t.grid : h->cu_count;
+    if (grid > MK_FLAG_STRIDE) return MK_ERR_TUNING;
     const int splits = t.attn_splits ? t.attn_splits : (grid / nkv > 0 ? grid / nkv : 1);
     if ((int64_t)splits * nkv > grid) return MK_ERR_TUNING;
     h->cooperative = t.cooperative == 2 ? 0 : 1;
@@ -188,7 +189,9 @@ static mk_status create_impl(const mk_model_desc *desc, const mk_weight_ptrs *wp
     const size_t nscratch = (size_t)H + 2 * (size_t)nh * d + F + part_floats;
     HIP_TRY(hipMalloc(&h->scratch, nscratch * sizeof(float)));
     HIP_TRY(hipMemset(h->scratch, 0, nscratch * sizeof(float)));
-    const size_t nwords = (size_t)nkv + grid + 2 + 64;
+    // [flag replicas][MK_FLAG_STRIDE] | head counters [nkv] | error | argmax counter
+    const size_t nflag = (size_t)MK_FLAG_REPLICAS * MK_FLAG_STRIDE;
+    const size_t nwords = nflag + (size_t)nkv + 2 + 64;
     HIP_TRY(hipMalloc(&h->words, nwords * sizeof(uint32_t)));
     HIP_TRY(hipMemset(h->words, 0, nwords * sizeof(uint32_t)));
     HIP_TRY(hipMalloc(&h->amax_val, grid * sizeof(float)));
@@ -252,9 +255,9 @@ static mk_status create_impl(const mk_model_desc *desc, const mk_weight_ptrs *wp
     P.o = P.q + (size_t)nh * d;
     P.a = P.o + (size_t)nh * d;
     P.part = P.a + F;
-    P.head_cnt = h->words;
-    P.flags = h->words + nkv;
-    P.err = P.flags + grid;
+    P.flags = h->words;
+    P.head_cnt = h->words + nflag;
+    P.err = P.head_cnt + nkv;
     P.amax_cnt = P.err + 1;
     P.amax_val = h->amax_val;
     P.amax_idx = h->amax_idx;

@@ -24,6 +24,8 @@
 #define MK_BLOCK_THREADS (64 * (MK_NUM_LOADERS + MK_NUM_CONSUMERS))
 #define MK_MAX_RING 8
 #define MK_LDS_LIMIT 163840
+#define MK_FLAG_REPLICAS 8
+#define MK_FLAG_STRIDE 1024  // words (4 KiB) between progress-word replicas; grid <= 1024
 
 // Stage kinds with weights; the attention stage streams the KV cache.
 enum { ST_QKV = 0, ST_O = 1, ST_GU = 2, ST_DOWN = 3, ST_LM = 4, ST_NUM = 5 };
@@ -57,7 +59,7 @@ struct MkParams {
     // scratch
     float *x, *q, *o, *a, *part;
     uint32_t *head_cnt;    // [nkv]
-    uint32_t *flags;       // [grid] progress epochs
+    uint32_t *flags;       // [MK_FLAG_REPLICAS][MK_FLAG_STRIDE] progress epochs
     uint32_t *err;         // device error word
     float *amax_val;       // [grid]
     int32_t *amax_idx;     // [grid]

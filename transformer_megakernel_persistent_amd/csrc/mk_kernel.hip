@@ -469,9 +469,14 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
     };
 
     // Progress publication (consumer 0, after its stores completed).
+    // The progress words exist in MK_FLAG_REPLICAS copies, MK_FLAG_STRIDE words
+    // apart; a waiter polls the copy of its XCD (w % 8), so the polling of
+    // the grid is spread over several memory channels instead of a few lines.
+    // Publishing waits for its own stores again before polling starts.
     auto publish = [&](int k) {
         MK_WAIT_VM0();  // every store of the stage is visible before the progress word
-        if (lane == 0) stcu(p.flags + w, p.epoch_base + (uint32_t)k);
+        if (lane < MK_FLAG_REPLICAS) stcu(p.flags + (size_t)lane * MK_FLAG_STRIDE + w, p.epoch_base + (uint32_t)k);
+        MK_WAIT_VM0();
     };
     // Wait until every workgroup published point k.  Consumer 0 polls; the
     // other consumers wait for its go signal in LDS.  Returns false on abort.
@@ -480,7 +485,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
             const uint32_t target = p.epoch_base + (uint32_t)k;
             const int64_t t_start = wall_clock64();
             bool good = true;
-            const __amdgpu_buffer_rsrc_t rf = rsrc(p.flags, (uint32_t)G * 4u);
+            const __amdgpu_buffer_rsrc_t rf = rsrc(p.flags + (size_t)(w % MK_FLAG_REPLICAS) * MK_FLAG_STRIDE, (uint32_t)G * 4u);
             while (true) {
                 bool mine = true;
                 u4v fv[4];
