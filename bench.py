@@ -105,7 +105,7 @@ def main():
     ap.add_argument("--ring", type=int, default=0)
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--launch", choices=["cooperative", "ordinary"], default="cooperative",
+    ap.add_argument("--launch", choices=["cooperative", "ordinary"], default="ordinary",
                     help="cooperative launch (co-residency checked by the runtime) or an ordinary launch")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="after the run, copy BYTES device-to-device three times (a plain copy kernel of known "

@@ -89,13 +89,21 @@ typedef struct {
 } mk_kv_cache;
 
 /* Tuning knobs.  Zero selects the default for every field.
-     grid:        workgroups of the persistent grid (default: CU count);
+     grid:        workgroups of the persistent grid, 1..1024 and no more than
+                  can be resident at once (default: CU count);
      ring_slots:  16 KiB LDS ring slots per workgroup, 3..8 (default: as many
                   as fit beside the activation buffer);
      attn_splits: sequence splits per KV head (default: grid / n_kv_heads);
      timeout_ms:  grid-wait timeout before the device error flag is raised
                   (default 2000);
-     cooperative: 1 = cooperative launch (default), 2 = ordinary launch;
+     cooperative: 2 = ordinary launch (default), 1 = cooperative launch.
+                  Either way the host first checks that the whole grid fits
+                  on the device at once (one workgroup per CU); the ordinary
+                  launch skips the runtime's own co-residency handling,
+                  which costs about 20 us per launch.  If workgroups are
+                  nevertheless not co-resident (another kernel holds CUs),
+                  the grid waits end by timeout with the device error flag,
+                  never by a hang;
      trace:       1 = record a per-workgroup stage timeline on every step
                   (read it with mk_read_trace; default 0 = off). */
 typedef struct {

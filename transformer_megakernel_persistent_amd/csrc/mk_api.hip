@@ -20,7 +20,7 @@ struct mk_handle {
     int eb = 0;
     int device = 0;
     int cu_count = 0;
-    int cooperative = 1;
+    int cooperative = 0;
     MkParams base;  // launch-invariant kernel arguments
     unsigned char *packed = nullptr;
     int64_t packed_bytes = 0;
@@ -70,6 +70,16 @@ mk_status validate_desc(const mk_model_desc *d) {
     if (!(d->rms_eps >= 0.0) || !(d->rope_theta > 0.0)) return MK_ERR_SHAPE;
     if ((int64_t)d->n_heads * d->head_dim > (1 << 20) || d->hidden > (1 << 20) || d->ffn > (1 << 22))
         return MK_ERR_SHAPE;
+    return MK_OK;
+}
+
+// Ranges of the tuning knobs that need no device query.
+mk_status validate_tuning(const mk_tuning *t) {
+    if (!t) return MK_OK;
+    if (t->grid < 0 || t->grid > MK_FLAG_STRIDE || t->ring_slots < 0 || t->attn_splits < 0 || t->timeout_ms < 0 ||
+        t->cooperative < 0 || t->cooperative > 2 || t->trace < 0 || t->trace > 1)
+        return MK_ERR_TUNING;
+    if (t->ring_slots != 0 && (t->ring_slots < 3 || t->ring_slots > MK_MAX_RING)) return MK_ERR_TUNING;
     return MK_OK;
 }
 
@@ -125,18 +135,14 @@ static mk_status create_impl(const mk_model_desc *desc, const mk_weight_ptrs *wp
     HIP_TRY(hipDeviceGetAttribute(&wclk_khz, hipDeviceAttributeWallClockRate, h->device));
     if (wclk_khz <= 0) wclk_khz = 100000;
 
-    // tuning
+    // tuning (ranges were checked by validate_tuning)
     mk_tuning t = {0, 0, 0, 0, 0, 0};
     if (tun) t = *tun;
-    if (t.grid < 0 || t.ring_slots < 0 || t.attn_splits < 0 || t.timeout_ms < 0 || t.cooperative < 0 ||
-        t.cooperative > 2 || t.trace < 0 || t.trace > 1)
-        return MK_ERR_TUNING;
-    if (t.ring_slots != 0 && (t.ring_slots < 3 || t.ring_slots > MK_MAX_RING)) return MK_ERR_TUNING;
     const int grid = t.grid ? t.grid : h->cu_count;
     if (grid > MK_FLAG_STRIDE) return MK_ERR_TUNING;
     const int splits = t.attn_splits ? t.attn_splits : (grid / nkv > 0 ? grid / nkv : 1);
     if ((int64_t)splits * nkv > grid) return MK_ERR_TUNING;
-    h->cooperative = t.cooperative == 2 ? 0 : 1;
+    h->cooperative = t.cooperative == 1 ? 1 : 0;
     const int timeout_ms = t.timeout_ms ? t.timeout_ms : 2000;
 
     // stage geometry
@@ -275,6 +281,8 @@ extern "C" mk_status mk_create(const mk_model_desc *desc, const mk_weight_ptrs *
     *out = nullptr;
     if (!desc || !weights) return MK_ERR_NULL;
     mk_status s = validate_desc(desc);
+    if (s != MK_OK) return s;
+    s = validate_tuning(tuning);
     if (s != MK_OK) return s;
     if (!weights->embed || !weights->final_norm || !weights->layers || (!desc->tied_embeddings && !weights->lm_head))
         return MK_ERR_NULL;

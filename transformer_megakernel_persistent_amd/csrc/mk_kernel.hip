@@ -1287,9 +1287,10 @@ extern "C" int mk_launch_decode(const MkParams *p, int dtype, int cooperative, v
     const int gq = p->nh / p->nkv;
     KernelFn fn = pick(dtype, gq, lpp, p->want_logits != 0);
     if (!fn) return (int)hipErrorInvalidValue;
+    // the dynamic-LDS limit of every instantiation was raised to MK_LDS_LIMIT
+    // when the handle was created (mk_kernel_max_blocks_per_cu)
     const int lds = mk_kernel_lds_bytes(p->ring_slots, p->lds_vec_floats, p->lds_out_rows, dtype, p->d, gq);
-    hipError_t e = hipFuncSetAttribute((const void *)fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (e != hipSuccess) return (int)e;
+    hipError_t e;
     MkParams copy = *p;
     void *args[] = {&copy};
     if (cooperative)
@@ -1305,7 +1306,8 @@ extern "C" int mk_kernel_max_blocks_per_cu(int dtype, int gq, int lpp, int lds) 
     for (int logits = 0; logits < 2; ++logits) {
         KernelFn fn = pick(dtype, gq, lpp, logits != 0);
         if (!fn) return 0;
-        if (hipFuncSetAttribute((const void *)fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
+        if (hipFuncSetAttribute((const void *)fn, hipFuncAttributeMaxDynamicSharedMemorySize, MK_LDS_LIMIT) !=
+            hipSuccess)
             return 0;
         int n = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, (const void *)fn, MK_BLOCK_THREADS, lds) != hipSuccess)
