@@ -93,7 +93,8 @@ typedef struct {
                   can be resident at once (default: CU count);
      ring_slots:  16 KiB LDS ring slots per workgroup, 3..8 (default: as many
                   as fit beside the activation buffer);
-     attn_splits: sequence splits per KV head (default: grid / n_kv_heads);
+     attn_splits: sequence splits per KV head, at most 64 (default:
+                  min(grid / n_kv_heads, 64));
      timeout_ms:  grid-wait timeout before the device error flag is raised
                   (default 2000);
      cooperative: 2 = ordinary launch (default), 1 = cooperative launch.

@@ -29,13 +29,11 @@ struct mk_handle {
     float *gains = nullptr;     // attn [L][H], ffn [L][H], final [H]
     void *embed = nullptr;
     float *rope = nullptr;
-    float *scratch = nullptr;   // x, q, o, a, partials
-    uint32_t *words = nullptr;  // head counters, progress words, error word, argmax counter
-    float *amax_val = nullptr;
-    int32_t *amax_idx = nullptr;
+    uint64_t *ll = nullptr;     // tagged cross-workgroup records (see MkParams)
+    uint32_t *err = nullptr;    // device error word
     uint64_t *trace = nullptr;
     int64_t trace_len = 0;
-    uint32_t epoch = 1;
+    uint32_t tag = 0;           // tag of the last launch
     bool disabled = false;
     hipStream_t last_stream = nullptr;
     int lds_bytes = 0;
@@ -76,7 +74,7 @@ mk_status validate_desc(const mk_model_desc *d) {
 // Ranges of the tuning knobs that need no device query.
 mk_status validate_tuning(const mk_tuning *t) {
     if (!t) return MK_OK;
-    if (t->grid < 0 || t->grid > MK_FLAG_STRIDE || t->ring_slots < 0 || t->attn_splits < 0 || t->timeout_ms < 0 ||
+    if (t->grid < 0 || t->grid > MK_MAX_GRID || t->ring_slots < 0 || t->attn_splits < 0 || t->attn_splits > MK_MAX_SPLITS || t->timeout_ms < 0 ||
         t->cooperative < 0 || t->cooperative > 2 || t->trace < 0 || t->trace > 1)
         return MK_ERR_TUNING;
     if (t->ring_slots != 0 && (t->ring_slots < 3 || t->ring_slots > MK_MAX_RING)) return MK_ERR_TUNING;
@@ -108,10 +106,8 @@ extern "C" void mk_destroy(mk_handle *h) {
     hipFree(h->gains);
     hipFree(h->embed);
     hipFree(h->rope);
-    hipFree(h->scratch);
-    hipFree(h->words);
-    hipFree(h->amax_val);
-    hipFree(h->amax_idx);
+    hipFree(h->ll);
+    hipFree(h->err);
     hipFree(h->trace);
     delete h;
 }
@@ -139,8 +135,9 @@ static mk_status create_impl(const mk_model_desc *desc, const mk_weight_ptrs *wp
     mk_tuning t = {0, 0, 0, 0, 0, 0};
     if (tun) t = *tun;
     const int grid = t.grid ? t.grid : h->cu_count;
-    if (grid > MK_FLAG_STRIDE) return MK_ERR_TUNING;
-    const int splits = t.attn_splits ? t.attn_splits : (grid / nkv > 0 ? grid / nkv : 1);
+    if (grid > MK_MAX_GRID) return MK_ERR_TUNING;
+    int splits = t.attn_splits ? t.attn_splits : (grid / nkv > 0 ? grid / nkv : 1);
+    if (!t.attn_splits && splits > MK_MAX_SPLITS) splits = MK_MAX_SPLITS;
     if ((int64_t)splits * nkv > grid) return MK_ERR_TUNING;
     h->cooperative = t.cooperative == 1 ? 1 : 0;
     const int timeout_ms = t.timeout_ms ? t.timeout_ms : 2000;
@@ -172,7 +169,8 @@ static mk_status create_impl(const mk_model_desc *desc, const mk_weight_ptrs *wp
         s.layer_stride = k == ST_LM ? 0 : block;
         total += k == ST_LM ? block : block * L;
     }
-    if (out_rows < splits) out_rows = splits;  // the attention combine keeps split weights there
+    // the attention stage gathers its group's queries and the new K/V row into vec
+    if (vec_floats < (gq + 2) * d) vec_floats = (gq + 2) * d;
     const int fixed = mk_kernel_lds_bytes(0, vec_floats, out_rows, dtype, d, gq);
     int ns = t.ring_slots ? t.ring_slots : (MK_LDS_LIMIT - fixed) / MK_SLOT_BYTES;
     if (ns > MK_MAX_RING) ns = MK_MAX_RING;
@@ -191,17 +189,15 @@ static mk_status create_impl(const mk_model_desc *desc, const mk_weight_ptrs *wp
     HIP_TRY(hipMalloc(&h->gains, ngain * sizeof(float)));
     HIP_TRY(hipMalloc(&h->embed, (size_t)V * H * eb));
     HIP_TRY(hipMalloc(&h->rope, (size_t)D.max_seq * d * sizeof(float)));
-    const size_t part_floats = (size_t)nkv * splits * gq * (d + 4);
-    const size_t nscratch = (size_t)H + 2 * (size_t)nh * d + F + part_floats;
-    HIP_TRY(hipMalloc(&h->scratch, nscratch * sizeof(float)));
-    HIP_TRY(hipMemset(h->scratch, 0, nscratch * sizeof(float)));
-    // [flag replicas][MK_FLAG_STRIDE] | head counters [nkv] | error | argmax counter
-    const size_t nflag = (size_t)MK_FLAG_REPLICAS * MK_FLAG_STRIDE;
-    const size_t nwords = nflag + (size_t)nkv + 2 + 64;
-    HIP_TRY(hipMalloc(&h->words, nwords * sizeof(uint32_t)));
-    HIP_TRY(hipMemset(h->words, 0, nwords * sizeof(uint32_t)));
-    HIP_TRY(hipMalloc(&h->amax_val, grid * sizeof(float)));
-    HIP_TRY(hipMalloc(&h->amax_idx, grid * sizeof(int32_t)));
+    // tagged records, one array per dependency point and layer
+    const size_t n_xq = (size_t)(L + 1) * H, n_xg = (size_t)L * H, n_q = (size_t)L * nh * d,
+                 n_kvn = (size_t)L * nkv * 2 * d, n_part = (size_t)L * nkv * splits * gq * (d + 2),
+                 n_o = (size_t)L * nh * d, n_a = (size_t)L * F, n_amax = (size_t)grid * 2;
+    const size_t n_ll = n_xq + n_xg + n_q + n_kvn + n_part + n_o + n_a + n_amax;
+    HIP_TRY(hipMalloc(&h->ll, n_ll * sizeof(uint64_t)));
+    HIP_TRY(hipMemset(h->ll, 0, n_ll * sizeof(uint64_t)));  // tag 0: never a launch's tag
+    HIP_TRY(hipMalloc(&h->err, 64 * sizeof(uint32_t)));
+    HIP_TRY(hipMemset(h->err, 0, 64 * sizeof(uint32_t)));
     if (t.trace) {
         h->trace_len = (int64_t)grid * (5 * L + 2) * 4 + (int64_t)grid * 64 * 2;
         HIP_TRY(hipMalloc(&h->trace, h->trace_len * sizeof(uint64_t)));
@@ -256,17 +252,15 @@ static mk_status create_impl(const mk_model_desc *desc, const mk_weight_ptrs *wp
     P.g_attn = h->gains; P.g_ffn = h->gains + (size_t)L * H; P.g_final = h->gains + (size_t)2 * L * H;
     P.embed = h->embed;
     P.rope = h->rope;
-    P.x = h->scratch;
-    P.q = P.x + H;
-    P.o = P.q + (size_t)nh * d;
-    P.a = P.o + (size_t)nh * d;
-    P.part = P.a + F;
-    P.flags = h->words;
-    P.head_cnt = h->words + nflag;
-    P.err = P.head_cnt + nkv;
-    P.amax_cnt = P.err + 1;
-    P.amax_val = h->amax_val;
-    P.amax_idx = h->amax_idx;
+    P.ll_xq = h->ll;
+    P.ll_xg = P.ll_xq + n_xq;
+    P.ll_q = P.ll_xg + n_xg;
+    P.ll_kvn = P.ll_q + n_q;
+    P.ll_part = P.ll_kvn + n_kvn;
+    P.ll_o = P.ll_part + n_part;
+    P.ll_a = P.ll_o + n_o;
+    P.ll_amax = P.ll_a + n_a;
+    P.err = h->err;
     P.timeout_ticks = (int64_t)timeout_ms * wclk_khz;
     P.trace = h->trace;
 
@@ -319,8 +313,8 @@ static mk_status launch(mk_handle *h, const mk_kv_cache *kv, int32_t token, cons
     p.want_logits = want_logits;
     p.logits = logits;
     p.token_out = token_out;
-    p.epoch_base = h->epoch;
-    h->epoch += (uint32_t)mk_points_per_launch(h->desc.n_layers);
+    if (++h->tag == 0) h->tag = 1;  // 0 marks a record never written
+    p.tag = h->tag;
     h->last_stream = (hipStream_t)stream;
     int rc = mk_launch_decode(&p, h->desc.dtype == MK_BF16 ? 1 : 0, h->cooperative, stream);
     return rc ? MK_ERR_HIP : MK_OK;

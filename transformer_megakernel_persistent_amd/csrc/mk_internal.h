@@ -24,8 +24,8 @@
 #define MK_BLOCK_THREADS (64 * (MK_NUM_LOADERS + MK_NUM_CONSUMERS))
 #define MK_MAX_RING 8
 #define MK_LDS_LIMIT 163840
-#define MK_FLAG_REPLICAS 8
-#define MK_FLAG_STRIDE 1024  // words (4 KiB) between progress-word replicas; grid <= 1024
+#define MK_MAX_GRID 1024
+#define MK_MAX_SPLITS 64  // attention splits per KV head (one lane each in the combine)
 
 // Stage kinds with weights; the attention stage streams the KV cache.
 enum { ST_QKV = 0, ST_O = 1, ST_GU = 2, ST_DOWN = 3, ST_LM = 4, ST_NUM = 5 };
@@ -56,14 +56,19 @@ struct MkParams {
     const float *rope;     // [max_seq][d/2][2] (cos, sin)
     // KV cache (caller-owned)
     void *kc, *vc;
-    // scratch
-    float *x, *q, *o, *a, *part;
-    uint32_t *head_cnt;    // [nkv]
-    uint32_t *flags;       // [MK_FLAG_REPLICAS][MK_FLAG_STRIDE] progress epochs
+    // Cross-workgroup values within a launch.  Every record is 64 bits: the
+    // float's bits in the low word, the launch tag in the high word.  Each
+    // dependency point of each layer has its own array, written exactly once
+    // per launch, so a reader polls until the tags equal this launch's tag.
+    uint64_t *ll_xq;       // [L+1][H]   x entering layer l >= 1, and the LM head (l = L)
+    uint64_t *ll_xg;       // [L][H]     x after the O projection
+    uint64_t *ll_q;        // [L][nh*d]  rotated queries
+    uint64_t *ll_kvn;      // [L][nkv][2][d] K and V of this step's position, bf16-rounded
+    uint64_t *ll_part;     // [L][nkv*splits][GQ][d+2] attention partials: o (unnormalised), m, l
+    uint64_t *ll_o;        // [L][nh*d]  attention output
+    uint64_t *ll_a;        // [L][F]     SwiGLU output
+    uint64_t *ll_amax;     // [grid][2]  per-workgroup (max logit, its index)
     uint32_t *err;         // device error word
-    float *amax_val;       // [grid]
-    int32_t *amax_idx;     // [grid]
-    uint32_t *amax_cnt;    // one counter
     // this call
     int32_t token;
     const int32_t *token_dev;
@@ -71,7 +76,7 @@ struct MkParams {
     int32_t want_logits;
     float *logits;
     int32_t *token_out;
-    uint32_t epoch_base;
+    uint32_t tag;          // this launch's tag (never 0)
     int64_t timeout_ticks; // wall-clock ticks (100 MHz) before a grid wait gives up
     uint64_t *trace;       // optional [grid][5L+2][4] stage timeline, or null
 };
@@ -79,9 +84,6 @@ struct MkParams {
 // Error codes written to the device error word.
 #define MK_DEVERR_TIMEOUT 1u
 #define MK_DEVERR_TOKEN 2u
-
-// Publish points per launch: 5 per layer + 1.
-static inline int mk_points_per_launch(int L) { return 5 * L + 1; }
 
 // Host-side launchers implemented in the .hip files.
 #ifdef __cplusplus

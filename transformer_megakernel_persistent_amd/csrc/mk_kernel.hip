@@ -24,16 +24,17 @@
 //
 // All waves step through the same program; each step starts with one
 // s_barrier.  A step is either a data step (consumers use one ring slot) or
-// a stage boundary (consumer 0 finishes the stage, publishes progress, waits
-// for the next stage's producers and the consumers load its input vector).
+// a stage boundary (the consumers finish the stage's epilogue and gather the
+// next stage's input).
 //
-// Cross-workgroup dependencies use per-workgroup progress words instead of a
-// counter barrier: a workgroup publishes epoch_base + k after point k; a
-// consumer of point k polls all progress words.  Every value read by another
-// workgroup within the launch (activations, q, the new K/V row, attention
-// partials, progress words) is written and read with device-scope (sc1)
-// accesses, so no L2 writeback/invalidate is needed.  The publisher waits for
-// its stores (vmcnt 0) before the progress store.
+// Cross-workgroup values travel as tagged records: each value is stored with
+// one 64-bit device-scope store together with the launch's tag, and readers
+// poll the records they need until every tag matches.  Every dependency
+// point of every layer has its own record array, written once per launch,
+// so the data carry their own validity: no flags, counters, store-completion
+// waits or separate flag round trips.  The attention splits write tagged
+// partials; each workgroup then merges a slice of the attention output
+// straight from them (log-sum-exp), with no atomic counter.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -45,18 +46,13 @@ namespace {
 
 typedef uint32_t u4v __attribute__((ext_vector_type(4)));
 typedef float f4v __attribute__((ext_vector_type(4)));
+typedef float f2v __attribute__((ext_vector_type(2)));
 
 #define LDS __attribute__((address_space(3)))
 #define MK_COMPILER_BARRIER() asm volatile("" ::: "memory")
 #define MK_WAIT_VM0() asm volatile("s_waitcnt vmcnt(0)" ::: "memory")
 
 // ---- device-scope (sc1) accesses ----------------------------------------
-__device__ __forceinline__ float ldc(const float *p) {
-    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint64_t ldc64(const void *p) {
-    return __hip_atomic_load((uint64_t *)const_cast<void *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 __device__ __forceinline__ uint32_t ldcu(const uint32_t *p) {
     return __hip_atomic_load(const_cast<uint32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -64,9 +60,6 @@ __device__ __forceinline__ void stc(float *p, float v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void stcu(uint32_t *p, uint32_t v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void stci(int32_t *p, int32_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -239,17 +232,24 @@ __device__ __forceinline__ void piece_load(const LDS unsigned char *p, float (&v
         v[0] = w.x; v[1] = w.y; v[2] = w.z; v[3] = w.w;
     }
 }
-// Same from global memory with device-scope loads (the newly appended row).
-template <int DT>
-__device__ __forceinline__ void piece_load_dev(const unsigned char *p, float (&v)[16 / (DT ? 2 : 4)]) {
-    uint64_t a = ldc64(p), b = ldc64(p + 8);
-    if constexpr (DT == 1) {
-        uint32_t w0 = (uint32_t)a, w1 = (uint32_t)(a >> 32), w2 = (uint32_t)b, w3 = (uint32_t)(b >> 32);
-        v[0] = bf_lo(w0); v[1] = bf_hi(w0); v[2] = bf_lo(w1); v[3] = bf_hi(w1);
-        v[4] = bf_lo(w2); v[5] = bf_hi(w2); v[6] = bf_lo(w3); v[7] = bf_hi(w3);
-    } else {
-        v[0] = __uint_as_float((uint32_t)a); v[1] = __uint_as_float((uint32_t)(a >> 32));
-        v[2] = __uint_as_float((uint32_t)b); v[3] = __uint_as_float((uint32_t)(b >> 32));
+
+// Poll N 16-byte pieces (two tagged records each) at byte offsets off(u)
+// of rs, for the lanes' bits set in mask, until both tags of every piece
+// equal tag; pieces already valid are not read again.  on_fail() is called
+// after each incomplete round and ends the wait by returning false.
+template <int N, class O, class F>
+__device__ __forceinline__ bool poll16(__amdgpu_buffer_rsrc_t rs, O &&off, uint32_t mask, u4v (&v)[N], uint32_t tag,
+                                       F &&on_fail) {
+    uint32_t pend = mask;
+    while (true) {
+#pragma unroll
+        for (int u = 0; u < N; ++u)
+            if (pend & (1u << u)) v[u] = ld16c(rs, off(u));
+#pragma unroll
+        for (int u = 0; u < N; ++u)
+            if ((pend & (1u << u)) && v[u].y == tag && v[u].w == tag) pend &= ~(1u << u);
+        if (!__any(pend != 0u)) return true;
+        if (!on_fail()) return false;
     }
 }
 
@@ -301,8 +301,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
     LDS float *cst = outv + p.lds_out_rows;
     LDS float *xown = cst + MK_NUM_CONSUMERS * GQ * (d + 2);
     LDS float *ssp = xown + 64;
-    volatile LDS int *ctl = (volatile LDS int *)(ssp + MK_NUM_CONSUMERS);  // [0] go step, [1] abort step,
-    // [2] combine-job step, [3] this workgroup combines, [4..7] per-consumer combine done
+    volatile LDS int *ctl = (volatile LDS int *)(ssp + MK_NUM_CONSUMERS);  // [1] abort step, [8] consumer meetings
 
     Geo g;
     make_geo(p, w, g);
@@ -333,7 +332,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
         }
     };
 
-    if (tid == 0) { ctl[0] = -1; ctl[1] = 0; ctl[2] = -1; ctl[3] = 0; ctl[4] = ctl[5] = ctl[6] = ctl[7] = -1; }
+    if (tid == 0) { ctl[0] = -1; ctl[1] = 0; ctl[8] = 0; }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
@@ -468,55 +467,87 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
         ++step;
     };
 
-    // Progress publication (consumer 0, after its stores completed).
-    // The progress words exist in MK_FLAG_REPLICAS copies, MK_FLAG_STRIDE words
-    // apart; a waiter polls the copy of its XCD (w % 8), so the polling of
-    // the grid is spread over several memory channels instead of a few lines.
-    // Publishing waits for its own stores again before polling starts.
-    auto publish = [&](int k) {
-        MK_WAIT_VM0();  // every store of the stage is visible before the progress word
-        if (lane < MK_FLAG_REPLICAS) stcu(p.flags + (size_t)lane * MK_FLAG_STRIDE + w, p.epoch_base + (uint32_t)k);
-        MK_WAIT_VM0();
+    // ---- tagged records ----------------------------------------------------
+    // A producer stores {value, tag} as one 64-bit device-scope store; a
+    // reader polls the records it needs until every tag is this launch's.
+    // No flag, no store-completion wait, no second load: the data carry
+    // their own validity.
+    const uint32_t tag = p.tag;
+    auto stll = [&](uint64_t *dst, float v) {
+        __hip_atomic_store(dst, ((uint64_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     };
-    // Wait until every workgroup published point k.  Consumer 0 polls; the
-    // other consumers wait for its go signal in LDS.  Returns false on abort.
-    auto wait_all = [&](int k) -> bool {
-        if (c == 0) {
-            const uint32_t target = p.epoch_base + (uint32_t)k;
-            const int64_t t_start = wall_clock64();
-            bool good = true;
-            const __amdgpu_buffer_rsrc_t rf = rsrc(p.flags + (size_t)(w % MK_FLAG_REPLICAS) * MK_FLAG_STRIDE, (uint32_t)G * 4u);
-            while (true) {
-                bool mine = true;
-                u4v fv[4];
-#pragma unroll
-                for (int k4 = 0; k4 < 4; ++k4) fv[k4] = ld16c(rf, (uint32_t)(lane + 64 * k4) * 16u);
-#pragma unroll
-                for (int k4 = 0; k4 < 4; ++k4) {
-                    const int i0 = (lane + 64 * k4) * 4;
-                    mine &= i0 + 0 >= G || (int32_t)(fv[k4].x - target) >= 0;
-                    mine &= i0 + 1 >= G || (int32_t)(fv[k4].y - target) >= 0;
-                    mine &= i0 + 2 >= G || (int32_t)(fv[k4].z - target) >= 0;
-                    mine &= i0 + 3 >= G || (int32_t)(fv[k4].w - target) >= 0;
-                }
-                if (__all(mine)) break;
-                if (ldcu(p.err) != 0u || wall_clock64() - t_start > p.timeout_ticks) {
-                    if (lane == 0) stcu(p.err, ldcu(p.err) | MK_DEVERR_TIMEOUT);
-                    good = false;
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(1);
-            }
-            MK_COMPILER_BARRIER();
+    int64_t poll_start = 0;
+    // After a failed poll round: false once this workgroup aborted, the wait
+    // timed out or the device error word is set (then the abort is marked).
+    auto poll_ok = [&]() -> bool {
+        if (ctl[1] != 0) return false;
+        const bool timed_out = wall_clock64() - poll_start > p.timeout_ticks;
+        if (timed_out || ldcu(p.err) != 0u) {
             if (lane == 0) {
-                if (!good) ctl[1] = step;
-                ctl[0] = step;
+                if (timed_out) __hip_atomic_fetch_or(p.err, MK_DEVERR_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                ctl[1] = step;
             }
-            return good;
+            return false;
         }
-        while (ctl[0] != step) __builtin_amdgcn_s_sleep(1);
-        MK_COMPILER_BARRIER();
+        __builtin_amdgcn_s_sleep(1);
+        return true;
+    };
+    // The consumers meet here after each gather.  An LDS counter, not
+    // s_barrier: the loaders take no part, so a loader stalled on issuing
+    // loads delays nobody.
+    int nsync = 0;
+    auto csync = [&]() -> bool {
+        ++nsync;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+        if (lane == 0) __hip_atomic_fetch_add((LDS int *)&ctl[8], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        while (ctl[8] < MK_NUM_CONSUMERS * nsync) {
+            if (ctl[1] != 0) return false;
+            __builtin_amdgcn_s_sleep(1);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
         return ctl[1] == 0;
+    };
+    // Gather n (even) tagged elements into vec (times gain, if given),
+    // zero-padded to pad.  The four consumers take interleaved 16-byte pieces
+    // (two records), so the workgroup reads each element once; ssp[c] gets
+    // this consumer's share of the sum of squares, summed in a fixed order.
+    auto gather_to = [&](LDS float *dst, const uint64_t *src, int n, const float *gain, int pad) -> bool {
+        const int npc = n >> 1;
+        const __amdgpu_buffer_rsrc_t rs = rsrc(src, (uint32_t)n * 8u);
+        float ss = 0.f;
+        poll_start = wall_clock64();
+        bool good = true;
+        for (int base = ct; base < npc; base += 256 * 8) {
+            uint32_t mask = 0;
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (base + u * 256 < npc) mask |= 1u << u;
+            u4v v[8];
+            if (!poll16<8>(rs, [&](int u) { return (uint32_t)(base + u * 256) * 16u; }, mask, v, tag, poll_ok)) {
+                good = false;
+                break;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                if (mask & (1u << u)) {
+                    const int e = 2 * (base + u * 256);
+                    const float x0 = __uint_as_float(v[u].x), x1 = __uint_as_float(v[u].z);
+                    ss = fmaf(x0, x0, ss);
+                    ss = fmaf(x1, x1, ss);
+                    const float g0 = gain ? gain[e] : 1.f, g1 = gain ? gain[e + 1] : 1.f;
+                    *(LDS f2v *)(dst + e) = f2v{g0 * x0, g1 * x1};
+                }
+            }
+        }
+        for (int i = n + ct; i < pad; i += 256) dst[i] = 0.f;
+        ss = wave_sum(ss);
+        if (lane == 0) ssp[c] = ss;
+        if (!good) return false;
+        return csync();
+    };
+    auto gather = [&](const uint64_t *src, int n, const float *gain, int pad) -> bool {
+        return gather_to(vec, src, n, gain, pad);
     };
 
     // ---- optional stage timeline (consumer 0, lane 0) ----
@@ -572,19 +603,6 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
         for (int i = n + ct; i < pad; i += 256) vec[i] = 0.f;
         ss = wave_sum(ss);
         if (lane == 0) ssp[c] = ss;
-    };
-    auto load_plain = [&](const float *src, int n, int pad) {
-        const int nqd = n / 4;
-        const __amdgpu_buffer_rsrc_t rs = rsrc(src, (uint32_t)n * 4u);
-        for (int base = ct; base < nqd; base += 256 * 8) {
-            u4v v[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = ld16c(rs, (uint32_t)(base + u * 256) * 16u);
-#pragma unroll
-            for (int u = 0; u < 8; ++u)
-                if (base + u * 256 < nqd) *(LDS f4v *)(vec + 4 * (base + u * 256)) = as_f4(v[u]);
-        }
-        for (int i = n + ct; i < pad; i += 256) vec[i] = 0.f;
     };
     auto inv_lds = [&](int n) {
         const float ss = ssp[0] + ssp[1] + ssp[2] + ssp[3];
@@ -819,65 +837,85 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
                 const float a0 = y0 * c0 - y1 * s0, b0 = y0 * s0 + y1 * c0;
                 const float a1 = y2 * c1 - y3 * s1, b1 = y2 * s1 + y3 * c1;
                 if (isq) {
-                    float *qd = p.q + (size_t)head * d;
-                    stc(qd + m0, a0);
-                    stc(qd + m0 + 1, a1);
-                    stc(qd + m0 + d / 2, b0);
-                    stc(qd + m0 + 1 + d / 2, b1);
+                    uint64_t *qd = p.ll_q + (size_t)l * nqd + (size_t)head * d;
+                    stll(qd + m0, a0);
+                    stll(qd + m0 + 1, a1);
+                    stll(qd + m0 + d / 2, b0);
+                    stll(qd + m0 + 1 + d / 2, b1);
                 } else {
                     unsigned char *row = (unsigned char *)p.kc + ((size_t)l * p.nkv + head) * head_bytes + (size_t)P * d * EB;
+                    uint64_t *kn = p.ll_kvn + ((size_t)l * p.nkv + head) * 2 * d;
                     if constexpr (DT == 1) {
-                        stcu((uint32_t *)(row + m0 * 2), f2bf(a0) | (f2bf(a1) << 16));
-                        stcu((uint32_t *)(row + (m0 + d / 2) * 2), f2bf(b0) | (f2bf(b1) << 16));
+                        const uint32_t ba0 = f2bf(a0), ba1 = f2bf(a1), bb0 = f2bf(b0), bb1 = f2bf(b1);
+                        stcu((uint32_t *)(row + m0 * 2), ba0 | (ba1 << 16));
+                        stcu((uint32_t *)(row + (m0 + d / 2) * 2), bb0 | (bb1 << 16));
+                        stll(kn + m0, __uint_as_float(ba0 << 16));
+                        stll(kn + m0 + 1, __uint_as_float(ba1 << 16));
+                        stll(kn + m0 + d / 2, __uint_as_float(bb0 << 16));
+                        stll(kn + m0 + 1 + d / 2, __uint_as_float(bb1 << 16));
                     } else {
                         stc((float *)row + m0, a0);
                         stc((float *)row + m0 + 1, a1);
                         stc((float *)row + m0 + d / 2, b0);
                         stc((float *)row + m0 + 1 + d / 2, b1);
+                        stll(kn + m0, a0);
+                        stll(kn + m0 + 1, a1);
+                        stll(kn + m0 + d / 2, b0);
+                        stll(kn + m0 + 1 + d / 2, b1);
                     }
                 }
             } else if (gr0 < nqd + 2 * nk) {
                 const int r = gr0 - nqd - nk;
                 const int head = r / d, e = r % d;
                 unsigned char *row = (unsigned char *)p.vc + ((size_t)l * p.nkv + head) * head_bytes + (size_t)P * d * EB;
+                uint64_t *vn = p.ll_kvn + ((size_t)l * p.nkv + head) * 2 * d + d;
                 if constexpr (DT == 1) {
-                    stcu((uint32_t *)(row + e * 2), f2bf(y0) | (f2bf(y1) << 16));
-                    stcu((uint32_t *)(row + e * 2 + 4), f2bf(y2) | (f2bf(y3) << 16));
+                    const uint32_t c0 = f2bf(y0), c1 = f2bf(y1), c2 = f2bf(y2), c3 = f2bf(y3);
+                    stcu((uint32_t *)(row + e * 2), c0 | (c1 << 16));
+                    stcu((uint32_t *)(row + e * 2 + 4), c2 | (c3 << 16));
+                    stll(vn + e, __uint_as_float(c0 << 16));
+                    stll(vn + e + 1, __uint_as_float(c1 << 16));
+                    stll(vn + e + 2, __uint_as_float(c2 << 16));
+                    stll(vn + e + 3, __uint_as_float(c3 << 16));
                 } else {
                     stc((float *)row + e, y0);
                     stc((float *)row + e + 1, y1);
                     stc((float *)row + e + 2, y2);
                     stc((float *)row + e + 3, y3);
+                    stll(vn + e, y0);
+                    stll(vn + e + 1, y1);
+                    stll(vn + e + 2, y2);
+                    stll(vn + e + 3, y3);
                 }
             }
         }
     };
-    auto epi_residual = [&](int st) {  // O or DOWN: x += out for the workgroup's rows
+    auto epi_residual = [&](int st, uint64_t *xdst) {  // O or DOWN: x += out for the workgroup's rows
         for (int i = lane; i < g.units[st] * 4; i += 64) {
             const int r = g.unit0[st] * 4 + i;
             if (r < p.H) {
                 const float xn = xown[i] + outv[i];
                 xown[i] = xn;
-                stc(p.x + r, xn);
+                stll(xdst + r, xn);
             }
         }
     };
-    auto epi_gu = [&](float inv) {
+    auto epi_gu = [&](int l, float inv) {
+        uint64_t *adst = p.ll_a + (size_t)l * p.F;
         for (int m = lane; m < g.units[ST_GU] * 2; m += 64) {
             const int f = g.unit0[ST_GU] * 2 + m;
             if (f < p.F) {
                 const float gv = outv[2 * m] * inv, uv = outv[2 * m + 1] * inv;
-                stc(p.a + f, gv / (1.0f + __expf(-gv)) * uv);
+                stll(adst + f, gv / (1.0f + __expf(-gv)) * uv);
             }
         }
     };
-    // Attention epilogue, part 1 (consumer 0): merge the four consumers'
-    // states into this split's partial (o unnormalised, m, l), publish it with
-    // device-scope stores and count the split in.  Returns true in the last
-    // split to arrive for this KV head.
-    constexpr int PSTRIDE = DH + 4;  // partial record: o[DH], m, l, pad (16-byte aligned)
-    auto attn_partial = [&]() -> bool {
-        float *part = p.part + ((size_t)kvj * S + kvs) * GQ * PSTRIDE;
+    // Attention epilogue (consumer 0): merge the four consumers' states into
+    // this split's partial record per query head: o (unnormalised over the
+    // split's positions), running max m, sum l.
+    constexpr int PREC = DH + 2;  // partial record: o[DH], m, l
+    auto attn_partial = [&](int l) {
+        uint64_t *part = p.ll_part + (((size_t)l * p.nkv + kvj) * S + kvs) * GQ * PREC;
         constexpr int cs = DH + 2;  // consumer-state record in LDS: o[DH], m, l
         for (int h = 0; h < GQ; ++h) {
             float M = -INFINITY;
@@ -892,68 +930,60 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
             for (int e = lane; e < d; e += 64) {
                 float o = 0.f;
                 for (int cc = 0; cc < MK_NUM_CONSUMERS; ++cc) o = fmaf(wgt[cc], cst[(cc * GQ + h) * cs + e], o);
-                stc(part + h * PSTRIDE + e, o);
+                stll(part + h * PREC + e, o);
             }
-            if (lane == 0) { stc(part + h * PSTRIDE + d, M); stc(part + h * PSTRIDE + d + 1, Lsum); }
+            if (lane == 0) {
+                stll(part + h * PREC + d, M);
+                stll(part + h * PREC + d + 1, Lsum);
+            }
         }
-        MK_WAIT_VM0();
-        uint32_t old = 0;
-        if (lane == 0) old = __hip_atomic_fetch_add(p.head_cnt + kvj, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        old = __builtin_amdgcn_readfirstlane(old);
-        return old == (uint32_t)(S - 1);
     };
-    // Part 2 (last arriver, one head per call): log-sum-exp merge of the S
-    // split partials of head kvj*GQ + h into o.  Lane (sub, e4) covers head
-    // dims 4*e4..4*e4+3 of the splits s = b + sub + nsub*u; each batch of
-    // eight splits per lane is one memory round trip, merged online.
-    auto attn_combine_head = [&](int h) {
-        constexpr int Q4 = DH / 4, NSUB = 64 / Q4;
-        const int sub = lane / Q4, e4 = lane % Q4;
-        const float *pb = p.part + (size_t)kvj * S * GQ * PSTRIDE;
-        const __amdgpu_buffer_rsrc_t rp = rsrc(pb, (uint32_t)((size_t)S * GQ * PSTRIDE * 4));
-        float M = -INFINITY, Lacc = 0.f;
-        f4v acc = {0.f, 0.f, 0.f, 0.f};
-        for (int b = 0; b < S; b += NSUB * 8) {
-            u4v ov[8], ml[8];
+    // Log-sum-exp merge of the splits (consumer 0): workgroup w produces
+    // attention-output elements [w*N/G, (w+1)*N/G) of N = n_heads*d.  Lane s
+    // reads split s's (m, l) and the element's o value; the weights are
+    // exp(m_s - max m) and the result sum(w_s o_s) / sum(w_s l_s).
+    auto combine_slice = [&](int l) -> bool {
+        const int N = p.nh * d;
+        const int e_0 = (int)((int64_t)w * N / G), e_1 = (int)((int64_t)(w + 1) * N / G);
+        const __amdgpu_buffer_rsrc_t rp =
+            rsrc(p.ll_part + (size_t)l * p.nkv * S * GQ * PREC, (uint32_t)((size_t)p.nkv * S * GQ * PREC * 8));
+        const bool ln = lane < S;
+        poll_start = wall_clock64();
+        int cur_h = -1;
+        float M = 0.f, Ls = 1.f;
+        for (int eb = e_0; eb < e_1; eb += 4) {
+            uint32_t mask = 0;
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const uint32_t rec = (uint32_t)(((b + sub + NSUB * u) * GQ + h) * PSTRIDE);
-                ov[u] = ld16c(rp, (rec + 4 * e4) * 4u);
-                ml[u] = ld16c(rp, (rec + d) * 4u);
-            }
-            float mb = -INFINITY;
+            for (int u = 0; u < 4; ++u)
+                if (eb + u < e_1 && ln) mask |= 3u << (2 * u);
+            // piece 2u: (m, l) of element eb+u's head; piece 2u+1: the pair holding its o value
+            auto off = [&](int i) {
+                const int e = eb + i / 2, h = e / d;
+                const uint32_t rec = (uint32_t)(((h / GQ) * S + lane) * GQ + h % GQ) * PREC;
+                return (rec + ((i & 1) ? ((e % d) & ~1) : d)) * 8u;
+            };
+            u4v v[8];
+            if (!poll16<8>(rp, off, mask, v, tag, poll_ok)) return false;
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
-                if (b + sub + NSUB * u < S) mb = fmaxf(mb, __uint_as_float(ml[u].x));
-            const float mn = fmaxf(M, wave_max(mb));
-            if (mn == -INFINITY) continue;  // wave-uniform: no non-empty split yet
-            const float alpha = M == -INFINITY ? 0.f : __expf(M - mn);
-            acc *= alpha;
-            Lacc *= alpha;
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const float ms = __uint_as_float(ml[u].x);
-                if (b + sub + NSUB * u < S && ms != -INFINITY) {
-                    const float wgt = __expf(ms - mn);
-                    acc += wgt * as_f4(ov[u]);
-                    Lacc = fmaf(wgt, __uint_as_float(ml[u].y), Lacc);
+            for (int u = 0; u < 4; ++u) {
+                const int e = eb + u;
+                if (e < e_1) {  // wave-uniform
+                    const int h = e / d, dim = e % d;
+                    const float ms = ln ? __uint_as_float(v[2 * u].x) : -INFINITY;
+                    const bool new_head = h != cur_h;  // wave-uniform
+                    if (new_head) M = wave_max(ms);
+                    const float wgt = ms == -INFINITY ? 0.f : __expf(ms - M);
+                    if (new_head) {
+                        Ls = wave_sum(ln ? wgt * __uint_as_float(v[2 * u].z) : 0.f);
+                        cur_h = h;
+                    }
+                    const float ov = ln ? __uint_as_float((dim & 1) ? v[2 * u + 1].z : v[2 * u + 1].x) : 0.f;
+                    const float os = wave_sum(wgt * ov);
+                    if (lane == 0) stll(p.ll_o + (size_t)l * N + e, os / Ls);
                 }
             }
-            M = mn;
         }
-        acc.x = xgroup_sum<Q4>(acc.x);
-        acc.y = xgroup_sum<Q4>(acc.y);
-        acc.z = xgroup_sum<Q4>(acc.z);
-        acc.w = xgroup_sum<Q4>(acc.w);
-        Lacc = xgroup_sum<Q4>(Lacc);
-        if (sub == 0) {
-            float *od = p.o + ((size_t)kvj * GQ + h) * d + 4 * e4;
-            const float invl = 1.0f / Lacc;
-            stc(od + 0, acc.x * invl);
-            stc(od + 1, acc.y * invl);
-            stc(od + 2, acc.z * invl);
-            stc(od + 3, acc.w * invl);
-        }
+        return true;
     };
     auto epi_lm = [&](float inv) {
         float best = -INFINITY;
@@ -973,34 +1003,32 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
             const int oi = __shfl_xor(besti, m);
             if (ob > best || (ob == best && oi < besti)) { best = ob; besti = oi; }
         }
-        if (lane == 0) { stc(p.amax_val + w, best); stci(p.amax_idx + w, besti); }
-        MK_WAIT_VM0();
-        uint32_t old = 0;
-        if (lane == 0) old = __hip_atomic_fetch_add(p.amax_cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        old = __builtin_amdgcn_readfirstlane(old);
-        if (old != (uint32_t)(G - 1)) return;
-        MK_COMPILER_BARRIER();
+        if (lane == 0) {
+            stll(p.ll_amax + 2 * (size_t)w, best);
+            stll(p.ll_amax + 2 * (size_t)w + 1, __int_as_float(besti));
+        }
+        if (w != 0) return;
+        // Workgroup 0 reduces the G (max, index) records.  This is the last
+        // wait of the step; if it fails the error word is already set and the
+        // token is not written.
+        const __amdgpu_buffer_rsrc_t ra = rsrc(p.ll_amax, (uint32_t)G * 16u);
+        poll_start = wall_clock64();
         best = -INFINITY;
         besti = 0x7FFFFFFF;
-        {
-            const __amdgpu_buffer_rsrc_t rv = rsrc(p.amax_val, (uint32_t)G * 4u);
-            const __amdgpu_buffer_rsrc_t ri = rsrc(p.amax_idx, (uint32_t)G * 4u);
-            u4v vv[4], iv[4];
+        for (int k0 = 0; k0 < 16; k0 += 8) {
+            uint32_t mask = 0;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                vv[k] = ld16c(rv, (uint32_t)(lane + 64 * k) * 16u);
-                iv[k] = ld16c(ri, (uint32_t)(lane + 64 * k) * 16u);
-            }
+            for (int k = 0; k < 8; ++k)
+                if (lane + 64 * (k0 + k) < G) mask |= 1u << k;
+            u4v v[8];
+            if (!poll16<8>(ra, [&](int k) { return (uint32_t)(lane + 64 * (k0 + k)) * 16u; }, mask, v, tag, poll_ok))
+                return;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const uint32_t vs[4] = {vv[k].x, vv[k].y, vv[k].z, vv[k].w};
-                const uint32_t is[4] = {iv[k].x, iv[k].y, iv[k].z, iv[k].w};
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    if ((lane + 64 * k) * 4 + t >= G) continue;
-                    const float v = __uint_as_float(vs[t]);
-                    const int ix = (int)is[t];
-                    if (v > best || (v == best && ix < besti)) { best = v; besti = ix; }
+            for (int k = 0; k < 8; ++k) {
+                if (mask & (1u << k)) {
+                    const float vb = __uint_as_float(v[k].x);
+                    const int ix = (int)v[k].z;
+                    if (vb > best || (vb == best && ix < besti)) { best = vb; besti = ix; }
                 }
             }
         }
@@ -1009,29 +1037,52 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
             const int oi = __shfl_xor(besti, m);
             if (ob > best || (ob == best && oi < besti)) { best = ob; besti = oi; }
         }
-        if (lane == 0) {
-            p.token_out[0] = besti;
-            stcu(p.amax_cnt, 0u);
-        }
+        if (lane == 0) p.token_out[0] = besti;
     };
 
 
     // ---- the program ----
     const int nq = p.nh * d;
+    // The register path's input slice (gain (.) x) from the gathered vector.
+    auto regs_from_vec = [&](float (&hr)[4][EPL]) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int e = 0; e < EPL; e += 4) {
+                const f4v t = *(const LDS f4v *)(vec + q * EPC + lane * EPL + e);
+                hr[q][e] = t.x;
+                hr[q][e + 1] = t.y;
+                hr[q][e + 2] = t.z;
+                hr[q][e + 3] = t.w;
+            }
+    };
+    // The GEMV data steps of stage st, input in vec (gathered) or, for the
+    // register path, loaded from it.
+    auto gemv_from_vec = [&](int st, int l, int b) {
+        if (p.st[st].rbp == 4) {
+            float hr[4][EPL];
+            regs_from_vec(hr);
+            stamp(b, 3);
+            gemv_reg_steps(st, l, hr);
+        } else {
+            stamp(b, 3);
+            gemv_lds_steps(st, l);
+        }
+    };
     for (int l = 0; l < L && ok; ++l) {
         // ===== stage QKV(l); boundary: [epilogue DOWN(l-1)] + input x =====
         float inv_q = 0.f;
         {
             barrier();
             stamp(5 * l, 0);
-            const void *erow = nullptr;
+            const float *gain = p.g_attn + (size_t)l * p.H;
             if (l == 0) {
                 int tok = p.token_dev ? p.token_dev[0] : p.token;
                 if (tok < 0 || tok >= p.V) {
-                    if (ct == 0) stcu(p.err, ldcu(p.err) | MK_DEVERR_TOKEN);
+                    if (ct == 0) __hip_atomic_fetch_or(p.err, MK_DEVERR_TOKEN, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     tok = 0;
                 }
-                erow = (const unsigned char *)p.embed + (size_t)tok * p.H * EB;
+                const void *erow = (const unsigned char *)p.embed + (size_t)tok * p.H * EB;
                 for (int i = ct; i < g.units[ST_O] * 4; i += 256) {
                     const int r = g.unit0[ST_O] * 4 + i;
                     float xv = 0.f;
@@ -1041,27 +1092,27 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
                     }
                     xown[i] = xv;
                 }
-            } else {
-                if (c == 0) {
-                    epi_residual(ST_DOWN);
-                    publish(5 * (l - 1) + 5);
+                if (p.st[ST_QKV].rbp == 4) {
+                    float hr[4][EPL];
+                    inv_q = inv_of(load_direct(nullptr, erow, gain, hr), p.H);
+                    stamp(5 * l, 3);
+                    gemv_reg_steps(ST_QKV, l, hr);
+                } else {
+                    load_normed(nullptr, erow, gain, p.H, p.st[ST_QKV].rbp * EPC);
+                    ok = csync();
+                    if (!ok) break;
+                    inv_q = inv_lds(p.H);
+                    stamp(5 * l, 3);
+                    gemv_lds_steps(ST_QKV, l);
                 }
-                stamp(5 * l, 1);
-                ok = wait_all(5 * (l - 1) + 5);
-                stamp(5 * l, 2);
-            }
-            if (!ok) break;
-            const float *gain = p.g_attn + (size_t)l * p.H;
-            if (p.st[ST_QKV].rbp == 4) {
-                float hr[4][EPL];
-                inv_q = inv_of(load_direct(l == 0 ? nullptr : p.x, erow, gain, hr), p.H);
-                stamp(5 * l, 3);
-                gemv_reg_steps(ST_QKV, l, hr);
             } else {
-                load_normed(l == 0 ? nullptr : p.x, erow, gain, p.H, p.st[ST_QKV].rbp * EPC);
-                stamp(5 * l, 3);
-                gemv_lds_steps(ST_QKV, l);
-                inv_q = -1.f;  // from ssp at the epilogue
+                if (c == 0) epi_residual(ST_DOWN, p.ll_xq + (size_t)l * p.H);
+                stamp(5 * l, 1);
+                ok = gather(p.ll_xq + (size_t)l * p.H, p.H, gain, p.st[ST_QKV].rbp * EPC);
+                stamp(5 * l, 2);
+                if (!ok) break;
+                inv_q = inv_lds(p.H);
+                gemv_from_vec(ST_QKV, l, 5 * l);
             }
         }
 
@@ -1069,28 +1120,29 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
         {
             barrier();
             stamp(5 * l + 1, 0);
-            if (c == 0) {
-                epi_qkv(l, inv_q >= 0.f ? inv_q : inv_lds(p.H));
-                publish(5 * l + 1);
-            }
+            if (c == 0) epi_qkv(l, inv_q);
             stamp(5 * l + 1, 1);
             if (has_split) {
-                ok = wait_all(5 * l + 1);
-                stamp(5 * l + 1, 2);
-                if (!ok) break;
+                // This group's rotated queries and, in the last split, the K/V
+                // row of position pos (bf16-rounded like the cache) into LDS;
+                // vec is free here (the QKV input is no longer needed).
+                ok = gather_to(vec, p.ll_q + (size_t)l * nq + (size_t)kvj * GQ * d, GQ * d, nullptr, GQ * d);
+                if (ok && is_last)
+                    ok = gather_to(vec + GQ * d, p.ll_kvn + ((size_t)l * p.nkv + kvj) * 2 * d, 2 * d, nullptr, 2 * d);
                 AttnState A;
-                const float *qb = p.q + (size_t)kvj * GQ * d;
 #pragma unroll
                 for (int h = 0; h < GQ; ++h)
 #pragma unroll
-                    for (int e = 0; e < EPL; ++e) A.qr[h][e] = ldc(qb + h * d + e0 + e);
+                    for (int e = 0; e < EPL; ++e) A.qr[h][e] = vec[h * d + e0 + e];
                 if (c == 0 && is_last) {
-                    const unsigned char *krow = (const unsigned char *)p.kc + ((size_t)l * p.nkv + kvj) * head_bytes + (size_t)P * d * EB;
-                    const unsigned char *vrow = (const unsigned char *)p.vc + ((size_t)l * p.nkv + kvj) * head_bytes + (size_t)P * d * EB;
-                    const int off = (lane < LPP ? lane : 0) * 16;
-                    piece_load_dev<DT>(krow + off, A.kp);
-                    piece_load_dev<DT>(vrow + off, A.vp);
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) {
+                        A.kp[e] = vec[GQ * d + e0 + e];
+                        A.vp[e] = vec[GQ * d + d + e0 + e];
+                    }
                 }
+                stamp(5 * l + 1, 2);
+                if (!ok) break;
 #pragma unroll
                 for (int h = 0; h < GQ; ++h) {
                     A.am[h] = -INFINITY;
@@ -1124,46 +1176,20 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
             }
         }
 
-        // ===== stage O(l); boundary: epilogue attention(l) + input o =====
+        // ===== stage O(l); boundary: attention partials, combine, input o =====
         {
             barrier();
             stamp(5 * l + 2, 0);
-            if (has_split) {
-                if (c == 0) {
-                    const bool last = attn_partial();
-                    ctl[3] = last ? 1 : 0;
-                    ctl[2] = step;
-                } else {
-                    while (ctl[2] != step) __builtin_amdgcn_s_sleep(1);
-                }
-                MK_COMPILER_BARRIER();
-                if (ctl[3]) {
-                    for (int h = c; h < GQ; h += MK_NUM_CONSUMERS) attn_combine_head(h);
-                    MK_WAIT_VM0();
-                    if (lane == 0) ctl[4 + c] = step;
-                    if (c == 0) {
-                        for (int cc = 1; cc < MK_NUM_CONSUMERS; ++cc)
-                            while (ctl[4 + cc] != step) __builtin_amdgcn_s_sleep(1);
-                        MK_COMPILER_BARRIER();
-                        if (lane == 0) stcu(p.head_cnt + kvj, 0u);
-                    }
-                }
+            bool mine = true;
+            if (c == 0) {
+                if (has_split) attn_partial(l);
+                mine = combine_slice(l);
             }
-            if (c == 0) publish(5 * l + 2);
             stamp(5 * l + 2, 1);
-            ok = wait_all(5 * l + 2);
+            ok = mine && gather(p.ll_o + (size_t)l * nq, nq, nullptr, p.st[ST_O].rbp * EPC);
             stamp(5 * l + 2, 2);
             if (!ok) break;
-            if (p.st[ST_O].rbp == 4) {
-                float hr[4][EPL];
-                load_direct(p.o, nullptr, nullptr, hr);
-                stamp(5 * l + 2, 3);
-                gemv_reg_steps(ST_O, l, hr);
-            } else {
-                load_plain(p.o, nq, p.st[ST_O].rbp * EPC);
-                stamp(5 * l + 2, 3);
-                gemv_lds_steps(ST_O, l);
-            }
+            gemv_from_vec(ST_O, l, 5 * l + 2);
         }
 
         // ===== stage gate/up(l); boundary: epilogue O(l) + input x =====
@@ -1171,81 +1197,48 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
         {
             barrier();
             stamp(5 * l + 3, 0);
-            if (c == 0) {
-                epi_residual(ST_O);
-                publish(5 * l + 3);
-            }
+            if (c == 0) epi_residual(ST_O, p.ll_xg + (size_t)l * p.H);
             stamp(5 * l + 3, 1);
-            ok = wait_all(5 * l + 3);
+            ok = gather(p.ll_xg + (size_t)l * p.H, p.H, p.g_ffn + (size_t)l * p.H, p.st[ST_GU].rbp * EPC);
             stamp(5 * l + 3, 2);
             if (!ok) break;
-            const float *gain = p.g_ffn + (size_t)l * p.H;
-            if (p.st[ST_GU].rbp == 4) {
-                float hr[4][EPL];
-                inv_g = inv_of(load_direct(p.x, nullptr, gain, hr), p.H);
-                stamp(5 * l + 3, 3);
-                gemv_reg_steps(ST_GU, l, hr);
-            } else {
-                load_normed(p.x, nullptr, gain, p.H, p.st[ST_GU].rbp * EPC);
-                stamp(5 * l + 3, 3);
-                gemv_lds_steps(ST_GU, l);
-                inv_g = -1.f;
-            }
+            inv_g = inv_lds(p.H);
+            gemv_from_vec(ST_GU, l, 5 * l + 3);
         }
 
         // ===== stage down(l); boundary: epilogue gate/up(l) + input a =====
         {
             barrier();
             stamp(5 * l + 4, 0);
-            if (c == 0) {
-                epi_gu(inv_g >= 0.f ? inv_g : inv_lds(p.H));
-                publish(5 * l + 4);
-            }
+            if (c == 0) epi_gu(l, inv_g);
             stamp(5 * l + 4, 1);
-            ok = wait_all(5 * l + 4);
+            ok = gather(p.ll_a + (size_t)l * p.F, p.F, nullptr, p.st[ST_DOWN].rbp * EPC);
             stamp(5 * l + 4, 2);
             if (!ok) break;
-            load_plain(p.a, p.F, p.st[ST_DOWN].rbp * EPC);
             stamp(5 * l + 4, 3);
             gemv_lds_steps(ST_DOWN, l);
         }
     }
     if (ok && LOGITS) {
         // ===== LM head; boundary: epilogue DOWN(L-1) + input x =====
-        float inv_lm = 0.f;
         barrier();
         stamp(5 * L, 0);
-        if (c == 0) {
-            epi_residual(ST_DOWN);
-            publish(5 * (L - 1) + 5);
-        }
+        if (c == 0) epi_residual(ST_DOWN, p.ll_xq + (size_t)L * p.H);
         stamp(5 * L, 1);
-        ok = wait_all(5 * (L - 1) + 5);
+        ok = gather(p.ll_xq + (size_t)L * p.H, p.H, p.g_final, p.st[ST_LM].rbp * EPC);
         stamp(5 * L, 2);
         if (ok) {
-            if (p.st[ST_LM].rbp == 4) {
-                float hr[4][EPL];
-                inv_lm = inv_of(load_direct(p.x, nullptr, p.g_final, hr), p.H);
-                stamp(5 * L, 3);
-                gemv_reg_steps(ST_LM, L, hr);
-            } else {
-                load_normed(p.x, nullptr, p.g_final, p.H, p.st[ST_LM].rbp * EPC);
-                stamp(5 * L, 3);
-                gemv_lds_steps(ST_LM, L);
-                inv_lm = -1.f;
-            }
+            const float inv_lm = inv_lds(p.H);
+            gemv_from_vec(ST_LM, L, 5 * L);
             barrier();
             stamp(5 * L + 1, 0);
-            if (c == 0) epi_lm(inv_lm >= 0.f ? inv_lm : inv_lds(p.H));
+            if (c == 0) epi_lm(inv_lm);
             stamp(5 * L + 1, 1);
         }
     } else if (ok) {
         barrier();
         stamp(5 * L + 1, 0);
-        if (c == 0) {
-            epi_residual(ST_DOWN);
-            publish(5 * (L - 1) + 5);
-        }
+        if (c == 0) epi_residual(ST_DOWN, p.ll_xq + (size_t)L * p.H);
         stamp(5 * L + 1, 1);
     }
     if (!ok) {
