@@ -150,25 +150,42 @@ static mk_status create_impl(const mk_model_desc *desc, const mk_weight_ptrs *wp
     int64_t total = 0;
     int vec_floats = 0, out_rows = 0;
     const int epc = MK_CHUNK_BYTES / eb;
+    int max_rows_o = 0;  // x rows a workgroup owns (O-stage rows): reduced and kept in LDS
     for (int k = 0; k < ST_NUM; ++k) {
         MkStage &s = P.st[k];
         s.rows = shapes[k].rows;
         s.k = shapes[k].k;
-        s.units = (int)ceil_div(s.rows, 4);
-        s.rbp = (int)ceil_div((int64_t)s.k * eb, MK_CHUNK_BYTES);
+        // the down stage is split along its input: its geometry follows the gate/up units
+        s.units = k == ST_DOWN ? (int)ceil_div(2LL * F, 4) : (int)ceil_div(s.rows, 4);
+        s.rbp = k == ST_DOWN ? 0 : (int)ceil_div((int64_t)s.k * eb, MK_CHUNK_BYTES);
         int64_t block = 0;
         for (int w = 0; w < grid; ++w) {
             const int u0 = (int)((int64_t)w * s.units / grid), u1 = (int)((int64_t)(w + 1) * s.units / grid);
             off_host[(size_t)k * grid + w] = block;
+            if (k == ST_DOWN) {
+                const MkDownGeo dg = mk_down_geo(w, grid, s.units, F, H, 16 / eb);
+                block += (int64_t)dg.nsl * MK_SLOT_BYTES;
+                continue;
+            }
             block += ceil_div((int64_t)(u1 - u0) * s.rbp, 4) * MK_SLOT_BYTES;
             if ((u1 - u0) * 4 > out_rows) out_rows = (u1 - u0) * 4;
-            if (k == ST_O && (u1 - u0) * 4 > 64) return MK_ERR_SHAPE;  // residual rows kept in LDS
+            if (k == ST_O) {
+                if ((u1 - u0) * 4 > 64) return MK_ERR_SHAPE;  // residual rows kept in LDS
+                if ((u1 - u0) * 4 > max_rows_o) max_rows_o = (u1 - u0) * 4;
+            }
         }
         if (s.rbp * epc > vec_floats) vec_floats = s.rbp * epc;
         s.base = total;
         s.layer_stride = k == ST_LM ? 0 : block;
         total += k == ST_LM ? block : block * L;
     }
+    // vec also holds: the SwiGLU outputs of this workgroup (down-stage input),
+    // and the G partial sums of its x rows while they are reduced
+    for (int w = 0; w < grid; ++w) {
+        const MkDownGeo dg = mk_down_geo(w, grid, P.st[ST_DOWN].units, F, H, 16 / eb);
+        if (dg.kp * (16 / eb) > vec_floats) vec_floats = dg.kp * (16 / eb);
+    }
+    if ((int64_t)grid * max_rows_o > vec_floats) vec_floats = grid * max_rows_o;
     // the attention stage gathers its group's queries and the new K/V row into vec
     if (vec_floats < (gq + 2) * d) vec_floats = (gq + 2) * d;
     const int fixed = mk_kernel_lds_bytes(0, vec_floats, out_rows, dtype, d, gq);
@@ -192,8 +209,8 @@ static mk_status create_impl(const mk_model_desc *desc, const mk_weight_ptrs *wp
     // tagged records, one array per dependency point and layer
     const size_t n_xq = (size_t)(L + 1) * H, n_xg = (size_t)L * H, n_q = (size_t)L * nh * d,
                  n_kvn = (size_t)L * nkv * 2 * d, n_part = (size_t)L * nkv * splits * gq * (d + 2),
-                 n_o = (size_t)L * nh * d, n_a = (size_t)L * F, n_amax = (size_t)grid * 2;
-    const size_t n_ll = n_xq + n_xg + n_q + n_kvn + n_part + n_o + n_a + n_amax;
+                 n_o = (size_t)L * nh * d, n_dpart = (size_t)L * grid * H, n_amax = (size_t)grid * 2;
+    const size_t n_ll = n_xq + n_xg + n_q + n_kvn + n_part + n_o + n_dpart + n_amax;
     HIP_TRY(hipMalloc(&h->ll, n_ll * sizeof(uint64_t)));
     HIP_TRY(hipMemset(h->ll, 0, n_ll * sizeof(uint64_t)));  // tag 0: never a launch's tag
     HIP_TRY(hipMalloc(&h->err, 64 * sizeof(uint32_t)));
@@ -258,8 +275,8 @@ static mk_status create_impl(const mk_model_desc *desc, const mk_weight_ptrs *wp
     P.ll_kvn = P.ll_q + n_q;
     P.ll_part = P.ll_kvn + n_kvn;
     P.ll_o = P.ll_part + n_part;
-    P.ll_a = P.ll_o + n_o;
-    P.ll_amax = P.ll_a + n_a;
+    P.ll_dpart = P.ll_o + n_o;
+    P.ll_amax = P.ll_dpart + n_dpart;
     P.err = h->err;
     P.timeout_ticks = (int64_t)timeout_ms * wclk_khz;
     P.trace = h->trace;

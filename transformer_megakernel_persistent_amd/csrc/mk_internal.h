@@ -27,11 +27,35 @@
 #define MK_MAX_GRID 1024
 #define MK_MAX_SPLITS 64  // attention splits per KV head (one lane each in the combine)
 
+// The down projection is split along its input instead of its output rows:
+// workgroup w owns the SwiGLU outputs f in [f0, f0 + nf) -- the gate/up rows
+// it computes -- and multiplies them by the matching Wd columns, producing a
+// partial sum for every one of the H output rows.  Its weights are streamed
+// as "piece columns" of 1 KiB: 64 lanes x 16 bytes, lane i holding 16 bytes
+// (EPL elements) of one output row.  Rows come in groups of 64 (one row per
+// lane); consumer c takes row groups c, c + 4, ...; a row group is kp piece
+// columns long (kp = ceil(nf / EPL)), and slot n carries piece columns
+// [4n, 4n + 4) of each consumer's stream.
+struct MkDownGeo {
+    int f0, nf, kp, nsl;
+};
+static inline __host__ __device__ MkDownGeo mk_down_geo(int w, int G, int units_gu, int F, int H, int epl) {
+    const int u0 = (int)(((long long)w * units_gu) / G), u1 = (int)(((long long)(w + 1) * units_gu) / G);
+    MkDownGeo g;
+    g.f0 = 2 * u0;
+    const int f1 = 2 * u1 < F ? 2 * u1 : F;
+    g.nf = f1 > g.f0 ? f1 - g.f0 : 0;
+    g.kp = (g.nf + epl - 1) / epl;
+    const int groups_per_consumer = ((H + 63) / 64 + 3) / 4;
+    g.nsl = (groups_per_consumer * g.kp + 3) / 4;
+    return g;
+}
+
 // Stage kinds with weights; the attention stage streams the KV cache.
 enum { ST_QKV = 0, ST_O = 1, ST_GU = 2, ST_DOWN = 3, ST_LM = 4, ST_NUM = 5 };
 
 struct MkStage {
-    int32_t units;        // total units (4 packed rows each)
+    int32_t units;        // total units (4 packed rows each); for the down stage: the gate/up units
     int32_t rbp;          // packed row length in 1 KiB chunks
     int32_t k;            // input length in elements
     int32_t rows;         // logical packed rows (units*4 >= rows; the rest are zero)
@@ -66,7 +90,7 @@ struct MkParams {
     uint64_t *ll_kvn;      // [L][nkv][2][d] K and V of this step's position, bf16-rounded
     uint64_t *ll_part;     // [L][nkv*splits][GQ][d+2] attention partials: o (unnormalised), m, l
     uint64_t *ll_o;        // [L][nh*d]  attention output
-    uint64_t *ll_a;        // [L][F]     SwiGLU output
+    uint64_t *ll_dpart;    // [L][grid][H] each workgroup's partial down projection
     uint64_t *ll_amax;     // [grid][2]  per-workgroup (max logit, its index)
     uint32_t *err;         // device error word
     // this call

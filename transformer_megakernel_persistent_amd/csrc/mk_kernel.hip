@@ -257,9 +257,10 @@ __device__ __forceinline__ int wg_unit0(int w, int U, int G) { return (int)(((in
 
 struct Geo {
     int unit0[ST_NUM], units[ST_NUM], nsl[ST_NUM];
+    MkDownGeo dn;
 };
 
-__device__ __forceinline__ void make_geo(const MkParams &p, int w, Geo &g) {
+__device__ __forceinline__ void make_geo(const MkParams &p, int w, int epl, Geo &g) {
 #pragma unroll
     for (int k = 0; k < ST_NUM; ++k) {
         const int U = p.st[k].units;
@@ -267,6 +268,8 @@ __device__ __forceinline__ void make_geo(const MkParams &p, int w, Geo &g) {
         g.units[k] = wg_unit0(w + 1, U, p.grid) - g.unit0[k];
         g.nsl[k] = (g.units[k] * p.st[k].rbp + 3) / 4;
     }
+    g.dn = mk_down_geo(w, p.grid, p.st[ST_DOWN].units, p.F, p.H, epl);
+    g.nsl[ST_DOWN] = g.dn.nsl;
 }
 
 // Order of streamed stages inside a layer; index 1 is the KV stream.
@@ -304,7 +307,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
     volatile LDS int *ctl = (volatile LDS int *)(ssp + MK_NUM_CONSUMERS);  // [1] abort step, [8] consumer meetings
 
     Geo g;
-    make_geo(p, w, g);
+    make_geo(p, w, EPL, g);
 
     // Attention split of this workgroup: KV head kvj, positions [t0, t1).
     const int S = p.splits;
@@ -410,7 +413,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
             settle();
         };
         for (int i = 0; i < NS - 1; ++i) issue(i);
-        int j = 0;
+        int jl = NS - 1;  // ring slot the next issue fills
         int lstep = 0;  // barriers passed; mirrors the consumers' step counter
         const int wait_n = (NS - 2) * 8;
         // ctl[1] holds the step in which a consumer aborted (0: none).  The
@@ -431,8 +434,8 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
             MK_COMPILER_BARRIER();
             ++lstep;
             if (aborted()) return false;
-            issue((j + NS - 1) % NS);
-            ++j;
+            issue(jl);
+            jl = jl + 1 == NS ? 0 : jl + 1;
             return true;
         };
         bool ok = true;
@@ -456,7 +459,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
     // its registers are free again for the next stage.
     const int c = wave - MK_NUM_LOADERS;        // consumer index 0..3
     const int ct = tid - MK_NUM_LOADERS * 64;   // consumer thread 0..255
-    int j = 0;      // next ring slot
+    int js = 0;     // ring slot of the next data step
     int step = 0;   // barriers passed (also the consumer-local go-flag value)
     bool ok = true;
 
@@ -512,9 +515,8 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
     // zero-padded to pad.  The four consumers take interleaved 16-byte pieces
     // (two records), so the workgroup reads each element once; ssp[c] gets
     // this consumer's share of the sum of squares, summed in a fixed order.
-    auto gather_to = [&](LDS float *dst, const uint64_t *src, int n, const float *gain, int pad) -> bool {
-        const int npc = n >> 1;
-        const __amdgpu_buffer_rsrc_t rs = rsrc(src, (uint32_t)n * 8u);
+    auto gather_fn = [&](LDS float *dst, int npc, __amdgpu_buffer_rsrc_t rs, auto &&off, const float *gain,
+                         int n, int pad) -> bool {
         float ss = 0.f;
         poll_start = wall_clock64();
         bool good = true;
@@ -524,7 +526,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
             for (int u = 0; u < 8; ++u)
                 if (base + u * 256 < npc) mask |= 1u << u;
             u4v v[8];
-            if (!poll16<8>(rs, [&](int u) { return (uint32_t)(base + u * 256) * 16u; }, mask, v, tag, poll_ok)) {
+            if (!poll16<8>(rs, [&](int u) { return off(base + u * 256); }, mask, v, tag, poll_ok)) {
                 good = false;
                 break;
             }
@@ -545,6 +547,10 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
         if (lane == 0) ssp[c] = ss;
         if (!good) return false;
         return csync();
+    };
+    auto gather_to = [&](LDS float *dst, const uint64_t *src, int n, const float *gain, int pad) -> bool {
+        return gather_fn(dst, n >> 1, rsrc(src, (uint32_t)n * 8u), [](int pc) { return (uint32_t)pc * 16u; }, gain, n,
+                         pad);
     };
     auto gather = [&](const uint64_t *src, int n, const float *gain, int pad) -> bool {
         return gather_to(vec, src, n, gain, pad);
@@ -663,7 +669,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
             barrier();
             stamp_step(l, 0);
             if (n < units) {
-                const LDS unsigned char *bp = ring + (j % NS) * MK_SLOT_BYTES + c * 4 * MK_CHUNK_BYTES + lane * 16;
+                const LDS unsigned char *bp = ring + js * MK_SLOT_BYTES + c * 4 * MK_CHUNK_BYTES + lane * 16;
                 float d[4];
                 if constexpr (DT == 1) {
                     u4v wv[4];
@@ -692,7 +698,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
                 const float t = wave_sum((d[0] + d[1]) + (d[2] + d[3]));
                 if (lane == 0) outv[n * 4 + c] = t;
             }
-            ++j;
+            js = js + 1 == NS ? 0 : js + 1;
             stamp_step(l, 1);
         }
     };
@@ -704,7 +710,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
         for (int n = 0; n < g.nsl[st]; ++n) {
             barrier();
             stamp_step(l, 0);
-            const LDS unsigned char *bp = ring + (j % NS) * MK_SLOT_BYTES + c * 4 * MK_CHUNK_BYTES + lane * 16;
+            const LDS unsigned char *bp = ring + js * MK_SLOT_BYTES + c * 4 * MK_CHUNK_BYTES + lane * 16;
             if ((rbp & 3) == 0) {  // the piece lies inside one row
                 if (row_c < units) {
                     const LDS float *hp = vec + kc * EPC + lane * EPL;
@@ -737,9 +743,115 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
                     }
                 }
             }
-            ++j;
+            js = js + 1 == NS ? 0 : js + 1;
             stamp_step(l, 1);
         }
+    };
+
+    // ---- down projection, split along its input ----
+    // Lane i of consumer c accumulates output row (c + 4*gl)*64 + i over the
+    // kp piece columns of its row group gl; the finished partial sum is
+    // stored as a tagged record of this workgroup's partial vector.
+    auto down_steps = [&](int l) {
+        uint64_t *dst = p.ll_dpart + ((size_t)l * G + w) * p.H;
+        const int kp = g.dn.kp, ng = (p.H + 63) >> 6;
+        if (kp == 0) {  // no SwiGLU outputs here: the partial is zero
+            for (int r = ct; r < p.H; r += 256) stll(dst + r, 0.f);
+            return;
+        }
+        if ((kp & 3) == 0) {
+            // Every step covers four pieces of one row group: straight-line
+            // code with four independent dot products; with kp == 4 the
+            // workgroup's SwiGLU outputs stay in registers.
+            float ar[4][EPL];
+            if (kp == 4) {
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) ar[qq][e] = vec[qq * EPL + e];
+            }
+            int gl = 0, q = 0;
+            float acc = 0.f;
+            for (int n = 0; n < g.nsl[ST_DOWN]; ++n) {
+                barrier();
+                stamp_step(l, 0);
+                const int grp = c + 4 * gl;
+                if (grp < ng) {  // wave-uniform
+                    const LDS unsigned char *bp = ring + js * MK_SLOT_BYTES + c * 4 * MK_CHUNK_BYTES + lane * 16;
+                    float dq[4];
+                    if (kp == 4) {
+#pragma unroll
+                        for (int qq = 0; qq < 4; ++qq) dq[qq] = piece_dot_reg<DT>(bp + qq * MK_CHUNK_BYTES, ar[qq]);
+                    } else {
+#pragma unroll
+                        for (int qq = 0; qq < 4; ++qq) dq[qq] = piece_dot<DT>(bp + qq * MK_CHUNK_BYTES, vec + (q + qq) * EPL);
+                    }
+                    acc += (dq[0] + dq[1]) + (dq[2] + dq[3]);
+                    q += 4;
+                    if (q == kp) {
+                        const int row = grp * 64 + lane;
+                        if (row < p.H) stll(dst + row, acc);
+                        acc = 0.f;
+                        q = 0;
+                        ++gl;
+                    }
+                }
+                js = js + 1 == NS ? 0 : js + 1;
+                stamp_step(l, 1);
+            }
+            return;
+        }
+        int gl = 0, q = 0;
+        float acc = 0.f;
+        for (int n = 0; n < g.nsl[ST_DOWN]; ++n) {
+            barrier();
+            stamp_step(l, 0);
+            const LDS unsigned char *bp = ring + js * MK_SLOT_BYTES + c * 4 * MK_CHUNK_BYTES + lane * 16;
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+                const int grp = c + 4 * gl;
+                if (grp < ng) {  // wave-uniform
+                    acc += piece_dot<DT>(bp + qq * MK_CHUNK_BYTES, vec + q * EPL);
+                    if (++q == kp) {
+                        const int row = grp * 64 + lane;
+                        if (row < p.H) stll(dst + row, acc);
+                        acc = 0.f;
+                        q = 0;
+                        ++gl;
+                    }
+                }
+            }
+            js = js + 1 == NS ? 0 : js + 1;
+            stamp_step(l, 1);
+        }
+    };
+    // x rows of this workgroup (its O-stage rows r0 .. r0+nr-1) = residual +
+    // the sum of the G partial down projections, summed in a fixed order;
+    // stored as tagged records for the next stage's gather.  Ends with the
+    // consumers' meeting so that vec may be overwritten afterwards.
+    auto down_reduce = [&](int l, uint64_t *xdst) -> bool {
+        const int r0 = g.unit0[ST_O] * 4;
+        const int nr = max(0, min(g.units[ST_O] * 4, p.H - r0));
+        const int hp = nr >> 1;  // 16-byte pieces per producer
+        const int H = p.H;
+        const __amdgpu_buffer_rsrc_t rs = rsrc(p.ll_dpart + (size_t)l * G * H, (uint32_t)((size_t)G * H * 8u));
+        // vec[wq * nr + i] = partial of producer wq for row r0 + i
+        auto off = [&](int pc) {
+            const int wq = pc / hp, i = pc - wq * hp;
+            return (uint32_t)(((size_t)wq * H + r0 + 2 * i) * 8u);
+        };
+        if (!gather_fn(vec, G * hp, rs, off, nullptr, G * nr, G * nr)) return false;
+        for (int i = c; i < nr; i += MK_NUM_CONSUMERS) {
+            float sum = 0.f;
+            for (int wq = lane; wq < G; wq += 64) sum += vec[wq * nr + i];
+            sum = wave_sum(sum);
+            if (lane == 0) {
+                const float xn = xown[i] + sum;
+                xown[i] = xn;
+                stll(xdst + r0 + i, xn);
+            }
+        }
+        return csync();
     };
 
     // ---- attention (split-K flash decode over this workgroup's positions) ----
@@ -900,14 +1012,16 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
             }
         }
     };
-    auto epi_gu = [&](int l, float inv) {
-        uint64_t *adst = p.ll_a + (size_t)l * p.F;
-        for (int m = lane; m < g.units[ST_GU] * 2; m += 64) {
-            const int f = g.unit0[ST_GU] * 2 + m;
-            if (f < p.F) {
+    // SwiGLU of this workgroup's gate/up rows: a[f0 + m] -> vec[m] (the
+    // down stage's input stays in the workgroup), zero-padded to kp pieces.
+    auto epi_gu = [&](float inv) {
+        for (int m = lane; m < g.dn.kp * EPL; m += 64) {
+            float av = 0.f;
+            if (m < g.dn.nf) {
                 const float gv = outv[2 * m] * inv, uv = outv[2 * m + 1] * inv;
-                stll(adst + f, gv / (1.0f + __expf(-gv)) * uv);
+                av = gv / (1.0f + __expf(-gv)) * uv;
             }
+            vec[m] = av;
         }
     };
     // Attention epilogue (consumer 0): merge the four consumers' states into
@@ -951,10 +1065,10 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
         poll_start = wall_clock64();
         int cur_h = -1;
         float M = 0.f, Ls = 1.f;
-        for (int eb = e_0; eb < e_1; eb += 4) {
+        for (int eb = e_0; eb < e_1; eb += 8) {
             uint32_t mask = 0;
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
+            for (int u = 0; u < 8; ++u)
                 if (eb + u < e_1 && ln) mask |= 3u << (2 * u);
             // piece 2u: (m, l) of element eb+u's head; piece 2u+1: the pair holding its o value
             auto off = [&](int i) {
@@ -962,10 +1076,10 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
                 const uint32_t rec = (uint32_t)(((h / GQ) * S + lane) * GQ + h % GQ) * PREC;
                 return (rec + ((i & 1) ? ((e % d) & ~1) : d)) * 8u;
             };
-            u4v v[8];
-            if (!poll16<8>(rp, off, mask, v, tag, poll_ok)) return false;
+            u4v v[16];
+            if (!poll16<16>(rp, off, mask, v, tag, poll_ok)) return false;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
+            for (int u = 0; u < 8; ++u) {
                 const int e = eb + u;
                 if (e < e_1) {  // wave-uniform
                     const int h = e / d, dim = e % d;
@@ -1106,9 +1220,9 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
                     gemv_lds_steps(ST_QKV, l);
                 }
             } else {
-                if (c == 0) epi_residual(ST_DOWN, p.ll_xq + (size_t)l * p.H);
+                ok = down_reduce(l - 1, p.ll_xq + (size_t)l * p.H);
                 stamp(5 * l, 1);
-                ok = gather(p.ll_xq + (size_t)l * p.H, p.H, gain, p.st[ST_QKV].rbp * EPC);
+                ok = ok && gather(p.ll_xq + (size_t)l * p.H, p.H, gain, p.st[ST_QKV].rbp * EPC);
                 stamp(5 * l, 2);
                 if (!ok) break;
                 inv_q = inv_lds(p.H);
@@ -1155,7 +1269,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
                 for (int n = 0; n < nsl_kv; ++n) {
                     barrier();
                     stamp_step(l, 0);
-                    const LDS unsigned char *kb = ring + (j % NS) * MK_SLOT_BYTES;
+                    const LDS unsigned char *kb = ring + js * MK_SLOT_BYTES;
                     const LDS unsigned char *vb = kb + 8 * MK_CHUNK_BYTES;
                     float kv[2][EPL], vv[2][EPL];
                     bool valid[2];
@@ -1168,7 +1282,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
                     }
                     attn_fold(A, std::integral_constant<int, 2>{}, kv, vv, valid);
                     if (n == nsl_kv - 1) attn_finish(A);
-                    ++j;
+                    js = js + 1 == NS ? 0 : js + 1;
                     stamp_step(l, 1);
                 }
             } else {
@@ -1210,22 +1324,22 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
         {
             barrier();
             stamp(5 * l + 4, 0);
-            if (c == 0) epi_gu(l, inv_g);
+            if (c == 0) epi_gu(inv_g);
             stamp(5 * l + 4, 1);
-            ok = gather(p.ll_a + (size_t)l * p.F, p.F, nullptr, p.st[ST_DOWN].rbp * EPC);
+            ok = csync();
             stamp(5 * l + 4, 2);
             if (!ok) break;
             stamp(5 * l + 4, 3);
-            gemv_lds_steps(ST_DOWN, l);
+            down_steps(l);
         }
     }
     if (ok && LOGITS) {
         // ===== LM head; boundary: epilogue DOWN(L-1) + input x =====
         barrier();
         stamp(5 * L, 0);
-        if (c == 0) epi_residual(ST_DOWN, p.ll_xq + (size_t)L * p.H);
+        ok = down_reduce(L - 1, p.ll_xq + (size_t)L * p.H);
         stamp(5 * L, 1);
-        ok = gather(p.ll_xq + (size_t)L * p.H, p.H, p.g_final, p.st[ST_LM].rbp * EPC);
+        ok = ok && gather(p.ll_xq + (size_t)L * p.H, p.H, p.g_final, p.st[ST_LM].rbp * EPC);
         stamp(5 * L, 2);
         if (ok) {
             const float inv_lm = inv_lds(p.H);
@@ -1236,9 +1350,10 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
             stamp(5 * L + 1, 1);
         }
     } else if (ok) {
+        // Without the LM head the last layer's output is not needed: only
+        // the cache rows written by the attention stages are the result.
         barrier();
         stamp(5 * L + 1, 0);
-        if (c == 0) epi_residual(ST_DOWN, p.ll_xq + (size_t)L * p.H);
         stamp(5 * L + 1, 1);
     }
     if (!ok) {

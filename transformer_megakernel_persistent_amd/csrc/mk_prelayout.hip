@@ -12,9 +12,12 @@
 //         natural order.
 //   GU  : gate row f and up row f interleaved (packed rows 2f, 2f+1), so a
 //         workgroup owns both halves of every SwiGLU product it emits.
-//   O, DOWN, LM: natural row order.
+//   O, LM: natural row order.
 // Within a workgroup's block, slot n holds for consumer c the 4 KiB of its row
 // stream at [4n, 4n+4) chunks; consumer c's rows are local rows c, c+4, ...
+//   DOWN: split along the input instead (see mk_down_geo): workgroup w's block
+//         holds the Wd columns of its SwiGLU outputs as piece columns, lane i
+//         of a piece column carrying 16 bytes of one output row.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -30,15 +33,33 @@ __global__ __launch_bounds__(256) void prelayout_kernel(unsigned char *dst_block
     const int U = st.units;
     const int unit0 = (int)(((int64_t)w * U) / grid);
     const int units = (int)(((int64_t)(w + 1) * U) / grid) - unit0;
-    const int nsl = (units * st.rbp + 3) / 4;
     const int chunk = blockIdx.x * 4 + (threadIdx.x >> 6);  // chunk index within this workgroup's block
     const int lane = threadIdx.x & 63;
-    if (chunk >= nsl * MK_CHUNKS_PER_SLOT) return;
     const int slot = chunk / MK_CHUNKS_PER_SLOT, cc = chunk % MK_CHUNKS_PER_SLOT;
     const int c = cc / 4, qi = cc % 4;
     const int qq = slot * 4 + qi;          // position in consumer c's chunk stream
-    const int row_c = qq / st.rbp, kc = qq % st.rbp;
     uint4 val = make_uint4(0, 0, 0, 0);
+    if (kind == ST_DOWN) {
+        const MkDownGeo dg = mk_down_geo(w, grid, U, st.k, st.rows, 16 / eb);
+        if (chunk >= dg.nsl * MK_CHUNKS_PER_SLOT) return;
+        const int grp = c + 4 * (qq / (dg.kp > 0 ? dg.kp : 1)), q = qq % (dg.kp > 0 ? dg.kp : 1);
+        const int row = grp * 64 + lane;
+        const int epl = 16 / eb;
+        if (dg.kp > 0 && row < st.rows) {
+            const int fa = dg.f0 + q * epl;  // first column of this piece
+            const unsigned char *srow = src0 + (int64_t)row * st.k * eb;
+            unsigned char tmp[16] = {0};
+            for (int e = 0; e < epl; ++e)
+                if (q * epl + e < dg.nf)
+                    for (int b = 0; b < eb; ++b) tmp[e * eb + b] = srow[(int64_t)(fa + e) * eb + b];
+            val = *(const uint4 *)tmp;
+        }
+        *(uint4 *)(dst_block + st.wg_off[w] + (int64_t)chunk * MK_CHUNK_BYTES + lane * 16) = val;
+        return;
+    }
+    const int nsl = (units * st.rbp + 3) / 4;
+    if (chunk >= nsl * MK_CHUNKS_PER_SLOT) return;
+    const int row_c = qq / st.rbp, kc = qq % st.rbp;
     if (row_c < units) {
         const int gr = (unit0 + row_c) * 4 + c;  // packed row
         if (gr < st.rows) {
@@ -93,7 +114,8 @@ extern "C" int mk_launch_prelayout_stage(unsigned char *dst, const MkStage *st, 
     for (int w = 0; w < grid; ++w) {
         const int U = st->units;
         const int u0 = (int)(((int64_t)w * U) / grid), u1 = (int)(((int64_t)(w + 1) * U) / grid);
-        const int nsl = ((u1 - u0) * st->rbp + 3) / 4;
+        const int nsl = kind == ST_DOWN ? mk_down_geo(w, grid, U, st->k, st->rows, dtype ? 8 : 4).nsl
+                                        : ((u1 - u0) * st->rbp + 3) / 4;
         if (nsl > max_nsl) max_nsl = nsl;
     }
     if (max_nsl == 0) return 0;
