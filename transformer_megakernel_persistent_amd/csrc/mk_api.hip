@@ -136,8 +136,12 @@ static mk_status create_impl(const mk_model_desc *desc, const mk_weight_ptrs *wp
     if (tun) t = *tun;
     const int grid = t.grid ? t.grid : h->cu_count;
     if (grid > MK_MAX_GRID) return MK_ERR_TUNING;
+    // consumers sharing one query head (GQ < 4) each produce a partial record,
+    // so the combine merges splits * cph records per head, one lane each
+    const int cph = MK_NUM_CONSUMERS / (gq < MK_NUM_CONSUMERS ? gq : MK_NUM_CONSUMERS);
     int splits = t.attn_splits ? t.attn_splits : (grid / nkv > 0 ? grid / nkv : 1);
-    if (!t.attn_splits && splits > MK_MAX_SPLITS) splits = MK_MAX_SPLITS;
+    if (!t.attn_splits && splits > MK_MAX_SPLITS / cph) splits = MK_MAX_SPLITS / cph;
+    if (splits * cph > MK_MAX_SPLITS) return MK_ERR_TUNING;
     if ((int64_t)splits * nkv > grid) return MK_ERR_TUNING;
     h->cooperative = t.cooperative == 1 ? 1 : 0;
     const int timeout_ms = t.timeout_ms ? t.timeout_ms : 2000;
@@ -207,10 +211,10 @@ static mk_status create_impl(const mk_model_desc *desc, const mk_weight_ptrs *wp
     HIP_TRY(hipMalloc(&h->embed, (size_t)V * H * eb));
     HIP_TRY(hipMalloc(&h->rope, (size_t)D.max_seq * d * sizeof(float)));
     // tagged records, one array per dependency point and layer
-    const size_t n_xq = (size_t)(L + 1) * H, n_xg = (size_t)L * H, n_q = (size_t)L * nh * d,
-                 n_kvn = (size_t)L * nkv * 2 * d, n_part = (size_t)L * nkv * splits * gq * (d + 2),
+    const size_t n_xq = (size_t)(L + 1) * H, n_xg = (size_t)L * H, n_q = (size_t)L * nkv * (gq + 2) * d,
+                 n_part = (size_t)L * nkv * splits * cph * gq * (d + 2),
                  n_o = (size_t)L * nh * d, n_dpart = (size_t)L * grid * H, n_amax = (size_t)grid * 2;
-    const size_t n_ll = n_xq + n_xg + n_q + n_kvn + n_part + n_o + n_dpart + n_amax;
+    const size_t n_ll = n_xq + n_xg + n_q + n_part + n_o + n_dpart + n_amax;
     HIP_TRY(hipMalloc(&h->ll, n_ll * sizeof(uint64_t)));
     HIP_TRY(hipMemset(h->ll, 0, n_ll * sizeof(uint64_t)));  // tag 0: never a launch's tag
     HIP_TRY(hipMalloc(&h->err, 64 * sizeof(uint32_t)));
@@ -271,9 +275,8 @@ static mk_status create_impl(const mk_model_desc *desc, const mk_weight_ptrs *wp
     P.rope = h->rope;
     P.ll_xq = h->ll;
     P.ll_xg = P.ll_xq + n_xq;
-    P.ll_q = P.ll_xg + n_xg;
-    P.ll_kvn = P.ll_q + n_q;
-    P.ll_part = P.ll_kvn + n_kvn;
+    P.ll_qkv = P.ll_xg + n_xg;
+    P.ll_part = P.ll_qkv + n_q;
     P.ll_o = P.ll_part + n_part;
     P.ll_dpart = P.ll_o + n_o;
     P.ll_amax = P.ll_dpart + n_dpart;

@@ -86,8 +86,8 @@ struct MkParams {
     // per launch, so a reader polls until the tags equal this launch's tag.
     uint64_t *ll_xq;       // [L+1][H]   x entering layer l >= 1, and the LM head (l = L)
     uint64_t *ll_xg;       // [L][H]     x after the O projection
-    uint64_t *ll_q;        // [L][nh*d]  rotated queries
-    uint64_t *ll_kvn;      // [L][nkv][2][d] K and V of this step's position, bf16-rounded
+    uint64_t *ll_qkv;      // [L][nkv][GQ+2][d] per KV group: rotated queries, then K and V of
+                           // this step's position (bf16-rounded), next to each other
     uint64_t *ll_part;     // [L][nkv*splits][GQ][d+2] attention partials: o (unnormalised), m, l
     uint64_t *ll_o;        // [L][nh*d]  attention output
     uint64_t *ll_dpart;    // [L][grid][H] each workgroup's partial down projection

@@ -253,6 +253,18 @@ __device__ __forceinline__ bool poll16(__amdgpu_buffer_rsrc_t rs, O &&off, uint3
     }
 }
 
+// Elements of a 16-byte piece in global memory (plain load).
+template <int DT>
+__device__ __forceinline__ void piece_load_glb(const unsigned char *p, float (&v)[16 / (DT ? 2 : 4)]) {
+    const u4v w = *(const u4v *)p;
+    if constexpr (DT == 1) {
+        v[0] = bf_lo(w.x); v[1] = bf_hi(w.x); v[2] = bf_lo(w.y); v[3] = bf_hi(w.y);
+        v[4] = bf_lo(w.z); v[5] = bf_hi(w.z); v[6] = bf_lo(w.w); v[7] = bf_hi(w.w);
+    } else {
+        v[0] = __uint_as_float(w.x); v[1] = __uint_as_float(w.y); v[2] = __uint_as_float(w.z); v[3] = __uint_as_float(w.w);
+    }
+}
+
 __device__ __forceinline__ int wg_unit0(int w, int U, int G) { return (int)(((int64_t)w * U) / G); }
 
 struct Geo {
@@ -297,12 +309,11 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
     const int w = blockIdx.x, G = p.grid, NS = p.ring_slots, L = p.L;
     constexpr int d = DH;
 
-    // LDS layout: ring | vec | out | cstate | xown | ss | control
+    // LDS layout: ring | vec | out | xown | ss | control
     LDS unsigned char *ring = smem;
     LDS float *vec = (LDS float *)(smem + NS * MK_SLOT_BYTES);
     LDS float *outv = vec + p.lds_vec_floats;
-    LDS float *cst = outv + p.lds_out_rows;
-    LDS float *xown = cst + MK_NUM_CONSUMERS * GQ * (d + 2);
+    LDS float *xown = outv + p.lds_out_rows;
     LDS float *ssp = xown + 64;
     volatile LDS int *ctl = (volatile LDS int *)(ssp + MK_NUM_CONSUMERS);  // [1] abort step, [8] consumer meetings
 
@@ -317,7 +328,11 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
     const int per = (P + S - 1) / S;
     const int t0 = min(P, kvs * per), t1 = min(P, t0 + per);
     const int nt = has_split ? t1 - t0 : 0;
-    const int nsl_kv = (nt + BP - 1) / BP;
+    // Whole KV slots go through the ring; a remainder of at most one chunk
+    // (PPC positions, one per lane group) is read straight into registers.
+    const int nfull = nt / BP, nrem = nt - nfull * BP;
+    const int ntail = nrem <= PPC ? nrem : 0;
+    const int nsl_kv = nfull + (nrem > PPC ? 1 : 0);
     const bool is_last = has_split && kvs == S - 1;
     const size_t head_bytes = (size_t)p.max_seq * d * EB;
     // Per-kind slot counts as scalars (kind 0 QKV, 1 KV, 2 O, 3 GU, 4 DOWN, 5 LM);
@@ -855,26 +870,38 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
     };
 
     // ---- attention (split-K flash decode over this workgroup's positions) ----
+    // Head-major mapping: the group's GQ query heads are dealt to the four
+    // consumers, HG of them distinct at a time.  Consumer c holds heads
+    // c % HG + HG*k (k < HPC) and, when several consumers share a head
+    // (GQ < 4), the chunk subset cs = c / HG of every KV slot.  With GQ >= 4
+    // a consumer owns its heads over all positions and writes the split's
+    // partial records itself; consumers sharing a head write one record each
+    // (an extra "effective split" that the combine merges like any other).
+    constexpr int HG = GQ < MK_NUM_CONSUMERS ? GQ : MK_NUM_CONSUMERS;
+    constexpr int HPC = GQ / HG;                // heads per consumer
+    constexpr int CPH = MK_NUM_CONSUMERS / HG;  // consumers per head
+    constexpr int CPS = 8 / CPH;                // K (and V) chunks per slot per consumer
+    constexpr int NQB = CPS < 4 ? CPS : 4;      // chunks folded together
+    const int hc = c % HG, cs = c / HG;
     const float scale = 1.0f / sqrtf((float)d);
     const int e0 = (lane % LPP) * EPL;
     struct AttnState {
-        float qr[GQ][EPL];           // the lane's dims of the group's query heads
-        float am[GQ], al[GQ];        // running max (wave-uniform), running sum
-        float ao[GQ][EPL];           // running unnormalised output (lane's dims)
-        float kp[EPL], vp[EPL];      // K/V of the position written this step
+        float qr[HPC][EPL];          // the lane's dims of this consumer's query heads
+        float am[HPC], al[HPC];      // running max (wave-uniform), running sum
+        float ao[HPC][EPL];          // running unnormalised output (lane's dims)
     };
-    // Fold NQ groups of positions (each lane holds one position of each group,
-    // PPC positions per group) into the running state: all scores first, then
-    // one running-max update, rescale and V accumulation per head.  Invalid
-    // positions get probability 0 and their V values are never used.
+    // Fold NQ chunks of positions (each lane holds one position of each
+    // chunk, PPC positions per chunk) into the running state: all scores
+    // first, then one running-max update, rescale and V accumulation per
+    // head.  Invalid positions get probability 0; their V values are not used.
     auto attn_fold = [&](AttnState &A, auto nq_tag, const float (*kv)[EPL], const float (*vv)[EPL],
                          const bool *valid) {
         constexpr int NQ = decltype(nq_tag)::value;
-        float sc[NQ][GQ];
+        float sc[NQ][HPC];
 #pragma unroll
         for (int q = 0; q < NQ; ++q)
 #pragma unroll
-            for (int h = 0; h < GQ; ++h) {
+            for (int h = 0; h < HPC; ++h) {
                 float t = 0.f;
 #pragma unroll
                 for (int e = 0; e < EPL; ++e) t = fmaf(A.qr[h][e], kv[q][e], t);
@@ -883,12 +910,12 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
 #pragma unroll
         for (int q = 0; q < NQ; ++q)
 #pragma unroll
-            for (int h = 0; h < GQ; ++h) {
+            for (int h = 0; h < HPC; ++h) {
                 const float gsum = group_sum<LPP>(sc[q][h]) * scale;  // all lanes take part
                 sc[q][h] = valid[q] ? gsum : -INFINITY;
             }
 #pragma unroll
-        for (int h = 0; h < GQ; ++h) {
+        for (int h = 0; h < HPC; ++h) {
             float mx = sc[0][h];
 #pragma unroll
             for (int q = 1; q < NQ; ++q) mx = fmaxf(mx, sc[q][h]);
@@ -913,22 +940,25 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
             A.am[h] = any ? mn : A.am[h];
         }
     };
-    // This consumer's final state -> LDS record (o over all its positions, m, l).
-    auto attn_finish = [&](AttnState &A) {
-        if (c == 0 && is_last) {  // the position written this step
-            const bool v1[1] = {lane < LPP};
-            attn_fold(A, std::integral_constant<int, 1>{}, &A.kp, &A.vp, v1);
-        }
+    // This consumer's final state -> its partial records (o over its
+    // positions, m, l), one per head, as tagged records.
+    constexpr int PREC = DH + 2;  // partial record: o[DH], m, l
+    const int S_eff = S * CPH;    // effective splits per KV head
+    auto attn_finish = [&](AttnState &A, int l) {
+        uint64_t *part = p.ll_part + (((size_t)l * p.nkv + kvj) * S_eff + kvs * CPH + cs) * GQ * PREC;
 #pragma unroll
-        for (int h = 0; h < GQ; ++h) {
-            const float lsum = xgroup_sum<LPP>(A.al[h]);
-            LDS float *dst = cst + (c * GQ + h) * (d + 2);
+        for (int k = 0; k < HPC; ++k) {
+            const int h = hc + HG * k;
+            const float lsum = xgroup_sum<LPP>(A.al[k]);
 #pragma unroll
             for (int e = 0; e < EPL; ++e) {
-                const float ov = xgroup_sum<LPP>(A.ao[h][e]);
-                if (lane < LPP) dst[e0 + e] = ov;
+                const float ov = xgroup_sum<LPP>(A.ao[k][e]);
+                if (lane < LPP) stll(part + h * PREC + e0 + e, ov);
             }
-            if (lane == 0) { dst[d] = A.am[h]; dst[d + 1] = lsum; }
+            if (lane == 0) {
+                stll(part + h * PREC + d, A.am[k]);
+                stll(part + h * PREC + d + 1, lsum);
+            }
         }
     };
 
@@ -949,14 +979,14 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
                 const float a0 = y0 * c0 - y1 * s0, b0 = y0 * s0 + y1 * c0;
                 const float a1 = y2 * c1 - y3 * s1, b1 = y2 * s1 + y3 * c1;
                 if (isq) {
-                    uint64_t *qd = p.ll_q + (size_t)l * nqd + (size_t)head * d;
+                    uint64_t *qd = p.ll_qkv + ((size_t)l * p.nkv + head / GQ) * (GQ + 2) * d + (size_t)(head % GQ) * d;
                     stll(qd + m0, a0);
                     stll(qd + m0 + 1, a1);
                     stll(qd + m0 + d / 2, b0);
                     stll(qd + m0 + 1 + d / 2, b1);
                 } else {
                     unsigned char *row = (unsigned char *)p.kc + ((size_t)l * p.nkv + head) * head_bytes + (size_t)P * d * EB;
-                    uint64_t *kn = p.ll_kvn + ((size_t)l * p.nkv + head) * 2 * d;
+                    uint64_t *kn = p.ll_qkv + ((size_t)l * p.nkv + head) * (GQ + 2) * d + (size_t)GQ * d;
                     if constexpr (DT == 1) {
                         const uint32_t ba0 = f2bf(a0), ba1 = f2bf(a1), bb0 = f2bf(b0), bb1 = f2bf(b1);
                         stcu((uint32_t *)(row + m0 * 2), ba0 | (ba1 << 16));
@@ -980,7 +1010,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
                 const int r = gr0 - nqd - nk;
                 const int head = r / d, e = r % d;
                 unsigned char *row = (unsigned char *)p.vc + ((size_t)l * p.nkv + head) * head_bytes + (size_t)P * d * EB;
-                uint64_t *vn = p.ll_kvn + ((size_t)l * p.nkv + head) * 2 * d + d;
+                uint64_t *vn = p.ll_qkv + ((size_t)l * p.nkv + head) * (GQ + 2) * d + (size_t)(GQ + 1) * d;
                 if constexpr (DT == 1) {
                     const uint32_t c0 = f2bf(y0), c1 = f2bf(y1), c2 = f2bf(y2), c3 = f2bf(y3);
                     stcu((uint32_t *)(row + e * 2), c0 | (c1 << 16));
@@ -1024,44 +1054,16 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
             vec[m] = av;
         }
     };
-    // Attention epilogue (consumer 0): merge the four consumers' states into
-    // this split's partial record per query head: o (unnormalised over the
-    // split's positions), running max m, sum l.
-    constexpr int PREC = DH + 2;  // partial record: o[DH], m, l
-    auto attn_partial = [&](int l) {
-        uint64_t *part = p.ll_part + (((size_t)l * p.nkv + kvj) * S + kvs) * GQ * PREC;
-        constexpr int cs = DH + 2;  // consumer-state record in LDS: o[DH], m, l
-        for (int h = 0; h < GQ; ++h) {
-            float M = -INFINITY;
-            for (int cc = 0; cc < MK_NUM_CONSUMERS; ++cc) M = fmaxf(M, cst[(cc * GQ + h) * cs + d]);
-            float Lsum = 0.f;
-            float wgt[MK_NUM_CONSUMERS];
-            for (int cc = 0; cc < MK_NUM_CONSUMERS; ++cc) {
-                const float mc = cst[(cc * GQ + h) * cs + d];
-                wgt[cc] = (mc == -INFINITY) ? 0.f : __expf(mc - M);
-                Lsum += wgt[cc] * cst[(cc * GQ + h) * cs + d + 1];
-            }
-            for (int e = lane; e < d; e += 64) {
-                float o = 0.f;
-                for (int cc = 0; cc < MK_NUM_CONSUMERS; ++cc) o = fmaf(wgt[cc], cst[(cc * GQ + h) * cs + e], o);
-                stll(part + h * PREC + e, o);
-            }
-            if (lane == 0) {
-                stll(part + h * PREC + d, M);
-                stll(part + h * PREC + d + 1, Lsum);
-            }
-        }
-    };
     // Log-sum-exp merge of the splits (consumer 0): workgroup w produces
     // attention-output elements [w*N/G, (w+1)*N/G) of N = n_heads*d.  Lane s
-    // reads split s's (m, l) and the element's o value; the weights are
-    // exp(m_s - max m) and the result sum(w_s o_s) / sum(w_s l_s).
+    // reads effective split s's (m, l) and the element's o value; the
+    // weights are exp(m_s - max m) and the result sum(w_s o_s) / sum(w_s l_s).
     auto combine_slice = [&](int l) -> bool {
         const int N = p.nh * d;
         const int e_0 = (int)((int64_t)w * N / G), e_1 = (int)((int64_t)(w + 1) * N / G);
-        const __amdgpu_buffer_rsrc_t rp =
-            rsrc(p.ll_part + (size_t)l * p.nkv * S * GQ * PREC, (uint32_t)((size_t)p.nkv * S * GQ * PREC * 8));
-        const bool ln = lane < S;
+        const __amdgpu_buffer_rsrc_t rp = rsrc(p.ll_part + (size_t)l * p.nkv * S_eff * GQ * PREC,
+                                               (uint32_t)((size_t)p.nkv * S_eff * GQ * PREC * 8));
+        const bool ln = lane < S_eff;
         poll_start = wall_clock64();
         int cur_h = -1;
         float M = 0.f, Ls = 1.f;
@@ -1073,7 +1075,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
             // piece 2u: (m, l) of element eb+u's head; piece 2u+1: the pair holding its o value
             auto off = [&](int i) {
                 const int e = eb + i / 2, h = e / d;
-                const uint32_t rec = (uint32_t)(((h / GQ) * S + lane) * GQ + h % GQ) * PREC;
+                const uint32_t rec = (uint32_t)(((h / GQ) * S_eff + lane) * GQ + h % GQ) * PREC;
                 return (rec + ((i & 1) ? ((e % d) & ~1) : d)) * 8u;
             };
             u4v v[16];
@@ -1237,51 +1239,79 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
             if (c == 0) epi_qkv(l, inv_q);
             stamp(5 * l + 1, 1);
             if (has_split) {
+                // Consumers of chunk subset 0 also fold the tail positions and,
+                // in the last split, position pos.  The tail rows were written
+                // by earlier steps: plain loads, issued first to hide latency.
+                const bool fold_extra = cs == 0;
+                const int tg = lane / LPP;
+                const bool tvalid = fold_extra && tg < ntail;
+                float kt[EPL], vt[EPL];
+                if (fold_extra && ntail > 0) {
+                    const size_t tp = (size_t)t0 + (size_t)nfull * BP + (tvalid ? tg : 0);
+                    const size_t roff = (((size_t)l * p.nkv + kvj) * p.max_seq + tp) * d * EB + (size_t)e0 * EB;
+                    piece_load_glb<DT>((const unsigned char *)p.kc + roff, kt);
+                    piece_load_glb<DT>((const unsigned char *)p.vc + roff, vt);
+                }
                 // This group's rotated queries and, in the last split, the K/V
-                // row of position pos (bf16-rounded like the cache) into LDS;
-                // vec is free here (the QKV input is no longer needed).
-                ok = gather_to(vec, p.ll_q + (size_t)l * nq + (size_t)kvj * GQ * d, GQ * d, nullptr, GQ * d);
-                if (ok && is_last)
-                    ok = gather_to(vec + GQ * d, p.ll_kvn + ((size_t)l * p.nkv + kvj) * 2 * d, 2 * d, nullptr, 2 * d);
+                // row of position pos (bf16-rounded like the cache) into LDS in
+                // one gather (they are stored next to each other); vec is free
+                // here (the QKV input is no longer needed).
+                {
+                    const int nrec = (is_last ? GQ + 2 : GQ) * d;  // the last split also takes K/V of pos
+                    ok = gather_to(vec, p.ll_qkv + ((size_t)l * p.nkv + kvj) * (GQ + 2) * d, nrec, nullptr, nrec);
+                }
                 AttnState A;
 #pragma unroll
-                for (int h = 0; h < GQ; ++h)
+                for (int k = 0; k < HPC; ++k)
 #pragma unroll
-                    for (int e = 0; e < EPL; ++e) A.qr[h][e] = vec[h * d + e0 + e];
-                if (c == 0 && is_last) {
-#pragma unroll
-                    for (int e = 0; e < EPL; ++e) {
-                        A.kp[e] = vec[GQ * d + e0 + e];
-                        A.vp[e] = vec[GQ * d + d + e0 + e];
-                    }
-                }
+                    for (int e = 0; e < EPL; ++e) A.qr[k][e] = vec[(hc + HG * k) * d + e0 + e];
                 stamp(5 * l + 1, 2);
                 if (!ok) break;
 #pragma unroll
-                for (int h = 0; h < GQ; ++h) {
-                    A.am[h] = -INFINITY;
-                    A.al[h] = 0.f;
+                for (int k = 0; k < HPC; ++k) {
+                    A.am[k] = -INFINITY;
+                    A.al[k] = 0.f;
 #pragma unroll
-                    for (int e = 0; e < EPL; ++e) A.ao[h][e] = 0.f;
+                    for (int e = 0; e < EPL; ++e) A.ao[k][e] = 0.f;
                 }
+                auto finish = [&]() {
+                    if (fold_extra && ntail > 0) {
+                        const bool v1[1] = {tvalid};
+                        attn_fold(A, std::integral_constant<int, 1>{}, &kt, &vt, v1);
+                    }
+                    if (fold_extra && is_last) {
+                        float kp[EPL], vp[EPL];
+#pragma unroll
+                        for (int e = 0; e < EPL; ++e) {
+                            kp[e] = vec[GQ * d + e0 + e];
+                            vp[e] = vec[GQ * d + d + e0 + e];
+                        }
+                        const bool v1[1] = {lane < LPP};
+                        attn_fold(A, std::integral_constant<int, 1>{}, &kp, &vp, v1);
+                    }
+                    attn_finish(A, l);
+                };
                 stamp(5 * l + 1, 3);
-                if (nsl_kv == 0) attn_finish(A);
+                if (nsl_kv == 0) finish();
                 for (int n = 0; n < nsl_kv; ++n) {
                     barrier();
                     stamp_step(l, 0);
                     const LDS unsigned char *kb = ring + js * MK_SLOT_BYTES;
                     const LDS unsigned char *vb = kb + 8 * MK_CHUNK_BYTES;
-                    float kv[2][EPL], vv[2][EPL];
-                    bool valid[2];
 #pragma unroll
-                    for (int q = 0; q < 2; ++q) {
-                        const int chunk = c * 2 + q;
-                        valid[q] = t0 + n * BP + chunk * PPC + lane / LPP < t1;
-                        piece_load<DT>(kb + chunk * MK_CHUNK_BYTES + lane * 16, kv[q]);
-                        piece_load<DT>(vb + chunk * MK_CHUNK_BYTES + lane * 16, vv[q]);
+                    for (int b = 0; b < CPS; b += NQB) {
+                        float kv[NQB][EPL], vv[NQB][EPL];
+                        bool valid[NQB];
+#pragma unroll
+                        for (int q = 0; q < NQB; ++q) {
+                            const int chunk = cs * CPS + b + q;
+                            valid[q] = t0 + n * BP + chunk * PPC + lane / LPP < t1;
+                            piece_load<DT>(kb + chunk * MK_CHUNK_BYTES + lane * 16, kv[q]);
+                            piece_load<DT>(vb + chunk * MK_CHUNK_BYTES + lane * 16, vv[q]);
+                        }
+                        attn_fold(A, std::integral_constant<int, NQB>{}, kv, vv, valid);
                     }
-                    attn_fold(A, std::integral_constant<int, 2>{}, kv, vv, valid);
-                    if (n == nsl_kv - 1) attn_finish(A);
+                    if (n == nsl_kv - 1) finish();
                     js = js + 1 == NS ? 0 : js + 1;
                     stamp_step(l, 1);
                 }
@@ -1295,10 +1325,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
             barrier();
             stamp(5 * l + 2, 0);
             bool mine = true;
-            if (c == 0) {
-                if (has_split) attn_partial(l);
-                mine = combine_slice(l);
-            }
+            if (c == 0) mine = combine_slice(l);
             stamp(5 * l + 2, 1);
             ok = mine && gather(p.ll_o + (size_t)l * nq, nq, nullptr, p.st[ST_O].rbp * EPC);
             stamp(5 * l + 2, 2);
@@ -1385,7 +1412,9 @@ KernelFn pick(int dtype, int gq, int lpp, bool logits) {
 
 extern "C" int mk_kernel_lds_bytes(int ring_slots, int vec_floats, int out_rows, int dtype, int d, int gq) {
     (void)dtype;
-    const int floats = vec_floats + out_rows + MK_NUM_CONSUMERS * gq * (d + 2) + 64 + MK_NUM_CONSUMERS + 16;
+    (void)d;
+    (void)gq;
+    const int floats = vec_floats + out_rows + 64 + MK_NUM_CONSUMERS + 16;
     return ring_slots * MK_SLOT_BYTES + floats * 4;
 }
 
