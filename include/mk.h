@@ -91,7 +91,7 @@ typedef struct {
 /* Tuning knobs.  Zero selects the default for every field.
      grid:        workgroups of the persistent grid, 1..1024 and no more than
                   can be resident at once (default: CU count);
-     ring_slots:  16 KiB LDS ring slots per workgroup, 3..8 (default: as many
+     ring_slots:  16 KiB LDS ring slots per workgroup, 3..9 (default: 8, or as many
                   as fit beside the activation buffer);
      attn_splits: sequence splits per KV head, at most 64 (default:
                   min(grid / n_kv_heads, 64));

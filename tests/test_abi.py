@@ -119,8 +119,8 @@ def test_create_rejects_bad_shapes(lib, over, status):
     assert _create(lib, _desc(**over), w)[0] == status
 
 
-@pytest.mark.parametrize("over", [dict(grid=-1), dict(grid=1025), dict(ring_slots=2), dict(ring_slots=9),
-                                  dict(attn_splits=-3), dict(timeout_ms=-1), dict(cooperative=3),
+@pytest.mark.parametrize("over", [dict(grid=-1), dict(grid=1025), dict(ring_slots=2), dict(ring_slots=10),
+                                  dict(attn_splits=-3), dict(attn_splits=65), dict(timeout_ms=-1), dict(cooperative=3),
                                   dict(trace=2)])
 def test_create_rejects_bad_tuning(lib, over):
     w, _keep = _weights(2)

@@ -194,6 +194,7 @@ static mk_status create_impl(const mk_model_desc *desc, const mk_weight_ptrs *wp
     if (vec_floats < (gq + 2) * d) vec_floats = (gq + 2) * d;
     const int fixed = mk_kernel_lds_bytes(0, vec_floats, out_rows, dtype, d, gq);
     int ns = t.ring_slots ? t.ring_slots : (MK_LDS_LIMIT - fixed) / MK_SLOT_BYTES;
+    if (ns > MK_DEFAULT_RING && !t.ring_slots) ns = MK_DEFAULT_RING;  // a 9th slot measured no faster
     if (ns > MK_MAX_RING) ns = MK_MAX_RING;
     if (ns < 3 || fixed + ns * MK_SLOT_BYTES > MK_LDS_LIMIT) return MK_ERR_SHAPE;
     h->lds_bytes = mk_kernel_lds_bytes(ns, vec_floats, out_rows, dtype, d, gq);

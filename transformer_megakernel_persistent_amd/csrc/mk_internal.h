@@ -22,7 +22,8 @@
 #define MK_NUM_LOADERS 2
 #define MK_NUM_CONSUMERS 4
 #define MK_BLOCK_THREADS (64 * (MK_NUM_LOADERS + MK_NUM_CONSUMERS))
-#define MK_MAX_RING 8
+#define MK_MAX_RING 9  // the loaders wait for (ring-2)*8 outstanding loads: at most 63
+#define MK_DEFAULT_RING 8
 #define MK_LDS_LIMIT 163840
 #define MK_MAX_GRID 1024
 #define MK_MAX_SPLITS 64  // attention splits per KV head (one lane each in the combine)

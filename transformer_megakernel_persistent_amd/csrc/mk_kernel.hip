@@ -90,6 +90,7 @@ __device__ __forceinline__ void wait_vm_rt(int n) {
     case 32: wait_vm<32>(); break;
     case 40: wait_vm<40>(); break;
     case 48: wait_vm<48>(); break;
+    case 56: wait_vm<56>(); break;
     default: wait_vm<0>(); break;
     }
 }
