@@ -147,3 +147,116 @@ def test_llama1b_prefill_short_prompt(env):
     cfg = synth.CONFIGS["llama1b"]
     errs, agree = run_pair(env, cfg, seed=6, n_prompt=5, n_steps=2, gains="random")
     assert max(errs) <= 2e-2 and agree == 2
+
+
+# ---- more shapes: group sizes and head widths the full-size models use ----
+
+def test_tiny_bf16_group8(env):
+    # eight query heads per KV head (the 70B shape's grouping): each consumer
+    # holds two heads of the group
+    cfg = synth.CONFIGS["tiny"].with_(dtype="bf16", n_heads=16, n_kv_heads=2, head_dim=64, rope_theta=500000.0)
+    errs, agree = run_pair(env, cfg, seed=7, n_prompt=30, n_steps=4)
+    assert max(errs) <= 2e-2 and agree == 4
+
+
+def test_tiny_fp32_mha(env):
+    # one query head per KV head: four consumers share each head and the
+    # combine merges their records as extra splits
+    cfg = synth.CONFIGS["tiny"].with_(n_heads=4, n_kv_heads=4)
+    errs, agree = run_pair(env, cfg, seed=8, n_prompt=50, n_steps=4)
+    assert max(errs) <= 1e-4 and agree == 4
+
+
+def test_tiny_bf16_head128(env):
+    # head_dim 128 in bfloat16 (the 8B/70B head width): 16 lanes per cache row
+    cfg = synth.CONFIGS["tiny"].with_(dtype="bf16", n_heads=4, n_kv_heads=1, head_dim=128, rope_theta=500000.0)
+    errs, agree = run_pair(env, cfg, seed=9, n_prompt=70, n_steps=4)
+    assert max(errs) <= 2e-2 and agree == 4
+
+
+@pytest.mark.parametrize("n_prompt", [63, 64, 65, 72, 200])
+def test_split_remainders(env, n_prompt):
+    # splits whose positions end exactly on a KV slot, one past it, a short
+    # tail folded from registers, and a long tail through the ring
+    cfg = synth.CONFIGS["tiny"]
+    errs, agree = run_pair(env, cfg, seed=10, n_prompt=n_prompt, n_steps=2, tuning={"attn_splits": 1})
+    assert max(errs) <= 1e-4 and agree == 2
+
+
+# ---- determinism and the device-token entry point ----
+
+def _make(env, cfg, seed, max_seq, tuning=None):
+    torch, oracle, mkp = env
+    host = synth.gen_weights(cfg, seed=seed)
+    dev_w = mkp.upload_weights(host)
+    mk = mkp.MegaKernel(shape_of(cfg), dev_w, max_seq, tuning=tuning)
+    return mk, host
+
+
+def test_bit_identical_reruns_and_device_token(env):
+    torch, oracle, mkp = env
+    cfg = synth.CONFIGS["tiny"].with_(dtype="bf16", n_heads=8, n_kv_heads=2, rope_theta=500000.0)
+    n_prompt, max_seq = 33, 40
+    mk, _ = _make(env, cfg, 11, max_seq)
+    toks = synth.gen_tokens(11, n_prompt + 1, cfg.vocab)
+    kv = mkp.KVCache(shape_of(cfg), max_seq)
+    mk.prefill_kv(toks[:n_prompt], 0, kv)
+    la = torch.empty(cfg.vocab, device="cuda")
+    lb = torch.empty(cfg.vocab, device="cuda")
+    mk.decode_step(int(toks[n_prompt]), n_prompt, kv, la)
+    # the same step again (it rewrites the same cache row with the same values)
+    mk.decode_step(int(toks[n_prompt]), n_prompt, kv, lb)
+    torch.cuda.synchronize()
+    assert torch.equal(la, lb), "two launches of the same step differ"
+    # device-token variant: same logits bit for bit, token = lowest-index argmax
+    tin = torch.tensor([int(toks[n_prompt])], dtype=torch.int32, device="cuda")
+    tout = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    lc = torch.empty(cfg.vocab, device="cuda")
+    mk.decode_step_device_token(tin, n_prompt, kv, lc, tout)
+    torch.cuda.synchronize()
+    assert mk.device_error() == 0
+    assert torch.equal(la, lc)
+    host_logits = la.cpu().numpy()
+    assert int(tout.item()) == int(np.flatnonzero(host_logits == host_logits.max())[0])
+    # and without logits
+    tout2 = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    mk.decode_step_device_token(tin, n_prompt, kv, None, tout2)
+    torch.cuda.synchronize()
+    assert int(tout2.item()) == int(tout.item())
+    mk.close()
+
+
+def test_prefill_equals_decode_loop(env):
+    # mk_prefill_kv(n) writes exactly the cache rows that n decode steps write
+    torch, oracle, mkp = env
+    cfg = synth.CONFIGS["tiny"].with_(dtype="bf16", n_heads=8, n_kv_heads=2, rope_theta=500000.0)
+    n, max_seq = 20, 24
+    mk, _ = _make(env, cfg, 12, max_seq)
+    toks = synth.gen_tokens(12, n, cfg.vocab)
+    kv1 = mkp.KVCache(shape_of(cfg), max_seq)
+    kv2 = mkp.KVCache(shape_of(cfg), max_seq)
+    mk.prefill_kv(toks, 0, kv1)
+    logits = torch.empty(cfg.vocab, device="cuda")
+    for i in range(n):
+        mk.decode_step(int(toks[i]), i, kv2, logits)
+    torch.cuda.synchronize()
+    assert mk.device_error() == 0
+    assert torch.equal(kv1.k, kv2.k) and torch.equal(kv1.v, kv2.v)
+    mk.close()
+
+
+def test_device_token_out_of_range_sets_device_error(env):
+    # a token id outside [0, vocab) read from device memory cannot be checked
+    # on the host: the kernel raises the device error flag (and embeds row 0)
+    torch, oracle, mkp = env
+    cfg = synth.CONFIGS["tiny"]
+    mk, _ = _make(env, cfg, 13, 8)
+    kv = mkp.KVCache(shape_of(cfg), 8)
+    tin = torch.tensor([cfg.vocab + 5], dtype=torch.int32, device="cuda")
+    tout = torch.empty(1, dtype=torch.int32, device="cuda")
+    mk.decode_step_device_token(tin, 0, kv, None, tout)
+    assert mk.device_error() == mkp.mk.MK_ERR_DEVICE
+    # the handle is now disabled
+    with pytest.raises(mkp.MkError):
+        mk.decode_step_device_token(tin, 1, kv, None, tout)
+    mk.close()
