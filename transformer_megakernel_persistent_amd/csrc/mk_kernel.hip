@@ -964,9 +964,17 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
     };
 
     // ---- epilogues (consumer 0) ----
+    // The rotary cos/sin pairs of this workgroup's query/key units depend only
+    // on the position, the same in every layer: consumer 0 keeps the first 64
+    // units' pairs in registers for the whole step.
+    const float *rope_row = p.rope + (size_t)P * d;  // [d/2][2]
+    auto rope_of_unit = [&](int u) -> f4v {
+        const int r = ((g.unit0[ST_QKV] + u) * 4) % d;  // query and key rows share the angles by head dim
+        return *(const f4v *)(rope_row + r);
+    };
+    const f4v rope_pre = (c == 0 && lane < g.units[ST_QKV]) ? rope_of_unit(lane) : f4v{0.f, 0.f, 0.f, 0.f};
     auto epi_qkv = [&](int l, float inv) {
         const int nqd = p.nh * d, nk = p.nkv * d;
-        const float *rope = p.rope + (size_t)P * d;  // [d/2][2]
         for (int u = lane; u < g.units[ST_QKV]; u += 64) {
             const int gr0 = (g.unit0[ST_QKV] + u) * 4;
             const float y0 = outv[u * 4] * inv, y1 = outv[u * 4 + 1] * inv;
@@ -975,8 +983,8 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
                 const bool isq = gr0 < nqd;
                 const int r = isq ? gr0 : gr0 - nqd;
                 const int head = r / d, m0 = (r % d) / 2;
-                const float c0 = rope[2 * m0], s0 = rope[2 * m0 + 1];
-                const float c1 = rope[2 * m0 + 2], s1 = rope[2 * m0 + 3];
+                const f4v rc = u < 64 ? rope_pre : rope_of_unit(u);
+                const float c0 = rc.x, s0 = rc.y, c1 = rc.z, s1 = rc.w;
                 const float a0 = y0 * c0 - y1 * s0, b0 = y0 * s0 + y1 * c0;
                 const float a1 = y2 * c1 - y3 * s1, b1 = y2 * s1 + y3 * c1;
                 if (isq) {
