@@ -283,6 +283,7 @@ static mk_status create_impl(const mk_model_desc *desc, const mk_weight_ptrs *wp
     P.ll_amax = P.ll_dpart + n_dpart;
     P.err = h->err;
     P.timeout_ticks = (int64_t)timeout_ms * wclk_khz;
+    P.err_check_ticks = (int64_t)wclk_khz / 50;  // 20 us
     P.trace = h->trace;
 
     const int64_t per_layer = (int64_t)((nh + 2 * nkv) * d) * H + (int64_t)H * nh * d + 3LL * H * F + 2LL * H;

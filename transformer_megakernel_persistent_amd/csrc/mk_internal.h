@@ -103,6 +103,7 @@ struct MkParams {
     int32_t *token_out;
     uint32_t tag;          // this launch's tag (never 0)
     int64_t timeout_ticks; // wall-clock ticks (100 MHz) before a grid wait gives up
+    int64_t err_check_ticks;  // wall-clock ticks a wait lasts before it also watches the device error word
     uint64_t *trace;       // optional [grid][5L+2][4] stage timeline, or null
 };
 

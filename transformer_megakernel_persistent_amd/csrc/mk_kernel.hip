@@ -499,10 +499,14 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
     int64_t poll_start = 0;
     // After a failed poll round: false once this workgroup aborted, the wait
     // timed out or the device error word is set (then the abort is marked).
+    // The error word is read only once a wait has lasted err_check_ticks:
+    // reading it after every failed round would add a second memory round
+    // trip to each poll period, and a healthy wait ends well before that.
     auto poll_ok = [&]() -> bool {
         if (ctl[1] != 0) return false;
-        const bool timed_out = wall_clock64() - poll_start > p.timeout_ticks;
-        if (timed_out || ldcu(p.err) != 0u) {
+        const int64_t waited = wall_clock64() - poll_start;
+        const bool timed_out = waited > p.timeout_ticks;
+        if (timed_out || (waited > p.err_check_ticks && ldcu(p.err) != 0u)) {
             if (lane == 0) {
                 if (timed_out) __hip_atomic_fetch_or(p.err, MK_DEVERR_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 ctl[1] = step;
@@ -541,6 +545,12 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
 #pragma unroll
             for (int u = 0; u < 8; ++u)
                 if (base + u * 256 < npc) mask |= 1u << u;
+            // the gain slice does not depend on the records: load it first so
+            // its latency hides behind the first poll round
+            f2v gg[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                gg[u] = (gain && (mask & (1u << u))) ? *(const f2v *)(gain + 2 * (base + u * 256)) : f2v{1.f, 1.f};
             u4v v[8];
             if (!poll16<8>(rs, [&](int u) { return off(base + u * 256); }, mask, v, tag, poll_ok)) {
                 good = false;
@@ -553,8 +563,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
                     const float x0 = __uint_as_float(v[u].x), x1 = __uint_as_float(v[u].z);
                     ss = fmaf(x0, x0, ss);
                     ss = fmaf(x1, x1, ss);
-                    const float g0 = gain ? gain[e] : 1.f, g1 = gain ? gain[e + 1] : 1.f;
-                    *(LDS f2v *)(dst + e) = f2v{g0 * x0, g1 * x1};
+                    *(LDS f2v *)(dst + e) = gg[u] * f2v{x0, x1};
                 }
             }
         }
