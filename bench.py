@@ -105,6 +105,10 @@ def main():
     ap.add_argument("--ring", type=int, default=0)
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--prefetch-depth", type=int, default=0,
+                    help="slots the loads run ahead (default: ring slots - 1); an ablation knob")
+    ap.add_argument("--stage-drain", action="store_true",
+                    help="ablation: no loads for a stage before its grid dependency is met")
     ap.add_argument("--launch", choices=["cooperative", "ordinary"], default="ordinary",
                     help="cooperative launch (co-residency checked by the runtime) or an ordinary launch")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -136,7 +140,8 @@ def main():
     print(f"[bench] {cfg.name}: weights generated in {time.perf_counter() - t:.1f}s", file=sys.stderr, flush=True)
     dev_w = mkp.upload_weights(host_w, dev)
     tuning = {"grid": args.grid, "ring_slots": args.ring, "attn_splits": args.splits,
-              "cooperative": 1 if args.launch == "cooperative" else 2}
+              "cooperative": 1 if args.launch == "cooperative" else 2,
+              "prefetch_depth": args.prefetch_depth, "stage_drain": 1 if args.stage_drain else 0}
     mk = mkp.MegaKernel(shape, dev_w, max_seq, tuning=tuning)
     del dev_w
     torch.cuda.empty_cache()
@@ -205,6 +210,7 @@ def main():
                         f"{cfg.dtype} weights+KV, fp32 accumulate; {ctx}-token context, {steps} greedy steps, batch 1",
             "context": ctx, "global_batch": 1, "decode_positions": [pos, pos + steps - 1],
             "launches_per_token": 1, "grid": info["grid"], "ring_slots": info["ring_slots"],
+            "prefetch_slots": info["prefetch_slots"], "stage_drain": bool(args.stage_drain),
             "attn_splits": info["attn_splits"], "block_threads": info["block_threads"],
             "lds_bytes": info["lds_bytes"], "launch": args.launch, "parallelism": "single GPU"},
         "us_per_token_p50": p50,

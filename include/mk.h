@@ -106,9 +106,16 @@ typedef struct {
                   the grid waits end by timeout with the device error flag,
                   never by a hang;
      trace:       1 = record a per-workgroup stage timeline on every step
-                  (read it with mk_read_trace; default 0 = off). */
+                  (read it with mk_read_trace; default 0 = off);
+     prefetch_depth: 16 KiB slots the weight and cache loads run ahead of
+                  the slot being multiplied, 1 .. ring_slots - 1 (default
+                  ring_slots - 1);
+     stage_drain: 1 = no cross-stage prefetch: a stage's first loads wait
+                  for the grid dependency before it (the consumers' opening
+                  barrier of the stage); 0 = loads run ahead across stage
+                  boundaries (default).  An ablation knob. */
 typedef struct {
-    int32_t grid, ring_slots, attn_splits, timeout_ms, cooperative, trace;
+    int32_t grid, ring_slots, attn_splits, timeout_ms, cooperative, trace, prefetch_depth, stage_drain;
 } mk_tuning;
 
 typedef struct mk_handle mk_handle;
@@ -116,6 +123,7 @@ typedef struct mk_handle mk_handle;
 /* Read-only facts about a created handle (for benchmarks and tests). */
 typedef struct {
     int32_t grid, ring_slots, attn_splits, block_threads, lds_bytes, cu_count;
+    int32_t prefetch_slots;  /* 16 KiB slots the loads run ahead of the arithmetic */
     int64_t packed_bytes;    /* library-owned pre-laid-out weight bytes */
     int64_t weight_bytes;    /* algorithmic weight bytes read per step */
 } mk_info;
@@ -159,14 +167,20 @@ mk_status mk_get_device_error(mk_handle *h);
 mk_status mk_get_info(const mk_handle *h, mk_info *info);
 
 /* Stage timeline of the most recent step (handles created with trace = 1):
-   synchronizes the last stream, then copies grid * (5*n_layers + 2) * 4
-   uint64 wall-clock ticks (100 MHz on MI355X) into host_out, laid out
-   [workgroup][boundary][event].  Boundary 5l+k is the start of stage k of
-   layer l (k: 0 QKV, 1 attention, 2 O, 3 gate/up, 4 down), 5L the LM head,
-   5L+1 the end of the step.  Events: 0 boundary reached (all of the previous
-   stage consumed), 1 previous stage finished and published, 2 inputs of the
-   next stage available (dependency wait over), 3 inputs loaded.  Unrecorded
-   entries are 0.  capacity is the number of uint64 host_out can hold. */
+   synchronizes the last stream, then copies uint64 wall-clock ticks (100 MHz
+   on MI355X) into host_out, three arrays one after the other:
+   1. grid * (5*n_layers + 2) * 4, laid out [workgroup][boundary][event].
+      Boundary 5l+k is the start of stage k of layer l (k: 0 QKV,
+      1 attention, 2 O, 3 gate/up, 4 down), 5L the LM head, 5L+1 the end of
+      the step.  Events: 0 boundary reached (all of the previous stage
+      consumed), 1 previous stage finished and published, 2 inputs of the
+      next stage available (dependency wait over), 3 inputs loaded.
+   2. grid * 64 * 2: consumer 0's first 64 data steps of layer 1
+      [workgroup][step][0 barrier passed, 1 arithmetic done].
+   3. grid * 96 * 2: loader 0's first 96 barriers of layer 1
+      [workgroup][barrier][0 arrival, 1 exit].
+   Unrecorded entries are 0.  capacity is the number of uint64 host_out can
+   hold (at least the sum of the three sizes). */
 mk_status mk_read_trace(mk_handle *h, uint64_t *host_out, int64_t capacity);
 
 const char *mk_status_str(mk_status s);

@@ -129,12 +129,24 @@ def test_first_position_with_poisoned_cache(env):
     assert max(errs) <= 1e-4 and agree == 3
 
 
-@pytest.mark.parametrize("grid,splits,ring", [(64, 8, 3), (37, 5, 4), (256, 1, 8)])
-def test_tiny_other_launch_shapes(env, grid, splits, ring):
+# depth: slots the loads run ahead (0: ring - 1); drain: no cross-stage prefetch
+@pytest.mark.parametrize("grid,splits,ring,depth,drain", [(64, 8, 3, 0, 0), (37, 5, 4, 0, 0), (256, 1, 8, 0, 0),
+                                                          (256, 1, 9, 0, 0), (64, 8, 3, 1, 0), (37, 5, 4, 2, 1),
+                                                          (256, 1, 8, 1, 1), (256, 1, 8, 0, 1)])
+def test_tiny_other_launch_shapes(env, grid, splits, ring, depth, drain):
     cfg = synth.CONFIGS["tiny"]
     errs, agree = run_pair(env, cfg, seed=4, n_prompt=21, n_steps=3,
-                           tuning={"grid": grid, "attn_splits": splits, "ring_slots": ring})
+                           tuning={"grid": grid, "attn_splits": splits, "ring_slots": ring, "prefetch_depth": depth,
+                                   "stage_drain": drain})
     assert max(errs) <= 1e-4 and agree == 3
+
+
+def test_prefetch_depth_beyond_ring_is_rejected(env):
+    torch, oracle, mkp = env
+    cfg = synth.CONFIGS["tiny"]
+    with pytest.raises(mkp.MkError) as e:
+        _make(env, cfg, seed=0, max_seq=32, tuning={"ring_slots": 4, "prefetch_depth": 4})
+    assert e.value.status == mkp.mk.MK_ERR_TUNING
 
 
 def test_llama1b_full_size_synthetic_context(env):
@@ -143,9 +155,11 @@ def test_llama1b_full_size_synthetic_context(env):
     assert max(errs) <= 2e-2 and agree == 3
 
 
-def test_llama1b_prefill_short_prompt(env):
+@pytest.mark.parametrize("depth,drain", [(0, 0), (2, 1)])
+def test_llama1b_prefill_short_prompt(env, depth, drain):
     cfg = synth.CONFIGS["llama1b"]
-    errs, agree = run_pair(env, cfg, seed=6, n_prompt=5, n_steps=2, gains="random")
+    errs, agree = run_pair(env, cfg, seed=6, n_prompt=5, n_steps=2, gains="random",
+                           tuning={"prefetch_depth": depth, "stage_drain": drain})
     assert max(errs) <= 2e-2 and agree == 2
 
 

@@ -75,7 +75,8 @@ mk_status validate_desc(const mk_model_desc *d) {
 mk_status validate_tuning(const mk_tuning *t) {
     if (!t) return MK_OK;
     if (t->grid < 0 || t->grid > MK_MAX_GRID || t->ring_slots < 0 || t->attn_splits < 0 || t->attn_splits > MK_MAX_SPLITS || t->timeout_ms < 0 ||
-        t->cooperative < 0 || t->cooperative > 2 || t->trace < 0 || t->trace > 1)
+        t->cooperative < 0 || t->cooperative > 2 || t->trace < 0 || t->trace > 1 || t->prefetch_depth < 0 ||
+        t->stage_drain < 0 || t->stage_drain > 1)
         return MK_ERR_TUNING;
     if (t->ring_slots != 0 && (t->ring_slots < 3 || t->ring_slots > MK_MAX_RING)) return MK_ERR_TUNING;
     return MK_OK;
@@ -197,6 +198,7 @@ static mk_status create_impl(const mk_model_desc *desc, const mk_weight_ptrs *wp
     if (ns > MK_DEFAULT_RING && !t.ring_slots) ns = MK_DEFAULT_RING;  // a 9th slot measured no faster
     if (ns > MK_MAX_RING) ns = MK_MAX_RING;
     if (ns < 3 || fixed + ns * MK_SLOT_BYTES > MK_LDS_LIMIT) return MK_ERR_SHAPE;
+    if (t.prefetch_depth > ns - 1) return MK_ERR_TUNING;  // a load needs a consumed ring slot
     h->lds_bytes = mk_kernel_lds_bytes(ns, vec_floats, out_rows, dtype, d, gq);
     const int per_cu = mk_kernel_max_blocks_per_cu(dtype, gq, lpp, h->lds_bytes);
     if (per_cu < 1) return MK_ERR_SHAPE;
@@ -221,7 +223,8 @@ static mk_status create_impl(const mk_model_desc *desc, const mk_weight_ptrs *wp
     HIP_TRY(hipMalloc(&h->err, 64 * sizeof(uint32_t)));
     HIP_TRY(hipMemset(h->err, 0, 64 * sizeof(uint32_t)));
     if (t.trace) {
-        h->trace_len = (int64_t)grid * (5 * L + 2) * 4 + (int64_t)grid * 64 * 2;
+        // stage timeline, consumer data steps of layer 1, loader barriers of layer 1
+        h->trace_len = (int64_t)grid * (5 * L + 2) * 4 + (int64_t)grid * 64 * 2 + (int64_t)grid * 96 * 2;
         HIP_TRY(hipMalloc(&h->trace, h->trace_len * sizeof(uint64_t)));
         HIP_TRY(hipMemset(h->trace, 0, h->trace_len * sizeof(uint64_t)));
     }
@@ -270,6 +273,8 @@ static mk_status create_impl(const mk_model_desc *desc, const mk_weight_ptrs *wp
     P.L = L; P.H = H; P.nh = nh; P.nkv = nkv; P.d = d; P.F = F; P.V = V; P.max_seq = D.max_seq;
     P.eps = (float)D.rms_eps;
     P.grid = grid; P.ring_slots = ns; P.splits = splits; P.lds_vec_floats = vec_floats; P.lds_out_rows = out_rows;
+    P.prefetch_depth = t.prefetch_depth ? t.prefetch_depth : ns - 1;
+    P.stage_drain = t.stage_drain;
     P.packed = h->packed;
     P.g_attn = h->gains; P.g_ffn = h->gains + (size_t)L * H; P.g_final = h->gains + (size_t)2 * L * H;
     P.embed = h->embed;
@@ -404,6 +409,7 @@ extern "C" mk_status mk_get_info(const mk_handle *h, mk_info *info) {
     if (!h || !info) return MK_ERR_NULL;
     info->grid = h->base.grid;
     info->ring_slots = h->base.ring_slots;
+    info->prefetch_slots = h->base.prefetch_depth;
     info->attn_splits = h->base.splits;
     info->block_threads = MK_BLOCK_THREADS;
     info->lds_bytes = h->lds_bytes;

@@ -19,10 +19,10 @@
 #define MK_SLOT_BYTES 16384
 #define MK_CHUNK_BYTES 1024
 #define MK_CHUNKS_PER_SLOT 16
-#define MK_NUM_LOADERS 2
+#define MK_NUM_LOADERS 4
 #define MK_NUM_CONSUMERS 4
 #define MK_BLOCK_THREADS (64 * (MK_NUM_LOADERS + MK_NUM_CONSUMERS))
-#define MK_MAX_RING 9  // the loaders wait for (ring-2)*8 outstanding loads: at most 63
+#define MK_MAX_RING 9  // LDS bound; the loaders wait for (ring-2)*4 outstanding loads (at most 63)
 #define MK_DEFAULT_RING 8
 #define MK_LDS_LIMIT 163840
 #define MK_MAX_GRID 1024
@@ -71,6 +71,8 @@ struct MkParams {
     float eps;
     // launch shape
     int32_t grid, ring_slots, splits, lds_vec_floats, lds_out_rows;
+    int32_t prefetch_depth;  // slots the loads run ahead of the arithmetic, 1 .. ring_slots-1
+    int32_t stage_drain;     // 1: no loads for a stage before its opening barrier
     // weights
     const unsigned char *packed;
     MkStage st[ST_NUM];

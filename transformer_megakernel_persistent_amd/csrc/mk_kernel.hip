@@ -49,6 +49,7 @@ typedef float f4v __attribute__((ext_vector_type(4)));
 typedef float f2v __attribute__((ext_vector_type(2)));
 
 #define LDS __attribute__((address_space(3)))
+#define GLB __attribute__((address_space(1)))
 #define MK_COMPILER_BARRIER() asm volatile("" ::: "memory")
 #define MK_WAIT_VM0() asm volatile("s_waitcnt vmcnt(0)" ::: "memory")
 
@@ -82,15 +83,24 @@ template <int N>
 __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
 }
+// n a multiple of 4 up to 60; anything else waits for every load
 __device__ __forceinline__ void wait_vm_rt(int n) {
     switch (n) {
+    case 4: wait_vm<4>(); break;
     case 8: wait_vm<8>(); break;
+    case 12: wait_vm<12>(); break;
     case 16: wait_vm<16>(); break;
+    case 20: wait_vm<20>(); break;
     case 24: wait_vm<24>(); break;
+    case 28: wait_vm<28>(); break;
     case 32: wait_vm<32>(); break;
+    case 36: wait_vm<36>(); break;
     case 40: wait_vm<40>(); break;
+    case 44: wait_vm<44>(); break;
     case 48: wait_vm<48>(); break;
+    case 52: wait_vm<52>(); break;
     case 56: wait_vm<56>(); break;
+    case 60: wait_vm<60>(); break;
     default: wait_vm<0>(); break;
     }
 }
@@ -285,11 +295,6 @@ __device__ __forceinline__ void make_geo(const MkParams &p, int w, int epl, Geo 
     g.nsl[ST_DOWN] = g.dn.nsl;
 }
 
-// Order of streamed stages inside a layer; index 1 is the KV stream.
-// kind 0: QKV, 1: KV, 2: O, 3: GU, 4: DOWN.  After the last layer: LM.
-__device__ __forceinline__ int st_of_kind(int kind) {
-    return kind == 0 ? ST_QKV : kind == 2 ? ST_O : kind == 3 ? ST_GU : kind == 4 ? ST_DOWN : ST_LM;
-}
 
 }  // namespace
 
@@ -358,113 +363,217 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
 
     if (wave < MK_NUM_LOADERS) {
         // ============================ loader ============================
-        const int wl = wave;
-        // this workgroup's weight blocks for layer 0, and the per-layer strides
-        const unsigned char *wb_q = p.packed + p.st[ST_QKV].base + p.st[ST_QKV].wg_off[w];
-        const unsigned char *wb_o = p.packed + p.st[ST_O].base + p.st[ST_O].wg_off[w];
-        const unsigned char *wb_gu = p.packed + p.st[ST_GU].base + p.st[ST_GU].wg_off[w];
-        const unsigned char *wb_dn = p.packed + p.st[ST_DOWN].base + p.st[ST_DOWN].wg_off[w];
-        const unsigned char *wb_lm = p.packed + p.st[ST_LM].base + p.st[ST_LM].wg_off[w];
+        const int wl = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform: keeps buffer resources scalar
+        // Each loader carries CPW of a slot's 16 chunks: chunks [wl*CPW, wl*CPW + CPW).
+        // In a cache slot chunks 0-7 are K and 8-15 are V, so the first half
+        // of the loaders reads K and the second half V.
+        constexpr int CPW = MK_CHUNKS_PER_SLOT / MK_NUM_LOADERS;
+        constexpr int HALF = MK_NUM_LOADERS / 2;
+        constexpr uint32_t WAVE_BYTES = CPW * MK_CHUNK_BYTES;  // this wave's share of a slot
+        const unsigned char *kv_src = (const unsigned char *)(wl < HALF ? p.kc : p.vc);
+        const int64_t kv_skip = (int64_t)(wl % HALF) * CPW * MK_CHUNK_BYTES;  // bytes before this loader's first K (V) chunk
+
+        // this workgroup's weight blocks for layer 0 (this wave's share), and
+        // the per-layer strides
+        const unsigned char *wb_q = p.packed + p.st[ST_QKV].base + p.st[ST_QKV].wg_off[w] + wl * WAVE_BYTES;
+        const unsigned char *wb_o = p.packed + p.st[ST_O].base + p.st[ST_O].wg_off[w] + wl * WAVE_BYTES;
+        const unsigned char *wb_gu = p.packed + p.st[ST_GU].base + p.st[ST_GU].wg_off[w] + wl * WAVE_BYTES;
+        const unsigned char *wb_dn = p.packed + p.st[ST_DOWN].base + p.st[ST_DOWN].wg_off[w] + wl * WAVE_BYTES;
+        const unsigned char *wb_lm = p.packed + p.st[ST_LM].base + p.st[ST_LM].wg_off[w] + wl * WAVE_BYTES;
         const int64_t ws_q = p.st[ST_QKV].layer_stride, ws_o = p.st[ST_O].layer_stride,
                       ws_gu = p.st[ST_GU].layer_stride, ws_dn = p.st[ST_DOWN].layer_stride;
-        int it_l = 0, it_k = 0, it_n = 0;
-        bool done = false;
-        // position the iterator on the first non-empty stage
-        auto settle = [&]() {
-            while (!done && it_n >= nslots(it_k)) {
-                it_n = 0;
-                if (it_k == 5) { done = true; break; }
-                if (++it_k == 5) {
-                    if (++it_l == L) {
-                        if (LOGITS) it_k = 5; else done = true;
-                    } else {
-                        it_k = 0;
-                    }
-                }
-            }
+        const unsigned char *kv_l0 = kv_src + (int64_t)kvj * (int64_t)head_bytes + (int64_t)t0 * d * EB + kv_skip;
+        const int64_t kv_lstride = (int64_t)p.nkv * (int64_t)head_bytes;
+
+        // ---- the stream: every slot of every stage, in consumption order ----
+        // (it_l, it_k) is the current stage (kind 0 QKV, 1 KV, 2 O, 3 gate/up,
+        // 4 down; kind 5 the LM head after the last layer), it_left the slots
+        // left in it, it_ptr this wave's source of the current slot.  A slot
+        // costs a pointer step; the stage bookkeeping runs once per stage.
+        int it_l = 0, it_k = 0, it_left = 0;
+        bool done = false, it_kv = false;
+        const unsigned char *it_ptr = p.packed;
+        int64_t it_step = 0, kv_rem = 0;  // kv_rem: bytes of this wave's chunks left in the split
+        auto last_kind = [&]() { return it_k == 5 || (!LOGITS && it_l == L - 1 && it_k == 4); };
+        // past the end of the stream: harmless re-reads of the first bytes of the weights
+        auto finish = [&]() {
+            done = true;
+            it_kv = false;
+            it_ptr = p.packed;
+            it_step = 0;
         };
-        settle();
-        auto issue = [&](int buf) {
-            LDS unsigned char *dst = ring + buf * MK_SLOT_BYTES + wl * 8 * MK_CHUNK_BYTES;
-            if (done) {
-#pragma unroll
-                for (int c = 0; c < 8; ++c)
-                    __builtin_amdgcn_global_load_lds((const void *)(p.packed + c * MK_CHUNK_BYTES + lane * 16),
-                                                     (LDS void *)(dst + c * MK_CHUNK_BYTES),
-                                                     16, 0, 0);
+        // Position on stage (it_l, it_k) or the first non-empty stage after it
+        // (bounded: every stage is visited at most once).
+        auto stage_setup = [&]() {
+            for (int guard = 0; guard <= 5 * L + 1; ++guard) {
+                const int n = nslots(it_k);
+                if (n > 0) {
+                    it_left = n;
+                    it_kv = it_k == 1;
+                    if (it_kv) {
+                        it_ptr = kv_l0 + (int64_t)it_l * kv_lstride;
+                        it_step = (int64_t)BP * d * EB;
+                        kv_rem = (int64_t)(t1 - t0) * d * EB - kv_skip;
+                    } else {
+                        switch (it_k) {
+                        case 0: it_ptr = wb_q + (int64_t)it_l * ws_q; break;
+                        case 2: it_ptr = wb_o + (int64_t)it_l * ws_o; break;
+                        case 3: it_ptr = wb_gu + (int64_t)it_l * ws_gu; break;
+                        case 4: it_ptr = wb_dn + (int64_t)it_l * ws_dn; break;
+                        default: it_ptr = wb_lm; break;
+                        }
+                        it_step = MK_SLOT_BYTES;
+                    }
+                    return;
+                }
+                if (last_kind()) break;
+                if (++it_k == 5 && ++it_l < L) it_k = 0;  // after the last layer: the LM head
+            }
+            finish();
+        };
+        auto advance = [&]() {
+            if (done) return;
+            if (--it_left > 0) {
+                it_ptr += it_step;
+                kv_rem -= it_step;
                 return;
             }
-            if (it_k == 1) {
-                const unsigned char *base = (const unsigned char *)(wl == 0 ? p.kc : p.vc) +
-                                            ((size_t)it_l * p.nkv + kvj) * head_bytes;
-                const size_t lim = (size_t)t1 * d * EB;
-                const size_t off0 = ((size_t)t0 + (size_t)it_n * BP) * d * EB + lane * 16;
-#pragma unroll
-                for (int c = 0; c < 8; ++c) {
-                    size_t off = off0 + c * MK_CHUNK_BYTES;
-                    if (off >= lim) off = (lane % LPP) * 16;  // beyond the split: re-read position 0, masked by consumers
-                    __builtin_amdgcn_global_load_lds((const void *)(base + off),
-                                                     (LDS void *)(dst + c * MK_CHUNK_BYTES),
-                                                     16, 0, 0);
-                }
-            } else {
-                const unsigned char *blk;
-                int64_t stride;
-                switch (it_k) {
-                case 0: blk = wb_q; stride = ws_q; break;
-                case 2: blk = wb_o; stride = ws_o; break;
-                case 3: blk = wb_gu; stride = ws_gu; break;
-                case 4: blk = wb_dn; stride = ws_dn; break;
-                default: blk = wb_lm; stride = 0; break;
-                }
-                const unsigned char *src = blk + (int64_t)it_l * stride + (int64_t)it_n * MK_SLOT_BYTES +
-                                           wl * 8 * MK_CHUNK_BYTES + lane * 16;
-#pragma unroll
-                for (int c = 0; c < 8; ++c)
-                    __builtin_amdgcn_global_load_lds((const void *)(src + c * MK_CHUNK_BYTES),
-                                                     (LDS void *)(dst + c * MK_CHUNK_BYTES),
-                                                     16, 0, 2 /* nt: streamed once */);
+            if (last_kind()) {
+                finish();
+                return;
             }
-            ++it_n;
-            settle();
+            if (++it_k == 5 && ++it_l < L) it_k = 0;
+            stage_setup();
         };
-        for (int i = 0; i < NS - 1; ++i) issue(i);
-        int jl = NS - 1;  // ring slot the next issue fills
+        stage_setup();
+        // This lane's 16 bytes of chunk c of the current slot.  Cache rows
+        // past the split re-read the first bytes of the weights instead (the
+        // consumers mask those positions).  Global loads: direct-to-LDS
+        // buffer loads measured slower for this stream.
+        auto piece_src = [&](int c) -> const GLB u4v * {
+            const int64_t o = (int64_t)c * MK_CHUNK_BYTES + lane * 16;
+            return (const GLB u4v *)(!it_kv || o < kv_rem ? it_ptr + o : p.packed + lane * 16);
+        };
+        // direct-to-LDS loads of the current slot into ring slot buf
+        auto issue = [&](int buf) {
+            LDS unsigned char *dst = ring + buf * MK_SLOT_BYTES + wl * WAVE_BYTES;
+            if (it_kv) {
+#pragma unroll
+                for (int c = 0; c < CPW; ++c)
+                    __builtin_amdgcn_global_load_lds((const void *)piece_src(c), (LDS void *)(dst + c * MK_CHUNK_BYTES), 16, 0, 0);
+            } else {
+#pragma unroll
+                for (int c = 0; c < CPW; ++c)
+                    __builtin_amdgcn_global_load_lds((const void *)piece_src(c), (LDS void *)(dst + c * MK_CHUNK_BYTES), 16, 0,
+                                                     2 /* nt: streamed once */);
+            }
+            advance();
+        };
+
         int lstep = 0;  // barriers passed; mirrors the consumers' step counter
-        const int wait_n = (NS - 2) * 8;
-        // ctl[1] holds the step in which a consumer aborted (0: none).  The
-        // consumers pass exactly one more barrier after aborting, so "aborted
-        // in an earlier step" is stable when read here.
-        auto aborted = [&]() { const int a = ctl[1]; return a != 0 && a < lstep; };
-        auto vstep = [&]() -> bool {
-            MK_COMPILER_BARRIER();
-            __builtin_amdgcn_s_barrier();
-            MK_COMPILER_BARRIER();
-            ++lstep;
-            return !aborted();
+        // optional timeline: loader 0's arrival at and exit from the barriers
+        // of layer 1 (and the start of layer 2), barrier indices [b0, b0 + 96)
+        const int lb0 = 5 + nsl_q + nsl_kv + nsl_o + nsl_gu + nsl_dn;
+        auto lstamp = [&](int e) {
+            if (p.trace && wl == 0 && lane == 0 && lstep >= lb0 && lstep < lb0 + 96)
+                p.trace[(size_t)G * (5 * L + 2) * 4 + (size_t)G * 64 * 2 + ((size_t)w * 96 + lstep - lb0) * 2 + e] =
+                    wall_clock64();
         };
-        auto dstep = [&]() -> bool {
-            wait_vm_rt(wait_n);
+        const int total = L * (nsl_q + nsl_kv + nsl_o + nsl_gu + nsl_dn) + (LOGITS ? nsl_lm : 0);
+        // Slot m goes straight into ring slot m % NS.  The loads run up to
+        // `depth` slots ahead of the slot being consumed (at most NS-1: the
+        // ring slot must have been consumed) and, unless stage_drain is set,
+        // across stage boundaries; with stage_drain a stage's first loads wait
+        // for its opening barrier.  `issued` counts the slots issued so far,
+        // so the wait before data step k is exact: slot k's loads are done
+        // when at most (issued - 1 - k) * CPW newer loads are outstanding.
+        const int depth = p.prefetch_depth;
+        int issued = 0, cons = 0;                  // slots issued; data barriers passed
+        int cap = p.stage_drain ? -1 : total - 1;  // last slot that may be issued now
+        int jl = 0;                                // ring slot of the next issue
+        auto issue_more = [&]() {
+            int lim = cons - 1 + depth;
+            if (lim > cap) lim = cap;
+            while (issued <= lim) {
+                issue(jl);
+                jl = jl + 1 == NS ? 0 : jl + 1;
+                ++issued;
+            }
+        };
+
+        // ctl[1] holds the step in which a consumer aborted (0: none).  The
+        // consumers pass exactly one more barrier after aborting and leave; a
+        // barrier then waits for the remaining waves only.  So the loaders
+        // read the word only at stage openings: the data-step path stays
+        // short, and after an abort the rest of the current stage is merely
+        // loaded in vain before they leave too.
+        auto bar = [&]() {
+            lstamp(0);
             MK_COMPILER_BARRIER();
             __builtin_amdgcn_s_barrier();
             MK_COMPILER_BARRIER();
+            lstamp(1);
             ++lstep;
-            if (aborted()) return false;
-            issue(jl);
-            jl = jl + 1 == NS ? 0 : jl + 1;
+        };
+        auto bar_check = [&]() -> bool {  // false: the consumers aborted in an earlier step
+            bar();
+            const int a = ctl[1];
+            return a == 0 || a >= lstep;
+        };
+        // The consumers' barrier sequence: each stage (layer sl, kind sk)
+        // opens with one barrier, then has one per data slot; one more closes
+        // the step.  wleft counts the data barriers left in the current stage.
+        int sl = 0, sk = -1, wleft = 0;
+        bool dead = false;
+        auto walk_next = [&]() -> bool {  // to the next stage; false after the last one
+            if (sk < 0) {
+                sk = 0;
+                return true;
+            }
+            if (sk == 5 || (!LOGITS && sl == L - 1 && sk == 4)) return false;
+            if (++sk == 5 && ++sl < L) sk = 0;
             return true;
         };
-        bool ok = true;
-        for (int l = 0; l < L && ok; ++l)
-            for (int kind = 0; kind < 5 && ok; ++kind) {
-                ok = vstep();
-                for (int n = 0; n < nslots(kind) && ok; ++n) ok = dstep();
+        // Opening barriers up to the next stage that has data steps.
+        auto open_next = [&]() {
+            for (int guard = 0; guard <= 5 * L + 1; ++guard) {
+                if (!walk_next()) return;
+                if (!bar_check()) {
+                    dead = true;
+                    return;
+                }
+                wleft = nslots(sk);
+                if (wleft > 0) {
+                    if (p.stage_drain) {  // this stage's loads may start now
+                        cap = cons + wleft - 1;
+                        issue_more();
+                    }
+                    return;
+                }
             }
-        if (ok && LOGITS) {
-            ok = vstep();
-            for (int n = 0; n < nsl_lm && ok; ++n) ok = dstep();
+        };
+        // The stages after the last data step (none has data steps) and the
+        // closing barrier.
+        auto close_walk = [&]() {
+            if (dead) return;
+            for (int guard = 0; guard <= 5 * L + 1; ++guard) {
+                if (!walk_next()) break;
+                if (!bar_check()) return;
+            }
+            bar();
+        };
+
+        issue_more();
+        for (int k = 0; k < total; ++k) {
+            if (wleft == 0) open_next();
+            if (dead) break;
+            wait_vm_rt((issued - 1 - k) * CPW);
+            bar();
+            ++cons;
+            --wleft;
+            issue_more();
         }
-        if (ok) vstep();
+        close_walk();
         wait_vm<0>();
         return;
     }

@@ -46,13 +46,14 @@ class KVDesc(ctypes.Structure):
 
 class Tuning(ctypes.Structure):
     _fields_ = [("grid", ctypes.c_int32), ("ring_slots", ctypes.c_int32), ("attn_splits", ctypes.c_int32),
-                ("timeout_ms", ctypes.c_int32), ("cooperative", ctypes.c_int32), ("trace", ctypes.c_int32)]
+                ("timeout_ms", ctypes.c_int32), ("cooperative", ctypes.c_int32), ("trace", ctypes.c_int32),
+                ("prefetch_depth", ctypes.c_int32), ("stage_drain", ctypes.c_int32)]
 
 
 class Info(ctypes.Structure):
     _fields_ = [("grid", ctypes.c_int32), ("ring_slots", ctypes.c_int32), ("attn_splits", ctypes.c_int32),
                 ("block_threads", ctypes.c_int32), ("lds_bytes", ctypes.c_int32), ("cu_count", ctypes.c_int32),
-                ("packed_bytes", ctypes.c_int64), ("weight_bytes", ctypes.c_int64)]
+                ("prefetch_slots", ctypes.c_int32), ("packed_bytes", ctypes.c_int64), ("weight_bytes", ctypes.c_int64)]
 
 
 _lib = None
@@ -184,9 +185,13 @@ class MegaKernel:
         import numpy as np
         n_b = 5 * self.shape["n_layers"] + 2
         grid = self.info()["grid"]
-        raw = np.zeros(grid * n_b * 4 + grid * 64 * 2, dtype=np.uint64)
+        n_stage, n_steps = grid * n_b * 4, grid * 64 * 2
+        raw = np.zeros(n_stage + n_steps + grid * 96 * 2, dtype=np.uint64)
         _check(load_library().mk_read_trace(self._h, raw.ctypes.data_as(ctypes.c_void_p), raw.size), "mk_read_trace")
-        self.last_steps = raw[grid * n_b * 4:].reshape(grid, 64, 2)
+        # consumer 0's layer-1 data steps (barrier exit, compute done) and
+        # loader 0's layer-1 barriers (arrival, exit)
+        self.last_steps = raw[n_stage:n_stage + n_steps].reshape(grid, 64, 2)
+        self.last_loader = raw[n_stage + n_steps:].reshape(grid, 96, 2)
         return raw[:grid * n_b * 4].reshape(grid, n_b, 4)
 
     def close(self):
