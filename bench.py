@@ -58,6 +58,38 @@ def traffic_from_profile(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+HOST_ORACLE_MAX_BYTES = 40e9
+
+
+def load_model(mkp, synth, cfg, shape, max_seq, tuning, seed, dev, keep_host):
+    """A handle made by mk_create_deferred; each layer is generated on the
+    host, uploaded, pre-laid out by mk_load_weights and freed, so the device
+    never holds more than one layer twice (an 80-layer hidden-8192 model
+    would not fit twice).  Returns the handle and, if keep_host, the host
+    weights (for the oracle baseline)."""
+    mk = mkp.MegaKernel(shape, None, max_seq, tuning=tuning)
+    host_layers = []
+    for l in range(cfg.n_layers):
+        lw = {k: synth.gen_tensor(cfg, seed, k, layer=l) for k in synth.LAYER_KINDS}
+        part = mkp.upload_weights({"layers": [lw]}, dev)
+        mk.load_weights(part, first_layer=l)
+        del part
+        if keep_host:
+            host_layers.append(lw)
+        if l % 16 == 15:
+            print(f"[bench] loaded layer {l + 1}/{cfg.n_layers}", file=sys.stderr, flush=True)
+    head = {"embed": synth.gen_tensor(cfg, seed, "embed"), "final_norm": synth.gen_tensor(cfg, seed, "final_norm")}
+    if not cfg.tied:
+        head["lm_head"] = synth.gen_tensor(cfg, seed, "lm_head")
+    part = mkp.upload_weights(head, dev)
+    mk.load_weights(part)
+    del part
+    if not keep_host:
+        return mk, None
+    head["layers"] = host_layers
+    return mk, head
+
+
 def percentile(xs, q):
     xs = sorted(xs)
     if not xs:
@@ -135,15 +167,16 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    t = time.perf_counter()
-    host_w = synth.gen_weights(cfg, seed=args.seed)
-    print(f"[bench] {cfg.name}: weights generated in {time.perf_counter() - t:.1f}s", file=sys.stderr, flush=True)
-    dev_w = mkp.upload_weights(host_w, dev)
     tuning = {"grid": args.grid, "ring_slots": args.ring, "attn_splits": args.splits,
               "cooperative": 1 if args.launch == "cooperative" else 2,
               "prefetch_depth": args.prefetch_depth, "stage_drain": 1 if args.stage_drain else 0}
-    mk = mkp.MegaKernel(shape, dev_w, max_seq, tuning=tuning)
-    del dev_w
+    # The oracle baseline needs every weight in host memory; past this size it
+    # is not taken (the weights are streamed to the device a layer at a time).
+    keep_host = not args.no_cpu_baseline and cfg.weight_bytes_per_step() <= HOST_ORACLE_MAX_BYTES
+    t = time.perf_counter()
+    mk, host_w = load_model(mkp, synth, cfg, shape, max_seq, tuning, args.seed, dev, keep_host)
+    print(f"[bench] {cfg.name}: weights generated and loaded in {time.perf_counter() - t:.1f}s", file=sys.stderr,
+          flush=True)
     torch.cuda.empty_cache()
     info = mk.info()
     kv = mkp.KVCache(shape, max_seq, dev)
@@ -188,7 +221,7 @@ def main():
     tokens = toks_out[warm:].cpu().numpy()
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if host_w is not None:
         cpu = cpu_baseline(cfg, host_w, shape, args.cpu_budget)
 
     out = {

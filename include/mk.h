@@ -48,7 +48,8 @@ typedef enum {
     MK_ERR_NOMEM = 5,   /* device allocation failed */
     MK_ERR_HIP = 6,     /* a HIP runtime call failed */
     MK_ERR_DEVICE = 7,  /* the device reported a failure (grid-wait timeout) */
-    MK_ERR_STATE = 8,   /* the handle was disabled by an earlier device failure */
+    MK_ERR_STATE = 8,   /* the handle was disabled by an earlier device failure, or its
+                           weights are not all loaded yet (mk_create_deferred) */
     MK_ERR_TUNING = 9   /* a tuning value is out of its documented range */
 } mk_status;
 
@@ -136,6 +137,29 @@ typedef struct {
    handle; on failure *out is set to NULL. */
 mk_status mk_create(const mk_model_desc *desc, const mk_weight_ptrs *weights, const mk_tuning *tuning,
                     mk_handle **out);
+
+/* Create a handle whose weights are supplied afterwards with
+   mk_load_weights, a part at a time.  For models whose caller-side weights
+   and the library's pre-laid-out copy do not both fit in device memory at
+   once (an 80-layer, hidden-8192 bf16 decoder holds about 139 GB of
+   weights; the device has 288 GB): the caller can upload, load and free one
+   layer at a time.  Validation, geometry and allocations are those of
+   mk_create.  Steps and prefill return MK_ERR_STATE until every layer and
+   the head weights (embedding, final norm, LM head) have been loaded.
+   Synchronous.  On failure *out is set to NULL. */
+mk_status mk_create_deferred(const mk_model_desc *desc, const mk_tuning *tuning, mk_handle **out);
+
+/* Pre-lay out part of a model's weights into h (the same re-layout mk_create
+   does, cloud.baidu.com/article/9434380 section 九): layers
+   [first_layer, first_layer + n_layers) are read from weights->layers[0 ..
+   n_layers) (a host array of device pointers; may be NULL when n_layers is
+   0), and, when weights->embed is not NULL, the embedding, final norm and
+   LM head (weights->lm_head, ignored when tied) are loaded too.  A part may
+   be loaded again; the last load wins.  Synchronous: the caller may free
+   the source tensors when it returns.  Errors: MK_ERR_NULL (h, weights, or a
+   pointer of a part being loaded is NULL), MK_ERR_RANGE (the layer range
+   is outside [0, n_layers)). */
+mk_status mk_load_weights(mk_handle *h, const mk_weight_ptrs *weights, int32_t first_layer, int32_t n_layers);
 
 /* One decode step for token_id at 0-based position pos: writes K/V of
    position pos into the cache, reads cache positions [0, pos] (never

@@ -153,3 +153,14 @@ def test_product_path_does_not_use_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(import|from)\s+oracle\b", text, flags=re.M), f
                 assert "or_decode_step" not in text and "liboracle" not in text, f
+
+
+def test_deferred_create_and_load_reject_bad_arguments(lib):
+    h = ctypes.c_void_p(0xDEAD)
+    assert lib.mk_create_deferred(None, None, ctypes.byref(h)) == mkb.MK_ERR_NULL and h.value is None
+    assert lib.mk_create_deferred(ctypes.byref(_desc()), None, None) == mkb.MK_ERR_NULL
+    assert lib.mk_create_deferred(ctypes.byref(_desc(head_dim=96)), None, ctypes.byref(h)) == mkb.MK_ERR_SHAPE
+    assert lib.mk_create_deferred(ctypes.byref(_desc()), ctypes.byref(mkb.Tuning(ring_slots=2)),
+                                  ctypes.byref(h)) == mkb.MK_ERR_TUNING
+    w, _keep = _weights(1)
+    assert lib.mk_load_weights(None, ctypes.byref(w), 0, 1) == mkb.MK_ERR_NULL

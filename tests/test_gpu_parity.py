@@ -53,8 +53,22 @@ def put_kv_prefix(cfg, seed, n_pos, ref, kv):
             dev[l, :, :n_pos, :] = t.to(dev.device)
 
 
+def create_deferred(mkp, shape, host, max_seq, tuning=None, order=None):
+    """A handle made by mk_create_deferred, its weights uploaded and loaded
+    one layer at a time (in `order`), the head weights last."""
+    mk = mkp.MegaKernel(shape, None, max_seq, tuning=tuning)
+    for l in (order if order is not None else range(shape["n_layers"])):
+        part = mkp.upload_weights({"layers": [host["layers"][l]]})
+        mk.load_weights(part, first_layer=l)
+        del part
+    head = mkp.upload_weights({k: v for k, v in host.items() if k != "layers"})
+    mk.load_weights(head)
+    del head
+    return mk
+
+
 def run_pair(env, cfg, seed, n_prompt, n_steps, gains="random", tuning=None, use_prefill=True, poison=True,
-             check_kv=True):
+             check_kv=True, deferred=False):
     """Prefill (or synthetic cache) then teacher-forced greedy steps on both
     sides; returns per-step max|dlogit| and the argmax agreement count."""
     torch, oracle, mkp = env
@@ -64,9 +78,12 @@ def run_pair(env, cfg, seed, n_prompt, n_steps, gains="random", tuning=None, use
     max_seq = n_prompt + n_steps
     host = synth.gen_weights(cfg, seed=seed, gains=gains)
     ref = oracle.Model(shape, host, max_seq)
-    dev_w = mkp.upload_weights(host)
-    mk = mkp.MegaKernel(shape, dev_w, max_seq, tuning=tuning)
-    del dev_w
+    if deferred:
+        mk = create_deferred(mkp, shape, host, max_seq, tuning)
+    else:
+        dev_w = mkp.upload_weights(host)
+        mk = mkp.MegaKernel(shape, dev_w, max_seq, tuning=tuning)
+        del dev_w
     kv = mkp.KVCache(shape, max_seq, fill=float("nan") if poison else 0.0)
     toks = synth.gen_tokens(seed, n_prompt + 1, cfg.vocab)
     if use_prefill:
@@ -274,3 +291,28 @@ def test_device_token_out_of_range_sets_device_error(env):
     with pytest.raises(mkp.MkError):
         mk.decode_step_device_token(tin, 1, kv, None, tout)
     mk.close()
+
+
+def test_deferred_weight_loading(env):
+    """mk_create_deferred + mk_load_weights, layers loaded in reverse order:
+    steps are refused until every part is loaded, then match the oracle like
+    a handle made by mk_create."""
+    torch, oracle, mkp = env
+    cfg = synth.CONFIGS["tiny"].with_(n_layers=3)
+    shape = shape_of(cfg)
+    host = synth.gen_weights(cfg, seed=31, gains="random")
+    mk = mkp.MegaKernel(shape, None, 40)
+    kv = mkp.KVCache(shape, 40)
+    logits = torch.empty(cfg.vocab, device="cuda")
+    for l in (2, 0):
+        mk.load_weights(mkp.upload_weights({"layers": [host["layers"][l]]}), first_layer=l)
+    mk.load_weights(mkp.upload_weights({k: v for k, v in host.items() if k != "layers"}))
+    with pytest.raises(mkp.MkError) as ei:  # layer 1 still missing
+        mk.decode_step(1, 0, kv, logits)
+    assert ei.value.status == mkp.mk.MK_ERR_STATE
+    with pytest.raises(mkp.MkError) as ei:
+        mk.load_weights(mkp.upload_weights({"layers": [host["layers"][1]]}), first_layer=3)
+    assert ei.value.status == mkp.mk.MK_ERR_RANGE
+    mk.close()
+    errs, agree = run_pair(env, cfg, seed=31, n_prompt=20, n_steps=6, deferred=True)
+    assert max(errs) <= 1e-4 and agree == 6

@@ -37,6 +37,9 @@ struct mk_handle {
     bool disabled = false;
     hipStream_t last_stream = nullptr;
     int lds_bytes = 0;
+    std::vector<char> layer_loaded;  // [n_layers]: weights of the layer pre-laid out
+    int layers_loaded = 0;
+    bool head_loaded = false;        // embedding, final norm and LM head in place
 };
 
 namespace {
@@ -94,7 +97,7 @@ extern "C" const char *mk_status_str(mk_status s) {
     case MK_ERR_NOMEM: return "device allocation failed";
     case MK_ERR_HIP: return "HIP runtime error";
     case MK_ERR_DEVICE: return "device reported a failure";
-    case MK_ERR_STATE: return "handle disabled by an earlier device failure";
+    case MK_ERR_STATE: return "handle not ready: disabled by a device failure, or weights not all loaded";
     case MK_ERR_TUNING: return "tuning value out of range";
     }
     return "unknown status";
@@ -113,7 +116,9 @@ extern "C" void mk_destroy(mk_handle *h) {
     delete h;
 }
 
-static mk_status create_impl(const mk_model_desc *desc, const mk_weight_ptrs *wp, const mk_tuning *tun, mk_handle *h) {
+// Geometry, allocations, RoPE table and launch-invariant arguments; the
+// weights are pre-laid out afterwards by load_impl.
+static mk_status create_impl(const mk_model_desc *desc, const mk_tuning *tun, mk_handle *h) {
     const mk_model_desc &D = *desc;
     const int L = D.n_layers, H = D.hidden, nh = D.n_heads, nkv = D.n_kv_heads, d = D.head_dim, F = D.ffn,
               V = D.vocab;
@@ -191,6 +196,8 @@ static mk_status create_impl(const mk_model_desc *desc, const mk_weight_ptrs *wp
         if (dg.kp * (16 / eb) > vec_floats) vec_floats = dg.kp * (16 / eb);
     }
     if ((int64_t)grid * max_rows_o > vec_floats) vec_floats = grid * max_rows_o;
+    // the down partials of one layer are addressed with a 32-bit buffer resource
+    if ((int64_t)grid * H * 8 >= (1LL << 32)) return MK_ERR_SHAPE;
     // the attention stage gathers its group's queries and the new K/V row into vec
     if (vec_floats < (gq + 2) * d) vec_floats = (gq + 2) * d;
     const int fixed = mk_kernel_lds_bytes(0, vec_floats, out_rows, dtype, d, gq);
@@ -229,32 +236,8 @@ static mk_status create_impl(const mk_model_desc *desc, const mk_weight_ptrs *wp
         HIP_TRY(hipMemset(h->trace, 0, h->trace_len * sizeof(uint64_t)));
     }
 
-    // pre-layout, gains, embedding copy
     for (int k = 0; k < ST_NUM; ++k) P.st[k].wg_off = h->wg_off + (size_t)k * grid;
-    for (int k = 0; k < ST_NUM; ++k) {
-        const int layers = k == ST_LM ? 1 : L;
-        for (int l = 0; l < layers; ++l) {
-            const mk_layer_ptrs &lw = wp->layers[k == ST_LM ? 0 : l];
-            const void *s0 = nullptr, *s1 = nullptr, *s2 = nullptr;
-            switch (k) {
-            case ST_QKV: s0 = lw.wq; s1 = lw.wk; s2 = lw.wv; break;
-            case ST_O: s0 = lw.wo; break;
-            case ST_GU: s0 = lw.w_gate; s1 = lw.w_up; break;
-            case ST_DOWN: s0 = lw.w_down; break;
-            default: s0 = D.tied_embeddings ? wp->embed : wp->lm_head; break;
-            }
-            int rc = mk_launch_prelayout_stage(h->packed + P.st[k].base + (int64_t)l * P.st[k].layer_stride, &P.st[k],
-                                               grid, k, dtype, s0, s1, s2, nh, nkv, d, nullptr);
-            if (rc) return MK_ERR_HIP;
-        }
-    }
-    for (int l = 0; l < L; ++l) {
-        if (mk_launch_to_f32(h->gains + (size_t)l * H, wp->layers[l].attn_norm, H, dtype, nullptr)) return MK_ERR_HIP;
-        if (mk_launch_to_f32(h->gains + (size_t)(L + l) * H, wp->layers[l].ffn_norm, H, dtype, nullptr))
-            return MK_ERR_HIP;
-    }
-    if (mk_launch_to_f32(h->gains + (size_t)2 * L * H, wp->final_norm, H, dtype, nullptr)) return MK_ERR_HIP;
-    HIP_TRY(hipMemcpy(h->embed, wp->embed, (size_t)V * H * eb, hipMemcpyDeviceToDevice));
+    h->layer_loaded.assign((size_t)L, 0);
 
     // rotary table: angle pos * theta^(-2i/d), evaluated in double
     {
@@ -296,6 +279,65 @@ static mk_status create_impl(const mk_model_desc *desc, const mk_weight_ptrs *wp
     return MK_OK;
 }
 
+
+// Pre-layout of layers [first, first + n) from wp->layers[0 .. n) and, when
+// wp->embed is set, of the embedding, final norm and LM head.  Synchronous.
+static mk_status load_impl(mk_handle *h, const mk_weight_ptrs *wp, int first, int n) {
+    const mk_model_desc &D = h->desc;
+    const MkParams &P = h->base;
+    const int L = D.n_layers, H = D.hidden, V = D.vocab, grid = P.grid;
+    const int dtype = D.dtype == MK_BF16 ? 1 : 0;
+    for (int i = 0; i < n; ++i) {
+        const int l = first + i;
+        const mk_layer_ptrs &lw = wp->layers[i];
+        for (int k = 0; k < ST_LM; ++k) {
+            const void *s0 = nullptr, *s1 = nullptr, *s2 = nullptr;
+            switch (k) {
+            case ST_QKV: s0 = lw.wq; s1 = lw.wk; s2 = lw.wv; break;
+            case ST_O: s0 = lw.wo; break;
+            case ST_GU: s0 = lw.w_gate; s1 = lw.w_up; break;
+            default: s0 = lw.w_down; break;
+            }
+            if (mk_launch_prelayout_stage(h->packed + P.st[k].base + (int64_t)l * P.st[k].layer_stride, &P.st[k], grid,
+                                          k, dtype, s0, s1, s2, D.n_heads, D.n_kv_heads, D.head_dim, nullptr))
+                return MK_ERR_HIP;
+        }
+        if (mk_launch_to_f32(h->gains + (size_t)l * H, lw.attn_norm, H, dtype, nullptr)) return MK_ERR_HIP;
+        if (mk_launch_to_f32(h->gains + (size_t)(L + l) * H, lw.ffn_norm, H, dtype, nullptr)) return MK_ERR_HIP;
+    }
+    if (wp->embed) {
+        const void *lm = D.tied_embeddings ? wp->embed : wp->lm_head;
+        if (mk_launch_prelayout_stage(h->packed + P.st[ST_LM].base, &P.st[ST_LM], grid, ST_LM, dtype, lm, nullptr,
+                                      nullptr, D.n_heads, D.n_kv_heads, D.head_dim, nullptr))
+            return MK_ERR_HIP;
+        if (mk_launch_to_f32(h->gains + (size_t)2 * L * H, wp->final_norm, H, dtype, nullptr)) return MK_ERR_HIP;
+        HIP_TRY(hipMemcpy(h->embed, wp->embed, (size_t)V * H * h->eb, hipMemcpyDeviceToDevice));
+    }
+    // the sources may be freed when this returns
+    HIP_TRY(hipDeviceSynchronize());
+    for (int i = 0; i < n; ++i) {
+        char &done = h->layer_loaded[(size_t)(first + i)];
+        if (!done) ++h->layers_loaded;
+        done = 1;
+    }
+    if (wp->embed) h->head_loaded = true;
+    return MK_OK;
+}
+
+// Null checks of the weight pointers a load will read: layers[0 .. n) and,
+// when embed is set, the head tensors.
+static mk_status check_weight_ptrs(const mk_model_desc *desc, const mk_weight_ptrs *w, int n) {
+    if (w->embed && (!w->final_norm || (!desc->tied_embeddings && !w->lm_head))) return MK_ERR_NULL;
+    if (n > 0 && !w->layers) return MK_ERR_NULL;
+    for (int l = 0; l < n; ++l) {
+        const mk_layer_ptrs &lw = w->layers[l];
+        if (!lw.attn_norm || !lw.wq || !lw.wk || !lw.wv || !lw.wo || !lw.ffn_norm || !lw.w_gate || !lw.w_up ||
+            !lw.w_down)
+            return MK_ERR_NULL;
+    }
+    return MK_OK;
+}
+
 extern "C" mk_status mk_create(const mk_model_desc *desc, const mk_weight_ptrs *weights, const mk_tuning *tuning,
                                mk_handle **out) {
     if (!out) return MK_ERR_NULL;
@@ -305,22 +347,45 @@ extern "C" mk_status mk_create(const mk_model_desc *desc, const mk_weight_ptrs *
     if (s != MK_OK) return s;
     s = validate_tuning(tuning);
     if (s != MK_OK) return s;
-    if (!weights->embed || !weights->final_norm || !weights->layers || (!desc->tied_embeddings && !weights->lm_head))
-        return MK_ERR_NULL;
-    for (int l = 0; l < desc->n_layers; ++l) {
-        const mk_layer_ptrs &lw = weights->layers[l];
-        if (!lw.attn_norm || !lw.wq || !lw.wk || !lw.wv || !lw.wo || !lw.ffn_norm || !lw.w_gate || !lw.w_up ||
-            !lw.w_down)
-            return MK_ERR_NULL;
-    }
+    if (!weights->embed) return MK_ERR_NULL;
+    s = check_weight_ptrs(desc, weights, desc->n_layers);
+    if (s != MK_OK) return s;
     mk_handle *h = new mk_handle();
-    s = create_impl(desc, weights, tuning, h);
+    s = create_impl(desc, tuning, h);
+    if (s == MK_OK) s = load_impl(h, weights, 0, desc->n_layers);
     if (s != MK_OK) {
         mk_destroy(h);
         return s;
     }
     *out = h;
     return MK_OK;
+}
+
+extern "C" mk_status mk_create_deferred(const mk_model_desc *desc, const mk_tuning *tuning, mk_handle **out) {
+    if (!out) return MK_ERR_NULL;
+    *out = nullptr;
+    if (!desc) return MK_ERR_NULL;
+    mk_status s = validate_desc(desc);
+    if (s != MK_OK) return s;
+    s = validate_tuning(tuning);
+    if (s != MK_OK) return s;
+    mk_handle *h = new mk_handle();
+    s = create_impl(desc, tuning, h);
+    if (s != MK_OK) {
+        mk_destroy(h);
+        return s;
+    }
+    *out = h;
+    return MK_OK;
+}
+
+extern "C" mk_status mk_load_weights(mk_handle *h, const mk_weight_ptrs *weights, int32_t first_layer,
+                                     int32_t n_layers) {
+    if (!h || !weights) return MK_ERR_NULL;
+    if (first_layer < 0 || n_layers < 0 || (int64_t)first_layer + n_layers > h->desc.n_layers) return MK_ERR_RANGE;
+    mk_status s = check_weight_ptrs(&h->desc, weights, n_layers);
+    if (s != MK_OK) return s;
+    return load_impl(h, weights, first_layer, n_layers);
 }
 
 static mk_status check_kv(const mk_handle *h, const mk_kv_cache *kv) {
@@ -331,6 +396,7 @@ static mk_status check_kv(const mk_handle *h, const mk_kv_cache *kv) {
 
 static mk_status launch(mk_handle *h, const mk_kv_cache *kv, int32_t token, const int32_t *token_dev, int32_t pos,
                         int want_logits, float *logits, int32_t *token_out, void *stream) {
+    if (h->layers_loaded < h->desc.n_layers || !h->head_loaded) return MK_ERR_STATE;  // weights still missing
     MkParams p = h->base;
     p.kc = kv->k;
     p.vc = kv->v;

@@ -1012,7 +1012,9 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
     // Fold NQ chunks of positions (each lane holds one position of each
     // chunk, PPC positions per chunk) into the running state: all scores
     // first, then one running-max update, rescale and V accumulation per
-    // head.  Invalid positions get probability 0; their V values are not used.
+    // head.  Invalid positions get probability 0.  Their V values are finite
+    // (the loaders read weights, not the cache, past a split's positions, and
+    // the register tail reads a valid row), so 0 * v adds nothing.
     auto attn_fold = [&](AttnState &A, auto nq_tag, const float (*kv)[EPL], const float (*vv)[EPL],
                          const bool *valid) {
         constexpr int NQ = decltype(nq_tag)::value;
@@ -1053,7 +1055,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
             for (int e = 0; e < EPL; ++e) {
                 float o = A.ao[h][e] * alpha;
 #pragma unroll
-                for (int q = 0; q < NQ; ++q) o = fmaf(pe[q], valid[q] ? vv[q][e] : 0.f, o);
+                for (int q = 0; q < NQ; ++q) o = fmaf(pe[q], vv[q][e], o);
                 A.ao[h][e] = o;
             }
             A.am[h] = any ? mn : A.am[h];

@@ -19,7 +19,7 @@ MK_OK, MK_ERR_NULL, MK_ERR_SHAPE, MK_ERR_DTYPE, MK_ERR_RANGE = 0, 1, 2, 3, 4
 MK_ERR_NOMEM, MK_ERR_HIP, MK_ERR_DEVICE, MK_ERR_STATE, MK_ERR_TUNING = 5, 6, 7, 8, 9
 MK_F32, MK_BF16 = 0, 1
 
-EXPORTED = ("mk_create", "mk_decode_step", "mk_decode_step_device_token", "mk_prefill_kv", "mk_get_device_error",
+EXPORTED = ("mk_create", "mk_create_deferred", "mk_load_weights", "mk_decode_step", "mk_decode_step_device_token", "mk_prefill_kv", "mk_get_device_error",
             "mk_get_info", "mk_read_trace", "mk_status_str", "mk_destroy")
 
 
@@ -70,6 +70,8 @@ def load_library(path: str = LIB_PATH):
     vp, i32, p = ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER
     sig = {
         "mk_create": ([p(ModelDesc), p(WeightPtrs), p(Tuning), p(vp)], ctypes.c_int),
+        "mk_create_deferred": ([p(ModelDesc), p(Tuning), p(vp)], ctypes.c_int),
+        "mk_load_weights": ([vp, p(WeightPtrs), i32, i32], ctypes.c_int),
         "mk_decode_step": ([vp, i32, i32, p(KVDesc), vp, vp], ctypes.c_int),
         "mk_decode_step_device_token": ([vp, vp, i32, p(KVDesc), vp, vp, vp], ctypes.c_int),
         "mk_prefill_kv": ([vp, vp, i32, i32, p(KVDesc), vp], ctypes.c_int),
@@ -138,20 +140,30 @@ class MegaKernel:
     in the model dtype: 'embed', 'final_norm', optional 'lm_head' and
     'layers' (a list of dicts keyed by LAYER_KINDS)."""
 
-    def __init__(self, shape: dict, weights: dict, max_seq: int, tuning: dict | None = None):
+    def __init__(self, shape: dict, weights: dict | None, max_seq: int, tuning: dict | None = None):
+        """weights=None creates the handle with mk_create_deferred; the
+        weights then come through load_weights."""
         lib = load_library()
         self.shape = dict(shape)
         self.max_seq = int(max_seq)
         self._desc = model_desc(shape, max_seq)
-        layers = (LayerPtrs * shape["n_layers"])()
-        for l, lw in enumerate(weights["layers"]):
-            layers[l] = LayerPtrs(*[_ptr(lw[k]) for k in LAYER_KINDS])
-        wp = WeightPtrs(_ptr(weights["embed"]), _ptr(weights["final_norm"]), _ptr(weights.get("lm_head")), layers)
         tun = Tuning(**(tuning or {}))
         h = ctypes.c_void_p()
-        _check(lib.mk_create(ctypes.byref(self._desc), ctypes.byref(wp), ctypes.byref(tun), ctypes.byref(h)),
-               "mk_create")
+        if weights is None:
+            _check(lib.mk_create_deferred(ctypes.byref(self._desc), ctypes.byref(tun), ctypes.byref(h)),
+                   "mk_create_deferred")
+        else:
+            wp, _layers = _weight_ptrs(weights)
+            _check(lib.mk_create(ctypes.byref(self._desc), ctypes.byref(wp), ctypes.byref(tun), ctypes.byref(h)),
+                   "mk_create")
         self._h = h
+
+    def load_weights(self, weights: dict, first_layer: int = 0):
+        """Pre-lay out weights['layers'] as layers first_layer.. and, if
+        weights has 'embed', the head tensors (mk_load_weights)."""
+        wp, _layers = _weight_ptrs(weights)
+        n = len(weights.get("layers", []))
+        _check(load_library().mk_load_weights(self._h, ctypes.byref(wp), int(first_layer), n), "mk_load_weights")
 
     # -- the four calls of the boundary --
     def decode_step(self, token: int, pos: int, kv: KVCache, logits: torch.Tensor, stream=None):
@@ -206,6 +218,16 @@ class MegaKernel:
             pass
 
 
+def _weight_ptrs(weights: dict):
+    layers_in = weights.get("layers", [])
+    layers = (LayerPtrs * max(len(layers_in), 1))()
+    for l, lw in enumerate(layers_in):
+        layers[l] = LayerPtrs(*[_ptr(lw[k]) for k in LAYER_KINDS])
+    wp = WeightPtrs(_ptr(weights.get("embed")), _ptr(weights.get("final_norm")), _ptr(weights.get("lm_head")),
+                    layers if layers_in else None)
+    return wp, layers
+
+
 def upload_weights(host: dict, device="cuda") -> dict:
     """Host numpy weights (float32, or uint16 bfloat16 bits) -> device tensors."""
     import numpy as np
@@ -218,5 +240,5 @@ def upload_weights(host: dict, device="cuda") -> dict:
         return t.to(device)
 
     out = {k: up(v) for k, v in host.items() if k != "layers"}
-    out["layers"] = [{k: up(v) for k, v in lw.items()} for lw in host["layers"]]
+    out["layers"] = [{k: up(v) for k, v in lw.items()} for lw in host.get("layers", [])]
     return out
