@@ -316,3 +316,14 @@ def test_deferred_weight_loading(env):
     mk.close()
     errs, agree = run_pair(env, cfg, seed=31, n_prompt=20, n_steps=6, deferred=True)
     assert max(errs) <= 1e-4 and agree == 6
+
+
+def test_row_groups_hidden4096(env):
+    """Rows of 8 KiB (hidden 4096 bf16): the pre-layout interleaves whole
+    groups of four rows chunk by chunk.  QKV has 6 units per workgroup (one
+    group and two rows after it), O exactly one group, gate/up two rows (no
+    group), the LM head 0 or 1 row per workgroup."""
+    cfg = synth.CONFIGS["tiny"].with_(dtype="bf16", hidden=4096, n_heads=32, n_kv_heads=8, head_dim=128, ffn=1024,
+                                      vocab=1000, tied=True, rope_theta=500000.0)
+    errs, agree = run_pair(env, cfg, seed=41, n_prompt=30, n_steps=4)
+    assert max(errs) <= 2e-2 and agree == 4

@@ -52,6 +52,29 @@ static inline __host__ __device__ MkDownGeo mk_down_geo(int w, int G, int units_
     return g;
 }
 
+// Order of a consumer's chunk stream for the matrix-vector stages.  Rows of
+// exactly 4 chunks are stored row after row (one row per slot).  Longer rows
+// of a multiple of 4 chunks are interleaved in groups of four rows: the
+// stream holds chunk 0 of rows 4g..4g+3, then chunk 1 of the same rows, and
+// so on, so the four pieces a consumer takes from one slot multiply the same
+// input elements (read once from LDS instead of once per piece).  Rows past
+// the last whole group, and rows of other lengths, follow row after row.
+static inline __host__ __device__ bool mk_row_groups(int rbp) { return rbp >= 8 && (rbp & 3) == 0; }
+// Stream position qq (in chunks) of a consumer holding `rows` rows of rbp
+// chunks -> its local row and the chunk within that row.
+static inline __host__ __device__ void mk_stream_pos(int qq, int rows, int rbp, int &row, int &kc) {
+    const int full = mk_row_groups(rbp) ? rows / 4 : 0;
+    const int span = 4 * rbp;  // chunks of one group of four rows
+    if (qq < full * span) {
+        row = (qq / span) * 4 + (qq % 4);
+        kc = (qq % span) / 4;
+    } else {
+        const int r = qq - full * span;
+        row = full * 4 + r / rbp;
+        kc = r % rbp;
+    }
+}
+
 // Stage kinds with weights; the attention stage streams the KV cache.
 enum { ST_QKV = 0, ST_O = 1, ST_GU = 2, ST_DOWN = 3, ST_LM = 4, ST_NUM = 5 };
 

@@ -244,6 +244,17 @@ __device__ __forceinline__ void piece_load(const LDS unsigned char *p, float (&v
     }
 }
 
+// The input elements matching a 16-byte weight piece, from LDS.
+template <int DT>
+__device__ __forceinline__ void piece_in(const LDS float *hp, float (&h)[16 / (DT ? 2 : 4)]) {
+    const f4v h0 = *(const LDS f4v *)hp;
+    h[0] = h0.x; h[1] = h0.y; h[2] = h0.z; h[3] = h0.w;
+    if constexpr (DT == 1) {
+        const f4v h1 = *(const LDS f4v *)(hp + 4);
+        h[4] = h1.x; h[5] = h1.y; h[6] = h1.z; h[7] = h1.w;
+    }
+}
+
 // Poll N 16-byte pieces (two tagged records each) at byte offsets off(u)
 // of rs, for the lanes' bits set in mask, until both tags of every piece
 // equal tag; pieces already valid are not read again.  on_fail() is called
@@ -836,12 +847,40 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
             stamp_step(l, 1);
         }
     };
-    // LDS path: any row length; the input vector is in vec.
+    // LDS path: any row length; the input vector is in vec.  Whole groups of
+    // four rows come first (mk_stream_pos): slot s of a group carries chunk s
+    // of four rows, so the lane's eight input elements are read from LDS once
+    // and multiply four weight pieces, with one accumulator per row.  The
+    // remaining rows follow row after row.
     auto gemv_lds_steps = [&](int st, int l) {
         const int units = g.units[st], rbp = p.st[st].rbp;
-        int row_c = 0, kc = 0;
+        const int full = mk_row_groups(rbp) ? units / 4 : 0;
+        int n = 0;
+        for (int grp = 0; grp < full; ++grp) {
+            float acc[4] = {0.f, 0.f, 0.f, 0.f};
+            for (int s = 0; s < rbp; ++s, ++n) {
+                barrier();
+                stamp_step(l, 0);
+                const LDS unsigned char *bp = ring + js * MK_SLOT_BYTES + c * 4 * MK_CHUNK_BYTES + lane * 16;
+                float hv[EPL];
+                piece_in<DT>(vec + s * EPC + lane * EPL, hv);
+                float d[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) d[j] = piece_dot_reg<DT>(bp + j * MK_CHUNK_BYTES, hv);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[j] += d[j];
+                js = js + 1 == NS ? 0 : js + 1;
+                stamp_step(l, 1);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float t = wave_sum(acc[j]);
+                if (lane == 0) outv[(grp * 4 + j) * 4 + c] = t;
+            }
+        }
+        int row_c = full * 4, kc = 0;
         float acc = 0.f;
-        for (int n = 0; n < g.nsl[st]; ++n) {
+        for (; n < g.nsl[st]; ++n) {
             barrier();
             stamp_step(l, 0);
             const LDS unsigned char *bp = ring + js * MK_SLOT_BYTES + c * 4 * MK_CHUNK_BYTES + lane * 16;

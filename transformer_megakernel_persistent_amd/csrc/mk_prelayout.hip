@@ -14,7 +14,9 @@
 //         workgroup owns both halves of every SwiGLU product it emits.
 //   O, LM: natural row order.
 // Within a workgroup's block, slot n holds for consumer c the 4 KiB of its row
-// stream at [4n, 4n+4) chunks; consumer c's rows are local rows c, c+4, ...
+// stream at [4n, 4n+4) chunks; consumer c's rows are local rows c, c+4, ...,
+// and rows of 8, 12, ... chunks are interleaved in groups of four (see
+// mk_stream_pos) so that one slot carries the same chunk of four rows.
 //   DOWN: split along the input instead (see mk_down_geo): workgroup w's block
 //         holds the Wd columns of its SwiGLU outputs as piece columns, lane i
 //         of a piece column carrying 16 bytes of one output row.
@@ -59,7 +61,8 @@ __global__ __launch_bounds__(256) void prelayout_kernel(unsigned char *dst_block
     }
     const int nsl = (units * st.rbp + 3) / 4;
     if (chunk >= nsl * MK_CHUNKS_PER_SLOT) return;
-    const int row_c = qq / st.rbp, kc = qq % st.rbp;
+    int row_c, kc;
+    mk_stream_pos(qq, units, st.rbp, row_c, kc);
     if (row_c < units) {
         const int gr = (unit0 + row_c) * 4 + c;  // packed row
         if (gr < st.rows) {
