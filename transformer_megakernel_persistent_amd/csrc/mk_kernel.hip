@@ -244,6 +244,17 @@ __device__ __forceinline__ void piece_load(const LDS unsigned char *p, float (&v
     }
 }
 
+// Element e of a 16-byte piece held as raw words (bf16 pairs or floats).
+template <int DT>
+__device__ __forceinline__ float piece_elem(const u4v &w, int e) {
+    if constexpr (DT == 1) {
+        const uint32_t x = e < 2 ? w.x : e < 4 ? w.y : e < 6 ? w.z : w.w;
+        return (e & 1) ? bf_hi(x) : bf_lo(x);
+    } else {
+        return __uint_as_float(e == 0 ? w.x : e == 1 ? w.y : e == 2 ? w.z : w.w);
+    }
+}
+
 // The input elements matching a 16-byte weight piece, from LDS.
 template <int DT>
 __device__ __forceinline__ void piece_in(const LDS float *hp, float (&h)[16 / (DT ? 2 : 4)]) {
@@ -1039,7 +1050,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
     constexpr int HPC = GQ / HG;                // heads per consumer
     constexpr int CPH = MK_NUM_CONSUMERS / HG;  // consumers per head
     constexpr int CPS = 8 / CPH;                // K (and V) chunks per slot per consumer
-    constexpr int NQB = CPS < 4 ? CPS : 4;      // chunks folded together
+    constexpr int NQB = (HPC == 1 && CPS >= 8) ? 8 : (CPS < 4 ? CPS : 4);  // chunks folded together
     const int hc = c % HG, cs = c / HG;
     const float scale = 1.0f / sqrtf((float)d);
     const int e0 = (lane % LPP) * EPL;
@@ -1054,8 +1065,8 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
     // head.  Invalid positions get probability 0.  Their V values are finite
     // (the loaders read weights, not the cache, past a split's positions, and
     // the register tail reads a valid row), so 0 * v adds nothing.
-    auto attn_fold = [&](AttnState &A, auto nq_tag, const float (*kv)[EPL], const float (*vv)[EPL],
-                         const bool *valid) {
+    // kget(q, e) / vget(q, e): element e of the lane's K / V piece of chunk q.
+    auto attn_fold = [&](AttnState &A, auto nq_tag, auto &&kget, auto &&vget, const bool *valid) {
         constexpr int NQ = decltype(nq_tag)::value;
         float sc[NQ][HPC];
 #pragma unroll
@@ -1064,7 +1075,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
             for (int h = 0; h < HPC; ++h) {
                 float t = 0.f;
 #pragma unroll
-                for (int e = 0; e < EPL; ++e) t = fmaf(A.qr[h][e], kv[q][e], t);
+                for (int e = 0; e < EPL; ++e) t = fmaf(A.qr[h][e], kget(q, e), t);
                 sc[q][h] = t;
             }
 #pragma unroll
@@ -1094,7 +1105,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
             for (int e = 0; e < EPL; ++e) {
                 float o = A.ao[h][e] * alpha;
 #pragma unroll
-                for (int q = 0; q < NQ; ++q) o = fmaf(pe[q], vv[q][e], o);
+                for (int q = 0; q < NQ; ++q) o = fmaf(pe[q], vget(q, e), o);
                 A.ao[h][e] = o;
             }
             A.am[h] = any ? mn : A.am[h];
@@ -1445,7 +1456,8 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
                 auto finish = [&]() {
                     if (fold_extra && ntail > 0) {
                         const bool v1[1] = {tvalid};
-                        attn_fold(A, std::integral_constant<int, 1>{}, &kt, &vt, v1);
+                        attn_fold(A, std::integral_constant<int, 1>{}, [&](int, int e) { return kt[e]; },
+                                  [&](int, int e) { return vt[e]; }, v1);
                     }
                     if (fold_extra && is_last) {
                         float kp[EPL], vp[EPL];
@@ -1455,7 +1467,8 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
                             vp[e] = vec[GQ * d + d + e0 + e];
                         }
                         const bool v1[1] = {lane < LPP};
-                        attn_fold(A, std::integral_constant<int, 1>{}, &kp, &vp, v1);
+                        attn_fold(A, std::integral_constant<int, 1>{}, [&](int, int e) { return kp[e]; },
+                                  [&](int, int e) { return vp[e]; }, v1);
                     }
                     attn_finish(A, l);
                 };
@@ -1468,16 +1481,18 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
                     const LDS unsigned char *vb = kb + 8 * MK_CHUNK_BYTES;
 #pragma unroll
                     for (int b = 0; b < CPS; b += NQB) {
-                        float kv[NQB][EPL], vv[NQB][EPL];
+                        // raw 16-byte pieces; each element is widened where it is used
+                        u4v kr[NQB], vr[NQB];
                         bool valid[NQB];
 #pragma unroll
                         for (int q = 0; q < NQB; ++q) {
                             const int chunk = cs * CPS + b + q;
                             valid[q] = t0 + n * BP + chunk * PPC + lane / LPP < t1;
-                            piece_load<DT>(kb + chunk * MK_CHUNK_BYTES + lane * 16, kv[q]);
-                            piece_load<DT>(vb + chunk * MK_CHUNK_BYTES + lane * 16, vv[q]);
+                            kr[q] = *(const LDS u4v *)(kb + chunk * MK_CHUNK_BYTES + lane * 16);
+                            vr[q] = *(const LDS u4v *)(vb + chunk * MK_CHUNK_BYTES + lane * 16);
                         }
-                        attn_fold(A, std::integral_constant<int, NQB>{}, kv, vv, valid);
+                        attn_fold(A, std::integral_constant<int, NQB>{}, [&](int q, int e) { return piece_elem<DT>(kr[q], e); },
+                                  [&](int q, int e) { return piece_elem<DT>(vr[q], e); }, valid);
                     }
                     if (n == nsl_kv - 1) finish();
                     js = js + 1 == NS ? 0 : js + 1;
