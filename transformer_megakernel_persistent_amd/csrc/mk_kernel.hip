@@ -1233,7 +1233,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
             vec[m] = av;
         }
     };
-    // Log-sum-exp merge of the splits (consumer 0): workgroup w produces
+    // Log-sum-exp merge of the splits (blocks of 8 elements per consumer): workgroup w produces
     // attention-output elements [w*N/G, (w+1)*N/G) of N = n_heads*d.  Lane s
     // reads effective split s's (m, l) and the element's o value; the
     // weights are exp(m_s - max m) and the result sum(w_s o_s) / sum(w_s l_s).
@@ -1246,7 +1246,9 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
         poll_start = wall_clock64();
         int cur_h = -1;
         float M = 0.f, Ls = 1.f;
-        for (int eb = e_0; eb < e_1; eb += 8) {
+        // blocks of 8 elements dealt to the four consumers, so that the
+        // blocks' waits run side by side
+        for (int eb = e_0 + 8 * c; eb < e_1; eb += 8 * MK_NUM_CONSUMERS) {
             uint32_t mask = 0;
 #pragma unroll
             for (int u = 0; u < 8; ++u)
@@ -1507,8 +1509,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
         {
             barrier();
             stamp(5 * l + 2, 0);
-            bool mine = true;
-            if (c == 0) mine = combine_slice(l);
+            const bool mine = combine_slice(l);
             stamp(5 * l + 2, 1);
             ok = mine && gather(p.ll_o + (size_t)l * nq, nq, nullptr, p.st[ST_O].rbp * EPC);
             stamp(5 * l + 2, 2);
