@@ -33,3 +33,34 @@ def test_llama70b_widths_two_layers(env):
     errs, agree = run_pair(env, cfg, seed=23, n_prompt=cfg.context, n_steps=2, gains="ones", use_prefill=False,
                            deferred=True)
     assert max(errs) <= 2e-2 and agree == 2
+
+
+def test_llama1b_bit_identical_over_100_launches(env):
+    """The same decode step launched 100 times at full size (256 workgroups,
+    every cross-workgroup dependency point): the logits and the greedy token
+    are identical bit for bit every time.  A missing wait or a record read
+    before it is valid shows up here as run-to-run differences."""
+    torch, _, mkp = env
+    cfg = synth.CONFIGS["llama1b"]
+    shape = {k: getattr(cfg, k) for k in ("n_layers", "hidden", "n_heads", "n_kv_heads", "head_dim", "ffn", "vocab",
+                                          "rms_eps", "rope_theta", "dtype", "tied")}
+    ctx = cfg.context
+    dev_w = mkp.upload_weights(synth.gen_weights(cfg, seed=24))
+    mk = mkp.MegaKernel(shape, dev_w, ctx + 1)
+    del dev_w
+    kv = mkp.KVCache(shape, ctx + 1, fill=None)
+    gen = torch.Generator(device="cuda").manual_seed(24)
+    kv.k.normal_(0.0, synth.kv_std(cfg), generator=gen)
+    kv.v.normal_(0.0, synth.kv_std(cfg), generator=gen)
+    tin = torch.tensor([12345], dtype=torch.int32, device="cuda")
+    outs = torch.empty((100, cfg.vocab), device="cuda")
+    toks = torch.full((100,), -1, dtype=torch.int32, device="cuda")
+    for i in range(100):
+        mk.decode_step_device_token(tin, ctx, kv, outs[i], toks[i:i + 1])
+    torch.cuda.synchronize()
+    assert mk.device_error() == 0
+    assert torch.isfinite(outs[0]).all()
+    same = (outs == outs[0]).all(dim=1)
+    assert bool(same.all()), f"{int((~same).sum())} of 100 launches differ from the first"
+    assert bool((toks == toks[0]).all())
+    mk.close()
