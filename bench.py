@@ -108,7 +108,7 @@ def cpu_baseline(cfg, host_w, shape, budget_s: float):
     import oracle
     import synth
     ctx = cfg.context
-    ref = oracle.Model(shape, host_w, ctx + 64)
+    ref = oracle.Model(shape, host_w, ctx + 65)
     for l in range(cfg.n_layers):
         ref.k[l, :, :ctx] = synth.gen_kv_prefix(cfg, 7, ctx, "k", l)
         ref.v[l, :, :ctx] = synth.gen_kv_prefix(cfg, 7, ctx, "v", l)
@@ -120,9 +120,18 @@ def cpu_baseline(cfg, host_w, shape, budget_s: float):
         el = time.perf_counter() - t0
         if el >= budget_s or n >= 64:
             break
-    return {"value": n / el, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+    cores = oracle.num_threads()
+    # one more step on a single thread (the same code; its row loops serial)
+    oracle.set_num_threads(1)
+    t1 = time.perf_counter()
+    ref.decode_step(tok, ctx + n)
+    el1 = time.perf_counter() - t1
+    oracle.set_num_threads(cores)
+    return {"value": n / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"{n} greedy decode steps of the same model from a synthetic {ctx}-token cache "
-                      f"(positions {ctx}..{ctx + n - 1}), {el:.1f} s, float64"}
+                      f"(positions {ctx}..{ctx + n - 1}), {el:.1f} s, float64; one more step on 1 thread "
+                      f"took {el1:.1f} s",
+            "value_1_thread": 1.0 / el1}
 
 
 def main():

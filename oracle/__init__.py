@@ -64,6 +64,7 @@ def _load():
             "or_decode_step": ([ctypes.POINTER(_Model), v, v, v, i32, i32, v], i32),
             "or_prefill": ([ctypes.POINTER(_Model), v, v, v, v, i32, i32], i32),
             "or_num_threads": ([], i32),
+            "or_set_num_threads": ([i32], None),
         }
         for name, (args, res) in sig.items():
             f = getattr(lib, name)
@@ -160,6 +161,11 @@ def silu(z: float) -> float:
 def num_threads() -> int:
     """OpenMP threads the oracle's row loops use."""
     return int(_load().or_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads for the oracle's row loops from now on (timing only)."""
+    _load().or_set_num_threads(int(n))
 
 
 def argmax(v) -> int:

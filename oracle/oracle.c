@@ -281,6 +281,8 @@ int or_prefill(const or_model *m, const void *const *w, void *kc, void *vc, cons
 #ifdef _OPENMP
 #include <omp.h>
 int or_num_threads(void) { return omp_get_max_threads(); }
+void or_set_num_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
 #else
 int or_num_threads(void) { return 1; }
+void or_set_num_threads(int n) { (void)n; }
 #endif
