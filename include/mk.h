@@ -155,8 +155,9 @@ mk_status mk_create_deferred(const mk_model_desc *desc, const mk_tuning *tuning,
    n_layers) (a host array of device pointers; may be NULL when n_layers is
    0), and, when weights->embed is not NULL, the embedding, final norm and
    LM head (weights->lm_head, ignored when tied) are loaded too.  A part may
-   be loaded again; the last load wins.  Synchronous: the caller may free
-   the source tensors when it returns.  Errors: MK_ERR_NULL (h, weights, or a
+   be loaded again; the last load wins.  Synchronous: it first waits for all
+   work on the device (so no step of the handle still reads the weights it
+   replaces), and the caller may free the source tensors when it returns.  Errors: MK_ERR_NULL (h, weights, or a
    pointer of a part being loaded is NULL), MK_ERR_RANGE (the layer range
    is outside [0, n_layers)). */
 mk_status mk_load_weights(mk_handle *h, const mk_weight_ptrs *weights, int32_t first_layer, int32_t n_layers);

@@ -287,6 +287,8 @@ static mk_status load_impl(mk_handle *h, const mk_weight_ptrs *wp, int first, in
     const MkParams &P = h->base;
     const int L = D.n_layers, H = D.hidden, V = D.vocab, grid = P.grid;
     const int dtype = D.dtype == MK_BF16 ? 1 : 0;
+    // no step of this handle may still be reading the weights being replaced
+    HIP_TRY(hipDeviceSynchronize());
     for (int i = 0; i < n; ++i) {
         const int l = first + i;
         const mk_layer_ptrs &lw = wp->layers[i];
