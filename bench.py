@@ -157,7 +157,7 @@ def main():
                          "size, to scale rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: the library runs on one GPU; --gpus {args.gpus} is not supported "
               "(the multi-GPU tensor-parallel design is described but not built).", file=sys.stderr)
         sys.exit(2)
 
