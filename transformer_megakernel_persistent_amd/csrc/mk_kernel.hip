@@ -604,6 +604,8 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
     // Each stage is a block: its per-lane register state (the input slice of
     // a GEMV, the attention accumulators) is declared inside the block, so
     // its registers are free again for the next stage.
+    // consumer waves issue ahead of the loader wave sharing their SIMD
+    __builtin_amdgcn_s_setprio(2);
     const int c = wave - MK_NUM_LOADERS;        // consumer index 0..3
     const int ct = tid - MK_NUM_LOADERS * 64;   // consumer thread 0..255
     int js = 0;     // ring slot of the next data step
