@@ -327,3 +327,14 @@ def test_row_groups_hidden4096(env):
                                       vocab=1000, tied=True, rope_theta=500000.0)
     errs, agree = run_pair(env, cfg, seed=41, n_prompt=30, n_steps=4)
     assert max(errs) <= 2e-2 and agree == 4
+
+
+def test_stage_timeline_tool_runs(env, capsys):
+    """The stage-timeline diagnostic (mk_read_trace) runs end to end and
+    reports every stage kind."""
+    from transformer_megakernel_persistent_amd import stage_timeline
+    stage_timeline.summarise("tiny", {})
+    out = capsys.readouterr().out
+    for st in stage_timeline.STAGES:
+        assert f"  {st:5s} epilogue" in out
+    assert "per layer" in out
