@@ -205,6 +205,15 @@ def test_tiny_bf16_head128(env):
     assert max(errs) <= 2e-2 and agree == 4
 
 
+def test_tiny_bf16_group8_head128_prefill(env):
+    # the 70B shape's pairing of eight query heads per KV head with head_dim
+    # 128, through both instantiations: the prefill (no LM head) fills the
+    # cache, whose rows are compared with the oracle's, then decode steps
+    cfg = synth.CONFIGS["tiny"].with_(dtype="bf16", n_heads=16, n_kv_heads=2, head_dim=128, rope_theta=500000.0)
+    errs, agree = run_pair(env, cfg, seed=13, n_prompt=45, n_steps=4)
+    assert max(errs) <= 2e-2 and agree == 4
+
+
 @pytest.mark.parametrize("n_prompt", [63, 64, 65, 72, 200])
 def test_split_remainders(env, n_prompt):
     # splits whose positions end exactly on a KV slot, one past it, a short
