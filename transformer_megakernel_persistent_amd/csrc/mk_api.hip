@@ -168,16 +168,19 @@ static mk_status create_impl(const mk_model_desc *desc, const mk_tuning *tun, mk
         // the down stage is split along its input: its geometry follows the gate/up units
         s.units = k == ST_DOWN ? (int)ceil_div(2LL * F, 4) : (int)ceil_div(s.rows, 4);
         s.rbp = k == ST_DOWN ? 0 : (int)ceil_div((int64_t)s.k * eb, MK_CHUNK_BYTES);
-        int64_t block = 0;
+        int64_t block = 0, max_nsl = 0;
         for (int w = 0; w < grid; ++w) {
             const int u0 = (int)((int64_t)w * s.units / grid), u1 = (int)((int64_t)(w + 1) * s.units / grid);
             off_host[(size_t)k * grid + w] = block;
             if (k == ST_DOWN) {
                 const MkDownGeo dg = mk_down_geo(w, grid, s.units, F, H, 16 / eb);
                 block += (int64_t)dg.nsl * MK_SLOT_BYTES;
+                if (dg.nsl > max_nsl) max_nsl = dg.nsl;
                 continue;
             }
-            block += ceil_div((int64_t)(u1 - u0) * s.rbp, 4) * MK_SLOT_BYTES;
+            const int64_t nsl_w = ceil_div((int64_t)(u1 - u0) * s.rbp, 4);
+            block += nsl_w * MK_SLOT_BYTES;
+            if (nsl_w > max_nsl) max_nsl = nsl_w;
             if ((u1 - u0) * 4 > out_rows) out_rows = (u1 - u0) * 4;
             if (k == ST_O) {
                 if ((u1 - u0) * 4 > 64) return MK_ERR_SHAPE;  // residual rows kept in LDS
@@ -185,6 +188,12 @@ static mk_status create_impl(const mk_model_desc *desc, const mk_tuning *tun, mk
             }
         }
         if (s.rbp * epc > vec_floats) vec_floats = s.rbp * epc;
+        // Striped slots: slot n of workgroup w at (n * grid + w) * 16 KiB of
+        // the layer block, so that at any moment the grid streams one compact
+        // window of memory (workgroups with fewer slots leave holes).
+        for (int w = 0; w < grid; ++w) off_host[(size_t)k * grid + w] = (int64_t)w * MK_SLOT_BYTES;
+        s.slot_stride = (int64_t)grid * MK_SLOT_BYTES;
+        block = max_nsl * s.slot_stride;
         s.base = total;
         s.layer_stride = k == ST_LM ? 0 : block;
         total += k == ST_LM ? block : block * L;

@@ -5,9 +5,11 @@
 //     consecutive packed rows; unit u of a stage goes to workgroup
 //     w = the w with floor(w*U/G) <= u < floor((w+1)*U/G).  Inside a
 //     workgroup, local row i belongs to consumer wave i % 4.
-//   - A workgroup's weights for a stage are one contiguous block of 16 KiB
-//     "slots".  Slot n holds, for each consumer c, the next 4 KiB of c's rows
-//     (row-major, each row zero-padded to whole 1 KiB chunks).  Loader waves
+//   - A workgroup's weights for a stage are a sequence of 16 KiB "slots",
+//     striped with the other workgroups' (slot n of workgroup w at
+//     (n * grid + w) * 16 KiB of the stage's layer block).  Slot n holds,
+//     for each consumer c, the next 4 KiB of c's rows (each row zero-padded
+//     to whole 1 KiB chunks; see mk_stream_pos for the order).  Loader waves
 //     copy slots into an LDS ring with direct-to-LDS loads; consumer waves
 //     read their 4 KiB piece of the slot.
 //   - Attention splits each KV head's positions [0, pos) into `splits`
@@ -85,7 +87,8 @@ struct MkStage {
     int32_t rows;         // logical packed rows (units*4 >= rows; the rest are zero)
     int64_t base;         // byte offset of layer 0's block in the packed buffer
     int64_t layer_stride; // bytes between consecutive layers' blocks
-    const int64_t *wg_off;   // [grid] byte offset of each workgroup's sub-block in a layer block
+    const int64_t *wg_off;   // [grid] byte offset of each workgroup's first slot in a layer block
+    int64_t slot_stride;     // bytes between a workgroup's consecutive slots (grid * 16 KiB: striped)
 };
 
 struct MkParams {

@@ -444,7 +444,8 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
                         case 4: it_ptr = wb_dn + (int64_t)it_l * ws_dn; break;
                         default: it_ptr = wb_lm; break;
                         }
-                        it_step = MK_SLOT_BYTES;
+                        it_step = p.st[it_k == 5 ? ST_LM : it_k == 0 ? ST_QKV : it_k == 2 ? ST_O : it_k == 3 ? ST_GU : ST_DOWN]
+                                      .slot_stride;
                     }
                     return;
                 }

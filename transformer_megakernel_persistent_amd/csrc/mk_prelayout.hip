@@ -13,7 +13,9 @@
 //   GU  : gate row f and up row f interleaved (packed rows 2f, 2f+1), so a
 //         workgroup owns both halves of every SwiGLU product it emits.
 //   O, LM: natural row order.
-// Within a workgroup's block, slot n holds for consumer c the 4 KiB of its row
+// The workgroups' slots are striped: slot n of workgroup w lies at
+// wg_off[w] + n * slot_stride (wg_off[w] = w * 16 KiB, slot_stride = grid *
+// 16 KiB).  Slot n holds for consumer c the 4 KiB of its row
 // stream at [4n, 4n+4) chunks; consumer c's rows are local rows c, c+4, ...,
 // and rows of 8, 12, ... chunks are interleaved in groups of four (see
 // mk_stream_pos) so that one slot carries the same chunk of four rows.
@@ -56,7 +58,8 @@ __global__ __launch_bounds__(256) void prelayout_kernel(unsigned char *dst_block
                     for (int b = 0; b < eb; ++b) tmp[e * eb + b] = srow[(int64_t)(fa + e) * eb + b];
             val = *(const uint4 *)tmp;
         }
-        *(uint4 *)(dst_block + st.wg_off[w] + (int64_t)chunk * MK_CHUNK_BYTES + lane * 16) = val;
+        *(uint4 *)(dst_block + st.wg_off[w] + (int64_t)(chunk / MK_CHUNKS_PER_SLOT) * st.slot_stride +
+                   (chunk % MK_CHUNKS_PER_SLOT) * MK_CHUNK_BYTES + lane * 16) = val;
         return;
     }
     const int nsl = (units * st.rbp + 3) / 4;
@@ -97,7 +100,8 @@ __global__ __launch_bounds__(256) void prelayout_kernel(unsigned char *dst_block
             }
         }
     }
-    *(uint4 *)(dst_block + st.wg_off[w] + (int64_t)chunk * MK_CHUNK_BYTES + lane * 16) = val;
+    *(uint4 *)(dst_block + st.wg_off[w] + (int64_t)(chunk / MK_CHUNKS_PER_SLOT) * st.slot_stride +
+               (chunk % MK_CHUNKS_PER_SLOT) * MK_CHUNK_BYTES + lane * 16) = val;
 }
 
 __global__ void to_f32_kernel(float *dst, const void *src, int64_t n, int dtype) {
