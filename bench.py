@@ -5,16 +5,20 @@
 A step is one decode step of the whole path (embedding -> all layers ->
 LM head -> greedy argmax), launched as ONE kernel through the C ABI
 (mk_decode_step_device_token): each launch reads the token the previous
-launch wrote, so the timed loop runs with no host round trip.  The default
+launch wrote, so the timed loop runs with no host round trip.  The headline
 workload is the Llama-3.2-1B-shaped decoder with a 2048-token context and
 128 greedy steps; weights are seeded N(0, 0.02) bf16 (synthetic, random
 init) and the context is filled by mk_prefill_kv from seeded token ids.
+The Llama-3-8B shape (2048-token context) and the 1B shape at a 32768-token
+context are measured in the same run and reported under `extra_workloads`.
 
-Prints ONE JSON line.  `value` is tokens/s over the timed steps (wall clock,
-inputs resident in HBM); `roofline` divides the algorithmic bytes of a step
-(every weight once + the K/V rows read at that position) by the average
-kernel duration measured with events on the launch stream; `cpu_baseline`
-times the CPU oracle on a bounded sample of the same workload.
+Each workload is timed in `--runs` (3) runs of K steps; the median run gives
+`value` (tokens/s, wall clock, inputs resident in HBM) and the roofline
+figure, p50/P99 pool the steps of every run.  Prints ONE JSON line.
+`roofline` divides the algorithmic bytes of a step (every weight once + the
+K/V rows read at that position) by the average kernel duration measured
+with events on the launch stream; `cpu_baseline` times the CPU oracle on a
+bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -134,12 +138,125 @@ def cpu_baseline(cfg, host_w, shape, budget_s: float):
             "value_1_thread": 1.0 / el1}
 
 
+def measure(name, args, dev, steps, warm, runs, cpu_budget, with_cpu):
+    """One workload: load, prefill, `warm` untimed steps, then `runs` timed
+    runs of `steps` chained device-token steps each.  Returns its record."""
+    import torch
+
+    import synth
+    import transformer_megakernel_persistent_amd as mkp
+
+    cfg = synth.CONFIGS[name]
+    shape = {k: v for k, v in dataclasses.asdict(cfg).items() if k in SHAPE_KEYS}
+    ctx = cfg.context
+    max_seq = ctx + warm + runs * steps
+    tuning = {"grid": args.grid, "ring_slots": args.ring, "attn_splits": args.splits,
+              "cooperative": 1 if args.launch == "cooperative" else 2,
+              "prefetch_depth": args.prefetch_depth, "stage_drain": 1 if args.stage_drain else 0}
+    # The oracle baseline needs every weight in host memory; past this size it
+    # is not taken (the weights are streamed to the device a layer at a time).
+    keep_host = with_cpu and cfg.weight_bytes_per_step() <= HOST_ORACLE_MAX_BYTES
+    t = time.perf_counter()
+    mk, host_w = load_model(mkp, synth, cfg, shape, max_seq, tuning, args.seed, dev, keep_host)
+    print(f"[bench] {cfg.name}: weights generated and loaded in {time.perf_counter() - t:.1f}s", file=sys.stderr,
+          flush=True)
+    torch.cuda.empty_cache()
+    info = mk.info()
+    kv = mkp.KVCache(shape, max_seq, dev)
+    prompt = synth.gen_tokens(args.seed, ctx + 1, cfg.vocab)
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    mk.prefill_kv(prompt[:ctx], 0, kv)
+    torch.cuda.synchronize()
+    prefill_s = time.perf_counter() - t
+    print(f"[bench] {cfg.name}: prefill of {ctx} positions: {prefill_s:.2f}s", file=sys.stderr, flush=True)
+    if mk.device_error() != 0:
+        raise RuntimeError("device error during prefill")
+
+    stream = torch.cuda.current_stream()
+    n_tok = warm + runs * steps
+    tok = torch.tensor([int(prompt[ctx])], dtype=torch.int32, device=dev)
+    toks_out = torch.empty(n_tok, dtype=torch.int32, device=dev)
+    logits = torch.empty(cfg.vocab, dtype=torch.float32, device=dev)
+
+    def step(i):  # launch i of the chain: position ctx + i, token from launch i - 1
+        src = toks_out[i - 1:i] if i > 0 else tok
+        mk.decode_step_device_token(src, ctx + i, kv, logits, toks_out[i:i + 1], stream)
+
+    for i in range(warm):
+        step(i)
+    torch.cuda.synchronize()
+    run_recs = []
+    for r in range(runs):
+        i0 = warm + r * steps
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev[0].record(stream)
+        for i in range(steps):
+            step(i0 + i)
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        step_us = [ev[i].elapsed_time(ev[i + 1]) * 1000.0 for i in range(steps)]
+        run_recs.append({"wall": wall, "step_us": step_us, "pos0": ctx + i0})
+    if mk.device_error() != 0:
+        raise RuntimeError("device error during the timed steps")
+    tokens = toks_out[warm:].cpu().numpy()
+    mk.close()
+    del kv
+    torch.cuda.empty_cache()
+
+    # the median run (by wall time) carries the figures; p50/P99 pool every step
+    order = sorted(range(runs), key=lambda r: run_recs[r]["wall"])
+    med = run_recs[order[runs // 2]]
+    all_us = [u for rr in run_recs for u in rr["step_us"]]
+    p50, p99 = percentile(all_us, 0.5), percentile(all_us, 0.99)
+    mean_us = sum(med["step_us"]) / steps
+    bytes_per_step = [cfg.step_bytes(med["pos0"] + i) for i in range(steps)]
+    mean_bytes = sum(bytes_per_step) / len(bytes_per_step)
+    achieved = mean_bytes / (mean_us * 1e-6) / 1e9
+    gbs_p50 = cfg.step_bytes(med["pos0"] + steps // 2) / (p50 * 1e-6) / 1e9
+    traffic = traffic_from_profile(cfg.name)
+
+    cpu = None
+    if host_w is not None:
+        cpu = cpu_baseline(cfg, host_w, shape, cpu_budget)
+    return {
+        "workload": f"{cfg.name}: {cfg.n_layers}L hidden {cfg.hidden}, {cfg.n_heads}q/{cfg.n_kv_heads}kv heads x "
+                    f"{cfg.head_dim}, SwiGLU {cfg.ffn}, vocab {cfg.vocab}{' tied' if cfg.tied else ''}, "
+                    f"{cfg.dtype} weights+KV, fp32 accumulate; {ctx}-token context, {steps} greedy steps per run, "
+                    f"batch 1",
+        "name": cfg.name,
+        "value": steps / med["wall"],
+        "runs_tokens_per_s": [steps / rr["wall"] for rr in run_recs],
+        "ms_per_step": med["wall"] * 1000.0 / steps,
+        "us_per_token_p50": p50,
+        "us_per_token_p99": p99,
+        "us_per_token_mean": mean_us,
+        "gbs_p50": gbs_p50,
+        "bytes_per_step": mean_bytes,
+        "decode_positions": [ctx + warm, ctx + n_tok - 1],
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic},
+        "cpu_baseline": cpu,
+        "prefill": {"positions": ctx, "seconds": prefill_s, "tokens_per_s": ctx / prefill_s},
+        "info": info,
+        "first_tokens": [int(x) for x in tokens[:8]],
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps per run (default: the workload's)")
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="llama1b")
+    ap.add_argument("--runs", type=int, default=3, help="timed runs; the median run is reported")
+    ap.add_argument("--config", default="llama1b", help="the headline workload")
+    ap.add_argument("--extra", default=None,
+                    help="comma-separated further workloads reported in the same line (default with the llama1b "
+                         "headline: llama8b,llama1b_32k; otherwise none)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--grid", type=int, default=0)
@@ -161,113 +278,64 @@ def main():
               "(the multi-GPU tensor-parallel design is described but not built).", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import synth
-    import transformer_megakernel_persistent_amd as mkp
 
-    cfg = synth.CONFIGS[args.config]
-    steps = args.steps if args.steps is not None else cfg.decode_steps
-    warm = args.warmup
-    shape = {k: v for k, v in dataclasses.asdict(cfg).items() if k in SHAPE_KEYS}
-    ctx = cfg.context
-    max_seq = ctx + warm + steps
+    if args.extra is None:
+        extra = ["llama8b", "llama1b_32k"] if args.config == "llama1b" else []
+    else:
+        extra = [x for x in args.extra.split(",") if x]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-
-    tuning = {"grid": args.grid, "ring_slots": args.ring, "attn_splits": args.splits,
-              "cooperative": 1 if args.launch == "cooperative" else 2,
-              "prefetch_depth": args.prefetch_depth, "stage_drain": 1 if args.stage_drain else 0}
-    # The oracle baseline needs every weight in host memory; past this size it
-    # is not taken (the weights are streamed to the device a layer at a time).
-    keep_host = not args.no_cpu_baseline and cfg.weight_bytes_per_step() <= HOST_ORACLE_MAX_BYTES
-    t = time.perf_counter()
-    mk, host_w = load_model(mkp, synth, cfg, shape, max_seq, tuning, args.seed, dev, keep_host)
-    print(f"[bench] {cfg.name}: weights generated and loaded in {time.perf_counter() - t:.1f}s", file=sys.stderr,
-          flush=True)
-    torch.cuda.empty_cache()
-    info = mk.info()
-    kv = mkp.KVCache(shape, max_seq, dev)
-    prompt = synth.gen_tokens(args.seed, ctx + 1, cfg.vocab)
-    t = time.perf_counter()
-    mk.prefill_kv(prompt[:ctx], 0, kv)
-    torch.cuda.synchronize()
-    print(f"[bench] prefill of {ctx} positions: {time.perf_counter() - t:.2f}s", file=sys.stderr, flush=True)
-    if mk.device_error() != 0:
-        raise RuntimeError("device error during prefill")
-
-    stream = torch.cuda.current_stream()
-    tok = torch.tensor([int(prompt[ctx])], dtype=torch.int32, device=dev)
-    toks_out = torch.empty(warm + steps, dtype=torch.int32, device=dev)
-    logits = torch.empty(cfg.vocab, dtype=torch.float32, device=dev)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-
-    pos = ctx
-    for i in range(warm):
-        mk.decode_step_device_token(tok if i == 0 else toks_out[i - 1:i], pos, kv, logits, toks_out[i:i + 1], stream)
-        pos += 1
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev[0].record(stream)
-    for i in range(steps):
-        src = toks_out[warm + i - 1:warm + i] if warm + i > 0 else tok
-        mk.decode_step_device_token(src, pos + i, kv, logits, toks_out[warm + i:warm + i + 1], stream)
-        ev[i + 1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    if mk.device_error() != 0:
-        raise RuntimeError("device error during the timed steps")
-
-    step_us = [ev[i].elapsed_time(ev[i + 1]) * 1000.0 for i in range(steps)]
-    p50, p99 = percentile(step_us, 0.5), percentile(step_us, 0.99)
-    mean_us = sum(step_us) / len(step_us)
-    bytes_per_step = [cfg.step_bytes(pos + i) for i in range(steps)]
-    mean_bytes = sum(bytes_per_step) / len(bytes_per_step)
-    achieved = mean_bytes / (mean_us * 1e-6) / 1e9
-    gbs_p50 = cfg.step_bytes(pos + steps // 2) / (p50 * 1e-6) / 1e9
-    traffic = traffic_from_profile(cfg.name)
-    tokens = toks_out[warm:].cpu().numpy()
-
-    cpu = None
-    if host_w is not None:
-        cpu = cpu_baseline(cfg, host_w, shape, args.cpu_budget)
-
+    with_cpu = not args.no_cpu_baseline
+    cfg = synth.CONFIGS[args.config]
+    steps = args.steps if args.steps is not None else cfg.decode_steps
+    head = measure(args.config, args, dev, steps, args.warmup, args.runs, args.cpu_budget, with_cpu)
+    extras = []
+    for name in extra:
+        c = synth.CONFIGS[name]
+        n = args.steps if args.steps is not None else c.decode_steps
+        rec = measure(name, args, dev, n, args.warmup, args.runs, min(args.cpu_budget, 10.0), with_cpu)
+        extras.append({k: rec[k] for k in ("name", "workload", "value", "runs_tokens_per_s", "ms_per_step",
+                                           "us_per_token_p50", "us_per_token_p99", "us_per_token_mean", "gbs_p50",
+                                           "bytes_per_step", "decode_positions", "roofline", "cpu_baseline",
+                                           "prefill", "first_tokens")} | {"unit": "tokens/s", "steps": n})
+    info = head["info"]
     out = {
         "metric": "batch-1 decode tokens/s (us/token p50/P99) + achieved HBM GB/s vs peak",
-        "value": steps / wall,
+        "value": head["value"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": steps,
-        "warmup": warm,
-        "ms_per_step": wall * 1000.0 / steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "dtype": head["dtype"],
         "data": "synthetic: seeded N(0,0.02) random-init weights, uniform random prompt tokens, greedy decode",
         "config": {
-            "workload": f"{cfg.name}: {cfg.n_layers}L hidden {cfg.hidden}, {cfg.n_heads}q/{cfg.n_kv_heads}kv heads x "
-                        f"{cfg.head_dim}, SwiGLU {cfg.ffn}, vocab {cfg.vocab}{' tied' if cfg.tied else ''}, "
-                        f"{cfg.dtype} weights+KV, fp32 accumulate; {ctx}-token context, {steps} greedy steps, batch 1",
-            "context": ctx, "global_batch": 1, "decode_positions": [pos, pos + steps - 1],
-            "launches_per_token": 1, "grid": info["grid"], "ring_slots": info["ring_slots"],
+            "workload": head["workload"],
+            "context": cfg.context, "global_batch": 1, "decode_positions": head["decode_positions"],
+            "runs": args.runs, "launches_per_token": 1, "grid": info["grid"], "ring_slots": info["ring_slots"],
             "prefetch_slots": info["prefetch_slots"], "stage_drain": bool(args.stage_drain),
             "attn_splits": info["attn_splits"], "block_threads": info["block_threads"],
             "lds_bytes": info["lds_bytes"], "launch": args.launch, "parallelism": "single GPU"},
-        "us_per_token_p50": p50,
-        "us_per_token_p99": p99,
-        "us_per_token_mean": mean_us,
-        "gbs_p50": gbs_p50,
-        "bytes_per_step": mean_bytes,
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic},
-        "cpu_baseline": cpu,
+        "runs_tokens_per_s": head["runs_tokens_per_s"],
+        "us_per_token_p50": head["us_per_token_p50"],
+        "us_per_token_p99": head["us_per_token_p99"],
+        "us_per_token_mean": head["us_per_token_mean"],
+        "gbs_p50": head["gbs_p50"],
+        "bytes_per_step": head["bytes_per_step"],
+        "roofline": head["roofline"],
+        "cpu_baseline": head["cpu_baseline"],
+        "prefill": head["prefill"],
+        "extra_workloads": extras,
         "kernel_hash": kernel_hash(),
-        "first_tokens": [int(x) for x in tokens[:8]],
+        "first_tokens": head["first_tokens"],
     }
     print(json.dumps(out), flush=True)
-    mk.close()
     if args.copy_calibration:
         n = args.copy_calibration // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)

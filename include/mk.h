@@ -24,11 +24,18 @@
  *     www.stapisi.com/news/3904786 section 3.3).
  *   - Every call returns an mk_status; nothing throws across the ABI.
  *     Argument checks are done on the host before any device work is
- *     enqueued ("defensive checks on input bounds", cloud.baidu.com/article/
- *     9434380 section 九).
+ *     enqueued (the page cloud.baidu.com/article/9434380, section 九, asks
+ *     for guards on input ranges in a fused kernel).
  *   - Device-side failures (a grid-wait timeout) are asynchronous: they set
  *     a device flag that mk_get_device_error reports, after which the handle
  *     refuses further steps (MK_ERR_STATE).
+ *   - Ordering: each call that enqueues work records an event of the handle
+ *     after its launches; a call on a different stream than the handle's
+ *     previous call first makes its stream wait on that event (record on one
+ *     stream, wait on another: www.stapisi.com/news/3904786 section 3.1).
+ *     So the calls of one handle run in the order they were made, whatever
+ *     streams the caller passes.  Calls on one handle from several host
+ *     threads at once are not supported.
  */
 #ifndef MK_H
 #define MK_H
@@ -127,6 +134,7 @@ typedef struct {
     int32_t prefetch_slots;  /* 16 KiB slots the loads run ahead of the arithmetic */
     int64_t packed_bytes;    /* library-owned pre-laid-out weight bytes */
     int64_t weight_bytes;    /* algorithmic weight bytes read per step */
+    int64_t record_bytes;    /* cross-workgroup record buffer of one launch */
 } mk_info;
 
 /* Create a handle: validates the shape, copies every weight into a
@@ -166,7 +174,16 @@ mk_status mk_load_weights(mk_handle *h, const mk_weight_ptrs *weights, int32_t f
    position pos into the cache, reads cache positions [0, pos] (never
    positions > pos) and writes vocab fp32 logits to logits_out (device).
    Enqueued on `stream`; returns immediately.  Requires 0 <= token_id < vocab
-   and 0 <= pos < max_seq. */
+   and 0 <= pos < max_seq.
+   The operation is the whole decode step of the pages' path as one launch
+   (cloud.baidu.com/article/9434380 section 4.2 and section 五 steps 2-3;
+   developer.baidu.com/article/detail.html?id=8006242 section 4.1); its
+   arguments follow the asynchronous forward entry of
+   www.stapisi.com/news/3904786 section 5.2 (a stream, the input, the output
+   and the KV cache, enqueued without waiting).  Errors: MK_ERR_NULL (h,
+   kv, its pointers or logits_out NULL), MK_ERR_SHAPE (kv->max_seq differs
+   from the model's), MK_ERR_RANGE, MK_ERR_STATE (disabled handle or weights
+   not all loaded), MK_ERR_HIP (the launch failed). */
 mk_status mk_decode_step(mk_handle *h, int32_t token_id, int32_t pos, const mk_kv_cache *kv,
                          float *logits_out, void *stream);
 
@@ -174,25 +191,45 @@ mk_status mk_decode_step(mk_handle *h, int32_t token_id, int32_t pos, const mk_k
    the greedy next token (argmax of the logits, lowest index on ties) written
    to device memory (token_out, one int32).  Lets a caller enqueue many steps
    back to back with no host round trip.  logits_out may be NULL.  A token id
-   outside [0, vocab) in token_in raises the device error flag. */
+   outside [0, vocab) in token_in raises the device error flag.
+   The greedy choice runs on the fused path itself, where the page
+   cloud.baidu.com/article/9434380 section 五 step 5 asks that sampling and
+   the state carried from step to step be checked again. */
 mk_status mk_decode_step_device_token(mk_handle *h, const int32_t *token_in, int32_t pos, const mk_kv_cache *kv,
                                       float *logits_out, int32_t *token_out, void *stream);
 
 /* Fill cache positions [start_pos, start_pos + n) from n host token ids: by
    definition under causal attention this is n decode steps at those
    positions with the LM head skipped.  Requires n >= 0 and
-   start_pos + n <= max_seq. */
+   start_pos + n <= max_seq.
+   The pages keep the prefill apart from the decode step and measure the two
+   phases separately (cloud.baidu.com/article/9434380 section 八, question
+   two); the cache it fills is the state handed between steps (same page,
+   section 五 step 4).  Errors: MK_ERR_NULL, MK_ERR_SHAPE, MK_ERR_RANGE (a
+   token id outside [0, vocab) or the range past max_seq), MK_ERR_STATE,
+   MK_ERR_HIP. */
 mk_status mk_prefill_kv(mk_handle *h, const int32_t *tokens, int32_t n, int32_t start_pos, const mk_kv_cache *kv,
                         void *stream);
 
-/* Synchronizes the handle's last stream and reports a device failure flag:
-   MK_OK, or MK_ERR_DEVICE (after which the handle is disabled). */
+/* Waits for the handle's last call to complete (its recorded event, on
+   whatever stream that call used: no stream argument is needed) and reports
+   the device failure flag: MK_OK, MK_ERR_DEVICE (after which the handle is
+   disabled), or MK_ERR_STATE for a handle disabled earlier.  The stability
+   advice of the pages (cloud.baidu.com/article/9434380 section 九;
+   developer.baidu.com/article/detail.html?id=8006242 section 6.2) asks for
+   bounds checks on a fused kernel; the kernel's device-side checks (a token
+   id read from device memory, a dependency wait that times out) report
+   here. */
 mk_status mk_get_device_error(mk_handle *h);
 
+/* Launch geometry and sizes of a created handle, for benchmarks and tests
+   (the tunables the page cloud.baidu.com/article/9434380 section 六 asks to
+   expose).  Errors: MK_ERR_NULL. */
 mk_status mk_get_info(const mk_handle *h, mk_info *info);
 
-/* Stage timeline of the most recent step (handles created with trace = 1):
-   synchronizes the last stream, then copies uint64 wall-clock ticks (100 MHz
+/* Stage timeline of the most recent step (handles created with trace = 1;
+   the per-stage timing points of www.stapisi.com/news/3904786 section 5.3):
+   waits for the handle's last call, then copies uint64 wall-clock ticks (100 MHz
    on MI355X) into host_out, three arrays one after the other:
    1. grid * (5*n_layers + 2) * 4, laid out [workgroup][boundary][event].
       Boundary 5l+k is the start of stage k of layer l (k: 0 QKV,
@@ -208,9 +245,13 @@ mk_status mk_get_info(const mk_handle *h, mk_info *info);
    hold (at least the sum of the three sizes). */
 mk_status mk_read_trace(mk_handle *h, uint64_t *host_out, int64_t capacity);
 
+/* A static, human-readable name of a status ("unknown status" for values
+   outside the enum).  Never NULL; the caller does not free it. */
 const char *mk_status_str(mk_status s);
 
-/* Frees everything the handle owns.  NULL is allowed. */
+/* Frees everything the handle owns (packed weights, records, tables,
+   event).  The caller must make sure no call of the handle is still running
+   (mk_get_device_error waits for the last one).  NULL is allowed. */
 void mk_destroy(mk_handle *h);
 
 #ifdef __cplusplus

@@ -6,8 +6,9 @@
  *
  * Plain, slow and deliberately obvious: every value is a float64, every dot
  * product is a single left-to-right sum, nothing is blocked, fused or
- * reordered.  OpenMP only splits independent output rows between threads, so
- * the result does not depend on the thread count.
+ * reordered.  OpenMP only splits independent output rows (and independent
+ * attention heads) between threads, so the result does not depend on the
+ * thread count.
  *
  * What is computed.  The pages name the operators of a decode step and the
  * order they run in, but write no formulas:
@@ -240,6 +241,9 @@ int or_decode_step(const or_model *m, const void *const *w, void *kc, void *vc, 
                 kvstore(kc, dt, kv_off(m, l, j, pos) + i, k[(size_t)j * d + i]);
                 kvstore(vc, dt, kv_off(m, l, j, pos) + i, v[(size_t)j * d + i]);
             }
+        /* heads are independent: OpenMP splits them between threads, each
+           head's sums keep their sequential order */
+#pragma omp parallel for schedule(static)
         for (int i = 0; i < nh; ++i) {
             int j = i / group;
             const size_t base = kv_off(m, l, j, 0) * (dt ? 2u : 4u);

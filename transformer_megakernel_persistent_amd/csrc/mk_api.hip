@@ -15,6 +15,14 @@
 
 extern "C" int mk_kernel_max_blocks_per_cu(int dtype, int gq, int lpp, int lds);
 
+// Offsets (in records) of the cross-workgroup record arrays inside one
+// record buffer, in MkParams order: xq, xg, qkv, part, o, dpart, amax; [7] is
+// the total.  Each per-layer array holds two layers (even and odd index).
+struct RecLayout {
+    size_t off[8];
+};
+
+
 struct mk_handle {
     mk_model_desc desc;
     int eb = 0;
@@ -30,11 +38,17 @@ struct mk_handle {
     void *embed = nullptr;
     float *rope = nullptr;
     uint64_t *ll = nullptr;     // tagged cross-workgroup records (see MkParams)
+    RecLayout rec;              // their layout
     uint32_t *err = nullptr;    // device error word
     uint64_t *trace = nullptr;
     int64_t trace_len = 0;
-    uint32_t tag = 0;           // tag of the last launch
+    uint32_t tag_end = 0;       // last tag used on the handle's own records
     bool disabled = false;
+    // Completion of the handle's last call: recorded on its stream after the
+    // launches; a call on another stream first waits for it, so the launches
+    // of one handle stay ordered whatever streams the caller uses.
+    hipEvent_t done = nullptr;
+    bool done_recorded = false;
     hipStream_t last_stream = nullptr;
     int lds_bytes = 0;
     std::vector<char> layer_loaded;  // [n_layers]: weights of the layer pre-laid out
@@ -53,6 +67,35 @@ mk_status hip_fail(hipError_t e) { return e == hipErrorOutOfMemory ? MK_ERR_NOME
     } while (0)
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Tag base of the next launch on a record buffer whose last launch used tags
+// up to `end` (a launch tags its records base + l for layer index l in
+// [0, L]): the range starts right after `end` and `end` moves to its last
+// tag.  A range that would hold 0 (the tag of a never-written record) or wrap
+// around 2^32 starts over at 1; *wrapped is then set, and the caller clears
+// the buffer first so that no record left from 2^32 tags ago can match.
+uint32_t next_tag_base(uint32_t &end, int L, bool *wrapped) {
+    uint64_t nb = (uint64_t)end + 1;
+    *wrapped = false;
+    if (nb + (uint64_t)L > 0xFFFFFFFFull) {
+        nb = 1;
+        *wrapped = true;
+    }
+    end = (uint32_t)(nb + (uint64_t)L);
+    return (uint32_t)nb;
+}
+
+// The record pointers of a launch, for a record buffer at `base`.
+void set_records(MkParams &P, uint64_t *base, const RecLayout &r) {
+    P.ll_xq = base + r.off[0];
+    P.ll_xg = base + r.off[1];
+    P.ll_qkv = base + r.off[2];
+    P.ll_part = base + r.off[3];
+    P.ll_o = base + r.off[4];
+    P.ll_dpart = base + r.off[5];
+    P.ll_amax = base + r.off[6];
+}
+
 
 struct StageShape {
     int rows, k;
@@ -113,6 +156,7 @@ extern "C" void mk_destroy(mk_handle *h) {
     hipFree(h->ll);
     hipFree(h->err);
     hipFree(h->trace);
+    if (h->done) hipEventDestroy(h->done);
     delete h;
 }
 
@@ -222,20 +266,35 @@ static mk_status create_impl(const mk_model_desc *desc, const mk_tuning *tun, mk
 
     // allocations
     h->packed_bytes = total;
-    HIP_TRY(hipMalloc(&h->packed, total > MK_SLOT_BYTES ? total : MK_SLOT_BYTES));  // the loaders' idle reads touch the first 8 KiB
+    // The loaders' idle reads (past a split's cache positions, past the end of
+    // the stream) touch the first 1 KiB of the buffer, and the striped layout
+    // leaves holes that no pre-layout writes (for example workgroup 0's first
+    // slot when a stage has fewer units than workgroups).  Zero it all once so
+    // that every byte a loader can read is a finite number: the attention
+    // fold multiplies masked V values by 0.
+    const int64_t packed_alloc = total > MK_SLOT_BYTES ? total : MK_SLOT_BYTES;
+    HIP_TRY(hipMalloc(&h->packed, packed_alloc));
+    HIP_TRY(hipMemset(h->packed, 0, packed_alloc));
     HIP_TRY(hipMalloc(&h->wg_off, off_host.size() * sizeof(int64_t)));
     HIP_TRY(hipMemcpy(h->wg_off, off_host.data(), off_host.size() * sizeof(int64_t), hipMemcpyHostToDevice));
     const size_t ngain = (size_t)2 * L * H + H;
     HIP_TRY(hipMalloc(&h->gains, ngain * sizeof(float)));
     HIP_TRY(hipMalloc(&h->embed, (size_t)V * H * eb));
     HIP_TRY(hipMalloc(&h->rope, (size_t)D.max_seq * d * sizeof(float)));
-    // tagged records, one array per dependency point and layer
-    const size_t n_xq = (size_t)(L + 1) * H, n_xg = (size_t)L * H, n_q = (size_t)L * nkv * (gq + 2) * d,
-                 n_part = (size_t)L * nkv * splits * cph * gq * (d + 2),
-                 n_o = (size_t)L * nh * d, n_dpart = (size_t)L * grid * H, n_amax = (size_t)grid * 2;
-    const size_t n_ll = n_xq + n_xg + n_q + n_part + n_o + n_dpart + n_amax;
+    // tagged records, one array per dependency point, each with two buffers
+    // (layers of even and odd index)
+    const size_t n_rec[7] = {(size_t)2 * H, (size_t)2 * H, (size_t)2 * nkv * (gq + 2) * d,
+                             (size_t)2 * nkv * splits * cph * gq * (d + 2), (size_t)2 * nh * d, (size_t)2 * grid * H,
+                             (size_t)grid * 2};
+    size_t n_ll = 0;
+    for (int i = 0; i < 7; ++i) {
+        h->rec.off[i] = n_ll;
+        n_ll += (n_rec[i] + 31) & ~(size_t)31;  // each array on a 256-byte boundary
+    }
+    h->rec.off[7] = n_ll;
     HIP_TRY(hipMalloc(&h->ll, n_ll * sizeof(uint64_t)));
     HIP_TRY(hipMemset(h->ll, 0, n_ll * sizeof(uint64_t)));  // tag 0: never a launch's tag
+    HIP_TRY(hipEventCreateWithFlags(&h->done, hipEventDisableTiming));
     HIP_TRY(hipMalloc(&h->err, 64 * sizeof(uint32_t)));
     HIP_TRY(hipMemset(h->err, 0, 64 * sizeof(uint32_t)));
     if (t.trace) {
@@ -271,13 +330,7 @@ static mk_status create_impl(const mk_model_desc *desc, const mk_tuning *tun, mk
     P.g_attn = h->gains; P.g_ffn = h->gains + (size_t)L * H; P.g_final = h->gains + (size_t)2 * L * H;
     P.embed = h->embed;
     P.rope = h->rope;
-    P.ll_xq = h->ll;
-    P.ll_xg = P.ll_xq + n_xq;
-    P.ll_qkv = P.ll_xg + n_xg;
-    P.ll_part = P.ll_qkv + n_q;
-    P.ll_o = P.ll_part + n_part;
-    P.ll_dpart = P.ll_o + n_o;
-    P.ll_amax = P.ll_dpart + n_dpart;
+    set_records(P, h->ll, h->rec);
     P.err = h->err;
     P.timeout_ticks = (int64_t)timeout_ms * wclk_khz;
     P.err_check_ticks = (int64_t)wclk_khz / 50;  // 20 us
@@ -405,8 +458,28 @@ static mk_status check_kv(const mk_handle *h, const mk_kv_cache *kv) {
     return MK_OK;
 }
 
+// Before a call's launches: a call on a stream other than the previous call's
+// waits for the previous call to complete (the tagged records and the cache
+// row at pos are shared by every launch of the handle).
+static mk_status order_before(mk_handle *h, void *stream) {
+    if (h->done_recorded && (hipStream_t)stream != h->last_stream)
+        HIP_TRY(hipStreamWaitEvent((hipStream_t)stream, h->done, 0));
+    return MK_OK;
+}
+// After a call's launches: mark its completion on its stream.
+static mk_status order_after(mk_handle *h, void *stream) {
+    HIP_TRY(hipEventRecord(h->done, (hipStream_t)stream));
+    h->done_recorded = true;
+    h->last_stream = (hipStream_t)stream;
+    return MK_OK;
+}
+
+// One launch.  records: the record buffer (NULL: the handle's own, tagged
+// from the handle's counter); tag_base: the launch's tag base when records
+// is given.
 static mk_status launch(mk_handle *h, const mk_kv_cache *kv, int32_t token, const int32_t *token_dev, int32_t pos,
-                        int want_logits, float *logits, int32_t *token_out, void *stream) {
+                        int want_logits, float *logits, int32_t *token_out, void *stream,
+                        uint64_t *records = nullptr, uint32_t tag_base = 0) {
     if (h->layers_loaded < h->desc.n_layers || !h->head_loaded) return MK_ERR_STATE;  // weights still missing
     MkParams p = h->base;
     p.kc = kv->k;
@@ -417,11 +490,26 @@ static mk_status launch(mk_handle *h, const mk_kv_cache *kv, int32_t token, cons
     p.want_logits = want_logits;
     p.logits = logits;
     p.token_out = token_out;
-    if (++h->tag == 0) h->tag = 1;  // 0 marks a record never written
-    p.tag = h->tag;
-    h->last_stream = (hipStream_t)stream;
+    if (records) {
+        set_records(p, records, h->rec);
+        p.tag = tag_base;
+    } else {
+        bool wrapped = false;
+        p.tag = next_tag_base(h->tag_end, h->desc.n_layers, &wrapped);
+        if (wrapped && mk_launch_zero(h->ll, (int64_t)h->rec.off[7] * 8, stream)) return MK_ERR_HIP;
+    }
     int rc = mk_launch_decode(&p, h->desc.dtype == MK_BF16 ? 1 : 0, h->cooperative, stream);
     return rc ? MK_ERR_HIP : MK_OK;
+}
+
+// One call's launches, ordered after the handle's previous call.
+static mk_status launch_one(mk_handle *h, const mk_kv_cache *kv, int32_t token, const int32_t *token_dev,
+                            int32_t pos, int want_logits, float *logits, int32_t *token_out, void *stream) {
+    if (h->layers_loaded < h->desc.n_layers || !h->head_loaded) return MK_ERR_STATE;
+    mk_status s = order_before(h, stream);
+    if (s == MK_OK) s = launch(h, kv, token, token_dev, pos, want_logits, logits, token_out, stream);
+    if (s == MK_OK) s = order_after(h, stream);
+    return s;
 }
 
 extern "C" mk_status mk_decode_step(mk_handle *h, int32_t token_id, int32_t pos, const mk_kv_cache *kv,
@@ -431,7 +519,7 @@ extern "C" mk_status mk_decode_step(mk_handle *h, int32_t token_id, int32_t pos,
     mk_status s = check_kv(h, kv);
     if (s != MK_OK) return s;
     if (token_id < 0 || token_id >= h->desc.vocab || pos < 0 || pos >= h->desc.max_seq) return MK_ERR_RANGE;
-    return launch(h, kv, token_id, nullptr, pos, 1, logits_out, nullptr, stream);
+    return launch_one(h, kv, token_id, nullptr, pos, 1, logits_out, nullptr, stream);
 }
 
 extern "C" mk_status mk_decode_step_device_token(mk_handle *h, const int32_t *token_in, int32_t pos,
@@ -442,7 +530,7 @@ extern "C" mk_status mk_decode_step_device_token(mk_handle *h, const int32_t *to
     mk_status s = check_kv(h, kv);
     if (s != MK_OK) return s;
     if (pos < 0 || pos >= h->desc.max_seq) return MK_ERR_RANGE;
-    return launch(h, kv, 0, token_in, pos, 1, logits_out, token_out, stream);
+    return launch_one(h, kv, 0, token_in, pos, 1, logits_out, token_out, stream);
 }
 
 extern "C" mk_status mk_prefill_kv(mk_handle *h, const int32_t *tokens, int32_t n, int32_t start_pos,
@@ -455,16 +543,19 @@ extern "C" mk_status mk_prefill_kv(mk_handle *h, const int32_t *tokens, int32_t 
     if (n > 0 && !tokens) return MK_ERR_NULL;
     for (int i = 0; i < n; ++i)
         if (tokens[i] < 0 || tokens[i] >= h->desc.vocab) return MK_ERR_RANGE;
-    for (int i = 0; i < n; ++i) {
+    if (n == 0) return MK_OK;
+    if (h->layers_loaded < h->desc.n_layers || !h->head_loaded) return MK_ERR_STATE;
+    s = order_before(h, stream);
+    for (int i = 0; i < n && s == MK_OK; ++i)
         s = launch(h, kv, tokens[i], nullptr, start_pos + i, 0, nullptr, nullptr, stream);
-        if (s != MK_OK) return s;
-    }
-    return MK_OK;
+    if (s == MK_OK) s = order_after(h, stream);
+    return s;
 }
 
 extern "C" mk_status mk_get_device_error(mk_handle *h) {
     if (!h) return MK_ERR_NULL;
-    HIP_TRY(hipStreamSynchronize(h->last_stream));
+    // the handle's last call, on whatever stream it was enqueued
+    if (h->done_recorded) HIP_TRY(hipEventSynchronize(h->done));
     uint32_t err = 0;
     HIP_TRY(hipMemcpy(&err, h->base.err, sizeof err, hipMemcpyDeviceToHost));
     if (err) {
@@ -477,7 +568,7 @@ extern "C" mk_status mk_get_device_error(mk_handle *h) {
 extern "C" mk_status mk_read_trace(mk_handle *h, uint64_t *host_out, int64_t capacity) {
     if (!h || !host_out) return MK_ERR_NULL;
     if (!h->trace || capacity < h->trace_len) return MK_ERR_RANGE;
-    HIP_TRY(hipStreamSynchronize(h->last_stream));
+    if (h->done_recorded) HIP_TRY(hipEventSynchronize(h->done));
     HIP_TRY(hipMemcpy(host_out, h->trace, h->trace_len * sizeof(uint64_t), hipMemcpyDeviceToHost));
     return MK_OK;
 }
@@ -493,5 +584,6 @@ extern "C" mk_status mk_get_info(const mk_handle *h, mk_info *info) {
     info->cu_count = h->cu_count;
     info->packed_bytes = h->packed_bytes;
     info->weight_bytes = h->weight_bytes;
+    info->record_bytes = (int64_t)h->rec.off[7] * (int64_t)sizeof(uint64_t);
     return MK_OK;
 }

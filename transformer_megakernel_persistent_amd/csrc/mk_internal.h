@@ -110,17 +110,19 @@ struct MkParams {
     // KV cache (caller-owned)
     void *kc, *vc;
     // Cross-workgroup values within a launch.  Every record is 64 bits: the
-    // float's bits in the low word, the launch tag in the high word.  Each
-    // dependency point of each layer has its own array, written exactly once
-    // per launch, so a reader polls until the tags equal this launch's tag.
-    uint64_t *ll_xq;       // [L+1][H]   x entering layer l >= 1, and the LM head (l = L)
-    uint64_t *ll_xg;       // [L][H]     x after the O projection
-    uint64_t *ll_qkv;      // [L][nkv][GQ+2][d] per KV group: rotated queries, then K and V of
+    // float's bits in the low word, the tag in the high word.  Each
+    // dependency point has its own array with two buffers, [2] below, used by
+    // layers of even and odd index (l & 1); a record of layer index l carries
+    // the tag `tag + l`, so a reader polls until the tags equal the one of
+    // its layer in this launch.
+    uint64_t *ll_xq;       // [2][H]     x entering layer l >= 1, and the LM head (l = L)
+    uint64_t *ll_xg;       // [2][H]     x after the O projection
+    uint64_t *ll_qkv;      // [2][nkv][GQ+2][d] per KV group: rotated queries, then K and V of
                            // this step's position (bf16-rounded), next to each other
-    uint64_t *ll_part;     // [L][nkv*splits][GQ][d+2] attention partials: o (unnormalised), m, l
-    uint64_t *ll_o;        // [L][nh*d]  attention output
-    uint64_t *ll_dpart;    // [L][grid][H] each workgroup's partial down projection
-    uint64_t *ll_amax;     // [grid][2]  per-workgroup (max logit, its index)
+    uint64_t *ll_part;     // [2][nkv*splits][GQ][d+2] attention partials: o (unnormalised), m, l
+    uint64_t *ll_o;        // [2][nh*d]  attention output
+    uint64_t *ll_dpart;    // [2][grid][H] each workgroup's partial down projection
+    uint64_t *ll_amax;     // [grid][2]  per-workgroup (max logit, its index), tag + L
     uint32_t *err;         // device error word
     // this call
     int32_t token;
@@ -129,7 +131,7 @@ struct MkParams {
     int32_t want_logits;
     float *logits;
     int32_t *token_out;
-    uint32_t tag;          // this launch's tag (never 0)
+    uint32_t tag;          // this launch's tag base: a record of layer index l carries tag + l (never 0)
     int64_t timeout_ticks; // wall-clock ticks (100 MHz) before a grid wait gives up
     int64_t err_check_ticks;  // wall-clock ticks a wait lasts before it also watches the device error word
     uint64_t *trace;       // optional [grid][5L+2][4] stage timeline, or null
@@ -149,6 +151,7 @@ int mk_launch_prelayout_stage(unsigned char *dst, const MkStage *st, int grid, i
                               void *stream);
 int mk_kernel_lds_bytes(int ring_slots, int vec_floats, int out_rows, int dtype, int d, int gq);
 int mk_launch_to_f32(float *dst, const void *src, int64_t n, int dtype, void *stream);
+int mk_launch_zero(void *dst, int64_t bytes, void *stream);
 #ifdef __cplusplus
 }
 #endif

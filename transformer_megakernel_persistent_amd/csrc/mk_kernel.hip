@@ -6,9 +6,14 @@
 // 4.1).  Each workgroup is resident on one CU for the whole step and has two
 // roles:
 //
-//   loader waves (2)    copy the workgroup's weight slots -- and, for the
+//   loader waves (4)    copy the workgroup's weight slots -- and, for the
 //                       attention stage, its KV-cache blocks -- from HBM into
-//                       an LDS ring with gfx950 direct-to-LDS 16-byte loads.
+//                       an LDS ring with gfx950 direct-to-LDS 16-byte loads,
+//                       each wave a quarter (four 1 KiB chunks) of every
+//                       16 KiB slot.  A workgroup's weight slots are striped
+//                       with the other workgroups': slot n of workgroup w
+//                       lies at w * 16 KiB + n * slot_stride of its stage's
+//                       layer block, slot_stride = grid * 16 KiB.
 //                       Weights and old cache positions do not depend on
 //                       activations, so the loaders run up to ring_slots-1
 //                       slots ahead ACROSS stage boundaries: weight streaming
@@ -28,10 +33,11 @@
 // next stage's input).
 //
 // Cross-workgroup values travel as tagged records: each value is stored with
-// one 64-bit device-scope store together with the launch's tag, and readers
-// poll the records they need until every tag matches.  Every dependency
-// point of every layer has its own record array, written once per launch,
-// so the data carry their own validity: no flags, counters, store-completion
+// one 64-bit device-scope store together with a tag naming the launch and
+// the layer (mixed with the value's bits, see tag_word), and readers poll
+// the records they need until every tag matches.  Every dependency point has
+// its own record array with two buffers (layers of even and odd index), so
+// the data carry their own validity: no flags, counters, store-completion
 // waits or separate flag round trips.  The attention splits write tagged
 // partials; each workgroup then merges a slice of the attention output
 // straight from them (log-sum-exp), with no atomic counter.
@@ -266,9 +272,18 @@ __device__ __forceinline__ void piece_in(const LDS float *hp, float (&h)[16 / (D
     }
 }
 
+// The high word of a tagged record: the tag XOR the value's bits.  A reader
+// accepts a record when its high word equals the tag it awaits XOR the low
+// word it read.  So it has read the awaited value even if its 16-byte load
+// combined the halves of two different stores: a stale low word passes only
+// if it equals the fresh value, a stale high word only next to the fresh low
+// word, and a stale record never (its tag differs).  No assumption on the
+// atomicity of a 16-byte load is needed, and the check is one XOR.
+__device__ __forceinline__ uint32_t tag_word(uint32_t tag, uint32_t bits) { return tag ^ bits; }
+
 // Poll N 16-byte pieces (two tagged records each) at byte offsets off(u)
-// of rs, for the lanes' bits set in mask, until both tags of every piece
-// equal tag; pieces already valid are not read again.  on_fail() is called
+// of rs, for the lanes' bits set in mask, until both records of every piece
+// carry tag; pieces already valid are not read again.  on_fail() is called
 // after each incomplete round and ends the wait by returning false.
 template <int N, class O, class F>
 __device__ __forceinline__ bool poll16(__amdgpu_buffer_rsrc_t rs, O &&off, uint32_t mask, u4v (&v)[N], uint32_t tag,
@@ -280,16 +295,19 @@ __device__ __forceinline__ bool poll16(__amdgpu_buffer_rsrc_t rs, O &&off, uint3
             if (pend & (1u << u)) v[u] = ld16c(rs, off(u));
 #pragma unroll
         for (int u = 0; u < N; ++u)
-            if ((pend & (1u << u)) && v[u].y == tag && v[u].w == tag) pend &= ~(1u << u);
+            if ((pend & (1u << u)) && v[u].y == tag_word(tag, v[u].x) && v[u].w == tag_word(tag, v[u].z))
+                pend &= ~(1u << u);
         if (!__any(pend != 0u)) return true;
         if (!on_fail()) return false;
     }
 }
 
-// Elements of a 16-byte piece in global memory (plain load).
+// Elements of the 16-byte piece at byte offset off of a buffer (plain load;
+// the wave-uniform base sits in the buffer resource, so the lane's part of
+// the address is one 32-bit register).
 template <int DT>
-__device__ __forceinline__ void piece_load_glb(const unsigned char *p, float (&v)[16 / (DT ? 2 : 4)]) {
-    const u4v w = *(const u4v *)p;
+__device__ __forceinline__ void piece_load_buf(__amdgpu_buffer_rsrc_t r, uint32_t off, float (&v)[16 / (DT ? 2 : 4)]) {
+    const u4v w = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
     if constexpr (DT == 1) {
         v[0] = bf_lo(w.x); v[1] = bf_hi(w.x); v[2] = bf_lo(w.y); v[3] = bf_hi(w.y);
         v[4] = bf_lo(w.z); v[5] = bf_hi(w.z); v[6] = bf_lo(w.w); v[7] = bf_hi(w.w);
@@ -337,12 +355,13 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
     const int w = blockIdx.x, G = p.grid, NS = p.ring_slots, L = p.L;
     constexpr int d = DH;
 
-    // LDS layout: ring | vec | out | xown | ss | control
+    // LDS layout: ring | vec | out | xown | rope | ss | control
     LDS unsigned char *ring = smem;
     LDS float *vec = (LDS float *)(smem + NS * MK_SLOT_BYTES);
     LDS float *outv = vec + p.lds_vec_floats;
     LDS float *xown = outv + p.lds_out_rows;
-    LDS float *ssp = xown + 64;
+    LDS float *ropel = xown + 64;  // [64][4] rotary (cos, sin) pairs of the first 64 QKV units
+    LDS float *ssp = ropel + 256;
     volatile LDS int *ctl = (volatile LDS int *)(ssp + MK_NUM_CONSUMERS);  // [1] abort step, [8] consumer meetings
 
     Geo g;
@@ -622,12 +641,21 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
 
     // ---- tagged records ----------------------------------------------------
     // A producer stores {value, tag} as one 64-bit device-scope store; a
-    // reader polls the records it needs until every tag is this launch's.
+    // reader polls the records it needs until every tag is the expected one.
     // No flag, no store-completion wait, no second load: the data carry
-    // their own validity.
-    const uint32_t tag = p.tag;
-    auto stll = [&](uint64_t *dst, float v) {
-        __hip_atomic_store(dst, ((uint64_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
+    // their own validity.  The tag names the launch and the layer: a record
+    // of layer index l (the index of its array: x entering layer l, layer
+    // l's queries, partials, ...; L for the argmax records) carries
+    // p.tag + l, and the host advances p.tag by L + 1 per launch.  Each
+    // per-layer array has two buffers, for even and odd l: a producer of
+    // layer l + 2 can only run once every workgroup has finished reading
+    // layer l's records (each dependency chain between them passes through
+    // an all-to-all gather of layer l + 1), and the slot it overwrites holds
+    // an older tag, never the awaited one.
+    auto tag_of = [&](int l) -> uint32_t { return p.tag + (uint32_t)l; };
+    auto stll = [&](uint64_t *dst, float v, uint32_t tg) {
+        const uint32_t bits = __float_as_uint(v);
+        __hip_atomic_store(dst, ((uint64_t)tag_word(tg, bits) << 32) | bits, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     };
     int64_t poll_start = 0;
@@ -670,7 +698,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
     // (two records), so the workgroup reads each element once; ssp[c] gets
     // this consumer's share of the sum of squares, summed in a fixed order.
     auto gather_fn = [&](LDS float *dst, int npc, __amdgpu_buffer_rsrc_t rs, auto &&off, const float *gain,
-                         int n, int pad) -> bool {
+                         int n, int pad, uint32_t tg) -> bool {
         float ss = 0.f;
         poll_start = wall_clock64();
         bool good = true;
@@ -686,7 +714,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
             for (int u = 0; u < 8; ++u)
                 gg[u] = (gain && (mask & (1u << u))) ? *(const f2v *)(gain + 2 * (base + u * 256)) : f2v{1.f, 1.f};
             u4v v[8];
-            if (!poll16<8>(rs, [&](int u) { return off(base + u * 256); }, mask, v, tag, poll_ok)) {
+            if (!poll16<8>(rs, [&](int u) { return off(base + u * 256); }, mask, v, tg, poll_ok)) {
                 good = false;
                 break;
             }
@@ -707,12 +735,12 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
         if (!good) return false;
         return csync();
     };
-    auto gather_to = [&](LDS float *dst, const uint64_t *src, int n, const float *gain, int pad) -> bool {
+    auto gather_to = [&](LDS float *dst, const uint64_t *src, int n, const float *gain, int pad, uint32_t tg) -> bool {
         return gather_fn(dst, n >> 1, rsrc(src, (uint32_t)n * 8u), [](int pc) { return (uint32_t)pc * 16u; }, gain, n,
-                         pad);
+                         pad, tg);
     };
-    auto gather = [&](const uint64_t *src, int n, const float *gain, int pad) -> bool {
-        return gather_to(vec, src, n, gain, pad);
+    auto gather = [&](const uint64_t *src, int n, const float *gain, int pad, uint32_t tg) -> bool {
+        return gather_to(vec, src, n, gain, pad, tg);
     };
 
     // ---- optional stage timeline (consumer 0, lane 0) ----
@@ -940,10 +968,17 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
     // kp piece columns of its row group gl; the finished partial sum is
     // stored as a tagged record of this workgroup's partial vector.
     auto down_steps = [&](int l) {
-        uint64_t *dst = p.ll_dpart + ((size_t)l * G + w) * p.H;
+        uint64_t *dst = p.ll_dpart + ((size_t)(l & 1) * G + w) * p.H;
+        const uint32_t tg = tag_of(l);
         const int kp = g.dn.kp, ng = (p.H + 63) >> 6;
         if (kp == 0) {  // no SwiGLU outputs here: the partial is zero
-            for (int r = ct; r < p.H; r += 256) stll(dst + r, 0.f);
+            // buffer stores (scalar base, 32-bit lane offset): the same
+            // device-scope 64-bit stores as stll, one register cheaper
+            const __amdgpu_buffer_rsrc_t rd = rsrc(dst, (uint32_t)p.H * 8u);
+            const uint64_t zero_rec = (uint64_t)tag_word(tg, 0u) << 32;
+            const u4v z = u4v{0u, (uint32_t)(zero_rec >> 32), 0u, (uint32_t)(zero_rec >> 32)};
+            for (int r = 2 * ct; r < p.H; r += 512)  // H is even: two records per 16-byte store
+                __builtin_amdgcn_raw_buffer_store_b128(z, rd, (uint32_t)r * 8u, 0, MK_SC1);
             return;
         }
         if ((kp & 3) == 0) {
@@ -977,7 +1012,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
                     q += 4;
                     if (q == kp) {
                         const int row = grp * 64 + lane;
-                        if (row < p.H) stll(dst + row, acc);
+                        if (row < p.H) stll(dst + row, acc, tg);
                         acc = 0.f;
                         q = 0;
                         ++gl;
@@ -1001,7 +1036,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
                     acc += piece_dot<DT>(bp + qq * MK_CHUNK_BYTES, vec + q * EPL);
                     if (++q == kp) {
                         const int row = grp * 64 + lane;
-                        if (row < p.H) stll(dst + row, acc);
+                        if (row < p.H) stll(dst + row, acc, tg);
                         acc = 0.f;
                         q = 0;
                         ++gl;
@@ -1021,13 +1056,13 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
         const int nr = max(0, min(g.units[ST_O] * 4, p.H - r0));
         const int hp = nr >> 1;  // 16-byte pieces per producer
         const int H = p.H;
-        const __amdgpu_buffer_rsrc_t rs = rsrc(p.ll_dpart + (size_t)l * G * H, (uint32_t)((size_t)G * H * 8u));
+        const __amdgpu_buffer_rsrc_t rs = rsrc(p.ll_dpart + (size_t)(l & 1) * G * H, (uint32_t)((size_t)G * H * 8u));
         // vec[wq * nr + i] = partial of producer wq for row r0 + i
         auto off = [&](int pc) {
             const int wq = pc / hp, i = pc - wq * hp;
             return (uint32_t)(((size_t)wq * H + r0 + 2 * i) * 8u);
         };
-        if (!gather_fn(vec, G * hp, rs, off, nullptr, G * nr, G * nr)) return false;
+        if (!gather_fn(vec, G * hp, rs, off, nullptr, G * nr, G * nr, tag_of(l))) return false;
         for (int i = c; i < nr; i += MK_NUM_CONSUMERS) {
             float sum = 0.f;
             for (int wq = lane; wq < G; wq += 64) sum += vec[wq * nr + i];
@@ -1035,7 +1070,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
             if (lane == 0) {
                 const float xn = xown[i] + sum;
                 xown[i] = xn;
-                stll(xdst + r0 + i, xn);
+                stll(xdst + r0 + i, xn, tag_of(l + 1));
             }
         }
         return csync();
@@ -1053,7 +1088,11 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
     constexpr int HPC = GQ / HG;                // heads per consumer
     constexpr int CPH = MK_NUM_CONSUMERS / HG;  // consumers per head
     constexpr int CPS = 8 / CPH;                // K (and V) chunks per slot per consumer
-    constexpr int NQB = (HPC == 1 && CPS >= 8) ? 8 : (CPS < 4 ? CPS : 4);  // chunks folded together
+    // Chunks folded per softmax update: all eight of a slot when a consumer
+    // holds one head of 64 dims; four otherwise (with 128-dim heads the
+    // eight-chunk fold needs more than the 256 VGPRs a wave has at two waves
+    // per SIMD, and the compiler spills to scratch).
+    constexpr int NQB = (HPC == 1 && CPS >= 8 && LPP == 8) ? 8 : (CPS < 4 ? CPS : 4);
     const int hc = c % HG, cs = c / HG;
     const float scale = 1.0f / sqrtf((float)d);
     const int e0 = (lane % LPP) * EPL;
@@ -1119,7 +1158,8 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
     constexpr int PREC = DH + 2;  // partial record: o[DH], m, l
     const int S_eff = S * CPH;    // effective splits per KV head
     auto attn_finish = [&](AttnState &A, int l) {
-        uint64_t *part = p.ll_part + (((size_t)l * p.nkv + kvj) * S_eff + kvs * CPH + cs) * GQ * PREC;
+        uint64_t *part = p.ll_part + (((size_t)(l & 1) * p.nkv + kvj) * S_eff + kvs * CPH + cs) * GQ * PREC;
+        const uint32_t tg = tag_of(l);
 #pragma unroll
         for (int k = 0; k < HPC; ++k) {
             const int h = hc + HG * k;
@@ -1127,27 +1167,30 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
 #pragma unroll
             for (int e = 0; e < EPL; ++e) {
                 const float ov = xgroup_sum<LPP>(A.ao[k][e]);
-                if (lane < LPP) stll(part + h * PREC + e0 + e, ov);
+                if (lane < LPP) stll(part + h * PREC + e0 + e, ov, tg);
             }
             if (lane == 0) {
-                stll(part + h * PREC + d, A.am[k]);
-                stll(part + h * PREC + d + 1, lsum);
+                stll(part + h * PREC + d, A.am[k], tg);
+                stll(part + h * PREC + d + 1, lsum, tg);
             }
         }
     };
 
     // ---- epilogues (consumer 0) ----
     // The rotary cos/sin pairs of this workgroup's query/key units depend only
-    // on the position, the same in every layer: consumer 0 keeps the first 64
-    // units' pairs in registers for the whole step.
+    // on the position, the same in every layer: consumer 0 parks the first 64
+    // units' pairs in LDS once per step (registers are the scarcer resource;
+    // consumer 0 alone writes and reads them, so no barrier is needed).
     const float *rope_row = p.rope + (size_t)P * d;  // [d/2][2]
     auto rope_of_unit = [&](int u) -> f4v {
         const int r = ((g.unit0[ST_QKV] + u) * 4) % d;  // query and key rows share the angles by head dim
         return *(const f4v *)(rope_row + r);
     };
-    const f4v rope_pre = (c == 0 && lane < g.units[ST_QKV]) ? rope_of_unit(lane) : f4v{0.f, 0.f, 0.f, 0.f};
+    if (c == 0 && lane < g.units[ST_QKV]) *(LDS f4v *)(ropel + 4 * lane) = rope_of_unit(lane);
     auto epi_qkv = [&](int l, float inv) {
         const int nqd = p.nh * d, nk = p.nkv * d;
+        const uint32_t tg = tag_of(l);
+        uint64_t *const qkv_l = p.ll_qkv + (size_t)(l & 1) * p.nkv * (GQ + 2) * d;
         for (int u = lane; u < g.units[ST_QKV]; u += 64) {
             const int gr0 = (g.unit0[ST_QKV] + u) * 4;
             const float y0 = outv[u * 4] * inv, y1 = outv[u * 4 + 1] * inv;
@@ -1156,71 +1199,71 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
                 const bool isq = gr0 < nqd;
                 const int r = isq ? gr0 : gr0 - nqd;
                 const int head = r / d, m0 = (r % d) / 2;
-                const f4v rc = u < 64 ? rope_pre : rope_of_unit(u);
+                const f4v rc = u < 64 ? *(const LDS f4v *)(ropel + 4 * u) : rope_of_unit(u);
                 const float c0 = rc.x, s0 = rc.y, c1 = rc.z, s1 = rc.w;
                 const float a0 = y0 * c0 - y1 * s0, b0 = y0 * s0 + y1 * c0;
                 const float a1 = y2 * c1 - y3 * s1, b1 = y2 * s1 + y3 * c1;
                 if (isq) {
-                    uint64_t *qd = p.ll_qkv + ((size_t)l * p.nkv + head / GQ) * (GQ + 2) * d + (size_t)(head % GQ) * d;
-                    stll(qd + m0, a0);
-                    stll(qd + m0 + 1, a1);
-                    stll(qd + m0 + d / 2, b0);
-                    stll(qd + m0 + 1 + d / 2, b1);
+                    uint64_t *qd = qkv_l + (size_t)(head / GQ) * (GQ + 2) * d + (size_t)(head % GQ) * d;
+                    stll(qd + m0, a0, tg);
+                    stll(qd + m0 + 1, a1, tg);
+                    stll(qd + m0 + d / 2, b0, tg);
+                    stll(qd + m0 + 1 + d / 2, b1, tg);
                 } else {
                     unsigned char *row = (unsigned char *)p.kc + ((size_t)l * p.nkv + head) * head_bytes + (size_t)P * d * EB;
-                    uint64_t *kn = p.ll_qkv + ((size_t)l * p.nkv + head) * (GQ + 2) * d + (size_t)GQ * d;
+                    uint64_t *kn = qkv_l + (size_t)head * (GQ + 2) * d + (size_t)GQ * d;
                     if constexpr (DT == 1) {
                         const uint32_t ba0 = f2bf(a0), ba1 = f2bf(a1), bb0 = f2bf(b0), bb1 = f2bf(b1);
                         stcu((uint32_t *)(row + m0 * 2), ba0 | (ba1 << 16));
                         stcu((uint32_t *)(row + (m0 + d / 2) * 2), bb0 | (bb1 << 16));
-                        stll(kn + m0, __uint_as_float(ba0 << 16));
-                        stll(kn + m0 + 1, __uint_as_float(ba1 << 16));
-                        stll(kn + m0 + d / 2, __uint_as_float(bb0 << 16));
-                        stll(kn + m0 + 1 + d / 2, __uint_as_float(bb1 << 16));
+                        stll(kn + m0, __uint_as_float(ba0 << 16), tg);
+                        stll(kn + m0 + 1, __uint_as_float(ba1 << 16), tg);
+                        stll(kn + m0 + d / 2, __uint_as_float(bb0 << 16), tg);
+                        stll(kn + m0 + 1 + d / 2, __uint_as_float(bb1 << 16), tg);
                     } else {
                         stc((float *)row + m0, a0);
                         stc((float *)row + m0 + 1, a1);
                         stc((float *)row + m0 + d / 2, b0);
                         stc((float *)row + m0 + 1 + d / 2, b1);
-                        stll(kn + m0, a0);
-                        stll(kn + m0 + 1, a1);
-                        stll(kn + m0 + d / 2, b0);
-                        stll(kn + m0 + 1 + d / 2, b1);
+                        stll(kn + m0, a0, tg);
+                        stll(kn + m0 + 1, a1, tg);
+                        stll(kn + m0 + d / 2, b0, tg);
+                        stll(kn + m0 + 1 + d / 2, b1, tg);
                     }
                 }
             } else if (gr0 < nqd + 2 * nk) {
                 const int r = gr0 - nqd - nk;
                 const int head = r / d, e = r % d;
                 unsigned char *row = (unsigned char *)p.vc + ((size_t)l * p.nkv + head) * head_bytes + (size_t)P * d * EB;
-                uint64_t *vn = p.ll_qkv + ((size_t)l * p.nkv + head) * (GQ + 2) * d + (size_t)(GQ + 1) * d;
+                uint64_t *vn = qkv_l + (size_t)head * (GQ + 2) * d + (size_t)(GQ + 1) * d;
                 if constexpr (DT == 1) {
                     const uint32_t c0 = f2bf(y0), c1 = f2bf(y1), c2 = f2bf(y2), c3 = f2bf(y3);
                     stcu((uint32_t *)(row + e * 2), c0 | (c1 << 16));
                     stcu((uint32_t *)(row + e * 2 + 4), c2 | (c3 << 16));
-                    stll(vn + e, __uint_as_float(c0 << 16));
-                    stll(vn + e + 1, __uint_as_float(c1 << 16));
-                    stll(vn + e + 2, __uint_as_float(c2 << 16));
-                    stll(vn + e + 3, __uint_as_float(c3 << 16));
+                    stll(vn + e, __uint_as_float(c0 << 16), tg);
+                    stll(vn + e + 1, __uint_as_float(c1 << 16), tg);
+                    stll(vn + e + 2, __uint_as_float(c2 << 16), tg);
+                    stll(vn + e + 3, __uint_as_float(c3 << 16), tg);
                 } else {
                     stc((float *)row + e, y0);
                     stc((float *)row + e + 1, y1);
                     stc((float *)row + e + 2, y2);
                     stc((float *)row + e + 3, y3);
-                    stll(vn + e, y0);
-                    stll(vn + e + 1, y1);
-                    stll(vn + e + 2, y2);
-                    stll(vn + e + 3, y3);
+                    stll(vn + e, y0, tg);
+                    stll(vn + e + 1, y1, tg);
+                    stll(vn + e + 2, y2, tg);
+                    stll(vn + e + 3, y3, tg);
                 }
             }
         }
     };
-    auto epi_residual = [&](int st, uint64_t *xdst) {  // O or DOWN: x += out for the workgroup's rows
+    auto epi_residual = [&](int st, uint64_t *xdst, uint32_t tg) {  // O or DOWN: x += out for the workgroup's rows
         for (int i = lane; i < g.units[st] * 4; i += 64) {
             const int r = g.unit0[st] * 4 + i;
             if (r < p.H) {
                 const float xn = xown[i] + outv[i];
                 xown[i] = xn;
-                stll(xdst + r, xn);
+                stll(xdst + r, xn, tg);
             }
         }
     };
@@ -1243,7 +1286,8 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
     auto combine_slice = [&](int l) -> bool {
         const int N = p.nh * d;
         const int e_0 = (int)((int64_t)w * N / G), e_1 = (int)((int64_t)(w + 1) * N / G);
-        const __amdgpu_buffer_rsrc_t rp = rsrc(p.ll_part + (size_t)l * p.nkv * S_eff * GQ * PREC,
+        const uint32_t tg = tag_of(l);
+        const __amdgpu_buffer_rsrc_t rp = rsrc(p.ll_part + (size_t)(l & 1) * p.nkv * S_eff * GQ * PREC,
                                                (uint32_t)((size_t)p.nkv * S_eff * GQ * PREC * 8));
         const bool ln = lane < S_eff;
         poll_start = wall_clock64();
@@ -1263,7 +1307,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
                 return (rec + ((i & 1) ? ((e % d) & ~1) : d)) * 8u;
             };
             u4v v[16];
-            if (!poll16<16>(rp, off, mask, v, tag, poll_ok)) return false;
+            if (!poll16<16>(rp, off, mask, v, tg, poll_ok)) return false;
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const int e = eb + u;
@@ -1279,7 +1323,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
                     }
                     const float ov = ln ? __uint_as_float((dim & 1) ? v[2 * u + 1].z : v[2 * u + 1].x) : 0.f;
                     const float os = wave_sum(wgt * ov);
-                    if (lane == 0) stll(p.ll_o + (size_t)l * N + e, os / Ls);
+                    if (lane == 0) stll(p.ll_o + (size_t)(l & 1) * N + e, os / Ls, tg);
                 }
             }
         }
@@ -1304,8 +1348,8 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
             if (ob > best || (ob == best && oi < besti)) { best = ob; besti = oi; }
         }
         if (lane == 0) {
-            stll(p.ll_amax + 2 * (size_t)w, best);
-            stll(p.ll_amax + 2 * (size_t)w + 1, __int_as_float(besti));
+            stll(p.ll_amax + 2 * (size_t)w, best, tag_of(L));
+            stll(p.ll_amax + 2 * (size_t)w + 1, __int_as_float(besti), tag_of(L));
         }
         if (w != 0) return;
         // Workgroup 0 reduces the G (max, index) records.  This is the last
@@ -1321,7 +1365,8 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
             for (int k = 0; k < 8; ++k)
                 if (lane + 64 * (k0 + k) < G) mask |= 1u << k;
             u4v v[8];
-            if (!poll16<8>(ra, [&](int k) { return (uint32_t)(lane + 64 * (k0 + k)) * 16u; }, mask, v, tag, poll_ok))
+            if (!poll16<8>(ra, [&](int k) { return (uint32_t)(lane + 64 * (k0 + k)) * 16u; }, mask, v, tag_of(L),
+                           poll_ok))
                 return;
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
@@ -1406,9 +1451,9 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
                     gemv_lds_steps(ST_QKV, l);
                 }
             } else {
-                ok = down_reduce(l - 1, p.ll_xq + (size_t)l * p.H);
+                ok = down_reduce(l - 1, p.ll_xq + (size_t)(l & 1) * p.H);
                 stamp(5 * l, 1);
-                ok = ok && gather(p.ll_xq + (size_t)l * p.H, p.H, gain, p.st[ST_QKV].rbp * EPC);
+                ok = ok && gather(p.ll_xq + (size_t)(l & 1) * p.H, p.H, gain, p.st[ST_QKV].rbp * EPC, tag_of(l));
                 stamp(5 * l, 2);
                 if (!ok) break;
                 inv_q = inv_lds(p.H);
@@ -1431,10 +1476,12 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
                 const bool tvalid = fold_extra && tg < ntail;
                 float kt[EPL], vt[EPL];
                 if (fold_extra && ntail > 0) {
-                    const size_t tp = (size_t)t0 + (size_t)nfull * BP + (tvalid ? tg : 0);
-                    const size_t roff = (((size_t)l * p.nkv + kvj) * p.max_seq + tp) * d * EB + (size_t)e0 * EB;
-                    piece_load_glb<DT>((const unsigned char *)p.kc + roff, kt);
-                    piece_load_glb<DT>((const unsigned char *)p.vc + roff, vt);
+                    // the tail's rows: at most PPC positions from t0 + nfull * BP
+                    const size_t rbase = (((size_t)l * p.nkv + kvj) * p.max_seq + (size_t)t0 + (size_t)nfull * BP) * d * EB;
+                    const uint32_t tbytes = (uint32_t)(PPC * d * EB);
+                    const uint32_t roff = (uint32_t)(((tvalid ? tg : 0) * d + e0) * EB);
+                    piece_load_buf<DT>(rsrc((const unsigned char *)p.kc + rbase, tbytes), roff, kt);
+                    piece_load_buf<DT>(rsrc((const unsigned char *)p.vc + rbase, tbytes), roff, vt);
                 }
                 // This group's rotated queries and, in the last split, the K/V
                 // row of position pos (bf16-rounded like the cache) into LDS in
@@ -1442,7 +1489,8 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
                 // here (the QKV input is no longer needed).
                 {
                     const int nrec = (is_last ? GQ + 2 : GQ) * d;  // the last split also takes K/V of pos
-                    ok = gather_to(vec, p.ll_qkv + ((size_t)l * p.nkv + kvj) * (GQ + 2) * d, nrec, nullptr, nrec);
+                    ok = gather_to(vec, p.ll_qkv + ((size_t)(l & 1) * p.nkv + kvj) * (GQ + 2) * d, nrec, nullptr, nrec,
+                                   tag_of(l));
                 }
                 AttnState A;
 #pragma unroll
@@ -1514,7 +1562,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
             stamp(5 * l + 2, 0);
             const bool mine = combine_slice(l);
             stamp(5 * l + 2, 1);
-            ok = mine && gather(p.ll_o + (size_t)l * nq, nq, nullptr, p.st[ST_O].rbp * EPC);
+            ok = mine && gather(p.ll_o + (size_t)(l & 1) * nq, nq, nullptr, p.st[ST_O].rbp * EPC, tag_of(l));
             stamp(5 * l + 2, 2);
             if (!ok) break;
             gemv_from_vec(ST_O, l, 5 * l + 2);
@@ -1525,9 +1573,10 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
         {
             barrier();
             stamp(5 * l + 3, 0);
-            if (c == 0) epi_residual(ST_O, p.ll_xg + (size_t)l * p.H);
+            if (c == 0) epi_residual(ST_O, p.ll_xg + (size_t)(l & 1) * p.H, tag_of(l));
             stamp(5 * l + 3, 1);
-            ok = gather(p.ll_xg + (size_t)l * p.H, p.H, p.g_ffn + (size_t)l * p.H, p.st[ST_GU].rbp * EPC);
+            ok = gather(p.ll_xg + (size_t)(l & 1) * p.H, p.H, p.g_ffn + (size_t)l * p.H, p.st[ST_GU].rbp * EPC,
+                        tag_of(l));
             stamp(5 * l + 3, 2);
             if (!ok) break;
             inv_g = inv_lds(p.H);
@@ -1551,9 +1600,9 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
         // ===== LM head; boundary: epilogue DOWN(L-1) + input x =====
         barrier();
         stamp(5 * L, 0);
-        ok = down_reduce(L - 1, p.ll_xq + (size_t)L * p.H);
+        ok = down_reduce(L - 1, p.ll_xq + (size_t)(L & 1) * p.H);
         stamp(5 * L, 1);
-        ok = ok && gather(p.ll_xq + (size_t)L * p.H, p.H, p.g_final, p.st[ST_LM].rbp * EPC);
+        ok = ok && gather(p.ll_xq + (size_t)(L & 1) * p.H, p.H, p.g_final, p.st[ST_LM].rbp * EPC, tag_of(L));
         stamp(5 * L, 2);
         if (ok) {
             const float inv_lm = inv_lds(p.H);
@@ -1601,7 +1650,7 @@ extern "C" int mk_kernel_lds_bytes(int ring_slots, int vec_floats, int out_rows,
     (void)dtype;
     (void)d;
     (void)gq;
-    const int floats = vec_floats + out_rows + 64 + MK_NUM_CONSUMERS + 16;
+    const int floats = vec_floats + out_rows + 64 + 256 + MK_NUM_CONSUMERS + 16;
     return ring_slots * MK_SLOT_BYTES + floats * 4;
 }
 

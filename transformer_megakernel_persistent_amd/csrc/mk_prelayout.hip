@@ -29,6 +29,19 @@
 
 namespace {
 
+// A 16-byte piece assembled byte by byte in registers (no private array):
+// byte_at(i) returns byte i of the piece, or a negative value for a zero.
+template <class F>
+__device__ __forceinline__ uint4 gather_piece(F &&byte_at) {
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int b = byte_at(i);
+        if (b >= 0) w[i >> 2] |= (uint32_t)b << (8 * (i & 3));
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // One 64-lane wave copies one 1 KiB chunk (16 bytes per lane).
 __global__ __launch_bounds__(256) void prelayout_kernel(unsigned char *dst_block, MkStage st, int grid, int kind,
                                                         int eb, const unsigned char *src0, const unsigned char *src1,
@@ -52,11 +65,11 @@ __global__ __launch_bounds__(256) void prelayout_kernel(unsigned char *dst_block
         if (dg.kp > 0 && row < st.rows) {
             const int fa = dg.f0 + q * epl;  // first column of this piece
             const unsigned char *srow = src0 + (int64_t)row * st.k * eb;
-            unsigned char tmp[16] = {0};
-            for (int e = 0; e < epl; ++e)
-                if (q * epl + e < dg.nf)
-                    for (int b = 0; b < eb; ++b) tmp[e * eb + b] = srow[(int64_t)(fa + e) * eb + b];
-            val = *(const uint4 *)tmp;
+            // byte i of the piece: element i / eb of the piece, byte i % eb of it
+            val = gather_piece([&](int i) -> int {
+                const int e = i / eb;
+                return q * epl + e < dg.nf ? (int)srow[(int64_t)(fa + e) * eb + i % eb] : -1;
+            });
         }
         *(uint4 *)(dst_block + st.wg_off[w] + (int64_t)(chunk / MK_CHUNKS_PER_SLOT) * st.slot_stride +
                    (chunk % MK_CHUNKS_PER_SLOT) * MK_CHUNK_BYTES + lane * 16) = val;
@@ -94,9 +107,9 @@ __global__ __launch_bounds__(256) void prelayout_kernel(unsigned char *dst_block
             if (off + 16 <= row_bytes) {
                 val = *(const uint4 *)(src + srow * row_bytes + off);
             } else if (off < row_bytes) {  // partial 16-byte piece at the row end
-                unsigned char tmp[16] = {0};
-                for (int b = 0; b < (int)(row_bytes - off); ++b) tmp[b] = src[srow * row_bytes + off + b];
-                val = *(const uint4 *)tmp;
+                const unsigned char *sp = src + srow * row_bytes + off;
+                const int nb = (int)(row_bytes - off);
+                val = gather_piece([&](int i) -> int { return i < nb ? (int)sp[i] : -1; });
             }
         }
     }
@@ -111,7 +124,24 @@ __global__ void to_f32_kernel(float *dst, const void *src, int64_t n, int dtype)
     }
 }
 
+__global__ void zero_kernel(uint4 *dst, int64_t n16) {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n16; i += (int64_t)gridDim.x * blockDim.x)
+        dst[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
 }  // namespace
+
+// Clears `bytes` (a multiple of 16) at dst with a fill kernel on `stream`
+// (a kernel rather than a memset so that the call can sit in a captured
+// graph).
+extern "C" int mk_launch_zero(void *dst, int64_t bytes, void *stream) {
+    const int64_t n16 = bytes / 16;
+    if (n16 <= 0) return 0;
+    int blocks = (int)((n16 + 255) / 256);
+    if (blocks > 2048) blocks = 2048;
+    hipLaunchKernelGGL(zero_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (uint4 *)dst, n16);
+    return (int)hipGetLastError();
+}
 
 extern "C" int mk_launch_prelayout_stage(unsigned char *dst, const MkStage *st, int grid, int kind, int dtype,
                                          const void *src0, const void *src1, const void *src2, int nh, int nkv,

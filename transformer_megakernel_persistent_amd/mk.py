@@ -19,8 +19,9 @@ MK_OK, MK_ERR_NULL, MK_ERR_SHAPE, MK_ERR_DTYPE, MK_ERR_RANGE = 0, 1, 2, 3, 4
 MK_ERR_NOMEM, MK_ERR_HIP, MK_ERR_DEVICE, MK_ERR_STATE, MK_ERR_TUNING = 5, 6, 7, 8, 9
 MK_F32, MK_BF16 = 0, 1
 
-EXPORTED = ("mk_create", "mk_create_deferred", "mk_load_weights", "mk_decode_step", "mk_decode_step_device_token", "mk_prefill_kv", "mk_get_device_error",
-            "mk_get_info", "mk_read_trace", "mk_status_str", "mk_destroy")
+EXPORTED = ("mk_create", "mk_create_deferred", "mk_load_weights", "mk_decode_step", "mk_decode_step_device_token",
+            "mk_prefill_kv", "mk_get_device_error", "mk_get_info",
+            "mk_read_trace", "mk_status_str", "mk_destroy")
 
 
 class ModelDesc(ctypes.Structure):
@@ -53,7 +54,8 @@ class Tuning(ctypes.Structure):
 class Info(ctypes.Structure):
     _fields_ = [("grid", ctypes.c_int32), ("ring_slots", ctypes.c_int32), ("attn_splits", ctypes.c_int32),
                 ("block_threads", ctypes.c_int32), ("lds_bytes", ctypes.c_int32), ("cu_count", ctypes.c_int32),
-                ("prefetch_slots", ctypes.c_int32), ("packed_bytes", ctypes.c_int64), ("weight_bytes", ctypes.c_int64)]
+                ("prefetch_slots", ctypes.c_int32), ("packed_bytes", ctypes.c_int64), ("weight_bytes", ctypes.c_int64),
+                ("record_bytes", ctypes.c_int64)]
 
 
 _lib = None

@@ -109,6 +109,16 @@ def summarise(name: str, tuning: dict, steps: int = 6) -> None:
         intv = np.median(np.diff(st_[:, :n, 0], axis=1), 0) * TICK_US
         print("  layer-1 data steps, arithmetic / barrier interval (us): " +
               " ".join(f"{a:.2f}/{b:.2f}" for a, b in zip(comp[:-1], intv)))
+    ld = mk.last_loader.astype(np.int64)
+    m = int((ld[0, :, 0] > 0).sum())
+    if m > 1:
+        # loader 0 at the barriers of layer 1: time spent waiting in the
+        # barrier (arrival to exit) and the interval between its exits.  A
+        # short wait means the loader arrives last (the loads pace the step).
+        wait = np.median(ld[:, :m, 1] - ld[:, :m, 0], 0) * TICK_US
+        gap = np.median(np.diff(ld[:, :m, 1], axis=1), 0) * TICK_US
+        print("  layer-1 loader barriers, wait / interval (us): " +
+              " ".join(f"{a:.2f}/{b:.2f}" for a, b in zip(wait[:-1], gap)))
     mk.close()
 
 
