@@ -138,6 +138,24 @@ def cpu_baseline(cfg, host_w, shape, budget_s: float):
             "value_1_thread": 1.0 / el1}
 
 
+PEAK_MFMA_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores, published
+
+
+def prefill_record(cfg, n, seconds, info):
+    """Prefill throughput and its roofline: the algorithmic flops of n
+    prompt positions (2 per weight of every layer matrix per token, plus the
+    causal attention's 4 * n_heads * head_dim per (token, earlier position)
+    pair per layer) over the wall time, against the bf16 matrix-core peak."""
+    H, F = cfg.hidden, cfg.ffn
+    per_layer = (cfg.q_dim + 2 * cfg.kv_dim) * H + H * cfg.q_dim + 3 * H * F
+    flops = 2.0 * cfg.n_layers * per_layer * n + 4.0 * cfg.n_layers * cfg.q_dim * n * (n + 1) / 2
+    tf = flops / seconds / 1e12
+    return {"positions": n, "seconds": seconds, "tokens_per_s": n / seconds,
+            "mode": f"batched, chunks of {info['prefill_chunk']}" if info["prefill_chunk"] else "decode launches",
+            "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": tf / PEAK_MFMA_BF16_TFLOPS, "traffic": None, "flops": flops}}
+
+
 def measure(name, args, dev, steps, warm, runs, cpu_budget, with_cpu):
     """One workload: load, prefill, `warm` untimed steps, then `runs` timed
     runs of `steps` chained device-token steps each.  Returns its record."""
@@ -240,7 +258,7 @@ def measure(name, args, dev, steps, warm, runs, cpu_budget, with_cpu):
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic},
         "cpu_baseline": cpu,
-        "prefill": {"positions": ctx, "seconds": prefill_s, "tokens_per_s": ctx / prefill_s},
+        "prefill": prefill_record(cfg, ctx, prefill_s, info),
         "info": info,
         "first_tokens": [int(x) for x in tokens[:8]],
         "dtype": "bf16" if cfg.dtype == "bf16" else "f32",

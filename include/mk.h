@@ -121,9 +121,17 @@ typedef struct {
      stage_drain: 1 = no cross-stage prefetch: a stage's first loads wait
                   for the grid dependency before it (the consumers' opening
                   barrier of the stage); 0 = loads run ahead across stage
-                  boundaries (default).  An ablation knob. */
+                  boundaries (default).  An ablation knob;
+     prefill_chunk: tokens per chunk of the batched prefill, 1..1024
+                  (default 256); -1 = prefill by one decode launch per
+                  position.  The batched prefill needs bf16 weights and a
+                  geometry whose down-stage workgroups own inputs starting at
+                  multiples of 8 (true of the Llama shapes at 256
+                  workgroups); otherwise mk_prefill_kv uses decode launches
+                  (mk_info.prefill_chunk reports which). */
 typedef struct {
     int32_t grid, ring_slots, attn_splits, timeout_ms, cooperative, trace, prefetch_depth, stage_drain;
+    int32_t prefill_chunk;
 } mk_tuning;
 
 typedef struct mk_handle mk_handle;
@@ -135,6 +143,7 @@ typedef struct {
     int64_t packed_bytes;    /* library-owned pre-laid-out weight bytes */
     int64_t weight_bytes;    /* algorithmic weight bytes read per step */
     int64_t record_bytes;    /* cross-workgroup record buffer of one launch */
+    int32_t prefill_chunk;   /* tokens per batched-prefill chunk; 0: prefill by decode launches */
 } mk_info;
 
 /* Create a handle: validates the shape, copies every weight into a
@@ -201,7 +210,15 @@ mk_status mk_decode_step_device_token(mk_handle *h, const int32_t *token_in, int
 /* Fill cache positions [start_pos, start_pos + n) from n host token ids: by
    definition under causal attention this is n decode steps at those
    positions with the LM head skipped.  Requires n >= 0 and
-   start_pos + n <= max_seq.
+   start_pos + n <= max_seq.  The caller's token array may be reused as soon
+   as the call returns.
+   Batched (mk_info.prefill_chunk > 0): chunks of up to prefill_chunk
+   positions; per layer the chunk's tokens go through matrix-core GEMMs
+   (bf16 weights, activations split into bf16 high and low parts, fp32
+   accumulation) that read the packed weights in place, and a causal
+   attention over positions [0, own].  The cache rows equal the decode
+   step's to within the bf16 rounding of the stored values.  Otherwise one
+   decode launch per position.
    The pages keep the prefill apart from the decode step and measure the two
    phases separately (cloud.baidu.com/article/9434380 section 八, question
    two); the cache it fills is the state handed between steps (same page,

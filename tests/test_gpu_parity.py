@@ -95,7 +95,7 @@ def create_deferred(mkp, shape, host, max_seq, tuning=None, order=None):
 
 
 def run_pair(env, cfg, seed, n_prompt, n_steps, gains="random", tuning=None, use_prefill=True, poison=True,
-             check_kv=True, deferred=False):
+             check_kv=True, deferred=False, expect_batched=None):
     """Prefill (or synthetic cache) then teacher-forced greedy steps on both
     sides; returns per-step max|dlogit| and the argmax agreement count."""
     torch, oracle, mkp = env
@@ -111,6 +111,8 @@ def run_pair(env, cfg, seed, n_prompt, n_steps, gains="random", tuning=None, use
         dev_w = mkp.upload_weights(host)
         mk = mkp.MegaKernel(shape, dev_w, max_seq, tuning=tuning)
         del dev_w
+    if expect_batched is not None:  # which prefill path the handle takes
+        assert (mk.info()["prefill_chunk"] > 0) == expect_batched, mk.info()
     kv = mkp.KVCache(shape, max_seq, fill=float("nan") if poison else 0.0)
     toks = synth.gen_tokens(seed, n_prompt + 1, cfg.vocab)
     if use_prefill:

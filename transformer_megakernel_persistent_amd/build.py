@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")  # the public C ABI header
 LIB = os.path.join(HERE, "libmk.so")
 RESOURCES = os.path.join(HERE, "libmk.resources.json")
-SOURCES = ["mk_api.hip", "mk_kernel.hip", "mk_prelayout.hip"]
+SOURCES = ["mk_api.hip", "mk_kernel.hip", "mk_prelayout.hip", "mk_prefill.hip"]
 HEADERS = [os.path.join(CSRC, "mk_internal.h"), os.path.join(INCLUDE, "mk.h")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -51,6 +51,8 @@ struct mk_handle {
     bool done_recorded = false;
     hipStream_t last_stream = nullptr;
     int lds_bytes = 0;
+    MkPrefillBufs pf = {};           // batched prefill (pf.t_max == 0: one decode launch per position)
+    int32_t *pf_tokens = nullptr;    // [max_seq] device copy of prompt token ids
     std::vector<char> layer_loaded;  // [n_layers]: weights of the layer pre-laid out
     int layers_loaded = 0;
     bool head_loaded = false;        // embedding, final norm and LM head in place
@@ -122,7 +124,7 @@ mk_status validate_tuning(const mk_tuning *t) {
     if (!t) return MK_OK;
     if (t->grid < 0 || t->grid > MK_MAX_GRID || t->ring_slots < 0 || t->attn_splits < 0 || t->attn_splits > MK_MAX_SPLITS || t->timeout_ms < 0 ||
         t->cooperative < 0 || t->cooperative > 2 || t->trace < 0 || t->trace > 1 || t->prefetch_depth < 0 ||
-        t->stage_drain < 0 || t->stage_drain > 1)
+        t->stage_drain < 0 || t->stage_drain > 1 || t->prefill_chunk < -1 || t->prefill_chunk > 1024)
         return MK_ERR_TUNING;
     if (t->ring_slots != 0 && (t->ring_slots < 3 || t->ring_slots > MK_MAX_RING)) return MK_ERR_TUNING;
     return MK_OK;
@@ -156,6 +158,12 @@ extern "C" void mk_destroy(mk_handle *h) {
     hipFree(h->ll);
     hipFree(h->err);
     hipFree(h->trace);
+    hipFree(h->pf.X);
+    hipFree(h->pf.Ah);
+    hipFree(h->pf.Al);
+    hipFree(h->pf.Y);
+    hipFree(h->pf.Q);
+    hipFree(h->pf_tokens);
     if (h->done) hipEventDestroy(h->done);
     delete h;
 }
@@ -182,7 +190,8 @@ static mk_status create_impl(const mk_model_desc *desc, const mk_tuning *tun, mk
     if (wclk_khz <= 0) wclk_khz = 100000;
 
     // tuning (ranges were checked by validate_tuning)
-    mk_tuning t = {0, 0, 0, 0, 0, 0};
+    mk_tuning t;
+    memset(&t, 0, sizeof t);
     if (tun) t = *tun;
     const int grid = t.grid ? t.grid : h->cu_count;
     if (grid > MK_MAX_GRID) return MK_ERR_TUNING;
@@ -335,6 +344,26 @@ static mk_status create_impl(const mk_model_desc *desc, const mk_tuning *tun, mk
     P.timeout_ticks = (int64_t)timeout_ms * wclk_khz;
     P.err_check_ticks = (int64_t)wclk_khz / 50;  // 20 us
     P.trace = h->trace;
+
+    // batched prefill buffers, when the geometry allows it (bf16, aligned
+    // down-stage inputs) and the tuning does not ask for decode launches
+    if (t.prefill_chunk != -1 && mk_prefill_supported(&P, dtype)) {
+        const int T = t.prefill_chunk > 0 ? t.prefill_chunk : 256;
+        auto r32 = [](int k) { return (k + 31) & ~31; };
+        int kmax = H > nh * d ? H : nh * d;
+        if (F > kmax) kmax = F;
+        const int nqkv = (nh + 2 * nkv) * d;
+        MkPrefillBufs &B = h->pf;
+        B.lda = r32(kmax);
+        B.ldy = nqkv > 2 * F ? nqkv : 2 * F;
+        HIP_TRY(hipMalloc(&B.X, (size_t)T * H * sizeof(float)));
+        HIP_TRY(hipMalloc(&B.Ah, (size_t)T * B.lda * sizeof(uint16_t)));
+        HIP_TRY(hipMalloc(&B.Al, (size_t)T * B.lda * sizeof(uint16_t)));
+        HIP_TRY(hipMalloc(&B.Y, (size_t)T * B.ldy * sizeof(float)));
+        HIP_TRY(hipMalloc(&B.Q, (size_t)T * nh * d * sizeof(float)));
+        HIP_TRY(hipMalloc(&h->pf_tokens, (size_t)D.max_seq * sizeof(int32_t)));
+        B.t_max = T;
+    }
 
     const int64_t per_layer = (int64_t)((nh + 2 * nkv) * d) * H + (int64_t)H * nh * d + 3LL * H * F + 2LL * H;
     h->weight_bytes = ((int64_t)L * per_layer + (int64_t)V * H + 2LL * H) * eb;
@@ -546,8 +575,25 @@ extern "C" mk_status mk_prefill_kv(mk_handle *h, const int32_t *tokens, int32_t 
     if (n == 0) return MK_OK;
     if (h->layers_loaded < h->desc.n_layers || !h->head_loaded) return MK_ERR_STATE;
     s = order_before(h, stream);
-    for (int i = 0; i < n && s == MK_OK; ++i)
-        s = launch(h, kv, tokens[i], nullptr, start_pos + i, 0, nullptr, nullptr, stream);
+    if (s == MK_OK && h->pf.t_max > 0) {
+        // batched: the token ids go to the device once, then chunks of up to
+        // t_max positions run the token-parallel kernels
+        if (hipMemcpyAsync(h->pf_tokens + start_pos, tokens, (size_t)n * sizeof(int32_t), hipMemcpyHostToDevice,
+                           (hipStream_t)stream) != hipSuccess)
+            s = MK_ERR_HIP;
+        MkParams p = h->base;
+        p.kc = kv->k;
+        p.vc = kv->v;
+        for (int i = 0; i < n && s == MK_OK; i += h->pf.t_max) {
+            const int T = n - i < h->pf.t_max ? n - i : h->pf.t_max;
+            MkPrefillBufs b = h->pf;
+            b.tok = h->pf_tokens + start_pos + i;
+            if (mk_prefill_chunk(&p, &b, T, start_pos + i, stream)) s = MK_ERR_HIP;
+        }
+    } else {
+        for (int i = 0; i < n && s == MK_OK; ++i)
+            s = launch(h, kv, tokens[i], nullptr, start_pos + i, 0, nullptr, nullptr, stream);
+    }
     if (s == MK_OK) s = order_after(h, stream);
     return s;
 }
@@ -585,5 +631,6 @@ extern "C" mk_status mk_get_info(const mk_handle *h, mk_info *info) {
     info->packed_bytes = h->packed_bytes;
     info->weight_bytes = h->weight_bytes;
     info->record_bytes = (int64_t)h->rec.off[7] * (int64_t)sizeof(uint64_t);
+    info->prefill_chunk = h->pf.t_max;
     return MK_OK;
 }

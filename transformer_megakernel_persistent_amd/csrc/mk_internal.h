@@ -137,6 +137,18 @@ struct MkParams {
     uint64_t *trace;       // optional [grid][5L+2][4] stage timeline, or null
 };
 
+// Buffers of the batched prefill (mk_prefill.hip), sized for chunks of up
+// to t_max tokens.
+struct MkPrefillBufs {
+    float *X;        // [t_max][H] residual stream
+    uint16_t *Ah;    // [t_max][lda] bf16 high parts of the current GEMM operand
+    uint16_t *Al;    // [t_max][lda] bf16 low parts (a - hi)
+    float *Y;        // [t_max][ldy] QKV or gate/up outputs, packed row order
+    float *Q;        // [t_max][nh*d] rotated queries
+    int32_t *tok;    // token ids of the chunk (device)
+    int32_t lda, ldy, t_max;
+};
+
 // Error codes written to the device error word.
 #define MK_DEVERR_TIMEOUT 1u
 #define MK_DEVERR_TOKEN 2u
@@ -152,6 +164,8 @@ int mk_launch_prelayout_stage(unsigned char *dst, const MkStage *st, int grid, i
 int mk_kernel_lds_bytes(int ring_slots, int vec_floats, int out_rows, int dtype, int d, int gq);
 int mk_launch_to_f32(float *dst, const void *src, int64_t n, int dtype, void *stream);
 int mk_launch_zero(void *dst, int64_t bytes, void *stream);
+int mk_prefill_chunk(const MkParams *p, const MkPrefillBufs *b, int T, int pos0, void *stream);
+int mk_prefill_supported(const MkParams *p, int dtype);
 #ifdef __cplusplus
 }
 #endif

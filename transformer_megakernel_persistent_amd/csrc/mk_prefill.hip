@@ -1,0 +1,444 @@
+// Batched prefill: the prompt's positions processed T tokens at a time, so
+// that every weight is read once per chunk instead of once per position, and
+// the matrix products become dense contractions for the matrix cores.
+//
+// The pages keep prefill apart from the decode step and measure the two
+// separately (cloud.baidu.com/article/9434380 section 八, question two); by
+// definition under causal attention the cache after a prompt equals what n
+// decode steps leave, which is what these kernels compute, in another order:
+//
+//   X = E[tokens]                                      [T][H] fp32
+//   per layer:
+//     A = split(rmsnorm(X, g_attn))                    bf16 hi + lo parts
+//     Y = A . Wqkv^T                                   MFMA, packed QKV rows
+//     rotate q, k; K, V rows of positions pos0..pos0+T-1 -> cache (bf16 RNE)
+//     A = split(causal GQA attention of each token over positions 0..its own)
+//     X += A . Wo^T
+//     A = split(rmsnorm(X, g_ffn));  Y = A . [Wg;Wu]^T
+//     A = split(silu(gate) * up);    X += A . Wd^T
+//
+// Numerics.  Weights are bf16 and enter the products exactly.  Activations
+// are fp32; each is split into bf16 hi = rne(a) and lo = rne(a - hi), and a
+// product is accumulated as W.hi + W.lo in fp32 by v_mfma_f32_16x16x32_bf16,
+// so an activation keeps about 16 bits of mantissa (relative error below
+// 2^-16) -- the decode step's activations are fp32 throughout; the cache
+// rows agree with it to within the bf16 rounding of the stored values.
+//
+// Weights are read in place from the decode kernel's packed layout (no
+// second copy of the model): a GEMM lane finds the 16-byte piece holding 8
+// consecutive inputs of a row from the row's owning workgroup, consumer and
+// stream position (mk_stream_pos, mk_down_geo).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mk_internal.h"
+
+namespace {
+
+typedef __bf16 bf8v __attribute__((ext_vector_type(8)));
+typedef float f4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf_to_f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+// float -> bfloat16 bits, round to nearest even (NaN stays NaN)
+__device__ __forceinline__ uint16_t f_to_bf(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// ---- embedding: X[t] = E[tok[t]] -----------------------------------------
+__global__ __launch_bounds__(256) void pf_embed(float *X, const int32_t *tok, const uint16_t *E, int H) {
+    const int t = blockIdx.x;
+    const uint16_t *row = E + (size_t)tok[t] * H;
+    for (int i = threadIdx.x; i < H; i += 256) X[(size_t)t * H + i] = bf_to_f(row[i]);
+}
+
+// ---- RMSNorm into the split operand ---------------------------------------
+// One workgroup per token: h = g * x / sqrt(mean(x^2) + eps), written as
+// bf16 hi and lo parts, zero-padded from H to kpad columns.
+__global__ __launch_bounds__(256) void pf_norm_split(const float *X, const float *g, int H, float eps,
+                                                     uint16_t *Ah, uint16_t *Al, int lda, int kpad) {
+    __shared__ float red[8];
+    const int t = blockIdx.x, tid = threadIdx.x;
+    const float *x = X + (size_t)t * H;
+    float ss = 0.f;
+    for (int i = tid; i < H; i += 256) ss = fmaf(x[i], x[i], ss);
+    for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
+    if ((tid & 63) == 0) red[tid >> 6] = ss;
+    __syncthreads();
+    const float inv = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)H + eps);
+    for (int i = tid; i < kpad; i += 256) {
+        const float h = i < H ? g[i] * (x[i] * inv) : 0.f;
+        const uint16_t hi = f_to_bf(h);
+        Ah[(size_t)t * lda + i] = hi;
+        Al[(size_t)t * lda + i] = f_to_bf(h - bf_to_f(hi));
+    }
+}
+
+// ---- the packed weight layout, read by row ---------------------------------
+// Owner workgroup of unit u among G workgroups holding U units (the w with
+// floor(w U / G) <= u < floor((w + 1) U / G)).
+__device__ __forceinline__ int unit_owner(int u, int U, int G) { return (int)(((int64_t)(u + 1) * G - 1) / U); }
+__device__ __forceinline__ int unit_first(int w, int U, int G) { return (int)(((int64_t)w * U) / G); }
+
+// Where packed row n of a row-split stage keeps its chunks: chunk kc of the
+// row is at base + ((qq0 + kc*qs) / 4) * slot_stride + ((qq0 + kc*qs) % 4) * 1 KiB
+// (the inverse of mk_stream_pos for the row's consumer stream).
+struct RowLoc {
+    const unsigned char *base;  // layer block + workgroup offset + consumer's 4 KiB of a slot
+    int qq0, qs;
+};
+__device__ __forceinline__ RowLoc row_loc(const MkStage &st, const unsigned char *layer_block, int grid, int n) {
+    const int U = st.units, u = n >> 2;
+    const int w = unit_owner(u, U, grid);
+    const int u0 = unit_first(w, U, grid), units = unit_first(w + 1, U, grid) - u0;
+    const int i = n - 4 * u0, c = i & 3, rc = i >> 2;
+    const int full = mk_row_groups(st.rbp) ? units / 4 : 0;
+    RowLoc r;
+    r.base = layer_block + st.wg_off[w] + c * 4 * MK_CHUNK_BYTES;
+    if (rc < full * 4) {
+        r.qq0 = (rc >> 2) * 4 * st.rbp + (rc & 3);
+        r.qs = 4;
+    } else {
+        r.qq0 = full * 4 * st.rbp + (rc - full * 4) * st.rbp;
+        r.qs = 1;
+    }
+    return r;
+}
+__device__ __forceinline__ const unsigned char *row_piece(const RowLoc &r, int64_t slot_stride, int k) {
+    const int kc = k >> 9;  // 512 bf16 per chunk
+    const int qq = r.qq0 + kc * r.qs;
+    return r.base + (int64_t)(qq >> 2) * slot_stride + (qq & 3) * MK_CHUNK_BYTES + (k & 511) * 2;
+}
+// The down stage (split along its input, piece columns): the 16-byte piece of
+// output row n holding inputs f .. f+7 (f a multiple of 8, the owning
+// workgroup's first input a multiple of 8), or NULL past the last input.
+__device__ __forceinline__ const unsigned char *down_piece(const MkStage &st, const unsigned char *layer_block,
+                                                           int grid, int F, int H, int n, int f) {
+    if (f >= F) return nullptr;
+    const int U = st.units;
+    const int w = unit_owner(f >> 1, U, grid);
+    const MkDownGeo dg = mk_down_geo(w, grid, U, F, H, 8);
+    const int q = (f - dg.f0) >> 3;
+    const int grp = n >> 6, c = grp & 3, gl = grp >> 2;
+    const int qq = gl * dg.kp + q;
+    return layer_block + st.wg_off[w] + (int64_t)(qq >> 2) * st.slot_stride + (c * 4 + (qq & 3)) * MK_CHUNK_BYTES +
+           (n & 63) * 16;
+}
+
+// ---- GEMM: out[t][n] (=|+=) sum_k (Ah + Al)[t][k] * W[n][k] -----------------
+// v_mfma_f32_16x16x32_bf16 operand layout (wave64): A[m][k] in lane
+// m + 16 * (k / 8), element k % 8; B[k][n] in lane n + 16 * (k / 8); the
+// result C[m][n] in lane n + 16 * (m / 4), element m % 4.  A workgroup of 4
+// waves covers 32 tokens x 128 rows, each wave 32 x 32 (2 x 2 blocks); a
+// lane loads its 16-byte A pieces from the split operand and its 16-byte B
+// pieces straight from the packed weights.
+template <bool DOWN, bool ADD>
+__global__ __launch_bounds__(256) void pf_gemm(const MkStage st, const unsigned char *layer_block, int grid, int F,
+                                               int H, const uint16_t *Ah, const uint16_t *Al, int lda, int T, int K,
+                                               int N, float *out, int ldo) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int m0 = blockIdx.y * 32, n0 = blockIdx.x * 128 + wv * 32;
+    const int r16 = lane & 15, kg = lane >> 4;
+    RowLoc rl[2];
+    bool nvalid[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+        const int n = n0 + 16 * nb + r16;
+        nvalid[nb] = n < N;
+        if (!DOWN) rl[nb] = row_loc(st, layer_block, grid, nvalid[nb] ? n : 0);
+    }
+    bool mvalid[2];
+    const uint16_t *ah[2], *al[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+        const int m = m0 + 16 * mb + r16;
+        mvalid[mb] = m < T;
+        ah[mb] = Ah + (size_t)(mvalid[mb] ? m : 0) * lda + 8 * kg;
+        al[mb] = Al + (size_t)(mvalid[mb] ? m : 0) * lda + 8 * kg;
+    }
+    f4v acc[2][2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = f4v{0.f, 0.f, 0.f, 0.f};
+    const u4v zero = u4v{0u, 0u, 0u, 0u};
+    auto load_b = [&](int nb, int k) -> u4v {
+        if (!nvalid[nb]) return zero;
+        if constexpr (DOWN) {
+            const unsigned char *p = down_piece(st, layer_block, grid, F, H, n0 + 16 * nb + r16, k);
+            return p ? *(const u4v *)p : zero;
+        } else {
+            return *(const u4v *)row_piece(rl[nb], st.slot_stride, k);
+        }
+    };
+    for (int k0 = 0; k0 < K; k0 += 32) {
+        const int k = k0 + 8 * kg;
+        u4v a_hi[2], a_lo[2], b[2];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+            a_hi[mb] = mvalid[mb] ? *(const u4v *)(ah[mb] + k0) : zero;
+            a_lo[mb] = mvalid[mb] ? *(const u4v *)(al[mb] + k0) : zero;
+        }
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) b[nb] = load_b(nb, k);
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) {
+                acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, a_hi[mb]),
+                                                                      __builtin_bit_cast(bf8v, b[nb]), acc[mb][nb], 0, 0, 0);
+                acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, a_lo[mb]),
+                                                                      __builtin_bit_cast(bf8v, b[nb]), acc[mb][nb], 0, 0, 0);
+            }
+    }
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+            const int n = n0 + 16 * nb + r16;
+            if (n >= N) continue;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = m0 + 16 * mb + 4 * kg + i;
+                if (m >= T) continue;
+                float *o = out + (size_t)m * ldo + n;
+                if (ADD) *o += acc[mb][nb][i];
+                else *o = acc[mb][nb][i];
+            }
+        }
+}
+
+// ---- rotary encoding and the cache rows of the chunk ------------------------
+// Y holds each token's packed QKV rows (query and key heads with the rotary
+// partners m and m + d/2 at packed rows 2m', 2m'+1, then value rows in
+// order).  Thread j of token t handles query/key pair j, or value element
+// j - (nh + nkv) * d / 2.
+__global__ __launch_bounds__(256) void pf_rope_kv(const float *Y, int ldy, int pos0, const float *rope, int nh,
+                                                  int nkv, int d, int layer, int max_seq, uint16_t *kc, uint16_t *vc,
+                                                  float *Q) {
+    const int t = blockIdx.y, j = blockIdx.x * 256 + threadIdx.x;
+    const int npair = (nh + nkv) * d / 2, nv = nkv * d;
+    if (j >= npair + nv) return;
+    const float *y = Y + (size_t)t * ldy;
+    const int pos = pos0 + t, nq = nh * d;
+    if (j < npair) {
+        const int gr = 2 * j;
+        const bool isq = gr < nq;
+        const int r = isq ? gr : gr - nq;
+        const int head = r / d, m = (r % d) / 2;
+        const float c = rope[((size_t)pos * (d / 2) + m) * 2], s = rope[((size_t)pos * (d / 2) + m) * 2 + 1];
+        const float y0 = y[gr], y1 = y[gr + 1];
+        const float a = y0 * c - y1 * s, b = y0 * s + y1 * c;
+        if (isq) {
+            Q[((size_t)t * nh + head) * d + m] = a;
+            Q[((size_t)t * nh + head) * d + m + d / 2] = b;
+        } else {
+            uint16_t *row = kc + (((size_t)layer * nkv + head) * max_seq + pos) * d;
+            row[m] = f_to_bf(a);
+            row[m + d / 2] = f_to_bf(b);
+        }
+    } else {
+        const int r = j - npair;
+        const int head = r / d, e = r % d;
+        vc[(((size_t)layer * nkv + head) * max_seq + pos) * d + e] = f_to_bf(y[nq + nkv * d + r]);
+    }
+}
+
+// ---- causal GQA attention of the chunk's tokens ------------------------------
+// Workgroup (token block, KV head j): pairs (token, query head of group j),
+// LPP = D / 8 lanes per pair (8 dims each).  Positions stream through LDS in
+// blocks of 64 K and V rows; each pair folds eight positions at a time into
+// its running max, sum and output (online softmax), positions past its own
+// masked out.  Output o / l goes to the split operand at [t][head*D + dim].
+template <int D, int GQ>
+__global__ __launch_bounds__(256) void pf_attn(const float *Q, const uint16_t *kc, const uint16_t *vc, int layer, int nh,
+                                               int nkv, int max_seq, int pos0, int T, uint16_t *Ah, uint16_t *Al,
+                                               int lda) {
+    constexpr int LPP = D / 8, PAIRS = 256 / LPP, TPW = PAIRS / GQ, BP = 64;
+    __shared__ __attribute__((aligned(16))) uint16_t ks[BP * D], vs[BP * D];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int pr = tid / LPP, sub = tid % LPP;  // pair, and this lane's dims [8 sub, 8 sub + 8)
+    const int j = blockIdx.y;
+    const int tl = pr / GQ, g = pr % GQ;         // token within the block, head within the group
+    const int t = blockIdx.x * TPW + tl;
+    const bool tv = t < T;
+    const int head = j * GQ + g;
+    const int my_last = pos0 + (tv ? t : 0);     // last position this pair attends
+    const int t_hi = min(T, (int)(blockIdx.x + 1) * TPW) - 1;
+    const int n_pos = pos0 + t_hi + 1;           // positions the workgroup needs
+    const float scale = 1.0f / sqrtf((float)D);
+    float q[8], o[8];
+    const float *qp = Q + ((size_t)(tv ? t : 0) * nh + head) * D + 8 * sub;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        q[e] = qp[e] * scale;
+        o[e] = 0.f;
+    }
+    float mrun = -INFINITY, lrun = 0.f;
+    const uint16_t *kbase = kc + ((size_t)layer * nkv + j) * max_seq * D;
+    const uint16_t *vbase = vc + ((size_t)layer * nkv + j) * max_seq * D;
+    for (int p0 = 0; p0 < n_pos; p0 += BP) {
+        const int nb = min(BP, n_pos - p0);
+        __syncthreads();
+        for (int i = tid; i < BP * D / 8; i += 256) {  // 16-byte pieces of the block
+            const int row = i / (D / 8);
+            u4v kv4 = u4v{0u, 0u, 0u, 0u}, vv4 = u4v{0u, 0u, 0u, 0u};
+            if (row < nb) {
+                kv4 = *(const u4v *)(kbase + (size_t)(p0 + row) * D + (i % (D / 8)) * 8);
+                vv4 = *(const u4v *)(vbase + (size_t)(p0 + row) * D + (i % (D / 8)) * 8);
+            }
+            *(u4v *)(ks + i * 8) = kv4;
+            *(u4v *)(vs + i * 8) = vv4;
+        }
+        __syncthreads();
+        for (int pb = 0; pb < nb; pb += 8) {
+            float s[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const u4v kw = *(const u4v *)(ks + (pb + u) * D + 8 * sub);
+                float a = 0.f;
+                a = fmaf(q[0], __uint_as_float(kw.x << 16), a);
+                a = fmaf(q[1], __uint_as_float(kw.x & 0xFFFF0000u), a);
+                a = fmaf(q[2], __uint_as_float(kw.y << 16), a);
+                a = fmaf(q[3], __uint_as_float(kw.y & 0xFFFF0000u), a);
+                a = fmaf(q[4], __uint_as_float(kw.z << 16), a);
+                a = fmaf(q[5], __uint_as_float(kw.z & 0xFFFF0000u), a);
+                a = fmaf(q[6], __uint_as_float(kw.w << 16), a);
+                a = fmaf(q[7], __uint_as_float(kw.w & 0xFFFF0000u), a);
+                // sum over the pair's LPP lanes (aligned groups within the wave)
+#pragma unroll
+                for (int m = 1; m < LPP; m <<= 1) a += __shfl_xor(a, m);
+                const int pos = p0 + pb + u;
+                s[u] = (pb + u < nb && pos <= my_last) ? a : -INFINITY;
+            }
+            float mx = s[0];
+#pragma unroll
+            for (int u = 1; u < 8; ++u) mx = fmaxf(mx, s[u]);
+            const float mn = fmaxf(mrun, mx);
+            if (mn == -INFINITY) continue;  // nothing valid yet for this pair (uniform per pair)
+            const float alpha = __expf(mrun - mn);
+            float pe[8], lsum = lrun * alpha;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                pe[u] = __expf(s[u] - mn);
+                lsum += pe[u];
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] *= alpha;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const u4v vw = *(const u4v *)(vs + (pb + u) * D + 8 * sub);
+                o[0] = fmaf(pe[u], __uint_as_float(vw.x << 16), o[0]);
+                o[1] = fmaf(pe[u], __uint_as_float(vw.x & 0xFFFF0000u), o[1]);
+                o[2] = fmaf(pe[u], __uint_as_float(vw.y << 16), o[2]);
+                o[3] = fmaf(pe[u], __uint_as_float(vw.y & 0xFFFF0000u), o[3]);
+                o[4] = fmaf(pe[u], __uint_as_float(vw.z << 16), o[4]);
+                o[5] = fmaf(pe[u], __uint_as_float(vw.z & 0xFFFF0000u), o[5]);
+                o[6] = fmaf(pe[u], __uint_as_float(vw.w << 16), o[6]);
+                o[7] = fmaf(pe[u], __uint_as_float(vw.w & 0xFFFF0000u), o[7]);
+            }
+            mrun = mn;
+            lrun = lsum;
+        }
+    }
+    (void)lane;
+    if (!tv) return;
+    const float inv = 1.0f / lrun;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float v = o[e] * inv;
+        const uint16_t hi = f_to_bf(v);
+        const size_t idx = (size_t)t * lda + (size_t)head * D + 8 * sub + e;
+        Ah[idx] = hi;
+        Al[idx] = f_to_bf(v - bf_to_f(hi));
+    }
+}
+
+// ---- SwiGLU of the interleaved gate/up rows into the split operand ----------
+__global__ __launch_bounds__(256) void pf_swiglu_split(const float *Y, int ldy, int F, uint16_t *Ah, uint16_t *Al,
+                                                       int lda, int kpad) {
+    const int t = blockIdx.y, f = blockIdx.x * 256 + threadIdx.x;
+    if (f >= kpad) return;
+    float a = 0.f;
+    if (f < F) {
+        const float gv = Y[(size_t)t * ldy + 2 * f], uv = Y[(size_t)t * ldy + 2 * f + 1];
+        a = gv / (1.0f + __expf(-gv)) * uv;
+    }
+    const uint16_t hi = f_to_bf(a);
+    Ah[(size_t)t * lda + f] = hi;
+    Al[(size_t)t * lda + f] = f_to_bf(a - bf_to_f(hi));
+}
+
+template <int D, int GQ>
+void launch_attn(dim3 g, hipStream_t s, const float *Q, const uint16_t *kc, const uint16_t *vc, int layer, int nh,
+                 int nkv, int max_seq, int pos0, int T, uint16_t *Ah, uint16_t *Al, int lda) {
+    hipLaunchKernelGGL((pf_attn<D, GQ>), g, dim3(256), 0, s, Q, kc, vc, layer, nh, nkv, max_seq, pos0, T, Ah, Al, lda);
+}
+
+int round32(int k) { return (k + 31) & ~31; }
+
+}  // namespace
+
+// Token-parallel work for positions [pos0, pos0 + T) of prompt tokens
+// tok (device, T ids): fills their cache rows in every layer.  Buffers are
+// the handle's (see MkPrefillBufs).  Requires a bf16 model whose down-stage
+// workgroups own inputs starting at multiples of 8 (mk_prefill_supported).
+extern "C" int mk_prefill_chunk(const MkParams *p, const MkPrefillBufs *b, int T, int pos0, void *stream) {
+    hipStream_t s = (hipStream_t)stream;
+    const int L = p->L, H = p->H, nh = p->nh, nkv = p->nkv, d = p->d, F = p->F, G = p->grid;
+    const int gq = nh / nkv;
+    const int nqkv = (nh + 2 * nkv) * d, nq = nh * d;
+    uint16_t *kc = (uint16_t *)p->kc, *vc = (uint16_t *)p->vc;
+    const int lda = b->lda, ldy = b->ldy;
+    hipLaunchKernelGGL(pf_embed, dim3(T), dim3(256), 0, s, b->X, b->tok, (const uint16_t *)p->embed, H);
+    for (int l = 0; l < L; ++l) {
+        const unsigned char *blk[ST_NUM];
+        for (int k = 0; k < ST_LM; ++k) blk[k] = p->packed + p->st[k].base + (int64_t)l * p->st[k].layer_stride;
+        // attention half
+        hipLaunchKernelGGL(pf_norm_split, dim3(T), dim3(256), 0, s, b->X, p->g_attn + (size_t)l * H, H, p->eps, b->Ah,
+                           b->Al, lda, round32(H));
+        hipLaunchKernelGGL((pf_gemm<false, false>), dim3((nqkv + 127) / 128, (T + 31) / 32), dim3(256), 0, s,
+                           p->st[ST_QKV], blk[ST_QKV], G, F, H, b->Ah, b->Al, lda, T, round32(H), nqkv, b->Y, ldy);
+        const int nthr = (nh + nkv) * d / 2 + nkv * d;
+        hipLaunchKernelGGL(pf_rope_kv, dim3((nthr + 255) / 256, T), dim3(256), 0, s, b->Y, ldy, pos0, p->rope, nh, nkv,
+                           d, l, p->max_seq, kc, vc, b->Q);
+        {
+            const int pairs = 256 / (d / 8), tpw = pairs / gq;
+            const dim3 g((T + tpw - 1) / tpw, nkv);
+#define MK_PF_ATTN(D_, GQ_) \
+    if (d == D_ && gq == GQ_) launch_attn<D_, GQ_>(g, s, b->Q, kc, vc, l, nh, nkv, p->max_seq, pos0, T, b->Ah, b->Al, lda);
+            MK_PF_ATTN(64, 1) MK_PF_ATTN(64, 2) MK_PF_ATTN(64, 4) MK_PF_ATTN(64, 8)
+            MK_PF_ATTN(128, 1) MK_PF_ATTN(128, 2) MK_PF_ATTN(128, 4) MK_PF_ATTN(128, 8)
+#undef MK_PF_ATTN
+        }
+        hipLaunchKernelGGL((pf_gemm<false, true>), dim3((H + 127) / 128, (T + 31) / 32), dim3(256), 0, s, p->st[ST_O],
+                           blk[ST_O], G, F, H, b->Ah, b->Al, lda, T, round32(nq), H, b->X, H);
+        // feed-forward half
+        hipLaunchKernelGGL(pf_norm_split, dim3(T), dim3(256), 0, s, b->X, p->g_ffn + (size_t)l * H, H, p->eps, b->Ah,
+                           b->Al, lda, round32(H));
+        hipLaunchKernelGGL((pf_gemm<false, false>), dim3((2 * F + 127) / 128, (T + 31) / 32), dim3(256), 0, s,
+                           p->st[ST_GU], blk[ST_GU], G, F, H, b->Ah, b->Al, lda, T, round32(H), 2 * F, b->Y, ldy);
+        hipLaunchKernelGGL(pf_swiglu_split, dim3((round32(F) + 255) / 256, T), dim3(256), 0, s, b->Y, ldy, F, b->Ah,
+                           b->Al, lda, round32(F));
+        hipLaunchKernelGGL((pf_gemm<true, true>), dim3((H + 127) / 128, (T + 31) / 32), dim3(256), 0, s,
+                           p->st[ST_DOWN], blk[ST_DOWN], G, F, H, b->Ah, b->Al, lda, T, round32(F), H, b->X, H);
+    }
+    return (int)hipGetLastError();
+}
+
+// Whether the batched prefill applies to a handle's geometry: bf16 weights,
+// head_dim 64 or 128, and every down-stage workgroup's first input a multiple
+// of 8 (a 16-byte piece of its piece columns then holds 8 consecutive inputs
+// of the row, the unit of a GEMM lane's B operand).
+extern "C" int mk_prefill_supported(const MkParams *p, int dtype) {
+    if (dtype != 1 || (p->d != 64 && p->d != 128)) return 0;
+    const int U = p->st[ST_DOWN].units;
+    for (int w = 0; w < p->grid; ++w) {
+        const MkDownGeo dg = mk_down_geo(w, p->grid, U, p->F, p->H, 8);
+        if (dg.f0 % 8 != 0) return 0;
+    }
+    return 1;
+}
