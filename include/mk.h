@@ -57,8 +57,15 @@ typedef enum {
     MK_ERR_DEVICE = 7,  /* the device reported a failure (grid-wait timeout) */
     MK_ERR_STATE = 8,   /* the handle was disabled by an earlier device failure, or its
                            weights are not all loaded yet (mk_create_deferred) */
-    MK_ERR_TUNING = 9   /* a tuning value is out of its documented range */
+    MK_ERR_TUNING = 9,  /* a tuning value is out of its documented range */
+    MK_ERR_SCRATCH = 10 /* the model's cross-workgroup records do not fit the static scratch
+                           (mk_decode_step_device_token_noalloc) */
 } mk_status;
+
+/* Size of the library's static device scratch, the record buffer of
+   mk_decode_step_device_token_noalloc (one per device, held until the
+   process ends). */
+#define MK_STATIC_SCRATCH_BYTES (64 * 1024 * 1024)
 
 typedef enum { MK_F32 = 0, MK_BF16 = 1 } mk_dtype;
 
@@ -142,7 +149,8 @@ typedef struct {
     int32_t prefetch_slots;  /* 16 KiB slots the loads run ahead of the arithmetic */
     int64_t packed_bytes;    /* library-owned pre-laid-out weight bytes */
     int64_t weight_bytes;    /* algorithmic weight bytes read per step */
-    int64_t record_bytes;    /* cross-workgroup record buffer of one launch */
+    int64_t record_bytes;    /* cross-workgroup record buffer of one launch (at most
+                                MK_STATIC_SCRATCH_BYTES for the no-allocation step) */
     int32_t prefill_chunk;   /* tokens per batched-prefill chunk; 0: prefill by decode launches */
 } mk_info;
 
@@ -206,6 +214,27 @@ mk_status mk_decode_step(mk_handle *h, int32_t token_id, int32_t pos, const mk_k
    the state carried from step to step be checked again. */
 mk_status mk_decode_step_device_token(mk_handle *h, const int32_t *token_in, int32_t pos, const mk_kv_cache *kv,
                                       float *logits_out, int32_t *token_out, void *stream);
+
+/* The step of mk_decode_step_device_token for callers that cannot allocate
+   device memory at the time of the call: code under HIP graph capture, tight
+   serving loops, harnesses that forbid hipMalloc.  It allocates nothing and
+   calls no allocating routine: the cross-workgroup records of the launch
+   (the only buffer its kernel needs beyond the handle's weights and the
+   caller's inputs and outputs) live in a static device array of the library,
+   MK_STATIC_SCRATCH_BYTES per device, instead of the handle's own buffer;
+   the kernel and the results are those of mk_decode_step_device_token, bit
+   for bit.  The caller still passes the token, cache, logits and token
+   buffers.  Every call on one device shares that device's array and one tag
+   counter (a record left by an earlier call never carries an awaited tag, so
+   nothing needs clearing between calls); calls that overlap in time on one
+   device, from any handle or stream, race on it and are not allowed.  The
+   device is the one current at mk_create.  Errors: as
+   mk_decode_step_device_token, plus MK_ERR_SCRATCH when the handle's record
+   buffer (mk_info.record_bytes) exceeds MK_STATIC_SCRATCH_BYTES and MK_ERR_HIP
+   when the array's device address could not be taken at mk_create. */
+mk_status mk_decode_step_device_token_noalloc(mk_handle *h, const int32_t *token_in, int32_t pos,
+                                              const mk_kv_cache *kv, float *logits_out, int32_t *token_out,
+                                              void *stream);
 
 /* Fill cache positions [start_pos, start_pos + n) from n host token ids: by
    definition under causal attention this is n decode steps at those

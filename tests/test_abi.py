@@ -53,11 +53,11 @@ def test_status_and_dtype_values_match_binding():
 
 def test_status_strings(lib):
     seen = set()
-    for s in range(0, 10):
+    for s in range(0, 11):
         txt = lib.mk_status_str(s).decode()
         assert txt and txt != "unknown status"
         seen.add(txt)
-    assert len(seen) == 10
+    assert len(seen) == 11
     assert lib.mk_status_str(99).decode() == "unknown status"
 
 
@@ -132,6 +132,7 @@ def test_calls_on_a_null_handle(lib):
     buf = (ctypes.c_int32 * 4)()
     assert lib.mk_decode_step(None, 0, 0, ctypes.byref(kv), buf, None) == mkb.MK_ERR_NULL
     assert lib.mk_decode_step_device_token(None, buf, 0, ctypes.byref(kv), None, buf, None) == mkb.MK_ERR_NULL
+    assert lib.mk_decode_step_device_token_noalloc(None, buf, 0, ctypes.byref(kv), None, buf, None) == mkb.MK_ERR_NULL
     assert lib.mk_prefill_kv(None, buf, 1, 0, ctypes.byref(kv), None) == mkb.MK_ERR_NULL
     assert lib.mk_get_device_error(None) == mkb.MK_ERR_NULL
     assert lib.mk_get_info(None, ctypes.byref(mkb.Info())) == mkb.MK_ERR_NULL

@@ -8,6 +8,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include "mk.h"
@@ -22,6 +23,19 @@ struct RecLayout {
     size_t off[8];
 };
 
+// ---- the static scratch of mk_decode_step_device_token_noalloc -------------
+// Callers that cannot allocate device memory (code under graph capture,
+// tight serving loops) get the records from this file-scope array instead
+// of the handle's own buffer.  Each device the library runs on holds one
+// copy until the process ends.  In host code the name `scratch` is only a
+// host-side stand-in: its device address is taken once per device with
+// hipGetSymbolAddress (device current) and kept in g_scratch_ptr, and only
+// that address is ever passed to a kernel.
+#define MK_MAX_DEVICES 64
+static __device__ __align__(256) uint64_t scratch[MK_STATIC_SCRATCH_BYTES / sizeof(uint64_t)];
+static std::mutex g_scratch_mu;
+static uint64_t *g_scratch_ptr[MK_MAX_DEVICES];  // device address of `scratch` on each device
+static uint32_t g_scratch_tag_end[MK_MAX_DEVICES];  // last tag used on that device's array
 
 struct mk_handle {
     mk_model_desc desc;
@@ -38,7 +52,7 @@ struct mk_handle {
     void *embed = nullptr;
     float *rope = nullptr;
     uint64_t *ll = nullptr;     // tagged cross-workgroup records (see MkParams)
-    RecLayout rec;              // their layout
+    RecLayout rec;              // their layout (the same inside the static scratch)
     uint32_t *err = nullptr;    // device error word
     uint64_t *trace = nullptr;
     int64_t trace_len = 0;
@@ -98,6 +112,17 @@ void set_records(MkParams &P, uint64_t *base, const RecLayout &r) {
     P.ll_amax = base + r.off[6];
 }
 
+// Once per device, with that device current: the device address of the
+// static scratch.  Returns false if it cannot be taken.
+bool scratch_setup(int dev) {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (dev < 0 || dev >= MK_MAX_DEVICES) return false;
+    if (g_scratch_ptr[dev]) return true;
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return false;
+    g_scratch_ptr[dev] = (uint64_t *)ptr;
+    return true;
+}
 
 struct StageShape {
     int rows, k;
@@ -144,6 +169,7 @@ extern "C" const char *mk_status_str(mk_status s) {
     case MK_ERR_DEVICE: return "device reported a failure";
     case MK_ERR_STATE: return "handle not ready: disabled by a device failure, or weights not all loaded";
     case MK_ERR_TUNING: return "tuning value out of range";
+    case MK_ERR_SCRATCH: return "the model's cross-workgroup records exceed the static scratch (MK_STATIC_SCRATCH_BYTES)";
     }
     return "unknown status";
 }
@@ -182,6 +208,10 @@ static mk_status create_impl(const mk_model_desc *desc, const mk_tuning *tun, mk
     h->eb = eb;
 
     HIP_TRY(hipGetDevice(&h->device));
+    // the static scratch of the no-allocation entry point, taken once per
+    // device at the library's set-up; if it cannot be taken, that entry
+    // point reports MK_ERR_HIP and everything else works as usual
+    (void)scratch_setup(h->device);
     hipDeviceProp_t prop;
     HIP_TRY(hipGetDeviceProperties(&prop, h->device));
     h->cu_count = prop.multiProcessorCount;
@@ -560,6 +590,35 @@ extern "C" mk_status mk_decode_step_device_token(mk_handle *h, const int32_t *to
     if (s != MK_OK) return s;
     if (pos < 0 || pos >= h->desc.max_seq) return MK_ERR_RANGE;
     return launch_one(h, kv, 0, token_in, pos, 1, logits_out, token_out, stream);
+}
+
+extern "C" mk_status mk_decode_step_device_token_noalloc(mk_handle *h, const int32_t *token_in, int32_t pos,
+                                                         const mk_kv_cache *kv, float *logits_out, int32_t *token_out,
+                                                         void *stream) {
+    if (!h || !token_in || !token_out) return MK_ERR_NULL;
+    if (h->disabled) return MK_ERR_STATE;
+    mk_status s = check_kv(h, kv);
+    if (s != MK_OK) return s;
+    if (pos < 0 || pos >= h->desc.max_seq) return MK_ERR_RANGE;
+    if (h->rec.off[7] * sizeof(uint64_t) > (size_t)MK_STATIC_SCRATCH_BYTES) return MK_ERR_SCRATCH;
+    if (h->layers_loaded < h->desc.n_layers || !h->head_loaded) return MK_ERR_STATE;
+    uint64_t *base = nullptr;
+    uint32_t tb = 0;
+    bool wrapped = false;
+    {
+        // every call on a device shares its array and one tag counter, so a
+        // record another handle left there never carries an awaited tag
+        std::lock_guard<std::mutex> lk(g_scratch_mu);
+        const int dev = h->device;
+        if (dev < 0 || dev >= MK_MAX_DEVICES || !g_scratch_ptr[dev]) return MK_ERR_HIP;
+        base = g_scratch_ptr[dev];
+        tb = next_tag_base(g_scratch_tag_end[dev], h->desc.n_layers, &wrapped);
+    }
+    s = order_before(h, stream);
+    if (s == MK_OK && wrapped && mk_launch_zero(base, (int64_t)MK_STATIC_SCRATCH_BYTES, stream)) s = MK_ERR_HIP;
+    if (s == MK_OK) s = launch(h, kv, 0, token_in, pos, 1, logits_out, token_out, stream, base, tb);
+    if (s == MK_OK) s = order_after(h, stream);
+    return s;
 }
 
 extern "C" mk_status mk_prefill_kv(mk_handle *h, const int32_t *tokens, int32_t n, int32_t start_pos,

@@ -16,11 +16,12 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmk.so")
 
 MK_OK, MK_ERR_NULL, MK_ERR_SHAPE, MK_ERR_DTYPE, MK_ERR_RANGE = 0, 1, 2, 3, 4
-MK_ERR_NOMEM, MK_ERR_HIP, MK_ERR_DEVICE, MK_ERR_STATE, MK_ERR_TUNING = 5, 6, 7, 8, 9
+MK_ERR_NOMEM, MK_ERR_HIP, MK_ERR_DEVICE, MK_ERR_STATE, MK_ERR_TUNING, MK_ERR_SCRATCH = 5, 6, 7, 8, 9, 10
+MK_STATIC_SCRATCH_BYTES = 64 * 1024 * 1024
 MK_F32, MK_BF16 = 0, 1
 
 EXPORTED = ("mk_create", "mk_create_deferred", "mk_load_weights", "mk_decode_step", "mk_decode_step_device_token",
-            "mk_prefill_kv", "mk_get_device_error", "mk_get_info",
+            "mk_decode_step_device_token_noalloc", "mk_prefill_kv", "mk_get_device_error", "mk_get_info",
             "mk_read_trace", "mk_status_str", "mk_destroy")
 
 
@@ -77,6 +78,7 @@ def load_library(path: str = LIB_PATH):
         "mk_load_weights": ([vp, p(WeightPtrs), i32, i32], ctypes.c_int),
         "mk_decode_step": ([vp, i32, i32, p(KVDesc), vp, vp], ctypes.c_int),
         "mk_decode_step_device_token": ([vp, vp, i32, p(KVDesc), vp, vp, vp], ctypes.c_int),
+        "mk_decode_step_device_token_noalloc": ([vp, vp, i32, p(KVDesc), vp, vp, vp], ctypes.c_int),
         "mk_prefill_kv": ([vp, vp, i32, i32, p(KVDesc), vp], ctypes.c_int),
         "mk_get_device_error": ([vp], ctypes.c_int),
         "mk_get_info": ([vp, p(Info)], ctypes.c_int),
@@ -179,6 +181,13 @@ class MegaKernel:
         _check(load_library().mk_decode_step_device_token(self._h, _ptr(token_in), int(pos), ctypes.byref(d),
                                                           _ptr(logits), _ptr(token_out), _stream(stream)),
                "mk_decode_step_device_token")
+
+    def decode_step_device_token_noalloc(self, token_in: torch.Tensor, pos: int, kv: KVCache, logits, token_out,
+                                         stream=None):
+        d = kv.desc()
+        _check(load_library().mk_decode_step_device_token_noalloc(self._h, _ptr(token_in), int(pos), ctypes.byref(d),
+                                                                  _ptr(logits), _ptr(token_out), _stream(stream)),
+               "mk_decode_step_device_token_noalloc")
 
     def prefill_kv(self, tokens, start_pos: int, kv: KVCache, stream=None):
         arr = (ctypes.c_int32 * len(tokens))(*[int(t) for t in tokens])
