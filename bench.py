@@ -170,7 +170,8 @@ def measure(name, args, dev, steps, warm, runs, cpu_budget, with_cpu):
     max_seq = ctx + warm + runs * steps
     tuning = {"grid": args.grid, "ring_slots": args.ring, "attn_splits": args.splits,
               "cooperative": 1 if args.launch == "cooperative" else 2,
-              "prefetch_depth": args.prefetch_depth, "stage_drain": 1 if args.stage_drain else 0}
+              "prefetch_depth": args.prefetch_depth, "stage_drain": 1 if args.stage_drain else 0,
+              "prefill_chunk": args.prefill_chunk, "attn_pm_slots": args.attn_pm_slots}
     # The oracle baseline needs every weight in host memory; past this size it
     # is not taken (the weights are streamed to the device a layer at a time).
     keep_host = with_cpu and cfg.weight_bytes_per_step() <= HOST_ORACLE_MAX_BYTES
@@ -285,6 +286,11 @@ def main():
                     help="slots the loads run ahead (default: ring slots - 1); an ablation knob")
     ap.add_argument("--stage-drain", action="store_true",
                     help="ablation: no loads for a stage before its grid dependency is met")
+    ap.add_argument("--prefill-chunk", type=int, default=0,
+                    help="tokens per batched-prefill chunk (default 256); -1: one decode launch per position")
+    ap.add_argument("--attn-pm-slots", type=int, default=0,
+                    help="position-major attention when a split holds at least this many KV slots "
+                         "(default 0: always head-major)")
     ap.add_argument("--launch", choices=["cooperative", "ordinary"], default="ordinary",
                     help="cooperative launch (co-residency checked by the runtime) or an ordinary launch")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",

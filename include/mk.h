@@ -129,6 +129,19 @@ typedef struct {
                   for the grid dependency before it (the consumers' opening
                   barrier of the stage); 0 = loads run ahead across stage
                   boundaries (default).  An ablation knob;
+     attn_pm_slots: per-length attention mapping.  With four query heads
+                  per KV head, when a split holds at least this many whole
+                  KV slots (64 positions each at head_dim 64, 32 at 128) the
+                  launch uses the position-major mapping (each consumer wave
+                  folds a quarter of every slot's positions for all four
+                  heads, so K and V are read from LDS once per workgroup);
+                  shorter splits use the head-major mapping (each consumer
+                  one head over all positions).  0 or -1 (default) = always
+                  head-major: on MI355X the position-major mapping measured
+                  slower at both the 2048- and the 32768-token contexts (the
+                  slot is bound by the consumers' arithmetic, not by LDS
+                  reads).  The page cloud.baidu.com/article/9434380 section
+                  八 (question five) advises tiling by length;
      prefill_chunk: tokens per chunk of the batched prefill, 1..1024
                   (default 256); -1 = prefill by one decode launch per
                   position.  The batched prefill needs bf16 weights and a
@@ -138,7 +151,7 @@ typedef struct {
                   (mk_info.prefill_chunk reports which). */
 typedef struct {
     int32_t grid, ring_slots, attn_splits, timeout_ms, cooperative, trace, prefetch_depth, stage_drain;
-    int32_t prefill_chunk;
+    int32_t prefill_chunk, attn_pm_slots;
 } mk_tuning;
 
 typedef struct mk_handle mk_handle;

@@ -377,3 +377,42 @@ def test_stage_timeline_tool_runs(env, capsys):
     for st in stage_timeline.STAGES:
         assert f"  {st:5s} epilogue" in out
     assert "per layer" in out
+
+
+# ---- per-length attention mapping: position-major for long splits ----
+
+@pytest.mark.parametrize("n_prompt,splits,dtype", [(130, 2, "f32"), (200, 2, "f32"), (333, 3, "f32"), (260, 2, "bf16")])
+def test_position_major_attention(env, n_prompt, splits, dtype):
+    """Four query heads per KV head with the position-major mapping forced
+    (attn_pm_slots 1): each consumer folds two chunks of every KV slot for all
+    four heads, the four partials merged in LDS.  Splits with whole slots plus
+    a register tail (130: 65 positions each), a second partial slot (200),
+    three splits (333), and the bf16 cache."""
+    cfg = synth.CONFIGS["tiny"].with_(n_heads=8, n_kv_heads=2, dtype=dtype,
+                                      rope_theta=10000.0 if dtype == "f32" else 500000.0)
+    errs, agree = run_pair(env, cfg, seed=81, n_prompt=n_prompt, n_steps=3,
+                           tuning={"attn_splits": splits, "attn_pm_slots": 1})
+    assert max(errs) <= tol_of(cfg) and agree == 3
+
+
+def test_position_major_equals_head_major(env):
+    """The same steps with the position-major mapping forced and with it off
+    agree to fp32 rounding (the mapping only changes the summation order)."""
+    torch, oracle, mkp = env
+    cfg = synth.CONFIGS["tiny"].with_(n_heads=8, n_kv_heads=2)
+    n, max_seq = 300, 304
+    toks = synth.gen_tokens(82, n + 1, cfg.vocab)
+    outs = []
+    for pm in (1, -1):
+        mk, _ = _make(env, cfg, 82, max_seq, tuning={"attn_splits": 2, "attn_pm_slots": pm})
+        kv = mkp.KVCache(shape_of(cfg), max_seq)
+        mk.prefill_kv(toks[:n], 0, kv)
+        lg = torch.empty(cfg.vocab, device="cuda")
+        mk.decode_step(int(toks[n]), n, kv, lg)
+        torch.cuda.synchronize()
+        assert mk.device_error() == 0
+        outs.append(lg.cpu().numpy().astype(np.float64))
+        mk.close()
+    d = float(np.abs(outs[0] - outs[1]).max())
+    print(f"[parity] position-major vs head-major logits max|d| = {d:.3e}", flush=True)
+    assert d <= 1e-5

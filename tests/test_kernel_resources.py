@@ -34,13 +34,16 @@ def resources():
 
 
 def test_every_decode_instantiation_is_reported(resources):
+    # <dtype, group, lanes per cache row, LOGITS, position-major attention>;
+    # the position-major mapping exists for groups of four query heads only
     names = {k["name"] for k in resources}
     for dt in (0, 1):
         for gq in GROUPS:
             for lpp in LANES:
                 for logits in ("b0", "b1"):
-                    n = f"_Z16mk_decode_kernelILi{dt}ELi{gq}ELi{lpp}EL{logits}EEv8MkParams"
-                    assert n in names, n
+                    for pm in (("b0", "b1") if gq == 4 else ("b0",)):
+                        n = f"_Z16mk_decode_kernelILi{dt}ELi{gq}ELi{lpp}EL{logits}EL{pm}EEv8MkParams"
+                        assert n in names, n
 
 
 def test_no_kernel_spills_to_scratch(resources):

@@ -149,7 +149,8 @@ mk_status validate_tuning(const mk_tuning *t) {
     if (!t) return MK_OK;
     if (t->grid < 0 || t->grid > MK_MAX_GRID || t->ring_slots < 0 || t->attn_splits < 0 || t->attn_splits > MK_MAX_SPLITS || t->timeout_ms < 0 ||
         t->cooperative < 0 || t->cooperative > 2 || t->trace < 0 || t->trace > 1 || t->prefetch_depth < 0 ||
-        t->stage_drain < 0 || t->stage_drain > 1 || t->prefill_chunk < -1 || t->prefill_chunk > 1024)
+        t->stage_drain < 0 || t->stage_drain > 1 || t->prefill_chunk < -1 || t->prefill_chunk > 1024 ||
+        t->attn_pm_slots < -1)
         return MK_ERR_TUNING;
     if (t->ring_slots != 0 && (t->ring_slots < 3 || t->ring_slots > MK_MAX_RING)) return MK_ERR_TUNING;
     return MK_OK;
@@ -292,6 +293,10 @@ static mk_status create_impl(const mk_model_desc *desc, const mk_tuning *tun, mk
     if ((int64_t)grid * H * 8 >= (1LL << 32)) return MK_ERR_SHAPE;
     // the attention stage gathers its group's queries and the new K/V row into vec
     if (vec_floats < (gq + 2) * d) vec_floats = (gq + 2) * d;
+    // position-major attention (groups of four query heads) merges the four
+    // consumers' per-head partials in vec, after the queries and the row of pos
+    if (gq == MK_NUM_CONSUMERS && vec_floats < (gq + 2) * d + MK_NUM_CONSUMERS * gq * (d + 2))
+        vec_floats = (gq + 2) * d + MK_NUM_CONSUMERS * gq * (d + 2);
     const int fixed = mk_kernel_lds_bytes(0, vec_floats, out_rows, dtype, d, gq);
     int ns = t.ring_slots ? t.ring_slots : (MK_LDS_LIMIT - fixed) / MK_SLOT_BYTES;
     if (ns > MK_DEFAULT_RING && !t.ring_slots) ns = MK_DEFAULT_RING;  // a 9th slot measured no faster
@@ -365,6 +370,10 @@ static mk_status create_impl(const mk_model_desc *desc, const mk_tuning *tun, mk
     P.grid = grid; P.ring_slots = ns; P.splits = splits; P.lds_vec_floats = vec_floats; P.lds_out_rows = out_rows;
     P.prefetch_depth = t.prefetch_depth ? t.prefetch_depth : ns - 1;
     P.stage_drain = t.stage_drain;
+    // default: head-major at every length (position-major measured slower,
+    // 947 against 937 us per 32K-context step; the slot is bound by the
+    // consumers' arithmetic, not by their LDS reads)
+    P.attn_pm_slots = t.attn_pm_slots > 0 ? t.attn_pm_slots : (1 << 30);
     P.packed = h->packed;
     P.g_attn = h->gains; P.g_ffn = h->gains + (size_t)L * H; P.g_final = h->gains + (size_t)2 * L * H;
     P.embed = h->embed;

@@ -318,6 +318,24 @@ __device__ __forceinline__ void piece_load_buf(__amdgpu_buffer_rsrc_t r, uint32_
 
 __device__ __forceinline__ int wg_unit0(int w, int U, int G) { return (int)(((int64_t)w * U) / G); }
 
+// Running attention state of NH query heads (flash decode): the lane's
+// query dims, running max (wave-uniform), running sums and unnormalised
+// outputs of the lane's position group.
+template <int NH, int EPLT>
+struct AttnSt {
+    static constexpr int nh = NH;
+    float qr[NH][EPLT];
+    float am[NH], al[NH];
+    float ao[NH][EPLT];
+};
+// The same without the queries (read from LDS at each fold instead).
+template <int NH, int EPLT>
+struct AttnStQ {
+    static constexpr int nh = NH;
+    float am[NH], al[NH];
+    float ao[NH][EPLT];
+};
+
 struct Geo {
     int unit0[ST_NUM], units[ST_NUM], nsl[ST_NUM];
     MkDownGeo dn;
@@ -340,7 +358,9 @@ __device__ __forceinline__ void make_geo(const MkParams &p, int w, int epl, Geo 
 
 // LOGITS = false is the cache-append variant used by prefill: the same step
 // without the final norm, LM head and argmax.
-template <int DT, int GQ, int LPP, bool LOGITS>
+// PMAP selects the position-major attention mapping (groups of four query
+// heads, long splits; chosen per launch by the host from the split length).
+template <int DT, int GQ, int LPP, bool LOGITS, bool PMAP>
 __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const MkParams p) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_[];
     LDS unsigned char *smem = (LDS unsigned char *)smem_;
@@ -1096,11 +1116,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
     const int hc = c % HG, cs = c / HG;
     const float scale = 1.0f / sqrtf((float)d);
     const int e0 = (lane % LPP) * EPL;
-    struct AttnState {
-        float qr[HPC][EPL];          // the lane's dims of this consumer's query heads
-        float am[HPC], al[HPC];      // running max (wave-uniform), running sum
-        float ao[HPC][EPL];          // running unnormalised output (lane's dims)
-    };
+    using AttnState = AttnSt<HPC, EPL>;  // head-major: this consumer's HPC heads
     // Fold NQ chunks of positions (each lane holds one position of each
     // chunk, PPC positions per chunk) into the running state: all scores
     // first, then one running-max update, rescale and V accumulation per
@@ -1108,27 +1124,33 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
     // (the loaders read weights, not the cache, past a split's positions, and
     // the register tail reads a valid row), so 0 * v adds nothing.
     // kget(q, e) / vget(q, e): element e of the lane's K / V piece of chunk q.
-    auto attn_fold = [&](AttnState &A, auto nq_tag, auto &&kget, auto &&vget, const bool *valid) {
+    // qget(h, e): element e of the lane's dims of head h's query.
+    auto attn_fold_q = [&](auto &A, auto nq_tag, auto &&qget, auto &&kget, auto &&vget, const bool *valid) {
         constexpr int NQ = decltype(nq_tag)::value;
-        float sc[NQ][HPC];
+        constexpr int NHS = std::remove_reference_t<decltype(A)>::nh;  // heads held by the state
+        float sc[NQ][NHS];
 #pragma unroll
-        for (int q = 0; q < NQ; ++q)
+        for (int h = 0; h < NHS; ++h) {
+            float qv[EPL];
 #pragma unroll
-            for (int h = 0; h < HPC; ++h) {
+            for (int e = 0; e < EPL; ++e) qv[e] = qget(h, e);
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
                 float t = 0.f;
 #pragma unroll
-                for (int e = 0; e < EPL; ++e) t = fmaf(A.qr[h][e], kget(q, e), t);
+                for (int e = 0; e < EPL; ++e) t = fmaf(qv[e], kget(q, e), t);
                 sc[q][h] = t;
             }
+        }
 #pragma unroll
         for (int q = 0; q < NQ; ++q)
 #pragma unroll
-            for (int h = 0; h < HPC; ++h) {
+            for (int h = 0; h < NHS; ++h) {
                 const float gsum = group_sum<LPP>(sc[q][h]) * scale;  // all lanes take part
                 sc[q][h] = valid[q] ? gsum : -INFINITY;
             }
 #pragma unroll
-        for (int h = 0; h < HPC; ++h) {
+        for (int h = 0; h < NHS; ++h) {
             float mx = sc[0][h];
 #pragma unroll
             for (int q = 1; q < NQ; ++q) mx = fmaxf(mx, sc[q][h]);
@@ -1152,6 +1174,10 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
             }
             A.am[h] = any ? mn : A.am[h];
         }
+    };
+    // The head-major state holds its queries in registers.
+    auto attn_fold = [&](auto &A, auto nq_tag, auto &&kget, auto &&vget, const bool *valid) {
+        attn_fold_q(A, nq_tag, [&](int h, int e) { return A.qr[h][e]; }, kget, vget, valid);
     };
     // This consumer's final state -> its partial records (o over its
     // positions, m, l), one per head, as tagged records.
@@ -1492,19 +1518,131 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
                     ok = gather_to(vec, p.ll_qkv + ((size_t)(l & 1) * p.nkv + kvj) * (GQ + 2) * d, nrec, nullptr, nrec,
                                    tag_of(l));
                 }
-                AttnState A;
-#pragma unroll
-                for (int k = 0; k < HPC; ++k)
-#pragma unroll
-                    for (int e = 0; e < EPL; ++e) A.qr[k][e] = vec[(hc + HG * k) * d + e0 + e];
                 stamp(5 * l + 1, 2);
                 if (!ok) break;
+                stamp(5 * l + 1, 3);
+                // Position-major mapping, for a group of exactly four query
+                // heads and a split of at least attn_pm_slots KV slots (long
+                // contexts): consumer c folds chunks 2c and 2c+1 of every slot
+                // for all four heads, so each K/V chunk is read from LDS once
+                // per workgroup instead of once per head, and each consumer
+                // runs four independent softmax chains.  At the end the four
+                // consumers' partials of each head are merged in LDS (log-sum-
+                // exp) into the same per-head records the head-major mapping
+                // writes.  Otherwise head-major (below).  The two mappings run
+                // separate loops so that only one running state is live.
+                constexpr bool PM_OK = PMAP && GQ == MK_NUM_CONSUMERS;
+                if constexpr (PM_OK) {
+                    {
+                        AttnStQ<GQ, EPL> P;  // the queries stay in vec (LDS)
+#pragma unroll
+                        for (int h = 0; h < GQ; ++h) {
+#pragma unroll
+                            for (int e = 0; e < EPL; ++e) P.ao[h][e] = 0.f;
+                            P.am[h] = -INFINITY;
+                            P.al[h] = 0.f;
+                        }
+                        auto qlds = [&](int h, int e) { return vec[h * d + e0 + e]; };
+                        // End of the split: consumer 0 folds the tail and
+                        // position pos for all heads, every consumer's
+                        // per-head partials go to LDS (after the queries and
+                        // the row of pos in vec), then consumer c merges head c
+                        // and writes its record.
+                        auto finish_pm = [&]() {
+                            if (c == 0 && ntail > 0) {
+                                const bool v1[1] = {tg < ntail};
+                                attn_fold_q(P, std::integral_constant<int, 1>{}, qlds, [&](int, int e) { return kt[e]; },
+                                            [&](int, int e) { return vt[e]; }, v1);
+                            }
+                            if (c == 0 && is_last) {
+                                float kp[EPL], vp[EPL];
+#pragma unroll
+                                for (int e = 0; e < EPL; ++e) {
+                                    kp[e] = vec[GQ * d + e0 + e];
+                                    vp[e] = vec[GQ * d + d + e0 + e];
+                                }
+                                const bool v1[1] = {lane < LPP};
+                                attn_fold_q(P, std::integral_constant<int, 1>{}, qlds, [&](int, int e) { return kp[e]; },
+                                            [&](int, int e) { return vp[e]; }, v1);
+                            }
+                            LDS float *mg = vec + (GQ + 2) * d;  // [consumer][head][d + 2]: o, m, l
+#pragma unroll
+                            for (int h = 0; h < GQ; ++h) {
+                                LDS float *dst = mg + (c * GQ + h) * PREC;
+                                const float lsum = xgroup_sum<LPP>(P.al[h]);
+#pragma unroll
+                                for (int e = 0; e < EPL; ++e) {
+                                    const float ov = xgroup_sum<LPP>(P.ao[h][e]);
+                                    if (lane < LPP) dst[e0 + e] = ov;
+                                }
+                                if (lane == 0) {
+                                    dst[d] = P.am[h];
+                                    dst[d + 1] = lsum;
+                                }
+                            }
+                            if (!csync()) {
+                                ok = false;
+                                return;
+                            }
+                            const int hh = c;  // the head this consumer merges
+                            float M = -INFINITY;
+#pragma unroll
+                            for (int j = 0; j < MK_NUM_CONSUMERS; ++j) M = fmaxf(M, mg[(j * GQ + hh) * PREC + d]);
+                            float wj[MK_NUM_CONSUMERS], Lsum = 0.f;
+#pragma unroll
+                            for (int j = 0; j < MK_NUM_CONSUMERS; ++j) {
+                                const float mj = mg[(j * GQ + hh) * PREC + d];
+                                wj[j] = mj == -INFINITY ? 0.f : __expf(mj - M);
+                                Lsum = fmaf(wj[j], mg[(j * GQ + hh) * PREC + d + 1], Lsum);
+                            }
+                            uint64_t *part = p.ll_part + (((size_t)(l & 1) * p.nkv + kvj) * S_eff + kvs) * GQ * PREC;
+                            const uint32_t tg2 = tag_of(l);
+                            for (int e = lane; e < d; e += 64) {
+                                float ov = 0.f;
+#pragma unroll
+                                for (int j = 0; j < MK_NUM_CONSUMERS; ++j)
+                                    ov = fmaf(wj[j], mg[(j * GQ + hh) * PREC + e], ov);
+                                stll(part + hh * PREC + e, ov, tg2);
+                            }
+                            if (lane == 0) {
+                                stll(part + hh * PREC + d, M, tg2);
+                                stll(part + hh * PREC + d + 1, Lsum, tg2);
+                            }
+                        };
+                        for (int n = 0; n < nsl_kv; ++n) {
+                            barrier();
+                            stamp_step(l, 0);
+                            const LDS unsigned char *kb = ring + js * MK_SLOT_BYTES;
+                            const LDS unsigned char *vb = kb + 8 * MK_CHUNK_BYTES;
+                            u4v kr[2], vr[2];
+                            bool valid[2];
+#pragma unroll
+                            for (int q = 0; q < 2; ++q) {
+                                const int chunk = 2 * c + q;
+                                valid[q] = t0 + n * BP + chunk * PPC + lane / LPP < t1;
+                                kr[q] = *(const LDS u4v *)(kb + chunk * MK_CHUNK_BYTES + lane * 16);
+                                vr[q] = *(const LDS u4v *)(vb + chunk * MK_CHUNK_BYTES + lane * 16);
+                            }
+                            attn_fold_q(P, std::integral_constant<int, 2>{}, qlds,
+                                        [&](int q, int e) { return piece_elem<DT>(kr[q], e); },
+                                        [&](int q, int e) { return piece_elem<DT>(vr[q], e); }, valid);
+                            if (n == nsl_kv - 1) finish_pm();
+                            js = js + 1 == NS ? 0 : js + 1;
+                            stamp_step(l, 1);
+                        }
+                        if (nsl_kv == 0) finish_pm();
+                    }
+                } else {
+                AttnState A;
 #pragma unroll
                 for (int k = 0; k < HPC; ++k) {
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) {
+                        A.qr[k][e] = vec[(hc + HG * k) * d + e0 + e];
+                        A.ao[k][e] = 0.f;
+                    }
                     A.am[k] = -INFINITY;
                     A.al[k] = 0.f;
-#pragma unroll
-                    for (int e = 0; e < EPL; ++e) A.ao[k][e] = 0.f;
                 }
                 auto finish = [&]() {
                     if (fold_extra && ntail > 0) {
@@ -1525,7 +1663,6 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
                     }
                     attn_finish(A, l);
                 };
-                stamp(5 * l + 1, 3);
                 if (nsl_kv == 0) finish();
                 for (int n = 0; n < nsl_kv; ++n) {
                     barrier();
@@ -1551,6 +1688,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
                     js = js + 1 == NS ? 0 : js + 1;
                     stamp_step(l, 1);
                 }
+                }  // head-major
             } else {
                 stamp(5 * l + 1, 3);
             }
@@ -1633,10 +1771,15 @@ namespace {
 typedef void (*KernelFn)(const MkParams);
 
 template <int DT, int GQ, int LPP>
-KernelFn kfn(bool logits) { return logits ? mk_decode_kernel<DT, GQ, LPP, true> : mk_decode_kernel<DT, GQ, LPP, false>; }
+KernelFn kfn(bool logits, bool pmap) {
+    if constexpr (GQ == MK_NUM_CONSUMERS) {
+        if (pmap) return logits ? mk_decode_kernel<DT, GQ, LPP, true, true> : mk_decode_kernel<DT, GQ, LPP, false, true>;
+    }
+    return logits ? mk_decode_kernel<DT, GQ, LPP, true, false> : mk_decode_kernel<DT, GQ, LPP, false, false>;
+}
 
-KernelFn pick(int dtype, int gq, int lpp, bool logits) {
-#define MK_PICK(DT_, GQ_, LPP_) if (dtype == DT_ && gq == GQ_ && lpp == LPP_) return kfn<DT_, GQ_, LPP_>(logits);
+KernelFn pick(int dtype, int gq, int lpp, bool logits, bool pmap) {
+#define MK_PICK(DT_, GQ_, LPP_) if (dtype == DT_ && gq == GQ_ && lpp == LPP_) return kfn<DT_, GQ_, LPP_>(logits, pmap);
     MK_PICK(1, 1, 8) MK_PICK(1, 2, 8) MK_PICK(1, 4, 8) MK_PICK(1, 8, 8)
     MK_PICK(1, 1, 16) MK_PICK(1, 2, 16) MK_PICK(1, 4, 16) MK_PICK(1, 8, 16)
     MK_PICK(0, 1, 8) MK_PICK(0, 2, 8) MK_PICK(0, 4, 8) MK_PICK(0, 8, 8)
@@ -1658,7 +1801,12 @@ extern "C" int mk_launch_decode(const MkParams *p, int dtype, int cooperative, v
     const int eb = dtype ? 2 : 4;
     const int lpp = p->d * eb / 16;
     const int gq = p->nh / p->nkv;
-    KernelFn fn = pick(dtype, gq, lpp, p->want_logits != 0);
+    // per-length attention mapping: position-major when a split holds at
+    // least attn_pm_slots whole KV slots (BP positions each)
+    const int bp = 8 * (64 / lpp);
+    const int per = (p->pos + p->splits - 1) / p->splits;
+    const bool pmap = gq == MK_NUM_CONSUMERS && per / bp >= p->attn_pm_slots;
+    KernelFn fn = pick(dtype, gq, lpp, p->want_logits != 0, pmap);
     if (!fn) return (int)hipErrorInvalidValue;
     // the dynamic-LDS limit of every instantiation was raised to MK_LDS_LIMIT
     // when the handle was created (mk_kernel_max_blocks_per_cu)
@@ -1676,8 +1824,8 @@ extern "C" int mk_launch_decode(const MkParams *p, int dtype, int cooperative, v
 
 extern "C" int mk_kernel_max_blocks_per_cu(int dtype, int gq, int lpp, int lds) {
     int best = 1 << 30;
-    for (int logits = 0; logits < 2; ++logits) {
-        KernelFn fn = pick(dtype, gq, lpp, logits != 0);
+    for (int k = 0; k < 4; ++k) {
+        KernelFn fn = pick(dtype, gq, lpp, (k & 1) != 0, (k & 2) != 0);
         if (!fn) return 0;
         if (hipFuncSetAttribute((const void *)fn, hipFuncAttributeMaxDynamicSharedMemorySize, MK_LDS_LIMIT) !=
             hipSuccess)

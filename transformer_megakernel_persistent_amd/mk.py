@@ -50,7 +50,7 @@ class Tuning(ctypes.Structure):
     _fields_ = [("grid", ctypes.c_int32), ("ring_slots", ctypes.c_int32), ("attn_splits", ctypes.c_int32),
                 ("timeout_ms", ctypes.c_int32), ("cooperative", ctypes.c_int32), ("trace", ctypes.c_int32),
                 ("prefetch_depth", ctypes.c_int32), ("stage_drain", ctypes.c_int32),
-                ("prefill_chunk", ctypes.c_int32)]
+                ("prefill_chunk", ctypes.c_int32), ("attn_pm_slots", ctypes.c_int32)]
 
 
 class Info(ctypes.Structure):

@@ -39,9 +39,16 @@ def _rows(directory: str, suffix: str):
     return out
 
 
+def _template_args(name: str):
+    a, b = name.find("<"), name.find(">")
+    return [x.strip() for x in name[a + 1:b].split(",")] if 0 <= a < b else []
+
+
 def _is_decode(name: str) -> bool:
-    # the token-producing instantiation has LOGITS=true; prefill launches use false
-    return DECODE_TAG in name and "true" in name
+    # the token-producing instantiation: its fourth template argument (LOGITS)
+    # is true; decode launches that fill the cache have false
+    args = _template_args(name)
+    return DECODE_TAG in name and len(args) >= 4 and args[3] == "true"
 
 
 def _is_copy(name: str) -> bool:
@@ -92,6 +99,8 @@ def main(argv=None):
     ap.add_argument("--command-write", required=True)
     ap.add_argument("--command-trace", required=True)
     ap.add_argument("--bench-json", default=None, help="the JSON line the traced bench run printed")
+    ap.add_argument("--dram", default=None, help="CSV directory of a --pmc TCC_EA0_RDREQ_DRAM_sum run (optional)")
+    ap.add_argument("--command-dram", default=None)
     args = ap.parse_args(argv)
 
     sys.path.insert(0, ROOT)
@@ -118,6 +127,15 @@ def main(argv=None):
            "fetch_scale": f_scale, "write_scale": w_scale, "decode_dispatches": [n_f, n_w],
            "algorithmic_bytes_per_launch": alg, "commands": {"fetch": args.command_fetch,
                                                              "write": args.command_write}}
+    if args.dram:
+        # read requests the memory-side caches passed on to DRAM, summed over
+        # the L2 channels; each request moves 64 bytes (32-byte requests are
+        # counted by a separate counter on this chip and ignored here)
+        d_dec, d_cpy, n_d, n_dc, _ = counter_per_dispatch(args.dram, "TCC_EA0_RDREQ_DRAM_sum")
+        rec["dram_read_requests_per_launch"] = d_dec
+        rec["dram_read_requests_per_copy"] = d_cpy
+        rec["dram_read_bytes_per_launch_scaled"] = d_dec * (args.copy_bytes / d_cpy) if d_cpy else None
+        rec["commands"]["dram"] = args.command_dram
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     with open(os.path.join(ROOT, "profiles", f"counters_{args.workload}.json"), "w") as f:
         json.dump(rec, f, indent=1)
@@ -150,6 +168,13 @@ def main(argv=None):
               f"| total | | {fetch_b + write_b:.4g} |", "",
               f"Algorithmic bytes per launch (every weight once + K/V rows of positions 0..{pos0}): {alg:.4g}; "
               f"measured / algorithmic = {(fetch_b + write_b) / alg:.3f}.", ""]
+    if args.dram:
+        lines += ["## DRAM read requests (rocprofv3 --pmc TCC_EA0_RDREQ_DRAM_sum)", "",
+                  f"Command: `{args.command_dram}`", "",
+                  f"Per decode launch {rec['dram_read_requests_per_launch']:.4g} requests; per calibration copy "
+                  f"{rec['dram_read_requests_per_copy']:.4g}; scaled by the copy's {args.copy_bytes} bytes: "
+                  f"{rec['dram_read_bytes_per_launch_scaled']:.4g} bytes read from DRAM per launch "
+                  f"({rec['dram_read_bytes_per_launch_scaled'] / alg:.3f} x the algorithmic bytes).", ""]
     out_md = os.path.join(ROOT, "profiles", f"{DECODE_TAG}_{args.workload}.md")
     with open(out_md, "w") as f:
         f.write("\n".join(lines))
