@@ -25,7 +25,7 @@ def resources():
     if not need:
         with open(mkbuild.RESOURCES) as f:
             need = json.load(f).get("sources_hash") != mkbuild.sources_hash()
-    if need:  # stale or missing: rebuild (about two minutes)
+    if need:  # stale or missing: rebuild (about a minute)
         mkbuild.build()
     with open(mkbuild.RESOURCES) as f:
         rec = json.load(f)

@@ -1,5 +1,9 @@
 """Build libmk.so (the C-ABI library) with hipcc for gfx950, in-tree.
 
+Every source compiles to an object in _build/ (in parallel), then one link.
+mk_kernel.hip compiles several times: once per (dtype, query-group) part of
+the decode kernel's instantiations, and once for the host launch code.
+
 The compiler's per-kernel resource report (VGPRs, SGPRs, scratch bytes per
 lane, occupancy) is saved beside the library as libmk.resources.json, keyed
 by a hash of the sources it was built from; tests/test_kernel_resources.py
@@ -13,26 +17,28 @@ import os
 import re
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")  # the public C ABI header
 LIB = os.path.join(HERE, "libmk.so")
 RESOURCES = os.path.join(HERE, "libmk.resources.json")
+OBJDIR = os.path.join(os.path.dirname(HERE), "_build")
 SOURCES = ["mk_api.hip", "mk_kernel.hip", "mk_prelayout.hip", "mk_prefill.hip"]
 HEADERS = [os.path.join(CSRC, "mk_internal.h"), os.path.join(INCLUDE, "mk.h")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+# (dtype, query heads per KV head) parts of the decode kernel's instantiations
+KERNEL_PARTS = [(dt, gq) for dt in (0, 1) for gq in (1, 2, 4, 8)]
 
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # packed FP32 instructions stay off (they are emitted only by the compiler)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
-    # per-kernel register / scratch report on stderr (parsed below)
-    "-Rpass-analysis=kernel-resource-usage",
 ]
-
-_REMARK = re.compile(r"remark: ([^:]*(?:\.hip|\.h)):\d+:\d+: *(?:remark: )?\s*([A-Za-z][A-Za-z /\[\]]*?)\s*:\s*(\S+)")
+# per-kernel register / scratch report on stderr (parsed below)
+REMARKS = "-Rpass-analysis=kernel-resource-usage"
 
 
 def sources_hash() -> str:
@@ -63,18 +69,43 @@ def parse_resources(text: str) -> list:
     return kernels
 
 
+def _jobs():
+    jobs = []
+    for s in SOURCES:
+        jobs.append((s, [], os.path.join(OBJDIR, s.replace(".hip", ".o"))))
+    for dt, gq in KERNEL_PARTS:
+        jobs.append(("mk_kernel.hip", ["-DMK_KERNEL_PART", f"-DMK_PART_DT={dt}", f"-DMK_PART_GQ={gq}"],
+                     os.path.join(OBJDIR, f"mk_kernel_part_{dt}_{gq}.o")))
+    return jobs
+
+
 def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    os.makedirs(OBJDIR, exist_ok=True)
+
+    def compile_one(job):
+        src, defs, obj = job
+        cmd = [HIPCC, *FLAGS, REMARKS, *defs, "-I", INCLUDE, "-c", "-o", obj, os.path.join(CSRC, src)]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        return subprocess.run(cmd, capture_output=True, text=True), src, defs
+
+    jobs = _jobs()
+    with ThreadPoolExecutor(max_workers=min(len(jobs), max(1, os.cpu_count() or 1))) as ex:
+        results = list(ex.map(compile_one, jobs))
+    remarks = []
+    for res, src, defs in results:
+        if res.returncode != 0:
+            sys.stderr.write(res.stdout + res.stderr)
+            raise RuntimeError(f"hipcc failed on {src} {' '.join(defs)}")
+        remarks.append(res.stderr)
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-o", tmp, *srcs]
-    if verbose:
-        print(" ".join(cmd), flush=True)
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *[j[2] for j in jobs]]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed building libmk.so")
+        raise RuntimeError("linking libmk.so failed")
     os.replace(tmp, LIB)
-    kernels = parse_resources(res.stderr)
+    kernels = parse_resources("\n".join(remarks))
     with open(RESOURCES, "w") as f:
         json.dump({"sources_hash": sources_hash(), "flags": FLAGS, "kernels": kernels}, f, indent=1)
     return LIB

@@ -1766,6 +1766,36 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
     MK_WAIT_VM0();
 }
 
+// ---- instantiations and host-side launch ----------------------------------
+// The kernel is instantiated for every (dtype, group, lanes per cache row,
+// LOGITS, position-major) combination the host can pick.  The build compiles
+// this file once per (dtype, group) part with MK_KERNEL_PART, MK_PART_DT and
+// MK_PART_GQ defined, each part instantiating its kernels, and once without,
+// for the host code below, which only declares them (extern template); the
+// parts compile in parallel.
+#define MK_FOR_LPP_LOGITS(X, DT_, GQ_, PM_) \
+    X(DT_, GQ_, 8, true, PM_) X(DT_, GQ_, 8, false, PM_) X(DT_, GQ_, 16, true, PM_) X(DT_, GQ_, 16, false, PM_)
+// position-major instantiations exist for groups of four query heads only
+#define MK_FOR_PM(X, DT_, GQ_) MK_FOR_LPP_LOGITS(X, DT_, GQ_, false) if_gq4_##GQ_(MK_FOR_LPP_LOGITS(X, DT_, GQ_, true))
+#define if_gq4_1(...)
+#define if_gq4_2(...)
+#define if_gq4_4(...) __VA_ARGS__
+#define if_gq4_8(...)
+
+#ifdef MK_KERNEL_PART
+#define MK_INST(DT_, GQ_, LPP_, LG_, PM_) \
+    template __global__ void mk_decode_kernel<DT_, GQ_, LPP_, LG_, PM_>(const MkParams);
+#define MK_PART_EXPAND(DT_, GQ_) MK_FOR_PM(MK_INST, DT_, GQ_)
+#define MK_PART_EXPAND2(DT_, GQ_) MK_PART_EXPAND(DT_, GQ_)
+MK_PART_EXPAND2(MK_PART_DT, MK_PART_GQ)
+#else
+#define MK_EXTERN(DT_, GQ_, LPP_, LG_, PM_) \
+    extern template __global__ void mk_decode_kernel<DT_, GQ_, LPP_, LG_, PM_>(const MkParams);
+#define MK_ALL_PARTS(X) \
+    MK_FOR_PM(X, 0, 1) MK_FOR_PM(X, 0, 2) MK_FOR_PM(X, 0, 4) MK_FOR_PM(X, 0, 8) \
+    MK_FOR_PM(X, 1, 1) MK_FOR_PM(X, 1, 2) MK_FOR_PM(X, 1, 4) MK_FOR_PM(X, 1, 8)
+MK_ALL_PARTS(MK_EXTERN)
+
 // ---- host-side launch ---------------------------------------------------
 namespace {
 typedef void (*KernelFn)(const MkParams);
@@ -1837,3 +1867,4 @@ extern "C" int mk_kernel_max_blocks_per_cu(int dtype, int gq, int lpp, int lds) 
     }
     return best;
 }
+#endif  // MK_KERNEL_PART
