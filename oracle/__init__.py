@@ -6,8 +6,8 @@ shares no code with the GPU library.  The arithmetic lives in ``oracle.c``
 (plain float64 C); this module only marshals numpy arrays.
 
 Parity status of each function (how it is pinned, see tests/test_oracle_*.py):
-  bf16 rounding, rmsnorm, gemv, rope, softmax, attend, silu, argmax,
-  decode_step, prefill: pinned by closed forms, hand-worked examples, library
+  bf16 rounding, rmsnorm, gemv, gemv_q8, rope, softmax, attend, silu, argmax,
+  decode_step (all three dtypes), prefill: pinned by closed forms, hand-worked examples, library
   special cases and invariants.  Full-model logits beyond those pins have no
   printed values on the pages to compare against.
 """
@@ -31,7 +31,8 @@ class _Model(ctypes.Structure):
     _fields_ = [("n_layers", ctypes.c_int32), ("hidden", ctypes.c_int32), ("n_heads", ctypes.c_int32),
                 ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("ffn", ctypes.c_int32),
                 ("vocab", ctypes.c_int32), ("max_seq", ctypes.c_int32), ("rms_eps", ctypes.c_double),
-                ("rope_theta", ctypes.c_double), ("dtype", ctypes.c_int32), ("tied", ctypes.c_int32)]
+                ("rope_theta", ctypes.c_double), ("dtype", ctypes.c_int32), ("tied", ctypes.c_int32),
+                ("scales", ctypes.c_void_p)]
 
 
 def build(force: bool = True) -> str:
@@ -56,6 +57,7 @@ def _load():
             "or_bf16_from_f64": ([dbl], ctypes.c_uint16),
             "or_rmsnorm": ([v, i32, v, i32, dbl, v], None),
             "or_gemv": ([v, i32, i32, i32, v, v], None),
+            "or_gemv_q8": ([v, v, i32, i32, v, v], None),
             "or_rope": ([v, i32, i32, i32, dbl], None),
             "or_softmax": ([v, i32, v], None),
             "or_attend": ([v, v, v, i32, i32, i32, v], None),
@@ -129,6 +131,20 @@ def gemv(W: np.ndarray, h) -> np.ndarray:
     return y
 
 
+def gemv_q8(q: np.ndarray, s: np.ndarray, h) -> np.ndarray:
+    """Weight-only INT8 product: int8 codes q [rows][cols], float32 scales
+    s [rows]; returns (s[:, None] * q) @ h in float64."""
+    q = np.ascontiguousarray(q)
+    s = np.ascontiguousarray(s)
+    assert q.dtype == np.int8 and s.dtype == np.float32
+    h = _f64(h)
+    rows, cols = q.shape
+    assert h.size == cols and s.shape == (rows,)
+    y = np.empty(rows, dtype=np.float64)
+    _load().or_gemv_q8(_p(q), _p(s), rows, cols, _p(h), _p(y))
+    return y
+
+
 def rope(v, n_heads: int, head_dim: int, pos: int, theta: float) -> np.ndarray:
     v = _f64(v).copy()
     assert v.size == n_heads * head_dim
@@ -180,35 +196,58 @@ LAYER_KINDS = ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate", "w_up"
 
 class Model:
     """Shapes plus host weights (numpy, row-major [out][in]) and the oracle's
-    own KV cache arrays [n_layers][n_kv_heads][max_seq][head_dim]."""
+    own KV cache arrays [n_layers][n_kv_heads][max_seq][head_dim].
+
+    shape["dtype"] is "f32", "bf16" or "w8".  A "w8" model (weight-only
+    INT8) holds each matrix as int8 codes under its usual key and its
+    float32 per-row scales under "<key>_scale" (the LM head as "lm_head" and
+    "lm_head_scale"; such a model is never tied); the embedding and the gains
+    are bf16 bits, and so is the cache."""
 
     def __init__(self, shape: dict, weights: dict, max_seq: int):
         self.shape = dict(shape)
         self.max_seq = int(max_seq)
-        dt = 1 if shape["dtype"] == "bf16" else 0
-        self._m = _Model(shape["n_layers"], shape["hidden"], shape["n_heads"], shape["n_kv_heads"],
-                         shape["head_dim"], shape["ffn"], shape["vocab"], self.max_seq,
-                         float(shape["rms_eps"]), float(shape["rope_theta"]), dt, int(bool(shape["tied"])))
+        dt = {"f32": 0, "bf16": 1, "w8": 2}[shape["dtype"]]
+        q8 = dt == 2
+        assert not (q8 and shape["tied"]), "a weight-only INT8 model has its own LM head"
         self._keep = []
-        ptrs = []
+        ptrs, sptrs = [], []
 
-        def add(a):
+        def add(a, matrix=False, scale=None):
             if a is None:
                 ptrs.append(None)
+                sptrs.append(None)
                 return
             a = np.ascontiguousarray(a)
-            assert _dt(a) == dt, "weight dtype must match the model dtype"
+            if q8 and matrix:
+                assert a.dtype == np.int8, "INT8 model matrices are int8 codes"
+                sc = np.ascontiguousarray(scale, dtype=np.float32)
+                assert sc.shape == (a.shape[0],), "one scale per output row"
+                self._keep.append(sc)
+                sptrs.append(sc.ctypes.data)
+            else:
+                assert _dt(a) == min(dt, 1), "weight dtype must match the model dtype"
+                sptrs.append(None)
             self._keep.append(a)
             ptrs.append(a.ctypes.data)
 
         add(weights["embed"])
         add(weights["final_norm"])
-        add(None if shape["tied"] else weights["lm_head"])
+        if shape["tied"]:
+            add(None)
+        else:
+            add(weights["lm_head"], True, weights.get("lm_head_scale"))
         assert len(weights["layers"]) == shape["n_layers"]
         for lw in weights["layers"]:
             for k in LAYER_KINDS:
-                add(lw[k])
+                mat = k not in ("attn_norm", "ffn_norm")
+                add(lw[k], mat, lw.get(k + "_scale") if mat else None)
         self._ptrs = (ctypes.c_void_p * len(ptrs))(*ptrs)
+        self._sptrs = (ctypes.c_void_p * len(sptrs))(*sptrs)
+        self._m = _Model(shape["n_layers"], shape["hidden"], shape["n_heads"], shape["n_kv_heads"],
+                         shape["head_dim"], shape["ffn"], shape["vocab"], self.max_seq,
+                         float(shape["rms_eps"]), float(shape["rope_theta"]), dt, int(bool(shape["tied"])),
+                         ctypes.cast(self._sptrs, ctypes.c_void_p) if q8 else None)
         npdt = np.uint16 if dt else np.float32
         cache_shape = (shape["n_layers"], shape["n_kv_heads"], self.max_seq, shape["head_dim"])
         self.k = np.zeros(cache_shape, dtype=npdt)

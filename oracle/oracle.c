@@ -38,8 +38,13 @@
 typedef struct {
     int32_t n_layers, hidden, n_heads, n_kv_heads, head_dim, ffn, vocab, max_seq;
     double rms_eps, rope_theta;
-    int32_t dtype; /* 0: float32 weights and KV cache; 1: bfloat16 */
-    int32_t tied;  /* 1: the LM head is the token-embedding matrix */
+    int32_t dtype; /* 0: float32 weights and KV cache; 1: bfloat16; 2: weight-only INT8 (the
+                      matrices are int8 codes with one float32 scale per output row; the
+                      embedding, the norm gains and the KV cache are bfloat16) */
+    int32_t tied;  /* 1: the LM head is the token-embedding matrix (dtype 0 and 1 only) */
+    /* dtype 2: per-row scales, a table indexed like the weight table below
+       (entries of the LM head and the seven layer matrices; others unused) */
+    const float *const *scales;
 } or_model;
 
 /* Weight pointer table: [0] embed [V][H], [1] final norm gain [H],
@@ -125,6 +130,23 @@ void or_gemv(const void *W, int dtype, int rows, int cols, const double *h, doub
     }
 }
 
+/* Weight-only INT8 matrix-vector product.  The stored matrix is int8 codes
+   q [rows][cols] and one float32 scale per output row, and the weight it
+   stands for is W[r][c] = s[r] * q[r][c] (dequantisation; the quantised
+   models that www.stapisi.com/news/3904786 section 6.1 names stream these
+   codes instead of 16-bit weights).  y = W h, each y_r one sequential sum
+   over c of (s_r * q_rc) * h_c in float64. */
+void or_gemv_q8(const int8_t *q, const float *s, int rows, int cols, const double *h, double *y) {
+#pragma omp parallel for schedule(static)
+    for (int r = 0; r < rows; ++r) {
+        double acc = 0.0;
+        const double sr = (double)s[r];
+        size_t base = (size_t)r * (size_t)cols;
+        for (int c = 0; c < cols; ++c) acc += (sr * (double)q[base + (size_t)c]) * h[c];
+        y[r] = acc;
+    }
+}
+
 /* Rotary position encoding, in place, on n_heads vectors of length d laid
    out back to back.  Pairing is "rotate half": element i is paired with
    i + d/2 for i < d/2, and the pair is rotated by the angle
@@ -203,6 +225,8 @@ static size_t kv_off(const or_model *m, int layer, int head, int pos) {
  *              x += Wo o;
  *              h = rmsnorm(x, g_ffn); x += Wd (silu(Wg h) * (Wu h))
  *   logits = W_lm rmsnorm(x, g_final)      (skipped when logits == NULL)
+ * Every "W h" is or_gemv, or or_gemv_q8 on the dequantised matrix of a
+ * weight-only INT8 model (dtype 2; its LM head is its own int8 matrix).
  * The cache arrays are [n_layers][n_kv_heads][max_seq][head_dim].
  * Returns 0, or a negative code for an out-of-range token/position or an
  * invalid shape.
@@ -210,10 +234,18 @@ static size_t kv_off(const or_model *m, int layer, int head, int pos) {
 int or_decode_step(const or_model *m, const void *const *w, void *kc, void *vc, int token, int pos,
                    double *logits) {
     const int H = m->hidden, nh = m->n_heads, nkv = m->n_kv_heads, d = m->head_dim, F = m->ffn;
-    const int dt = m->dtype;
+    const int q8 = m->dtype == 2;
+    const int dt = q8 ? 1 : m->dtype; /* storage of the embedding, gains and cache */
     if (token < 0 || token >= m->vocab) return -1;
     if (pos < 0 || pos >= m->max_seq) return -2;
     if (nkv <= 0 || nh % nkv != 0 || d % 2 != 0) return -3;
+    if (m->dtype < 0 || m->dtype > 2 || (q8 && (m->tied || !m->scales))) return -3;
+    /* matrix i of the weight table times h: plain or dequantised */
+#define MAT(i, rows, cols, h, y)                                                              \
+    do {                                                                                      \
+        if (q8) or_gemv_q8((const int8_t *)w[i], m->scales[i], (rows), (cols), (h), (y));    \
+        else or_gemv(w[i], dt, (rows), (cols), (h), (y));                                    \
+    } while (0)
     const int group = nh / nkv;
 
     double *x = (double *)calloc((size_t)H, sizeof(double));
@@ -229,11 +261,12 @@ int or_decode_step(const or_model *m, const void *const *w, void *kc, void *vc, 
     for (int i = 0; i < H; ++i) x[i] = wload(w[W_EMBED], dt, (size_t)token * H + i);
 
     for (int l = 0; l < m->n_layers; ++l) {
-        const void *const *lw = w + W_LAYER0 + (size_t)W_PER_LAYER * l;
+        const size_t l0 = W_LAYER0 + (size_t)W_PER_LAYER * l;
+        const void *const *lw = w + l0;
         or_rmsnorm(x, H, lw[L_ATTN_NORM], dt, m->rms_eps, h);
-        or_gemv(lw[L_WQ], dt, nh * d, H, h, q);
-        or_gemv(lw[L_WK], dt, nkv * d, H, h, k);
-        or_gemv(lw[L_WV], dt, nkv * d, H, h, v);
+        MAT(l0 + L_WQ, nh * d, H, h, q);
+        MAT(l0 + L_WK, nkv * d, H, h, k);
+        MAT(l0 + L_WV, nkv * d, H, h, v);
         or_rope(q, nh, d, pos, m->rope_theta);
         or_rope(k, nkv, d, pos, m->rope_theta);
         for (int j = 0; j < nkv; ++j)
@@ -250,21 +283,22 @@ int or_decode_step(const or_model *m, const void *const *w, void *kc, void *vc, 
             or_attend(q + (size_t)i * d, (const char *)kc + base, (const char *)vc + base, dt, d, pos + 1,
                       o + (size_t)i * d);
         }
-        or_gemv(lw[L_WO], dt, H, nh * d, o, t);
+        MAT(l0 + L_WO, H, nh * d, o, t);
         for (int i = 0; i < H; ++i) x[i] += t[i];
 
         or_rmsnorm(x, H, lw[L_FFN_NORM], dt, m->rms_eps, h);
-        or_gemv(lw[L_GATE], dt, F, H, h, g);
-        or_gemv(lw[L_UP], dt, F, H, h, u);
+        MAT(l0 + L_GATE, F, H, h, g);
+        MAT(l0 + L_UP, F, H, h, u);
         for (int i = 0; i < F; ++i) g[i] = or_silu(g[i]) * u[i];
-        or_gemv(lw[L_DOWN], dt, H, F, g, t);
+        MAT(l0 + L_DOWN, H, F, g, t);
         for (int i = 0; i < H; ++i) x[i] += t[i];
     }
     if (logits) {
         or_rmsnorm(x, H, w[W_FINAL_NORM], dt, m->rms_eps, h);
-        const void *lm = m->tied ? w[W_EMBED] : w[W_LM_HEAD];
-        or_gemv(lm, dt, m->vocab, H, h, logits);
+        if (m->tied) or_gemv(w[W_EMBED], dt, m->vocab, H, h, logits);
+        else MAT(W_LM_HEAD, m->vocab, H, h, logits);
     }
+#undef MAT
     free(x); free(h); free(q); free(k); free(v); free(o); free(t); free(g); free(u);
     return 0;
 }

@@ -12,6 +12,15 @@ the standard deviation), stored as float32 for the tiny model and as bfloat16
 (round-to-nearest-even) otherwise.  Norm gains are 1.0 unless ``gains="random"``
 (1 + 0.1 * N(0,1), used by tests so a dropped gain cannot hide).  Prompt tokens
 are uniform over [0, vocab).
+
+Weight-only INT8 workloads (dtype "w8") keep the embedding, the gains and the
+KV cache in bfloat16 and give every matrix (the LM head included; such a
+model is never tied) as int8 codes with one float32 scale per output row.
+The codes are N(0, 32^2) draws rounded to integers and clamped to
+[-127, 127] -- the shape of the codes that max-abs quantisation of a Gaussian
+row leaves -- and the scales are uniform in [0.75, 1.25) * 0.02 / 32, so the
+dequantised weights have about the 0.02 standard deviation of the other
+workloads while every row has its own scale.
 """
 from __future__ import annotations
 
@@ -49,6 +58,9 @@ def _load():
         lib.synth_uniform_int.argtypes = [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_uint64,
                                           ctypes.c_uint32, ctypes.c_void_p]
         lib.synth_uniform_int.restype = None
+        lib.synth_uniform_f32.argtypes = [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_uint64,
+                                          ctypes.c_double, ctypes.c_double, ctypes.c_void_p]
+        lib.synth_uniform_f32.restype = None
         lib.synth_philox4x32_10.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         lib.synth_philox4x32_10.restype = None
         _lib = lib
@@ -71,7 +83,7 @@ class ModelConfig:
     vocab: int
     rms_eps: float
     rope_theta: float
-    dtype: str            # "f32" or "bf16": weights and KV cache
+    dtype: str            # "f32" or "bf16": weights and KV cache; "w8": int8 matrices, bf16 rest
     tied: bool            # LM head shares the token-embedding matrix
     context: int          # prompt tokens prefilled into the KV cache
     decode_steps: int     # greedy decode steps after the prompt
@@ -93,15 +105,24 @@ class ModelConfig:
 
     @property
     def wbytes(self) -> int:
+        """Bytes per element of the embedding, the gains and the KV cache."""
         return 4 if self.dtype == "f32" else 2
 
+    @property
+    def mbytes(self) -> int:
+        """Bytes per element of the layer matrices and the LM head."""
+        return 1 if self.dtype == "w8" else self.wbytes
+
     def weight_bytes_per_step(self) -> int:
-        """Every weight read once per step: all layer matrices and gains, the
-        final gain, the LM head and one embedding row."""
+        """Every weight read once per step: all layer matrices (with their
+        per-row scales for INT8) and gains, the final gain, the LM head and
+        one embedding row."""
         H, F = self.hidden, self.ffn
-        per_layer = (self.q_dim + 2 * self.kv_dim) * H + H * self.q_dim + 3 * H * F + 2 * H
-        elems = self.n_layers * per_layer + self.vocab * H + H + H
-        return elems * self.wbytes
+        mat = (self.q_dim + 2 * self.kv_dim) * H + H * self.q_dim + 3 * H * F
+        rows = (self.q_dim + 2 * self.kv_dim) + H + 2 * F + H  # output rows of the seven matrices
+        per_layer = mat * self.mbytes + 2 * H * self.wbytes + (4 * rows if self.dtype == "w8" else 0)
+        head = self.vocab * H * self.mbytes + (4 * self.vocab if self.dtype == "w8" else 0)
+        return self.n_layers * per_layer + head + 2 * H * self.wbytes
 
     def kv_read_bytes(self, pos: int) -> int:
         """K and V bytes read by attention at decode position pos (0..pos)."""
@@ -120,15 +141,20 @@ CONFIGS = {
     "llama8b": ModelConfig("llama8b", 32, 4096, 32, 8, 128, 14336, 128256, 1e-5, 500000.0, "bf16", False, 2048, 128),
     "llama1b_32k": ModelConfig("llama1b_32k", 16, 2048, 32, 8, 64, 8192, 128256, 1e-5, 500000.0, "bf16", True, 32768, 64),
     "llama70b": ModelConfig("llama70b", 80, 8192, 64, 8, 128, 28672, 128256, 1e-5, 500000.0, "bf16", False, 4096, 32),
+    # weight-only INT8 versions of the 1B and 8B shapes (own int8 LM head)
+    "llama1b_w8": ModelConfig("llama1b_w8", 16, 2048, 32, 8, 64, 8192, 128256, 1e-5, 500000.0, "w8", False, 2048, 128),
+    "llama8b_w8": ModelConfig("llama8b_w8", 32, 4096, 32, 8, 128, 14336, 128256, 1e-5, 500000.0, "w8", False, 2048, 128),
 }
 
 WEIGHT_STD = 0.02
+CODE_STD = 32.0  # int8 codes of the "w8" workloads
 
 # Stream ids: one per tensor so each can be regenerated on its own.
 LAYER_KINDS = ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate", "w_up", "w_down")
 _STREAM_EMBED, _STREAM_FINAL_NORM, _STREAM_LM_HEAD = 1, 2, 3
 _STREAM_TOKENS = 0x70000000
 _STREAM_KV = 0x60000000
+_STREAM_SCALE = 0x50000000  # + the matrix's stream: its per-row INT8 scales
 
 
 def layer_stream(layer: int, kind: str) -> int:
@@ -151,16 +177,25 @@ def _code(cfg: ModelConfig) -> int:
     return 0 if cfg.dtype == "f32" else 1
 
 
+_STORE = {"f32": (np.float32, 0), "bf16": (np.uint16, 1), "i8": (np.int8, 2)}
+
+
 def normal(seed: int, stream: int, shape, std: float, mean: float = 0.0, dtype: str = "bf16",
            out: np.ndarray | None = None, offset: int = 0) -> np.ndarray:
-    """mean + std*N(0,1) for elements [offset, offset+size) of a stream."""
+    """mean + std*N(0,1) for elements [offset, offset+size) of a stream,
+    stored as dtype "f32", "bf16" (bits) or "i8" (rounded, clamped codes)."""
     n = int(np.prod(shape))
-    npdt = np.float32 if dtype == "f32" else np.uint16
+    npdt, code = _STORE[dtype]
     if out is None:
         out = np.empty(shape, dtype=npdt)
     assert out.dtype == npdt and out.size == n and out.flags["C_CONTIGUOUS"]
-    _load().synth_normal(seed, stream, offset, n, mean, std, 0 if dtype == "f32" else 1,
-                         out.ctypes.data_as(ctypes.c_void_p))
+    _load().synth_normal(seed, stream, offset, n, mean, std, code, out.ctypes.data_as(ctypes.c_void_p))
+    return out
+
+
+def uniform_f32(seed: int, stream: int, n: int, lo: float, hi: float) -> np.ndarray:
+    out = np.empty(n, dtype=np.float32)
+    _load().synth_uniform_f32(seed, stream, 0, n, lo, hi, out.ctypes.data_as(ctypes.c_void_p))
     return out
 
 
@@ -180,13 +215,41 @@ def gen_tensor(cfg: ModelConfig, seed: int, name: str, layer: int | None = None,
         shape, stream, is_gain = (H,), _STREAM_FINAL_NORM, True
     else:
         raise KeyError(name)
+    store = "f32" if cfg.dtype == "f32" else "bf16"  # embedding, gains
     if is_gain and gains == "ones":
         arr = np.empty(shape, dtype=_np_dtype(cfg)) if out is None else out
         arr[...] = 1.0 if cfg.dtype == "f32" else 0x3F80  # bf16 bits of 1.0
         return arr
     if is_gain:
-        return normal(seed, stream, shape, 0.1, 1.0, cfg.dtype, out)
-    return normal(seed, stream, shape, WEIGHT_STD, 0.0, cfg.dtype, out)
+        return normal(seed, stream, shape, 0.1, 1.0, store, out)
+    if cfg.dtype == "w8" and name != "embed":  # a matrix: int8 codes
+        return normal(seed, stream, shape, CODE_STD, 0.0, "i8", out)
+    return normal(seed, stream, shape, WEIGHT_STD, 0.0, store, out)
+
+
+def gen_scale(cfg: ModelConfig, seed: int, name: str, layer: int | None = None) -> np.ndarray:
+    """Per-row float32 scales of an INT8 matrix ("w8" workloads)."""
+    assert cfg.dtype == "w8"
+    if layer is not None:
+        rows, stream = layer_shapes(cfg)[name][0], layer_stream(layer, name)
+    elif name == "lm_head":
+        rows, stream = cfg.vocab, _STREAM_LM_HEAD
+    else:
+        raise KeyError(name)
+    base = WEIGHT_STD / CODE_STD
+    return uniform_f32(seed, _STREAM_SCALE + stream, rows, 0.75 * base, 1.25 * base)
+
+
+MATRIX_KINDS = ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")
+
+
+def gen_layer(cfg: ModelConfig, seed: int, layer: int, gains: str = "ones") -> dict:
+    """One layer's tensors (and, for "w8", the matrices' "<kind>_scale")."""
+    lw = {k: gen_tensor(cfg, seed, k, layer=layer, gains=gains) for k in LAYER_KINDS}
+    if cfg.dtype == "w8":
+        for k in MATRIX_KINDS:
+            lw[k + "_scale"] = gen_scale(cfg, seed, k, layer)
+    return lw
 
 
 def gen_weights(cfg: ModelConfig, seed: int = 0, gains: str = "ones") -> dict:
@@ -195,8 +258,9 @@ def gen_weights(cfg: ModelConfig, seed: int = 0, gains: str = "ones") -> dict:
     w = {"embed": gen_tensor(cfg, seed, "embed"), "final_norm": gen_tensor(cfg, seed, "final_norm", gains=gains)}
     if not cfg.tied:
         w["lm_head"] = gen_tensor(cfg, seed, "lm_head")
-    w["layers"] = [{k: gen_tensor(cfg, seed, k, layer=l, gains=gains) for k in LAYER_KINDS}
-                   for l in range(cfg.n_layers)]
+        if cfg.dtype == "w8":
+            w["lm_head_scale"] = gen_scale(cfg, seed, "lm_head")
+    w["layers"] = [gen_layer(cfg, seed, l, gains) for l in range(cfg.n_layers)]
     return w
 
 
@@ -218,7 +282,8 @@ def gen_kv_prefix(cfg: ModelConfig, seed: int, n_pos: int, which: str, layer: in
     """Synthetic cache contents for positions [0, n_pos) of one layer,
     shape [n_kv_heads][n_pos][head_dim], stream (layer, K or V)."""
     stream = _STREAM_KV + 2 * layer + (0 if which == "k" else 1)
-    return normal(seed, stream, (cfg.n_kv_heads, n_pos, cfg.head_dim), kv_std(cfg), 0.0, cfg.dtype, out)
+    return normal(seed, stream, (cfg.n_kv_heads, n_pos, cfg.head_dim), kv_std(cfg), 0.0,
+                  "f32" if cfg.dtype == "f32" else "bf16", out)
 
 
 def philox4x32_10(ctr, key) -> list:

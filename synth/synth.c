@@ -84,7 +84,9 @@ static inline uint16_t f64_to_bf16_rne(double v) {
 
 /*
  * Fill out[0..n) with mean + std * N(0,1) for elements [offset, offset+n) of
- * stream `stream`.  dtype 0 = float32, 1 = bfloat16 bits (uint16).
+ * stream `stream`.  dtype 0 = float32, 1 = bfloat16 bits (uint16), 2 = int8
+ * codes (the draw rounded to the nearest integer and clamped to [-127, 127]:
+ * the code distribution of a weight-only INT8 matrix).
  */
 void synth_normal(uint64_t seed, uint32_t stream, uint64_t offset, uint64_t n,
                   double mean, double std, int dtype, void *out) {
@@ -101,8 +103,14 @@ void synth_normal(uint64_t seed, uint32_t stream, uint64_t offset, uint64_t n,
             if (e < offset || e >= offset + n) continue;
             double v = mean + std * z[k];
             uint64_t i = e - offset;
-            if (dtype == 0) ((float *)out)[i] = (float)v;
-            else ((uint16_t *)out)[i] = f64_to_bf16_rne(v);
+            if (dtype == 0) {
+                ((float *)out)[i] = (float)v;
+            } else if (dtype == 1) {
+                ((uint16_t *)out)[i] = f64_to_bf16_rne(v);
+            } else {
+                double r = nearbyint(v);
+                ((int8_t *)out)[i] = (int8_t)(r > 127.0 ? 127 : r < -127.0 ? -127 : (int)r);
+            }
         }
     }
 }
@@ -115,5 +123,17 @@ void synth_uniform_int(uint64_t seed, uint32_t stream, uint64_t offset, uint64_t
         uint32_t w[4];
         block_words(seed, stream, e >> 2, w);
         out[i] = (int32_t)(((uint64_t)w[e & 3] * (uint64_t)hi) >> 32);
+    }
+}
+
+/* Uniform float32 values in [lo, hi) for elements [offset, offset+n) of a
+   stream (per-row scales of the INT8 matrices). */
+void synth_uniform_f32(uint64_t seed, uint32_t stream, uint64_t offset, uint64_t n, double lo, double hi,
+                       float *out) {
+    for (uint64_t i = 0; i < n; ++i) {
+        uint64_t e = offset + i;
+        uint32_t w[4];
+        block_words(seed, stream, e >> 2, w);
+        out[i] = (float)(lo + (hi - lo) * ((double)w[e & 3] * (1.0 / 4294967296.0)));
     }
 }

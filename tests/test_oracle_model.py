@@ -25,7 +25,9 @@ def make(orc, cfg, weights, max_seq=None):
 
 
 def widen(orc, a):
-    return a.astype(np.float64) if a.dtype == np.float32 else orc.f64_array_from_bf16(a)
+    if a.dtype in (np.float32, np.float64):
+        return a.astype(np.float64)
+    return orc.f64_array_from_bf16(a)
 
 
 def hf_logits(orc, cfg, weights, tokens):
