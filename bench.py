@@ -9,8 +9,10 @@ launch wrote, so the timed loop runs with no host round trip.  The headline
 workload is the Llama-3.2-1B-shaped decoder with a 2048-token context and
 128 greedy steps; weights are seeded N(0, 0.02) bf16 (synthetic, random
 init) and the context is filled by mk_prefill_kv from seeded token ids.
-The Llama-3-8B shape (2048-token context) and the 1B shape at a 32768-token
-context are measured in the same run and reported under `extra_workloads`.
+The Llama-3-8B shape (2048-token context), the 1B shape at a 32768-token
+context, and the 1B and 8B shapes with weight-only INT8 matrices (int8 codes
+with per-row fp32 scales, bf16 cache) are measured in the same run and
+reported under `extra_workloads`.
 
 Each workload is timed in `--runs` (3) runs of K steps; the median run gives
 `value` (tokens/s, wall clock, inputs resident in HBM) and the roofline
@@ -74,7 +76,7 @@ def load_model(mkp, synth, cfg, shape, max_seq, tuning, seed, dev, keep_host):
     mk = mkp.MegaKernel(shape, None, max_seq, tuning=tuning)
     host_layers = []
     for l in range(cfg.n_layers):
-        lw = {k: synth.gen_tensor(cfg, seed, k, layer=l) for k in synth.LAYER_KINDS}
+        lw = synth.gen_layer(cfg, seed, l)  # (with the per-row scales of an INT8 model)
         part = mkp.upload_weights({"layers": [lw]}, dev)
         mk.load_weights(part, first_layer=l)
         del part
@@ -85,6 +87,8 @@ def load_model(mkp, synth, cfg, shape, max_seq, tuning, seed, dev, keep_host):
     head = {"embed": synth.gen_tensor(cfg, seed, "embed"), "final_norm": synth.gen_tensor(cfg, seed, "final_norm")}
     if not cfg.tied:
         head["lm_head"] = synth.gen_tensor(cfg, seed, "lm_head")
+        if cfg.dtype == "w8":
+            head["lm_head_scale"] = synth.gen_scale(cfg, seed, "lm_head")
     part = mkp.upload_weights(head, dev)
     mk.load_weights(part)
     del part
@@ -150,10 +154,13 @@ def prefill_record(cfg, n, seconds, info):
     per_layer = (cfg.q_dim + 2 * cfg.kv_dim) * H + H * cfg.q_dim + 3 * H * F
     flops = 2.0 * cfg.n_layers * per_layer * n + 4.0 * cfg.n_layers * cfg.q_dim * n * (n + 1) / 2
     tf = flops / seconds / 1e12
-    return {"positions": n, "seconds": seconds, "tokens_per_s": n / seconds,
-            "mode": f"batched, chunks of {info['prefill_chunk']}" if info["prefill_chunk"] else "decode launches",
-            "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
-                         "frac": tf / PEAK_MFMA_BF16_TFLOPS, "traffic": None, "flops": flops}}
+    rec = {"positions": n, "seconds": seconds, "tokens_per_s": n / seconds,
+           "mode": f"batched, chunks of {info['prefill_chunk']}" if info["prefill_chunk"] else "decode launches",
+           "roofline": None}
+    if info["prefill_chunk"]:  # the matrix-core path; decode launches are the decode step's own roofline
+        rec["roofline"] = {"bound": "mfma", "achieved": tf, "peak": PEAK_MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
+                           "frac": tf / PEAK_MFMA_BF16_TFLOPS, "traffic": None, "flops": flops}
+    return rec
 
 
 def measure(name, args, dev, steps, warm, runs, cpu_budget, with_cpu):
@@ -262,7 +269,7 @@ def measure(name, args, dev, steps, warm, runs, cpu_budget, with_cpu):
         "prefill": prefill_record(cfg, ctx, prefill_s, info),
         "info": info,
         "first_tokens": [int(x) for x in tokens[:8]],
-        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "dtype": {"bf16": "bf16", "f32": "f32", "w8": "int8 weights x bf16 activations, fp32 accumulate"}[cfg.dtype],
     }
 
 
@@ -307,7 +314,7 @@ def main():
     import synth
 
     if args.extra is None:
-        extra = ["llama8b", "llama1b_32k"] if args.config == "llama1b" else []
+        extra = ["llama8b", "llama1b_32k", "llama1b_w8", "llama8b_w8"] if args.config == "llama1b" else []
     else:
         extra = [x for x in args.extra.split(",") if x]
     dev = torch.device("cuda:0")
@@ -324,7 +331,7 @@ def main():
         extras.append({k: rec[k] for k in ("name", "workload", "value", "runs_tokens_per_s", "ms_per_step",
                                            "us_per_token_p50", "us_per_token_p99", "us_per_token_mean", "gbs_p50",
                                            "bytes_per_step", "decode_positions", "roofline", "cpu_baseline",
-                                           "prefill", "first_tokens")} | {"unit": "tokens/s", "steps": n})
+                                           "prefill", "first_tokens", "dtype")} | {"unit": "tokens/s", "steps": n})
     info = head["info"]
     out = {
         "metric": "batch-1 decode tokens/s (us/token p50/P99) + achieved HBM GB/s vs peak",

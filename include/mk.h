@@ -67,13 +67,22 @@ typedef enum {
    process ends). */
 #define MK_STATIC_SCRATCH_BYTES (64 * 1024 * 1024)
 
-typedef enum { MK_F32 = 0, MK_BF16 = 1 } mk_dtype;
+/* MK_F32, MK_BF16: every weight and the KV cache in that type.
+   MK_W8: weight-only INT8 -- the seven layer matrices and the LM head are
+   int8 codes q with one float32 scale s per output row, standing for the
+   weights W[r][c] = s[r] * q[r][c]; the embedding, the norm gains and the KV
+   cache are bf16.  Quantised models stream fewer bytes per token, and the
+   dequantisation runs inside the fused step (www.stapisi.com/news/3904786
+   section 6.1).  The kernel multiplies the int8 codes by the activations in
+   fp32 and applies each row's scale to the row's sum. */
+typedef enum { MK_F32 = 0, MK_BF16 = 1, MK_W8 = 2 } mk_dtype;
 
 /* Model shape.  Supported: n_heads % n_kv_heads == 0; head_dim * element
-   size equal to 128 or 256 bytes (bf16: head_dim 64 or 128; f32: 32 or 64);
-   hidden and ffn multiples of 8; max_seq >= 1.  rms_eps is added to the mean
-   square inside the square root; RoPE rotates pairs (i, i + head_dim/2) by
-   pos * rope_theta^(-2i/head_dim). */
+   size of the cache equal to 128 or 256 bytes (bf16 and MK_W8: head_dim 64
+   or 128; f32: 32 or 64); hidden and ffn multiples of 8; max_seq >= 1;
+   MK_W8 models are not tied (their LM head is its own int8 matrix).
+   rms_eps is added to the mean square inside the square root; RoPE rotates
+   pairs (i, i + head_dim/2) by pos * rope_theta^(-2i/head_dim). */
 typedef struct {
     int32_t n_layers, hidden, n_heads, n_kv_heads, head_dim, ffn, vocab, max_seq;
     double rms_eps, rope_theta;
@@ -84,16 +93,22 @@ typedef struct {
 /* Device pointers to one layer's weights in the model dtype:
    attn_norm [H], wq [n_heads*head_dim][H], wk [n_kv*head_dim][H],
    wv [n_kv*head_dim][H], wo [H][n_heads*head_dim], ffn_norm [H],
-   w_gate [F][H], w_up [F][H], w_down [H][F]. */
+   w_gate [F][H], w_up [F][H], w_down [H][F].  For MK_W8 the matrices are
+   int8 codes, the norms bf16, and s_* are the matrices' float32 per-row
+   scales (one per output row: s_wq [n_heads*head_dim], ..., s_w_down [H]);
+   the s_* pointers are ignored for the other dtypes and may be NULL. */
 typedef struct {
     const void *attn_norm, *wq, *wk, *wv, *wo, *ffn_norm, *w_gate, *w_up, *w_down;
+    const float *s_wq, *s_wk, *s_wv, *s_wo, *s_w_gate, *s_w_up, *s_w_down;
 } mk_layer_ptrs;
 
 /* embed [V][H], final_norm [H], lm_head [V][H] (ignored when tied);
-   layers is a HOST array of n_layers entries holding device pointers. */
+   layers is a HOST array of n_layers entries holding device pointers;
+   lm_head_scale [V] is the LM head's per-row scales (MK_W8 only). */
 typedef struct {
     const void *embed, *final_norm, *lm_head;
     const mk_layer_ptrs *layers;
+    const float *lm_head_scale;
 } mk_weight_ptrs;
 
 /* Caller-owned contiguous KV cache, device memory in the model dtype, each of

@@ -47,8 +47,9 @@ def test_status_and_dtype_values_match_binding():
     st = header_enum("MK_ERR_") | header_enum("MK_OK")
     for k, v in st.items():
         assert getattr(mkb, k) == v, k
-    dt = header_enum("MK_F32") | header_enum("MK_BF16")
-    assert dt == {"MK_F32": mkb.MK_F32, "MK_BF16": mkb.MK_BF16}
+    dt = header_enum("MK_F32") | header_enum("MK_BF16") | header_enum("MK_W8")
+    assert dt == {"MK_F32": mkb.MK_F32, "MK_BF16": mkb.MK_BF16, "MK_W8": mkb.MK_W8}
+    assert [f for f, _ in mkb.LayerPtrs._fields_[9:]] == ["s_" + k for k in mkb.MATRIX_KINDS]
 
 
 def test_status_strings(lib):
@@ -98,6 +99,20 @@ def test_create_rejects_null_arguments(lib):
     assert _create(lib, _desc(), w2)[0] == mkb.MK_ERR_NULL
     w3, _keep3 = _weights(2)
     assert _create(lib, _desc(tied_embeddings=0), w3)[0] == mkb.MK_ERR_NULL  # untied needs lm_head
+
+
+def test_int8_models_need_scales_and_their_own_head(lib):
+    fake = ctypes.c_void_p(0x1000).value  # never dereferenced: validation fails first
+    layers = (mkb.LayerPtrs * 2)()
+    for l in range(2):
+        layers[l] = mkb.LayerPtrs(*[fake] * 9, *[fake] * 7)
+    w = mkb.WeightPtrs(fake, fake, fake, layers, fake)
+    # weight-only INT8 with a tied head: the int8 LM head is its own matrix
+    assert _create(lib, _desc(dtype=mkb.MK_W8, tied_embeddings=1), w)[0] == mkb.MK_ERR_SHAPE
+    w_nohs = mkb.WeightPtrs(fake, fake, fake, layers, None)
+    assert _create(lib, _desc(dtype=mkb.MK_W8, tied_embeddings=0), w_nohs)[0] == mkb.MK_ERR_NULL
+    layers[1] = mkb.LayerPtrs(*[fake] * 9, *[fake] * 6, None)  # no w_down scales
+    assert _create(lib, _desc(dtype=mkb.MK_W8, tied_embeddings=0), w)[0] == mkb.MK_ERR_NULL
 
 
 @pytest.mark.parametrize("over,status", [

@@ -37,7 +37,7 @@ def test_every_decode_instantiation_is_reported(resources):
     # <dtype, group, lanes per cache row, LOGITS, position-major attention>;
     # the position-major mapping exists for groups of four query heads only
     names = {k["name"] for k in resources}
-    for dt in (0, 1):
+    for dt in (0, 1, 2):  # float32, bfloat16, weight-only INT8
         for gq in GROUPS:
             for lpp in LANES:
                 for logits in ("b0", "b1"):

@@ -29,7 +29,8 @@ SOURCES = ["mk_api.hip", "mk_kernel.hip", "mk_prelayout.hip", "mk_prefill.hip"]
 HEADERS = [os.path.join(CSRC, "mk_internal.h"), os.path.join(INCLUDE, "mk.h")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # (dtype, query heads per KV head) parts of the decode kernel's instantiations
-KERNEL_PARTS = [(dt, gq) for dt in (0, 1) for gq in (1, 2, 4, 8)]
+# (dtype 0 float32, 1 bfloat16, 2 weight-only INT8)
+KERNEL_PARTS = [(dt, gq) for dt in (0, 1, 2) for gq in (1, 2, 4, 8)]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

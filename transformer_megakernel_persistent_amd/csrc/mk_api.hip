@@ -39,7 +39,7 @@ static uint32_t g_scratch_tag_end[MK_MAX_DEVICES];  // last tag used on that dev
 
 struct mk_handle {
     mk_model_desc desc;
-    int eb = 0;
+    int emb_bytes = 0;  // bytes per embedding element (bf16 for MK_W8)
     int device = 0;
     int cu_count = 0;
     int cooperative = 0;
@@ -51,6 +51,7 @@ struct mk_handle {
     float *gains = nullptr;     // attn [L][H], ffn [L][H], final [H]
     void *embed = nullptr;
     float *rope = nullptr;
+    float *scl = nullptr;       // per-row scales of the INT8 matrices (MK_W8; see MkParams::scl)
     uint64_t *ll = nullptr;     // tagged cross-workgroup records (see MkParams)
     RecLayout rec;              // their layout (the same inside the static scratch)
     uint32_t *err = nullptr;    // device error word
@@ -83,6 +84,16 @@ mk_status hip_fail(hipError_t e) { return e == hipErrorOutOfMemory ? MK_ERR_NOME
     } while (0)
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// The kernel's dtype code: 0 float32, 1 bfloat16, 2 weight-only INT8 (bf16
+// cache, embedding and gains).
+int dtype_code(mk_dtype t) { return t == MK_W8 ? 2 : t == MK_BF16 ? 1 : 0; }
+// Bytes per element of the weight matrices, and of the cache, embedding and gains.
+int matrix_bytes(mk_dtype t) { return t == MK_W8 ? 1 : t == MK_BF16 ? 2 : 4; }
+int cache_bytes(mk_dtype t) { return t == MK_F32 ? 4 : 2; }
+// Largest block of per-row scales one workgroup keeps in LDS (four consumer
+// waves of 64 lanes carry four floats each between its load and its LDS store).
+constexpr int MK_SC_MAX = 1024;
 
 // Tag base of the next launch on a record buffer whose last launch used tags
 // up to `end` (a launch tags its records base + l for layer index l in
@@ -129,8 +140,9 @@ struct StageShape {
 };
 
 mk_status validate_desc(const mk_model_desc *d) {
-    if (d->dtype != MK_F32 && d->dtype != MK_BF16) return MK_ERR_DTYPE;
-    const int eb = d->dtype == MK_BF16 ? 2 : 4;
+    if (d->dtype != MK_F32 && d->dtype != MK_BF16 && d->dtype != MK_W8) return MK_ERR_DTYPE;
+    const int eb = cache_bytes(d->dtype);
+    if (d->dtype == MK_W8 && d->tied_embeddings) return MK_ERR_SHAPE;  // the int8 LM head is its own matrix
     if (d->n_layers < 1 || d->hidden < 8 || d->n_heads < 1 || d->n_kv_heads < 1 || d->head_dim < 2 || d->ffn < 8 ||
         d->vocab < 1 || d->max_seq < 1)
         return MK_ERR_SHAPE;
@@ -182,6 +194,7 @@ extern "C" void mk_destroy(mk_handle *h) {
     hipFree(h->gains);
     hipFree(h->embed);
     hipFree(h->rope);
+    hipFree(h->scl);
     hipFree(h->ll);
     hipFree(h->err);
     hipFree(h->trace);
@@ -201,12 +214,13 @@ static mk_status create_impl(const mk_model_desc *desc, const mk_tuning *tun, mk
     const mk_model_desc &D = *desc;
     const int L = D.n_layers, H = D.hidden, nh = D.n_heads, nkv = D.n_kv_heads, d = D.head_dim, F = D.ffn,
               V = D.vocab;
-    const int dtype = D.dtype == MK_BF16 ? 1 : 0;
-    const int eb = dtype ? 2 : 4;
+    const int dtype = dtype_code(D.dtype);
+    const int eb = matrix_bytes(D.dtype);  // geometry of the packed matrices
+    const int ebc = cache_bytes(D.dtype);  // cache rows, embedding
     const int gq = nh / nkv;
-    const int lpp = d * eb / 16;
+    const int lpp = d * ebc / 16;
     h->desc = D;
-    h->eb = eb;
+    h->emb_bytes = ebc;
 
     HIP_TRY(hipGetDevice(&h->device));
     // the static scratch of the no-allocation entry point, taken once per
@@ -241,7 +255,9 @@ static mk_status create_impl(const mk_model_desc *desc, const mk_tuning *tun, mk
     MkParams &P = h->base;
     memset(&P, 0, sizeof P);
     std::vector<int64_t> off_host((size_t)ST_NUM * grid);
-    int64_t total = 0;
+    // the packed buffer opens with one zeroed 16 KiB slot that no stage owns:
+    // the loaders' masked reads land there (see the allocation below)
+    int64_t total = MK_SLOT_BYTES;
     int vec_floats = 0, out_rows = 0;
     const int epc = MK_CHUNK_BYTES / eb;
     int max_rows_o = 0;  // x rows a workgroup owns (O-stage rows): reduced and kept in LDS
@@ -297,34 +313,57 @@ static mk_status create_impl(const mk_model_desc *desc, const mk_tuning *tun, mk
     // consumers' per-head partials in vec, after the queries and the row of pos
     if (gq == MK_NUM_CONSUMERS && vec_floats < (gq + 2) * d + MK_NUM_CONSUMERS * gq * (d + 2))
         vec_floats = (gq + 2) * d + MK_NUM_CONSUMERS * gq * (d + 2);
-    const int fixed = mk_kernel_lds_bytes(0, vec_floats, out_rows, dtype, d, gq);
+    // per-row scale blocks of the INT8 matrices (two LDS copies, by layer parity)
+    int sc_blk = 0, sc_lm = 0;
+    if (dtype == 2) {
+        auto nu = [&](int k, int w) {
+            return (int)((int64_t)(w + 1) * P.st[k].units / grid) - (int)((int64_t)w * P.st[k].units / grid);
+        };
+        for (int w = 0; w < grid; ++w) {
+            const int blk = 4 * (nu(ST_QKV, w) + 2 * nu(ST_O, w) + nu(ST_GU, w));
+            if (blk > sc_blk) sc_blk = blk;
+            if (4 * nu(ST_LM, w) > sc_lm) sc_lm = 4 * nu(ST_LM, w);
+        }
+        sc_blk = (sc_blk + 63) & ~63;
+        sc_lm = (sc_lm + 63) & ~63;
+        if (sc_blk > MK_SC_MAX || sc_lm > MK_SC_MAX) return MK_ERR_SHAPE;
+    }
+    const int lds_sc = sc_blk > sc_lm ? sc_blk : sc_lm;
+    const int fixed = mk_kernel_lds_bytes(0, vec_floats, out_rows, 2 * lds_sc);
     int ns = t.ring_slots ? t.ring_slots : (MK_LDS_LIMIT - fixed) / MK_SLOT_BYTES;
     if (ns > MK_DEFAULT_RING && !t.ring_slots) ns = MK_DEFAULT_RING;  // a 9th slot measured no faster
     if (ns > MK_MAX_RING) ns = MK_MAX_RING;
     if (ns < 3 || fixed + ns * MK_SLOT_BYTES > MK_LDS_LIMIT) return MK_ERR_SHAPE;
     if (t.prefetch_depth > ns - 1) return MK_ERR_TUNING;  // a load needs a consumed ring slot
-    h->lds_bytes = mk_kernel_lds_bytes(ns, vec_floats, out_rows, dtype, d, gq);
+    h->lds_bytes = mk_kernel_lds_bytes(ns, vec_floats, out_rows, 2 * lds_sc);
     const int per_cu = mk_kernel_max_blocks_per_cu(dtype, gq, lpp, h->lds_bytes);
     if (per_cu < 1) return MK_ERR_SHAPE;
     if (grid > per_cu * h->cu_count) return MK_ERR_TUNING;  // every workgroup must be resident
 
     // allocations
     h->packed_bytes = total;
-    // The loaders' idle reads (past a split's cache positions, past the end of
-    // the stream) touch the first 1 KiB of the buffer, and the striped layout
-    // leaves holes that no pre-layout writes (for example workgroup 0's first
-    // slot when a stage has fewer units than workgroups).  Zero it all once so
-    // that every byte a loader can read is a finite number: the attention
-    // fold multiplies masked V values by 0.
-    const int64_t packed_alloc = total > MK_SLOT_BYTES ? total : MK_SLOT_BYTES;
+    // The loaders' idle reads (cache positions past a split's end, slots past
+    // the end of the stream) read the first 1 KiB of the buffer, which lies in
+    // the zeroed slot that opens it and that no stage owns.  The attention
+    // fold multiplies masked V values by probability 0, so they must be
+    // finite numbers, whatever the weights are: int8 codes read as bf16 pairs
+    // can spell a NaN.  The striped layout also leaves holes that no
+    // pre-layout writes (for example workgroup 0's first slot when a stage has
+    // fewer units than workgroups); the whole buffer is zeroed once.
+    const int64_t packed_alloc = total;
     HIP_TRY(hipMalloc(&h->packed, packed_alloc));
     HIP_TRY(hipMemset(h->packed, 0, packed_alloc));
     HIP_TRY(hipMalloc(&h->wg_off, off_host.size() * sizeof(int64_t)));
     HIP_TRY(hipMemcpy(h->wg_off, off_host.data(), off_host.size() * sizeof(int64_t), hipMemcpyHostToDevice));
     const size_t ngain = (size_t)2 * L * H + H;
     HIP_TRY(hipMalloc(&h->gains, ngain * sizeof(float)));
-    HIP_TRY(hipMalloc(&h->embed, (size_t)V * H * eb));
+    HIP_TRY(hipMalloc(&h->embed, (size_t)V * H * ebc));
     HIP_TRY(hipMalloc(&h->rope, (size_t)D.max_seq * d * sizeof(float)));
+    if (dtype == 2) {
+        const size_t n_sc = (size_t)L * grid * sc_blk + (size_t)grid * sc_lm;
+        HIP_TRY(hipMalloc(&h->scl, n_sc * sizeof(float)));
+        HIP_TRY(hipMemset(h->scl, 0, n_sc * sizeof(float)));
+    }
     // tagged records, one array per dependency point, each with two buffers
     // (layers of even and odd index)
     const size_t n_rec[7] = {(size_t)2 * H, (size_t)2 * H, (size_t)2 * nkv * (gq + 2) * d,
@@ -375,6 +414,10 @@ static mk_status create_impl(const mk_model_desc *desc, const mk_tuning *tun, mk
     // consumers' arithmetic, not by their LDS reads)
     P.attn_pm_slots = t.attn_pm_slots > 0 ? t.attn_pm_slots : (1 << 30);
     P.packed = h->packed;
+    P.scl = h->scl;
+    P.sc_blk = sc_blk;
+    P.sc_lm = sc_lm;
+    P.lds_sc_floats = lds_sc;
     P.g_attn = h->gains; P.g_ffn = h->gains + (size_t)L * H; P.g_final = h->gains + (size_t)2 * L * H;
     P.embed = h->embed;
     P.rope = h->rope;
@@ -404,8 +447,13 @@ static mk_status create_impl(const mk_model_desc *desc, const mk_tuning *tun, mk
         B.t_max = T;
     }
 
-    const int64_t per_layer = (int64_t)((nh + 2 * nkv) * d) * H + (int64_t)H * nh * d + 3LL * H * F + 2LL * H;
-    h->weight_bytes = ((int64_t)L * per_layer + (int64_t)V * H + 2LL * H) * eb;
+    // algorithmic bytes: every matrix (with its per-row scales when INT8),
+    // the gains, the LM head and one embedding row
+    const int64_t mat = (int64_t)((nh + 2 * nkv) * d) * H + (int64_t)H * nh * d + 3LL * H * F;
+    const int64_t mrows = (int64_t)(nh + 2 * nkv) * d + H + 2LL * F + H;
+    const int64_t sc = dtype == 2 ? 4 : 0;
+    h->weight_bytes = (int64_t)L * (mat * eb + mrows * sc + 2LL * H * ebc) + (int64_t)V * H * eb + (int64_t)V * sc +
+                      2LL * H * ebc;
     return MK_OK;
 }
 
@@ -416,7 +464,9 @@ static mk_status load_impl(mk_handle *h, const mk_weight_ptrs *wp, int first, in
     const mk_model_desc &D = h->desc;
     const MkParams &P = h->base;
     const int L = D.n_layers, H = D.hidden, V = D.vocab, grid = P.grid;
-    const int dtype = D.dtype == MK_BF16 ? 1 : 0;
+    const int eb = matrix_bytes(D.dtype);
+    const int gdt = D.dtype == MK_F32 ? 0 : 1;  // storage of the gains
+    const bool q8 = D.dtype == MK_W8;
     // no step of this handle may still be reading the weights being replaced
     HIP_TRY(hipDeviceSynchronize());
     for (int i = 0; i < n; ++i) {
@@ -431,19 +481,27 @@ static mk_status load_impl(mk_handle *h, const mk_weight_ptrs *wp, int first, in
             default: s0 = lw.w_down; break;
             }
             if (mk_launch_prelayout_stage(h->packed + P.st[k].base + (int64_t)l * P.st[k].layer_stride, &P.st[k], grid,
-                                          k, dtype, s0, s1, s2, D.n_heads, D.n_kv_heads, D.head_dim, nullptr))
+                                          k, eb, s0, s1, s2, D.n_heads, D.n_kv_heads, D.head_dim, nullptr))
                 return MK_ERR_HIP;
         }
-        if (mk_launch_to_f32(h->gains + (size_t)l * H, lw.attn_norm, H, dtype, nullptr)) return MK_ERR_HIP;
-        if (mk_launch_to_f32(h->gains + (size_t)(L + l) * H, lw.ffn_norm, H, dtype, nullptr)) return MK_ERR_HIP;
+        if (q8) {
+            const float *sc[7] = {lw.s_wq, lw.s_wk, lw.s_wv, lw.s_wo, lw.s_w_gate, lw.s_w_up, lw.s_w_down};
+            if (mk_launch_prelayout_scales(h->scl, &P, l, sc, nullptr)) return MK_ERR_HIP;
+        }
+        if (mk_launch_to_f32(h->gains + (size_t)l * H, lw.attn_norm, H, gdt, nullptr)) return MK_ERR_HIP;
+        if (mk_launch_to_f32(h->gains + (size_t)(L + l) * H, lw.ffn_norm, H, gdt, nullptr)) return MK_ERR_HIP;
     }
     if (wp->embed) {
         const void *lm = D.tied_embeddings ? wp->embed : wp->lm_head;
-        if (mk_launch_prelayout_stage(h->packed + P.st[ST_LM].base, &P.st[ST_LM], grid, ST_LM, dtype, lm, nullptr,
+        if (mk_launch_prelayout_stage(h->packed + P.st[ST_LM].base, &P.st[ST_LM], grid, ST_LM, eb, lm, nullptr,
                                       nullptr, D.n_heads, D.n_kv_heads, D.head_dim, nullptr))
             return MK_ERR_HIP;
-        if (mk_launch_to_f32(h->gains + (size_t)2 * L * H, wp->final_norm, H, dtype, nullptr)) return MK_ERR_HIP;
-        HIP_TRY(hipMemcpy(h->embed, wp->embed, (size_t)V * H * h->eb, hipMemcpyDeviceToDevice));
+        if (q8) {
+            const float *sc[7] = {wp->lm_head_scale, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+            if (mk_launch_prelayout_scales(h->scl, &P, L, sc, nullptr)) return MK_ERR_HIP;
+        }
+        if (mk_launch_to_f32(h->gains + (size_t)2 * L * H, wp->final_norm, H, gdt, nullptr)) return MK_ERR_HIP;
+        HIP_TRY(hipMemcpy(h->embed, wp->embed, (size_t)V * H * h->emb_bytes, hipMemcpyDeviceToDevice));
     }
     // the sources may be freed when this returns
     HIP_TRY(hipDeviceSynchronize());
@@ -459,12 +517,16 @@ static mk_status load_impl(mk_handle *h, const mk_weight_ptrs *wp, int first, in
 // Null checks of the weight pointers a load will read: layers[0 .. n) and,
 // when embed is set, the head tensors.
 static mk_status check_weight_ptrs(const mk_model_desc *desc, const mk_weight_ptrs *w, int n) {
-    if (w->embed && (!w->final_norm || (!desc->tied_embeddings && !w->lm_head))) return MK_ERR_NULL;
+    const bool q8 = desc->dtype == MK_W8;
+    if (w->embed && (!w->final_norm || (!desc->tied_embeddings && !w->lm_head) || (q8 && !w->lm_head_scale)))
+        return MK_ERR_NULL;
     if (n > 0 && !w->layers) return MK_ERR_NULL;
     for (int l = 0; l < n; ++l) {
         const mk_layer_ptrs &lw = w->layers[l];
         if (!lw.attn_norm || !lw.wq || !lw.wk || !lw.wv || !lw.wo || !lw.ffn_norm || !lw.w_gate || !lw.w_up ||
             !lw.w_down)
+            return MK_ERR_NULL;
+        if (q8 && (!lw.s_wq || !lw.s_wk || !lw.s_wv || !lw.s_wo || !lw.s_w_gate || !lw.s_w_up || !lw.s_w_down))
             return MK_ERR_NULL;
     }
     return MK_OK;
@@ -566,7 +628,7 @@ static mk_status launch(mk_handle *h, const mk_kv_cache *kv, int32_t token, cons
         p.tag = next_tag_base(h->tag_end, h->desc.n_layers, &wrapped);
         if (wrapped && mk_launch_zero(h->ll, (int64_t)h->rec.off[7] * 8, stream)) return MK_ERR_HIP;
     }
-    int rc = mk_launch_decode(&p, h->desc.dtype == MK_BF16 ? 1 : 0, h->cooperative, stream);
+    int rc = mk_launch_decode(&p, dtype_code(h->desc.dtype), h->cooperative, stream);
     return rc ? MK_ERR_HIP : MK_OK;
 }
 

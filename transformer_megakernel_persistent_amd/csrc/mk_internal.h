@@ -54,18 +54,24 @@ static inline __host__ __device__ MkDownGeo mk_down_geo(int w, int G, int units_
     return g;
 }
 
-// Order of a consumer's chunk stream for the matrix-vector stages.  Rows of
-// exactly 4 chunks are stored row after row (one row per slot).  Longer rows
-// of a multiple of 4 chunks are interleaved in groups of four rows: the
-// stream holds chunk 0 of rows 4g..4g+3, then chunk 1 of the same rows, and
-// so on, so the four pieces a consumer takes from one slot multiply the same
-// input elements (read once from LDS instead of once per piece).  Rows past
-// the last whole group, and rows of other lengths, follow row after row.
-static inline __host__ __device__ bool mk_row_groups(int rbp) { return rbp >= 8 && (rbp & 3) == 0; }
+// Order of a consumer's chunk stream for the matrix-vector stages.  Rows
+// may be interleaved in groups of four rows: the stream holds chunk 0 of
+// rows 4g..4g+3, then chunk 1 of the same rows, and so on, so the four
+// pieces a consumer takes from one slot multiply the same input elements
+// (read once from LDS instead of once per piece).  Rows past the last whole
+// group follow row after row.  Grouped: int8 rows (eb == 1) of any length --
+// a 16-byte int8 piece needs 16 input floats, so re-reading them per piece
+// would cost four times the weight bytes in LDS reads; float32 and bfloat16
+// rows of 8, 12, 16 ... chunks.  Float32 and bfloat16 rows of exactly 4
+// chunks go row after row (the kernel keeps their input slice in registers),
+// and so do rows of other lengths.
+static inline __host__ __device__ bool mk_row_groups(int rbp, int eb) {
+    return eb == 1 ? rbp >= 1 : (rbp >= 8 && (rbp & 3) == 0);
+}
 // Stream position qq (in chunks) of a consumer holding `rows` rows of rbp
-// chunks -> its local row and the chunk within that row.
-static inline __host__ __device__ void mk_stream_pos(int qq, int rows, int rbp, int &row, int &kc) {
-    const int full = mk_row_groups(rbp) ? rows / 4 : 0;
+// chunks of eb-byte elements -> its local row and the chunk within that row.
+static inline __host__ __device__ void mk_stream_pos(int qq, int rows, int rbp, int eb, int &row, int &kc) {
+    const int full = mk_row_groups(rbp, eb) ? rows / 4 : 0;
     const int span = 4 * rbp;  // chunks of one group of four rows
     if (qq < full * span) {
         row = (qq / span) * 4 + (qq % 4);
@@ -103,6 +109,15 @@ struct MkParams {
     // weights
     const unsigned char *packed;
     MkStage st[ST_NUM];
+    // Weight-only INT8 (dtype 2): per-row scales of the matrices, one block
+    // per (layer, workgroup) of sc_blk floats -- the workgroup's QKV rows,
+    // O rows, gate/up rows (packed local order) and the down-projection rows
+    // of its x rows (the O rows' indices), one after the other, zero padded
+    // -- at scl + (l * grid + w) * sc_blk, and the LM head's block of sc_lm
+    // floats at scl + L * grid * sc_blk + w * sc_lm.  lds_sc_floats: the LDS
+    // copy of one block (max(sc_blk, sc_lm)); two copies, by layer parity.
+    const float *scl;
+    int32_t sc_blk, sc_lm, lds_sc_floats;
     const float *g_attn;   // [L][H]
     const float *g_ffn;    // [L][H]
     const float *g_final;  // [H]
@@ -159,10 +174,14 @@ struct MkPrefillBufs {
 extern "C" {
 #endif
 int mk_launch_decode(const MkParams *p, int dtype, int cooperative, void *stream);
-int mk_launch_prelayout_stage(unsigned char *dst, const MkStage *st, int grid, int kind, int dtype,
+int mk_launch_prelayout_stage(unsigned char *dst, const MkStage *st, int grid, int kind, int eb,
                               const void *src0, const void *src1, const void *src2, int nh, int nkv, int d,
                               void *stream);
-int mk_kernel_lds_bytes(int ring_slots, int vec_floats, int out_rows, int dtype, int d, int gq);
+// One block of per-row scales per workgroup (see MkParams::scl) for layer
+// `layer` (src[0..6]: wq, wk, wv, wo, w_gate, w_up, w_down scales) or, with
+// layer == L, the LM head's (src[0]).
+int mk_launch_prelayout_scales(float *scl, const MkParams *p, int layer, const float *const *src, void *stream);
+int mk_kernel_lds_bytes(int ring_slots, int vec_floats, int out_rows, int sc_floats);
 int mk_launch_to_f32(float *dst, const void *src, int64_t n, int dtype, void *stream);
 int mk_launch_zero(void *dst, int64_t bytes, void *stream);
 int mk_prefill_chunk(const MkParams *p, const MkPrefillBufs *b, int T, int pos0, void *stream);

@@ -189,11 +189,41 @@ __device__ __forceinline__ uint32_t f2bf(float f) {
     return u >> 16;
 }
 
+// Weight elements per 16-byte piece: float32, bfloat16, int8 (dtype 2).
+constexpr int wepl(int dt) { return dt == 2 ? 16 : dt ? 8 : 4; }
+
+// Signed byte k of w as a float (an int8 weight code; exact).
+__device__ __forceinline__ float i8f(uint32_t w, int k) { return (float)((int32_t)(w << (24 - 8 * k)) >> 24); }
+
 // Dot product of one 16-byte weight piece (in LDS) with the matching input
-// elements (in LDS).
+// elements (in LDS).  INT8 pieces give the sum of code * input; the row's
+// scale is applied to the finished row sum.
 template <int DT>
 __device__ __forceinline__ float piece_dot(const LDS unsigned char *wp, const LDS float *hp) {
-    if constexpr (DT == 1) {
+    if constexpr (DT == 2) {
+        const u4v w = *(const LDS u4v *)wp;
+        const f4v h0 = *(const LDS f4v *)hp;
+        const f4v h1 = *(const LDS f4v *)(hp + 4);
+        const f4v h2 = *(const LDS f4v *)(hp + 8);
+        const f4v h3 = *(const LDS f4v *)(hp + 12);
+        float a = i8f(w.x, 0) * h0.x;
+        float b = i8f(w.x, 1) * h0.y;
+        a = fmaf(i8f(w.x, 2), h0.z, a);
+        b = fmaf(i8f(w.x, 3), h0.w, b);
+        a = fmaf(i8f(w.y, 0), h1.x, a);
+        b = fmaf(i8f(w.y, 1), h1.y, b);
+        a = fmaf(i8f(w.y, 2), h1.z, a);
+        b = fmaf(i8f(w.y, 3), h1.w, b);
+        a = fmaf(i8f(w.z, 0), h2.x, a);
+        b = fmaf(i8f(w.z, 1), h2.y, b);
+        a = fmaf(i8f(w.z, 2), h2.z, a);
+        b = fmaf(i8f(w.z, 3), h2.w, b);
+        a = fmaf(i8f(w.w, 0), h3.x, a);
+        b = fmaf(i8f(w.w, 1), h3.y, b);
+        a = fmaf(i8f(w.w, 2), h3.z, a);
+        b = fmaf(i8f(w.w, 3), h3.w, b);
+        return a + b;
+    } else if constexpr (DT == 1) {
         const u4v w = *(const LDS u4v *)wp;
         const f4v h0 = *(const LDS f4v *)hp;
         const f4v h1 = *(const LDS f4v *)(hp + 4);
@@ -219,8 +249,19 @@ __device__ __forceinline__ float piece_dot(const LDS unsigned char *wp, const LD
 
 // Same with the input elements already in registers.
 template <int DT>
-__device__ __forceinline__ float piece_dot_reg(const LDS unsigned char *wp, const float (&h)[16 / (DT ? 2 : 4)]) {
-    if constexpr (DT == 1) {
+__device__ __forceinline__ float piece_dot_reg(const LDS unsigned char *wp, const float (&h)[wepl(DT)]) {
+    if constexpr (DT == 2) {
+        const u4v w = *(const LDS u4v *)wp;
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+        float a = i8f(ww[0], 0) * h[0];
+        float b = i8f(ww[0], 1) * h[1];
+#pragma unroll
+        for (int e = 2; e < 16; e += 2) {
+            a = fmaf(i8f(ww[e >> 2], e & 3), h[e], a);
+            b = fmaf(i8f(ww[e >> 2], (e & 3) + 1), h[e + 1], b);
+        }
+        return a + b;
+    } else if constexpr (DT == 1) {
         const u4v w = *(const LDS u4v *)wp;
         float a = bf_lo(w.x) * h[0];
         float b = bf_hi(w.x) * h[1];
@@ -263,12 +304,11 @@ __device__ __forceinline__ float piece_elem(const u4v &w, int e) {
 
 // The input elements matching a 16-byte weight piece, from LDS.
 template <int DT>
-__device__ __forceinline__ void piece_in(const LDS float *hp, float (&h)[16 / (DT ? 2 : 4)]) {
-    const f4v h0 = *(const LDS f4v *)hp;
-    h[0] = h0.x; h[1] = h0.y; h[2] = h0.z; h[3] = h0.w;
-    if constexpr (DT == 1) {
-        const f4v h1 = *(const LDS f4v *)(hp + 4);
-        h[4] = h1.x; h[5] = h1.y; h[6] = h1.z; h[7] = h1.w;
+__device__ __forceinline__ void piece_in(const LDS float *hp, float (&h)[wepl(DT)]) {
+#pragma unroll
+    for (int k = 0; k < wepl(DT); k += 4) {
+        const f4v t = *(const LDS f4v *)(hp + k);
+        h[k] = t.x; h[k + 1] = t.y; h[k + 2] = t.z; h[k + 3] = t.w;
     }
 }
 
@@ -364,9 +404,17 @@ template <int DT, int GQ, int LPP, bool LOGITS, bool PMAP>
 __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const MkParams p) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_[];
     LDS unsigned char *smem = (LDS unsigned char *)smem_;
-    constexpr int EB = DT ? 2 : 4;          // bytes per element
-    constexpr int EPL = 16 / EB;            // elements per 16-byte lane piece
-    constexpr int EPC = MK_CHUNK_BYTES / EB;  // elements per 1 KiB chunk
+    // DT 0 float32, 1 bfloat16, 2 weight-only INT8: int8 matrices with
+    // per-row scales, the cache and the embedding in bfloat16 (CDT 1).
+    constexpr int CDT = DT == 2 ? 1 : DT;   // storage of the cache and the embedding
+    constexpr int EB = CDT ? 2 : 4;         // bytes per cache / embedding element
+    constexpr int EPL = 16 / EB;            // cache elements per 16-byte lane piece
+    constexpr int EPLW = wepl(DT);          // weight elements per 16-byte lane piece
+    constexpr int EBW = 16 / EPLW;          // bytes per weight element
+    constexpr int EPCW = MK_CHUNK_BYTES * EPLW / 16;  // weight elements per 1 KiB chunk
+    // the register input paths (rows of exactly four chunks, down row groups of
+    // four pieces) are built for float32 and bfloat16 pieces
+    constexpr bool REGP = DT != 2;
     constexpr int PPC = 64 / LPP;           // cache positions per 1 KiB chunk
     constexpr int BP = 8 * PPC;             // positions per KV slot (8 K chunks + 8 V chunks)
     constexpr int DH = LPP * 16 / EB;       // head dim
@@ -375,7 +423,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
     const int w = blockIdx.x, G = p.grid, NS = p.ring_slots, L = p.L;
     constexpr int d = DH;
 
-    // LDS layout: ring | vec | out | xown | rope | ss | control
+    // LDS layout: ring | vec | out | xown | rope | ss | control | INT8 scales
     LDS unsigned char *ring = smem;
     LDS float *vec = (LDS float *)(smem + NS * MK_SLOT_BYTES);
     LDS float *outv = vec + p.lds_vec_floats;
@@ -383,9 +431,10 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
     LDS float *ropel = xown + 64;  // [64][4] rotary (cos, sin) pairs of the first 64 QKV units
     LDS float *ssp = ropel + 256;
     volatile LDS int *ctl = (volatile LDS int *)(ssp + MK_NUM_CONSUMERS);  // [1] abort step, [8] consumer meetings
+    LDS float *sbuf = ssp + MK_NUM_CONSUMERS + 16;  // [2][lds_sc_floats] per-row scales (DT 2), by layer parity
 
     Geo g;
-    make_geo(p, w, EPL, g);
+    make_geo(p, w, EPLW, g);
 
     // Attention split of this workgroup: KV head kvj, positions [t0, t1).
     const int S = p.splits;
@@ -456,7 +505,8 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
         const unsigned char *it_ptr = p.packed;
         int64_t it_step = 0, kv_rem = 0;  // kv_rem: bytes of this wave's chunks left in the split
         auto last_kind = [&]() { return it_k == 5 || (!LOGITS && it_l == L - 1 && it_k == 4); };
-        // past the end of the stream: harmless re-reads of the first bytes of the weights
+        // past the end of the stream: harmless re-reads of the packed buffer's
+        // opening slot (zeros, owned by no stage)
         auto finish = [&]() {
             done = true;
             it_kv = false;
@@ -509,9 +559,10 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
         };
         stage_setup();
         // This lane's 16 bytes of chunk c of the current slot.  Cache rows
-        // past the split re-read the first bytes of the weights instead (the
-        // consumers mask those positions).  Global loads: direct-to-LDS
-        // buffer loads measured slower for this stream.
+        // past the split read the packed buffer's zeroed opening slot instead
+        // (the consumers mask those positions; the values they multiply by 0
+        // are zeros).  Global loads: direct-to-LDS buffer loads measured
+        // slower for this stream.
         auto piece_src = [&](int c) -> const GLB u4v * {
             const int64_t o = (int64_t)c * MK_CHUNK_BYTES + lane * 16;
             return (const GLB u4v *)(!it_kv || o < kv_rem ? it_ptr + o : p.packed + lane * 16);
@@ -713,6 +764,45 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
         return ctl[1] == 0;
     };
+    // ---- per-row scales of the INT8 matrices (DT 2) ----
+    // Block bl (a layer's QKV, O, gate/up and down rows of this workgroup;
+    // bl == L: its LM-head rows) is read into registers -- consumer c lane i
+    // holds entries j*256 + c*64 + i -- while the gate/up weights of layer
+    // bl-1 stream, and stored to LDS copy bl & 1 when the down stage of that
+    // layer opens.  So the loads never stand in a dependency wait, and a
+    // copy is rewritten only after the last reader of the block two layers
+    // back (the down reduction) has passed a consumer meeting.  Block 0 is
+    // read and stored when the step starts.
+    float sreg[4];
+    auto sc_fetch = [&](int bl) {
+        if constexpr (DT == 2) {
+            const bool head = bl == L;
+            const float *src = head ? p.scl + (size_t)L * G * p.sc_blk + (size_t)w * p.sc_lm
+                                    : p.scl + ((size_t)bl * G + w) * p.sc_blk;
+            // entries past the block read as 0 (buffer range check)
+            const __amdgpu_buffer_rsrc_t rs = rsrc(src, (uint32_t)(head ? p.sc_lm : p.sc_blk) * 4u);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                sreg[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (uint32_t)(j * 256 + ct) * 4u, 0, 0));
+        }
+    };
+    auto sc_park = [&](int bl) {
+        if constexpr (DT == 2) {
+            LDS float *dst = sbuf + (bl & 1) * p.lds_sc_floats;
+            const int n = bl == L ? p.sc_lm : p.sc_blk;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (j * 256 + ct < n) dst[j * 256 + ct] = sreg[j];
+        }
+    };
+    // the LDS copy of block bl
+    auto scl_of = [&](int bl) -> const LDS float * { return sbuf + (bl & 1) * p.lds_sc_floats; };
+    // row i's scale in the copy sc (1 when the weights are not INT8)
+    auto rsc = [&](const LDS float *sc, int i) -> float {
+        if constexpr (DT == 2) return sc[i];
+        else return 1.0f;
+    };
+
     // Gather n (even) tagged elements into vec (times gain, if given),
     // zero-padded to pad.  The four consumers take interleaved 16-byte pieces
     // (two records), so the workgroup reads each element once; ssp[c] gets
@@ -792,7 +882,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
                 const int qi = base + u * 256;
                 if (xsrc) {
                     xv[u] = as_f4(ld16c(rx, (uint32_t)qi * 16u));
-                } else if constexpr (DT == 1) {
+                } else if constexpr (CDT == 1) {
                     const uint64_t e = qi < nqd ? ((const uint64_t *)erow)[qi] : 0ull;
                     xv[u] = f4v{bf_lo((uint32_t)e), bf_hi((uint32_t)e), bf_lo((uint32_t)(e >> 32)), bf_hi((uint32_t)(e >> 32))};
                 } else {
@@ -822,17 +912,18 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
         return 1.0f / sqrtf(ss / (float)n + p.eps);
     };
     // Register path (rows of exactly four chunks): every consumer loads the
-    // lane's slice of the input vector -- element q*EPC + lane*EPL + e feeds
+    // lane's slice of the input vector -- element q*EPCW + lane*EPLW + e feeds
     // chunk q -- straight into registers with the gain applied, and returns
-    // the full sum of squares of x (it sees all 4*EPC elements).
-    auto load_direct = [&](const float *xsrc, const void *erow, const float *gain, float (&hr)[4][EPL]) -> float {
-        f4v xv[4][EPL / 4], gv[4][EPL / 4];
-        const __amdgpu_buffer_rsrc_t rx = rsrc(xsrc ? (const void *)xsrc : erow, 4u * EPC * (xsrc ? 4u : (uint32_t)EB));
+    // the full sum of squares of x (it sees all 4*EPCW elements).  Float32 and
+    // bfloat16 weights (REGP) only.
+    auto load_direct = [&](const float *xsrc, const void *erow, const float *gain, float (&hr)[4][EPLW]) -> float {
+        f4v xv[4][EPLW / 4], gv[4][EPLW / 4];
+        const __amdgpu_buffer_rsrc_t rx = rsrc(xsrc ? (const void *)xsrc : erow, 4u * EPCW * (xsrc ? 4u : (uint32_t)EB));
 #pragma unroll
         for (int q = 0; q < 4; ++q)
 #pragma unroll
-            for (int k4 = 0; k4 < EPL / 4; ++k4) {
-                const int el = q * EPC + lane * EPL + 4 * k4;  // first of 4 elements
+            for (int k4 = 0; k4 < EPLW / 4; ++k4) {
+                const int el = q * EPCW + lane * EPLW + 4 * k4;  // first of 4 elements
                 if (xsrc) {
                     xv[q][k4] = as_f4(ld16c(rx, (uint32_t)el * 4u));
                 } else if constexpr (DT == 1) {
@@ -851,7 +942,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
 #pragma unroll
         for (int q = 0; q < 4; ++q)
 #pragma unroll
-            for (int k4 = 0; k4 < EPL / 4; ++k4) {
+            for (int k4 = 0; k4 < EPLW / 4; ++k4) {
                 const f4v x = xv[q][k4];
                 ss = fmaf(x.x, x.x, ss);
                 ss = fmaf(x.y, x.y, ss);
@@ -870,7 +961,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
     // ---- GEMV data steps ----
     // Register path: slot n holds row n of this consumer (4 chunks); the four
     // 16-byte ring reads are issued before any arithmetic.
-    auto gemv_reg_steps = [&](int st, int l, const float (&hr)[4][EPL]) {
+    auto gemv_reg_steps = [&](int st, int l, const float (&hr)[4][EPLW]) {
         const int units = g.units[st];
         for (int n = 0; n < g.nsl[st]; ++n) {
             barrier();
@@ -914,9 +1005,9 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
     // of four rows, so the lane's eight input elements are read from LDS once
     // and multiply four weight pieces, with one accumulator per row.  The
     // remaining rows follow row after row.
-    auto gemv_lds_steps = [&](int st, int l) {
+    auto gemv_lds_steps = [&](int st, int l) __attribute__((always_inline)) {
         const int units = g.units[st], rbp = p.st[st].rbp;
-        const int full = mk_row_groups(rbp) ? units / 4 : 0;
+        const int full = mk_row_groups(rbp, EBW) ? units / 4 : 0;
         int n = 0;
         for (int grp = 0; grp < full; ++grp) {
             float acc[4] = {0.f, 0.f, 0.f, 0.f};
@@ -924,8 +1015,8 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
                 barrier();
                 stamp_step(l, 0);
                 const LDS unsigned char *bp = ring + js * MK_SLOT_BYTES + c * 4 * MK_CHUNK_BYTES + lane * 16;
-                float hv[EPL];
-                piece_in<DT>(vec + s * EPC + lane * EPL, hv);
+                float hv[EPLW];
+                piece_in<DT>(vec + s * EPCW + lane * EPLW, hv);
                 float d[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) d[j] = piece_dot_reg<DT>(bp + j * MK_CHUNK_BYTES, hv);
@@ -948,11 +1039,11 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
             const LDS unsigned char *bp = ring + js * MK_SLOT_BYTES + c * 4 * MK_CHUNK_BYTES + lane * 16;
             if ((rbp & 3) == 0) {  // the piece lies inside one row
                 if (row_c < units) {
-                    const LDS float *hp = vec + kc * EPC + lane * EPL;
+                    const LDS float *hp = vec + kc * EPCW + lane * EPLW;
                     const float d0 = piece_dot<DT>(bp, hp);
-                    const float d1 = piece_dot<DT>(bp + MK_CHUNK_BYTES, hp + EPC);
-                    const float d2 = piece_dot<DT>(bp + 2 * MK_CHUNK_BYTES, hp + 2 * EPC);
-                    const float d3 = piece_dot<DT>(bp + 3 * MK_CHUNK_BYTES, hp + 3 * EPC);
+                    const float d1 = piece_dot<DT>(bp + MK_CHUNK_BYTES, hp + EPCW);
+                    const float d2 = piece_dot<DT>(bp + 2 * MK_CHUNK_BYTES, hp + 2 * EPCW);
+                    const float d3 = piece_dot<DT>(bp + 3 * MK_CHUNK_BYTES, hp + 3 * EPCW);
                     acc += (d0 + d1) + (d2 + d3);
                     kc += 4;
                     if (kc == rbp) {
@@ -967,7 +1058,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
 #pragma unroll
                 for (int qi = 0; qi < 4; ++qi) {
                     if (row_c < units) {
-                        acc += piece_dot<DT>(bp + qi * MK_CHUNK_BYTES, vec + kc * EPC + lane * EPL);
+                        acc += piece_dot<DT>(bp + qi * MK_CHUNK_BYTES, vec + kc * EPCW + lane * EPLW);
                         if (++kc == rbp) {
                             const float t = wave_sum(acc);
                             if (lane == 0) outv[row_c * 4 + c] = t;
@@ -1005,12 +1096,12 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
             // Every step covers four pieces of one row group: straight-line
             // code with four independent dot products; with kp == 4 the
             // workgroup's SwiGLU outputs stay in registers.
-            float ar[4][EPL];
-            if (kp == 4) {
+            float ar[4][EPLW];
+            if (REGP && kp == 4) {
 #pragma unroll
                 for (int qq = 0; qq < 4; ++qq)
 #pragma unroll
-                    for (int e = 0; e < EPL; ++e) ar[qq][e] = vec[qq * EPL + e];
+                    for (int e = 0; e < EPLW; ++e) ar[qq][e] = vec[qq * EPLW + e];
             }
             int gl = 0, q = 0;
             float acc = 0.f;
@@ -1021,12 +1112,12 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
                 if (grp < ng) {  // wave-uniform
                     const LDS unsigned char *bp = ring + js * MK_SLOT_BYTES + c * 4 * MK_CHUNK_BYTES + lane * 16;
                     float dq[4];
-                    if (kp == 4) {
+                    if (REGP && kp == 4) {
 #pragma unroll
                         for (int qq = 0; qq < 4; ++qq) dq[qq] = piece_dot_reg<DT>(bp + qq * MK_CHUNK_BYTES, ar[qq]);
                     } else {
 #pragma unroll
-                        for (int qq = 0; qq < 4; ++qq) dq[qq] = piece_dot<DT>(bp + qq * MK_CHUNK_BYTES, vec + (q + qq) * EPL);
+                        for (int qq = 0; qq < 4; ++qq) dq[qq] = piece_dot<DT>(bp + qq * MK_CHUNK_BYTES, vec + (q + qq) * EPLW);
                     }
                     acc += (dq[0] + dq[1]) + (dq[2] + dq[3]);
                     q += 4;
@@ -1053,7 +1144,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
             for (int qq = 0; qq < 4; ++qq) {
                 const int grp = c + 4 * gl;
                 if (grp < ng) {  // wave-uniform
-                    acc += piece_dot<DT>(bp + qq * MK_CHUNK_BYTES, vec + q * EPL);
+                    acc += piece_dot<DT>(bp + qq * MK_CHUNK_BYTES, vec + q * EPLW);
                     if (++q == kp) {
                         const int row = grp * 64 + lane;
                         if (row < p.H) stll(dst + row, acc, tg);
@@ -1083,12 +1174,14 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
             return (uint32_t)(((size_t)wq * H + r0 + 2 * i) * 8u);
         };
         if (!gather_fn(vec, G * hp, rs, off, nullptr, G * nr, G * nr, tag_of(l))) return false;
+        // INT8: the down rows' scales follow the QKV, O and gate/up rows in the block
+        const LDS float *scd = scl_of(l) + 4 * (g.units[ST_QKV] + g.units[ST_O] + g.units[ST_GU]);
         for (int i = c; i < nr; i += MK_NUM_CONSUMERS) {
             float sum = 0.f;
             for (int wq = lane; wq < G; wq += 64) sum += vec[wq * nr + i];
             sum = wave_sum(sum);
             if (lane == 0) {
-                const float xn = xown[i] + sum;
+                const float xn = xown[i] + sum * rsc(scd, i);
                 xown[i] = xn;
                 stll(xdst + r0 + i, xn, tag_of(l + 1));
             }
@@ -1120,9 +1213,10 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
     // Fold NQ chunks of positions (each lane holds one position of each
     // chunk, PPC positions per chunk) into the running state: all scores
     // first, then one running-max update, rescale and V accumulation per
-    // head.  Invalid positions get probability 0.  Their V values are finite
-    // (the loaders read weights, not the cache, past a split's positions, and
-    // the register tail reads a valid row), so 0 * v adds nothing.
+    // head.  Invalid positions get probability 0.  Their V values are zeros
+    // (the loaders read the packed buffer's zeroed opening slot, not the
+    // cache, past a split's positions) or a valid row (the register tail), so
+    // 0 * v adds nothing.
     // kget(q, e) / vget(q, e): element e of the lane's K / V piece of chunk q.
     // qget(h, e): element e of the lane's dims of head h's query.
     auto attn_fold_q = [&](auto &A, auto nq_tag, auto &&qget, auto &&kget, auto &&vget, const bool *valid) {
@@ -1217,10 +1311,11 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
         const int nqd = p.nh * d, nk = p.nkv * d;
         const uint32_t tg = tag_of(l);
         uint64_t *const qkv_l = p.ll_qkv + (size_t)(l & 1) * p.nkv * (GQ + 2) * d;
+        const LDS float *sc = scl_of(l);  // INT8: the QKV rows' scales open the block
         for (int u = lane; u < g.units[ST_QKV]; u += 64) {
             const int gr0 = (g.unit0[ST_QKV] + u) * 4;
-            const float y0 = outv[u * 4] * inv, y1 = outv[u * 4 + 1] * inv;
-            const float y2 = outv[u * 4 + 2] * inv, y3 = outv[u * 4 + 3] * inv;
+            const float y0 = outv[u * 4] * inv * rsc(sc, u * 4), y1 = outv[u * 4 + 1] * inv * rsc(sc, u * 4 + 1);
+            const float y2 = outv[u * 4 + 2] * inv * rsc(sc, u * 4 + 2), y3 = outv[u * 4 + 3] * inv * rsc(sc, u * 4 + 3);
             if (gr0 < nqd + nk) {
                 const bool isq = gr0 < nqd;
                 const int r = isq ? gr0 : gr0 - nqd;
@@ -1238,7 +1333,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
                 } else {
                     unsigned char *row = (unsigned char *)p.kc + ((size_t)l * p.nkv + head) * head_bytes + (size_t)P * d * EB;
                     uint64_t *kn = qkv_l + (size_t)head * (GQ + 2) * d + (size_t)GQ * d;
-                    if constexpr (DT == 1) {
+                    if constexpr (CDT == 1) {
                         const uint32_t ba0 = f2bf(a0), ba1 = f2bf(a1), bb0 = f2bf(b0), bb1 = f2bf(b1);
                         stcu((uint32_t *)(row + m0 * 2), ba0 | (ba1 << 16));
                         stcu((uint32_t *)(row + (m0 + d / 2) * 2), bb0 | (bb1 << 16));
@@ -1262,7 +1357,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
                 const int head = r / d, e = r % d;
                 unsigned char *row = (unsigned char *)p.vc + ((size_t)l * p.nkv + head) * head_bytes + (size_t)P * d * EB;
                 uint64_t *vn = qkv_l + (size_t)head * (GQ + 2) * d + (size_t)(GQ + 1) * d;
-                if constexpr (DT == 1) {
+                if constexpr (CDT == 1) {
                     const uint32_t c0 = f2bf(y0), c1 = f2bf(y1), c2 = f2bf(y2), c3 = f2bf(y3);
                     stcu((uint32_t *)(row + e * 2), c0 | (c1 << 16));
                     stcu((uint32_t *)(row + e * 2 + 4), c2 | (c3 << 16));
@@ -1283,11 +1378,12 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
             }
         }
     };
-    auto epi_residual = [&](int st, uint64_t *xdst, uint32_t tg) {  // O or DOWN: x += out for the workgroup's rows
-        for (int i = lane; i < g.units[st] * 4; i += 64) {
-            const int r = g.unit0[st] * 4 + i;
+    auto epi_o = [&](int l, uint64_t *xdst, uint32_t tg) {  // O(l): x += out for the workgroup's rows
+        const LDS float *sc = scl_of(l) + 4 * g.units[ST_QKV];  // INT8: the O rows' scales
+        for (int i = lane; i < g.units[ST_O] * 4; i += 64) {
+            const int r = g.unit0[ST_O] * 4 + i;
             if (r < p.H) {
-                const float xn = xown[i] + outv[i];
+                const float xn = xown[i] + outv[i] * rsc(sc, i);
                 xown[i] = xn;
                 stll(xdst + r, xn, tg);
             }
@@ -1295,11 +1391,12 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
     };
     // SwiGLU of this workgroup's gate/up rows: a[f0 + m] -> vec[m] (the
     // down stage's input stays in the workgroup), zero-padded to kp pieces.
-    auto epi_gu = [&](float inv) {
-        for (int m = lane; m < g.dn.kp * EPL; m += 64) {
+    auto epi_gu = [&](int l, float inv) {
+        const LDS float *sc = scl_of(l) + 4 * (g.units[ST_QKV] + g.units[ST_O]);  // INT8: the gate/up rows' scales
+        for (int m = lane; m < g.dn.kp * EPLW; m += 64) {
             float av = 0.f;
             if (m < g.dn.nf) {
-                const float gv = outv[2 * m] * inv, uv = outv[2 * m + 1] * inv;
+                const float gv = outv[2 * m] * inv * rsc(sc, 2 * m), uv = outv[2 * m + 1] * inv * rsc(sc, 2 * m + 1);
                 av = gv / (1.0f + __expf(-gv)) * uv;
             }
             vec[m] = av;
@@ -1361,7 +1458,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
         for (int i = lane; i < g.units[ST_LM] * 4; i += 64) {
             const int r = g.unit0[ST_LM] * 4 + i;
             if (r < p.V) {
-                const float lg = outv[i] * inv;
+                const float lg = outv[i] * inv * rsc(scl_of(L), i);
                 if (p.logits) p.logits[r] = lg;
                 if (lg > best) { best = lg; besti = r; }
             }
@@ -1415,12 +1512,12 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
     // ---- the program ----
     const int nq = p.nh * d;
     // The register path's input slice (gain (.) x) from the gathered vector.
-    auto regs_from_vec = [&](float (&hr)[4][EPL]) {
+    auto regs_from_vec = [&](float (&hr)[4][EPLW]) {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
 #pragma unroll
-            for (int e = 0; e < EPL; e += 4) {
-                const f4v t = *(const LDS f4v *)(vec + q * EPC + lane * EPL + e);
+            for (int e = 0; e < EPLW; e += 4) {
+                const f4v t = *(const LDS f4v *)(vec + q * EPCW + lane * EPLW + e);
                 hr[q][e] = t.x;
                 hr[q][e + 1] = t.y;
                 hr[q][e + 2] = t.z;
@@ -1429,9 +1526,9 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
     };
     // The GEMV data steps of stage st, input in vec (gathered) or, for the
     // register path, loaded from it.
-    auto gemv_from_vec = [&](int st, int l, int b) {
-        if (p.st[st].rbp == 4) {
-            float hr[4][EPL];
+    auto gemv_from_vec = [&](int st, int l, int b) __attribute__((always_inline)) {
+        if (REGP && p.st[st].rbp == 4) {
+            float hr[4][EPLW];
             regs_from_vec(hr);
             stamp(b, 3);
             gemv_reg_steps(st, l, hr);
@@ -1440,6 +1537,8 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
             gemv_lds_steps(st, l);
         }
     };
+    sc_fetch(0);  // INT8: layer 0's scales
+    sc_park(0);
     for (int l = 0; l < L && ok; ++l) {
         // ===== stage QKV(l); boundary: [epilogue DOWN(l-1)] + input x =====
         float inv_q = 0.f;
@@ -1458,18 +1557,18 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
                     const int r = g.unit0[ST_O] * 4 + i;
                     float xv = 0.f;
                     if (r < p.H) {
-                        if constexpr (DT == 1) xv = __uint_as_float((uint32_t)((const uint16_t *)erow)[r] << 16);
+                        if constexpr (CDT == 1) xv = __uint_as_float((uint32_t)((const uint16_t *)erow)[r] << 16);
                         else xv = ((const float *)erow)[r];
                     }
                     xown[i] = xv;
                 }
-                if (p.st[ST_QKV].rbp == 4) {
-                    float hr[4][EPL];
+                if (REGP && p.st[ST_QKV].rbp == 4) {
+                    float hr[4][EPLW];
                     inv_q = inv_of(load_direct(nullptr, erow, gain, hr), p.H);
                     stamp(5 * l, 3);
                     gemv_reg_steps(ST_QKV, l, hr);
                 } else {
-                    load_normed(nullptr, erow, gain, p.H, p.st[ST_QKV].rbp * EPC);
+                    load_normed(nullptr, erow, gain, p.H, p.st[ST_QKV].rbp * EPCW);
                     ok = csync();
                     if (!ok) break;
                     inv_q = inv_lds(p.H);
@@ -1479,7 +1578,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
             } else {
                 ok = down_reduce(l - 1, p.ll_xq + (size_t)(l & 1) * p.H);
                 stamp(5 * l, 1);
-                ok = ok && gather(p.ll_xq + (size_t)(l & 1) * p.H, p.H, gain, p.st[ST_QKV].rbp * EPC, tag_of(l));
+                ok = ok && gather(p.ll_xq + (size_t)(l & 1) * p.H, p.H, gain, p.st[ST_QKV].rbp * EPCW, tag_of(l));
                 stamp(5 * l, 2);
                 if (!ok) break;
                 inv_q = inv_lds(p.H);
@@ -1506,8 +1605,8 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
                     const size_t rbase = (((size_t)l * p.nkv + kvj) * p.max_seq + (size_t)t0 + (size_t)nfull * BP) * d * EB;
                     const uint32_t tbytes = (uint32_t)(PPC * d * EB);
                     const uint32_t roff = (uint32_t)(((tvalid ? tg : 0) * d + e0) * EB);
-                    piece_load_buf<DT>(rsrc((const unsigned char *)p.kc + rbase, tbytes), roff, kt);
-                    piece_load_buf<DT>(rsrc((const unsigned char *)p.vc + rbase, tbytes), roff, vt);
+                    piece_load_buf<CDT>(rsrc((const unsigned char *)p.kc + rbase, tbytes), roff, kt);
+                    piece_load_buf<CDT>(rsrc((const unsigned char *)p.vc + rbase, tbytes), roff, vt);
                 }
                 // This group's rotated queries and, in the last split, the K/V
                 // row of position pos (bf16-rounded like the cache) into LDS in
@@ -1624,8 +1723,8 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
                                 vr[q] = *(const LDS u4v *)(vb + chunk * MK_CHUNK_BYTES + lane * 16);
                             }
                             attn_fold_q(P, std::integral_constant<int, 2>{}, qlds,
-                                        [&](int q, int e) { return piece_elem<DT>(kr[q], e); },
-                                        [&](int q, int e) { return piece_elem<DT>(vr[q], e); }, valid);
+                                        [&](int q, int e) { return piece_elem<CDT>(kr[q], e); },
+                                        [&](int q, int e) { return piece_elem<CDT>(vr[q], e); }, valid);
                             if (n == nsl_kv - 1) finish_pm();
                             js = js + 1 == NS ? 0 : js + 1;
                             stamp_step(l, 1);
@@ -1681,8 +1780,8 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
                             kr[q] = *(const LDS u4v *)(kb + chunk * MK_CHUNK_BYTES + lane * 16);
                             vr[q] = *(const LDS u4v *)(vb + chunk * MK_CHUNK_BYTES + lane * 16);
                         }
-                        attn_fold(A, std::integral_constant<int, NQB>{}, [&](int q, int e) { return piece_elem<DT>(kr[q], e); },
-                                  [&](int q, int e) { return piece_elem<DT>(vr[q], e); }, valid);
+                        attn_fold(A, std::integral_constant<int, NQB>{}, [&](int q, int e) { return piece_elem<CDT>(kr[q], e); },
+                                  [&](int q, int e) { return piece_elem<CDT>(vr[q], e); }, valid);
                     }
                     if (n == nsl_kv - 1) finish();
                     js = js + 1 == NS ? 0 : js + 1;
@@ -1700,7 +1799,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
             stamp(5 * l + 2, 0);
             const bool mine = combine_slice(l);
             stamp(5 * l + 2, 1);
-            ok = mine && gather(p.ll_o + (size_t)(l & 1) * nq, nq, nullptr, p.st[ST_O].rbp * EPC, tag_of(l));
+            ok = mine && gather(p.ll_o + (size_t)(l & 1) * nq, nq, nullptr, p.st[ST_O].rbp * EPCW, tag_of(l));
             stamp(5 * l + 2, 2);
             if (!ok) break;
             gemv_from_vec(ST_O, l, 5 * l + 2);
@@ -1711,13 +1810,14 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
         {
             barrier();
             stamp(5 * l + 3, 0);
-            if (c == 0) epi_residual(ST_O, p.ll_xg + (size_t)(l & 1) * p.H, tag_of(l));
+            if (c == 0) epi_o(l, p.ll_xg + (size_t)(l & 1) * p.H, tag_of(l));
             stamp(5 * l + 3, 1);
-            ok = gather(p.ll_xg + (size_t)(l & 1) * p.H, p.H, p.g_ffn + (size_t)l * p.H, p.st[ST_GU].rbp * EPC,
+            ok = gather(p.ll_xg + (size_t)(l & 1) * p.H, p.H, p.g_ffn + (size_t)l * p.H, p.st[ST_GU].rbp * EPCW,
                         tag_of(l));
             stamp(5 * l + 3, 2);
             if (!ok) break;
             inv_g = inv_lds(p.H);
+            if (LOGITS || l + 1 < L) sc_fetch(l + 1);  // INT8: the next block (layer l + 1, or the LM head)
             gemv_from_vec(ST_GU, l, 5 * l + 3);
         }
 
@@ -1725,7 +1825,8 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
         {
             barrier();
             stamp(5 * l + 4, 0);
-            if (c == 0) epi_gu(inv_g);
+            if (c == 0) epi_gu(l, inv_g);
+            if (LOGITS || l + 1 < L) sc_park(l + 1);  // INT8: the next block (read during gate/up) to LDS
             stamp(5 * l + 4, 1);
             ok = csync();
             stamp(5 * l + 4, 2);
@@ -1740,7 +1841,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
         stamp(5 * L, 0);
         ok = down_reduce(L - 1, p.ll_xq + (size_t)(L & 1) * p.H);
         stamp(5 * L, 1);
-        ok = ok && gather(p.ll_xq + (size_t)(L & 1) * p.H, p.H, p.g_final, p.st[ST_LM].rbp * EPC, tag_of(L));
+        ok = ok && gather(p.ll_xq + (size_t)(L & 1) * p.H, p.H, p.g_final, p.st[ST_LM].rbp * EPCW, tag_of(L));
         stamp(5 * L, 2);
         if (ok) {
             const float inv_lm = inv_lds(p.H);
@@ -1793,7 +1894,8 @@ MK_PART_EXPAND2(MK_PART_DT, MK_PART_GQ)
     extern template __global__ void mk_decode_kernel<DT_, GQ_, LPP_, LG_, PM_>(const MkParams);
 #define MK_ALL_PARTS(X) \
     MK_FOR_PM(X, 0, 1) MK_FOR_PM(X, 0, 2) MK_FOR_PM(X, 0, 4) MK_FOR_PM(X, 0, 8) \
-    MK_FOR_PM(X, 1, 1) MK_FOR_PM(X, 1, 2) MK_FOR_PM(X, 1, 4) MK_FOR_PM(X, 1, 8)
+    MK_FOR_PM(X, 1, 1) MK_FOR_PM(X, 1, 2) MK_FOR_PM(X, 1, 4) MK_FOR_PM(X, 1, 8) \
+    MK_FOR_PM(X, 2, 1) MK_FOR_PM(X, 2, 2) MK_FOR_PM(X, 2, 4) MK_FOR_PM(X, 2, 8)
 MK_ALL_PARTS(MK_EXTERN)
 
 // ---- host-side launch ---------------------------------------------------
@@ -1814,21 +1916,21 @@ KernelFn pick(int dtype, int gq, int lpp, bool logits, bool pmap) {
     MK_PICK(1, 1, 16) MK_PICK(1, 2, 16) MK_PICK(1, 4, 16) MK_PICK(1, 8, 16)
     MK_PICK(0, 1, 8) MK_PICK(0, 2, 8) MK_PICK(0, 4, 8) MK_PICK(0, 8, 8)
     MK_PICK(0, 1, 16) MK_PICK(0, 2, 16) MK_PICK(0, 4, 16) MK_PICK(0, 8, 16)
+    MK_PICK(2, 1, 8) MK_PICK(2, 2, 8) MK_PICK(2, 4, 8) MK_PICK(2, 8, 8)
+    MK_PICK(2, 1, 16) MK_PICK(2, 2, 16) MK_PICK(2, 4, 16) MK_PICK(2, 8, 16)
 #undef MK_PICK
     return nullptr;
 }
 }  // namespace
 
-extern "C" int mk_kernel_lds_bytes(int ring_slots, int vec_floats, int out_rows, int dtype, int d, int gq) {
-    (void)dtype;
-    (void)d;
-    (void)gq;
-    const int floats = vec_floats + out_rows + 64 + 256 + MK_NUM_CONSUMERS + 16;
+// sc_floats: both LDS copies of the INT8 scale blocks (0 for other dtypes)
+extern "C" int mk_kernel_lds_bytes(int ring_slots, int vec_floats, int out_rows, int sc_floats) {
+    const int floats = vec_floats + out_rows + 64 + 256 + MK_NUM_CONSUMERS + 16 + sc_floats;
     return ring_slots * MK_SLOT_BYTES + floats * 4;
 }
 
 extern "C" int mk_launch_decode(const MkParams *p, int dtype, int cooperative, void *stream) {
-    const int eb = dtype ? 2 : 4;
+    const int eb = dtype ? 2 : 4;  // cache element bytes (dtype 2 keeps a bf16 cache)
     const int lpp = p->d * eb / 16;
     const int gq = p->nh / p->nkv;
     // per-length attention mapping: position-major when a split holds at
@@ -1840,7 +1942,7 @@ extern "C" int mk_launch_decode(const MkParams *p, int dtype, int cooperative, v
     if (!fn) return (int)hipErrorInvalidValue;
     // the dynamic-LDS limit of every instantiation was raised to MK_LDS_LIMIT
     // when the handle was created (mk_kernel_max_blocks_per_cu)
-    const int lds = mk_kernel_lds_bytes(p->ring_slots, p->lds_vec_floats, p->lds_out_rows, dtype, p->d, gq);
+    const int lds = mk_kernel_lds_bytes(p->ring_slots, p->lds_vec_floats, p->lds_out_rows, 2 * p->lds_sc_floats);
     hipError_t e;
     MkParams copy = *p;
     void *args[] = {&copy};

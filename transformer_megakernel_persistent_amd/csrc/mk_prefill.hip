@@ -95,7 +95,7 @@ __device__ __forceinline__ RowLoc row_loc(const MkStage &st, const unsigned char
     const int w = unit_owner(u, U, grid);
     const int u0 = unit_first(w, U, grid), units = unit_first(w + 1, U, grid) - u0;
     const int i = n - 4 * u0, c = i & 3, rc = i >> 2;
-    const int full = mk_row_groups(st.rbp) ? units / 4 : 0;
+    const int full = mk_row_groups(st.rbp, 2) ? units / 4 : 0;  // bf16 weights
     RowLoc r;
     r.base = layer_block + st.wg_off[w] + c * 4 * MK_CHUNK_BYTES;
     if (rc < full * 4) {

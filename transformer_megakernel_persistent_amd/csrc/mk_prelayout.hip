@@ -78,7 +78,7 @@ __global__ __launch_bounds__(256) void prelayout_kernel(unsigned char *dst_block
     const int nsl = (units * st.rbp + 3) / 4;
     if (chunk >= nsl * MK_CHUNKS_PER_SLOT) return;
     int row_c, kc;
-    mk_stream_pos(qq, units, st.rbp, row_c, kc);
+    mk_stream_pos(qq, units, st.rbp, eb, row_c, kc);
     if (row_c < units) {
         const int gr = (unit0 + row_c) * 4 + c;  // packed row
         if (gr < st.rows) {
@@ -117,6 +117,51 @@ __global__ __launch_bounds__(256) void prelayout_kernel(unsigned char *dst_block
                (chunk % MK_CHUNKS_PER_SLOT) * MK_CHUNK_BYTES + lane * 16) = val;
 }
 
+// Per-row scales of the INT8 matrices, one block per workgroup (layout in
+// MkParams::scl): the rows of each stage in the order the workgroup's
+// epilogues index them.  One workgroup of threads per block.
+__global__ __launch_bounds__(256) void prelayout_scales_kernel(float *scl, const MkParams p, int layer,
+                                                               const float *s_q, const float *s_k, const float *s_v,
+                                                               const float *s_o, const float *s_g, const float *s_u,
+                                                               const float *s_d) {
+    const int w = blockIdx.x, G = p.grid;
+    auto unit0 = [&](int k) { return (int)(((int64_t)w * p.st[k].units) / G); };
+    auto nunits = [&](int k) { return (int)(((int64_t)(w + 1) * p.st[k].units) / G) - unit0(k); };
+    if (layer == p.L) {
+        float *dst = scl + (size_t)p.L * G * p.sc_blk + (size_t)w * p.sc_lm;
+        const int n = nunits(ST_LM) * 4, r0 = unit0(ST_LM) * 4;
+        for (int i = threadIdx.x; i < p.sc_lm; i += blockDim.x) dst[i] = (i < n && r0 + i < p.V) ? s_q[r0 + i] : 0.f;
+        return;
+    }
+    float *dst = scl + ((size_t)layer * G + w) * p.sc_blk;
+    const int nq = nunits(ST_QKV) * 4, no = nunits(ST_O) * 4, ng = nunits(ST_GU) * 4;
+    const int nqd = p.nh * p.d, nk = p.nkv * p.d, d = p.d;
+    for (int i = threadIdx.x; i < p.sc_blk; i += blockDim.x) {
+        float v = 0.f;
+        if (i < nq) {
+            const int gr = unit0(ST_QKV) * 4 + i;  // packed QKV row
+            if (gr < nqd + nk) {
+                const int r = gr < nqd ? gr : gr - nqd;
+                const int head = r / d, wi = r % d;
+                const int srow = head * d + wi / 2 + (wi % 2) * (d / 2);  // rotary pairing of the packed rows
+                v = gr < nqd ? s_q[srow] : s_k[srow];
+            } else if (gr < nqd + 2 * nk) {
+                v = s_v[gr - nqd - nk];
+            }
+        } else if (i < nq + no) {
+            const int r = unit0(ST_O) * 4 + i - nq;
+            if (r < p.H) v = s_o[r];
+        } else if (i < nq + no + ng) {
+            const int gr = unit0(ST_GU) * 4 + i - nq - no;  // gate and up rows interleaved
+            if (gr < 2 * p.F) v = (gr % 2 == 0) ? s_g[gr / 2] : s_u[gr / 2];
+        } else if (i < nq + 2 * no + ng) {
+            const int r = unit0(ST_O) * 4 + i - nq - no - ng;  // the x rows this workgroup reduces
+            if (r < p.H) v = s_d[r];
+        }
+        dst[i] = v;
+    }
+}
+
 __global__ void to_f32_kernel(float *dst, const void *src, int64_t n, int dtype) {
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
         if (dtype == 1) dst[i] = __uint_as_float((uint32_t)((const uint16_t *)src)[i] << 16);
@@ -143,7 +188,17 @@ extern "C" int mk_launch_zero(void *dst, int64_t bytes, void *stream) {
     return (int)hipGetLastError();
 }
 
-extern "C" int mk_launch_prelayout_stage(unsigned char *dst, const MkStage *st, int grid, int kind, int dtype,
+extern "C" int mk_launch_prelayout_scales(float *scl, const MkParams *p, int layer, const float *const *src,
+                                          void *stream) {
+    const bool head = layer == p->L;
+    hipLaunchKernelGGL(prelayout_scales_kernel, dim3(p->grid), dim3(256), 0, (hipStream_t)stream, scl, *p, layer,
+                       src[0], head ? nullptr : src[1], head ? nullptr : src[2], head ? nullptr : src[3],
+                       head ? nullptr : src[4], head ? nullptr : src[5], head ? nullptr : src[6]);
+    return (int)hipGetLastError();
+}
+
+// eb: bytes per weight element (4 float32, 2 bfloat16, 1 int8)
+extern "C" int mk_launch_prelayout_stage(unsigned char *dst, const MkStage *st, int grid, int kind, int eb,
                                          const void *src0, const void *src1, const void *src2, int nh, int nkv,
                                          int d, void *stream) {
     // the largest per-workgroup slot count bounds the x-extent of the launch
@@ -151,13 +206,13 @@ extern "C" int mk_launch_prelayout_stage(unsigned char *dst, const MkStage *st, 
     for (int w = 0; w < grid; ++w) {
         const int U = st->units;
         const int u0 = (int)(((int64_t)w * U) / grid), u1 = (int)(((int64_t)(w + 1) * U) / grid);
-        const int nsl = kind == ST_DOWN ? mk_down_geo(w, grid, U, st->k, st->rows, dtype ? 8 : 4).nsl
+        const int nsl = kind == ST_DOWN ? mk_down_geo(w, grid, U, st->k, st->rows, 16 / eb).nsl
                                         : ((u1 - u0) * st->rbp + 3) / 4;
         if (nsl > max_nsl) max_nsl = nsl;
     }
     if (max_nsl == 0) return 0;
     dim3 g((max_nsl * MK_CHUNKS_PER_SLOT + 3) / 4, grid);
-    hipLaunchKernelGGL(prelayout_kernel, g, dim3(256), 0, (hipStream_t)stream, dst, *st, grid, kind, dtype ? 2 : 4,
+    hipLaunchKernelGGL(prelayout_kernel, g, dim3(256), 0, (hipStream_t)stream, dst, *st, grid, kind, eb,
                        (const unsigned char *)src0, (const unsigned char *)src1, (const unsigned char *)src2, nh, nkv, d);
     return (int)hipGetLastError();
 }

@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(_HERE, "libmk.so")
 MK_OK, MK_ERR_NULL, MK_ERR_SHAPE, MK_ERR_DTYPE, MK_ERR_RANGE = 0, 1, 2, 3, 4
 MK_ERR_NOMEM, MK_ERR_HIP, MK_ERR_DEVICE, MK_ERR_STATE, MK_ERR_TUNING, MK_ERR_SCRATCH = 5, 6, 7, 8, 9, 10
 MK_STATIC_SCRATCH_BYTES = 64 * 1024 * 1024
-MK_F32, MK_BF16 = 0, 1
+MK_F32, MK_BF16, MK_W8 = 0, 1, 2
+DTYPES = {"f32": MK_F32, "bf16": MK_BF16, "w8": MK_W8}
 
 EXPORTED = ("mk_create", "mk_create_deferred", "mk_load_weights", "mk_decode_step", "mk_decode_step_device_token",
             "mk_decode_step_device_token_noalloc", "mk_prefill_kv", "mk_get_device_error", "mk_get_info",
@@ -32,14 +33,17 @@ class ModelDesc(ctypes.Structure):
                 ("rope_theta", ctypes.c_double), ("dtype", ctypes.c_int32), ("tied_embeddings", ctypes.c_int32)]
 
 
+MATRIX_KINDS = ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")
+
+
 class LayerPtrs(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate", "w_up",
-                                               "w_down")]
+                                               "w_down")] + [("s_" + n, ctypes.c_void_p) for n in MATRIX_KINDS]
 
 
 class WeightPtrs(ctypes.Structure):
     _fields_ = [("embed", ctypes.c_void_p), ("final_norm", ctypes.c_void_p), ("lm_head", ctypes.c_void_p),
-                ("layers", ctypes.POINTER(LayerPtrs))]
+                ("layers", ctypes.POINTER(LayerPtrs)), ("lm_head_scale", ctypes.c_void_p)]
 
 
 class KVDesc(ctypes.Structure):
@@ -117,14 +121,14 @@ def _stream(stream) -> int | None:
 def model_desc(shape: dict, max_seq: int) -> ModelDesc:
     return ModelDesc(shape["n_layers"], shape["hidden"], shape["n_heads"], shape["n_kv_heads"], shape["head_dim"],
                      shape["ffn"], shape["vocab"], int(max_seq), float(shape["rms_eps"]), float(shape["rope_theta"]),
-                     MK_BF16 if shape["dtype"] == "bf16" else MK_F32, int(bool(shape["tied"])))
+                     DTYPES[shape["dtype"]], int(bool(shape["tied"])))
 
 
 class KVCache:
     """Caller-owned contiguous cache: K and V each [n_layers][n_kv_heads][max_seq][head_dim]."""
 
     def __init__(self, shape: dict, max_seq: int, device="cuda", fill: float | None = 0.0):
-        dt = torch.bfloat16 if shape["dtype"] == "bf16" else torch.float32
+        dt = torch.float32 if shape["dtype"] == "f32" else torch.bfloat16  # "w8" keeps a bf16 cache
         size = (shape["n_layers"], shape["n_kv_heads"], int(max_seq), shape["head_dim"])
         self.k = torch.empty(size, dtype=dt, device=device)
         self.v = torch.empty(size, dtype=dt, device=device)
@@ -143,7 +147,9 @@ LAYER_KINDS = ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate", "w_up"
 class MegaKernel:
     """A created handle.  `weights` holds device tensors (row-major [out][in])
     in the model dtype: 'embed', 'final_norm', optional 'lm_head' and
-    'layers' (a list of dicts keyed by LAYER_KINDS)."""
+    'layers' (a list of dicts keyed by LAYER_KINDS).  A "w8" model's
+    matrices are int8 tensors with float32 per-row scales under
+    '<kind>_scale' (and 'lm_head_scale')."""
 
     def __init__(self, shape: dict, weights: dict | None, max_seq: int, tuning: dict | None = None):
         """weights=None creates the handle with mk_create_deferred; the
@@ -234,14 +240,14 @@ def _weight_ptrs(weights: dict):
     layers_in = weights.get("layers", [])
     layers = (LayerPtrs * max(len(layers_in), 1))()
     for l, lw in enumerate(layers_in):
-        layers[l] = LayerPtrs(*[_ptr(lw[k]) for k in LAYER_KINDS])
+        layers[l] = LayerPtrs(*[_ptr(lw[k]) for k in LAYER_KINDS], *[_ptr(lw.get(k + "_scale")) for k in MATRIX_KINDS])
     wp = WeightPtrs(_ptr(weights.get("embed")), _ptr(weights.get("final_norm")), _ptr(weights.get("lm_head")),
-                    layers if layers_in else None)
+                    layers if layers_in else None, _ptr(weights.get("lm_head_scale")))
     return wp, layers
 
 
 def upload_weights(host: dict, device="cuda") -> dict:
-    """Host numpy weights (float32, or uint16 bfloat16 bits) -> device tensors."""
+    """Host numpy weights (float32, uint16 bfloat16 bits, int8 codes) -> device tensors."""
     import numpy as np
 
     def up(a):
