@@ -296,6 +296,43 @@ def test_bit_identical_reruns_and_device_token(env):
     mk.close()
 
 
+def test_alternating_streams_keep_call_order(env):
+    """One handle's calls on two streams, alternating, with no host
+    synchronisation between them: the prefill on one stream, then every
+    decode step on the other stream than the call before.  Each step reads
+    the cache rows the previous calls wrote, so the steps match the oracle
+    only if the library orders each call after the handle's last one (it
+    records an event after each call and makes a new stream wait on it)."""
+    torch, oracle, mkp = env
+    cfg = synth.CONFIGS["tiny"].with_(dtype="bf16", n_heads=8, n_kv_heads=2, rope_theta=500000.0)
+    n_prompt, n_steps = 150, 12
+    max_seq = n_prompt + n_steps
+    mk, host = _make(env, cfg, 17, max_seq)
+    ref = oracle.Model(shape_of(cfg), host, max_seq)
+    toks = synth.gen_tokens(17, n_prompt + 1, cfg.vocab)
+    ref.prefill(toks[:n_prompt])
+    # the oracle's teacher-forced run first: the GPU calls are then enqueued back to back
+    feed, want = [int(toks[n_prompt])], []
+    for s in range(n_steps):
+        want.append(ref.decode_step(feed[-1], n_prompt + s))
+        feed.append(oracle.argmax(want[-1]))
+    kv = mkp.KVCache(shape_of(cfg), max_seq, fill=float("nan"))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]  # default priority
+    logits = torch.full((n_steps, cfg.vocab), float("nan"), device="cuda")
+    torch.cuda.synchronize()
+    mk.prefill_kv(toks[:n_prompt], 0, kv, stream=streams[0])
+    for s in range(n_steps):
+        mk.decode_step(feed[s], n_prompt + s, kv, logits[s], stream=streams[(s + 1) % 2])
+    torch.cuda.synchronize()
+    assert mk.device_error() == 0
+    got = logits.cpu().numpy().astype(np.float64)
+    for s in range(n_steps):
+        assert np.isfinite(got[s]).all(), s
+        assert float(np.abs(got[s] - want[s]).max()) <= 2e-2, s
+        assert int(np.argmax(got[s])) == feed[s + 1], s
+    mk.close()
+
+
 def test_prefill_equals_decode_loop(env):
     # mk_prefill_kv(n) writes exactly the cache rows that n decode steps write
     torch, oracle, mkp = env

@@ -49,11 +49,13 @@ TICK_US = 0.01
 def load(cfg, shape, max_seq, tuning):
     mk = MegaKernel(shape, None, max_seq, tuning=tuning)
     for l in range(cfg.n_layers):
-        lw = {k: synth.gen_tensor(cfg, 0, k, layer=l) for k in synth.LAYER_KINDS}
+        lw = synth.gen_layer(cfg, 0, l)  # (with the per-row scales of an INT8 model)
         mk.load_weights(upload_weights({"layers": [lw]}), first_layer=l)
     head = {"embed": synth.gen_tensor(cfg, 0, "embed"), "final_norm": synth.gen_tensor(cfg, 0, "final_norm")}
     if not cfg.tied:
         head["lm_head"] = synth.gen_tensor(cfg, 0, "lm_head")
+        if cfg.dtype == "w8":
+            head["lm_head_scale"] = synth.gen_scale(cfg, 0, "lm_head")
     mk.load_weights(upload_weights(head))
     return mk
 
