@@ -159,8 +159,8 @@ typedef struct {
                   八 (question five) advises tiling by length;
      prefill_chunk: tokens per chunk of the batched prefill, 1..1024
                   (default 256); -1 = prefill by one decode launch per
-                  position.  The batched prefill needs bf16 weights and a
-                  geometry whose down-stage workgroups own inputs starting at
+                  position.  The batched prefill needs bf16 or INT8 weights and
+                  a geometry whose down-stage workgroups own inputs starting at
                   multiples of 8 (true of the Llama shapes at 256
                   workgroups); otherwise mk_prefill_kv uses decode launches
                   (mk_info.prefill_chunk reports which). */
@@ -271,7 +271,8 @@ mk_status mk_decode_step_device_token_noalloc(mk_handle *h, const int32_t *token
    as the call returns.
    Batched (mk_info.prefill_chunk > 0): chunks of up to prefill_chunk
    positions; per layer the chunk's tokens go through matrix-core GEMMs
-   (bf16 weights, activations split into bf16 high and low parts, fp32
+   (bf16 weights, or int8 codes widened to bf16 with the row scale applied
+   to each sum; activations split into bf16 high and low parts; fp32
    accumulation) that read the packed weights in place, and a causal
    attention over positions [0, own].  The cache rows equal the decode
    step's to within the bf16 rounding of the stored values.  Otherwise one

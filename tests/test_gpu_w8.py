@@ -6,8 +6,10 @@ same seeded inputs.
 Bars: max|dlogit| <= 2e-2 on every step and greedy agreement (the bf16 bar;
 the weights the kernel multiplies are exactly the oracle's s * q, only the
 order of the fp32 rounding differs); prefilled K/V rows within 5e-2, and
-within one bf16 rounding step in layer 0.  An INT8 model's prefill runs as
-one decode launch per position (the batched prefill reads bf16 weights).
+within one bf16 rounding step in layer 0.  An INT8 model's prefill goes
+through the matrix-core GEMMs (codes widened to bf16, row scales on the
+sums) when its down-stage slices start at multiples of 8, else it runs as
+one decode launch per position.
 
 Cases: every query-group size with both head sizes; ragged shapes (an int8
 row shorter than one 1 KiB chunk, SwiGLU slices that end inside a 16-element
@@ -44,6 +46,18 @@ def test_tiny_w8_ragged_shapes_and_small_grid(env):
                            expect_batched=False)
     assert max(errs) <= 2e-2
     assert agree == 6
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_tiny_w8_batched_prefill(env, d):
+    # 64 workgroups own 8 gate/up units each, so every down slice starts at a
+    # multiple of 16 inputs and the batched prefill applies; chunks of 32
+    # positions with a ragged last chunk
+    cfg = W8_TINY.with_(n_heads=8, n_kv_heads=2, head_dim=d, ffn=1024)
+    errs, agree = run_pair(env, cfg, seed=77 + d, n_prompt=70, n_steps=4,
+                           tuning={"grid": 64, "attn_splits": 8, "prefill_chunk": 32}, expect_batched=True)
+    assert max(errs) <= 2e-2
+    assert agree == 4
 
 
 def test_tiny_w8_deferred_load(env):

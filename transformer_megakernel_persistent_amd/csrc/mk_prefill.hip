@@ -17,7 +17,9 @@
 //     A = split(rmsnorm(X, g_ffn));  Y = A . [Wg;Wu]^T
 //     A = split(silu(gate) * up);    X += A . Wd^T
 //
-// Numerics.  Weights are bf16 and enter the products exactly.  Activations
+// Numerics.  Weights are bf16, or int8 codes widened to bf16 (exact: an int8
+// value has at most 8 significant bits) whose per-row scale multiplies the
+// finished dot product; either way they enter the products exactly.  Activations
 // are fp32; each is split into bf16 hi = rne(a) and lo = rne(a - hi), and a
 // product is accumulated as W.hi + W.lo in fp32 by v_mfma_f32_16x16x32_bf16,
 // so an activation keeps about 16 bits of mantissa (relative error below
@@ -90,12 +92,13 @@ struct RowLoc {
     const unsigned char *base;  // layer block + workgroup offset + consumer's 4 KiB of a slot
     int qq0, qs;
 };
-__device__ __forceinline__ RowLoc row_loc(const MkStage &st, const unsigned char *layer_block, int grid, int n) {
+__device__ __forceinline__ RowLoc row_loc(const MkStage &st, const unsigned char *layer_block, int grid, int n,
+                                          int eb) {
     const int U = st.units, u = n >> 2;
     const int w = unit_owner(u, U, grid);
     const int u0 = unit_first(w, U, grid), units = unit_first(w + 1, U, grid) - u0;
     const int i = n - 4 * u0, c = i & 3, rc = i >> 2;
-    const int full = mk_row_groups(st.rbp, 2) ? units / 4 : 0;  // bf16 weights
+    const int full = mk_row_groups(st.rbp, eb) ? units / 4 : 0;
     RowLoc r;
     r.base = layer_block + st.wg_off[w] + c * 4 * MK_CHUNK_BYTES;
     if (rc < full * 4) {
@@ -107,25 +110,49 @@ __device__ __forceinline__ RowLoc row_loc(const MkStage &st, const unsigned char
     }
     return r;
 }
-__device__ __forceinline__ const unsigned char *row_piece(const RowLoc &r, int64_t slot_stride, int k) {
-    const int kc = k >> 9;  // 512 bf16 per chunk
+// Element k of the row (eb bytes per element: 2 bf16, 1 int8).
+__device__ __forceinline__ const unsigned char *row_piece(const RowLoc &r, int64_t slot_stride, int k, int eb) {
+    const int epc = MK_CHUNK_BYTES / eb;  // elements per chunk
+    const int kc = k / epc;
     const int qq = r.qq0 + kc * r.qs;
-    return r.base + (int64_t)(qq >> 2) * slot_stride + (qq & 3) * MK_CHUNK_BYTES + (k & 511) * 2;
+    return r.base + (int64_t)(qq >> 2) * slot_stride + (qq & 3) * MK_CHUNK_BYTES + (k % epc) * eb;
 }
-// The down stage (split along its input, piece columns): the 16-byte piece of
-// output row n holding inputs f .. f+7 (f a multiple of 8, the owning
-// workgroup's first input a multiple of 8), or NULL past the last input.
+// The down stage (split along its input, piece columns): where output row n
+// keeps inputs f .. f+7 (f a multiple of 8, the owning workgroup's first
+// input a multiple of 8; a 16-byte piece holds 8 bf16 or 16 int8 inputs), or
+// NULL past the last input.
 __device__ __forceinline__ const unsigned char *down_piece(const MkStage &st, const unsigned char *layer_block,
-                                                           int grid, int F, int H, int n, int f) {
+                                                           int grid, int F, int H, int n, int f, int eb) {
     if (f >= F) return nullptr;
-    const int U = st.units;
+    const int U = st.units, epl = 16 / eb;
     const int w = unit_owner(f >> 1, U, grid);
-    const MkDownGeo dg = mk_down_geo(w, grid, U, F, H, 8);
-    const int q = (f - dg.f0) >> 3;
+    const MkDownGeo dg = mk_down_geo(w, grid, U, F, H, epl);
+    const int q = (f - dg.f0) / epl;
     const int grp = n >> 6, c = grp & 3, gl = grp >> 2;
     const int qq = gl * dg.kp + q;
     return layer_block + st.wg_off[w] + (int64_t)(qq >> 2) * st.slot_stride + (c * 4 + (qq & 3)) * MK_CHUNK_BYTES +
-           (n & 63) * 16;
+           (n & 63) * 16 + ((f - dg.f0) % epl) * eb;
+}
+
+// INT8: the scale of output n of stage `kind` in one layer, read from the
+// decode kernel's per-workgroup scale blocks (MkParams::scl): a block holds
+// the workgroup's QKV, O and gate/up rows and then the down rows of its x
+// rows (the O rows' indices), in local order.
+struct ScaleIdx {
+    const float *blk;  // the layer's blocks: [grid][sc_blk]
+    int sc_blk, grid, uq, uo, ugu;
+};
+__device__ __forceinline__ float row_scale(const ScaleIdx &si, int kind, int n) {
+    const int G = si.grid;
+    auto first = [&](int w, int U) { return unit_first(w, U, G); };
+    auto count = [&](int w, int U) { return unit_first(w + 1, U, G) - unit_first(w, U, G); };
+    const int U = kind == ST_QKV ? si.uq : kind == ST_GU ? si.ugu : si.uo;  // O and down: the O rows' owner
+    const int w = unit_owner(n >> 2, U, G);
+    int off = n - 4 * first(w, U);
+    if (kind != ST_QKV) off += 4 * count(w, si.uq);
+    if (kind == ST_GU || kind == ST_DOWN) off += 4 * count(w, si.uo);
+    if (kind == ST_DOWN) off += 4 * count(w, si.ugu);
+    return si.blk[(size_t)w * si.sc_blk + off];
 }
 
 // ---- GEMM: out[t][n] (=|+=) sum_k (Ah + Al)[t][k] * W[n][k] -----------------
@@ -135,10 +162,13 @@ __device__ __forceinline__ const unsigned char *down_piece(const MkStage &st, co
 // waves covers 32 tokens x 128 rows, each wave 32 x 32 (2 x 2 blocks); a
 // lane loads its 16-byte A pieces from the split operand and its 16-byte B
 // pieces straight from the packed weights.
-template <bool DOWN, bool ADD>
+// Q8: int8 weights (8 codes widened to bf16 per lane and k-step); the row's
+// scale multiplies the sum before it is stored or added.
+template <bool DOWN, bool ADD, bool Q8>
 __global__ __launch_bounds__(256) void pf_gemm(const MkStage st, const unsigned char *layer_block, int grid, int F,
                                                int H, const uint16_t *Ah, const uint16_t *Al, int lda, int T, int K,
-                                               int N, float *out, int ldo) {
+                                               int N, float *out, int ldo, const ScaleIdx si, int kind) {
+    constexpr int EB = Q8 ? 1 : 2;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int m0 = blockIdx.y * 32, n0 = blockIdx.x * 128 + wv * 32;
     const int r16 = lane & 15, kg = lane >> 4;
@@ -148,7 +178,7 @@ __global__ __launch_bounds__(256) void pf_gemm(const MkStage st, const unsigned 
     for (int nb = 0; nb < 2; ++nb) {
         const int n = n0 + 16 * nb + r16;
         nvalid[nb] = n < N;
-        if (!DOWN) rl[nb] = row_loc(st, layer_block, grid, nvalid[nb] ? n : 0);
+        if (!DOWN) rl[nb] = row_loc(st, layer_block, grid, nvalid[nb] ? n : 0, EB);
     }
     bool mvalid[2];
     const uint16_t *ah[2], *al[2];
@@ -165,13 +195,33 @@ __global__ __launch_bounds__(256) void pf_gemm(const MkStage st, const unsigned 
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = f4v{0.f, 0.f, 0.f, 0.f};
     const u4v zero = u4v{0u, 0u, 0u, 0u};
+    // eight int8 codes -> eight bf16 values (exact)
+    auto widen8 = [](uint32_t lo, uint32_t hi) -> u4v {
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t src = i < 2 ? lo : hi;
+            const int b0 = (i & 1) * 2;
+            const uint32_t e0 = __float_as_uint((float)((int32_t)(src << (24 - 8 * b0)) >> 24)) >> 16;
+            const uint32_t e1 = __float_as_uint((float)((int32_t)(src << (16 - 8 * b0)) >> 24)) >> 16;
+            w[i] = e0 | (e1 << 16);
+        }
+        return u4v{w[0], w[1], w[2], w[3]};
+    };
     auto load_b = [&](int nb, int k) -> u4v {
         if (!nvalid[nb]) return zero;
+        const unsigned char *p;
         if constexpr (DOWN) {
-            const unsigned char *p = down_piece(st, layer_block, grid, F, H, n0 + 16 * nb + r16, k);
-            return p ? *(const u4v *)p : zero;
+            p = down_piece(st, layer_block, grid, F, H, n0 + 16 * nb + r16, k, EB);
+            if (!p) return zero;
         } else {
-            return *(const u4v *)row_piece(rl[nb], st.slot_stride, k);
+            p = row_piece(rl[nb], st.slot_stride, k, EB);
+        }
+        if constexpr (Q8) {
+            const uint2 c = *(const uint2 *)p;
+            return widen8(c.x, c.y);
+        } else {
+            return *(const u4v *)p;
         }
     };
     for (int k0 = 0; k0 < K; k0 += 32) {
@@ -200,13 +250,15 @@ __global__ __launch_bounds__(256) void pf_gemm(const MkStage st, const unsigned 
         for (int nb = 0; nb < 2; ++nb) {
             const int n = n0 + 16 * nb + r16;
             if (n >= N) continue;
+            const float sc = Q8 ? row_scale(si, kind, n) : 1.0f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int m = m0 + 16 * mb + 4 * kg + i;
                 if (m >= T) continue;
                 float *o = out + (size_t)m * ldo + n;
-                if (ADD) *o += acc[mb][nb][i];
-                else *o = acc[mb][nb][i];
+                const float v = Q8 ? acc[mb][nb][i] * sc : acc[mb][nb][i];
+                if (ADD) *o += v;
+                else *o = v;
             }
         }
 }
@@ -380,12 +432,26 @@ void launch_attn(dim3 g, hipStream_t s, const float *Q, const uint16_t *kc, cons
 
 int round32(int k) { return (k + 31) & ~31; }
 
+// One GEMM of the chunk: bf16 or int8 weights of stage `kind`.
+template <bool DOWN, bool ADD>
+void launch_gemm(bool q8, dim3 g, hipStream_t s, const MkStage &st, const unsigned char *blk, int grid, int F, int H,
+                 const uint16_t *Ah, const uint16_t *Al, int lda, int T, int K, int N, float *out, int ldo,
+                 const ScaleIdx &si, int kind) {
+    if (q8)
+        hipLaunchKernelGGL((pf_gemm<DOWN, ADD, true>), g, dim3(256), 0, s, st, blk, grid, F, H, Ah, Al, lda, T, K, N,
+                           out, ldo, si, kind);
+    else
+        hipLaunchKernelGGL((pf_gemm<DOWN, ADD, false>), g, dim3(256), 0, s, st, blk, grid, F, H, Ah, Al, lda, T, K, N,
+                           out, ldo, si, kind);
+}
+
 }  // namespace
 
 // Token-parallel work for positions [pos0, pos0 + T) of prompt tokens
 // tok (device, T ids): fills their cache rows in every layer.  Buffers are
-// the handle's (see MkPrefillBufs).  Requires a bf16 model whose down-stage
-// workgroups own inputs starting at multiples of 8 (mk_prefill_supported).
+// the handle's (see MkPrefillBufs).  Requires a bf16 or weight-only INT8
+// model (p->scl set) whose down-stage workgroups own inputs starting at
+// multiples of 8 (mk_prefill_supported).
 extern "C" int mk_prefill_chunk(const MkParams *p, const MkPrefillBufs *b, int T, int pos0, void *stream) {
     hipStream_t s = (hipStream_t)stream;
     const int L = p->L, H = p->H, nh = p->nh, nkv = p->nkv, d = p->d, F = p->F, G = p->grid;
@@ -393,15 +459,18 @@ extern "C" int mk_prefill_chunk(const MkParams *p, const MkPrefillBufs *b, int T
     const int nqkv = (nh + 2 * nkv) * d, nq = nh * d;
     uint16_t *kc = (uint16_t *)p->kc, *vc = (uint16_t *)p->vc;
     const int lda = b->lda, ldy = b->ldy;
+    const bool q8 = p->scl != nullptr;
+    ScaleIdx si = {nullptr, p->sc_blk, G, p->st[ST_QKV].units, p->st[ST_O].units, p->st[ST_GU].units};
     hipLaunchKernelGGL(pf_embed, dim3(T), dim3(256), 0, s, b->X, b->tok, (const uint16_t *)p->embed, H);
     for (int l = 0; l < L; ++l) {
         const unsigned char *blk[ST_NUM];
         for (int k = 0; k < ST_LM; ++k) blk[k] = p->packed + p->st[k].base + (int64_t)l * p->st[k].layer_stride;
+        if (q8) si.blk = p->scl + (size_t)l * G * p->sc_blk;
         // attention half
         hipLaunchKernelGGL(pf_norm_split, dim3(T), dim3(256), 0, s, b->X, p->g_attn + (size_t)l * H, H, p->eps, b->Ah,
                            b->Al, lda, round32(H));
-        hipLaunchKernelGGL((pf_gemm<false, false>), dim3((nqkv + 127) / 128, (T + 31) / 32), dim3(256), 0, s,
-                           p->st[ST_QKV], blk[ST_QKV], G, F, H, b->Ah, b->Al, lda, T, round32(H), nqkv, b->Y, ldy);
+        launch_gemm<false, false>(q8, dim3((nqkv + 127) / 128, (T + 31) / 32), s, p->st[ST_QKV], blk[ST_QKV], G, F, H,
+                                  b->Ah, b->Al, lda, T, round32(H), nqkv, b->Y, ldy, si, ST_QKV);
         const int nthr = (nh + nkv) * d / 2 + nkv * d;
         hipLaunchKernelGGL(pf_rope_kv, dim3((nthr + 255) / 256, T), dim3(256), 0, s, b->Y, ldy, pos0, p->rope, nh, nkv,
                            d, l, p->max_seq, kc, vc, b->Q);
@@ -414,30 +483,31 @@ extern "C" int mk_prefill_chunk(const MkParams *p, const MkPrefillBufs *b, int T
             MK_PF_ATTN(128, 1) MK_PF_ATTN(128, 2) MK_PF_ATTN(128, 4) MK_PF_ATTN(128, 8)
 #undef MK_PF_ATTN
         }
-        hipLaunchKernelGGL((pf_gemm<false, true>), dim3((H + 127) / 128, (T + 31) / 32), dim3(256), 0, s, p->st[ST_O],
-                           blk[ST_O], G, F, H, b->Ah, b->Al, lda, T, round32(nq), H, b->X, H);
+        launch_gemm<false, true>(q8, dim3((H + 127) / 128, (T + 31) / 32), s, p->st[ST_O], blk[ST_O], G, F, H, b->Ah,
+                                 b->Al, lda, T, round32(nq), H, b->X, H, si, ST_O);
         // feed-forward half
         hipLaunchKernelGGL(pf_norm_split, dim3(T), dim3(256), 0, s, b->X, p->g_ffn + (size_t)l * H, H, p->eps, b->Ah,
                            b->Al, lda, round32(H));
-        hipLaunchKernelGGL((pf_gemm<false, false>), dim3((2 * F + 127) / 128, (T + 31) / 32), dim3(256), 0, s,
-                           p->st[ST_GU], blk[ST_GU], G, F, H, b->Ah, b->Al, lda, T, round32(H), 2 * F, b->Y, ldy);
+        launch_gemm<false, false>(q8, dim3((2 * F + 127) / 128, (T + 31) / 32), s, p->st[ST_GU], blk[ST_GU], G, F, H,
+                                  b->Ah, b->Al, lda, T, round32(H), 2 * F, b->Y, ldy, si, ST_GU);
         hipLaunchKernelGGL(pf_swiglu_split, dim3((round32(F) + 255) / 256, T), dim3(256), 0, s, b->Y, ldy, F, b->Ah,
                            b->Al, lda, round32(F));
-        hipLaunchKernelGGL((pf_gemm<true, true>), dim3((H + 127) / 128, (T + 31) / 32), dim3(256), 0, s,
-                           p->st[ST_DOWN], blk[ST_DOWN], G, F, H, b->Ah, b->Al, lda, T, round32(F), H, b->X, H);
+        launch_gemm<true, true>(q8, dim3((H + 127) / 128, (T + 31) / 32), s, p->st[ST_DOWN], blk[ST_DOWN], G, F, H,
+                                b->Ah, b->Al, lda, T, round32(F), H, b->X, H, si, ST_DOWN);
     }
     return (int)hipGetLastError();
 }
 
-// Whether the batched prefill applies to a handle's geometry: bf16 weights,
-// head_dim 64 or 128, and every down-stage workgroup's first input a multiple
-// of 8 (a 16-byte piece of its piece columns then holds 8 consecutive inputs
-// of the row, the unit of a GEMM lane's B operand).
+// Whether the batched prefill applies to a handle's geometry: bf16 or INT8
+// weights (a bf16 cache), head_dim 64 or 128, and every down-stage
+// workgroup's first input a multiple of 8 (8 consecutive inputs of a row, the
+// unit of a GEMM lane's B operand, then lie in one 16-byte piece of its piece
+// columns).
 extern "C" int mk_prefill_supported(const MkParams *p, int dtype) {
-    if (dtype != 1 || (p->d != 64 && p->d != 128)) return 0;
+    if ((dtype != 1 && dtype != 2) || (p->d != 64 && p->d != 128)) return 0;
     const int U = p->st[ST_DOWN].units;
     for (int w = 0; w < p->grid; ++w) {
-        const MkDownGeo dg = mk_down_geo(w, p->grid, U, p->F, p->H, 8);
+        const MkDownGeo dg = mk_down_geo(w, p->grid, U, p->F, p->H, dtype == 2 ? 16 : 8);
         if (dg.f0 % 8 != 0) return 0;
     }
     return 1;
