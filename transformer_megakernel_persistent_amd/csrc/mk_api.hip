@@ -204,6 +204,7 @@ extern "C" void mk_destroy(mk_handle *h) {
     hipFree(h->pf.Y);
     hipFree(h->pf.Q);
     hipFree(h->pf_tokens);
+    hipFree((void *)h->pf.dmap);
     if (h->done) hipEventDestroy(h->done);
     delete h;
 }
@@ -444,6 +445,24 @@ static mk_status create_impl(const mk_model_desc *desc, const mk_tuning *tun, mk
         HIP_TRY(hipMalloc(&B.Y, (size_t)T * B.ldy * sizeof(float)));
         HIP_TRY(hipMalloc(&B.Q, (size_t)T * nh * d * sizeof(float)));
         HIP_TRY(hipMalloc(&h->pf_tokens, (size_t)D.max_seq * sizeof(int32_t)));
+        // where each block of 8 down-projection inputs lives (mk_down_geo)
+        {
+            const int epl = 16 / eb, U = P.st[ST_DOWN].units;
+            std::vector<int32_t> dm((size_t)(F / 8) * 4);
+            for (int f8 = 0; f8 < F / 8; ++f8) {
+                const int f = 8 * f8, u = f >> 1;
+                const int w = (int)(((int64_t)(u + 1) * grid - 1) / U);  // owner of gate/up unit u
+                const MkDownGeo dg = mk_down_geo(w, grid, U, F, H, epl);
+                dm[(size_t)f8 * 4 + 0] = (int32_t)off_host[(size_t)ST_DOWN * grid + w];
+                dm[(size_t)f8 * 4 + 1] = dg.kp;
+                dm[(size_t)f8 * 4 + 2] = (f - dg.f0) / epl;
+                dm[(size_t)f8 * 4 + 3] = ((f - dg.f0) % epl) * eb;
+            }
+            int32_t *dmap = nullptr;
+            HIP_TRY(hipMalloc(&dmap, dm.size() * sizeof(int32_t)));
+            HIP_TRY(hipMemcpy(dmap, dm.data(), dm.size() * sizeof(int32_t), hipMemcpyHostToDevice));
+            B.dmap = dmap;
+        }
         B.t_max = T;
     }
 

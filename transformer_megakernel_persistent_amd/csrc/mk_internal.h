@@ -162,6 +162,11 @@ struct MkPrefillBufs {
     float *Y;        // [t_max][ldy] QKV or gate/up outputs, packed row order
     float *Q;        // [t_max][nh*d] rotated queries
     int32_t *tok;    // token ids of the chunk (device)
+    // [F/8][4] where the down projection keeps each block of 8 consecutive
+    // inputs (one 16-byte piece or half of one): the owning workgroup's
+    // byte offset in a layer block, its pieces per row group (kp), the
+    // piece index q and the byte offset inside the piece
+    const int32_t *dmap;
     int32_t lda, ldy, t_max;
 };
 

@@ -120,18 +120,17 @@ __device__ __forceinline__ const unsigned char *row_piece(const RowLoc &r, int64
 // The down stage (split along its input, piece columns): where output row n
 // keeps inputs f .. f+7 (f a multiple of 8, the owning workgroup's first
 // input a multiple of 8; a 16-byte piece holds 8 bf16 or 16 int8 inputs), or
-// NULL past the last input.
+// NULL past the last input.  dmap gives, per block of 8 inputs, the owning
+// workgroup's block offset, its pieces per row group, the piece and the byte
+// offset inside it (mk_down_geo, tabulated by the host).
 __device__ __forceinline__ const unsigned char *down_piece(const MkStage &st, const unsigned char *layer_block,
-                                                           int grid, int F, int H, int n, int f, int eb) {
+                                                           const int32_t *dmap, int F, int n, int f) {
     if (f >= F) return nullptr;
-    const int U = st.units, epl = 16 / eb;
-    const int w = unit_owner(f >> 1, U, grid);
-    const MkDownGeo dg = mk_down_geo(w, grid, U, F, H, epl);
-    const int q = (f - dg.f0) / epl;
+    const int4 e = *(const int4 *)(dmap + 4 * (f >> 3));
     const int grp = n >> 6, c = grp & 3, gl = grp >> 2;
-    const int qq = gl * dg.kp + q;
-    return layer_block + st.wg_off[w] + (int64_t)(qq >> 2) * st.slot_stride + (c * 4 + (qq & 3)) * MK_CHUNK_BYTES +
-           (n & 63) * 16 + ((f - dg.f0) % epl) * eb;
+    const int qq = gl * e.y + e.z;
+    return layer_block + e.x + (int64_t)(qq >> 2) * st.slot_stride + (c * 4 + (qq & 3)) * MK_CHUNK_BYTES +
+           (n & 63) * 16 + e.w;
 }
 
 // INT8: the scale of output n of stage `kind` in one layer, read from the
@@ -167,7 +166,8 @@ __device__ __forceinline__ float row_scale(const ScaleIdx &si, int kind, int n) 
 template <bool DOWN, bool ADD, bool Q8>
 __global__ __launch_bounds__(256) void pf_gemm(const MkStage st, const unsigned char *layer_block, int grid, int F,
                                                int H, const uint16_t *Ah, const uint16_t *Al, int lda, int T, int K,
-                                               int N, float *out, int ldo, const ScaleIdx si, int kind) {
+                                               int N, float *out, int ldo, const ScaleIdx si, int kind,
+                                               const int32_t *dmap) {
     constexpr int EB = Q8 ? 1 : 2;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int m0 = blockIdx.y * 32, n0 = blockIdx.x * 128 + wv * 32;
@@ -212,7 +212,7 @@ __global__ __launch_bounds__(256) void pf_gemm(const MkStage st, const unsigned 
         if (!nvalid[nb]) return zero;
         const unsigned char *p;
         if constexpr (DOWN) {
-            p = down_piece(st, layer_block, grid, F, H, n0 + 16 * nb + r16, k, EB);
+            p = down_piece(st, layer_block, dmap, F, n0 + 16 * nb + r16, k);
             if (!p) return zero;
         } else {
             p = row_piece(rl[nb], st.slot_stride, k, EB);
@@ -224,25 +224,35 @@ __global__ __launch_bounds__(256) void pf_gemm(const MkStage st, const unsigned 
             return *(const u4v *)p;
         }
     };
-    for (int k0 = 0; k0 < K; k0 += 32) {
-        const int k = k0 + 8 * kg;
-        u4v a_hi[2], a_lo[2], b[2];
+    // KU k-steps of operands are loaded before any of their products, so
+    // that KU rounds of memory latency overlap instead of following each
+    // other (K is a multiple of 32; a step past K loads nothing).
+    constexpr int KU = 4;
+    for (int kb = 0; kb < K; kb += 32 * KU) {
+        u4v a_hi[KU][2], a_lo[KU][2], b[KU][2];
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-            a_hi[mb] = mvalid[mb] ? *(const u4v *)(ah[mb] + k0) : zero;
-            a_lo[mb] = mvalid[mb] ? *(const u4v *)(al[mb] + k0) : zero;
+        for (int u = 0; u < KU; ++u) {
+            const int k0 = kb + 32 * u, k = k0 + 8 * kg;
+            const bool kin = k0 < K;
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) {
+                a_hi[u][mb] = kin && mvalid[mb] ? *(const u4v *)(ah[mb] + k0) : zero;
+                a_lo[u][mb] = kin && mvalid[mb] ? *(const u4v *)(al[mb] + k0) : zero;
+            }
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) b[u][nb] = kin ? load_b(nb, k) : zero;
         }
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) b[nb] = load_b(nb, k);
+        for (int u = 0; u < KU; ++u)
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+            for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
-                acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, a_hi[mb]),
-                                                                      __builtin_bit_cast(bf8v, b[nb]), acc[mb][nb], 0, 0, 0);
-                acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, a_lo[mb]),
-                                                                      __builtin_bit_cast(bf8v, b[nb]), acc[mb][nb], 0, 0, 0);
-            }
+                for (int nb = 0; nb < 2; ++nb) {
+                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf8v, a_hi[u][mb]), __builtin_bit_cast(bf8v, b[u][nb]), acc[mb][nb], 0, 0, 0);
+                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf8v, a_lo[u][mb]), __builtin_bit_cast(bf8v, b[u][nb]), acc[mb][nb], 0, 0, 0);
+                }
     }
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
@@ -432,17 +442,19 @@ void launch_attn(dim3 g, hipStream_t s, const float *Q, const uint16_t *kc, cons
 
 int round32(int k) { return (k + 31) & ~31; }
 
-// One GEMM of the chunk: bf16 or int8 weights of stage `kind`.
+// One GEMM of the chunk: bf16 or int8 weights of stage `kind`, N outputs
+// per token; workgroups cover 32 tokens x 128 outputs.
 template <bool DOWN, bool ADD>
-void launch_gemm(bool q8, dim3 g, hipStream_t s, const MkStage &st, const unsigned char *blk, int grid, int F, int H,
+void launch_gemm(bool q8, hipStream_t s, const MkStage &st, const unsigned char *blk, int grid, int F, int H,
                  const uint16_t *Ah, const uint16_t *Al, int lda, int T, int K, int N, float *out, int ldo,
-                 const ScaleIdx &si, int kind) {
+                 const ScaleIdx &si, int kind, const int32_t *dmap) {
+    const dim3 g((N + 127) / 128, (T + 31) / 32);
     if (q8)
         hipLaunchKernelGGL((pf_gemm<DOWN, ADD, true>), g, dim3(256), 0, s, st, blk, grid, F, H, Ah, Al, lda, T, K, N,
-                           out, ldo, si, kind);
+                           out, ldo, si, kind, dmap);
     else
         hipLaunchKernelGGL((pf_gemm<DOWN, ADD, false>), g, dim3(256), 0, s, st, blk, grid, F, H, Ah, Al, lda, T, K, N,
-                           out, ldo, si, kind);
+                           out, ldo, si, kind, dmap);
 }
 
 }  // namespace
@@ -469,8 +481,8 @@ extern "C" int mk_prefill_chunk(const MkParams *p, const MkPrefillBufs *b, int T
         // attention half
         hipLaunchKernelGGL(pf_norm_split, dim3(T), dim3(256), 0, s, b->X, p->g_attn + (size_t)l * H, H, p->eps, b->Ah,
                            b->Al, lda, round32(H));
-        launch_gemm<false, false>(q8, dim3((nqkv + 127) / 128, (T + 31) / 32), s, p->st[ST_QKV], blk[ST_QKV], G, F, H,
-                                  b->Ah, b->Al, lda, T, round32(H), nqkv, b->Y, ldy, si, ST_QKV);
+        launch_gemm<false, false>(q8, s, p->st[ST_QKV], blk[ST_QKV], G, F, H, b->Ah, b->Al, lda, T, round32(H), nqkv,
+                                  b->Y, ldy, si, ST_QKV, b->dmap);
         const int nthr = (nh + nkv) * d / 2 + nkv * d;
         hipLaunchKernelGGL(pf_rope_kv, dim3((nthr + 255) / 256, T), dim3(256), 0, s, b->Y, ldy, pos0, p->rope, nh, nkv,
                            d, l, p->max_seq, kc, vc, b->Q);
@@ -483,17 +495,17 @@ extern "C" int mk_prefill_chunk(const MkParams *p, const MkPrefillBufs *b, int T
             MK_PF_ATTN(128, 1) MK_PF_ATTN(128, 2) MK_PF_ATTN(128, 4) MK_PF_ATTN(128, 8)
 #undef MK_PF_ATTN
         }
-        launch_gemm<false, true>(q8, dim3((H + 127) / 128, (T + 31) / 32), s, p->st[ST_O], blk[ST_O], G, F, H, b->Ah,
-                                 b->Al, lda, T, round32(nq), H, b->X, H, si, ST_O);
+        launch_gemm<false, true>(q8, s, p->st[ST_O], blk[ST_O], G, F, H, b->Ah, b->Al, lda, T, round32(nq), H, b->X, H,
+                                 si, ST_O, b->dmap);
         // feed-forward half
         hipLaunchKernelGGL(pf_norm_split, dim3(T), dim3(256), 0, s, b->X, p->g_ffn + (size_t)l * H, H, p->eps, b->Ah,
                            b->Al, lda, round32(H));
-        launch_gemm<false, false>(q8, dim3((2 * F + 127) / 128, (T + 31) / 32), s, p->st[ST_GU], blk[ST_GU], G, F, H,
-                                  b->Ah, b->Al, lda, T, round32(H), 2 * F, b->Y, ldy, si, ST_GU);
+        launch_gemm<false, false>(q8, s, p->st[ST_GU], blk[ST_GU], G, F, H, b->Ah, b->Al, lda, T, round32(H), 2 * F,
+                                  b->Y, ldy, si, ST_GU, b->dmap);
         hipLaunchKernelGGL(pf_swiglu_split, dim3((round32(F) + 255) / 256, T), dim3(256), 0, s, b->Y, ldy, F, b->Ah,
                            b->Al, lda, round32(F));
-        launch_gemm<true, true>(q8, dim3((H + 127) / 128, (T + 31) / 32), s, p->st[ST_DOWN], blk[ST_DOWN], G, F, H,
-                                b->Ah, b->Al, lda, T, round32(F), H, b->X, H, si, ST_DOWN);
+        launch_gemm<true, true>(q8, s, p->st[ST_DOWN], blk[ST_DOWN], G, F, H, b->Ah, b->Al, lda, T, round32(F), H,
+                                b->X, H, si, ST_DOWN, b->dmap);
     }
     return (int)hipGetLastError();
 }
