@@ -91,58 +91,62 @@ def kernel_stats(directory: str):
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", required=True)
-    ap.add_argument("--fetch", required=True, help="CSV directory of the --pmc FETCH_SIZE run")
-    ap.add_argument("--write", required=True, help="CSV directory of the --pmc WRITE_SIZE run")
+    ap.add_argument("--fetch", default=None, help="CSV directory of the --pmc FETCH_SIZE run")
+    ap.add_argument("--write", default=None, help="CSV directory of the --pmc WRITE_SIZE run")
     ap.add_argument("--trace", required=True, help="CSV directory of the --kernel-trace --stats run")
     ap.add_argument("--copy-bytes", type=int, required=True, help="bytes of each calibration copy")
-    ap.add_argument("--command-fetch", required=True)
-    ap.add_argument("--command-write", required=True)
+    ap.add_argument("--command-fetch", default=None)
+    ap.add_argument("--command-write", default=None)
     ap.add_argument("--command-trace", required=True)
     ap.add_argument("--bench-json", default=None, help="the JSON line the traced bench run printed")
     ap.add_argument("--dram", default=None, help="CSV directory of a --pmc TCC_EA0_RDREQ_DRAM_sum run (optional)")
     ap.add_argument("--command-dram", default=None)
+    ap.add_argument("--note", default=None, help="a line for the summary (e.g. why a counter pass is missing)")
     args = ap.parse_args(argv)
+    if (args.fetch is None) != (args.write is None):
+        ap.error("--fetch and --write go together")
 
     sys.path.insert(0, ROOT)
     import synth
     from bench import kernel_hash
 
-    f_dec, f_cpy, n_f, n_fc, copy_name = counter_per_dispatch(args.fetch, "FETCH_SIZE")
-    w_dec, w_cpy, n_w, n_wc, _ = counter_per_dispatch(args.write, "WRITE_SIZE")
-    kib = args.copy_bytes / 1024.0
-    f_scale, w_scale = kib / f_cpy, kib / w_cpy
-    fetch_b = f_dec * f_scale * 1024.0
-    write_b = w_dec * w_scale * 1024.0
     stats = kernel_stats(args.trace)
     dec = [s for s in stats if _is_decode(s["name"])]
     cfg = synth.CONFIGS[args.workload]
     bench = json.loads(args.bench_json) if args.bench_json else None
     pos0 = bench["config"]["decode_positions"][0] if bench else cfg.context
     alg = cfg.step_bytes(pos0)
-
-    rec = {"workload": args.workload, "kernel_hash": kernel_hash(), "kernel": DECODE_TAG + "<..., LOGITS=true>",
-           "hbm_bytes_per_launch": fetch_b + write_b, "fetch_bytes_per_launch": fetch_b,
-           "write_bytes_per_launch": write_b, "fetch_kib_raw": f_dec, "write_kib_raw": w_dec,
-           "copy_bytes": args.copy_bytes, "copy_fetch_kib_raw": f_cpy, "copy_write_kib_raw": w_cpy,
-           "fetch_scale": f_scale, "write_scale": w_scale, "decode_dispatches": [n_f, n_w],
-           "algorithmic_bytes_per_launch": alg, "commands": {"fetch": args.command_fetch,
-                                                             "write": args.command_write}}
-    if args.dram:
-        # read requests the memory-side caches passed on to DRAM, summed over
-        # the L2 channels; each request moves 64 bytes (32-byte requests are
-        # counted by a separate counter on this chip and ignored here)
-        d_dec, d_cpy, n_d, n_dc, _ = counter_per_dispatch(args.dram, "TCC_EA0_RDREQ_DRAM_sum")
-        rec["dram_read_requests_per_launch"] = d_dec
-        rec["dram_read_requests_per_copy"] = d_cpy
-        rec["dram_read_bytes_per_launch_scaled"] = d_dec * (args.copy_bytes / d_cpy) if d_cpy else None
-        rec["commands"]["dram"] = args.command_dram
+    rec = None
+    if args.fetch:
+        f_dec, f_cpy, n_f, n_fc, copy_name = counter_per_dispatch(args.fetch, "FETCH_SIZE")
+        w_dec, w_cpy, n_w, n_wc, _ = counter_per_dispatch(args.write, "WRITE_SIZE")
+        kib = args.copy_bytes / 1024.0
+        f_scale, w_scale = kib / f_cpy, kib / w_cpy
+        fetch_b = f_dec * f_scale * 1024.0
+        write_b = w_dec * w_scale * 1024.0
+        rec = {"workload": args.workload, "kernel_hash": kernel_hash(), "kernel": DECODE_TAG + "<..., LOGITS=true>",
+               "hbm_bytes_per_launch": fetch_b + write_b, "fetch_bytes_per_launch": fetch_b,
+               "write_bytes_per_launch": write_b, "fetch_kib_raw": f_dec, "write_kib_raw": w_dec,
+               "copy_bytes": args.copy_bytes, "copy_fetch_kib_raw": f_cpy, "copy_write_kib_raw": w_cpy,
+               "fetch_scale": f_scale, "write_scale": w_scale, "decode_dispatches": [n_f, n_w],
+               "algorithmic_bytes_per_launch": alg, "commands": {"fetch": args.command_fetch,
+                                                                 "write": args.command_write}}
+        if args.dram:
+            # read requests the memory-side caches passed on to DRAM, summed over
+            # the L2 channels, scaled by the same counter's reading for the copy
+            d_dec, d_cpy, n_d, n_dc, _ = counter_per_dispatch(args.dram, "TCC_EA0_RDREQ_DRAM_sum")
+            rec["dram_read_requests_per_launch"] = d_dec
+            rec["dram_read_requests_per_copy"] = d_cpy
+            rec["dram_read_bytes_per_launch_scaled"] = d_dec * (args.copy_bytes / d_cpy) if d_cpy else None
+            rec["commands"]["dram"] = args.command_dram
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    with open(os.path.join(ROOT, "profiles", f"counters_{args.workload}.json"), "w") as f:
-        json.dump(rec, f, indent=1)
-        f.write("\n")
+    if rec is not None:
+        with open(os.path.join(ROOT, "profiles", f"counters_{args.workload}.json"), "w") as f:
+            json.dump(rec, f, indent=1)
+            f.write("\n")
 
     lines = [f"# {DECODE_TAG} on {args.workload}", "",
-             f"Kernel sources hash: `{rec['kernel_hash']}`", "",
+             f"Kernel sources hash: `{kernel_hash()}`", "",
              "## Kernel trace (rocprofv3 --kernel-trace --stats)", "",
              f"Command: `{args.command_trace}`", "",
              "| kernel | calls | avg us | min us | max us | total ms | % |", "|---|---|---|---|---|---|---|"]
@@ -157,6 +161,14 @@ def main(argv=None):
     if bench:
         lines += ["", f"The traced bench run printed: value {bench['value']:.1f} tokens/s, mean event-timed step "
                       f"{bench['us_per_token_mean']:.2f} us, roofline.achieved {bench['roofline']['achieved']:.1f} GB/s."]
+    if args.note:
+        lines += ["", args.note]
+    if rec is None:
+        out_md = os.path.join(ROOT, "profiles", f"{DECODE_TAG}_{args.workload}.md")
+        with open(out_md, "w") as f:
+            f.write("\n".join(lines) + "\n")
+        print(json.dumps({"counters": None, "md": out_md}))
+        return
     lines += ["", "## HBM traffic (rocprofv3 --pmc, one counter per run)", "",
               f"FETCH_SIZE command: `{args.command_fetch}`", "",
               f"WRITE_SIZE command: `{args.command_write}`", "",
