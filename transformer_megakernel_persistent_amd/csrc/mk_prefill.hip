@@ -309,113 +309,177 @@ __global__ __launch_bounds__(256) void pf_rope_kv(const float *Y, int ldy, int p
     }
 }
 
-// ---- causal GQA attention of the chunk's tokens ------------------------------
-// Workgroup (token block, KV head j): pairs (token, query head of group j),
-// LPP = D / 8 lanes per pair (8 dims each).  Positions stream through LDS in
-// blocks of 64 K and V rows; each pair folds eight positions at a time into
-// its running max, sum and output (online softmax), positions past its own
-// masked out.  Output o / l goes to the split operand at [t][head*D + dim].
+// ---- causal GQA attention of the chunk on the matrix cores -----------------
+// Workgroup (query block, KV head j): 64 query rows -- QB = 64 / GQ tokens x
+// the GQ heads of group j, row m = token (m / GQ), head (m % GQ) -- against
+// blocks of 64 cached positions staged in LDS (K as [pos][dim], V transposed
+// to [dim][pos]).  Wave w owns rows 16w .. 16w+15.  Per block:
+//   S = Q K^T with v_mfma_f32_16x16x32_bf16 (Q split into bf16 hi + lo, K
+//   exact), positions past each row's own masked out, an online-softmax
+//   update of each row's running max, P = exp(S - max), then O += P V (P
+//   split into hi + lo through LDS into the A-operand layout, V exact).
+// In the C layout lane l holds rows 4 (l / 16) + i (i < 4) of a 16 x 16 tile
+// at column l % 16, so a row's max over a tile is a reduction over the 16
+// lanes of one lane group, and the output rows a lane rescales are the rows
+// whose scores it holds.  The result o / l goes to the split operand.
 template <int D, int GQ>
-__global__ __launch_bounds__(256) void pf_attn(const float *Q, const uint16_t *kc, const uint16_t *vc, int layer, int nh,
-                                               int nkv, int max_seq, int pos0, int T, uint16_t *Ah, uint16_t *Al,
-                                               int lda) {
-    constexpr int LPP = D / 8, PAIRS = 256 / LPP, TPW = PAIRS / GQ, BP = 64;
-    __shared__ __attribute__((aligned(16))) uint16_t ks[BP * D], vs[BP * D];
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int pr = tid / LPP, sub = tid % LPP;  // pair, and this lane's dims [8 sub, 8 sub + 8)
-    const int j = blockIdx.y;
-    const int tl = pr / GQ, g = pr % GQ;         // token within the block, head within the group
-    const int t = blockIdx.x * TPW + tl;
-    const bool tv = t < T;
-    const int head = j * GQ + g;
-    const int my_last = pos0 + (tv ? t : 0);     // last position this pair attends
-    const int t_hi = min(T, (int)(blockIdx.x + 1) * TPW) - 1;
-    const int n_pos = pos0 + t_hi + 1;           // positions the workgroup needs
+__global__ __launch_bounds__(256) void pf_attn_mfma(const float *Q, const uint16_t *kc, const uint16_t *vc, int layer,
+                                                    int nh, int nkv, int max_seq, int pos0, int T, uint16_t *Ah,
+                                                    uint16_t *Al, int lda) {
+    constexpr int QB = 64 / GQ;  // tokens per workgroup
+    constexpr int KS = D / 32;   // k-steps of S = Q K^T
+    constexpr int NT = D / 16;   // output tiles (16 dims each) per wave
+    constexpr int BP = 64;       // positions per block
+    __shared__ __attribute__((aligned(16))) uint16_t ks[BP * D];    // [pos][dim]
+    __shared__ __attribute__((aligned(16))) uint16_t vt[D * BP];    // [dim][pos]
+    __shared__ __attribute__((aligned(16))) float ps[4][16 * BP];   // per wave: P [row][pos]
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int j = blockIdx.y, t_base = blockIdx.x * QB;
+    const int r16 = lane & 15, kg = lane >> 4;
     const float scale = 1.0f / sqrtf((float)D);
-    float q[8], o[8];
-    const float *qp = Q + ((size_t)(tv ? t : 0) * nh + head) * D + 8 * sub;
+    // A-operand rows: m = 16 wv + r16
+    u4v qh[KS], ql[KS];
+    {
+        const int m = wv * 16 + r16, t = t_base + m / GQ, g = m % GQ;
+        const bool tv = t < T;
+        const float *qp = Q + ((size_t)(tv ? t : 0) * nh + j * GQ + g) * D + 8 * kg;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        q[e] = qp[e] * scale;
-        o[e] = 0.f;
+        for (int k = 0; k < KS; ++k) {
+            uint32_t hw[4], lw[4];
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                const float a = tv ? qp[32 * k + e] * scale : 0.f, b = tv ? qp[32 * k + e + 1] * scale : 0.f;
+                const uint16_t ah = f_to_bf(a), bh = f_to_bf(b);
+                hw[e / 2] = (uint32_t)ah | ((uint32_t)bh << 16);
+                lw[e / 2] = (uint32_t)f_to_bf(a - bf_to_f(ah)) | ((uint32_t)f_to_bf(b - bf_to_f(bh)) << 16);
+            }
+            qh[k] = u4v{hw[0], hw[1], hw[2], hw[3]};
+            ql[k] = u4v{lw[0], lw[1], lw[2], lw[3]};
+        }
     }
-    float mrun = -INFINITY, lrun = 0.f;
+    // C-layout rows of this lane: m = 16 wv + 4 kg + i; the last position each may attend
+    int plast[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int m = wv * 16 + 4 * kg + i, t = t_base + m / GQ;
+        plast[i] = t < T ? pos0 + t : -1;
+    }
+    float mrun[4], lrun[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        mrun[i] = -INFINITY;
+        lrun[i] = 0.f;  // this lane's share of the row sum
+    }
+    f4v o[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) o[n] = f4v{0.f, 0.f, 0.f, 0.f};
+    const int t_last = min(T, t_base + QB) - 1;
+    const int n_pos = pos0 + t_last + 1;  // positions the workgroup needs
     const uint16_t *kbase = kc + ((size_t)layer * nkv + j) * max_seq * D;
     const uint16_t *vbase = vc + ((size_t)layer * nkv + j) * max_seq * D;
+    float *pw = ps[wv];
     for (int p0 = 0; p0 < n_pos; p0 += BP) {
         const int nb = min(BP, n_pos - p0);
-        __syncthreads();
-        for (int i = tid; i < BP * D / 8; i += 256) {  // 16-byte pieces of the block
-            const int row = i / (D / 8);
-            u4v kv4 = u4v{0u, 0u, 0u, 0u}, vv4 = u4v{0u, 0u, 0u, 0u};
-            if (row < nb) {
-                kv4 = *(const u4v *)(kbase + (size_t)(p0 + row) * D + (i % (D / 8)) * 8);
-                vv4 = *(const u4v *)(vbase + (size_t)(p0 + row) * D + (i % (D / 8)) * 8);
-            }
-            *(u4v *)(ks + i * 8) = kv4;
-            *(u4v *)(vs + i * 8) = vv4;
+        __syncthreads();  // the previous block's K, V and P are consumed
+        for (int i = tid; i < BP * D / 8; i += 256) {  // K: 16-byte pieces, row-major
+            const int row = i / (D / 8), cp = i % (D / 8);
+            const u4v kw = row < nb ? *(const u4v *)(kbase + (size_t)(p0 + row) * D + 8 * cp) : u4v{0u, 0u, 0u, 0u};
+            *(u4v *)(ks + row * D + 8 * cp) = kw;
+        }
+        for (int i = tid; i < BP * D / 8; i += 256) {  // V: consecutive threads take consecutive positions
+            const int row = i % BP, cp = i / BP;
+            const u4v vw = row < nb ? *(const u4v *)(vbase + (size_t)(p0 + row) * D + 8 * cp) : u4v{0u, 0u, 0u, 0u};
+            const uint32_t w4[4] = {vw.x, vw.y, vw.z, vw.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vt[(8 * cp + e) * BP + row] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
         }
         __syncthreads();
-        for (int pb = 0; pb < nb; pb += 8) {
-            float s[8];
+        // S: four 16-position tiles
+        f4v sc[4];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const u4v kw = *(const u4v *)(ks + (pb + u) * D + 8 * sub);
-                float a = 0.f;
-                a = fmaf(q[0], __uint_as_float(kw.x << 16), a);
-                a = fmaf(q[1], __uint_as_float(kw.x & 0xFFFF0000u), a);
-                a = fmaf(q[2], __uint_as_float(kw.y << 16), a);
-                a = fmaf(q[3], __uint_as_float(kw.y & 0xFFFF0000u), a);
-                a = fmaf(q[4], __uint_as_float(kw.z << 16), a);
-                a = fmaf(q[5], __uint_as_float(kw.z & 0xFFFF0000u), a);
-                a = fmaf(q[6], __uint_as_float(kw.w << 16), a);
-                a = fmaf(q[7], __uint_as_float(kw.w & 0xFFFF0000u), a);
-                // sum over the pair's LPP lanes (aligned groups within the wave)
+        for (int nt = 0; nt < 4; ++nt) {
+            sc[nt] = f4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int m = 1; m < LPP; m <<= 1) a += __shfl_xor(a, m);
-                const int pos = p0 + pb + u;
-                s[u] = (pb + u < nb && pos <= my_last) ? a : -INFINITY;
+            for (int k = 0; k < KS; ++k) {
+                const u4v b = *(const u4v *)(ks + (nt * 16 + r16) * D + 32 * k + 8 * kg);
+                sc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, qh[k]),
+                                                                 __builtin_bit_cast(bf8v, b), sc[nt], 0, 0, 0);
+                sc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, ql[k]),
+                                                                 __builtin_bit_cast(bf8v, b), sc[nt], 0, 0, 0);
             }
-            float mx = s[0];
+        }
+        // mask, running max, P
+        float alpha[4];
 #pragma unroll
-            for (int u = 1; u < 8; ++u) mx = fmaxf(mx, s[u]);
-            const float mn = fmaxf(mrun, mx);
-            if (mn == -INFINITY) continue;  // nothing valid yet for this pair (uniform per pair)
-            const float alpha = __expf(mrun - mn);
-            float pe[8], lsum = lrun * alpha;
+        for (int i = 0; i < 4; ++i) {
+            float mx = -INFINITY;
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                pe[u] = __expf(s[u] - mn);
-                lsum += pe[u];
+            for (int nt = 0; nt < 4; ++nt) {
+                const int p = p0 + nt * 16 + r16;
+                const float v = p <= plast[i] ? sc[nt][i] : -INFINITY;
+                sc[nt][i] = v;
+                mx = fmaxf(mx, v);
             }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] *= alpha;
+            for (int m = 1; m < 16; m <<= 1) mx = fmaxf(mx, __shfl_xor(mx, m));  // over the lane group
+            const float mn = fmaxf(mrun[i], mx);
+            alpha[i] = mn == -INFINITY ? 1.f : __expf(mrun[i] - mn);
+            mrun[i] = mn;
+            float lsum = 0.f;
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const u4v vw = *(const u4v *)(vs + (pb + u) * D + 8 * sub);
-                o[0] = fmaf(pe[u], __uint_as_float(vw.x << 16), o[0]);
-                o[1] = fmaf(pe[u], __uint_as_float(vw.x & 0xFFFF0000u), o[1]);
-                o[2] = fmaf(pe[u], __uint_as_float(vw.y << 16), o[2]);
-                o[3] = fmaf(pe[u], __uint_as_float(vw.y & 0xFFFF0000u), o[3]);
-                o[4] = fmaf(pe[u], __uint_as_float(vw.z << 16), o[4]);
-                o[5] = fmaf(pe[u], __uint_as_float(vw.z & 0xFFFF0000u), o[5]);
-                o[6] = fmaf(pe[u], __uint_as_float(vw.w << 16), o[6]);
-                o[7] = fmaf(pe[u], __uint_as_float(vw.w & 0xFFFF0000u), o[7]);
+            for (int nt = 0; nt < 4; ++nt) {
+                const float pe = sc[nt][i] == -INFINITY ? 0.f : __expf(sc[nt][i] - mn);
+                lsum += pe;
+                pw[(4 * kg + i) * BP + nt * 16 + r16] = pe;
             }
-            mrun = mn;
-            lrun = lsum;
+            lrun[i] = lrun[i] * alpha[i] + lsum;
+        }
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[n][i] *= alpha[i];
+        __syncthreads();  // P of every lane of the wave is in LDS
+        // O += P V: two 32-position k-steps
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+            const float *pp = pw + r16 * BP + 32 * k2 + 8 * kg;
+            const f4v pa = *(const f4v *)pp, pb = *(const f4v *)(pp + 4);
+            const float pv[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+            uint32_t hw[4], lw[4];
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                const uint16_t ah = f_to_bf(pv[e]), bh = f_to_bf(pv[e + 1]);
+                hw[e / 2] = (uint32_t)ah | ((uint32_t)bh << 16);
+                lw[e / 2] = (uint32_t)f_to_bf(pv[e] - bf_to_f(ah)) | ((uint32_t)f_to_bf(pv[e + 1] - bf_to_f(bh)) << 16);
+            }
+            const u4v ph = u4v{hw[0], hw[1], hw[2], hw[3]}, pl = u4v{lw[0], lw[1], lw[2], lw[3]};
+#pragma unroll
+            for (int n = 0; n < NT; ++n) {
+                const u4v b = *(const u4v *)(vt + (n * 16 + r16) * BP + 32 * k2 + 8 * kg);
+                o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, ph), __builtin_bit_cast(bf8v, b),
+                                                               o[n], 0, 0, 0);
+                o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, pl), __builtin_bit_cast(bf8v, b),
+                                                               o[n], 0, 0, 0);
+            }
         }
     }
-    (void)lane;
-    if (!tv) return;
-    const float inv = 1.0f / lrun;
+    // row sums over the lane group, then o / l into the split operand
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const float v = o[e] * inv;
-        const uint16_t hi = f_to_bf(v);
-        const size_t idx = (size_t)t * lda + (size_t)head * D + 8 * sub + e;
-        Ah[idx] = hi;
-        Al[idx] = f_to_bf(v - bf_to_f(hi));
+    for (int i = 0; i < 4; ++i) {
+        float l = lrun[i];
+#pragma unroll
+        for (int m = 1; m < 16; m <<= 1) l += __shfl_xor(l, m);
+        const int m = wv * 16 + 4 * kg + i, t = t_base + m / GQ, g = m % GQ;
+        if (t >= T) continue;
+        const float inv = 1.0f / l;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            const float v = o[n][i] * inv;
+            const uint16_t hi = f_to_bf(v);
+            const size_t idx = (size_t)t * lda + (size_t)(j * GQ + g) * D + n * 16 + r16;
+            Ah[idx] = hi;
+            Al[idx] = f_to_bf(v - bf_to_f(hi));
+        }
     }
 }
 
@@ -435,9 +499,11 @@ __global__ __launch_bounds__(256) void pf_swiglu_split(const float *Y, int ldy, 
 }
 
 template <int D, int GQ>
-void launch_attn(dim3 g, hipStream_t s, const float *Q, const uint16_t *kc, const uint16_t *vc, int layer, int nh,
-                 int nkv, int max_seq, int pos0, int T, uint16_t *Ah, uint16_t *Al, int lda) {
-    hipLaunchKernelGGL((pf_attn<D, GQ>), g, dim3(256), 0, s, Q, kc, vc, layer, nh, nkv, max_seq, pos0, T, Ah, Al, lda);
+void launch_attn(hipStream_t s, const float *Q, const uint16_t *kc, const uint16_t *vc, int layer, int nh, int nkv,
+                 int max_seq, int pos0, int T, uint16_t *Ah, uint16_t *Al, int lda) {
+    const dim3 g((T + 64 / GQ - 1) / (64 / GQ), nkv);
+    hipLaunchKernelGGL((pf_attn_mfma<D, GQ>), g, dim3(256), 0, s, Q, kc, vc, layer, nh, nkv, max_seq, pos0, T, Ah, Al,
+                       lda);
 }
 
 int round32(int k) { return (k + 31) & ~31; }
@@ -487,10 +553,8 @@ extern "C" int mk_prefill_chunk(const MkParams *p, const MkPrefillBufs *b, int T
         hipLaunchKernelGGL(pf_rope_kv, dim3((nthr + 255) / 256, T), dim3(256), 0, s, b->Y, ldy, pos0, p->rope, nh, nkv,
                            d, l, p->max_seq, kc, vc, b->Q);
         {
-            const int pairs = 256 / (d / 8), tpw = pairs / gq;
-            const dim3 g((T + tpw - 1) / tpw, nkv);
 #define MK_PF_ATTN(D_, GQ_) \
-    if (d == D_ && gq == GQ_) launch_attn<D_, GQ_>(g, s, b->Q, kc, vc, l, nh, nkv, p->max_seq, pos0, T, b->Ah, b->Al, lda);
+    if (d == D_ && gq == GQ_) launch_attn<D_, GQ_>(s, b->Q, kc, vc, l, nh, nkv, p->max_seq, pos0, T, b->Ah, b->Al, lda);
             MK_PF_ATTN(64, 1) MK_PF_ATTN(64, 2) MK_PF_ATTN(64, 4) MK_PF_ATTN(64, 8)
             MK_PF_ATTN(128, 1) MK_PF_ATTN(128, 2) MK_PF_ATTN(128, 4) MK_PF_ATTN(128, 8)
 #undef MK_PF_ATTN
