@@ -294,7 +294,7 @@ def main():
     ap.add_argument("--stage-drain", action="store_true",
                     help="ablation: no loads for a stage before its grid dependency is met")
     ap.add_argument("--prefill-chunk", type=int, default=0,
-                    help="tokens per batched-prefill chunk (default 256); -1: one decode launch per position")
+                    help="tokens per batched-prefill chunk (default 2048); -1: one decode launch per position")
     ap.add_argument("--attn-pm-slots", type=int, default=0,
                     help="position-major attention when a split holds at least this many KV slots "
                          "(default 0: always head-major)")

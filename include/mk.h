@@ -157,9 +157,10 @@ typedef struct {
                   slot is bound by the consumers' arithmetic, not by LDS
                   reads).  The page cloud.baidu.com/article/9434380 section
                   八 (question five) advises tiling by length;
-     prefill_chunk: tokens per chunk of the batched prefill, 1..1024
-                  (default 256); -1 = prefill by one decode launch per
-                  position.  The batched prefill needs bf16 or INT8 weights and
+     prefill_chunk: tokens per chunk of the batched prefill, 1..4096
+                  (default 2048, or max_seq if smaller); -1 = prefill by one
+                  decode launch per position.  The batched prefill needs bf16
+                  or INT8 weights and
                   a geometry whose down-stage workgroups own inputs starting at
                   multiples of 8 (true of the Llama shapes at 256
                   workgroups); otherwise mk_prefill_kv uses decode launches

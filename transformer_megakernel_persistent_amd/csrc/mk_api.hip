@@ -161,7 +161,7 @@ mk_status validate_tuning(const mk_tuning *t) {
     if (!t) return MK_OK;
     if (t->grid < 0 || t->grid > MK_MAX_GRID || t->ring_slots < 0 || t->attn_splits < 0 || t->attn_splits > MK_MAX_SPLITS || t->timeout_ms < 0 ||
         t->cooperative < 0 || t->cooperative > 2 || t->trace < 0 || t->trace > 1 || t->prefetch_depth < 0 ||
-        t->stage_drain < 0 || t->stage_drain > 1 || t->prefill_chunk < -1 || t->prefill_chunk > 1024 ||
+        t->stage_drain < 0 || t->stage_drain > 1 || t->prefill_chunk < -1 || t->prefill_chunk > 4096 ||
         t->attn_pm_slots < -1)
         return MK_ERR_TUNING;
     if (t->ring_slots != 0 && (t->ring_slots < 3 || t->ring_slots > MK_MAX_RING)) return MK_ERR_TUNING;
@@ -431,7 +431,9 @@ static mk_status create_impl(const mk_model_desc *desc, const mk_tuning *tun, mk
     // batched prefill buffers, when the geometry allows it (bf16, aligned
     // down-stage inputs) and the tuning does not ask for decode launches
     if (t.prefill_chunk != -1 && mk_prefill_supported(&P, dtype)) {
-        const int T = t.prefill_chunk > 0 ? t.prefill_chunk : 256;
+        // default: chunks of 2048 tokens (every GEMM then has 256 or more
+        // workgroups at the Llama shapes), or max_seq if shorter
+        const int T = t.prefill_chunk > 0 ? t.prefill_chunk : (D.max_seq < 2048 ? D.max_seq : 2048);
         auto r32 = [](int k) { return (k + 31) & ~31; };
         int kmax = H > nh * d ? H : nh * d;
         if (F > kmax) kmax = F;

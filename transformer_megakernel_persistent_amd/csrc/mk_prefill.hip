@@ -119,14 +119,12 @@ __device__ __forceinline__ const unsigned char *row_piece(const RowLoc &r, int64
 }
 // The down stage (split along its input, piece columns): where output row n
 // keeps inputs f .. f+7 (f a multiple of 8, the owning workgroup's first
-// input a multiple of 8; a 16-byte piece holds 8 bf16 or 16 int8 inputs), or
-// NULL past the last input.  dmap gives, per block of 8 inputs, the owning
-// workgroup's block offset, its pieces per row group, the piece and the byte
-// offset inside it (mk_down_geo, tabulated by the host).
+// input a multiple of 8; a 16-byte piece holds 8 bf16 or 16 int8 inputs).
+// e = dmap[f / 8] gives the owning workgroup's block offset, its pieces per
+// row group, the piece and the byte offset inside it (mk_down_geo,
+// tabulated by the host).
 __device__ __forceinline__ const unsigned char *down_piece(const MkStage &st, const unsigned char *layer_block,
-                                                           const int32_t *dmap, int F, int n, int f) {
-    if (f >= F) return nullptr;
-    const int4 e = *(const int4 *)(dmap + 4 * (f >> 3));
+                                                           const int4 e, int n) {
     const int grp = n >> 6, c = grp & 3, gl = grp >> 2;
     const int qq = gl * e.y + e.z;
     return layer_block + e.x + (int64_t)(qq >> 2) * st.slot_stride + (c * 4 + (qq & 3)) * MK_CHUNK_BYTES +
@@ -157,44 +155,61 @@ __device__ __forceinline__ float row_scale(const ScaleIdx &si, int kind, int n) 
 // ---- GEMM: out[t][n] (=|+=) sum_k (Ah + Al)[t][k] * W[n][k] -----------------
 // v_mfma_f32_16x16x32_bf16 operand layout (wave64): A[m][k] in lane
 // m + 16 * (k / 8), element k % 8; B[k][n] in lane n + 16 * (k / 8); the
-// result C[m][n] in lane n + 16 * (m / 4), element m % 4.  A workgroup of 4
-// waves covers 32 tokens x 128 rows, each wave 32 x 32 (2 x 2 blocks); a
-// lane loads its 16-byte A pieces from the split operand and its 16-byte B
-// pieces straight from the packed weights.
-// Q8: int8 weights (8 codes widened to bf16 per lane and k-step); the row's
-// scale multiplies the sum before it is stored or added.
+// result C[m][n] in lane n + 16 * (m / 4), element m % 4.
+// Workgroup tile: 128 tokens x 128 outputs; its 4 waves in 2 x 2, each
+// 64 x 64 (4 x 4 blocks).  Per k-tile of 64 the operands are staged in LDS
+// -- A hi, A lo and B as [row][k], rows padded to 72 elements (144 bytes)
+// so that the 16 rows one ds_read_b128 instruction touches fall in
+// different banks -- and every wave reads its fragments from there: each A
+// row is fetched from memory once for 128 outputs, each weight row once for
+// 128 tokens.  The next k-tile's global loads are issued into registers
+// before the current tile's products.
+// B is read in units of 8 consecutive inputs of one row: 16 bytes of bf16,
+// or 8 int8 codes widened to bf16 (exact); Q8 multiplies each output
+// column's sum by its row's scale.  Rows at or past N, tokens at or past T
+// and inputs at or past K (a multiple of 32) enter as zeros.
 template <bool DOWN, bool ADD, bool Q8>
 __global__ __launch_bounds__(256) void pf_gemm(const MkStage st, const unsigned char *layer_block, int grid, int F,
                                                int H, const uint16_t *Ah, const uint16_t *Al, int lda, int T, int K,
                                                int N, float *out, int ldo, const ScaleIdx si, int kind,
                                                const int32_t *dmap) {
     constexpr int EB = Q8 ? 1 : 2;
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int m0 = blockIdx.y * 32, n0 = blockIdx.x * 128 + wv * 32;
+    constexpr int BM = 128, BN = 128, BK = 64, LDK = BK + 8;
+    __shared__ __attribute__((aligned(16))) uint16_t sah[BM * LDK], sal[BM * LDK], sb[BN * LDK];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int wm = wv >> 1, wn = wv & 1;
+    const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
     const int r16 = lane & 15, kg = lane >> 4;
-    RowLoc rl[2];
-    bool nvalid[2];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-        const int n = n0 + 16 * nb + r16;
-        nvalid[nb] = n < N;
-        if (!DOWN) rl[nb] = row_loc(st, layer_block, grid, nvalid[nb] ? n : 0, EB);
-    }
-    bool mvalid[2];
-    const uint16_t *ah[2], *al[2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-        const int m = m0 + 16 * mb + r16;
-        mvalid[mb] = m < T;
-        ah[mb] = Ah + (size_t)(mvalid[mb] ? m : 0) * lda + 8 * kg;
-        al[mb] = Al + (size_t)(mvalid[mb] ? m : 0) * lda + 8 * kg;
-    }
-    f4v acc[2][2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = f4v{0.f, 0.f, 0.f, 0.f};
     const u4v zero = u4v{0u, 0u, 0u, 0u};
+    // Staging: piece j (0..3) of this thread.  A: row (tid >> 3) + 32 j,
+    // inputs 8 (tid & 7) .. +7 of the k-tile.  B, row-split stages: the same
+    // (8 threads read one row's 64 inputs, contiguous in its chunk); B, down
+    // stage: output row tid & 127, input blocks (tid >> 7) + 2 j, so that
+    // neighbouring threads read neighbouring rows' pieces.
+    const int arow = tid >> 3, apart = tid & 7;
+    const uint16_t *pah[4], *pal[4];
+    bool am[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int m = m0 + arow + 32 * j;
+        am[j] = m < T;
+        pah[j] = Ah + (size_t)(am[j] ? m : 0) * lda + 8 * apart;
+        pal[j] = Al + (size_t)(am[j] ? m : 0) * lda + 8 * apart;
+    }
+    RowLoc rl[4];
+    bool bn[4];
+    const int dn = n0 + (tid & 127), dfb = tid >> 7;
+    if constexpr (!DOWN) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int n = n0 + arow + 32 * j;
+            bn[j] = n < N;
+            rl[j] = row_loc(st, layer_block, grid, bn[j] ? n : 0, EB);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bn[j] = dn < N;
+    }
     // eight int8 codes -> eight bf16 values (exact)
     auto widen8 = [](uint32_t lo, uint32_t hi) -> u4v {
         uint32_t w[4];
@@ -208,69 +223,109 @@ __global__ __launch_bounds__(256) void pf_gemm(const MkStage st, const unsigned 
         }
         return u4v{w[0], w[1], w[2], w[3]};
     };
-    auto load_b = [&](int nb, int k) -> u4v {
-        if (!nvalid[nb]) return zero;
-        const unsigned char *p;
-        if constexpr (DOWN) {
-            p = down_piece(st, layer_block, dmap, F, n0 + 16 * nb + r16, k);
-            if (!p) return zero;
-        } else {
-            p = row_piece(rl[nb], st.slot_stride, k, EB);
-        }
+    auto load_b8 = [&](const unsigned char *q) -> u4v {
         if constexpr (Q8) {
-            const uint2 c = *(const uint2 *)p;
+            const uint2 c = *(const uint2 *)q;
             return widen8(c.x, c.y);
         } else {
-            return *(const u4v *)p;
+            return *(const u4v *)q;
         }
     };
-    // KU k-steps of operands are loaded before any of their products, so
-    // that KU rounds of memory latency overlap instead of following each
-    // other (K is a multiple of 32; a step past K loads nothing).
-    constexpr int KU = 4;
-    for (int kb = 0; kb < K; kb += 32 * KU) {
-        u4v a_hi[KU][2], a_lo[KU][2], b[KU][2];
+    // down stage: the map entries of the next fetch's input blocks, read one
+    // k-tile ahead so that no fetch waits for its own lookups
+    int4 dme[4];
+    auto dmap_read = [&](int kb) {
 #pragma unroll
-        for (int u = 0; u < KU; ++u) {
-            const int k0 = kb + 32 * u, k = k0 + 8 * kg;
-            const bool kin = k0 < K;
+        for (int j = 0; j < 4; ++j) {
+            const int f = kb + 8 * (dfb + 2 * j);
+            dme[j] = f < F ? *(const int4 *)(dmap + 4 * (f >> 3)) : int4{0, 0, 0, 0};
+        }
+    };
+    u4v rah[4], ral[4], rb[4];
+    auto fetch = [&](int kb) {
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb) {
-                a_hi[u][mb] = kin && mvalid[mb] ? *(const u4v *)(ah[mb] + k0) : zero;
-                a_lo[u][mb] = kin && mvalid[mb] ? *(const u4v *)(al[mb] + k0) : zero;
-            }
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb) b[u][nb] = kin ? load_b(nb, k) : zero;
+        for (int j = 0; j < 4; ++j) {
+            const bool kin = kb + 8 * apart < K;
+            rah[j] = am[j] && kin ? *(const u4v *)(pah[j] + kb) : zero;
+            ral[j] = am[j] && kin ? *(const u4v *)(pal[j] + kb) : zero;
         }
 #pragma unroll
-        for (int u = 0; u < KU; ++u)
+        for (int j = 0; j < 4; ++j) {
+            if constexpr (DOWN) {
+                const int f = kb + 8 * (dfb + 2 * j);
+                rb[j] = bn[j] && f < F ? load_b8(down_piece(st, layer_block, dme[j], dn)) : zero;
+            } else {
+                const int k = kb + 8 * apart;
+                rb[j] = bn[j] && k < K ? load_b8(row_piece(rl[j], st.slot_stride, k, EB)) : zero;
+            }
+        }
+        if constexpr (DOWN) dmap_read(kb + BK);
+    };
+    auto stage = [&]() {
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
+        for (int j = 0; j < 4; ++j) {
+            const int r = arow + 32 * j;
+            *(u4v *)(sah + r * LDK + 8 * apart) = rah[j];
+            *(u4v *)(sal + r * LDK + 8 * apart) = ral[j];
+            if constexpr (DOWN)
+                *(u4v *)(sb + (tid & 127) * LDK + 8 * (dfb + 2 * j)) = rb[j];
+            else
+                *(u4v *)(sb + r * LDK + 8 * apart) = rb[j];
+        }
+    };
+    f4v acc[4][4];
 #pragma unroll
-                for (int nb = 0; nb < 2; ++nb) {
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f4v{0.f, 0.f, 0.f, 0.f};
+    if constexpr (DOWN) dmap_read(0);
+    fetch(0);
+    for (int kb = 0; kb < K; kb += BK) {
+        __syncthreads();  // every wave has read the previous tile
+        stage();
+        __syncthreads();
+        if (kb + BK < K) fetch(kb + BK);
+#pragma unroll
+        for (int ks = 0; ks < BK / 32; ++ks) {
+            if (kb + 32 * ks >= K) break;  // uniform: a half tile at the end
+            u4v fh[4], fl[4], fb[4];
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) {
+                const int r = wm * 64 + mb * 16 + r16;
+                fh[mb] = *(const u4v *)(sah + r * LDK + 32 * ks + 8 * kg);
+                fl[mb] = *(const u4v *)(sal + r * LDK + 32 * ks + 8 * kg);
+            }
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb)
+                fb[nb] = *(const u4v *)(sb + (wn * 64 + nb * 16 + r16) * LDK + 32 * ks + 8 * kg);
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb) {
                     acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf8v, a_hi[u][mb]), __builtin_bit_cast(bf8v, b[u][nb]), acc[mb][nb], 0, 0, 0);
+                        __builtin_bit_cast(bf8v, fh[mb]), __builtin_bit_cast(bf8v, fb[nb]), acc[mb][nb], 0, 0, 0);
                     acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf8v, a_lo[u][mb]), __builtin_bit_cast(bf8v, b[u][nb]), acc[mb][nb], 0, 0, 0);
+                        __builtin_bit_cast(bf8v, fl[mb]), __builtin_bit_cast(bf8v, fb[nb]), acc[mb][nb], 0, 0, 0);
                 }
+        }
     }
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int nb = 0; nb < 4; ++nb) {
+        const int n = n0 + wn * 64 + nb * 16 + r16;
+        if (n >= N) continue;
+        const float sc = Q8 ? row_scale(si, kind, n) : 1.0f;
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-            const int n = n0 + 16 * nb + r16;
-            if (n >= N) continue;
-            const float sc = Q8 ? row_scale(si, kind, n) : 1.0f;
+        for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int m = m0 + 16 * mb + 4 * kg + i;
+                const int m = m0 + wm * 64 + mb * 16 + 4 * kg + i;
                 if (m >= T) continue;
                 float *o = out + (size_t)m * ldo + n;
                 const float v = Q8 ? acc[mb][nb][i] * sc : acc[mb][nb][i];
                 if (ADD) *o += v;
                 else *o = v;
             }
-        }
+    }
 }
 
 // ---- rotary encoding and the cache rows of the chunk ------------------------
@@ -509,12 +564,12 @@ void launch_attn(hipStream_t s, const float *Q, const uint16_t *kc, const uint16
 int round32(int k) { return (k + 31) & ~31; }
 
 // One GEMM of the chunk: bf16 or int8 weights of stage `kind`, N outputs
-// per token; workgroups cover 32 tokens x 128 outputs.
+// per token; workgroups cover 128 tokens x 128 outputs.
 template <bool DOWN, bool ADD>
 void launch_gemm(bool q8, hipStream_t s, const MkStage &st, const unsigned char *blk, int grid, int F, int H,
                  const uint16_t *Ah, const uint16_t *Al, int lda, int T, int K, int N, float *out, int ldo,
                  const ScaleIdx &si, int kind, const int32_t *dmap) {
-    const dim3 g((N + 127) / 128, (T + 31) / 32);
+    const dim3 g((N + 127) / 128, (T + 127) / 128);
     if (q8)
         hipLaunchKernelGGL((pf_gemm<DOWN, ADD, true>), g, dim3(256), 0, s, st, blk, grid, F, H, Ah, Al, lda, T, K, N,
                            out, ldo, si, kind, dmap);
