@@ -70,10 +70,16 @@ def parse_resources(text: str) -> list:
     return kernels
 
 
+# per-source options: the prefill kernels keep their matrix-core
+# accumulators in ordinary VGPRs (the online-softmax rescaling and the GEMM
+# epilogues then need no moves between accumulation and vector registers)
+SOURCE_FLAGS = {"mk_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _jobs():
     jobs = []
     for s in SOURCES:
-        jobs.append((s, [], os.path.join(OBJDIR, s.replace(".hip", ".o"))))
+        jobs.append((s, SOURCE_FLAGS.get(s, []), os.path.join(OBJDIR, s.replace(".hip", ".o"))))
     for dt, gq in KERNEL_PARTS:
         jobs.append(("mk_kernel.hip", ["-DMK_KERNEL_PART", f"-DMK_PART_DT={dt}", f"-DMK_PART_GQ={gq}"],
                      os.path.join(OBJDIR, f"mk_kernel_part_{dt}_{gq}.o")))

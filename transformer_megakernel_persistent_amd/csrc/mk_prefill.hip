@@ -365,177 +365,226 @@ __global__ __launch_bounds__(256) void pf_rope_kv(const float *Y, int ldy, int p
 }
 
 // ---- causal GQA attention of the chunk on the matrix cores -----------------
-// Workgroup (query block, KV head j): 64 query rows -- QB = 64 / GQ tokens x
-// the GQ heads of group j, row m = token (m / GQ), head (m % GQ) -- against
-// blocks of 64 cached positions staged in LDS (K as [pos][dim], V transposed
-// to [dim][pos]).  Wave w owns rows 16w .. 16w+15.  Per block:
+// Workgroup (query block, KV head j): 64 RB query rows -- QB = 64 RB / GQ
+// tokens x the GQ heads of group j, row m = token (m / GQ), head (m % GQ)
+// -- against blocks of 64 cached positions staged in LDS (K as [pos][dim],
+// V transposed to [dim][pos]); the next block's K and V are loaded into
+// registers while the current one is multiplied.  Wave w owns the RB
+// 16-row blocks 16 (w RB + r) ...  Per position block and row block:
 //   S = Q K^T with v_mfma_f32_16x16x32_bf16 (Q split into bf16 hi + lo, K
-//   exact), positions past each row's own masked out, an online-softmax
-//   update of each row's running max, P = exp(S - max), then O += P V (P
-//   split into hi + lo through LDS into the A-operand layout, V exact).
+//   exact; Q carries the factor log2(e) / sqrt(d), so that exp2 of a score
+//   is exp of the scaled score), positions past each row's own masked out
+//   (only blocks that reach past the workgroup's first token need the
+//   mask), an online-softmax update of each row's running max, P =
+//   exp2(S - max), then O += P V (P split into hi + lo through LDS into the
+//   A-operand layout, V exact).
 // In the C layout lane l holds rows 4 (l / 16) + i (i < 4) of a 16 x 16 tile
 // at column l % 16, so a row's max over a tile is a reduction over the 16
 // lanes of one lane group, and the output rows a lane rescales are the rows
 // whose scores it holds.  The result o / l goes to the split operand.
-template <int D, int GQ>
+// bf16 hi + lo parts of two floats, packed in pairs (v_cvt_pk_bf16_f32
+// rounds to nearest even): hi = rne(a), lo = rne(a - hi)
+__device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t &lo) {
+    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+    const bf2 h = {(__bf16)a, (__bf16)b};
+    hi = __builtin_bit_cast(uint32_t, h);
+    const bf2 l = {(__bf16)(a - __uint_as_float(hi << 16)), (__bf16)(b - __uint_as_float(hi & 0xFFFF0000u))};
+    lo = __builtin_bit_cast(uint32_t, l);
+}
+// max / sum over the 16 lanes of a DPP row (one lane group of the C layout)
+template <int CTRL>
+__device__ __forceinline__ float dpp16(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, dpp16<0xB1>(v));   // quad_perm [1,0,3,2]
+    v = fmaxf(v, dpp16<0x4E>(v));   // quad_perm [2,3,0,1]
+    v = fmaxf(v, dpp16<0x141>(v));  // row_half_mirror
+    return fmaxf(v, dpp16<0x140>(v));  // row_mirror
+}
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp16<0xB1>(v);
+    v += dpp16<0x4E>(v);
+    v += dpp16<0x141>(v);
+    return v + dpp16<0x140>(v);
+}
+
+template <int D, int GQ, int RB>
 __global__ __launch_bounds__(256) void pf_attn_mfma(const float *Q, const uint16_t *kc, const uint16_t *vc, int layer,
                                                     int nh, int nkv, int max_seq, int pos0, int T, uint16_t *Ah,
                                                     uint16_t *Al, int lda) {
-    constexpr int QB = 64 / GQ;  // tokens per workgroup
-    constexpr int KS = D / 32;   // k-steps of S = Q K^T
-    constexpr int NT = D / 16;   // output tiles (16 dims each) per wave
-    constexpr int BP = 64;       // positions per block
-    __shared__ __attribute__((aligned(16))) uint16_t ks[BP * D];    // [pos][dim]
-    __shared__ __attribute__((aligned(16))) uint16_t vt[D * BP];    // [dim][pos]
-    __shared__ __attribute__((aligned(16))) float ps[4][16 * BP];   // per wave: P [row][pos]
+    constexpr int QB = 64 * RB / GQ;  // tokens per workgroup
+    constexpr int KS = D / 32;        // k-steps of S = Q K^T
+    constexpr int NT = D / 16;        // output tiles (16 dims each) per row block
+    constexpr int BP = 64;            // positions per block
+    constexpr int PPT = BP * D / 8 / 256;  // 16-byte K (and V) pieces per thread and block
+    __shared__ __attribute__((aligned(16))) uint16_t ks[BP * D];        // [pos][dim]
+    __shared__ __attribute__((aligned(16))) uint16_t vt[D * BP];        // [dim][pos]
+    __shared__ __attribute__((aligned(16))) float ps[4][RB][16 * BP];   // per wave and row block: P [row][pos]
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int j = blockIdx.y, t_base = blockIdx.x * QB;
+    // One-dimensional grid, KV head fastest: workgroup w runs on XCD w mod 8,
+    // so with 8 KV heads each head's K/V stream stays in one XCD's L2; the
+    // query blocks go last-first, so the longest causal ranges start first.
+    const int nqb = (T + QB - 1) / QB;
+    const int j = (int)blockIdx.x % nkv, t_base = (nqb - 1 - (int)blockIdx.x / nkv) * QB;
     const int r16 = lane & 15, kg = lane >> 4;
-    const float scale = 1.0f / sqrtf((float)D);
-    // A-operand rows: m = 16 wv + r16
-    u4v qh[KS], ql[KS];
-    {
-        const int m = wv * 16 + r16, t = t_base + m / GQ, g = m % GQ;
+    const float scale = 1.4426950408889634f / sqrtf((float)D);  // log2(e) / sqrt(d)
+    // A-operand rows of row block r: m = 16 (wv RB + r) + r16
+    u4v qh[RB][KS], ql[RB][KS];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+        const int m = (wv * RB + r) * 16 + r16, t = t_base + m / GQ, g = m % GQ;
         const bool tv = t < T;
         const float *qp = Q + ((size_t)(tv ? t : 0) * nh + j * GQ + g) * D + 8 * kg;
 #pragma unroll
         for (int k = 0; k < KS; ++k) {
             uint32_t hw[4], lw[4];
 #pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-                const float a = tv ? qp[32 * k + e] * scale : 0.f, b = tv ? qp[32 * k + e + 1] * scale : 0.f;
-                const uint16_t ah = f_to_bf(a), bh = f_to_bf(b);
-                hw[e / 2] = (uint32_t)ah | ((uint32_t)bh << 16);
-                lw[e / 2] = (uint32_t)f_to_bf(a - bf_to_f(ah)) | ((uint32_t)f_to_bf(b - bf_to_f(bh)) << 16);
-            }
-            qh[k] = u4v{hw[0], hw[1], hw[2], hw[3]};
-            ql[k] = u4v{lw[0], lw[1], lw[2], lw[3]};
+            for (int e = 0; e < 8; e += 2)
+                split2(tv ? qp[32 * k + e] * scale : 0.f, tv ? qp[32 * k + e + 1] * scale : 0.f, hw[e / 2], lw[e / 2]);
+            qh[r][k] = u4v{hw[0], hw[1], hw[2], hw[3]};
+            ql[r][k] = u4v{lw[0], lw[1], lw[2], lw[3]};
         }
     }
-    // C-layout rows of this lane: m = 16 wv + 4 kg + i; the last position each may attend
-    int plast[4];
+    // C-layout rows of this lane: m = 16 (wv RB + r) + 4 kg + i; the last
+    // position each may attend (rows past the chunk's last token attend
+    // everything and are never written).  The running max starts at a
+    // finite floor, so exp2(-inf - max) is 0 for masked scores and the
+    // first block's rescaling factor is 0, with no special cases.
+    int plast[RB][4];
+    float mrun[RB][4], lrun[RB][4];  // lrun: this lane's share of the row sum
+    f4v o[RB][NT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int m = wv * 16 + 4 * kg + i, t = t_base + m / GQ;
-        plast[i] = t < T ? pos0 + t : -1;
+    for (int r = 0; r < RB; ++r) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int m = (wv * RB + r) * 16 + 4 * kg + i, t = t_base + m / GQ;
+            plast[r][i] = t < T ? pos0 + t : 0x7FFFFFFF;
+            mrun[r][i] = -1e30f;
+            lrun[r][i] = 0.f;
+        }
+#pragma unroll
+        for (int n = 0; n < NT; ++n) o[r][n] = f4v{0.f, 0.f, 0.f, 0.f};
     }
-    float mrun[4], lrun[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        mrun[i] = -INFINITY;
-        lrun[i] = 0.f;  // this lane's share of the row sum
-    }
-    f4v o[NT];
-#pragma unroll
-    for (int n = 0; n < NT; ++n) o[n] = f4v{0.f, 0.f, 0.f, 0.f};
     const int t_last = min(T, t_base + QB) - 1;
     const int n_pos = pos0 + t_last + 1;  // positions the workgroup needs
     const uint16_t *kbase = kc + ((size_t)layer * nkv + j) * max_seq * D;
     const uint16_t *vbase = vc + ((size_t)layer * nkv + j) * max_seq * D;
-    float *pw = ps[wv];
-    for (int p0 = 0; p0 < n_pos; p0 += BP) {
+    // K piece i of a block: row i / (D / 8), 16-byte column i % (D / 8); V
+    // piece i: row i % BP (neighbouring threads take neighbouring
+    // positions, so the transposed LDS stores spread over the banks)
+    u4v kr[PPT], vr[PPT];
+    auto fetch = [&](int p0) {
         const int nb = min(BP, n_pos - p0);
-        __syncthreads();  // the previous block's K, V and P are consumed
-        for (int i = tid; i < BP * D / 8; i += 256) {  // K: 16-byte pieces, row-major
-            const int row = i / (D / 8), cp = i % (D / 8);
-            const u4v kw = row < nb ? *(const u4v *)(kbase + (size_t)(p0 + row) * D + 8 * cp) : u4v{0u, 0u, 0u, 0u};
-            *(u4v *)(ks + row * D + 8 * cp) = kw;
-        }
-        for (int i = tid; i < BP * D / 8; i += 256) {  // V: consecutive threads take consecutive positions
-            const int row = i % BP, cp = i / BP;
-            const u4v vw = row < nb ? *(const u4v *)(vbase + (size_t)(p0 + row) * D + 8 * cp) : u4v{0u, 0u, 0u, 0u};
-            const uint32_t w4[4] = {vw.x, vw.y, vw.z, vw.w};
 #pragma unroll
-            for (int e = 0; e < 8; ++e) vt[(8 * cp + e) * BP + row] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
+        for (int u = 0; u < PPT; ++u) {
+            const int i = tid + 256 * u;
+            const int krow = i / (D / 8), kcp = i % (D / 8), vrow = i % BP, vcp = i / BP;
+            kr[u] = krow < nb ? *(const u4v *)(kbase + (size_t)(p0 + krow) * D + 8 * kcp) : u4v{0u, 0u, 0u, 0u};
+            vr[u] = vrow < nb ? *(const u4v *)(vbase + (size_t)(p0 + vrow) * D + 8 * vcp) : u4v{0u, 0u, 0u, 0u};
+        }
+    };
+    fetch(0);
+    for (int p0 = 0; p0 < n_pos; p0 += BP) {
+        __syncthreads();  // the previous block's K, V and P are consumed
+#pragma unroll
+        for (int u = 0; u < PPT; ++u) {
+            const int i = tid + 256 * u;
+            *(u4v *)(ks + (i / (D / 8)) * D + 8 * (i % (D / 8))) = kr[u];
+            const int vrow = i % BP, vcp = i / BP;
+            const uint32_t w4[4] = {vr[u].x, vr[u].y, vr[u].z, vr[u].w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vt[(8 * vcp + e) * BP + vrow] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
         }
         __syncthreads();
-        // S: four 16-position tiles
-        f4v sc[4];
+        if (p0 + BP < n_pos) fetch(p0 + BP);
+        float alpha[RB][4];
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-            sc[nt] = f4v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int k = 0; k < KS; ++k) {
-                const u4v b = *(const u4v *)(ks + (nt * 16 + r16) * D + 32 * k + 8 * kg);
-                sc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, qh[k]),
-                                                                 __builtin_bit_cast(bf8v, b), sc[nt], 0, 0, 0);
-                sc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, ql[k]),
-                                                                 __builtin_bit_cast(bf8v, b), sc[nt], 0, 0, 0);
-            }
-        }
-        // mask, running max, P
-        float alpha[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float mx = -INFINITY;
+        for (int r = 0; r < RB; ++r) {
+            float *pw = ps[wv][r];
+            // S: four 16-position tiles
+            f4v sc[4];
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) {
-                const int p = p0 + nt * 16 + r16;
-                const float v = p <= plast[i] ? sc[nt][i] : -INFINITY;
-                sc[nt][i] = v;
-                mx = fmaxf(mx, v);
+                sc[nt] = f4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int k = 0; k < KS; ++k) {
+                    const u4v bk = *(const u4v *)(ks + (nt * 16 + r16) * D + 32 * k + 8 * kg);
+                    sc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, qh[r][k]),
+                                                                     __builtin_bit_cast(bf8v, bk), sc[nt], 0, 0, 0);
+                    sc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, ql[r][k]),
+                                                                     __builtin_bit_cast(bf8v, bk), sc[nt], 0, 0, 0);
+                }
+            }
+            // mask (blocks that reach past the workgroup's first token), running max, P
+            if (p0 + BP - 1 > pos0 + t_base) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int nt = 0; nt < 4; ++nt)
+                        if (p0 + nt * 16 + r16 > plast[r][i]) sc[nt][i] = -INFINITY;
             }
 #pragma unroll
-            for (int m = 1; m < 16; m <<= 1) mx = fmaxf(mx, __shfl_xor(mx, m));  // over the lane group
-            const float mn = fmaxf(mrun[i], mx);
-            alpha[i] = mn == -INFINITY ? 1.f : __expf(mrun[i] - mn);
-            mrun[i] = mn;
-            float lsum = 0.f;
+            for (int i = 0; i < 4; ++i) {
+                const float mx = row16_max(fmaxf(fmaxf(sc[0][i], sc[1][i]), fmaxf(sc[2][i], sc[3][i])));
+                const float mn = fmaxf(mrun[r][i], mx);
+                alpha[r][i] = __builtin_amdgcn_exp2f(mrun[r][i] - mn);
+                mrun[r][i] = mn;
+                float lsum = 0.f;
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
-                const float pe = sc[nt][i] == -INFINITY ? 0.f : __expf(sc[nt][i] - mn);
-                lsum += pe;
-                pw[(4 * kg + i) * BP + nt * 16 + r16] = pe;
+                for (int nt = 0; nt < 4; ++nt) {
+                    const float pe = __builtin_amdgcn_exp2f(sc[nt][i] - mn);
+                    lsum += pe;
+                    pw[(4 * kg + i) * BP + nt * 16 + r16] = pe;
+                }
+                lrun[r][i] = lrun[r][i] * alpha[r][i] + lsum;
             }
-            lrun[i] = lrun[i] * alpha[i] + lsum;
+#pragma unroll
+            for (int n = 0; n < NT; ++n)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[r][n][i] *= alpha[r][i];
         }
-#pragma unroll
-        for (int n = 0; n < NT; ++n)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) o[n][i] *= alpha[i];
         __syncthreads();  // P of every lane of the wave is in LDS
         // O += P V: two 32-position k-steps
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-            const float *pp = pw + r16 * BP + 32 * k2 + 8 * kg;
-            const f4v pa = *(const f4v *)pp, pb = *(const f4v *)(pp + 4);
-            const float pv[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
-            uint32_t hw[4], lw[4];
+        for (int r = 0; r < RB; ++r)
 #pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-                const uint16_t ah = f_to_bf(pv[e]), bh = f_to_bf(pv[e + 1]);
-                hw[e / 2] = (uint32_t)ah | ((uint32_t)bh << 16);
-                lw[e / 2] = (uint32_t)f_to_bf(pv[e] - bf_to_f(ah)) | ((uint32_t)f_to_bf(pv[e + 1] - bf_to_f(bh)) << 16);
-            }
-            const u4v ph = u4v{hw[0], hw[1], hw[2], hw[3]}, pl = u4v{lw[0], lw[1], lw[2], lw[3]};
+            for (int k2 = 0; k2 < 2; ++k2) {
+                const float *pp = ps[wv][r] + r16 * BP + 32 * k2 + 8 * kg;
+                const f4v pa = *(const f4v *)pp, pb = *(const f4v *)(pp + 4);
+                const float pv[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+                uint32_t hw[4], lw[4];
 #pragma unroll
-            for (int n = 0; n < NT; ++n) {
-                const u4v b = *(const u4v *)(vt + (n * 16 + r16) * BP + 32 * k2 + 8 * kg);
-                o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, ph), __builtin_bit_cast(bf8v, b),
-                                                               o[n], 0, 0, 0);
-                o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, pl), __builtin_bit_cast(bf8v, b),
-                                                               o[n], 0, 0, 0);
+                for (int e = 0; e < 8; e += 2) split2(pv[e], pv[e + 1], hw[e / 2], lw[e / 2]);
+                const u4v ph = u4v{hw[0], hw[1], hw[2], hw[3]}, pl = u4v{lw[0], lw[1], lw[2], lw[3]};
+#pragma unroll
+                for (int n = 0; n < NT; ++n) {
+                    const u4v bv = *(const u4v *)(vt + (n * 16 + r16) * BP + 32 * k2 + 8 * kg);
+                    o[r][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, ph),
+                                                                      __builtin_bit_cast(bf8v, bv), o[r][n], 0, 0, 0);
+                    o[r][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, pl),
+                                                                      __builtin_bit_cast(bf8v, bv), o[r][n], 0, 0, 0);
+                }
             }
-        }
     }
     // row sums over the lane group, then o / l into the split operand
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        float l = lrun[i];
+    for (int r = 0; r < RB; ++r)
 #pragma unroll
-        for (int m = 1; m < 16; m <<= 1) l += __shfl_xor(l, m);
-        const int m = wv * 16 + 4 * kg + i, t = t_base + m / GQ, g = m % GQ;
-        if (t >= T) continue;
-        const float inv = 1.0f / l;
+        for (int i = 0; i < 4; ++i) {
+            const float l = row16_sum(lrun[r][i]);
+            const int m = (wv * RB + r) * 16 + 4 * kg + i, t = t_base + m / GQ, g = m % GQ;
+            if (t >= T) continue;
+            const float inv = 1.0f / l;
 #pragma unroll
-        for (int n = 0; n < NT; ++n) {
-            const float v = o[n][i] * inv;
-            const uint16_t hi = f_to_bf(v);
-            const size_t idx = (size_t)t * lda + (size_t)(j * GQ + g) * D + n * 16 + r16;
-            Ah[idx] = hi;
-            Al[idx] = f_to_bf(v - bf_to_f(hi));
+            for (int n = 0; n < NT; ++n) {
+                const float v = o[r][n][i] * inv;
+                const uint16_t hi = f_to_bf(v);
+                const size_t idx = (size_t)t * lda + (size_t)(j * GQ + g) * D + n * 16 + r16;
+                Ah[idx] = hi;
+                Al[idx] = f_to_bf(v - bf_to_f(hi));
+            }
         }
-    }
 }
 
 // ---- SwiGLU of the interleaved gate/up rows into the split operand ----------
@@ -556,9 +605,13 @@ __global__ __launch_bounds__(256) void pf_swiglu_split(const float *Y, int ldy, 
 template <int D, int GQ>
 void launch_attn(hipStream_t s, const float *Q, const uint16_t *kc, const uint16_t *vc, int layer, int nh, int nkv,
                  int max_seq, int pos0, int T, uint16_t *Ah, uint16_t *Al, int lda) {
-    const dim3 g((T + 64 / GQ - 1) / (64 / GQ), nkv);
-    hipLaunchKernelGGL((pf_attn_mfma<D, GQ>), g, dim3(256), 0, s, Q, kc, vc, layer, nh, nkv, max_seq, pos0, T, Ah, Al,
-                       lda);
+    // one 16-row block per wave: two measured slower for 2048-token prompts
+    // (the longest query block's chain of position blocks sets the time)
+    constexpr int RB = 1;
+    constexpr int QB = 64 * RB / GQ;
+    const dim3 g((T + QB - 1) / QB * nkv);
+    hipLaunchKernelGGL((pf_attn_mfma<D, GQ, RB>), g, dim3(256), 0, s, Q, kc, vc, layer, nh, nkv, max_seq, pos0, T, Ah,
+                       Al, lda);
 }
 
 int round32(int k) { return (k + 31) & ~31; }
