@@ -605,13 +605,20 @@ __global__ __launch_bounds__(256) void pf_swiglu_split(const float *Y, int ldy, 
 template <int D, int GQ>
 void launch_attn(hipStream_t s, const float *Q, const uint16_t *kc, const uint16_t *vc, int layer, int nh, int nkv,
                  int max_seq, int pos0, int T, uint16_t *Ah, uint16_t *Al, int lda) {
-    // one 16-row block per wave: two measured slower for 2048-token prompts
-    // (the longest query block's chain of position blocks sets the time)
-    constexpr int RB = 1;
-    constexpr int QB = 64 * RB / GQ;
-    const dim3 g((T + QB - 1) / QB * nkv);
-    hipLaunchKernelGGL((pf_attn_mfma<D, GQ, RB>), g, dim3(256), 0, s, Q, kc, vc, layer, nh, nkv, max_seq, pos0, T, Ah,
-                       Al, lda);
+    // Two 16-row blocks per wave halve the K/V fragment reads from LDS per
+    // query row; that pays once the causal ranges are long (a 32768-token
+    // prompt: 259 -> 246 ms of attention), while for short prompts the
+    // longest query block's chain of position blocks sets the time and one
+    // row block per wave is faster (1B, 2048 tokens: 17.4 against 18.4 ms).
+    if (pos0 + T > 8192) {
+        constexpr int QB = 64 * 2 / GQ;
+        hipLaunchKernelGGL((pf_attn_mfma<D, GQ, 2>), dim3((T + QB - 1) / QB * nkv), dim3(256), 0, s, Q, kc, vc, layer, nh,
+                           nkv, max_seq, pos0, T, Ah, Al, lda);
+    } else {
+        constexpr int QB = 64 / GQ;
+        hipLaunchKernelGGL((pf_attn_mfma<D, GQ, 1>), dim3((T + QB - 1) / QB * nkv), dim3(256), 0, s, Q, kc, vc, layer, nh,
+                           nkv, max_seq, pos0, T, Ah, Al, lda);
+    }
 }
 
 int round32(int k) { return (k + 31) & ~31; }
