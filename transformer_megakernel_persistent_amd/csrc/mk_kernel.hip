@@ -1219,23 +1219,11 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
     // 0 * v adds nothing.
     // kget(q, e) / vget(q, e): element e of the lane's K / V piece of chunk q.
     // qget(h, e): element e of the lane's dims of head h's query.
-    auto attn_fold_q = [&](auto &A, auto nq_tag, auto &&qget, auto &&kget, auto &&vget, const bool *valid) {
+    // The update from raw scores sc[q][h] (the lane's share of the dot
+    // product, before the sum over the lane group).
+    auto attn_update = [&](auto &A, auto nq_tag, auto &sc, auto &&vget, const bool *valid) {
         constexpr int NQ = decltype(nq_tag)::value;
         constexpr int NHS = std::remove_reference_t<decltype(A)>::nh;  // heads held by the state
-        float sc[NQ][NHS];
-#pragma unroll
-        for (int h = 0; h < NHS; ++h) {
-            float qv[EPL];
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) qv[e] = qget(h, e);
-#pragma unroll
-            for (int q = 0; q < NQ; ++q) {
-                float t = 0.f;
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) t = fmaf(qv[e], kget(q, e), t);
-                sc[q][h] = t;
-            }
-        }
 #pragma unroll
         for (int q = 0; q < NQ; ++q)
 #pragma unroll
@@ -1269,9 +1257,75 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
             A.am[h] = any ? mn : A.am[h];
         }
     };
+    auto attn_fold_q = [&](auto &A, auto nq_tag, auto &&qget, auto &&kget, auto &&vget, const bool *valid) {
+        constexpr int NQ = decltype(nq_tag)::value;
+        constexpr int NHS = std::remove_reference_t<decltype(A)>::nh;
+        float sc[NQ][NHS];
+#pragma unroll
+        for (int h = 0; h < NHS; ++h) {
+            float qv[EPL];
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) qv[e] = qget(h, e);
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+                float t = 0.f;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) t = fmaf(qv[e], kget(q, e), t);
+                sc[q][h] = t;
+            }
+        }
+        attn_update(A, nq_tag, sc, vget, valid);
+    };
+    // Head-major state, bf16 cache, one head per consumer (QPAIR; with two
+    // heads per consumer the 128-dim instantiation would spill): the query
+    // is held as bf16 hi + lo pairs (A.qr[h][j] carries the bits of the hi
+    // pair of dims 2j, 2j+1 and A.qr[h][4 + j] the lo pair; hi + lo keeps
+    // about 16 bits of each element), and the scores of whole cache pieces
+    // take two v_dot2c_f32_bf16 per pair of dims against the raw K words.
+    constexpr bool QPAIR = CDT == 1 && HPC == 1;
+    auto qpair_set = [&](float (&qr)[EPL], const float *qv) {
+        typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+        for (int j = 0; j < EPL / 2; ++j) {
+            const bf2 h2 = {(__bf16)qv[2 * j], (__bf16)qv[2 * j + 1]};
+            const uint32_t hw = __builtin_bit_cast(uint32_t, h2);
+            const bf2 l2 = {(__bf16)(qv[2 * j] - bf_lo(hw)), (__bf16)(qv[2 * j + 1] - bf_hi(hw))};
+            qr[j] = __uint_as_float(hw);
+            qr[EPL / 2 + j] = __uint_as_float(__builtin_bit_cast(uint32_t, l2));
+        }
+    };
+    auto qpair_elem = [&](const float (&qr)[EPL], int e) -> float {
+        const uint32_t hw = __float_as_uint(qr[e >> 1]), lw = __float_as_uint(qr[EPL / 2 + (e >> 1)]);
+        return (e & 1) ? bf_hi(hw) + bf_hi(lw) : bf_lo(hw) + bf_lo(lw);
+    };
+    auto attn_fold_w = [&](auto &A, auto nq_tag, const u4v *kr, auto &&vget, const bool *valid) {
+        typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+        constexpr int NQ = decltype(nq_tag)::value;
+        constexpr int NHS = std::remove_reference_t<decltype(A)>::nh;
+        float sc[NQ][NHS];
+#pragma unroll
+        for (int h = 0; h < NHS; ++h)
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+                const uint32_t kw[4] = {kr[q].x, kr[q].y, kr[q].z, kr[q].w};
+                float t = 0.f;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const bf2 k2 = __builtin_bit_cast(bf2, kw[j]);
+                    t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, __float_as_uint(A.qr[h][j])), k2, t, false);
+                    t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, __float_as_uint(A.qr[h][4 + j])), k2, t,
+                                                        false);
+                }
+                sc[q][h] = t;
+            }
+        attn_update(A, nq_tag, sc, vget, valid);
+    };
     // The head-major state holds its queries in registers.
     auto attn_fold = [&](auto &A, auto nq_tag, auto &&kget, auto &&vget, const bool *valid) {
-        attn_fold_q(A, nq_tag, [&](int h, int e) { return A.qr[h][e]; }, kget, vget, valid);
+        if constexpr (QPAIR)
+            attn_fold_q(A, nq_tag, [&](int h, int e) { return qpair_elem(A.qr[h], e); }, kget, vget, valid);
+        else
+            attn_fold_q(A, nq_tag, [&](int h, int e) { return A.qr[h][e]; }, kget, vget, valid);
     };
     // This consumer's final state -> its partial records (o over its
     // positions, m, l), one per head, as tagged records.
@@ -1735,10 +1789,17 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
                 AttnState A;
 #pragma unroll
                 for (int k = 0; k < HPC; ++k) {
+                    float qv[EPL];
 #pragma unroll
                     for (int e = 0; e < EPL; ++e) {
-                        A.qr[k][e] = vec[(hc + HG * k) * d + e0 + e];
+                        qv[e] = vec[(hc + HG * k) * d + e0 + e];
                         A.ao[k][e] = 0.f;
+                    }
+                    if constexpr (QPAIR) {
+                        qpair_set(A.qr[k], qv);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < EPL; ++e) A.qr[k][e] = qv[e];
                     }
                     A.am[k] = -INFINITY;
                     A.al[k] = 0.f;
@@ -1780,8 +1841,13 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
                             kr[q] = *(const LDS u4v *)(kb + chunk * MK_CHUNK_BYTES + lane * 16);
                             vr[q] = *(const LDS u4v *)(vb + chunk * MK_CHUNK_BYTES + lane * 16);
                         }
-                        attn_fold(A, std::integral_constant<int, NQB>{}, [&](int q, int e) { return piece_elem<CDT>(kr[q], e); },
-                                  [&](int q, int e) { return piece_elem<CDT>(vr[q], e); }, valid);
+                        if constexpr (QPAIR)
+                            attn_fold_w(A, std::integral_constant<int, NQB>{}, kr,
+                                        [&](int q, int e) { return piece_elem<CDT>(vr[q], e); }, valid);
+                        else
+                            attn_fold(A, std::integral_constant<int, NQB>{},
+                                      [&](int q, int e) { return piece_elem<CDT>(kr[q], e); },
+                                      [&](int q, int e) { return piece_elem<CDT>(vr[q], e); }, valid);
                     }
                     if (n == nsl_kv - 1) finish();
                     js = js + 1 == NS ? 0 : js + 1;
