@@ -365,23 +365,6 @@ __global__ __launch_bounds__(256) void pf_rope_kv(const float *Y, int ldy, int p
 }
 
 // ---- causal GQA attention of the chunk on the matrix cores -----------------
-// Workgroup (query block, KV head j): 64 RB query rows -- QB = 64 RB / GQ
-// tokens x the GQ heads of group j, row m = token (m / GQ), head (m % GQ)
-// -- against blocks of 64 cached positions staged in LDS (K as [pos][dim],
-// V transposed to [dim][pos]); the next block's K and V are loaded into
-// registers while the current one is multiplied.  Wave w owns the RB
-// 16-row blocks 16 (w RB + r) ...  Per position block and row block:
-//   S = Q K^T with v_mfma_f32_16x16x32_bf16 (Q split into bf16 hi + lo, K
-//   exact; Q carries the factor log2(e) / sqrt(d), so that exp2 of a score
-//   is exp of the scaled score), positions past each row's own masked out
-//   (only blocks that reach past the workgroup's first token need the
-//   mask), an online-softmax update of each row's running max, P =
-//   exp2(S - max), then O += P V (P split into hi + lo through LDS into the
-//   A-operand layout, V exact).
-// In the C layout lane l holds rows 4 (l / 16) + i (i < 4) of a 16 x 16 tile
-// at column l % 16, so a row's max over a tile is a reduction over the 16
-// lanes of one lane group, and the output rows a lane rescales are the rows
-// whose scores it holds.  The result o / l goes to the split operand.
 // bf16 hi + lo parts of two floats, packed in pairs (v_cvt_pk_bf16_f32
 // rounds to nearest even): hi = rne(a), lo = rne(a - hi)
 __device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t &lo) {
@@ -391,36 +374,63 @@ __device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t 
     const bf2 l = {(__bf16)(a - __uint_as_float(hi << 16)), (__bf16)(b - __uint_as_float(hi & 0xFFFF0000u))};
     lo = __builtin_bit_cast(uint32_t, l);
 }
-// max / sum over the 16 lanes of a DPP row (one lane group of the C layout)
-template <int CTRL>
-__device__ __forceinline__ float dpp16(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+// Max / sum over the four lanes l, l^16, l^32, l^48 (the gfx950 permlane
+// swaps exchange 16-lane rows 0<->1, 2<->3 and 0<->2, 1<->3).
+__device__ __forceinline__ float cross4_max(float v) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-__device__ __forceinline__ float row16_max(float v) {
-    v = fmaxf(v, dpp16<0xB1>(v));   // quad_perm [1,0,3,2]
-    v = fmaxf(v, dpp16<0x4E>(v));   // quad_perm [2,3,0,1]
-    v = fmaxf(v, dpp16<0x141>(v));  // row_half_mirror
-    return fmaxf(v, dpp16<0x140>(v));  // row_mirror
+__device__ __forceinline__ float cross4_sum(float v) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
-__device__ __forceinline__ float row16_sum(float v) {
-    v += dpp16<0xB1>(v);
-    v += dpp16<0x4E>(v);
-    v += dpp16<0x141>(v);
-    return v + dpp16<0x140>(v);
+// Rows g of x (tile a) and y (tile b), 16 lanes each, rearranged so that
+// row 0 holds (x.row0, x.row1), row 1 (x.row2, x.row3), row 2 (y.row0,
+// y.row1), row 3 (y.row2, y.row3): returned as (first, second).
+__device__ __forceinline__ void rows_pair(uint32_t x, uint32_t y, uint32_t &first, uint32_t &second) {
+    const auto r = __builtin_amdgcn_permlane32_swap(x, y, false, false);  // (x0 x1 y0 y1), (x2 x3 y2 y3)
+    const auto q = __builtin_amdgcn_permlane16_swap(r[0], r[1], false, false);
+    first = q[0];   // (x0 x2 y0 y2)
+    second = q[1];  // (x1 x3 y1 y3)
 }
 
+// Workgroup (query block, KV head j): 64 RB query rows -- QB = 64 RB / GQ
+// tokens x the GQ heads of group j, row m = token (m / GQ), head (m % GQ)
+// -- against blocks of 64 cached positions staged in LDS (K as [pos][dim],
+// V transposed to [dim][pos]); the next block's K and V are loaded into
+// registers while the current one is multiplied.  Wave w owns the RB
+// 16-row blocks 16 (w RB + r) ...  Per position block and row block, with
+// v_mfma_f32_16x16x32_bf16 and the query rows as the N dimension:
+//   S^T = K Q^T (Q split into bf16 hi + lo, K exact; Q carries the factor
+//   log2(e) / sqrt(d), so that exp2 of a score is exp of the scaled score);
+//   in the result layout lane l holds positions 4 (l / 16) + i (i < 4) of
+//   each 16-position tile for the single query row l % 16, so a row's
+//   running max, sum and rescaling are one lane's, completed over the four
+//   lanes l % 16 + 16 k by two lane swaps.  Positions past each row's own
+//   are masked (only blocks that reach past the workgroup's first token
+//   need it); P = exp2(S - max);
+//   O^T += V^T P^T (V exact, P split into hi + lo): P reaches the operand
+//   layout (8 consecutive positions per lane) through two lane swaps per
+//   register pair, not through LDS.
+// The running max starts at a finite floor, so exp2(-inf - max) is 0 for
+// masked scores and the first block's rescaling factor is 0, with no
+// special cases; rows past the chunk's last token attend everything and
+// are never written.  The result o / l goes to the split operand.
 template <int D, int GQ, int RB>
 __global__ __launch_bounds__(256) void pf_attn_mfma(const float *Q, const uint16_t *kc, const uint16_t *vc, int layer,
                                                     int nh, int nkv, int max_seq, int pos0, int T, uint16_t *Ah,
                                                     uint16_t *Al, int lda) {
     constexpr int QB = 64 * RB / GQ;  // tokens per workgroup
-    constexpr int KS = D / 32;        // k-steps of S = Q K^T
+    constexpr int KS = D / 32;        // k-steps of S^T = K Q^T
     constexpr int NT = D / 16;        // output tiles (16 dims each) per row block
     constexpr int BP = 64;            // positions per block
     constexpr int PPT = BP * D / 8 / 256;  // 16-byte K (and V) pieces per thread and block
-    __shared__ __attribute__((aligned(16))) uint16_t ks[BP * D];        // [pos][dim]
-    __shared__ __attribute__((aligned(16))) uint16_t vt[D * BP];        // [dim][pos]
-    __shared__ __attribute__((aligned(16))) float ps[4][RB][16 * BP];   // per wave and row block: P [row][pos]
+    __shared__ __attribute__((aligned(16))) uint16_t ks[BP * D];  // [pos][dim]
+    __shared__ __attribute__((aligned(16))) uint16_t vt[D * BP];  // [dim][pos]
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     // One-dimensional grid, KV head fastest: workgroup w runs on XCD w mod 8,
     // so with 8 KV heads each head's K/V stream stays in one XCD's L2; the
@@ -429,8 +439,11 @@ __global__ __launch_bounds__(256) void pf_attn_mfma(const float *Q, const uint16
     const int j = (int)blockIdx.x % nkv, t_base = (nqb - 1 - (int)blockIdx.x / nkv) * QB;
     const int r16 = lane & 15, kg = lane >> 4;
     const float scale = 1.4426950408889634f / sqrtf((float)D);  // log2(e) / sqrt(d)
-    // A-operand rows of row block r: m = 16 (wv RB + r) + r16
+    // query row of this lane in row block r: m = 16 (wv RB + r) + r16
     u4v qh[RB][KS], ql[RB][KS];
+    int plast[RB];
+    float mrun[RB], lrun[RB];  // lrun: this lane's share of the row sum
+    f4v o[RB][NT];
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
         const int m = (wv * RB + r) * 16 + r16, t = t_base + m / GQ, g = m % GQ;
@@ -445,24 +458,9 @@ __global__ __launch_bounds__(256) void pf_attn_mfma(const float *Q, const uint16
             qh[r][k] = u4v{hw[0], hw[1], hw[2], hw[3]};
             ql[r][k] = u4v{lw[0], lw[1], lw[2], lw[3]};
         }
-    }
-    // C-layout rows of this lane: m = 16 (wv RB + r) + 4 kg + i; the last
-    // position each may attend (rows past the chunk's last token attend
-    // everything and are never written).  The running max starts at a
-    // finite floor, so exp2(-inf - max) is 0 for masked scores and the
-    // first block's rescaling factor is 0, with no special cases.
-    int plast[RB][4];
-    float mrun[RB][4], lrun[RB][4];  // lrun: this lane's share of the row sum
-    f4v o[RB][NT];
-#pragma unroll
-    for (int r = 0; r < RB; ++r) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int m = (wv * RB + r) * 16 + 4 * kg + i, t = t_base + m / GQ;
-            plast[r][i] = t < T ? pos0 + t : 0x7FFFFFFF;
-            mrun[r][i] = -1e30f;
-            lrun[r][i] = 0.f;
-        }
+        plast[r] = tv ? pos0 + t : 0x7FFFFFFF;
+        mrun[r] = -1e30f;
+        lrun[r] = 0.f;
 #pragma unroll
         for (int n = 0; n < NT; ++n) o[r][n] = f4v{0.f, 0.f, 0.f, 0.f};
     }
@@ -486,7 +484,7 @@ __global__ __launch_bounds__(256) void pf_attn_mfma(const float *Q, const uint16
     };
     fetch(0);
     for (int p0 = 0; p0 < n_pos; p0 += BP) {
-        __syncthreads();  // the previous block's K, V and P are consumed
+        __syncthreads();  // the previous block's K and V are consumed
 #pragma unroll
         for (int u = 0; u < PPT; ++u) {
             const int i = tid + 256 * u;
@@ -498,93 +496,92 @@ __global__ __launch_bounds__(256) void pf_attn_mfma(const float *Q, const uint16
         }
         __syncthreads();
         if (p0 + BP < n_pos) fetch(p0 + BP);
-        float alpha[RB][4];
+        const bool diag = p0 + BP - 1 > pos0 + t_base;  // uniform
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
-            float *pw = ps[wv][r];
-            // S: four 16-position tiles
+            // S^T: four 16-position tiles; lane: positions 16 nt + 4 kg + i of row r16
             f4v sc[4];
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) {
                 sc[nt] = f4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int k = 0; k < KS; ++k) {
-                    const u4v bk = *(const u4v *)(ks + (nt * 16 + r16) * D + 32 * k + 8 * kg);
-                    sc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, qh[r][k]),
-                                                                     __builtin_bit_cast(bf8v, bk), sc[nt], 0, 0, 0);
-                    sc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, ql[r][k]),
-                                                                     __builtin_bit_cast(bf8v, bk), sc[nt], 0, 0, 0);
+                    const u4v ak = *(const u4v *)(ks + (nt * 16 + r16) * D + 32 * k + 8 * kg);
+                    sc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, ak),
+                                                                     __builtin_bit_cast(bf8v, qh[r][k]), sc[nt], 0, 0, 0);
+                    sc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, ak),
+                                                                     __builtin_bit_cast(bf8v, ql[r][k]), sc[nt], 0, 0, 0);
                 }
             }
-            // mask (blocks that reach past the workgroup's first token), running max, P
-            if (p0 + BP - 1 > pos0 + t_base) {
+            if (diag) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+                for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-                    for (int nt = 0; nt < 4; ++nt)
-                        if (p0 + nt * 16 + r16 > plast[r][i]) sc[nt][i] = -INFINITY;
+                    for (int i = 0; i < 4; ++i)
+                        if (p0 + nt * 16 + 4 * kg + i > plast[r]) sc[nt][i] = -INFINITY;
             }
+            float mx = sc[0][0];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float mx = row16_max(fmaxf(fmaxf(sc[0][i], sc[1][i]), fmaxf(sc[2][i], sc[3][i])));
-                const float mn = fmaxf(mrun[r][i], mx);
-                alpha[r][i] = __builtin_amdgcn_exp2f(mrun[r][i] - mn);
-                mrun[r][i] = mn;
-                float lsum = 0.f;
+            for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-                for (int nt = 0; nt < 4; ++nt) {
-                    const float pe = __builtin_amdgcn_exp2f(sc[nt][i] - mn);
-                    lsum += pe;
-                    pw[(4 * kg + i) * BP + nt * 16 + r16] = pe;
+                for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[nt][i]);
+            const float mn = fmaxf(mrun[r], cross4_max(mx));
+            const float alpha = __builtin_amdgcn_exp2f(mrun[r] - mn);
+            mrun[r] = mn;
+            float lsum = 0.f;
+            uint32_t ph[4][2], pl[4][2];  // P of each tile as bf16 hi / lo pairs (positions 4 kg + 0,1 and 2,3)
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                float pe[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    pe[i] = __builtin_amdgcn_exp2f(sc[nt][i] - mn);
+                    lsum += pe[i];
                 }
-                lrun[r][i] = lrun[r][i] * alpha[r][i] + lsum;
+                split2(pe[0], pe[1], ph[nt][0], pl[nt][0]);
+                split2(pe[2], pe[3], ph[nt][1], pl[nt][1]);
             }
+            lrun[r] = lrun[r] * alpha + lsum;
 #pragma unroll
-            for (int n = 0; n < NT; ++n)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) o[r][n][i] *= alpha[r][i];
-        }
-        __syncthreads();  // P of every lane of the wave is in LDS
-        // O += P V: two 32-position k-steps
-#pragma unroll
-        for (int r = 0; r < RB; ++r)
+            for (int n = 0; n < NT; ++n) o[r][n] *= alpha;
+            // O^T += V^T P^T: two 32-position k-steps (tiles 2 k2, 2 k2 + 1)
 #pragma unroll
             for (int k2 = 0; k2 < 2; ++k2) {
-                const float *pp = ps[wv][r] + r16 * BP + 32 * k2 + 8 * kg;
-                const f4v pa = *(const f4v *)pp, pb = *(const f4v *)(pp + 4);
-                const float pv[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
-                uint32_t hw[4], lw[4];
-#pragma unroll
-                for (int e = 0; e < 8; e += 2) split2(pv[e], pv[e + 1], hw[e / 2], lw[e / 2]);
-                const u4v ph = u4v{hw[0], hw[1], hw[2], hw[3]}, pl = u4v{lw[0], lw[1], lw[2], lw[3]};
+                uint32_t bh[4], bl[4];
+                rows_pair(ph[2 * k2][0], ph[2 * k2 + 1][0], bh[0], bh[2]);
+                rows_pair(ph[2 * k2][1], ph[2 * k2 + 1][1], bh[1], bh[3]);
+                rows_pair(pl[2 * k2][0], pl[2 * k2 + 1][0], bl[0], bl[2]);
+                rows_pair(pl[2 * k2][1], pl[2 * k2 + 1][1], bl[1], bl[3]);
+                const u4v bph = u4v{bh[0], bh[1], bh[2], bh[3]}, bpl = u4v{bl[0], bl[1], bl[2], bl[3]};
 #pragma unroll
                 for (int n = 0; n < NT; ++n) {
-                    const u4v bv = *(const u4v *)(vt + (n * 16 + r16) * BP + 32 * k2 + 8 * kg);
-                    o[r][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, ph),
-                                                                      __builtin_bit_cast(bf8v, bv), o[r][n], 0, 0, 0);
-                    o[r][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, pl),
-                                                                      __builtin_bit_cast(bf8v, bv), o[r][n], 0, 0, 0);
+                    const u4v av = *(const u4v *)(vt + (n * 16 + r16) * BP + 32 * k2 + 8 * kg);
+                    o[r][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, av),
+                                                                      __builtin_bit_cast(bf8v, bph), o[r][n], 0, 0, 0);
+                    o[r][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, av),
+                                                                      __builtin_bit_cast(bf8v, bpl), o[r][n], 0, 0, 0);
                 }
             }
-    }
-    // row sums over the lane group, then o / l into the split operand
-#pragma unroll
-    for (int r = 0; r < RB; ++r)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float l = row16_sum(lrun[r][i]);
-            const int m = (wv * RB + r) * 16 + 4 * kg + i, t = t_base + m / GQ, g = m % GQ;
-            if (t >= T) continue;
-            const float inv = 1.0f / l;
-#pragma unroll
-            for (int n = 0; n < NT; ++n) {
-                const float v = o[r][n][i] * inv;
-                const uint16_t hi = f_to_bf(v);
-                const size_t idx = (size_t)t * lda + (size_t)(j * GQ + g) * D + n * 16 + r16;
-                Ah[idx] = hi;
-                Al[idx] = f_to_bf(v - bf_to_f(hi));
-            }
         }
+    }
+    // row sums over the four lanes of a row, then o / l into the split
+    // operand: lane holds dims 16 n + 4 kg + i of its row
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+        const float l = cross4_sum(lrun[r]);
+        const int m = (wv * RB + r) * 16 + r16, t = t_base + m / GQ, g = m % GQ;
+        if (t >= T) continue;
+        const float inv = 1.0f / l;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            uint32_t hw[2], lw[2];
+            split2(o[r][n][0] * inv, o[r][n][1] * inv, hw[0], lw[0]);
+            split2(o[r][n][2] * inv, o[r][n][3] * inv, hw[1], lw[1]);
+            const size_t idx = (size_t)t * lda + (size_t)(j * GQ + g) * D + n * 16 + 4 * kg;
+            *(uint2 *)(Ah + idx) = uint2{hw[0], hw[1]};
+            *(uint2 *)(Al + idx) = uint2{lw[0], lw[1]};
+        }
+    }
 }
 
 // ---- SwiGLU of the interleaved gate/up rows into the split operand ----------
