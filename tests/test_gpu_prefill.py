@@ -62,6 +62,16 @@ def test_batched_prefill_mha_tied(env):
     assert max(errs) <= 2e-2 and agree == 3
 
 
+def test_batched_prefill_ragged_gemm_tiles(env):
+    # hidden 160: the QKV and gate/up GEMMs end on a half k-tile (64 + 64 +
+    # 32 inputs) and the O and down GEMMs on a partial tile of 128 outputs
+    # (160 = 128 + 32); one chunk of 150 tokens ends inside the second tile
+    # of 128 tokens; two query heads per KV head
+    cfg = tiny_bf16(hidden=160, n_heads=4, n_kv_heads=2)
+    errs, agree = run_pair(env, cfg, seed=76, n_prompt=150, n_steps=4, expect_batched=True)
+    assert max(errs) <= 2e-2 and agree == 4
+
+
 def test_chunking_is_invisible_and_start_pos(env):
     """Chunks of 7, 64 and 256 positions, and the same prompt prefilled in
     two calls (positions 0..99, then 100..149), leave identical caches."""
