@@ -178,7 +178,8 @@ def measure(name, args, dev, steps, warm, runs, cpu_budget, with_cpu):
     tuning = {"grid": args.grid, "ring_slots": args.ring, "attn_splits": args.splits,
               "cooperative": 1 if args.launch == "cooperative" else 2,
               "prefetch_depth": args.prefetch_depth, "stage_drain": 1 if args.stage_drain else 0,
-              "prefill_chunk": args.prefill_chunk, "attn_pm_slots": args.attn_pm_slots}
+              "prefill_chunk": args.prefill_chunk, "attn_pm_slots": args.attn_pm_slots,
+              "slots_per_step": args.slots_per_step}
     # The oracle baseline needs every weight in host memory; past this size it
     # is not taken (the weights are streamed to the device a layer at a time).
     keep_host = with_cpu and cfg.weight_bytes_per_step() <= HOST_ORACLE_MAX_BYTES
@@ -295,6 +296,8 @@ def main():
                     help="ablation: no loads for a stage before its grid dependency is met")
     ap.add_argument("--prefill-chunk", type=int, default=0,
                     help="tokens per batched-prefill chunk (default 2048); -1: one decode launch per position")
+    ap.add_argument("--slots-per-step", type=int, default=0,
+                    help="16 KiB ring slots per data step, the stream's tile (default 1); a tunable")
     ap.add_argument("--attn-pm-slots", type=int, default=0,
                     help="position-major attention when a split holds at least this many KV slots "
                          "(default 0: always head-major)")
@@ -350,7 +353,8 @@ def main():
             "workload": head["workload"],
             "context": cfg.context, "global_batch": 1, "decode_positions": head["decode_positions"],
             "runs": args.runs, "launches_per_token": 1, "grid": info["grid"], "ring_slots": info["ring_slots"],
-            "prefetch_slots": info["prefetch_slots"], "stage_drain": bool(args.stage_drain),
+            "prefetch_slots": info["prefetch_slots"], "slots_per_step": info["slots_per_step"],
+            "stage_drain": bool(args.stage_drain),
             "attn_splits": info["attn_splits"], "block_threads": info["block_threads"],
             "lds_bytes": info["lds_bytes"], "launch": args.launch, "parallelism": "single GPU"},
         "runs_tokens_per_s": head["runs_tokens_per_s"],

@@ -138,8 +138,8 @@ typedef struct {
      trace:       1 = record a per-workgroup stage timeline on every step
                   (read it with mk_read_trace; default 0 = off);
      prefetch_depth: 16 KiB slots the weight and cache loads run ahead of
-                  the slot being multiplied, 1 .. ring_slots - 1 (default
-                  ring_slots - 1);
+                  the slot being multiplied, slots_per_step .. ring_slots -
+                  slots_per_step (default ring_slots - slots_per_step);
      stage_drain: 1 = no cross-stage prefetch: a stage's first loads wait
                   for the grid dependency before it (the consumers' opening
                   barrier of the stage); 0 = loads run ahead across stage
@@ -160,14 +160,20 @@ typedef struct {
      prefill_chunk: tokens per chunk of the batched prefill, 1..4096
                   (default 2048, or max_seq if smaller); -1 = prefill by one
                   decode launch per position.  The batched prefill needs bf16
-                  or INT8 weights and
-                  a geometry whose down-stage workgroups own inputs starting at
-                  multiples of 8 (true of the Llama shapes at 256
-                  workgroups); otherwise mk_prefill_kv uses decode launches
-                  (mk_info.prefill_chunk reports which). */
+                  or INT8 weights and a geometry whose down-stage workgroups
+                  own inputs starting at multiples of 8 (true of the Llama
+                  shapes at 256 workgroups); otherwise mk_prefill_kv uses
+                  decode launches (mk_info.prefill_chunk reports which);
+     slots_per_step: the tile of the weight and cache stream: 16 KiB ring
+                  slots the consumer waves take per data step, between two
+                  workgroup barriers, 1 or 2 (default 1).  With 2 the loads
+                  of both slots are complete before the step's barrier and
+                  prefetch_depth lies in 2 .. ring_slots - 2.  The tile
+                  granularity is the first tunable of
+                  cloud.baidu.com/article/9434380 section 六. */
 typedef struct {
     int32_t grid, ring_slots, attn_splits, timeout_ms, cooperative, trace, prefetch_depth, stage_drain;
-    int32_t prefill_chunk, attn_pm_slots;
+    int32_t prefill_chunk, attn_pm_slots, slots_per_step;
 } mk_tuning;
 
 typedef struct mk_handle mk_handle;
@@ -181,6 +187,7 @@ typedef struct {
     int64_t record_bytes;    /* cross-workgroup record buffer of one launch (at most
                                 MK_STATIC_SCRATCH_BYTES for the no-allocation step) */
     int32_t prefill_chunk;   /* tokens per batched-prefill chunk; 0: prefill by decode launches */
+    int32_t slots_per_step;  /* 16 KiB ring slots per data step (the stream's tile) */
 } mk_info;
 
 /* Create a handle: validates the shape, copies every weight into a

@@ -137,7 +137,8 @@ def test_create_rejects_bad_shapes(lib, over, status):
 @pytest.mark.parametrize("over", [dict(grid=-1), dict(grid=1025), dict(ring_slots=2), dict(ring_slots=10),
                                   dict(attn_splits=-3), dict(attn_splits=65), dict(timeout_ms=-1), dict(cooperative=3),
                                   dict(trace=2), dict(prefetch_depth=-1), dict(stage_drain=2),
-                                  dict(prefill_chunk=-2), dict(prefill_chunk=4097), dict(attn_pm_slots=-2)])
+                                  dict(prefill_chunk=-2), dict(prefill_chunk=4097), dict(attn_pm_slots=-2),
+                                  dict(slots_per_step=-1), dict(slots_per_step=3)])
 def test_create_rejects_bad_tuning(lib, over):
     w, _keep = _weights(2)
     assert _create(lib, _desc(), w, mkb.Tuning(**over))[0] == mkb.MK_ERR_TUNING

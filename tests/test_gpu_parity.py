@@ -191,9 +191,68 @@ def test_tiny_other_launch_shapes(env, grid, splits, ring, depth, drain):
 def test_prefetch_depth_beyond_ring_is_rejected(env):
     torch, oracle, mkp = env
     cfg = synth.CONFIGS["tiny"]
-    with pytest.raises(mkp.MkError) as e:
-        _make(env, cfg, seed=0, max_seq=32, tuning={"ring_slots": 4, "prefetch_depth": 4})
-    assert e.value.status == mkp.mk.MK_ERR_TUNING
+    for tun in ({"ring_slots": 4, "prefetch_depth": 4},
+                # two slots per data step: the depth must leave both slots of
+                # a step unclaimed and cover both before the step's barrier
+                {"ring_slots": 4, "prefetch_depth": 3, "slots_per_step": 2},
+                {"ring_slots": 8, "prefetch_depth": 1, "slots_per_step": 2}):
+        with pytest.raises(mkp.MkError) as e:
+            _make(env, cfg, seed=0, max_seq=32, tuning=tun)
+        assert e.value.status == mkp.mk.MK_ERR_TUNING, tun
+
+
+# ---- the stream's tile: two ring slots per data step ----
+# Every stage's slot count is odd or even somewhere in these shapes (1B: 3
+# QKV slots; ragged shapes: partial pieces and row groups), so steps of one
+# slot at a stage's end are covered; the ring sizes and depths cover the
+# limits of depth 2 .. ring - 2; fp32 with prefill by decode launches runs
+# the cache-append instantiation.
+
+@pytest.mark.parametrize("case", ["fp32_mha_decode_launch_prefill", "bf16_gqa4_ring4", "bf16_long_context",
+                                  "bf16_position_major", "bf16_group8_head128", "w8_ragged_small_grid",
+                                  "bf16_stage_drain"])
+def test_two_slots_per_step(env, case):
+    tiny = synth.CONFIGS["tiny"]
+    bf = dict(dtype="bf16", rope_theta=500000.0)
+    tun = {"slots_per_step": 2}
+    kw = {}
+    if case == "fp32_mha_decode_launch_prefill":
+        cfg, tol = tiny.with_(n_heads=4, n_kv_heads=4), 1e-4
+        tun.update(prefill_chunk=-1)
+        kw = dict(n_prompt=50, n_steps=4)
+    elif case == "bf16_gqa4_ring4":
+        cfg, tol = tiny.with_(n_heads=8, n_kv_heads=2, **bf), 2e-2
+        tun.update(ring_slots=4, prefetch_depth=2)
+        kw = dict(n_prompt=37, n_steps=4)
+    elif case == "bf16_long_context":
+        cfg, tol = tiny.with_(n_heads=8, n_kv_heads=2, **bf), 2e-2
+        tun.update(grid=64, attn_splits=8)
+        kw = dict(n_prompt=900, n_steps=4, use_prefill=False)
+    elif case == "bf16_position_major":
+        cfg, tol = tiny.with_(n_heads=8, n_kv_heads=2, **bf), 2e-2
+        tun.update(grid=64, attn_splits=8, attn_pm_slots=1)
+        kw = dict(n_prompt=900, n_steps=4, use_prefill=False)
+    elif case == "bf16_group8_head128":
+        cfg, tol = tiny.with_(n_heads=16, n_kv_heads=2, head_dim=128, **bf), 2e-2
+        kw = dict(n_prompt=45, n_steps=4)
+    elif case == "w8_ragged_small_grid":
+        cfg, tol = tiny.with_(dtype="w8", rope_theta=500000.0, tied=False, hidden=264, ffn=696, vocab=1000, n_heads=8,
+                              n_kv_heads=2), 2e-2
+        tun.update(grid=64, attn_splits=8)
+        kw = dict(n_prompt=50, n_steps=4, expect_batched=False)
+    else:  # bf16_stage_drain
+        cfg, tol = tiny.with_(n_heads=8, n_kv_heads=2, **bf), 2e-2
+        tun.update(stage_drain=1, ring_slots=5, prefetch_depth=3)
+        kw = dict(n_prompt=60, n_steps=4)
+    errs, agree = run_pair(env, cfg, seed=80, tuning=tun, **kw)
+    assert max(errs) <= tol and agree == kw["n_steps"]
+
+
+def test_llama1b_two_slots_per_step(env):
+    cfg = synth.CONFIGS["llama1b"]
+    errs, agree = run_pair(env, cfg, seed=81, n_prompt=cfg.context, n_steps=3, gains="random", use_prefill=False,
+                           tuning={"slots_per_step": 2})
+    assert max(errs) <= 2e-2 and agree == 3
 
 
 def test_llama1b_full_size_synthetic_context(env):

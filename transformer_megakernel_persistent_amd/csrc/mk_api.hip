@@ -162,7 +162,7 @@ mk_status validate_tuning(const mk_tuning *t) {
     if (t->grid < 0 || t->grid > MK_MAX_GRID || t->ring_slots < 0 || t->attn_splits < 0 || t->attn_splits > MK_MAX_SPLITS || t->timeout_ms < 0 ||
         t->cooperative < 0 || t->cooperative > 2 || t->trace < 0 || t->trace > 1 || t->prefetch_depth < 0 ||
         t->stage_drain < 0 || t->stage_drain > 1 || t->prefill_chunk < -1 || t->prefill_chunk > 4096 ||
-        t->attn_pm_slots < -1)
+        t->attn_pm_slots < -1 || t->slots_per_step < 0 || t->slots_per_step > 2)
         return MK_ERR_TUNING;
     if (t->ring_slots != 0 && (t->ring_slots < 3 || t->ring_slots > MK_MAX_RING)) return MK_ERR_TUNING;
     return MK_OK;
@@ -335,7 +335,10 @@ static mk_status create_impl(const mk_model_desc *desc, const mk_tuning *tun, mk
     if (ns > MK_DEFAULT_RING && !t.ring_slots) ns = MK_DEFAULT_RING;  // a 9th slot measured no faster
     if (ns > MK_MAX_RING) ns = MK_MAX_RING;
     if (ns < 3 || fixed + ns * MK_SLOT_BYTES > MK_LDS_LIMIT) return MK_ERR_SHAPE;
-    if (t.prefetch_depth > ns - 1) return MK_ERR_TUNING;  // a load needs a consumed ring slot
+    // A load needs a ring slot already consumed, and a data step's slots
+    // must all have been issued before its barrier.
+    const int sps = t.slots_per_step ? t.slots_per_step : 1;
+    if (t.prefetch_depth > ns - sps || (t.prefetch_depth != 0 && t.prefetch_depth < sps)) return MK_ERR_TUNING;
     h->lds_bytes = mk_kernel_lds_bytes(ns, vec_floats, out_rows, 2 * lds_sc);
     const int per_cu = mk_kernel_max_blocks_per_cu(dtype, gq, lpp, h->lds_bytes);
     if (per_cu < 1) return MK_ERR_SHAPE;
@@ -408,7 +411,8 @@ static mk_status create_impl(const mk_model_desc *desc, const mk_tuning *tun, mk
     P.L = L; P.H = H; P.nh = nh; P.nkv = nkv; P.d = d; P.F = F; P.V = V; P.max_seq = D.max_seq;
     P.eps = (float)D.rms_eps;
     P.grid = grid; P.ring_slots = ns; P.splits = splits; P.lds_vec_floats = vec_floats; P.lds_out_rows = out_rows;
-    P.prefetch_depth = t.prefetch_depth ? t.prefetch_depth : ns - 1;
+    P.slots_per_step = sps;
+    P.prefetch_depth = t.prefetch_depth ? t.prefetch_depth : ns - sps;
     P.stage_drain = t.stage_drain;
     // default: head-major at every length (position-major measured slower,
     // 947 against 937 us per 32K-context step; the slot is bound by the
@@ -783,5 +787,6 @@ extern "C" mk_status mk_get_info(const mk_handle *h, mk_info *info) {
     info->weight_bytes = h->weight_bytes;
     info->record_bytes = (int64_t)h->rec.off[7] * (int64_t)sizeof(uint64_t);
     info->prefill_chunk = h->pf.t_max;
+    info->slots_per_step = h->base.slots_per_step;
     return MK_OK;
 }

@@ -103,7 +103,8 @@ struct MkParams {
     float eps;
     // launch shape
     int32_t grid, ring_slots, splits, lds_vec_floats, lds_out_rows;
-    int32_t prefetch_depth;  // slots the loads run ahead of the arithmetic, 1 .. ring_slots-1
+    int32_t prefetch_depth;  // slots the loads run ahead of the arithmetic, slots_per_step .. ring_slots-slots_per_step
+    int32_t slots_per_step;  // ring slots the consumers take between two workgroup barriers (1 or 2)
     int32_t stage_drain;     // 1: no loads for a stage before its opening barrier
     int32_t attn_pm_slots;   // position-major attention when a split holds at least this many whole KV slots
     // weights

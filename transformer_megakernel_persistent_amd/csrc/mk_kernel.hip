@@ -676,14 +676,23 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
             bar();
         };
 
+        // A data step takes TS slots of the current stage (fewer at its end):
+        // the loads of all of them are complete before the step's barrier
+        // (the host keeps depth >= TS, so they have been issued), and with
+        // cons counting the slots handed to the consumers, the issue limit
+        // cons - 1 + depth stays below the ring slots still in use (depth
+        // <= ring - TS).
+        const int TS = p.slots_per_step;
         issue_more();
-        for (int k = 0; k < total; ++k) {
+        for (int k = 0; k < total;) {
             if (wleft == 0) open_next();
             if (dead) break;
-            wait_vm_rt((issued - 1 - k) * CPW);
+            const int take = wleft < TS ? wleft : TS;
+            wait_vm_rt((issued - k - take) * CPW);  // slots k .. k + take - 1 have landed
             bar();
-            ++cons;
-            --wleft;
+            cons += take;
+            wleft -= take;
+            k += take;
             issue_more();
         }
         close_walk();
@@ -708,6 +717,12 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
         ++step;
+    };
+    // The barrier of a data step: before slot n (stage-local) of every stage
+    // when n is a multiple of slots_per_step -- the loaders' schedule.
+    const bool ts2 = p.slots_per_step == 2;
+    auto data_barrier = [&](int n) {
+        if (!ts2 || (n & 1) == 0) barrier();
     };
 
     // ---- tagged records ----------------------------------------------------
@@ -964,7 +979,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
     auto gemv_reg_steps = [&](int st, int l, const float (&hr)[4][EPLW]) {
         const int units = g.units[st];
         for (int n = 0; n < g.nsl[st]; ++n) {
-            barrier();
+            data_barrier(n);
             stamp_step(l, 0);
             if (n < units) {
                 const LDS unsigned char *bp = ring + js * MK_SLOT_BYTES + c * 4 * MK_CHUNK_BYTES + lane * 16;
@@ -1012,7 +1027,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
         for (int grp = 0; grp < full; ++grp) {
             float acc[4] = {0.f, 0.f, 0.f, 0.f};
             for (int s = 0; s < rbp; ++s, ++n) {
-                barrier();
+                data_barrier(n);
                 stamp_step(l, 0);
                 const LDS unsigned char *bp = ring + js * MK_SLOT_BYTES + c * 4 * MK_CHUNK_BYTES + lane * 16;
                 float hv[EPLW];
@@ -1034,7 +1049,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
         int row_c = full * 4, kc = 0;
         float acc = 0.f;
         for (; n < g.nsl[st]; ++n) {
-            barrier();
+            data_barrier(n);
             stamp_step(l, 0);
             const LDS unsigned char *bp = ring + js * MK_SLOT_BYTES + c * 4 * MK_CHUNK_BYTES + lane * 16;
             if ((rbp & 3) == 0) {  // the piece lies inside one row
@@ -1106,7 +1121,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
             int gl = 0, q = 0;
             float acc = 0.f;
             for (int n = 0; n < g.nsl[ST_DOWN]; ++n) {
-                barrier();
+                data_barrier(n);
                 stamp_step(l, 0);
                 const int grp = c + 4 * gl;
                 if (grp < ng) {  // wave-uniform
@@ -1137,7 +1152,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
         int gl = 0, q = 0;
         float acc = 0.f;
         for (int n = 0; n < g.nsl[ST_DOWN]; ++n) {
-            barrier();
+            data_barrier(n);
             stamp_step(l, 0);
             const LDS unsigned char *bp = ring + js * MK_SLOT_BYTES + c * 4 * MK_CHUNK_BYTES + lane * 16;
 #pragma unroll
@@ -1763,7 +1778,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
                             }
                         };
                         for (int n = 0; n < nsl_kv; ++n) {
-                            barrier();
+                            data_barrier(n);
                             stamp_step(l, 0);
                             const LDS unsigned char *kb = ring + js * MK_SLOT_BYTES;
                             const LDS unsigned char *vb = kb + 8 * MK_CHUNK_BYTES;
@@ -1825,7 +1840,7 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
                 };
                 if (nsl_kv == 0) finish();
                 for (int n = 0; n < nsl_kv; ++n) {
-                    barrier();
+                    data_barrier(n);
                     stamp_step(l, 0);
                     const LDS unsigned char *kb = ring + js * MK_SLOT_BYTES;
                     const LDS unsigned char *vb = kb + 8 * MK_CHUNK_BYTES;

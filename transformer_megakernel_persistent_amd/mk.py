@@ -54,14 +54,16 @@ class Tuning(ctypes.Structure):
     _fields_ = [("grid", ctypes.c_int32), ("ring_slots", ctypes.c_int32), ("attn_splits", ctypes.c_int32),
                 ("timeout_ms", ctypes.c_int32), ("cooperative", ctypes.c_int32), ("trace", ctypes.c_int32),
                 ("prefetch_depth", ctypes.c_int32), ("stage_drain", ctypes.c_int32),
-                ("prefill_chunk", ctypes.c_int32), ("attn_pm_slots", ctypes.c_int32)]
+                ("prefill_chunk", ctypes.c_int32), ("attn_pm_slots", ctypes.c_int32),
+                ("slots_per_step", ctypes.c_int32)]
 
 
 class Info(ctypes.Structure):
     _fields_ = [("grid", ctypes.c_int32), ("ring_slots", ctypes.c_int32), ("attn_splits", ctypes.c_int32),
                 ("block_threads", ctypes.c_int32), ("lds_bytes", ctypes.c_int32), ("cu_count", ctypes.c_int32),
                 ("prefetch_slots", ctypes.c_int32), ("packed_bytes", ctypes.c_int64), ("weight_bytes", ctypes.c_int64),
-                ("record_bytes", ctypes.c_int64), ("prefill_chunk", ctypes.c_int32)]
+                ("record_bytes", ctypes.c_int64), ("prefill_chunk", ctypes.c_int32),
+                ("slots_per_step", ctypes.c_int32)]
 
 
 _lib = None
