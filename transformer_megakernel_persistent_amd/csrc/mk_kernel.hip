@@ -586,7 +586,9 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
         int lstep = 0;  // barriers passed; mirrors the consumers' step counter
         // optional timeline: loader 0's arrival at and exit from the barriers
         // of layer 1 (and the start of layer 2), barrier indices [b0, b0 + 96)
-        const int lb0 = 5 + nsl_q + nsl_kv + nsl_o + nsl_gu + nsl_dn;
+        const int sps = p.slots_per_step;
+        auto nsteps = [&](int n) { return (n + sps - 1) / sps; };  // data steps of a stage of n slots
+        const int lb0 = 5 + nsteps(nsl_q) + nsteps(nsl_kv) + nsteps(nsl_o) + nsteps(nsl_gu) + nsteps(nsl_dn);
         auto lstamp = [&](int e) {
             if (p.trace && wl == 0 && lane == 0 && lstep >= lb0 && lstep < lb0 + 96)
                 p.trace[(size_t)G * (5 * L + 2) * 4 + (size_t)G * 64 * 2 + ((size_t)w * 96 + lstep - lb0) * 2 + e] =
@@ -594,14 +596,15 @@ __global__ __launch_bounds__(MK_BLOCK_THREADS, 1) void mk_decode_kernel(const Mk
         };
         const int total = L * (nsl_q + nsl_kv + nsl_o + nsl_gu + nsl_dn) + (LOGITS ? nsl_lm : 0);
         // Slot m goes straight into ring slot m % NS.  The loads run up to
-        // `depth` slots ahead of the slot being consumed (at most NS-1: the
-        // ring slot must have been consumed) and, unless stage_drain is set,
-        // across stage boundaries; with stage_drain a stage's first loads wait
-        // for its opening barrier.  `issued` counts the slots issued so far,
-        // so the wait before data step k is exact: slot k's loads are done
-        // when at most (issued - 1 - k) * CPW newer loads are outstanding.
+        // `depth` slots ahead of the slot being consumed (at most NS -
+        // slots_per_step: the ring slot must have been consumed) and, unless
+        // stage_drain is set, across stage boundaries; with stage_drain a
+        // stage's first loads wait for its opening barrier.  `issued` counts
+        // the slots issued so far, so the wait before a data step is exact:
+        // slot k's loads are done when at most (issued - 1 - k) * CPW newer
+        // loads are outstanding.
         const int depth = p.prefetch_depth;
-        int issued = 0, cons = 0;                  // slots issued; data barriers passed
+        int issued = 0, cons = 0;                  // slots issued; slots handed to the consumers
         int cap = p.stage_drain ? -1 : total - 1;  // last slot that may be issued now
         int jl = 0;                                // ring slot of the next issue
         auto issue_more = [&]() {
