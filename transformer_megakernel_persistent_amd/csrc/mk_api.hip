@@ -189,23 +189,12 @@ extern "C" const char *mk_status_str(mk_status s) {
 
 extern "C" void mk_destroy(mk_handle *h) {
     if (!h) return;
-    hipFree(h->packed);
-    hipFree(h->wg_off);
-    hipFree(h->gains);
-    hipFree(h->embed);
-    hipFree(h->rope);
-    hipFree(h->scl);
-    hipFree(h->ll);
-    hipFree(h->err);
-    hipFree(h->trace);
-    hipFree(h->pf.X);
-    hipFree(h->pf.Ah);
-    hipFree(h->pf.Al);
-    hipFree(h->pf.Y);
-    hipFree(h->pf.Q);
-    hipFree(h->pf_tokens);
-    hipFree((void *)h->pf.dmap);
-    if (h->done) hipEventDestroy(h->done);
+    // Teardown has no way to report a failure: the frees' statuses are
+    // deliberately dropped (a failed free leaves nothing to undo).
+    void *const bufs[] = {h->packed, h->wg_off, h->gains, h->embed, h->rope, h->scl, h->ll, h->err, h->trace,
+                          h->pf.X, h->pf.Ah, h->pf.Al, h->pf.Y, h->pf.Q, h->pf_tokens, (void *)h->pf.dmap};
+    for (void *b : bufs) (void)hipFree(b);
+    if (h->done) (void)hipEventDestroy(h->done);
     delete h;
 }
 
