@@ -196,13 +196,18 @@ __global__ __launch_bounds__(256) void pf_gemm(const MkStage st, const unsigned 
         pah[j] = Ah + (size_t)(am[j] ? m : 0) * lda + 8 * apart;
         pal[j] = Al + (size_t)(am[j] ? m : 0) * lda + 8 * apart;
     }
-    RowLoc rl[4];
+    // int8 rows of the row-split stages: 16 codes per load, row
+    // (tid >> 2) + 64 j (j < 2), inputs 16 (tid & 3) .. +15 of the k-tile
+    constexpr bool WIDE = Q8 && !DOWN;
+    constexpr int NBR = WIDE ? 2 : 4;  // B loads per thread and k-tile
+    const int brow = WIDE ? tid >> 2 : arow, bstep = WIDE ? 64 : 32, bpart = WIDE ? tid & 3 : apart;
+    RowLoc rl[NBR];
     bool bn[4];
     const int dn = n0 + (tid & 127), dfb = tid >> 7;
     if constexpr (!DOWN) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int n = n0 + arow + 32 * j;
+        for (int j = 0; j < NBR; ++j) {
+            const int n = n0 + brow + bstep * j;
             bn[j] = n < N;
             rl[j] = row_loc(st, layer_block, grid, bn[j] ? n : 0, EB);
         }
@@ -223,14 +228,9 @@ __global__ __launch_bounds__(256) void pf_gemm(const MkStage st, const unsigned 
         }
         return u4v{w[0], w[1], w[2], w[3]};
     };
-    auto load_b8 = [&](const unsigned char *q) -> u4v {
-        if constexpr (Q8) {
-            const uint2 c = *(const uint2 *)q;
-            return widen8(c.x, c.y);
-        } else {
-            return *(const u4v *)q;
-        }
-    };
+    // B loads keep their raw bytes (bf16 pieces, or 8 / 16 int8 codes) until
+    // the tile is staged: widening at the load would make the next tile's
+    // loads complete before the current tile's products.
     // down stage: the map entries of the next fetch's input blocks, read one
     // k-tile ahead so that no fetch waits for its own lookups
     int4 dme[4];
@@ -241,7 +241,7 @@ __global__ __launch_bounds__(256) void pf_gemm(const MkStage st, const unsigned 
             dme[j] = f < F ? *(const int4 *)(dmap + 4 * (f >> 3)) : int4{0, 0, 0, 0};
         }
     };
-    u4v rah[4], ral[4], rb[4];
+    u4v rah[4], ral[4], rb[NBR];
     auto fetch = [&](int kb) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -250,13 +250,19 @@ __global__ __launch_bounds__(256) void pf_gemm(const MkStage st, const unsigned 
             ral[j] = am[j] && kin ? *(const u4v *)(pal[j] + kb) : zero;
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < NBR; ++j) {
             if constexpr (DOWN) {
                 const int f = kb + 8 * (dfb + 2 * j);
-                rb[j] = bn[j] && f < F ? load_b8(down_piece(st, layer_block, dme[j], dn)) : zero;
+                const unsigned char *q = down_piece(st, layer_block, dme[j], dn);
+                if constexpr (Q8) {
+                    const uint2 c = bn[j] && f < F ? *(const uint2 *)q : uint2{0u, 0u};
+                    rb[j] = u4v{c.x, c.y, 0u, 0u};
+                } else {
+                    rb[j] = bn[j] && f < F ? *(const u4v *)q : zero;
+                }
             } else {
-                const int k = kb + 8 * apart;
-                rb[j] = bn[j] && k < K ? load_b8(row_piece(rl[j], st.slot_stride, k, EB)) : zero;
+                const int k = kb + (WIDE ? 16 : 8) * bpart;
+                rb[j] = bn[j] && k < K ? *(const u4v *)row_piece(rl[j], st.slot_stride, k, EB) : zero;
             }
         }
         if constexpr (DOWN) dmap_read(kb + BK);
@@ -267,10 +273,18 @@ __global__ __launch_bounds__(256) void pf_gemm(const MkStage st, const unsigned 
             const int r = arow + 32 * j;
             *(u4v *)(sah + r * LDK + 8 * apart) = rah[j];
             *(u4v *)(sal + r * LDK + 8 * apart) = ral[j];
-            if constexpr (DOWN)
-                *(u4v *)(sb + (tid & 127) * LDK + 8 * (dfb + 2 * j)) = rb[j];
-            else
-                *(u4v *)(sb + r * LDK + 8 * apart) = rb[j];
+        }
+#pragma unroll
+        for (int j = 0; j < NBR; ++j) {
+            if constexpr (DOWN) {
+                *(u4v *)(sb + (tid & 127) * LDK + 8 * (dfb + 2 * j)) = Q8 ? widen8(rb[j].x, rb[j].y) : rb[j];
+            } else if constexpr (WIDE) {
+                uint16_t *d = sb + (brow + bstep * j) * LDK + 16 * bpart;
+                *(u4v *)d = widen8(rb[j].x, rb[j].y);
+                *(u4v *)(d + 8) = widen8(rb[j].z, rb[j].w);
+            } else {
+                *(u4v *)(sb + (arow + 32 * j) * LDK + 8 * apart) = rb[j];
+            }
         }
     };
     f4v acc[4][4];
