@@ -14,8 +14,8 @@
 //     rotate q, k; K, V rows of positions pos0..pos0+T-1 -> cache (bf16 RNE)
 //     A = split(causal GQA attention of each token over positions 0..its own)
 //     X += A . Wo^T
-//     A = split(rmsnorm(X, g_ffn));  Y = A . [Wg;Wu]^T
-//     A = split(silu(gate) * up);    X += A . Wd^T
+//     A = split(rmsnorm(X, g_ffn));  A' = split(silu(gate) * up) of
+//       [gate; up] = A . [Wg;Wu]^T (in the GEMM's epilogue);  X += A' . Wd^T
 //
 // Numerics.  Weights are bf16, or int8 codes widened to bf16 (exact: an int8
 // value has at most 8 significant bits) whose per-row scale multiplies the
@@ -168,11 +168,11 @@ __device__ __forceinline__ float row_scale(const ScaleIdx &si, int kind, int n) 
 // or 8 int8 codes widened to bf16 (exact); Q8 multiplies each output
 // column's sum by its row's scale.  Rows at or past N, tokens at or past T
 // and inputs at or past K (a multiple of 32) enter as zeros.
-template <bool DOWN, bool ADD, bool Q8>
+template <bool DOWN, bool ADD, bool Q8, bool SWIGLU>
 __global__ __launch_bounds__(256) void pf_gemm(const MkStage st, const unsigned char *layer_block, int grid, int F,
                                                int H, const uint16_t *Ah, const uint16_t *Al, int lda, int T, int K,
-                                               int N, float *out, int ldo, const ScaleIdx si, int kind,
-                                               const int32_t *dmap) {
+                                               int N, float *out, int ldo, uint16_t *oh, uint16_t *ol,
+                                               const ScaleIdx si, int kind, const int32_t *dmap) {
     constexpr int EB = Q8 ? 1 : 2;
     constexpr int BM = 128, BN = 128, BK = 64, LDK = BK + 8;
     __shared__ __attribute__((aligned(16))) uint16_t sah[BM * LDK], sal[BM * LDK], sb[BN * LDK];
@@ -322,6 +322,33 @@ __global__ __launch_bounds__(256) void pf_gemm(const MkStage st, const unsigned 
                         __builtin_bit_cast(bf8v, fl[mb]), __builtin_bit_cast(bf8v, fb[nb]), acc[mb][nb], 0, 0, 0);
                 }
         }
+    }
+    if constexpr (SWIGLU) {
+        // gate/up rows interleave in the packed order (row 2f the gate, row
+        // 2f + 1 the up projection of SwiGLU input f), so lane r16 ^ 1 holds
+        // the partner of this lane's column: a = silu(gate) * up, split into
+        // the down projection's bf16 hi + lo operand at [token][f]
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+            const int n = n0 + wn * 64 + nb * 16 + r16;
+            const float sc = Q8 && n < N ? row_scale(si, kind, n) : 1.0f;
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float v = Q8 ? acc[mb][nb][i] * sc : acc[mb][nb][i];
+                    const float up = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+                    const int m = m0 + wm * 64 + mb * 16 + 4 * kg + i;
+                    if ((r16 & 1) == 0 && n < N && m < T) {
+                        const float a = v / (1.0f + __expf(-v)) * up;
+                        const uint16_t hi = f_to_bf(a);
+                        const size_t idx = (size_t)m * ldo + (n >> 1);
+                        oh[idx] = hi;
+                        ol[idx] = f_to_bf(a - bf_to_f(hi));
+                    }
+                }
+        }
+        return;
     }
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
@@ -598,19 +625,15 @@ __global__ __launch_bounds__(256) void pf_attn_mfma(const float *Q, const uint16
     }
 }
 
-// ---- SwiGLU of the interleaved gate/up rows into the split operand ----------
-__global__ __launch_bounds__(256) void pf_swiglu_split(const float *Y, int ldy, int F, uint16_t *Ah, uint16_t *Al,
-                                                       int lda, int kpad) {
-    const int t = blockIdx.y, f = blockIdx.x * 256 + threadIdx.x;
-    if (f >= kpad) return;
-    float a = 0.f;
-    if (f < F) {
-        const float gv = Y[(size_t)t * ldy + 2 * f], uv = Y[(size_t)t * ldy + 2 * f + 1];
-        a = gv / (1.0f + __expf(-gv)) * uv;
+// ---- zero padding of the down projection's operand ------------------------
+// Columns [F, kpad) of the SwiGLU operand (the gate/up GEMM writes [0, F)),
+// when F is not a multiple of 32.
+__global__ __launch_bounds__(64) void pf_zero_cols(uint16_t *Ah, uint16_t *Al, int lda, int F, int kpad) {
+    const int t = blockIdx.x, f = F + (int)threadIdx.x;
+    if (f < kpad) {
+        Ah[(size_t)t * lda + f] = 0;
+        Al[(size_t)t * lda + f] = 0;
     }
-    const uint16_t hi = f_to_bf(a);
-    Ah[(size_t)t * lda + f] = hi;
-    Al[(size_t)t * lda + f] = f_to_bf(a - bf_to_f(hi));
 }
 
 template <int D, int GQ>
@@ -635,18 +658,20 @@ void launch_attn(hipStream_t s, const float *Q, const uint16_t *kc, const uint16
 int round32(int k) { return (k + 31) & ~31; }
 
 // One GEMM of the chunk: bf16 or int8 weights of stage `kind`, N outputs
-// per token; workgroups cover 128 tokens x 128 outputs.
-template <bool DOWN, bool ADD>
+// per token; workgroups cover 128 tokens x 128 outputs.  SWIGLU: the
+// outputs are gate/up rows and the epilogue writes the down projection's
+// split operand (oh, ol with leading dimension ldo) instead of out.
+template <bool DOWN, bool ADD, bool SWIGLU = false>
 void launch_gemm(bool q8, hipStream_t s, const MkStage &st, const unsigned char *blk, int grid, int F, int H,
                  const uint16_t *Ah, const uint16_t *Al, int lda, int T, int K, int N, float *out, int ldo,
-                 const ScaleIdx &si, int kind, const int32_t *dmap) {
+                 uint16_t *oh, uint16_t *ol, const ScaleIdx &si, int kind, const int32_t *dmap) {
     const dim3 g((N + 127) / 128, (T + 127) / 128);
     if (q8)
-        hipLaunchKernelGGL((pf_gemm<DOWN, ADD, true>), g, dim3(256), 0, s, st, blk, grid, F, H, Ah, Al, lda, T, K, N,
-                           out, ldo, si, kind, dmap);
+        hipLaunchKernelGGL((pf_gemm<DOWN, ADD, true, SWIGLU>), g, dim3(256), 0, s, st, blk, grid, F, H, Ah, Al, lda, T, K,
+                           N, out, ldo, oh, ol, si, kind, dmap);
     else
-        hipLaunchKernelGGL((pf_gemm<DOWN, ADD, false>), g, dim3(256), 0, s, st, blk, grid, F, H, Ah, Al, lda, T, K, N,
-                           out, ldo, si, kind, dmap);
+        hipLaunchKernelGGL((pf_gemm<DOWN, ADD, false, SWIGLU>), g, dim3(256), 0, s, st, blk, grid, F, H, Ah, Al, lda, T,
+                           K, N, out, ldo, oh, ol, si, kind, dmap);
 }
 
 }  // namespace
@@ -674,7 +699,7 @@ extern "C" int mk_prefill_chunk(const MkParams *p, const MkPrefillBufs *b, int T
         hipLaunchKernelGGL(pf_norm_split, dim3(T), dim3(256), 0, s, b->X, p->g_attn + (size_t)l * H, H, p->eps, b->Ah,
                            b->Al, lda, round32(H));
         launch_gemm<false, false>(q8, s, p->st[ST_QKV], blk[ST_QKV], G, F, H, b->Ah, b->Al, lda, T, round32(H), nqkv,
-                                  b->Y, ldy, si, ST_QKV, b->dmap);
+                                  b->Y, ldy, nullptr, nullptr, si, ST_QKV, b->dmap);
         const int nthr = (nh + nkv) * d / 2 + nkv * d;
         hipLaunchKernelGGL(pf_rope_kv, dim3((nthr + 255) / 256, T), dim3(256), 0, s, b->Y, ldy, pos0, p->rope, nh, nkv,
                            d, l, p->max_seq, kc, vc, b->Q);
@@ -686,27 +711,34 @@ extern "C" int mk_prefill_chunk(const MkParams *p, const MkPrefillBufs *b, int T
 #undef MK_PF_ATTN
         }
         launch_gemm<false, true>(q8, s, p->st[ST_O], blk[ST_O], G, F, H, b->Ah, b->Al, lda, T, round32(nq), H, b->X, H,
-                                 si, ST_O, b->dmap);
+                                 nullptr, nullptr, si, ST_O, b->dmap);
         // feed-forward half
         hipLaunchKernelGGL(pf_norm_split, dim3(T), dim3(256), 0, s, b->X, p->g_ffn + (size_t)l * H, H, p->eps, b->Ah,
                            b->Al, lda, round32(H));
-        launch_gemm<false, false>(q8, s, p->st[ST_GU], blk[ST_GU], G, F, H, b->Ah, b->Al, lda, T, round32(H), 2 * F,
-                                  b->Y, ldy, si, ST_GU, b->dmap);
-        hipLaunchKernelGGL(pf_swiglu_split, dim3((round32(F) + 255) / 256, T), dim3(256), 0, s, b->Y, ldy, F, b->Ah,
-                           b->Al, lda, round32(F));
-        launch_gemm<true, true>(q8, s, p->st[ST_DOWN], blk[ST_DOWN], G, F, H, b->Ah, b->Al, lda, T, round32(F), H,
-                                b->X, H, si, ST_DOWN, b->dmap);
+        // gate/up with SwiGLU in the epilogue: the down projection's split
+        // operand goes to the Y buffer (free until the next layer's QKV; it
+        // holds T x 2F floats, the operand 2 x T x round32(F) bf16 values)
+        const int ldf = round32(F);
+        uint16_t *Fh = (uint16_t *)b->Y, *Fl = Fh + (size_t)T * ldf;
+        launch_gemm<false, false, true>(q8, s, p->st[ST_GU], blk[ST_GU], G, F, H, b->Ah, b->Al, lda, T, round32(H),
+                                        2 * F, nullptr, ldf, Fh, Fl, si, ST_GU, b->dmap);
+        if (ldf != F) hipLaunchKernelGGL(pf_zero_cols, dim3(T), dim3(64), 0, s, Fh, Fl, ldf, F, ldf);
+        launch_gemm<true, true>(q8, s, p->st[ST_DOWN], blk[ST_DOWN], G, F, H, Fh, Fl, ldf, T, ldf, H, b->X, H, nullptr,
+                                nullptr, si, ST_DOWN, b->dmap);
     }
     return (int)hipGetLastError();
 }
 
 // Whether the batched prefill applies to a handle's geometry: bf16 or INT8
-// weights (a bf16 cache), head_dim 64 or 128, and every down-stage
+// weights (a bf16 cache), head_dim 64 or 128, FFN width 16 or more, and every down-stage
 // workgroup's first input a multiple of 8 (8 consecutive inputs of a row, the
 // unit of a GEMM lane's B operand, then lie in one 16-byte piece of its piece
 // columns).
 extern "C" int mk_prefill_supported(const MkParams *p, int dtype) {
     if ((dtype != 1 && dtype != 2) || (p->d != 64 && p->d != 128)) return 0;
+    // the SwiGLU operand (2 x round32(F) bf16 values per token) lives in the
+    // gate/up output buffer (2F floats per token)
+    if (round32(p->F) > 2 * p->F) return 0;
     const int U = p->st[ST_DOWN].units;
     for (int w = 0; w < p->grid; ++w) {
         const MkDownGeo dg = mk_down_geo(w, p->grid, U, p->F, p->H, dtype == 2 ? 16 : 8);
