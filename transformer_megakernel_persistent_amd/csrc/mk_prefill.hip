@@ -470,8 +470,11 @@ __global__ __launch_bounds__(256) void pf_attn_mfma(const float *Q, const uint16
     constexpr int NT = D / 16;        // output tiles (16 dims each) per row block
     constexpr int BP = 64;            // positions per block
     constexpr int PPT = BP * D / 8 / 256;  // 16-byte K (and V) pieces per thread and block
-    __shared__ __attribute__((aligned(16))) uint16_t ks[BP * D];  // [pos][dim]
-    __shared__ __attribute__((aligned(16))) uint16_t vt[D * BP];  // [dim][pos]
+    // rows padded by 16 bytes, so that the 16 rows one fragment read touches
+    // (lanes l % 16) fall in different banks
+    constexpr int LK = D + 8, LV = BP + 8;
+    __shared__ __attribute__((aligned(16))) uint16_t ks[BP * LK];  // [pos][dim]
+    __shared__ __attribute__((aligned(16))) uint16_t vt[D * LV];   // [dim][pos]
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     // One-dimensional grid, KV head fastest: workgroup w runs on XCD w mod 8,
     // so with 8 KV heads each head's K/V stream stays in one XCD's L2; the
@@ -529,11 +532,11 @@ __global__ __launch_bounds__(256) void pf_attn_mfma(const float *Q, const uint16
 #pragma unroll
         for (int u = 0; u < PPT; ++u) {
             const int i = tid + 256 * u;
-            *(u4v *)(ks + (i / (D / 8)) * D + 8 * (i % (D / 8))) = kr[u];
+            *(u4v *)(ks + (i / (D / 8)) * LK + 8 * (i % (D / 8))) = kr[u];
             const int vrow = i % BP, vcp = i / BP;
             const uint32_t w4[4] = {vr[u].x, vr[u].y, vr[u].z, vr[u].w};
 #pragma unroll
-            for (int e = 0; e < 8; ++e) vt[(8 * vcp + e) * BP + vrow] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
+            for (int e = 0; e < 8; ++e) vt[(8 * vcp + e) * LV + vrow] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
         }
         __syncthreads();
         if (p0 + BP < n_pos) fetch(p0 + BP);
@@ -547,7 +550,7 @@ __global__ __launch_bounds__(256) void pf_attn_mfma(const float *Q, const uint16
                 sc[nt] = f4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int k = 0; k < KS; ++k) {
-                    const u4v ak = *(const u4v *)(ks + (nt * 16 + r16) * D + 32 * k + 8 * kg);
+                    const u4v ak = *(const u4v *)(ks + (nt * 16 + r16) * LK + 32 * k + 8 * kg);
                     sc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, ak),
                                                                      __builtin_bit_cast(bf8v, qh[r][k]), sc[nt], 0, 0, 0);
                     sc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, ak),
@@ -596,7 +599,7 @@ __global__ __launch_bounds__(256) void pf_attn_mfma(const float *Q, const uint16
                 const u4v bph = u4v{bh[0], bh[1], bh[2], bh[3]}, bpl = u4v{bl[0], bl[1], bl[2], bl[3]};
 #pragma unroll
                 for (int n = 0; n < NT; ++n) {
-                    const u4v av = *(const u4v *)(vt + (n * 16 + r16) * BP + 32 * k2 + 8 * kg);
+                    const u4v av = *(const u4v *)(vt + (n * 16 + r16) * LV + 32 * k2 + 8 * kg);
                     o[r][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, av),
                                                                       __builtin_bit_cast(bf8v, bph), o[r][n], 0, 0, 0);
                     o[r][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, av),
