@@ -72,6 +72,18 @@ def test_batched_prefill_ragged_gemm_tiles(env):
     assert max(errs) <= 2e-2 and agree == 4
 
 
+def test_batched_prefill_wide_tiles_ragged(env):
+    # GEMMs with at least 256 tiles of 128 tokens x 256 outputs take the
+    # wide tile.  ffn 2112 over 8 workgroups (264 SwiGLU inputs each, slices
+    # on multiples of 8): gate/up has 4224 outputs, 16.5 wide tiles, and a
+    # 2000-token chunk ends inside its 16th tile of 128 tokens (17 x 16 =
+    # 272 tiles); the other GEMMs stay on 128-output tiles
+    cfg = tiny_bf16(ffn=2112, n_layers=2)
+    errs, agree = run_pair(env, cfg, seed=78, n_prompt=2000, n_steps=3, tuning={"grid": 8, "attn_splits": 4},
+                           expect_batched=True)
+    assert max(errs) <= 2e-2 and agree == 3
+
+
 @pytest.mark.parametrize("heads,head_dim", [(4, 64), (8, 128)])
 def test_batched_prefill_long_prompt_two_row_blocks(env, heads, head_dim):
     # Once a chunk's causal range passes 8192 positions the attention takes

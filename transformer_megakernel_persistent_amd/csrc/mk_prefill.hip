@@ -131,6 +131,12 @@ __device__ __forceinline__ const unsigned char *down_piece(const MkStage &st, co
            (n & 63) * 16 + e.w;
 }
 
+// Entry i of the down stage's map (int4 per block of 8 inputs), read at a
+// wave-uniform index.
+__device__ __forceinline__ int4 dmap4(const int32_t *__restrict__ dmap, int i) {
+    return *(const int4 *)(dmap + 4 * i);
+}
+
 // INT8: the scale of output n of stage `kind` in one layer, read from the
 // decode kernel's per-workgroup scale blocks (MkParams::scl): a block holds
 // the workgroup's QKV, O and gate/up rows and then the down rows of its x
@@ -150,6 +156,61 @@ __device__ __forceinline__ float row_scale(const ScaleIdx &si, int kind, int n) 
     if (kind == ST_GU || kind == ST_DOWN) off += 4 * count(w, si.uo);
     if (kind == ST_DOWN) off += 4 * count(w, si.ugu);
     return si.blk[(size_t)w * si.sc_blk + off];
+}
+
+// The epilogue of both GEMM kernels: wave (wm, wn)'s 64 x 64 block of
+// products in the v_mfma_f32_16x16x32_bf16 result layout (acc[mb][nb]
+// element i is C[m0 + wm*64 + mb*16 + 4*kg + i][n0 + wn*64 + nb*16 + r16]),
+// stored, added to out, or (SWIGLU) turned into the down projection's
+// operand.
+template <bool ADD, bool Q8, bool SWIGLU>
+__device__ __forceinline__ void gemm_store(const f4v (&acc)[4][4], int m0, int n0, int wm, int wn, int r16, int kg,
+                                           int T, int N, float *out, int ldo, uint16_t *oh, uint16_t *ol,
+                                           const ScaleIdx &si, int kind) {
+    if constexpr (SWIGLU) {
+        // gate/up rows interleave in the packed order (row 2f the gate, row
+        // 2f + 1 the up projection of SwiGLU input f), so lane r16 ^ 1 holds
+        // the partner of this lane's column: a = silu(gate) * up, split into
+        // the down projection's bf16 hi + lo operand at [token][f]
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+            const int n = n0 + wn * 64 + nb * 16 + r16;
+            const float sc = Q8 && n < N ? row_scale(si, kind, n) : 1.0f;
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float v = Q8 ? acc[mb][nb][i] * sc : acc[mb][nb][i];
+                    const float up = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+                    const int m = m0 + wm * 64 + mb * 16 + 4 * kg + i;
+                    if ((r16 & 1) == 0 && n < N && m < T) {
+                        const float a = v / (1.0f + __expf(-v)) * up;
+                        const uint16_t hi = f_to_bf(a);
+                        const size_t idx = (size_t)m * ldo + (n >> 1);
+                        oh[idx] = hi;
+                        ol[idx] = f_to_bf(a - bf_to_f(hi));
+                    }
+                }
+        }
+    } else {
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+            const int n = n0 + wn * 64 + nb * 16 + r16;
+            if (n >= N) continue;
+            const float sc = Q8 ? row_scale(si, kind, n) : 1.0f;
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int m = m0 + wm * 64 + mb * 16 + 4 * kg + i;
+                    if (m >= T) continue;
+                    float *o = out + (size_t)m * ldo + n;
+                    const float v = Q8 ? acc[mb][nb][i] * sc : acc[mb][nb][i];
+                    if (ADD) *o += v;
+                    else *o = v;
+                }
+        }
+    }
 }
 
 // ---- GEMM: out[t][n] (=|+=) sum_k (Ah + Al)[t][k] * W[n][k] -----------------
@@ -323,49 +384,249 @@ __global__ __launch_bounds__(256) void pf_gemm(const MkStage st, const unsigned 
                 }
         }
     }
-    if constexpr (SWIGLU) {
-        // gate/up rows interleave in the packed order (row 2f the gate, row
-        // 2f + 1 the up projection of SwiGLU input f), so lane r16 ^ 1 holds
-        // the partner of this lane's column: a = silu(gate) * up, split into
-        // the down projection's bf16 hi + lo operand at [token][f]
+    gemm_store<ADD, Q8, SWIGLU>(acc, m0, n0, wm, wn, r16, kg, T, N, out, ldo, oh, ol, si, kind);
+}
+
+// ---- GEMM with a load ring (bf16 weights) ----------------------------------
+// The same products and epilogue as pf_gemm, organised like the decode
+// kernel: 8 waves, 4 of them loaders that stream 32-input steps of A hi, A
+// lo and B into a ring of LDS stages with direct-to-LDS loads, 4 of them
+// multiplying (2 x 2).  The loads run NST - 1 steps ahead of the products,
+// with one workgroup barrier per step, and no register holds an operand
+// between its load and its LDS copy.
+// Tile 128 tokens x BN outputs.  BN = 128: 6 stages of 24 KiB, waves of
+// 64 x 64, fragments double-buffered (a wave reads step s + 1's fragments
+// before it multiplies step s's).  BN = 256: 5 stages of 32 KiB, waves of
+// 64 x 128; a third fewer operand bytes per product (A, the bf16 hi + lo
+// pair, costs 4 bytes per element against B's 2), for GEMMs with enough
+// output tiles to fill the chip.
+// Stage layout: [row][32 inputs] for A hi, A lo and row-split B (64-byte
+// rows, the four 16-byte pieces of row r at position piece ^ rg_swz(r), so
+// that the 16 rows of one fragment read fall in distinct banks); the down
+// stage's B as [8-input block][row] (its piece columns, 64 rows of one block
+// contiguous in memory).  Rows past T or N and down inputs past F read a
+// zeroed 1 KiB (zsrc).
+constexpr int RG_BK = 32;
+constexpr int RG_WIDE_MIN_TILES = 256;  // 128 x 256 tiles when they fill the 256 CUs once
+constexpr int RG_SEC = 128 * RG_BK * 2;  // A hi (or A lo) of one step: 128 rows of 64 bytes
+template <int BN>
+struct RgCfg {
+    static constexpr int NST = BN == 128 ? 6 : 5;          // ring stages
+    static constexpr int SECB = BN * RG_BK * 2;            // B of one step
+    static constexpr int STAGE = 2 * RG_SEC + SECB;
+    static constexpr int LDS = NST * STAGE;
+    static constexpr int QB = BN / 64;                     // B loads per loader wave and step
+    static constexpr int LOADS = 4 + QB;                   // direct-to-LDS loads per loader wave and step
+    static constexpr int NB = BN / 32;                     // 16-output blocks per multiplying wave
+};
+static_assert(RgCfg<128>::LDS <= MK_LDS_LIMIT && RgCfg<256>::LDS <= MK_LDS_LIMIT, "ring fits the LDS");
+__device__ __forceinline__ int rg_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+// s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt bits [3:0] and [15:14]; expcnt and
+// lgkmcnt left at their maxima)
+template <int N>
+__device__ __forceinline__ void rg_wait_vm() {
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+// n a multiple of L up to 3 L; anything else waits for every load
+template <int L>
+__device__ __forceinline__ void rg_wait_vm_rt(int n) {
+    if (n == L) rg_wait_vm<L>();
+    else if (n == 2 * L) rg_wait_vm<2 * L>();
+    else if (n == 3 * L) rg_wait_vm<3 * L>();
+    else if (n == 4 * L) rg_wait_vm<4 * L>();
+    else rg_wait_vm<0>();
+}
+static_assert((RgCfg<128>::NST - 2) * RgCfg<128>::LOADS <= 4 * RgCfg<128>::LOADS &&
+                  (RgCfg<256>::NST - 2) * RgCfg<256>::LOADS <= 4 * RgCfg<256>::LOADS &&
+                  4 * RgCfg<256>::LOADS < 64,
+              "the waits cover the steady-state counts within the counter");
+
+template <bool DOWN, bool ADD, bool SWIGLU, int BN>
+__global__ __launch_bounds__(512, 1) void pf_gemm_ring(const MkStage st, const unsigned char *layer_block, int grid,
+                                                       int F, const uint16_t *Ah, const uint16_t *Al, int lda, int T,
+                                                       int K, int N, float *out, int ldo, uint16_t *oh, uint16_t *ol,
+                                                       const int32_t *__restrict__ dmap,
+                                                       const unsigned char *__restrict__ zsrc) {
+    typedef RgCfg<BN> C;
+    typedef __attribute__((address_space(3))) unsigned char lds_u8;
+    extern __shared__ __attribute__((aligned(16))) unsigned char rg_smem[];
+    lds_u8 *ring = (lds_u8 *)rg_smem;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int m0 = blockIdx.y * 128, n0 = blockIdx.x * BN;
+    const int nst = K / RG_BK;
+
+    if (wave < 4) {
+        // ============================ loader ============================
+        // Wave lw carries rows [32 lw, 32 lw + 32) of A hi and A lo and rows
+        // [BN/4 lw, BN/4 (lw + 1)) of row-split B, 16 rows per load: lane l
+        // takes row base + l / 4 and LDS position l % 4, i.e. the row's piece
+        // (l % 4) ^ rg_swz(row).  Down stage: B block lw of every step, rows
+        // 64 h + l.
+        const int lw = wave;
+        const unsigned char *zl = zsrc + lane * 16;
+        const unsigned char *pah[2], *pal[2];
+        int ja[2];
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-            const int n = n0 + wn * 64 + nb * 16 + r16;
-            const float sc = Q8 && n < N ? row_scale(si, kind, n) : 1.0f;
-#pragma unroll
-            for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float v = Q8 ? acc[mb][nb][i] * sc : acc[mb][nb][i];
-                    const float up = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
-                    const int m = m0 + wm * 64 + mb * 16 + 4 * kg + i;
-                    if ((r16 & 1) == 0 && n < N && m < T) {
-                        const float a = v / (1.0f + __expf(-v)) * up;
-                        const uint16_t hi = f_to_bf(a);
-                        const size_t idx = (size_t)m * ldo + (n >> 1);
-                        oh[idx] = hi;
-                        ol[idx] = f_to_bf(a - bf_to_f(hi));
-                    }
-                }
+        for (int q = 0; q < 2; ++q) {
+            const int row = 32 * lw + 16 * q + (lane >> 2);
+            ja[q] = (lane & 3) ^ rg_swz(row);
+            const int m = m0 + row;
+            pah[q] = m < T ? (const unsigned char *)(Ah + (size_t)m * lda + 8 * ja[q]) : nullptr;
+            pal[q] = m < T ? (const unsigned char *)(Al + (size_t)m * lda + 8 * ja[q]) : nullptr;
         }
+        RowLoc rl[C::QB];
+        bool bok[C::QB];
+        int jb[C::QB];
+#pragma unroll
+        for (int q = 0; q < C::QB; ++q) {
+            const int row = (BN / 4) * lw + 16 * q + (lane >> 2);
+            jb[q] = (lane & 3) ^ rg_swz(row);
+            const int n = DOWN ? n0 + 64 * q + lane : n0 + row;
+            bok[q] = n < N;
+            if constexpr (!DOWN) rl[q] = row_loc(st, layer_block, grid, bok[q] ? n : 0, 2);
+        }
+        auto issue = [&](int s) {
+            lds_u8 *base = ring + (s % C::NST) * C::STAGE;
+            const int k0 = s * RG_BK;
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                lds_u8 *dst = base + (32 * lw + 16 * q) * (RG_BK * 2);
+                __builtin_amdgcn_global_load_lds((const void *)(pah[q] ? pah[q] + 2 * k0 : zl),
+                                                 (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
+                __builtin_amdgcn_global_load_lds((const void *)(pal[q] ? pal[q] + 2 * k0 : zl),
+                                                 (__attribute__((address_space(3))) void *)(dst + RG_SEC), 16, 0, 0);
+            }
+            if constexpr (DOWN) {
+                const int f = k0 + 8 * lw;  // this wave's block of the step (wave-uniform)
+                const int4 e = f < F ? dmap4(dmap, f >> 3) : int4{0, 0, 0, 0};
+#pragma unroll
+                for (int h = 0; h < C::QB; ++h) {
+                    const unsigned char *src = f < F && bok[h] ? down_piece(st, layer_block, e, n0 + 64 * h + lane) : zl;
+                    __builtin_amdgcn_global_load_lds(
+                        (const void *)src,
+                        (__attribute__((address_space(3))) void *)(base + 2 * RG_SEC + lw * (BN * 16) + h * 1024), 16, 0,
+                        0);
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < C::QB; ++q) {
+                    const unsigned char *src = bok[q] ? row_piece(rl[q], st.slot_stride, k0 + 8 * jb[q], 2) : zl;
+                    __builtin_amdgcn_global_load_lds(
+                        (const void *)src,
+                        (__attribute__((address_space(3))) void *)(base + 2 * RG_SEC +
+                                                                   ((BN / 4) * lw + 16 * q) * (RG_BK * 2)),
+                        16, 0, 0);
+                }
+            }
+        };
+        // Step s is in stage s % NST.  Before barrier s a loader waits until
+        // its loads of step s have landed (loads of later steps may still be
+        // in flight); after it, every multiplying wave has read step s - 1
+        // into registers, so that stage takes step s + NST - 1.
+        const int pro = nst < C::NST - 1 ? nst : C::NST - 1;
+        for (int s = 0; s < pro; ++s) issue(s);
+        int issued = pro;
+        for (int s = 0; s < nst; ++s) {
+            rg_wait_vm_rt<C::LOADS>((issued - 1 - s) * C::LOADS);
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            if (issued < nst) {
+                issue(issued);
+                ++issued;
+            }
+        }
+        rg_wait_vm<0>();
         return;
     }
+
+    // ============================ products ============================
+    const int c = wave - 4, wm = c >> 1, wn = c & 1;
+    const int r16 = lane & 15, kg = lane >> 4;
+    int aoff[4], boff[C::NB];
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-        const int n = n0 + wn * 64 + nb * 16 + r16;
-        if (n >= N) continue;
-        const float sc = Q8 ? row_scale(si, kind, n) : 1.0f;
+    for (int i = 0; i < 4; ++i) {
+        const int ra = wm * 64 + i * 16 + r16;
+        aoff[i] = ra * (RG_BK * 2) + ((kg ^ rg_swz(ra)) << 4);
+    }
+#pragma unroll
+    for (int i = 0; i < C::NB; ++i) {
+        const int rb = wn * (BN / 2) + i * 16 + r16;
+        boff[i] = 2 * RG_SEC + (DOWN ? kg * (BN * 16) + rb * 16 : rb * (RG_BK * 2) + ((kg ^ rg_swz(rb)) << 4));
+    }
+    f4v acc[4][C::NB];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb) acc[mb][nb] = f4v{0.f, 0.f, 0.f, 0.f};
+    auto step_barrier = [&]() {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    };
+    constexpr int NX = BN == 128 ? 2 : 1;  // fragment buffers
+    u4v fh[NX][4], fl[NX][4], fb[NX][C::NB];
+    auto read_step = [&](int sb, int x) {
+        const lds_u8 *base = ring + sb * C::STAGE;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            fh[x][i] = *(const __attribute__((address_space(3))) u4v *)(base + aoff[i]);
+            fl[x][i] = *(const __attribute__((address_space(3))) u4v *)(base + RG_SEC + aoff[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < C::NB; ++i) fb[x][i] = *(const __attribute__((address_space(3))) u4v *)(base + boff[i]);
+    };
+    auto products = [&](int x) {
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int m = m0 + wm * 64 + mb * 16 + 4 * kg + i;
-                if (m >= T) continue;
-                float *o = out + (size_t)m * ldo + n;
-                const float v = Q8 ? acc[mb][nb][i] * sc : acc[mb][nb][i];
-                if (ADD) *o += v;
-                else *o = v;
+            for (int nb = 0; nb < C::NB; ++nb) {
+                acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, fh[x][mb]),
+                                                                      __builtin_bit_cast(bf8v, fb[x][nb]), acc[mb][nb], 0, 0, 0);
+                acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, fl[x][mb]),
+                                                                      __builtin_bit_cast(bf8v, fb[x][nb]), acc[mb][nb], 0, 0, 0);
             }
+    };
+    if constexpr (NX == 2) {
+        // double-buffered: after barrier s + 1 read step s + 1, then multiply
+        // step s (barrier s + 1 also frees step s's stage for the loaders)
+        step_barrier();
+        read_step(0, 0);
+        int sb = 1;  // stage of step s + 1
+        for (int s = 0; s + 1 < nst; s += 2) {
+            step_barrier();
+            read_step(sb, 1);
+            sb = sb + 1 == C::NST ? 0 : sb + 1;
+            products(0);
+            if (s + 2 < nst) {
+                step_barrier();
+                read_step(sb, 0);
+                sb = sb + 1 == C::NST ? 0 : sb + 1;
+            }
+            products(1);
+        }
+        if (nst & 1) products(0);  // the last step of an odd count
+    } else {
+        int sb = 0;
+        for (int s = 0; s < nst; ++s) {
+            step_barrier();
+            read_step(sb, 0);
+            sb = sb + 1 == C::NST ? 0 : sb + 1;
+            products(0);
+        }
+    }
+    const ScaleIdx none = {nullptr, 0, 1, 0, 0, 0};
+#pragma unroll
+    for (int h = 0; h < C::NB / 4; ++h) {
+        f4v part[4][4];
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) part[mb][nb] = acc[mb][4 * h + nb];
+        // columns n0 + wn * BN/2 + 64 h + nb * 16 + r16
+        gemm_store<ADD, false, SWIGLU>(part, m0, n0 + wn * (BN / 2) + 64 * h, wm, 0, r16, kg, T, N, out, ldo, oh, ol,
+                                       none, 0);
     }
 }
 
@@ -667,14 +928,27 @@ int round32(int k) { return (k + 31) & ~31; }
 template <bool DOWN, bool ADD, bool SWIGLU = false>
 void launch_gemm(bool q8, hipStream_t s, const MkStage &st, const unsigned char *blk, int grid, int F, int H,
                  const uint16_t *Ah, const uint16_t *Al, int lda, int T, int K, int N, float *out, int ldo,
-                 uint16_t *oh, uint16_t *ol, const ScaleIdx &si, int kind, const int32_t *dmap) {
+                 uint16_t *oh, uint16_t *ol, const ScaleIdx &si, int kind, const int32_t *dmap,
+                 const unsigned char *zsrc) {
     const dim3 g((N + 127) / 128, (T + 127) / 128);
-    if (q8)
+    if (q8) {
         hipLaunchKernelGGL((pf_gemm<DOWN, ADD, true, SWIGLU>), g, dim3(256), 0, s, st, blk, grid, F, H, Ah, Al, lda, T, K,
                            N, out, ldo, oh, ol, si, kind, dmap);
-    else
-        hipLaunchKernelGGL((pf_gemm<DOWN, ADD, false, SWIGLU>), g, dim3(256), 0, s, st, blk, grid, F, H, Ah, Al, lda, T,
-                           K, N, out, ldo, oh, ol, si, kind, dmap);
+    } else if ((int64_t)((N + 255) / 256) * ((T + 127) / 128) >= RG_WIDE_MIN_TILES) {
+        // 128 x 256 tiles: fewer operand bytes per product, when there are
+        // enough of them for every CU
+        constexpr int lds = RgCfg<256>::LDS;
+        (void)hipFuncSetAttribute((const void *)pf_gemm_ring<DOWN, ADD, SWIGLU, 256>,
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        hipLaunchKernelGGL((pf_gemm_ring<DOWN, ADD, SWIGLU, 256>), dim3((N + 255) / 256, (T + 127) / 128), dim3(512), lds,
+                           s, st, blk, grid, F, Ah, Al, lda, T, K, N, out, ldo, oh, ol, dmap, zsrc);
+    } else {
+        constexpr int lds = RgCfg<128>::LDS;  // above the default dynamic limit
+        (void)hipFuncSetAttribute((const void *)pf_gemm_ring<DOWN, ADD, SWIGLU, 128>,
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        hipLaunchKernelGGL((pf_gemm_ring<DOWN, ADD, SWIGLU, 128>), g, dim3(512), lds, s, st, blk, grid, F, Ah, Al, lda,
+                           T, K, N, out, ldo, oh, ol, dmap, zsrc);
+    }
 }
 
 }  // namespace
@@ -702,7 +976,7 @@ extern "C" int mk_prefill_chunk(const MkParams *p, const MkPrefillBufs *b, int T
         hipLaunchKernelGGL(pf_norm_split, dim3(T), dim3(256), 0, s, b->X, p->g_attn + (size_t)l * H, H, p->eps, b->Ah,
                            b->Al, lda, round32(H));
         launch_gemm<false, false>(q8, s, p->st[ST_QKV], blk[ST_QKV], G, F, H, b->Ah, b->Al, lda, T, round32(H), nqkv,
-                                  b->Y, ldy, nullptr, nullptr, si, ST_QKV, b->dmap);
+                                  b->Y, ldy, nullptr, nullptr, si, ST_QKV, b->dmap, p->packed);
         const int nthr = (nh + nkv) * d / 2 + nkv * d;
         hipLaunchKernelGGL(pf_rope_kv, dim3((nthr + 255) / 256, T), dim3(256), 0, s, b->Y, ldy, pos0, p->rope, nh, nkv,
                            d, l, p->max_seq, kc, vc, b->Q);
@@ -714,7 +988,7 @@ extern "C" int mk_prefill_chunk(const MkParams *p, const MkPrefillBufs *b, int T
 #undef MK_PF_ATTN
         }
         launch_gemm<false, true>(q8, s, p->st[ST_O], blk[ST_O], G, F, H, b->Ah, b->Al, lda, T, round32(nq), H, b->X, H,
-                                 nullptr, nullptr, si, ST_O, b->dmap);
+                                 nullptr, nullptr, si, ST_O, b->dmap, p->packed);
         // feed-forward half
         hipLaunchKernelGGL(pf_norm_split, dim3(T), dim3(256), 0, s, b->X, p->g_ffn + (size_t)l * H, H, p->eps, b->Ah,
                            b->Al, lda, round32(H));
@@ -724,10 +998,10 @@ extern "C" int mk_prefill_chunk(const MkParams *p, const MkPrefillBufs *b, int T
         const int ldf = round32(F);
         uint16_t *Fh = (uint16_t *)b->Y, *Fl = Fh + (size_t)T * ldf;
         launch_gemm<false, false, true>(q8, s, p->st[ST_GU], blk[ST_GU], G, F, H, b->Ah, b->Al, lda, T, round32(H),
-                                        2 * F, nullptr, ldf, Fh, Fl, si, ST_GU, b->dmap);
+                                        2 * F, nullptr, ldf, Fh, Fl, si, ST_GU, b->dmap, p->packed);
         if (ldf != F) hipLaunchKernelGGL(pf_zero_cols, dim3(T), dim3(64), 0, s, Fh, Fl, ldf, F, ldf);
         launch_gemm<true, true>(q8, s, p->st[ST_DOWN], blk[ST_DOWN], G, F, H, Fh, Fl, ldf, T, ldf, H, b->X, H, nullptr,
-                                nullptr, si, ST_DOWN, b->dmap);
+                                nullptr, si, ST_DOWN, b->dmap, p->packed);
     }
     return (int)hipGetLastError();
 }
