@@ -84,6 +84,16 @@ def test_batched_prefill_wide_tiles_ragged(env):
     assert max(errs) <= 2e-2 and agree == 3
 
 
+def test_batched_prefill_input_split_ragged(env):
+    # hidden 2048 (the 1B width): the down GEMM has 8 x 16 wide tiles, too
+    # few for the chip, and 4096 inputs, so it runs as two input splits (the
+    # second one's sums added afterwards); a 1930-token chunk ends inside the
+    # 16th tile of 128 tokens
+    cfg = tiny_bf16(hidden=2048, n_heads=16, n_kv_heads=2, head_dim=128, ffn=4096, n_layers=1)
+    errs, agree = run_pair(env, cfg, seed=77, n_prompt=1930, n_steps=3, expect_batched=True)
+    assert max(errs) <= 2e-2 and agree == 3
+
+
 @pytest.mark.parametrize("heads,head_dim", [(4, 64), (8, 128)])
 def test_batched_prefill_long_prompt_two_row_blocks(env, heads, head_dim):
     # Once a chunk's causal range passes 8192 positions the attention takes

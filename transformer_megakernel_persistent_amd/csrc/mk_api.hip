@@ -438,7 +438,9 @@ static mk_status create_impl(const mk_model_desc *desc, const mk_tuning *tun, mk
         HIP_TRY(hipMalloc(&B.Ah, (size_t)T * B.lda * sizeof(uint16_t)));
         HIP_TRY(hipMalloc(&B.Al, (size_t)T * B.lda * sizeof(uint16_t)));
         HIP_TRY(hipMalloc(&B.Y, (size_t)T * B.ldy * sizeof(float)));
-        HIP_TRY(hipMalloc(&B.Q, (size_t)T * nh * d * sizeof(float)));
+        // the rotated queries, and during the O and down projections the
+        // second input split's sums ([T][H])
+        HIP_TRY(hipMalloc(&B.Q, (size_t)T * (nh * d > H ? nh * d : H) * sizeof(float)));
         HIP_TRY(hipMalloc(&h->pf_tokens, (size_t)D.max_seq * sizeof(int32_t)));
         // where each block of 8 down-projection inputs lives (mk_down_geo)
         {

@@ -161,7 +161,7 @@ struct MkPrefillBufs {
     uint16_t *Ah;    // [t_max][lda] bf16 high parts of the current GEMM operand
     uint16_t *Al;    // [t_max][lda] bf16 low parts (a - hi)
     float *Y;        // [t_max][ldy] QKV or gate/up outputs, packed row order
-    float *Q;        // [t_max][nh*d] rotated queries
+    float *Q;        // [t_max][max(nh*d, H)] rotated queries; an input split's sums in the O and down GEMMs
     int32_t *tok;    // token ids of the chunk (device)
     // [F/8][4] where the down projection keeps each block of 8 consecutive
     // inputs (one 16-byte piece or half of one): the owning workgroup's

@@ -446,7 +446,7 @@ __global__ __launch_bounds__(512, 1) void pf_gemm_ring(const MkStage st, const u
                                                        int F, const uint16_t *Ah, const uint16_t *Al, int lda, int T,
                                                        int K, int N, float *out, int ldo, uint16_t *oh, uint16_t *ol,
                                                        const int32_t *__restrict__ dmap,
-                                                       const unsigned char *__restrict__ zsrc) {
+                                                       const unsigned char *__restrict__ zsrc, float *part) {
     typedef RgCfg<BN> C;
     typedef __attribute__((address_space(3))) unsigned char lds_u8;
     extern __shared__ __attribute__((aligned(16))) unsigned char rg_smem[];
@@ -454,7 +454,13 @@ __global__ __launch_bounds__(512, 1) void pf_gemm_ring(const MkStage st, const u
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int m0 = blockIdx.y * 128, n0 = blockIdx.x * BN;
-    const int nst = K / RG_BK;
+    // Split along the inputs (gridDim.z = 2, ADD only): split 0 takes the
+    // first half of the steps and adds its sums to out as usual, split 1 the
+    // rest and stores its sums to part [T][N]; pf_add_part then adds part
+    // to out.  out + sums0 + sums1, in that order: deterministic.
+    const int nall = K / RG_BK, kz = blockIdx.z;
+    const int sbeg = kz ? nall / 2 : 0;
+    const int nst = gridDim.z == 1 ? nall : kz ? nall - nall / 2 : nall / 2;
 
     if (wave < 4) {
         // ============================ loader ============================
@@ -488,7 +494,7 @@ __global__ __launch_bounds__(512, 1) void pf_gemm_ring(const MkStage st, const u
         }
         auto issue = [&](int s) {
             lds_u8 *base = ring + (s % C::NST) * C::STAGE;
-            const int k0 = s * RG_BK;
+            const int k0 = (sbeg + s) * RG_BK;
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
                 lds_u8 *dst = base + (32 * lw + 16 * q) * (RG_BK * 2);
@@ -608,6 +614,9 @@ __global__ __launch_bounds__(512, 1) void pf_gemm_ring(const MkStage st, const u
         }
         if (nst & 1) products(0);  // the last step of an odd count
     } else {
+        // 64 x 128 per wave: one set of fragments (a second one, or reading
+        // the next step's A fragments as each block row finishes, measured
+        // slower: 238 VGPRs and hazards on the matrix-core sources)
         int sb = 0;
         for (int s = 0; s < nst; ++s) {
             step_barrier();
@@ -619,15 +628,25 @@ __global__ __launch_bounds__(512, 1) void pf_gemm_ring(const MkStage st, const u
     const ScaleIdx none = {nullptr, 0, 1, 0, 0, 0};
 #pragma unroll
     for (int h = 0; h < C::NB / 4; ++h) {
-        f4v part[4][4];
+        f4v sub[4][4];
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb) part[mb][nb] = acc[mb][4 * h + nb];
+            for (int nb = 0; nb < 4; ++nb) sub[mb][nb] = acc[mb][4 * h + nb];
         // columns n0 + wn * BN/2 + 64 h + nb * 16 + r16
-        gemm_store<ADD, false, SWIGLU>(part, m0, n0 + wn * (BN / 2) + 64 * h, wm, 0, r16, kg, T, N, out, ldo, oh, ol,
-                                       none, 0);
+        if (kz == 0)
+            gemm_store<ADD, false, SWIGLU>(sub, m0, n0 + wn * (BN / 2) + 64 * h, wm, 0, r16, kg, T, N, out, ldo, oh, ol,
+                                           none, 0);
+        else
+            gemm_store<false, false, false>(sub, m0, n0 + wn * (BN / 2) + 64 * h, wm, 0, r16, kg, T, N, part, N,
+                                            nullptr, nullptr, none, 0);
     }
+}
+
+// out[t][n] += part[t][n] (the second input split of a ring GEMM)
+__global__ __launch_bounds__(256) void pf_add_part(float *out, int ldo, const float *part, int N) {
+    const int t = blockIdx.y, n = blockIdx.x * 256 + threadIdx.x;
+    if (n < N) out[(size_t)t * ldo + n] += part[(size_t)t * N + n];
 }
 
 // ---- rotary encoding and the cache rows of the chunk ------------------------
@@ -929,25 +948,35 @@ template <bool DOWN, bool ADD, bool SWIGLU = false>
 void launch_gemm(bool q8, hipStream_t s, const MkStage &st, const unsigned char *blk, int grid, int F, int H,
                  const uint16_t *Ah, const uint16_t *Al, int lda, int T, int K, int N, float *out, int ldo,
                  uint16_t *oh, uint16_t *ol, const ScaleIdx &si, int kind, const int32_t *dmap,
-                 const unsigned char *zsrc) {
+                 const unsigned char *zsrc, float *part) {
     const dim3 g((N + 127) / 128, (T + 127) / 128);
+    const int64_t wide = (int64_t)((N + 255) / 256) * ((T + 127) / 128);
+    // An adding GEMM whose wide tiles fill half the chip and whose inputs
+    // run long is split in two along the inputs (the 1B down projection):
+    // twice the workgroups at a third fewer operand bytes per product.  At
+    // 2048 inputs (the 1B O projection) the halves are too short to pay for
+    // the extra pass over the sums.
+    const bool split = ADD && part && wide * 2 >= RG_WIDE_MIN_TILES && wide < RG_WIDE_MIN_TILES && K >= 4096;
     if (q8) {
         hipLaunchKernelGGL((pf_gemm<DOWN, ADD, true, SWIGLU>), g, dim3(256), 0, s, st, blk, grid, F, H, Ah, Al, lda, T, K,
                            N, out, ldo, oh, ol, si, kind, dmap);
-    } else if ((int64_t)((N + 255) / 256) * ((T + 127) / 128) >= RG_WIDE_MIN_TILES) {
+    } else if (wide >= RG_WIDE_MIN_TILES || split) {
         // 128 x 256 tiles: fewer operand bytes per product, when there are
         // enough of them for every CU
         constexpr int lds = RgCfg<256>::LDS;
         (void)hipFuncSetAttribute((const void *)pf_gemm_ring<DOWN, ADD, SWIGLU, 256>,
                                   hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-        hipLaunchKernelGGL((pf_gemm_ring<DOWN, ADD, SWIGLU, 256>), dim3((N + 255) / 256, (T + 127) / 128), dim3(512), lds,
-                           s, st, blk, grid, F, Ah, Al, lda, T, K, N, out, ldo, oh, ol, dmap, zsrc);
+        hipLaunchKernelGGL((pf_gemm_ring<DOWN, ADD, SWIGLU, 256>), dim3((N + 255) / 256, (T + 127) / 128, split ? 2 : 1),
+                           dim3(512), lds, s, st, blk, grid, F, Ah, Al, lda, T, K, N, out, ldo, oh, ol, dmap, zsrc,
+                           part);
+        if (split)
+            hipLaunchKernelGGL(pf_add_part, dim3((N + 255) / 256, T), dim3(256), 0, s, out, ldo, (const float *)part, N);
     } else {
         constexpr int lds = RgCfg<128>::LDS;  // above the default dynamic limit
         (void)hipFuncSetAttribute((const void *)pf_gemm_ring<DOWN, ADD, SWIGLU, 128>,
                                   hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         hipLaunchKernelGGL((pf_gemm_ring<DOWN, ADD, SWIGLU, 128>), g, dim3(512), lds, s, st, blk, grid, F, Ah, Al, lda,
-                           T, K, N, out, ldo, oh, ol, dmap, zsrc);
+                           T, K, N, out, ldo, oh, ol, dmap, zsrc, part);
     }
 }
 
@@ -976,7 +1005,7 @@ extern "C" int mk_prefill_chunk(const MkParams *p, const MkPrefillBufs *b, int T
         hipLaunchKernelGGL(pf_norm_split, dim3(T), dim3(256), 0, s, b->X, p->g_attn + (size_t)l * H, H, p->eps, b->Ah,
                            b->Al, lda, round32(H));
         launch_gemm<false, false>(q8, s, p->st[ST_QKV], blk[ST_QKV], G, F, H, b->Ah, b->Al, lda, T, round32(H), nqkv,
-                                  b->Y, ldy, nullptr, nullptr, si, ST_QKV, b->dmap, p->packed);
+                                  b->Y, ldy, nullptr, nullptr, si, ST_QKV, b->dmap, p->packed, nullptr);
         const int nthr = (nh + nkv) * d / 2 + nkv * d;
         hipLaunchKernelGGL(pf_rope_kv, dim3((nthr + 255) / 256, T), dim3(256), 0, s, b->Y, ldy, pos0, p->rope, nh, nkv,
                            d, l, p->max_seq, kc, vc, b->Q);
@@ -988,7 +1017,7 @@ extern "C" int mk_prefill_chunk(const MkParams *p, const MkPrefillBufs *b, int T
 #undef MK_PF_ATTN
         }
         launch_gemm<false, true>(q8, s, p->st[ST_O], blk[ST_O], G, F, H, b->Ah, b->Al, lda, T, round32(nq), H, b->X, H,
-                                 nullptr, nullptr, si, ST_O, b->dmap, p->packed);
+                                 nullptr, nullptr, si, ST_O, b->dmap, p->packed, b->Q);
         // feed-forward half
         hipLaunchKernelGGL(pf_norm_split, dim3(T), dim3(256), 0, s, b->X, p->g_ffn + (size_t)l * H, H, p->eps, b->Ah,
                            b->Al, lda, round32(H));
@@ -998,10 +1027,10 @@ extern "C" int mk_prefill_chunk(const MkParams *p, const MkPrefillBufs *b, int T
         const int ldf = round32(F);
         uint16_t *Fh = (uint16_t *)b->Y, *Fl = Fh + (size_t)T * ldf;
         launch_gemm<false, false, true>(q8, s, p->st[ST_GU], blk[ST_GU], G, F, H, b->Ah, b->Al, lda, T, round32(H),
-                                        2 * F, nullptr, ldf, Fh, Fl, si, ST_GU, b->dmap, p->packed);
+                                        2 * F, nullptr, ldf, Fh, Fl, si, ST_GU, b->dmap, p->packed, nullptr);
         if (ldf != F) hipLaunchKernelGGL(pf_zero_cols, dim3(T), dim3(64), 0, s, Fh, Fl, ldf, F, ldf);
         launch_gemm<true, true>(q8, s, p->st[ST_DOWN], blk[ST_DOWN], G, F, H, Fh, Fl, ldf, T, ldf, H, b->X, H, nullptr,
-                                nullptr, si, ST_DOWN, b->dmap, p->packed);
+                                nullptr, si, ST_DOWN, b->dmap, p->packed, b->Q);
     }
     return (int)hipGetLastError();
 }
