@@ -737,10 +737,9 @@ __device__ __forceinline__ void rows_pair(uint32_t x, uint32_t y, uint32_t &firs
 //   O^T += V^T P^T (V exact, P split into hi + lo): P reaches the operand
 //   layout (8 consecutive positions per lane) through two lane swaps per
 //   register pair, not through LDS.
-// The running max starts at a finite floor, so exp2(-inf - max) is 0 for
-// masked scores and the first block's rescaling factor is 0, with no
-// special cases; rows past the chunk's last token attend everything and
-// are never written.  The result o / l goes to the split operand.
+// Masked scores are -inf, so exp2 makes them 0; rows past the chunk's last
+// token attend everything and are never written.  The result o / l goes to
+// the split operand.
 template <int D, int GQ, int RB>
 __global__ __launch_bounds__(256) void pf_attn_mfma(const float *Q, const uint16_t *kc, const uint16_t *vc, int layer,
                                                     int nh, int nkv, int max_seq, int pos0, int T, uint16_t *Ah,
@@ -783,7 +782,7 @@ __global__ __launch_bounds__(256) void pf_attn_mfma(const float *Q, const uint16
             ql[r][k] = u4v{lw[0], lw[1], lw[2], lw[3]};
         }
         plast[r] = tv ? pos0 + t : 0x7FFFFFFF;
-        mrun[r] = -1e30f;
+        mrun[r] = 0.f;  // set by the first block
         lrun[r] = 0.f;
 #pragma unroll
         for (int n = 0; n < NT; ++n) o[r][n] = f4v{0.f, 0.f, 0.f, 0.f};
@@ -792,18 +791,28 @@ __global__ __launch_bounds__(256) void pf_attn_mfma(const float *Q, const uint16
     const int n_pos = pos0 + t_last + 1;  // positions the workgroup needs
     const uint16_t *kbase = kc + ((size_t)layer * nkv + j) * max_seq * D;
     const uint16_t *vbase = vc + ((size_t)layer * nkv + j) * max_seq * D;
-    // K piece i of a block: row i / (D / 8), 16-byte column i % (D / 8); V
-    // piece i: row i % BP (neighbouring threads take neighbouring
-    // positions, so the transposed LDS stores spread over the banks)
+    // K piece i of a block: row i / (D / 8), 16-byte column i % (D / 8).  V
+    // pieces 2 u and 2 u + 1 of a thread: positions 2 pp and 2 pp + 1 of
+    // the same 16-byte column vcp (pair i = tid + 256 u: pp = i % 32, vcp =
+    // i / 32), so that each transposed LDS word holds two neighbouring
+    // positions of one dimension (32 lanes write 32 neighbouring words)
     u4v kr[PPT], vr[PPT];
     auto fetch = [&](int p0) {
         const int nb = min(BP, n_pos - p0);
 #pragma unroll
         for (int u = 0; u < PPT; ++u) {
             const int i = tid + 256 * u;
-            const int krow = i / (D / 8), kcp = i % (D / 8), vrow = i % BP, vcp = i / BP;
+            const int krow = i / (D / 8), kcp = i % (D / 8);
             kr[u] = krow < nb ? *(const u4v *)(kbase + (size_t)(p0 + krow) * D + 8 * kcp) : u4v{0u, 0u, 0u, 0u};
-            vr[u] = vrow < nb ? *(const u4v *)(vbase + (size_t)(p0 + vrow) * D + 8 * vcp) : u4v{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < PPT / 2; ++u) {
+            const int i = tid + 256 * u, pp = i % (BP / 2), vcp = i / (BP / 2);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int vrow = 2 * pp + h;
+                vr[2 * u + h] = vrow < nb ? *(const u4v *)(vbase + (size_t)(p0 + vrow) * D + 8 * vcp) : u4v{0u, 0u, 0u, 0u};
+            }
         }
     };
     fetch(0);
@@ -813,21 +822,32 @@ __global__ __launch_bounds__(256) void pf_attn_mfma(const float *Q, const uint16
         for (int u = 0; u < PPT; ++u) {
             const int i = tid + 256 * u;
             *(u4v *)(ks + (i / (D / 8)) * LK + 8 * (i % (D / 8))) = kr[u];
-            const int vrow = i % BP, vcp = i / BP;
-            const uint32_t w4[4] = {vr[u].x, vr[u].y, vr[u].z, vr[u].w};
+        }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) vt[(8 * vcp + e) * LV + vrow] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
+        for (int u = 0; u < PPT / 2; ++u) {
+            const int i = tid + 256 * u, pp = i % (BP / 2), vcp = i / (BP / 2);
+            const uint32_t a4[4] = {vr[2 * u].x, vr[2 * u].y, vr[2 * u].z, vr[2 * u].w};
+            const uint32_t b4[4] = {vr[2 * u + 1].x, vr[2 * u + 1].y, vr[2 * u + 1].z, vr[2 * u + 1].w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                // dimension 8 vcp + e at positions 2 pp (low half) and 2 pp + 1
+                const uint32_t lo = (a4[e >> 1] >> (16 * (e & 1))) & 0xFFFFu, hi = (b4[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                *(uint32_t *)(vt + (8 * vcp + e) * LV + 2 * pp) = lo | (hi << 16);
+            }
         }
         __syncthreads();
         if (p0 + BP < n_pos) fetch(p0 + BP);
         const bool diag = p0 + BP - 1 > pos0 + t_base;  // uniform
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
-            // S^T: four 16-position tiles; lane: positions 16 nt + 4 kg + i of row r16
+            // S^T - m: four 16-position tiles; lane: positions 16 nt + 4 kg + i
+            // of row r16 (the accumulators start at minus the row's running
+            // max, so the products land already shifted for exp2)
             f4v sc[4];
+            const float nm = -mrun[r];
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) {
-                sc[nt] = f4v{0.f, 0.f, 0.f, 0.f};
+                sc[nt] = f4v{nm, nm, nm, nm};
 #pragma unroll
                 for (int k = 0; k < KS; ++k) {
                     const u4v ak = *(const u4v *)(ks + (nt * 16 + r16) * LK + 32 * k + 8 * kg);
@@ -844,14 +864,31 @@ __global__ __launch_bounds__(256) void pf_attn_mfma(const float *Q, const uint16
                     for (int i = 0; i < 4; ++i)
                         if (p0 + nt * 16 + 4 * kg + i > plast[r]) sc[nt][i] = -INFINITY;
             }
+            // Lazy rescaling: the reference m moves only when a row's block
+            // max passes it by more than 8 (log2 units), so P stays at most
+            // 2^8; o / l is unchanged, and most blocks skip the rescaling
+            // (a wave-uniform branch).  The first block sets m to its max
+            // (every row has an unmasked position there: position 0), with
+            // o and l still 0; later a fully masked row (-inf) keeps its m.
             float mx = sc[0][0];
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[nt][i]);
-            const float mn = fmaxf(mrun[r], cross4_max(mx));
-            const float alpha = __builtin_amdgcn_exp2f(mrun[r] - mn);
-            mrun[r] = mn;
+            const float bm = cross4_max(mx);  // block max minus m
+            const bool first = p0 == 0;       // uniform
+            if (first || __builtin_amdgcn_ballot_w64(bm > 8.0f) != 0) {
+                const float dm = first ? bm : fmaxf(bm, 0.f);  // m's move (0 for rows that keep theirs)
+                const float alpha = first ? 0.f : __builtin_amdgcn_exp2f(-dm);
+                mrun[r] += dm;
+                lrun[r] *= alpha;
+#pragma unroll
+                for (int n = 0; n < NT; ++n) o[r][n] *= alpha;
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) sc[nt][i] -= dm;
+            }
             float lsum = 0.f;
             uint32_t ph[4][2], pl[4][2];  // P of each tile as bf16 hi / lo pairs (positions 4 kg + 0,1 and 2,3)
 #pragma unroll
@@ -859,15 +896,13 @@ __global__ __launch_bounds__(256) void pf_attn_mfma(const float *Q, const uint16
                 float pe[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    pe[i] = __builtin_amdgcn_exp2f(sc[nt][i] - mn);
+                    pe[i] = __builtin_amdgcn_exp2f(sc[nt][i]);
                     lsum += pe[i];
                 }
                 split2(pe[0], pe[1], ph[nt][0], pl[nt][0]);
                 split2(pe[2], pe[3], ph[nt][1], pl[nt][1]);
             }
-            lrun[r] = lrun[r] * alpha + lsum;
-#pragma unroll
-            for (int n = 0; n < NT; ++n) o[r][n] *= alpha;
+            lrun[r] += lsum;
             // O^T += V^T P^T: two 32-position k-steps (tiles 2 k2, 2 k2 + 1)
 #pragma unroll
             for (int k2 = 0; k2 < 2; ++k2) {
