@@ -217,181 +217,15 @@ __device__ __forceinline__ void gemm_store(const f4v (&acc)[4][4], int m0, int n
 // v_mfma_f32_16x16x32_bf16 operand layout (wave64): A[m][k] in lane
 // m + 16 * (k / 8), element k % 8; B[k][n] in lane n + 16 * (k / 8); the
 // result C[m][n] in lane n + 16 * (m / 4), element m % 4.
-// Workgroup tile: 128 tokens x 128 outputs; its 4 waves in 2 x 2, each
-// 64 x 64 (4 x 4 blocks).  Per k-tile of 64 the operands are staged in LDS
-// -- A hi, A lo and B as [row][k], rows padded to 72 elements (144 bytes)
-// so that the 16 rows one ds_read_b128 instruction touches fall in
-// different banks -- and every wave reads its fragments from there: each A
-// row is fetched from memory once for 128 outputs, each weight row once for
-// 128 tokens.  The next k-tile's global loads are issued into registers
-// before the current tile's products.
-// B is read in units of 8 consecutive inputs of one row: 16 bytes of bf16,
+// B is taken in units of 8 consecutive inputs of one row: 16 bytes of bf16,
 // or 8 int8 codes widened to bf16 (exact); Q8 multiplies each output
 // column's sum by its row's scale.  Rows at or past N, tokens at or past T
 // and inputs at or past K (a multiple of 32) enter as zeros.
-template <bool DOWN, bool ADD, bool Q8, bool SWIGLU>
-__global__ __launch_bounds__(256) void pf_gemm(const MkStage st, const unsigned char *layer_block, int grid, int F,
-                                               int H, const uint16_t *Ah, const uint16_t *Al, int lda, int T, int K,
-                                               int N, float *out, int ldo, uint16_t *oh, uint16_t *ol,
-                                               const ScaleIdx si, int kind, const int32_t *dmap) {
-    constexpr int EB = Q8 ? 1 : 2;
-    constexpr int BM = 128, BN = 128, BK = 64, LDK = BK + 8;
-    __shared__ __attribute__((aligned(16))) uint16_t sah[BM * LDK], sal[BM * LDK], sb[BN * LDK];
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int wm = wv >> 1, wn = wv & 1;
-    const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
-    const int r16 = lane & 15, kg = lane >> 4;
-    const u4v zero = u4v{0u, 0u, 0u, 0u};
-    // Staging: piece j (0..3) of this thread.  A: row (tid >> 3) + 32 j,
-    // inputs 8 (tid & 7) .. +7 of the k-tile.  B, row-split stages: the same
-    // (8 threads read one row's 64 inputs, contiguous in its chunk); B, down
-    // stage: output row tid & 127, input blocks (tid >> 7) + 2 j, so that
-    // neighbouring threads read neighbouring rows' pieces.
-    const int arow = tid >> 3, apart = tid & 7;
-    const uint16_t *pah[4], *pal[4];
-    bool am[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int m = m0 + arow + 32 * j;
-        am[j] = m < T;
-        pah[j] = Ah + (size_t)(am[j] ? m : 0) * lda + 8 * apart;
-        pal[j] = Al + (size_t)(am[j] ? m : 0) * lda + 8 * apart;
-    }
-    // int8 rows of the row-split stages: 16 codes per load, row
-    // (tid >> 2) + 64 j (j < 2), inputs 16 (tid & 3) .. +15 of the k-tile
-    constexpr bool WIDE = Q8 && !DOWN;
-    constexpr int NBR = WIDE ? 2 : 4;  // B loads per thread and k-tile
-    const int brow = WIDE ? tid >> 2 : arow, bstep = WIDE ? 64 : 32, bpart = WIDE ? tid & 3 : apart;
-    RowLoc rl[NBR];
-    bool bn[4];
-    const int dn = n0 + (tid & 127), dfb = tid >> 7;
-    if constexpr (!DOWN) {
-#pragma unroll
-        for (int j = 0; j < NBR; ++j) {
-            const int n = n0 + brow + bstep * j;
-            bn[j] = n < N;
-            rl[j] = row_loc(st, layer_block, grid, bn[j] ? n : 0, EB);
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) bn[j] = dn < N;
-    }
-    // eight int8 codes -> eight bf16 values (exact)
-    auto widen8 = [](uint32_t lo, uint32_t hi) -> u4v {
-        uint32_t w[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t src = i < 2 ? lo : hi;
-            const int b0 = (i & 1) * 2;
-            const uint32_t e0 = __float_as_uint((float)((int32_t)(src << (24 - 8 * b0)) >> 24)) >> 16;
-            const uint32_t e1 = __float_as_uint((float)((int32_t)(src << (16 - 8 * b0)) >> 24)) >> 16;
-            w[i] = e0 | (e1 << 16);
-        }
-        return u4v{w[0], w[1], w[2], w[3]};
-    };
-    // B loads keep their raw bytes (bf16 pieces, or 8 / 16 int8 codes) until
-    // the tile is staged: widening at the load would make the next tile's
-    // loads complete before the current tile's products.
-    // down stage: the map entries of the next fetch's input blocks, read one
-    // k-tile ahead so that no fetch waits for its own lookups
-    int4 dme[4];
-    auto dmap_read = [&](int kb) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int f = kb + 8 * (dfb + 2 * j);
-            dme[j] = f < F ? *(const int4 *)(dmap + 4 * (f >> 3)) : int4{0, 0, 0, 0};
-        }
-    };
-    u4v rah[4], ral[4], rb[NBR];
-    auto fetch = [&](int kb) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const bool kin = kb + 8 * apart < K;
-            rah[j] = am[j] && kin ? *(const u4v *)(pah[j] + kb) : zero;
-            ral[j] = am[j] && kin ? *(const u4v *)(pal[j] + kb) : zero;
-        }
-#pragma unroll
-        for (int j = 0; j < NBR; ++j) {
-            if constexpr (DOWN) {
-                const int f = kb + 8 * (dfb + 2 * j);
-                const unsigned char *q = down_piece(st, layer_block, dme[j], dn);
-                if constexpr (Q8) {
-                    const uint2 c = bn[j] && f < F ? *(const uint2 *)q : uint2{0u, 0u};
-                    rb[j] = u4v{c.x, c.y, 0u, 0u};
-                } else {
-                    rb[j] = bn[j] && f < F ? *(const u4v *)q : zero;
-                }
-            } else {
-                const int k = kb + (WIDE ? 16 : 8) * bpart;
-                rb[j] = bn[j] && k < K ? *(const u4v *)row_piece(rl[j], st.slot_stride, k, EB) : zero;
-            }
-        }
-        if constexpr (DOWN) dmap_read(kb + BK);
-    };
-    auto stage = [&]() {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = arow + 32 * j;
-            *(u4v *)(sah + r * LDK + 8 * apart) = rah[j];
-            *(u4v *)(sal + r * LDK + 8 * apart) = ral[j];
-        }
-#pragma unroll
-        for (int j = 0; j < NBR; ++j) {
-            if constexpr (DOWN) {
-                *(u4v *)(sb + (tid & 127) * LDK + 8 * (dfb + 2 * j)) = Q8 ? widen8(rb[j].x, rb[j].y) : rb[j];
-            } else if constexpr (WIDE) {
-                uint16_t *d = sb + (brow + bstep * j) * LDK + 16 * bpart;
-                *(u4v *)d = widen8(rb[j].x, rb[j].y);
-                *(u4v *)(d + 8) = widen8(rb[j].z, rb[j].w);
-            } else {
-                *(u4v *)(sb + (arow + 32 * j) * LDK + 8 * apart) = rb[j];
-            }
-        }
-    };
-    f4v acc[4][4];
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f4v{0.f, 0.f, 0.f, 0.f};
-    if constexpr (DOWN) dmap_read(0);
-    fetch(0);
-    for (int kb = 0; kb < K; kb += BK) {
-        __syncthreads();  // every wave has read the previous tile
-        stage();
-        __syncthreads();
-        if (kb + BK < K) fetch(kb + BK);
-#pragma unroll
-        for (int ks = 0; ks < BK / 32; ++ks) {
-            if (kb + 32 * ks >= K) break;  // uniform: a half tile at the end
-            u4v fh[4], fl[4], fb[4];
-#pragma unroll
-            for (int mb = 0; mb < 4; ++mb) {
-                const int r = wm * 64 + mb * 16 + r16;
-                fh[mb] = *(const u4v *)(sah + r * LDK + 32 * ks + 8 * kg);
-                fl[mb] = *(const u4v *)(sal + r * LDK + 32 * ks + 8 * kg);
-            }
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb)
-                fb[nb] = *(const u4v *)(sb + (wn * 64 + nb * 16 + r16) * LDK + 32 * ks + 8 * kg);
-#pragma unroll
-            for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-                for (int nb = 0; nb < 4; ++nb) {
-                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf8v, fh[mb]), __builtin_bit_cast(bf8v, fb[nb]), acc[mb][nb], 0, 0, 0);
-                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf8v, fl[mb]), __builtin_bit_cast(bf8v, fb[nb]), acc[mb][nb], 0, 0, 0);
-                }
-        }
-    }
-    gemm_store<ADD, Q8, SWIGLU>(acc, m0, n0, wm, wn, r16, kg, T, N, out, ldo, oh, ol, si, kind);
-}
 
-// ---- GEMM with a load ring (bf16 weights) ----------------------------------
-// The same products and epilogue as pf_gemm, organised like the decode
-// kernel: 8 waves, 4 of them loaders that stream 32-input steps of A hi, A
-// lo and B into a ring of LDS stages with direct-to-LDS loads, 4 of them
-// multiplying (2 x 2).  The loads run NST - 1 steps ahead of the products,
+// ---- GEMM with a load ring ---------------------------------------------------
+// Organised like the decode kernel: 8 waves, 4 of them loaders that stream
+// 32-input steps of A hi, A lo and B into a ring of LDS stages with
+// direct-to-LDS loads, 4 of them multiplying (2 x 2).  The loads run NST - 1 steps ahead of the products,
 // with one workgroup barrier per step, and no register holds an operand
 // between its load and its LDS copy.
 // Tile 128 tokens x BN outputs.  BN = 128: 6 stages of 24 KiB, waves of
@@ -404,22 +238,49 @@ __global__ __launch_bounds__(256) void pf_gemm(const MkStage st, const unsigned 
 // rows, the four 16-byte pieces of row r at position piece ^ rg_swz(r), so
 // that the 16 rows of one fragment read fall in distinct banks); the down
 // stage's B as [8-input block][row] (its piece columns, 64 rows of one block
-// contiguous in memory).  Rows past T or N and down inputs past F read a
-// zeroed 1 KiB (zsrc).
+// contiguous in memory).  INT8 weights (Q8) stay codes in LDS, half the B
+// bytes, widened when a fragment is read: row-split rows of 32 codes, their
+// two 16-code halves at position half ^ ((r >> 3) & 1) (8-byte reads of 16
+// rows in distinct banks); the down stage in 4-code words, [word][row], as
+// its slices are aligned to 8 inputs only.  Rows past T or N and down
+// inputs past F read a zeroed 1 KiB (zsrc).
 constexpr int RG_BK = 32;
 constexpr int RG_WIDE_MIN_TILES = 256;  // 128 x 256 tiles when they fill the 256 CUs once
 constexpr int RG_SEC = 128 * RG_BK * 2;  // A hi (or A lo) of one step: 128 rows of 64 bytes
-template <int BN>
+// Q8: B holds int8 codes (one byte per input), widened to bf16 when a
+// fragment is read.
+template <int BN, bool Q8, bool DOWN>
 struct RgCfg {
-    static constexpr int NST = BN == 128 ? 6 : 5;          // ring stages
-    static constexpr int SECB = BN * RG_BK * 2;            // B of one step
+    static constexpr int NST = BN == 256 && !Q8 ? 5 : 6;   // ring stages
+    static constexpr int SECB = BN * RG_BK * (Q8 ? 1 : 2); // B of one step
     static constexpr int STAGE = 2 * RG_SEC + SECB;
     static constexpr int LDS = NST * STAGE;
-    static constexpr int QB = BN / 64;                     // B loads per loader wave and step
+    // B loads per loader wave and step: bf16, 16 rows (row split) or 64
+    // rows of one 8-input block (down) per load; int8 row split, 32 rows of
+    // 32 codes per load; int8 down, 64 rows of one 4-code block per load
+    static constexpr int QB = !Q8 ? BN / 64 : DOWN ? BN / 32 : BN / 128;
     static constexpr int LOADS = 4 + QB;                   // direct-to-LDS loads per loader wave and step
     static constexpr int NB = BN / 32;                     // 16-output blocks per multiplying wave
 };
-static_assert(RgCfg<128>::LDS <= MK_LDS_LIMIT && RgCfg<256>::LDS <= MK_LDS_LIMIT, "ring fits the LDS");
+template <int BN, bool Q8, bool DOWN>
+constexpr bool rg_fits() {
+    typedef RgCfg<BN, Q8, DOWN> C;
+    return C::LDS <= MK_LDS_LIMIT && (C::NST - 2) <= 4 && (C::NST - 1) * C::LOADS < 64;
+}
+static_assert(rg_fits<128, false, false>() && rg_fits<128, false, true>() && rg_fits<256, false, false>() &&
+                  rg_fits<256, false, true>() && rg_fits<128, true, false>() && rg_fits<128, true, true>() &&
+                  rg_fits<256, true, false>() && rg_fits<256, true, true>(),
+              "each ring fits the LDS, its steady-state waits are covered and its loads stay within the counter");
+// eight int8 codes (two words, code e in byte e % 4 of word e / 4) -> eight
+// bf16 values in the operand layout (value e in half e % 2 of word e / 2);
+// exact: |code| <= 128
+__device__ __forceinline__ u4v rg_widen8(uint32_t lo, uint32_t hi) {
+    auto pair = [](uint32_t w, int b) -> uint32_t {
+        const float f0 = (float)(int8_t)(w >> (8 * b)), f1 = (float)(int8_t)(w >> (8 * b + 8));
+        return (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xFFFF0000u);
+    };
+    return u4v{pair(lo, 0), pair(lo, 2), pair(hi, 0), pair(hi, 2)};
+}
 __device__ __forceinline__ int rg_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 // s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt bits [3:0] and [15:14]; expcnt and
 // lgkmcnt left at their maxima)
@@ -427,7 +288,7 @@ template <int N>
 __device__ __forceinline__ void rg_wait_vm() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
 }
-// n a multiple of L up to 3 L; anything else waits for every load
+// n a multiple of L up to 4 L; anything else waits for every load
 template <int L>
 __device__ __forceinline__ void rg_wait_vm_rt(int n) {
     if (n == L) rg_wait_vm<L>();
@@ -436,18 +297,15 @@ __device__ __forceinline__ void rg_wait_vm_rt(int n) {
     else if (n == 4 * L) rg_wait_vm<4 * L>();
     else rg_wait_vm<0>();
 }
-static_assert((RgCfg<128>::NST - 2) * RgCfg<128>::LOADS <= 4 * RgCfg<128>::LOADS &&
-                  (RgCfg<256>::NST - 2) * RgCfg<256>::LOADS <= 4 * RgCfg<256>::LOADS &&
-                  4 * RgCfg<256>::LOADS < 64,
-              "the waits cover the steady-state counts within the counter");
 
-template <bool DOWN, bool ADD, bool SWIGLU, int BN>
+template <bool DOWN, bool ADD, bool SWIGLU, int BN, bool Q8>
 __global__ __launch_bounds__(512, 1) void pf_gemm_ring(const MkStage st, const unsigned char *layer_block, int grid,
                                                        int F, const uint16_t *Ah, const uint16_t *Al, int lda, int T,
                                                        int K, int N, float *out, int ldo, uint16_t *oh, uint16_t *ol,
                                                        const int32_t *__restrict__ dmap,
-                                                       const unsigned char *__restrict__ zsrc, float *part) {
-    typedef RgCfg<BN> C;
+                                                       const unsigned char *__restrict__ zsrc, float *part,
+                                                       const ScaleIdx si, int kind) {
+    typedef RgCfg<BN, Q8, DOWN> C;
     typedef __attribute__((address_space(3))) unsigned char lds_u8;
     extern __shared__ __attribute__((aligned(16))) unsigned char rg_smem[];
     lds_u8 *ring = (lds_u8 *)rg_smem;
@@ -481,16 +339,21 @@ __global__ __launch_bounds__(512, 1) void pf_gemm_ring(const MkStage st, const u
             pah[q] = m < T ? (const unsigned char *)(Ah + (size_t)m * lda + 8 * ja[q]) : nullptr;
             pal[q] = m < T ? (const unsigned char *)(Al + (size_t)m * lda + 8 * ja[q]) : nullptr;
         }
-        RowLoc rl[C::QB];
-        bool bok[C::QB];
-        int jb[C::QB];
+        // B rows of this lane, per load q: bf16 row split, row (BN/4) lw +
+        // 16 q + l / 4 and piece jb = (l % 4) ^ rg_swz(row); int8 row split,
+        // row (BN/4) lw + 32 q + l / 2 and 16-code half jb = (l % 2) ^
+        // ((row >> 3) & 1); down, row 64 (q % (BN/64)) + l
+        constexpr int NQ = DOWN ? BN / 64 : C::QB;
+        RowLoc rl[NQ];
+        bool bok[NQ];
+        int jb[NQ];
 #pragma unroll
-        for (int q = 0; q < C::QB; ++q) {
-            const int row = (BN / 4) * lw + 16 * q + (lane >> 2);
-            jb[q] = (lane & 3) ^ rg_swz(row);
+        for (int q = 0; q < NQ; ++q) {
+            const int row = Q8 ? (BN / 4) * lw + 32 * q + (lane >> 1) : (BN / 4) * lw + 16 * q + (lane >> 2);
+            jb[q] = Q8 ? (lane & 1) ^ ((row >> 3) & 1) : (lane & 3) ^ rg_swz(row);
             const int n = DOWN ? n0 + 64 * q + lane : n0 + row;
             bok[q] = n < N;
-            if constexpr (!DOWN) rl[q] = row_loc(st, layer_block, grid, bok[q] ? n : 0, 2);
+            if constexpr (!DOWN) rl[q] = row_loc(st, layer_block, grid, bok[q] ? n : 0, Q8 ? 1 : 2);
         }
         auto issue = [&](int s) {
             lds_u8 *base = ring + (s % C::NST) * C::STAGE;
@@ -503,7 +366,23 @@ __global__ __launch_bounds__(512, 1) void pf_gemm_ring(const MkStage st, const u
                 __builtin_amdgcn_global_load_lds((const void *)(pal[q] ? pal[q] + 2 * k0 : zl),
                                                  (__attribute__((address_space(3))) void *)(dst + RG_SEC), 16, 0, 0);
             }
-            if constexpr (DOWN) {
+            if constexpr (DOWN && Q8) {
+                // 4-code blocks 2 lw and 2 lw + 1 of the step (8-input block
+                // lw): LDS [4-code block][row], 4 bytes per row
+                const int f = k0 + 8 * lw;  // wave-uniform
+                const int4 e = f < F ? dmap4(dmap, f >> 3) : int4{0, 0, 0, 0};
+#pragma unroll
+                for (int h = 0; h < BN / 64; ++h) {
+                    const unsigned char *src = f < F && bok[h] ? down_piece(st, layer_block, e, n0 + 64 * h + lane) : zl;
+#pragma unroll
+                    for (int b = 0; b < 2; ++b)
+                        __builtin_amdgcn_global_load_lds(
+                            (const void *)(src == zl ? zl : src + 4 * b),
+                            (__attribute__((address_space(3))) void *)(base + 2 * RG_SEC + (2 * lw + b) * (BN * 4) +
+                                                                       h * 256),
+                            4, 0, 0);
+                }
+            } else if constexpr (DOWN) {
                 const int f = k0 + 8 * lw;  // this wave's block of the step (wave-uniform)
                 const int4 e = f < F ? dmap4(dmap, f >> 3) : int4{0, 0, 0, 0};
 #pragma unroll
@@ -513,6 +392,15 @@ __global__ __launch_bounds__(512, 1) void pf_gemm_ring(const MkStage st, const u
                         (const void *)src,
                         (__attribute__((address_space(3))) void *)(base + 2 * RG_SEC + lw * (BN * 16) + h * 1024), 16, 0,
                         0);
+                }
+            } else if constexpr (Q8) {
+#pragma unroll
+                for (int q = 0; q < C::QB; ++q) {
+                    const unsigned char *src = bok[q] ? row_piece(rl[q], st.slot_stride, k0 + 16 * jb[q], 1) : zl;
+                    __builtin_amdgcn_global_load_lds(
+                        (const void *)src,
+                        (__attribute__((address_space(3))) void *)(base + 2 * RG_SEC + ((BN / 4) * lw + 32 * q) * RG_BK),
+                        16, 0, 0);
                 }
             } else {
 #pragma unroll
@@ -558,8 +446,12 @@ __global__ __launch_bounds__(512, 1) void pf_gemm_ring(const MkStage st, const u
     }
 #pragma unroll
     for (int i = 0; i < C::NB; ++i) {
+        // B fragment of row rb, inputs 8 kg .. 8 kg + 7 of the step (int8
+        // down: the first of its two 4-code words; the second is BN * 4 on)
         const int rb = wn * (BN / 2) + i * 16 + r16;
-        boff[i] = 2 * RG_SEC + (DOWN ? kg * (BN * 16) + rb * 16 : rb * (RG_BK * 2) + ((kg ^ rg_swz(rb)) << 4));
+        if constexpr (Q8 && DOWN) boff[i] = 2 * RG_SEC + 2 * kg * (BN * 4) + rb * 4;
+        else if constexpr (Q8) boff[i] = 2 * RG_SEC + rb * RG_BK + ((((kg >> 1) ^ ((rb >> 3) & 1)) << 4) | ((kg & 1) << 3));
+        else boff[i] = 2 * RG_SEC + (DOWN ? kg * (BN * 16) + rb * 16 : rb * (RG_BK * 2) + ((kg ^ rg_swz(rb)) << 4));
     }
     f4v acc[4][C::NB];
 #pragma unroll
@@ -581,7 +473,17 @@ __global__ __launch_bounds__(512, 1) void pf_gemm_ring(const MkStage st, const u
             fl[x][i] = *(const __attribute__((address_space(3))) u4v *)(base + RG_SEC + aoff[i]);
         }
 #pragma unroll
-        for (int i = 0; i < C::NB; ++i) fb[x][i] = *(const __attribute__((address_space(3))) u4v *)(base + boff[i]);
+        for (int i = 0; i < C::NB; ++i) {
+            if constexpr (Q8 && DOWN)
+                fb[x][i] = rg_widen8(*(const __attribute__((address_space(3))) uint32_t *)(base + boff[i]),
+                                     *(const __attribute__((address_space(3))) uint32_t *)(base + boff[i] + BN * 4));
+            else if constexpr (Q8) {
+                typedef uint32_t u2v __attribute__((ext_vector_type(2)));
+                const u2v c = *(const __attribute__((address_space(3))) u2v *)(base + boff[i]);
+                fb[x][i] = rg_widen8(c.x, c.y);
+            } else
+                fb[x][i] = *(const __attribute__((address_space(3))) u4v *)(base + boff[i]);
+        }
     };
     auto products = [&](int x) {
 #pragma unroll
@@ -625,7 +527,6 @@ __global__ __launch_bounds__(512, 1) void pf_gemm_ring(const MkStage st, const u
             products(0);
         }
     }
-    const ScaleIdx none = {nullptr, 0, 1, 0, 0, 0};
 #pragma unroll
     for (int h = 0; h < C::NB / 4; ++h) {
         f4v sub[4][4];
@@ -635,11 +536,11 @@ __global__ __launch_bounds__(512, 1) void pf_gemm_ring(const MkStage st, const u
             for (int nb = 0; nb < 4; ++nb) sub[mb][nb] = acc[mb][4 * h + nb];
         // columns n0 + wn * BN/2 + 64 h + nb * 16 + r16
         if (kz == 0)
-            gemm_store<ADD, false, SWIGLU>(sub, m0, n0 + wn * (BN / 2) + 64 * h, wm, 0, r16, kg, T, N, out, ldo, oh, ol,
-                                           none, 0);
+            gemm_store<ADD, Q8, SWIGLU>(sub, m0, n0 + wn * (BN / 2) + 64 * h, wm, 0, r16, kg, T, N, out, ldo, oh, ol, si,
+                                        kind);
         else
-            gemm_store<false, false, false>(sub, m0, n0 + wn * (BN / 2) + 64 * h, wm, 0, r16, kg, T, N, part, N,
-                                            nullptr, nullptr, none, 0);
+            gemm_store<false, Q8, false>(sub, m0, n0 + wn * (BN / 2) + 64 * h, wm, 0, r16, kg, T, N, part, N, nullptr,
+                                         nullptr, si, kind);
     }
 }
 
@@ -979,12 +880,23 @@ int round32(int k) { return (k + 31) & ~31; }
 // per token; workgroups cover 128 tokens x 128 outputs.  SWIGLU: the
 // outputs are gate/up rows and the epilogue writes the down projection's
 // split operand (oh, ol with leading dimension ldo) instead of out.
+template <bool DOWN, bool ADD, bool SWIGLU, int BN, bool Q8>
+void launch_ring(hipStream_t s, dim3 g, const MkStage &st, const unsigned char *blk, int grid, int F,
+                 const uint16_t *Ah, const uint16_t *Al, int lda, int T, int K, int N, float *out, int ldo,
+                 uint16_t *oh, uint16_t *ol, const int32_t *dmap, const unsigned char *zsrc, float *part,
+                 const ScaleIdx &si, int kind) {
+    constexpr int lds = RgCfg<BN, Q8, DOWN>::LDS;  // above the default dynamic limit
+    (void)hipFuncSetAttribute((const void *)pf_gemm_ring<DOWN, ADD, SWIGLU, BN, Q8>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    hipLaunchKernelGGL((pf_gemm_ring<DOWN, ADD, SWIGLU, BN, Q8>), g, dim3(512), lds, s, st, blk, grid, F, Ah, Al, lda, T,
+                       K, N, out, ldo, oh, ol, dmap, zsrc, part, si, kind);
+}
+
 template <bool DOWN, bool ADD, bool SWIGLU = false>
-void launch_gemm(bool q8, hipStream_t s, const MkStage &st, const unsigned char *blk, int grid, int F, int H,
+void launch_gemm(bool q8, hipStream_t s, const MkStage &st, const unsigned char *blk, int grid, int F,
                  const uint16_t *Ah, const uint16_t *Al, int lda, int T, int K, int N, float *out, int ldo,
                  uint16_t *oh, uint16_t *ol, const ScaleIdx &si, int kind, const int32_t *dmap,
                  const unsigned char *zsrc, float *part) {
-    const dim3 g((N + 127) / 128, (T + 127) / 128);
     const int64_t wide = (int64_t)((N + 255) / 256) * ((T + 127) / 128);
     // An adding GEMM whose wide tiles fill half the chip and whose inputs
     // run long is split in two along the inputs (the 1B down projection):
@@ -992,26 +904,26 @@ void launch_gemm(bool q8, hipStream_t s, const MkStage &st, const unsigned char 
     // 2048 inputs (the 1B O projection) the halves are too short to pay for
     // the extra pass over the sums.
     const bool split = ADD && part && wide * 2 >= RG_WIDE_MIN_TILES && wide < RG_WIDE_MIN_TILES && K >= 4096;
-    if (q8) {
-        hipLaunchKernelGGL((pf_gemm<DOWN, ADD, true, SWIGLU>), g, dim3(256), 0, s, st, blk, grid, F, H, Ah, Al, lda, T, K,
-                           N, out, ldo, oh, ol, si, kind, dmap);
-    } else if (wide >= RG_WIDE_MIN_TILES || split) {
+    if (wide >= RG_WIDE_MIN_TILES || split) {
         // 128 x 256 tiles: fewer operand bytes per product, when there are
         // enough of them for every CU
-        constexpr int lds = RgCfg<256>::LDS;
-        (void)hipFuncSetAttribute((const void *)pf_gemm_ring<DOWN, ADD, SWIGLU, 256>,
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-        hipLaunchKernelGGL((pf_gemm_ring<DOWN, ADD, SWIGLU, 256>), dim3((N + 255) / 256, (T + 127) / 128, split ? 2 : 1),
-                           dim3(512), lds, s, st, blk, grid, F, Ah, Al, lda, T, K, N, out, ldo, oh, ol, dmap, zsrc,
-                           part);
+        const dim3 g((N + 255) / 256, (T + 127) / 128, split ? 2 : 1);
+        if (q8)
+            launch_ring<DOWN, ADD, SWIGLU, 256, true>(s, g, st, blk, grid, F, Ah, Al, lda, T, K, N, out, ldo, oh, ol, dmap,
+                                                      zsrc, part, si, kind);
+        else
+            launch_ring<DOWN, ADD, SWIGLU, 256, false>(s, g, st, blk, grid, F, Ah, Al, lda, T, K, N, out, ldo, oh, ol,
+                                                       dmap, zsrc, part, si, kind);
         if (split)
             hipLaunchKernelGGL(pf_add_part, dim3((N + 255) / 256, T), dim3(256), 0, s, out, ldo, (const float *)part, N);
     } else {
-        constexpr int lds = RgCfg<128>::LDS;  // above the default dynamic limit
-        (void)hipFuncSetAttribute((const void *)pf_gemm_ring<DOWN, ADD, SWIGLU, 128>,
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-        hipLaunchKernelGGL((pf_gemm_ring<DOWN, ADD, SWIGLU, 128>), g, dim3(512), lds, s, st, blk, grid, F, Ah, Al, lda,
-                           T, K, N, out, ldo, oh, ol, dmap, zsrc, part);
+        const dim3 g((N + 127) / 128, (T + 127) / 128);
+        if (q8)
+            launch_ring<DOWN, ADD, SWIGLU, 128, true>(s, g, st, blk, grid, F, Ah, Al, lda, T, K, N, out, ldo, oh, ol, dmap,
+                                                      zsrc, part, si, kind);
+        else
+            launch_ring<DOWN, ADD, SWIGLU, 128, false>(s, g, st, blk, grid, F, Ah, Al, lda, T, K, N, out, ldo, oh, ol,
+                                                       dmap, zsrc, part, si, kind);
     }
 }
 
@@ -1039,7 +951,7 @@ extern "C" int mk_prefill_chunk(const MkParams *p, const MkPrefillBufs *b, int T
         // attention half
         hipLaunchKernelGGL(pf_norm_split, dim3(T), dim3(256), 0, s, b->X, p->g_attn + (size_t)l * H, H, p->eps, b->Ah,
                            b->Al, lda, round32(H));
-        launch_gemm<false, false>(q8, s, p->st[ST_QKV], blk[ST_QKV], G, F, H, b->Ah, b->Al, lda, T, round32(H), nqkv,
+        launch_gemm<false, false>(q8, s, p->st[ST_QKV], blk[ST_QKV], G, F, b->Ah, b->Al, lda, T, round32(H), nqkv,
                                   b->Y, ldy, nullptr, nullptr, si, ST_QKV, b->dmap, p->packed, nullptr);
         const int nthr = (nh + nkv) * d / 2 + nkv * d;
         hipLaunchKernelGGL(pf_rope_kv, dim3((nthr + 255) / 256, T), dim3(256), 0, s, b->Y, ldy, pos0, p->rope, nh, nkv,
@@ -1051,7 +963,7 @@ extern "C" int mk_prefill_chunk(const MkParams *p, const MkPrefillBufs *b, int T
             MK_PF_ATTN(128, 1) MK_PF_ATTN(128, 2) MK_PF_ATTN(128, 4) MK_PF_ATTN(128, 8)
 #undef MK_PF_ATTN
         }
-        launch_gemm<false, true>(q8, s, p->st[ST_O], blk[ST_O], G, F, H, b->Ah, b->Al, lda, T, round32(nq), H, b->X, H,
+        launch_gemm<false, true>(q8, s, p->st[ST_O], blk[ST_O], G, F, b->Ah, b->Al, lda, T, round32(nq), H, b->X, H,
                                  nullptr, nullptr, si, ST_O, b->dmap, p->packed, b->Q);
         // feed-forward half
         hipLaunchKernelGGL(pf_norm_split, dim3(T), dim3(256), 0, s, b->X, p->g_ffn + (size_t)l * H, H, p->eps, b->Ah,
@@ -1061,10 +973,10 @@ extern "C" int mk_prefill_chunk(const MkParams *p, const MkPrefillBufs *b, int T
         // holds T x 2F floats, the operand 2 x T x round32(F) bf16 values)
         const int ldf = round32(F);
         uint16_t *Fh = (uint16_t *)b->Y, *Fl = Fh + (size_t)T * ldf;
-        launch_gemm<false, false, true>(q8, s, p->st[ST_GU], blk[ST_GU], G, F, H, b->Ah, b->Al, lda, T, round32(H),
+        launch_gemm<false, false, true>(q8, s, p->st[ST_GU], blk[ST_GU], G, F, b->Ah, b->Al, lda, T, round32(H),
                                         2 * F, nullptr, ldf, Fh, Fl, si, ST_GU, b->dmap, p->packed, nullptr);
         if (ldf != F) hipLaunchKernelGGL(pf_zero_cols, dim3(T), dim3(64), 0, s, Fh, Fl, ldf, F, ldf);
-        launch_gemm<true, true>(q8, s, p->st[ST_DOWN], blk[ST_DOWN], G, F, H, Fh, Fl, ldf, T, ldf, H, b->X, H, nullptr,
+        launch_gemm<true, true>(q8, s, p->st[ST_DOWN], blk[ST_DOWN], G, F, Fh, Fl, ldf, T, ldf, H, b->X, H, nullptr,
                                 nullptr, si, ST_DOWN, b->dmap, p->packed, b->Q);
     }
     return (int)hipGetLastError();
