@@ -37,6 +37,8 @@
 
 namespace {
 
+constexpr int MK_PF_MAX_H = 16384;  // widest hidden size of the batched prefill
+
 typedef __bf16 bf8v __attribute__((ext_vector_type(8)));
 typedef float f4v __attribute__((ext_vector_type(4)));
 typedef uint32_t u4v __attribute__((ext_vector_type(4)));
@@ -60,22 +62,46 @@ __global__ __launch_bounds__(256) void pf_embed(float *X, const int32_t *tok, co
 // ---- RMSNorm into the split operand ---------------------------------------
 // One workgroup per token: h = g * x / sqrt(mean(x^2) + eps), written as
 // bf16 hi and lo parts, zero-padded from H to kpad columns.
+// Thread tid takes groups of 4 consecutive elements, 4 tid + 1024 k (H a
+// multiple of 8, so a group is all inside or all past H; at most NI groups,
+// H <= 1024 NI), kept in registers between the sum of squares and the
+// stores of the hi and lo parts; the loads of x and g and the 8-byte stores
+// are contiguous across the lanes.
+template <int NI>
 __global__ __launch_bounds__(256) void pf_norm_split(const float *X, const float *g, int H, float eps,
                                                      uint16_t *Ah, uint16_t *Al, int lda, int kpad) {
     __shared__ float red[8];
     const int t = blockIdx.x, tid = threadIdx.x;
     const float *x = X + (size_t)t * H;
+    f4v v[NI];
     float ss = 0.f;
-    for (int i = tid; i < H; i += 256) ss = fmaf(x[i], x[i], ss);
+#pragma unroll
+    for (int k = 0; k < NI; ++k) {
+        const int i0 = 4 * tid + 1024 * k;
+        v[k] = i0 < H ? *(const f4v *)(x + i0) : f4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ss = fmaf(v[k][e], v[k][e], ss);
+    }
     for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
     if ((tid & 63) == 0) red[tid >> 6] = ss;
     __syncthreads();
     const float inv = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)H + eps);
-    for (int i = tid; i < kpad; i += 256) {
-        const float h = i < H ? g[i] * (x[i] * inv) : 0.f;
-        const uint16_t hi = f_to_bf(h);
-        Ah[(size_t)t * lda + i] = hi;
-        Al[(size_t)t * lda + i] = f_to_bf(h - bf_to_f(hi));
+    typedef uint32_t u2v __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int k = 0; k < NI; ++k) {
+        const int i0 = 4 * tid + 1024 * k;
+        if (i0 >= kpad) break;
+        const f4v gg = i0 < H ? *(const f4v *)(g + i0) : f4v{0.f, 0.f, 0.f, 0.f};
+        uint32_t hw[2], lw[2];
+#pragma unroll
+        for (int e = 0; e < 4; e += 2) {
+            const float a = gg[e] * (v[k][e] * inv), b = gg[e + 1] * (v[k][e + 1] * inv);
+            const uint16_t ha = f_to_bf(a), hb = f_to_bf(b);
+            hw[e / 2] = ha | ((uint32_t)hb << 16);
+            lw[e / 2] = f_to_bf(a - bf_to_f(ha)) | ((uint32_t)f_to_bf(b - bf_to_f(hb)) << 16);
+        }
+        *(u2v *)(Ah + (size_t)t * lda + i0) = u2v{hw[0], hw[1]};
+        *(u2v *)(Al + (size_t)t * lda + i0) = u2v{lw[0], lw[1]};
     }
 }
 
@@ -880,6 +906,21 @@ int round32(int k) { return (k + 31) & ~31; }
 // per token; workgroups cover 128 tokens x 128 outputs.  SWIGLU: the
 // outputs are gate/up rows and the epilogue writes the down projection's
 // split operand (oh, ol with leading dimension ldo) instead of out.
+// RMSNorm of T rows into the split operand, columns [0, round32(H)); H <=
+// MK_PF_MAX_H (mk_prefill_supported)
+void launch_norm_split(hipStream_t s, int T, const float *X, const float *g, int H, float eps, uint16_t *Ah,
+                       uint16_t *Al, int lda) {
+    const int kpad = round32(H), groups = (kpad + 1023) / 1024;
+    if (groups <= 2)
+        hipLaunchKernelGGL(pf_norm_split<2>, dim3(T), dim3(256), 0, s, X, g, H, eps, Ah, Al, lda, kpad);
+    else if (groups <= 4)
+        hipLaunchKernelGGL(pf_norm_split<4>, dim3(T), dim3(256), 0, s, X, g, H, eps, Ah, Al, lda, kpad);
+    else if (groups <= 8)
+        hipLaunchKernelGGL(pf_norm_split<8>, dim3(T), dim3(256), 0, s, X, g, H, eps, Ah, Al, lda, kpad);
+    else
+        hipLaunchKernelGGL(pf_norm_split<16>, dim3(T), dim3(256), 0, s, X, g, H, eps, Ah, Al, lda, kpad);
+}
+
 template <bool DOWN, bool ADD, bool SWIGLU, int BN, bool Q8>
 void launch_ring(hipStream_t s, dim3 g, const MkStage &st, const unsigned char *blk, int grid, int F,
                  const uint16_t *Ah, const uint16_t *Al, int lda, int T, int K, int N, float *out, int ldo,
@@ -949,8 +990,7 @@ extern "C" int mk_prefill_chunk(const MkParams *p, const MkPrefillBufs *b, int T
         for (int k = 0; k < ST_LM; ++k) blk[k] = p->packed + p->st[k].base + (int64_t)l * p->st[k].layer_stride;
         if (q8) si.blk = p->scl + (size_t)l * G * p->sc_blk;
         // attention half
-        hipLaunchKernelGGL(pf_norm_split, dim3(T), dim3(256), 0, s, b->X, p->g_attn + (size_t)l * H, H, p->eps, b->Ah,
-                           b->Al, lda, round32(H));
+        launch_norm_split(s, T, b->X, p->g_attn + (size_t)l * H, H, p->eps, b->Ah, b->Al, lda);
         launch_gemm<false, false>(q8, s, p->st[ST_QKV], blk[ST_QKV], G, F, b->Ah, b->Al, lda, T, round32(H), nqkv,
                                   b->Y, ldy, nullptr, nullptr, si, ST_QKV, b->dmap, p->packed, nullptr);
         const int nthr = (nh + nkv) * d / 2 + nkv * d;
@@ -966,8 +1006,7 @@ extern "C" int mk_prefill_chunk(const MkParams *p, const MkPrefillBufs *b, int T
         launch_gemm<false, true>(q8, s, p->st[ST_O], blk[ST_O], G, F, b->Ah, b->Al, lda, T, round32(nq), H, b->X, H,
                                  nullptr, nullptr, si, ST_O, b->dmap, p->packed, b->Q);
         // feed-forward half
-        hipLaunchKernelGGL(pf_norm_split, dim3(T), dim3(256), 0, s, b->X, p->g_ffn + (size_t)l * H, H, p->eps, b->Ah,
-                           b->Al, lda, round32(H));
+        launch_norm_split(s, T, b->X, p->g_ffn + (size_t)l * H, H, p->eps, b->Ah, b->Al, lda);
         // gate/up with SwiGLU in the epilogue: the down projection's split
         // operand goes to the Y buffer (free until the next layer's QKV; it
         // holds T x 2F floats, the operand 2 x T x round32(F) bf16 values)
@@ -983,12 +1022,14 @@ extern "C" int mk_prefill_chunk(const MkParams *p, const MkPrefillBufs *b, int T
 }
 
 // Whether the batched prefill applies to a handle's geometry: bf16 or INT8
-// weights (a bf16 cache), head_dim 64 or 128, FFN width 16 or more, and every down-stage
+// weights (a bf16 cache), head_dim 64 or 128, hidden at most MK_PF_MAX_H,
+// FFN width 16 or more, and every down-stage
 // workgroup's first input a multiple of 8 (8 consecutive inputs of a row, the
 // unit of a GEMM lane's B operand, then lie in one 16-byte piece of its piece
 // columns).
 extern "C" int mk_prefill_supported(const MkParams *p, int dtype) {
     if ((dtype != 1 && dtype != 2) || (p->d != 64 && p->d != 128)) return 0;
+    if (p->H > MK_PF_MAX_H) return 0;  // the RMSNorm split keeps a row in registers
     // the SwiGLU operand (2 x round32(F) bf16 values per token) lives in the
     // gate/up output buffer (2F floats per token)
     if (round32(p->F) > 2 * p->F) return 0;
