@@ -27,9 +27,10 @@
 // rows agree with it to within the bf16 rounding of the stored values.
 //
 // Weights are read in place from the decode kernel's packed layout (no
-// second copy of the model): a GEMM lane finds the 16-byte piece holding 8
-// consecutive inputs of a row from the row's owning workgroup, consumer and
-// stream position (mk_stream_pos, mk_down_geo).
+// second copy of the model): a GEMM loader lane finds the 16-byte piece
+// holding consecutive inputs of a row (8 bf16 values, 16 int8 codes; 4-code
+// words in the int8 down stage) from the row's owning workgroup, consumer
+// and stream position (mk_stream_pos, mk_down_geo).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
