@@ -60,6 +60,24 @@ def test_tiny_w8_batched_prefill(env, d):
     assert agree == 4
 
 
+@pytest.mark.parametrize("case", ["wide_ragged", "input_split"])
+def test_tiny_w8_batched_prefill_wide_and_split(env, case):
+    # The int8 codes on the GEMM's 128 x 256 tiles: ffn 2112 over 8
+    # workgroups (slices on multiples of 8), gate/up of 4224 outputs = 16.5
+    # wide tiles, a 2000-token chunk ending inside its 16th token tile.  Or
+    # the int8 down projection in two input splits: hidden 2048 (8 x 16 wide
+    # tiles), ffn 4096, a ragged 1930-token chunk.
+    if case == "wide_ragged":
+        cfg = W8_TINY.with_(n_heads=8, n_kv_heads=2, ffn=2112)
+        kw = dict(n_prompt=2000, tuning={"grid": 8, "attn_splits": 4})
+    else:
+        cfg = W8_TINY.with_(hidden=2048, n_heads=16, n_kv_heads=2, head_dim=128, ffn=4096, n_layers=1)
+        kw = dict(n_prompt=1930)
+    errs, agree = run_pair(env, cfg, seed=79, n_steps=3, expect_batched=True, **kw)
+    assert max(errs) <= 2e-2
+    assert agree == 3
+
+
 def test_tiny_w8_deferred_load(env):
     cfg = W8_TINY.with_(n_layers=3, n_heads=8, n_kv_heads=2)
     errs, agree = run_pair(env, cfg, seed=72, n_prompt=20, n_steps=4, deferred=True, expect_batched=False)
