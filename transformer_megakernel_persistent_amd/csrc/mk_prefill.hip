@@ -331,7 +331,7 @@ __global__ __launch_bounds__(512, 1) void pf_gemm_ring(const MkStage st, const u
                                                        int K, int N, float *out, int ldo, uint16_t *oh, uint16_t *ol,
                                                        const int32_t *__restrict__ dmap,
                                                        const unsigned char *__restrict__ zsrc, float *part,
-                                                       const ScaleIdx si, int kind) {
+                                                       int ldp, const ScaleIdx si, int kind) {
     typedef RgCfg<BN, Q8, DOWN> C;
     typedef __attribute__((address_space(3))) unsigned char lds_u8;
     extern __shared__ __attribute__((aligned(16))) unsigned char rg_smem[];
@@ -339,10 +339,11 @@ __global__ __launch_bounds__(512, 1) void pf_gemm_ring(const MkStage st, const u
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int m0 = blockIdx.y * 128, n0 = blockIdx.x * BN;
-    // Split along the inputs (gridDim.z = 2, ADD only): split 0 takes the
-    // first half of the steps and adds its sums to out as usual, split 1 the
-    // rest and stores its sums to part [T][N]; pf_add_part then adds part
-    // to out.  out + sums0 + sums1, in that order: deterministic.
+    // Split along the inputs (gridDim.z = 2): split 0 takes the first half
+    // of the steps and stores (or adds) its sums to out as usual, split 1
+    // the rest and stores its sums to part [T][ldp]; the sums of part are
+    // then added in by pf_add_part or by the kernel that reads out next.
+    // out (+ sums0) + sums1, in that order: deterministic.
     const int nall = K / RG_BK, kz = blockIdx.z;
     const int sbeg = kz ? nall / 2 : 0;
     const int nst = gridDim.z == 1 ? nall : kz ? nall - nall / 2 : nall / 2;
@@ -566,15 +567,15 @@ __global__ __launch_bounds__(512, 1) void pf_gemm_ring(const MkStage st, const u
             gemm_store<ADD, Q8, SWIGLU>(sub, m0, n0 + wn * (BN / 2) + 64 * h, wm, 0, r16, kg, T, N, out, ldo, oh, ol, si,
                                         kind);
         else
-            gemm_store<false, Q8, false>(sub, m0, n0 + wn * (BN / 2) + 64 * h, wm, 0, r16, kg, T, N, part, N, nullptr,
+            gemm_store<false, Q8, false>(sub, m0, n0 + wn * (BN / 2) + 64 * h, wm, 0, r16, kg, T, N, part, ldp, nullptr,
                                          nullptr, si, kind);
     }
 }
 
 // out[t][n] += part[t][n] (the second input split of a ring GEMM)
-__global__ __launch_bounds__(256) void pf_add_part(float *out, int ldo, const float *part, int N) {
+__global__ __launch_bounds__(256) void pf_add_part(float *out, int ldo, const float *part, int ldp, int N) {
     const int t = blockIdx.y, n = blockIdx.x * 256 + threadIdx.x;
-    if (n < N) out[(size_t)t * ldo + n] += part[(size_t)t * N + n];
+    if (n < N) out[(size_t)t * ldo + n] += part[(size_t)t * ldp + n];
 }
 
 // ---- rotary encoding and the cache rows of the chunk ------------------------
@@ -582,9 +583,11 @@ __global__ __launch_bounds__(256) void pf_add_part(float *out, int ldo, const fl
 // partners m and m + d/2 at packed rows 2m', 2m'+1, then value rows in
 // order).  Thread j of token t handles query/key pair j, or value element
 // j - (nh + nkv) * d / 2.
-__global__ __launch_bounds__(256) void pf_rope_kv(const float *Y, int ldy, int pos0, const float *rope, int nh,
-                                                  int nkv, int d, int layer, int max_seq, uint16_t *kc, uint16_t *vc,
-                                                  float *Q) {
+// poff > 0: the QKV GEMM ran as two input splits and left the second
+// one's sums at columns [poff, poff + nqkv) of Y, added here as Y is read.
+__global__ __launch_bounds__(256) void pf_rope_kv(const float *Y, int ldy, int poff, int pos0, const float *rope,
+                                                  int nh, int nkv, int d, int layer, int max_seq, uint16_t *kc,
+                                                  uint16_t *vc, float *Q) {
     const int t = blockIdx.y, j = blockIdx.x * 256 + threadIdx.x;
     const int npair = (nh + nkv) * d / 2, nv = nkv * d;
     if (j >= npair + nv) return;
@@ -596,7 +599,7 @@ __global__ __launch_bounds__(256) void pf_rope_kv(const float *Y, int ldy, int p
         const int r = isq ? gr : gr - nq;
         const int head = r / d, m = (r % d) / 2;
         const float c = rope[((size_t)pos * (d / 2) + m) * 2], s = rope[((size_t)pos * (d / 2) + m) * 2 + 1];
-        const float y0 = y[gr], y1 = y[gr + 1];
+        const float y0 = poff ? y[gr] + y[poff + gr] : y[gr], y1 = poff ? y[gr + 1] + y[poff + gr + 1] : y[gr + 1];
         const float a = y0 * c - y1 * s, b = y0 * s + y1 * c;
         if (isq) {
             Q[((size_t)t * nh + head) * d + m] = a;
@@ -609,7 +612,8 @@ __global__ __launch_bounds__(256) void pf_rope_kv(const float *Y, int ldy, int p
     } else {
         const int r = j - npair;
         const int head = r / d, e = r % d;
-        vc[(((size_t)layer * nkv + head) * max_seq + pos) * d + e] = f_to_bf(y[nq + nkv * d + r]);
+        const int cv = nq + nkv * d + r;
+        vc[(((size_t)layer * nkv + head) * max_seq + pos) * d + e] = f_to_bf(poff ? y[cv] + y[poff + cv] : y[cv]);
     }
 }
 
@@ -925,48 +929,61 @@ void launch_norm_split(hipStream_t s, int T, const float *X, const float *g, int
 template <bool DOWN, bool ADD, bool SWIGLU, int BN, bool Q8>
 void launch_ring(hipStream_t s, dim3 g, const MkStage &st, const unsigned char *blk, int grid, int F,
                  const uint16_t *Ah, const uint16_t *Al, int lda, int T, int K, int N, float *out, int ldo,
-                 uint16_t *oh, uint16_t *ol, const int32_t *dmap, const unsigned char *zsrc, float *part,
+                 uint16_t *oh, uint16_t *ol, const int32_t *dmap, const unsigned char *zsrc, float *part, int ldp,
                  const ScaleIdx &si, int kind) {
     constexpr int lds = RgCfg<BN, Q8, DOWN>::LDS;  // above the default dynamic limit
     (void)hipFuncSetAttribute((const void *)pf_gemm_ring<DOWN, ADD, SWIGLU, BN, Q8>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     hipLaunchKernelGGL((pf_gemm_ring<DOWN, ADD, SWIGLU, BN, Q8>), g, dim3(512), lds, s, st, blk, grid, F, Ah, Al, lda, T,
-                       K, N, out, ldo, oh, ol, dmap, zsrc, part, si, kind);
+                       K, N, out, ldo, oh, ol, dmap, zsrc, part, ldp, si, kind);
 }
 
+// Returns whether the GEMM ran as two input splits.  part (nullable) [T][ldp]
+// takes the second split's sums; with add_part they are added to out here,
+// else the caller adds them (the QKV sums, in the RoPE kernel).
 template <bool DOWN, bool ADD, bool SWIGLU = false>
-void launch_gemm(bool q8, hipStream_t s, const MkStage &st, const unsigned char *blk, int grid, int F,
+bool launch_gemm(bool q8, hipStream_t s, const MkStage &st, const unsigned char *blk, int grid, int F,
                  const uint16_t *Ah, const uint16_t *Al, int lda, int T, int K, int N, float *out, int ldo,
                  uint16_t *oh, uint16_t *ol, const ScaleIdx &si, int kind, const int32_t *dmap,
-                 const unsigned char *zsrc, float *part) {
-    const int64_t wide = (int64_t)((N + 255) / 256) * ((T + 127) / 128);
-    // An adding GEMM whose wide tiles fill half the chip and whose inputs
-    // run long is split in two along the inputs (the 1B down projection):
-    // twice the workgroups at a third fewer operand bytes per product.  At
-    // 2048 inputs (the 1B O projection) the halves are too short to pay for
-    // the extra pass over the sums.
-    const bool split = ADD && part && wide * 2 >= RG_WIDE_MIN_TILES && wide < RG_WIDE_MIN_TILES && K >= 4096;
-    if (wide >= RG_WIDE_MIN_TILES || split) {
+                 const unsigned char *zsrc, float *part, int ldp, bool add_part) {
+    const int mt = (T + 127) / 128;
+    const int64_t wide = (int64_t)((N + 255) / 256) * mt, narrow = (int64_t)((N + 127) / 128) * mt;
+    const bool use_wide = wide >= RG_WIDE_MIN_TILES;
+    const int64_t tiles = use_wide ? wide : narrow;
+    auto rounds = [](int64_t n) { return (n + RG_WIDE_MIN_TILES - 1) / RG_WIDE_MIN_TILES; };
+    // Two input splits (never for SwiGLU, whose epilogue needs whole sums):
+    // an adding GEMM whose wide tiles fill half the chip and whose inputs
+    // run long (the 1B down projection: twice the workgroups at a third
+    // fewer operand bytes per product; at 2048 inputs, the 1B O projection,
+    // the halves are too short to pay for the extra pass over the sums), or
+    // any GEMM whose last round of tiles would leave CUs idle where twice
+    // the tiles at half the length finish in fewer full-length rounds (384
+    // tiles: 2 rounds against 3 half rounds; the 1B and 8B QKV products).
+    const bool split_wide = ADD && wide * 2 >= RG_WIDE_MIN_TILES && wide < RG_WIDE_MIN_TILES && K >= 4096;
+    const bool split_tail = tiles > RG_WIDE_MIN_TILES && rounds(2 * tiles) < 2 * rounds(tiles) && K >= 2048;
+    const bool split = !SWIGLU && part && (split_wide || split_tail);
+    const bool wide_tiles = use_wide || split_wide;
+    const dim3 g(wide_tiles ? (N + 255) / 256 : (N + 127) / 128, mt, split ? 2 : 1);
+    if (wide_tiles) {
         // 128 x 256 tiles: fewer operand bytes per product, when there are
         // enough of them for every CU
-        const dim3 g((N + 255) / 256, (T + 127) / 128, split ? 2 : 1);
         if (q8)
             launch_ring<DOWN, ADD, SWIGLU, 256, true>(s, g, st, blk, grid, F, Ah, Al, lda, T, K, N, out, ldo, oh, ol, dmap,
-                                                      zsrc, part, si, kind);
+                                                      zsrc, part, ldp, si, kind);
         else
             launch_ring<DOWN, ADD, SWIGLU, 256, false>(s, g, st, blk, grid, F, Ah, Al, lda, T, K, N, out, ldo, oh, ol,
-                                                       dmap, zsrc, part, si, kind);
-        if (split)
-            hipLaunchKernelGGL(pf_add_part, dim3((N + 255) / 256, T), dim3(256), 0, s, out, ldo, (const float *)part, N);
+                                                       dmap, zsrc, part, ldp, si, kind);
     } else {
-        const dim3 g((N + 127) / 128, (T + 127) / 128);
         if (q8)
             launch_ring<DOWN, ADD, SWIGLU, 128, true>(s, g, st, blk, grid, F, Ah, Al, lda, T, K, N, out, ldo, oh, ol, dmap,
-                                                      zsrc, part, si, kind);
+                                                      zsrc, part, ldp, si, kind);
         else
             launch_ring<DOWN, ADD, SWIGLU, 128, false>(s, g, st, blk, grid, F, Ah, Al, lda, T, K, N, out, ldo, oh, ol,
-                                                       dmap, zsrc, part, si, kind);
+                                                       dmap, zsrc, part, ldp, si, kind);
     }
+    if (split && add_part)
+        hipLaunchKernelGGL(pf_add_part, dim3((N + 255) / 256, T), dim3(256), 0, s, out, ldo, (const float *)part, ldp, N);
+    return split;
 }
 
 }  // namespace
@@ -992,11 +1009,15 @@ extern "C" int mk_prefill_chunk(const MkParams *p, const MkPrefillBufs *b, int T
         if (q8) si.blk = p->scl + (size_t)l * G * p->sc_blk;
         // attention half
         launch_norm_split(s, T, b->X, p->g_attn + (size_t)l * H, H, p->eps, b->Ah, b->Al, lda);
-        launch_gemm<false, false>(q8, s, p->st[ST_QKV], blk[ST_QKV], G, F, b->Ah, b->Al, lda, T, round32(H), nqkv,
-                                  b->Y, ldy, nullptr, nullptr, si, ST_QKV, b->dmap, p->packed, nullptr);
+        // an input split of the QKV product leaves its second half's sums in
+        // Y's spare columns [nqkv, 2 nqkv), added by the RoPE kernel
+        float *qkv_part = 2 * nqkv <= ldy ? b->Y + nqkv : nullptr;
+        const bool qkv_split = launch_gemm<false, false>(q8, s, p->st[ST_QKV], blk[ST_QKV], G, F, b->Ah, b->Al, lda, T,
+                                                         round32(H), nqkv, b->Y, ldy, nullptr, nullptr, si, ST_QKV,
+                                                         b->dmap, p->packed, qkv_part, ldy, false);
         const int nthr = (nh + nkv) * d / 2 + nkv * d;
-        hipLaunchKernelGGL(pf_rope_kv, dim3((nthr + 255) / 256, T), dim3(256), 0, s, b->Y, ldy, pos0, p->rope, nh, nkv,
-                           d, l, p->max_seq, kc, vc, b->Q);
+        hipLaunchKernelGGL(pf_rope_kv, dim3((nthr + 255) / 256, T), dim3(256), 0, s, b->Y, ldy, qkv_split ? nqkv : 0,
+                           pos0, p->rope, nh, nkv, d, l, p->max_seq, kc, vc, b->Q);
         {
 #define MK_PF_ATTN(D_, GQ_) \
     if (d == D_ && gq == GQ_) launch_attn<D_, GQ_>(s, b->Q, kc, vc, l, nh, nkv, p->max_seq, pos0, T, b->Ah, b->Al, lda);
@@ -1005,7 +1026,7 @@ extern "C" int mk_prefill_chunk(const MkParams *p, const MkPrefillBufs *b, int T
 #undef MK_PF_ATTN
         }
         launch_gemm<false, true>(q8, s, p->st[ST_O], blk[ST_O], G, F, b->Ah, b->Al, lda, T, round32(nq), H, b->X, H,
-                                 nullptr, nullptr, si, ST_O, b->dmap, p->packed, b->Q);
+                                 nullptr, nullptr, si, ST_O, b->dmap, p->packed, b->Q, H, true);
         // feed-forward half
         launch_norm_split(s, T, b->X, p->g_ffn + (size_t)l * H, H, p->eps, b->Ah, b->Al, lda);
         // gate/up with SwiGLU in the epilogue: the down projection's split
@@ -1014,10 +1035,10 @@ extern "C" int mk_prefill_chunk(const MkParams *p, const MkPrefillBufs *b, int T
         const int ldf = round32(F);
         uint16_t *Fh = (uint16_t *)b->Y, *Fl = Fh + (size_t)T * ldf;
         launch_gemm<false, false, true>(q8, s, p->st[ST_GU], blk[ST_GU], G, F, b->Ah, b->Al, lda, T, round32(H),
-                                        2 * F, nullptr, ldf, Fh, Fl, si, ST_GU, b->dmap, p->packed, nullptr);
+                                        2 * F, nullptr, ldf, Fh, Fl, si, ST_GU, b->dmap, p->packed, nullptr, 0, false);
         if (ldf != F) hipLaunchKernelGGL(pf_zero_cols, dim3(T), dim3(64), 0, s, Fh, Fl, ldf, F, ldf);
         launch_gemm<true, true>(q8, s, p->st[ST_DOWN], blk[ST_DOWN], G, F, Fh, Fl, ldf, T, ldf, H, b->X, H, nullptr,
-                                nullptr, si, ST_DOWN, b->dmap, p->packed, b->Q);
+                                nullptr, si, ST_DOWN, b->dmap, p->packed, b->Q, H, true);
     }
     return (int)hipGetLastError();
 }
