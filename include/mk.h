@@ -160,9 +160,10 @@ typedef struct {
      prefill_chunk: tokens per chunk of the batched prefill, 1..4096
                   (default 2048, or max_seq if smaller); -1 = prefill by one
                   decode launch per position.  The batched prefill needs bf16
-                  or INT8 weights and a geometry whose down-stage workgroups
-                  own inputs starting at multiples of 8 (true of the Llama
-                  shapes at 256 workgroups); otherwise mk_prefill_kv uses
+                  or INT8 weights, a hidden size of at most 16384 and a
+                  geometry whose down-stage workgroups own inputs starting at
+                  multiples of 8 (true of the Llama shapes at 256
+                  workgroups); otherwise mk_prefill_kv uses
                   decode launches (mk_info.prefill_chunk reports which);
      slots_per_step: the tile of the weight and cache stream: 16 KiB ring
                   slots the consumer waves take per data step, between two
