@@ -627,19 +627,13 @@ __device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t 
     const bf2 l = {(__bf16)(a - __uint_as_float(hi << 16)), (__bf16)(b - __uint_as_float(hi & 0xFFFF0000u))};
     lo = __builtin_bit_cast(uint32_t, l);
 }
-// Max / sum over the four lanes l, l^16, l^32, l^48 (the gfx950 permlane
-// swaps exchange 16-lane rows 0<->1, 2<->3 and 0<->2, 1<->3).
+// Max over the four lanes l, l^16, l^32, l^48 (the gfx950 permlane swaps
+// exchange 16-lane rows 0<->1, 2<->3 and 0<->2, 1<->3).
 __device__ __forceinline__ float cross4_max(float v) {
     auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
     v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
     r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float cross4_sum(float v) {
-    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-    r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 // Rows g of x (tile a) and y (tile b), 16 lanes each, rearranged so that
 // row 0 holds (x.row0, x.row1), row 1 (x.row2, x.row3), row 2 (y.row0,
@@ -685,7 +679,9 @@ __global__ __launch_bounds__(256) void pf_attn_mfma(const float *Q, const uint16
     // (lanes l % 16) fall in different banks
     constexpr int LK = D + 8, LV = BP + 8;
     __shared__ __attribute__((aligned(16))) uint16_t ks[BP * LK];  // [pos][dim]
-    __shared__ __attribute__((aligned(16))) uint16_t vt[D * LV];   // [dim][pos]
+    // [dim][pos], then 16 rows of ones: the products with them are the row
+    // sums of P (output tile NT), from the same hi + lo parts as o
+    __shared__ __attribute__((aligned(16))) uint16_t vt[(D + 16) * LV];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     // One-dimensional grid, KV head fastest: workgroup w runs on XCD w mod 8,
     // so with 8 KV heads each head's K/V stream stays in one XCD's L2; the
@@ -697,8 +693,8 @@ __global__ __launch_bounds__(256) void pf_attn_mfma(const float *Q, const uint16
     // query row of this lane in row block r: m = 16 (wv RB + r) + r16
     u4v qh[RB][KS], ql[RB][KS];
     int plast[RB];
-    float mrun[RB], lrun[RB];  // lrun: this lane's share of the row sum
-    f4v o[RB][NT];
+    float mrun[RB];
+    f4v o[RB][NT + 1];  // tile NT: the row sum of P
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
         const int m = (wv * RB + r) * 16 + r16, t = t_base + m / GQ, g = m % GQ;
@@ -715,10 +711,10 @@ __global__ __launch_bounds__(256) void pf_attn_mfma(const float *Q, const uint16
         }
         plast[r] = tv ? pos0 + t : 0x7FFFFFFF;
         mrun[r] = 0.f;  // set by the first block
-        lrun[r] = 0.f;
 #pragma unroll
-        for (int n = 0; n < NT; ++n) o[r][n] = f4v{0.f, 0.f, 0.f, 0.f};
+        for (int n = 0; n <= NT; ++n) o[r][n] = f4v{0.f, 0.f, 0.f, 0.f};
     }
+    for (int i = tid; i < 16 * LV; i += 256) vt[D * LV + i] = 0x3F80;  // bf16 1.0 (the staging never writes these rows)
     const int t_last = min(T, t_base + QB) - 1;
     const int n_pos = pos0 + t_last + 1;  // positions the workgroup needs
     const uint16_t *kbase = kc + ((size_t)layer * nkv + j) * max_seq * D;
@@ -813,28 +809,22 @@ __global__ __launch_bounds__(256) void pf_attn_mfma(const float *Q, const uint16
                 const float dm = first ? bm : fmaxf(bm, 0.f);  // m's move (0 for rows that keep theirs)
                 const float alpha = first ? 0.f : __builtin_amdgcn_exp2f(-dm);
                 mrun[r] += dm;
-                lrun[r] *= alpha;
 #pragma unroll
-                for (int n = 0; n < NT; ++n) o[r][n] *= alpha;
+                for (int n = 0; n <= NT; ++n) o[r][n] *= alpha;
 #pragma unroll
                 for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) sc[nt][i] -= dm;
             }
-            float lsum = 0.f;
             uint32_t ph[4][2], pl[4][2];  // P of each tile as bf16 hi / lo pairs (positions 4 kg + 0,1 and 2,3)
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) {
                 float pe[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    pe[i] = __builtin_amdgcn_exp2f(sc[nt][i]);
-                    lsum += pe[i];
-                }
+                for (int i = 0; i < 4; ++i) pe[i] = __builtin_amdgcn_exp2f(sc[nt][i]);
                 split2(pe[0], pe[1], ph[nt][0], pl[nt][0]);
                 split2(pe[2], pe[3], ph[nt][1], pl[nt][1]);
             }
-            lrun[r] += lsum;
             // O^T += V^T P^T: two 32-position k-steps (tiles 2 k2, 2 k2 + 1)
 #pragma unroll
             for (int k2 = 0; k2 < 2; ++k2) {
@@ -845,7 +835,7 @@ __global__ __launch_bounds__(256) void pf_attn_mfma(const float *Q, const uint16
                 rows_pair(pl[2 * k2][1], pl[2 * k2 + 1][1], bl[1], bl[3]);
                 const u4v bph = u4v{bh[0], bh[1], bh[2], bh[3]}, bpl = u4v{bl[0], bl[1], bl[2], bl[3]};
 #pragma unroll
-                for (int n = 0; n < NT; ++n) {
+                for (int n = 0; n <= NT; ++n) {
                     const u4v av = *(const u4v *)(vt + (n * 16 + r16) * LV + 32 * k2 + 8 * kg);
                     o[r][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, av),
                                                                       __builtin_bit_cast(bf8v, bph), o[r][n], 0, 0, 0);
@@ -855,11 +845,11 @@ __global__ __launch_bounds__(256) void pf_attn_mfma(const float *Q, const uint16
             }
         }
     }
-    // row sums over the four lanes of a row, then o / l into the split
-    // operand: lane holds dims 16 n + 4 kg + i of its row
+    // o / l into the split operand: lane holds dims 16 n + 4 kg + i of its
+    // row, and the whole row sum in tile NT
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
-        const float l = cross4_sum(lrun[r]);
+        const float l = o[r][NT][0];
         const int m = (wv * RB + r) * 16 + r16, t = t_base + m / GQ, g = m % GQ;
         if (t >= T) continue;
         const float inv = 1.0f / l;
