@@ -300,7 +300,7 @@ def main():
     ap.add_argument("--stage-drain", action="store_true",
                     help="ablation: no loads for a stage before its grid dependency is met")
     ap.add_argument("--prefill-chunk", type=int, default=0,
-                    help="tokens per batched-prefill chunk (default 2048); -1: one decode launch per position")
+                    help="tokens per batched-prefill chunk (default 4096, or the context if smaller); -1: one decode launch per position")
     ap.add_argument("--slots-per-step", type=int, default=0,
                     help="16 KiB ring slots per data step, the stream's tile (default 1); a tunable")
     ap.add_argument("--attn-pm-slots", type=int, default=0,

@@ -158,7 +158,7 @@ typedef struct {
                   reads).  The page cloud.baidu.com/article/9434380 section
                   八 (question five) advises tiling by length;
      prefill_chunk: tokens per chunk of the batched prefill, 1..4096
-                  (default 2048, or max_seq if smaller); -1 = prefill by one
+                  (default 4096, or max_seq if smaller); -1 = prefill by one
                   decode launch per position.  The batched prefill needs bf16
                   or INT8 weights, a hidden size of at most 16384 and a
                   geometry whose down-stage workgroups own inputs starting at

@@ -424,9 +424,10 @@ static mk_status create_impl(const mk_model_desc *desc, const mk_tuning *tun, mk
     // batched prefill buffers, when the geometry allows it (bf16, aligned
     // down-stage inputs) and the tuning does not ask for decode launches
     if (t.prefill_chunk != -1 && mk_prefill_supported(&P, dtype)) {
-        // default: chunks of 2048 tokens (every GEMM then has 256 or more
-        // workgroups at the Llama shapes), or max_seq if shorter
-        const int T = t.prefill_chunk > 0 ? t.prefill_chunk : (D.max_seq < 2048 ? D.max_seq : 2048);
+        // default: chunks of 4096 tokens, or max_seq if smaller (a prompt of
+        // up to 4096 tokens in one chunk; longer prompts get twice the
+        // workgroups per launch of 2048-token chunks: 32K prefill 320 -> 309 ms)
+        const int T = t.prefill_chunk > 0 ? t.prefill_chunk : (D.max_seq < 4096 ? D.max_seq : 4096);
         auto r32 = [](int k) { return (k + 31) & ~31; };
         int kmax = H > nh * d ? H : nh * d;
         if (F > kmax) kmax = F;
