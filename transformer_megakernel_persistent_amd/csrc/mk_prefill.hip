@@ -302,9 +302,11 @@ static_assert(rg_fits<128, false, false>() && rg_fits<128, false, true>() && rg_
 // bf16 values in the operand layout (value e in half e % 2 of word e / 2);
 // exact: |code| <= 128
 __device__ __forceinline__ u4v rg_widen8(uint32_t lo, uint32_t hi) {
+    // the upper halves of the two floats, packed by one byte permute
+    // (bytes 2, 3 of f0 then bytes 2, 3 of f1)
     auto pair = [](uint32_t w, int b) -> uint32_t {
         const float f0 = (float)(int8_t)(w >> (8 * b)), f1 = (float)(int8_t)(w >> (8 * b + 8));
-        return (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xFFFF0000u);
+        return __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
     };
     return u4v{pair(lo, 0), pair(lo, 2), pair(hi, 0), pair(hi, 2)};
 }
