@@ -155,7 +155,7 @@ def prefill_record(cfg, n, seconds, info):
     flops = 2.0 * cfg.n_layers * per_layer * n + 4.0 * cfg.n_layers * cfg.q_dim * n * (n + 1) / 2
     tf = flops / seconds / 1e12
     rec = {"positions": n, "seconds": seconds, "tokens_per_s": n / seconds,
-           "mode": f"batched, chunks of {info['prefill_chunk']}" if info["prefill_chunk"] else "decode launches",
+           "mode": f"batched, chunks of up to {info['prefill_chunk']} positions" if info["prefill_chunk"] else "decode launches",
            "warmup": "one untimed 16-token prefill first" if info["prefill_chunk"] else "none",
            "roofline": None}
     if info["prefill_chunk"]:  # the matrix-core path; decode launches are the decode step's own roofline
