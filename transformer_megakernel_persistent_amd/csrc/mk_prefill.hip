@@ -185,8 +185,9 @@ __device__ __forceinline__ float row_scale(const ScaleIdx &si, int kind, int n) 
     return si.blk[(size_t)w * si.sc_blk + off];
 }
 
-// The epilogue of both GEMM kernels: wave (wm, wn)'s 64 x 64 block of
-// products in the v_mfma_f32_16x16x32_bf16 result layout (acc[mb][nb]
+// The GEMM epilogue, per 64 x 64 block of a wave's products (the 128 x 256
+// tiles' waves call it for each 64-column half) in the
+// v_mfma_f32_16x16x32_bf16 result layout (acc[mb][nb]
 // element i is C[m0 + wm*64 + mb*16 + 4*kg + i][n0 + wn*64 + nb*16 + r16]),
 // stored, added to out, or (SWIGLU) turned into the down projection's
 // operand.
@@ -658,13 +659,15 @@ __device__ __forceinline__ void rows_pair(uint32_t x, uint32_t y, uint32_t &firs
 //   log2(e) / sqrt(d), so that exp2 of a score is exp of the scaled score);
 //   in the result layout lane l holds positions 4 (l / 16) + i (i < 4) of
 //   each 16-position tile for the single query row l % 16, so a row's
-//   running max, sum and rescaling are one lane's, completed over the four
-//   lanes l % 16 + 16 k by two lane swaps.  Positions past each row's own
-//   are masked (only blocks that reach past the workgroup's first token
-//   need it); P = exp2(S - max);
-//   O^T += V^T P^T (V exact, P split into hi + lo): P reaches the operand
-//   layout (8 consecutive positions per lane) through two lane swaps per
-//   register pair, not through LDS.
+//   running max is one lane's, completed over the four lanes l % 16 + 16 k
+//   by two lane swaps.  Positions past each row's own are masked (only
+//   blocks that reach past the workgroup's first token need it); P =
+//   exp2(S - m) for a reference m that moves only when a block's max
+//   passes it by more than 8;
+//   O^T += V^T P^T (V exact, P split into hi + lo), with 16 rows of ones
+//   after V^T so that one more output tile holds the row sums of P: P
+//   reaches the operand layout (8 consecutive positions per lane) through
+//   two lane swaps per register pair, not through LDS.
 // Masked scores are -inf, so exp2 makes them 0; rows past the chunk's last
 // token attend everything and are never written.  The result o / l goes to
 // the split operand.
@@ -1037,10 +1040,9 @@ extern "C" int mk_prefill_chunk(const MkParams *p, const MkPrefillBufs *b, int T
 
 // Whether the batched prefill applies to a handle's geometry: bf16 or INT8
 // weights (a bf16 cache), head_dim 64 or 128, hidden at most MK_PF_MAX_H,
-// FFN width 16 or more, and every down-stage
-// workgroup's first input a multiple of 8 (8 consecutive inputs of a row, the
-// unit of a GEMM lane's B operand, then lie in one 16-byte piece of its piece
-// columns).
+// FFN width 16 or more, and every down-stage workgroup's first input a
+// multiple of 8 (8 consecutive inputs of a row, the unit a GEMM loader lane
+// fetches, then lie in one 16-byte piece of its piece columns).
 extern "C" int mk_prefill_supported(const MkParams *p, int dtype) {
     if ((dtype != 1 && dtype != 2) || (p->d != 64 && p->d != 128)) return 0;
     if (p->H > MK_PF_MAX_H) return 0;  // the RMSNorm split keeps a row in registers
