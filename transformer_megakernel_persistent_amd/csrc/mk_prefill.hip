@@ -638,21 +638,20 @@ __device__ __forceinline__ float cross4_max(float v) {
     r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-// Rows g of x (tile a) and y (tile b), 16 lanes each, rearranged so that
-// row 0 holds (x.row0, x.row1), row 1 (x.row2, x.row3), row 2 (y.row0,
-// y.row1), row 3 (y.row2, y.row3): returned as (first, second).
-__device__ __forceinline__ void rows_pair(uint32_t x, uint32_t y, uint32_t &first, uint32_t &second) {
-    const auto r = __builtin_amdgcn_permlane32_swap(x, y, false, false);  // (x0 x1 y0 y1), (x2 x3 y2 y3)
-    const auto q = __builtin_amdgcn_permlane16_swap(r[0], r[1], false, false);
-    first = q[0];   // (x0 x2 y0 y2)
-    second = q[1];  // (x1 x3 y1 y3)
+// Column of position p (0..63) of a block in the transposed V tile.  With
+// p = 32 a + 16 h + 4 g + i (i < 4) the column is 32 a + 8 g + 4 h + i: the
+// eight columns 32 a + 8 g ... + 7 that one lane of the P V product reads
+// as its operand (k-step a, lane group g) then hold positions 4 g + i of the
+// score tiles 2 a and 2 a + 1, the positions that same lane holds in S.
+__device__ __forceinline__ int vt_col(int p) {
+    return (p & 32) | (((p >> 2) & 3) << 3) | (((p >> 4) & 1) << 2) | (p & 3);
 }
 
 // Workgroup (query block, KV head j): 64 RB query rows -- QB = 64 RB / GQ
 // tokens x the GQ heads of group j, row m = token (m / GQ), head (m % GQ)
 // -- against blocks of 64 cached positions staged in LDS (K as [pos][dim],
-// V transposed to [dim][pos]); the next block's K and V are loaded into
-// registers while the current one is multiplied.  Wave w owns the RB
+// V transposed to [dim][vt_col(pos)]); the next block's K and V are loaded
+// into registers while the current one is multiplied.  Wave w owns the RB
 // 16-row blocks 16 (w RB + r) ...  Per position block and row block, with
 // v_mfma_f32_16x16x32_bf16 and the query rows as the N dimension:
 //   S^T = K Q^T (Q split into bf16 hi + lo, K exact; Q carries the factor
@@ -663,11 +662,14 @@ __device__ __forceinline__ void rows_pair(uint32_t x, uint32_t y, uint32_t &firs
 //   by two lane swaps.  Positions past each row's own are masked (only
 //   blocks that reach past the workgroup's first token need it); P =
 //   exp2(S - m) for a reference m that moves only when a block's max
-//   passes it by more than 8;
-//   O^T += V^T P^T (V exact, P split into hi + lo), with 16 rows of ones
-//   after V^T so that one more output tile holds the row sums of P: P
-//   reaches the operand layout (8 consecutive positions per lane) through
-//   two lane swaps per register pair, not through LDS.
+//   passes it by more than 8, rounded once to bf16;
+//   O^T += V^T P^T (V exact), with 16 rows of ones after V^T so that one
+//   more output tile holds the row sums of the same rounded P: the result
+//   o / l is an exact weighted mean of the V rows whose weights differ from
+//   the softmax's by at most 2^-8 of themselves.  The positions of V^T's
+//   columns are permuted within each block (vt_col), so that the operand
+//   of the P V product is in each lane already: its own eight scores of
+//   score tiles 2 k2 and 2 k2 + 1.
 // Masked scores are -inf, so exp2 makes them 0; rows past the chunk's last
 // token attend everything and are never written.  The result o / l goes to
 // the split operand.
@@ -758,14 +760,15 @@ __global__ __launch_bounds__(256) void pf_attn_mfma(const float *Q, const uint16
         }
 #pragma unroll
         for (int u = 0; u < PPT / 2; ++u) {
-            const int i = tid + 256 * u, pp = i % (BP / 2), vcp = i / (BP / 2);
+            const int i = tid + 256 * u, pp = i % (BP / 2), vcp = i / (BP / 2), col = vt_col(2 * pp);
             const uint32_t a4[4] = {vr[2 * u].x, vr[2 * u].y, vr[2 * u].z, vr[2 * u].w};
             const uint32_t b4[4] = {vr[2 * u + 1].x, vr[2 * u + 1].y, vr[2 * u + 1].z, vr[2 * u + 1].w};
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                // dimension 8 vcp + e at positions 2 pp (low half) and 2 pp + 1
+                // dimension 8 vcp + e at positions 2 pp (low half) and 2 pp + 1,
+                // which vt_col keeps in neighbouring columns
                 const uint32_t lo = (a4[e >> 1] >> (16 * (e & 1))) & 0xFFFFu, hi = (b4[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-                *(uint32_t *)(vt + (8 * vcp + e) * LV + 2 * pp) = lo | (hi << 16);
+                *(uint32_t *)(vt + (8 * vcp + e) * LV + col) = lo | (hi << 16);
             }
         }
         __syncthreads();
@@ -821,31 +824,27 @@ __global__ __launch_bounds__(256) void pf_attn_mfma(const float *Q, const uint16
 #pragma unroll
                     for (int i = 0; i < 4; ++i) sc[nt][i] -= dm;
             }
-            uint32_t ph[4][2], pl[4][2];  // P of each tile as bf16 hi / lo pairs (positions 4 kg + 0,1 and 2,3)
+            // P of each tile as bf16 pairs (positions 4 kg + 0,1 and 2,3)
+            typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+            uint32_t ph[4][2];
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) {
                 float pe[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) pe[i] = __builtin_amdgcn_exp2f(sc[nt][i]);
-                split2(pe[0], pe[1], ph[nt][0], pl[nt][0]);
-                split2(pe[2], pe[3], ph[nt][1], pl[nt][1]);
+                ph[nt][0] = __builtin_bit_cast(uint32_t, bf2{(__bf16)pe[0], (__bf16)pe[1]});
+                ph[nt][1] = __builtin_bit_cast(uint32_t, bf2{(__bf16)pe[2], (__bf16)pe[3]});
             }
-            // O^T += V^T P^T: two 32-position k-steps (tiles 2 k2, 2 k2 + 1)
+            // O^T += V^T P^T: two 32-position k-steps, k-step k2 over the
+            // columns that hold score tiles 2 k2 and 2 k2 + 1
 #pragma unroll
             for (int k2 = 0; k2 < 2; ++k2) {
-                uint32_t bh[4], bl[4];
-                rows_pair(ph[2 * k2][0], ph[2 * k2 + 1][0], bh[0], bh[2]);
-                rows_pair(ph[2 * k2][1], ph[2 * k2 + 1][1], bh[1], bh[3]);
-                rows_pair(pl[2 * k2][0], pl[2 * k2 + 1][0], bl[0], bl[2]);
-                rows_pair(pl[2 * k2][1], pl[2 * k2 + 1][1], bl[1], bl[3]);
-                const u4v bph = u4v{bh[0], bh[1], bh[2], bh[3]}, bpl = u4v{bl[0], bl[1], bl[2], bl[3]};
+                const u4v bp = u4v{ph[2 * k2][0], ph[2 * k2][1], ph[2 * k2 + 1][0], ph[2 * k2 + 1][1]};
 #pragma unroll
                 for (int n = 0; n <= NT; ++n) {
                     const u4v av = *(const u4v *)(vt + (n * 16 + r16) * LV + 32 * k2 + 8 * kg);
                     o[r][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, av),
-                                                                      __builtin_bit_cast(bf8v, bph), o[r][n], 0, 0, 0);
-                    o[r][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, av),
-                                                                      __builtin_bit_cast(bf8v, bpl), o[r][n], 0, 0, 0);
+                                                                      __builtin_bit_cast(bf8v, bp), o[r][n], 0, 0, 0);
                 }
             }
         }
