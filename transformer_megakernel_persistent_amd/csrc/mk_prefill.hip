@@ -659,8 +659,9 @@ __device__ __forceinline__ int vt_col(int p) {
 //   in the result layout lane l holds positions 4 (l / 16) + i (i < 4) of
 //   each 16-position tile for the single query row l % 16, so a row's
 //   running max is one lane's, completed over the four lanes l % 16 + 16 k
-//   by two lane swaps.  Positions past each row's own are masked (only
-//   blocks that reach past the workgroup's first token need it); P =
+//   by two lane swaps (only when the reference moves).  Positions past
+//   each row's own are masked (only blocks that reach past the workgroup's
+//   first token need it); P =
 //   exp2(S - m) for a reference m that moves only when a block's max
 //   passes it by more than 8, rounded once to bf16;
 //   O^T += V^T P^T (V exact), with 16 rows of ones after V^T so that one
@@ -811,9 +812,12 @@ __global__ __launch_bounds__(256) void pf_attn_mfma(const float *Q, const uint16
             for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[nt][i]);
-            const float bm = cross4_max(mx);  // block max minus m
-            const bool first = p0 == 0;       // uniform
-            if (first || __builtin_amdgcn_ballot_w64(bm > 8.0f) != 0) {
+            // Some lane's share of a row passes the reference by more than 8
+            // exactly when that row's block max does, so the row max over the
+            // four lanes is needed only inside the branch.
+            const bool first = p0 == 0;  // uniform
+            if (first || __builtin_amdgcn_ballot_w64(mx > 8.0f) != 0) {
+                const float bm = cross4_max(mx);  // block max minus m
                 const float dm = first ? bm : fmaxf(bm, 0.f);  // m's move (0 for rows that keep theirs)
                 const float alpha = first ? 0.f : __builtin_amdgcn_exp2f(-dm);
                 mrun[r] += dm;
@@ -884,19 +888,24 @@ template <int D, int GQ>
 void launch_attn(hipStream_t s, const float *Q, const uint16_t *kc, const uint16_t *vc, int layer, int nh, int nkv,
                  int max_seq, int pos0, int T, uint16_t *Ah, uint16_t *Al, int lda) {
     // Two 16-row blocks per wave halve the K/V fragment reads from LDS per
-    // query row; that pays once the causal ranges are long (a 32768-token
-    // prompt: 259 -> 246 ms of attention), while for short prompts the
-    // longest query block's chain of position blocks sets the time and one
-    // row block per wave is faster (1B, 2048 tokens: 17.4 against 18.4 ms).
-    if (pos0 + T > 8192) {
-        constexpr int QB = 64 * 2 / GQ;
-        hipLaunchKernelGGL((pf_attn_mfma<D, GQ, 2>), dim3((T + QB - 1) / QB * nkv), dim3(256), 0, s, Q, kc, vc, layer, nh,
-                           nkv, max_seq, pos0, T, Ah, Al, lda);
-    } else {
-        constexpr int QB = 64 / GQ;
-        hipLaunchKernelGGL((pf_attn_mfma<D, GQ, 1>), dim3((T + QB - 1) / QB * nkv), dim3(256), 0, s, Q, kc, vc, layer, nh,
-                           nkv, max_seq, pos0, T, Ah, Al, lda);
+    // query row; for 64-dim heads that pays once the causal ranges are long
+    // (a 32768-token prompt: 259 -> 246 ms of attention), while for short
+    // prompts the longest query block's chain of position blocks sets the
+    // time and one row block per wave is faster (1B, 2048 tokens: 17.4
+    // against 18.4 ms).  For 128-dim heads two row blocks need more than 256
+    // VGPRs (occupancy 1) and one is faster (an 8B-shaped 16384-token
+    // prompt: 22.8 against 17.1 ms of attention).
+    if constexpr (D == 64) {
+        if (pos0 + T > 8192) {
+            constexpr int QB = 64 * 2 / GQ;
+            hipLaunchKernelGGL((pf_attn_mfma<D, GQ, 2>), dim3((T + QB - 1) / QB * nkv), dim3(256), 0, s, Q, kc, vc, layer,
+                               nh, nkv, max_seq, pos0, T, Ah, Al, lda);
+            return;
+        }
     }
+    constexpr int QB = 64 / GQ;
+    hipLaunchKernelGGL((pf_attn_mfma<D, GQ, 1>), dim3((T + QB - 1) / QB * nkv), dim3(256), 0, s, Q, kc, vc, layer, nh,
+                       nkv, max_seq, pos0, T, Ah, Al, lda);
 }
 
 int round32(int k) { return (k + 31) & ~31; }
