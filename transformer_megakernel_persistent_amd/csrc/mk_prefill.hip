@@ -24,7 +24,11 @@
 // product is accumulated as W.hi + W.lo in fp32 by v_mfma_f32_16x16x32_bf16,
 // so an activation keeps about 16 bits of mantissa (relative error below
 // 2^-16) -- the decode step's activations are fp32 throughout; the cache
-// rows agree with it to within the bf16 rounding of the stored values.
+// rows agree with it to within the bf16 rounding of the stored values.  In
+// the attention the queries are split the same way; the probabilities are
+// rounded once to bf16 and their row sums taken over the same rounded
+// values, so each output is an exact weighted mean of V rows whose weights
+// are within 2^-8 (relative) of the softmax's.
 //
 // Weights are read in place from the decode kernel's packed layout (no
 // second copy of the model): a GEMM loader lane finds the 16-byte piece
