@@ -94,13 +94,13 @@ def test_batched_prefill_input_split_ragged(env):
     assert max(errs) <= 2e-2 and agree == 3
 
 
-@pytest.mark.parametrize("heads,head_dim,chunk", [(4, 64, 2048), (8, 128, 2048), (4, 64, 0)])
+@pytest.mark.parametrize("heads,head_dim,chunk", [(4, 64, 2048), (8, 64, 2048), (8, 128, 2048), (4, 64, 0)])
 def test_batched_prefill_long_prompt_two_row_blocks(env, heads, head_dim, chunk):
     # Once a chunk's causal range passes 8192 positions the attention takes
-    # two 16-row query blocks per wave.  8300 positions in chunks of 2048
-    # (or the default 4096): the last chunk (pos0 8192, 108 tokens) ends
-    # inside a query block of that path, with one KV head (four or eight
-    # query heads per KV head)
+    # two 16-row query blocks per wave for 64-dim heads (128-dim heads keep
+    # one).  8300 positions in chunks of 2048 (or the default 4096): the
+    # last chunk (pos0 8192, 108 tokens) ends inside a query block of that
+    # path, with one KV head (four or eight query heads per KV head)
     cfg = tiny_bf16(n_layers=1, n_heads=heads, n_kv_heads=1, head_dim=head_dim)
     errs, agree = run_pair(env, cfg, seed=79, n_prompt=8300, n_steps=2, tuning={"prefill_chunk": chunk},
                            expect_batched=True)
