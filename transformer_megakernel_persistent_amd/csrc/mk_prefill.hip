@@ -153,13 +153,14 @@ __device__ __forceinline__ const unsigned char *row_piece(const RowLoc &r, int64
 // input a multiple of 8; a 16-byte piece holds 8 bf16 or 16 int8 inputs).
 // e = dmap[f / 8] gives the owning workgroup's block offset, its pieces per
 // row group, the piece and the byte offset inside it (mk_down_geo,
-// tabulated by the host).
+// tabulated by the host).  Output row n = 64 grp + r: with grp the same for
+// a whole wave, everything but the row's 16-byte column r is wave-uniform.
 __device__ __forceinline__ const unsigned char *down_piece(const MkStage &st, const unsigned char *layer_block,
-                                                           const int4 e, int n) {
-    const int grp = n >> 6, c = grp & 3, gl = grp >> 2;
+                                                           const int4 e, int grp, int r) {
+    const int c = grp & 3, gl = grp >> 2;
     const int qq = gl * e.y + e.z;
-    return layer_block + e.x + (int64_t)(qq >> 2) * st.slot_stride + (c * 4 + (qq & 3)) * MK_CHUNK_BYTES +
-           (n & 63) * 16 + e.w;
+    return layer_block + e.x + (int64_t)(qq >> 2) * st.slot_stride + (c * 4 + (qq & 3)) * MK_CHUNK_BYTES + e.w +
+           r * 16;
 }
 
 // Entry i of the down stage's map (int4 per block of 8 inputs), read at a
@@ -390,6 +391,14 @@ __global__ __launch_bounds__(512, 1) void pf_gemm_ring(const MkStage st, const u
             bok[q] = n < N;
             if constexpr (!DOWN) rl[q] = row_loc(st, layer_block, grid, bok[q] ? n : 0, Q8 ? 1 : 2);
         }
+        // Row split: the address of each B row's current 1 KiB chunk, found
+        // again only when a step enters the next chunk (every 16 steps for
+        // bf16, 32 for int8; a step's 32 inputs never straddle two chunks, so
+        // the chunk is wave-uniform); a load adds the step's offset inside
+        // the chunk and the lane's piece.  Issued in increasing step order.
+        constexpr int EB = Q8 ? 1 : 2, EPC = MK_CHUNK_BYTES / EB;  // bytes per element, elements per chunk
+        const unsigned char *bch[NQ];
+        int kc_cur = -1;
         auto issue = [&](int s) {
             lds_u8 *base = ring + (s % C::NST) * C::STAGE;
             const int k0 = (sbeg + s) * RG_BK;
@@ -408,7 +417,7 @@ __global__ __launch_bounds__(512, 1) void pf_gemm_ring(const MkStage st, const u
                 const int4 e = f < F ? dmap4(dmap, f >> 3) : int4{0, 0, 0, 0};
 #pragma unroll
                 for (int h = 0; h < BN / 64; ++h) {
-                    const unsigned char *src = f < F && bok[h] ? down_piece(st, layer_block, e, n0 + 64 * h + lane) : zl;
+                    const unsigned char *src = f < F && bok[h] ? down_piece(st, layer_block, e, (n0 >> 6) + h, lane) : zl;
 #pragma unroll
                     for (int b = 0; b < 2; ++b)
                         __builtin_amdgcn_global_load_lds(
@@ -422,30 +431,28 @@ __global__ __launch_bounds__(512, 1) void pf_gemm_ring(const MkStage st, const u
                 const int4 e = f < F ? dmap4(dmap, f >> 3) : int4{0, 0, 0, 0};
 #pragma unroll
                 for (int h = 0; h < C::QB; ++h) {
-                    const unsigned char *src = f < F && bok[h] ? down_piece(st, layer_block, e, n0 + 64 * h + lane) : zl;
+                    const unsigned char *src = f < F && bok[h] ? down_piece(st, layer_block, e, (n0 >> 6) + h, lane) : zl;
                     __builtin_amdgcn_global_load_lds(
                         (const void *)src,
                         (__attribute__((address_space(3))) void *)(base + 2 * RG_SEC + lw * (BN * 16) + h * 1024), 16, 0,
                         0);
                 }
-            } else if constexpr (Q8) {
-#pragma unroll
-                for (int q = 0; q < C::QB; ++q) {
-                    const unsigned char *src = bok[q] ? row_piece(rl[q], st.slot_stride, k0 + 16 * jb[q], 1) : zl;
-                    __builtin_amdgcn_global_load_lds(
-                        (const void *)src,
-                        (__attribute__((address_space(3))) void *)(base + 2 * RG_SEC + ((BN / 4) * lw + 32 * q) * RG_BK),
-                        16, 0, 0);
-                }
             } else {
+                const int kc = k0 / EPC;  // wave-uniform
+                if (kc != kc_cur) {
+#pragma unroll
+                    for (int q = 0; q < NQ; ++q) bch[q] = row_piece(rl[q], st.slot_stride, kc * EPC, EB);
+                    kc_cur = kc;
+                }
+                const int ko = (k0 % EPC) * EB;  // the step's first input, bytes into the chunk
+                // the lane's piece: inputs 8 jb (bf16) or 16 jb (int8) of the step
 #pragma unroll
                 for (int q = 0; q < C::QB; ++q) {
-                    const unsigned char *src = bok[q] ? row_piece(rl[q], st.slot_stride, k0 + 8 * jb[q], 2) : zl;
+                    const unsigned char *src = bok[q] ? bch[q] + ko + 16 * jb[q] : zl;
+                    const int row0 = Q8 ? (BN / 4) * lw + 32 * q : (BN / 4) * lw + 16 * q;  // first LDS row of the load
                     __builtin_amdgcn_global_load_lds(
                         (const void *)src,
-                        (__attribute__((address_space(3))) void *)(base + 2 * RG_SEC +
-                                                                   ((BN / 4) * lw + 16 * q) * (RG_BK * 2)),
-                        16, 0, 0);
+                        (__attribute__((address_space(3))) void *)(base + 2 * RG_SEC + row0 * (RG_BK * EB)), 16, 0, 0);
                 }
             }
         };
