@@ -25,10 +25,9 @@
 // so an activation keeps about 16 bits of mantissa (relative error below
 // 2^-16) -- the decode step's activations are fp32 throughout; the cache
 // rows agree with it to within the bf16 rounding of the stored values.  In
-// the attention the queries are split the same way; the probabilities are
-// rounded once to bf16 and their row sums taken over the same rounded
-// values, so each output is an exact weighted mean of V rows whose weights
-// are within 2^-8 (relative) of the softmax's.
+// the attention the queries and the probabilities are split the same way
+// (with the probabilities rounded once to bf16, an 80-layer prefill's cache
+// rows drift to several bf16 steps from the oracle's in the last layers).
 //
 // Weights are read in place from the decode kernel's packed layout (no
 // second copy of the model): a GEMM loader lane finds the 16-byte piece
@@ -674,14 +673,12 @@ __device__ __forceinline__ int vt_col(int p) {
 //   each row's own are masked (only blocks that reach past the workgroup's
 //   first token need it); P =
 //   exp2(S - m) for a reference m that moves only when a block's max
-//   passes it by more than 8, rounded once to bf16;
-//   O^T += V^T P^T (V exact), with 16 rows of ones after V^T so that one
-//   more output tile holds the row sums of the same rounded P: the result
-//   o / l is an exact weighted mean of the V rows whose weights differ from
-//   the softmax's by at most 2^-8 of themselves.  The positions of V^T's
-//   columns are permuted within each block (vt_col), so that the operand
-//   of the P V product is in each lane already: its own eight scores of
-//   score tiles 2 k2 and 2 k2 + 1.
+//   passes it by more than 8;
+//   O^T += V^T P^T (V exact, P split into hi + lo), with 16 rows of ones
+//   after V^T so that one more output tile holds the row sums of P.  The
+//   positions of V^T's columns are permuted within each block (vt_col), so
+//   that the operand of the P V product is in each lane already: its own
+//   eight scores of score tiles 2 k2 and 2 k2 + 1.
 // Masked scores are -inf, so exp2 makes them 0; rows past the chunk's last
 // token attend everything and are never written.  The result o / l goes to
 // the split operand.
@@ -843,18 +840,17 @@ __global__ __launch_bounds__(256) void pf_attn_mfma(const float *Q, const uint16
                     for (int i = 0; i < 4; ++i) sc[r][nt][i] -= dm;
             }
         };
-        typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) qk_tile(0, nt);
         prep(0);
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
-            // P of each tile as bf16 pairs (positions 4 kg + 0,1 and 2,3).
+            // P of each tile as bf16 hi / lo pairs (positions 4 kg + 0,1 and 2,3).
             // With a next row block, its score products of tile nt go first
             // and this block's exponentials of tile nt after them, fenced in
             // that order, so that the vector work issues while the matrix
             // cores run (1B, 32768 tokens: attention 116.6 -> 110.7 ms).
-            uint32_t ph[4][2];
+            uint32_t ph[4][2], pl[4][2];
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) {
                 if (r + 1 < RB) {
@@ -864,8 +860,8 @@ __global__ __launch_bounds__(256) void pf_attn_mfma(const float *Q, const uint16
                 float pe[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) pe[i] = __builtin_amdgcn_exp2f(sc[r][nt][i]);
-                ph[nt][0] = __builtin_bit_cast(uint32_t, bf2{(__bf16)pe[0], (__bf16)pe[1]});
-                ph[nt][1] = __builtin_bit_cast(uint32_t, bf2{(__bf16)pe[2], (__bf16)pe[3]});
+                split2(pe[0], pe[1], ph[nt][0], pl[nt][0]);
+                split2(pe[2], pe[3], ph[nt][1], pl[nt][1]);
                 if (r + 1 < RB) __builtin_amdgcn_sched_barrier(0);
             }
             // O^T += V^T P^T: two 32-position k-steps, k-step k2 over the
@@ -873,11 +869,14 @@ __global__ __launch_bounds__(256) void pf_attn_mfma(const float *Q, const uint16
 #pragma unroll
             for (int k2 = 0; k2 < 2; ++k2) {
                 const u4v bp = u4v{ph[2 * k2][0], ph[2 * k2][1], ph[2 * k2 + 1][0], ph[2 * k2 + 1][1]};
+                const u4v bq = u4v{pl[2 * k2][0], pl[2 * k2][1], pl[2 * k2 + 1][0], pl[2 * k2 + 1][1]};
 #pragma unroll
                 for (int n = 0; n <= NT; ++n) {
                     const u4v av = *(const u4v *)(vt + (n * 16 + r16) * LV + 32 * k2 + 8 * kg);
                     o[r][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, av),
                                                                       __builtin_bit_cast(bf8v, bp), o[r][n], 0, 0, 0);
+                    o[r][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, av),
+                                                                      __builtin_bit_cast(bf8v, bq), o[r][n], 0, 0, 0);
                 }
             }
             if (r + 1 < RB) prep(r + 1);
