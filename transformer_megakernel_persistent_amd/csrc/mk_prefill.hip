@@ -784,12 +784,18 @@ __global__ __launch_bounds__(256) void pf_attn_mfma(const float *Q, const uint16
         if (p0 + BP < n_pos) fetch(p0 + BP);
         const bool diag = p0 + BP - 1 > pos0 + t_base;  // uniform
         const bool first = p0 == 0;                     // uniform
-        // the block's K fragments, shared by the row blocks
+        // the block's K fragments: read once for two row blocks, in place for one
         u4v kf[4][KS];
+        if constexpr (RB > 1) {
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
+            for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-            for (int k = 0; k < KS; ++k) kf[nt][k] = *(const u4v *)(ks + (nt * 16 + r16) * LK + 32 * k + 8 * kg);
+                for (int k = 0; k < KS; ++k) kf[nt][k] = *(const u4v *)(ks + (nt * 16 + r16) * LK + 32 * k + 8 * kg);
+        }
+        auto kfrag = [&](int nt, int k) -> u4v {
+            if constexpr (RB > 1) return kf[nt][k];
+            else return *(const u4v *)(ks + (nt * 16 + r16) * LK + 32 * k + 8 * kg);
+        };
         // S^T - m of row block r, tile nt: lane holds positions 16 nt + 4 kg
         // + i of row r16 (the accumulators start at minus the row's running
         // max, so the products land already shifted for exp2)
@@ -799,9 +805,10 @@ __global__ __launch_bounds__(256) void pf_attn_mfma(const float *Q, const uint16
             sc[r][nt] = f4v{nm, nm, nm, nm};
 #pragma unroll
             for (int k = 0; k < KS; ++k) {
-                sc[r][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, kf[nt][k]),
+                const u4v ak = kfrag(nt, k);
+                sc[r][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, ak),
                                                                     __builtin_bit_cast(bf8v, qh[r][k]), sc[r][nt], 0, 0, 0);
-                sc[r][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, kf[nt][k]),
+                sc[r][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, ak),
                                                                     __builtin_bit_cast(bf8v, ql[r][k]), sc[r][nt], 0, 0, 0);
             }
         };
